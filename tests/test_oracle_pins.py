@@ -1,0 +1,408 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+The FlashDP and DP-GRAPE pages print no worked example, so every pin here is
+a closed form, an invariant, a textbook identity, brute force on tiny inputs,
+or agreement with an independent library (rocRAND's Philox4x32-10 engine).
+The last group plants mistakes in the oracle (on the CPU) and checks that at
+least one pin catches each of them.
+"""
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import dp_linear, philox
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def _rand_case(rng, B, T, din, dout, masked=False, dtype="f32"):
+    X = rng.standard_normal((B, T, din)).astype(np.float32)
+    G = (0.3 * rng.standard_normal((B, T, dout))).astype(np.float32)
+    mask = None
+    if masked:
+        mask = (rng.random((B, T)) < 0.6).astype(np.uint8)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(X), f32_to_bf16_bits(G), mask
+    return X, G, mask
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(b), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 against rocRAND (independent library implementation)
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def rocrand_ref(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND reference helper")
+    out = tmp_path_factory.mktemp("rr") / "rocrand_philox_ref"
+    src = os.path.join(HERE, "golden", "rocrand_philox_ref.cpp")
+    subprocess.run([hipcc, "-x", "c++", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                    "-O1", src, "-o", str(out)], check=True, capture_output=True)
+
+    def run(pairs):
+        text = "".join(f"{s} {b}\n" for s, b in pairs)
+        res = subprocess.run([str(out)], input=text, capture_output=True, text=True, check=True)
+        return [list(map(int, line.split())) for line in res.stdout.strip().splitlines()]
+    return run
+
+
+def _philox_cases():
+    rng = np.random.default_rng(123)
+    pairs = [(0, 0), (0, 1), (7, 0), (1, 2**32 - 1), (1, 2**32), (3, 2**32 + 5),
+             (2**64 - 1, 2**64 - 1), (0xDEADBEEFCAFEF00D, 2**63 + 17)]
+    pairs += [(int(s), int(b)) for s, b in zip(rng.integers(0, 2**63, 40, dtype=np.int64),
+                                               rng.integers(0, 2**40, 40, dtype=np.int64))]
+    return pairs
+
+
+def test_philox_scalar_matches_rocrand(rocrand_ref):
+    pairs = _philox_cases()
+    ref = rocrand_ref(pairs)
+    for (s, b), r in zip(pairs, ref):
+        assert philox.philox4x32_10(philox.block_counter(b), philox.seed_key(s)) == r, (s, b)
+
+
+def test_philox_vector_matches_rocrand(rocrand_ref):
+    pairs = [(5, b) for b in range(2**32 - 6, 2**32 + 6)]   # carry into hi32(block)
+    ref = np.array(rocrand_ref(pairs), dtype=np.uint32)
+    got = philox.philox_words(5, [b for _, b in pairs])
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_philox_vector_matches_scalar():
+    got = philox.philox_words(99, np.arange(1000, 1064, dtype=np.uint64))
+    ref = np.array(philox.philox_words_scalar(99, 1000, 64), dtype=np.uint32)
+    np.testing.assert_array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# uniform map and Box-Muller
+# --------------------------------------------------------------------------
+def test_uniform_map_endpoints():
+    u = philox.words_to_uniform(np.array([0, 511, 512, 2**32 - 1], dtype=np.uint64))
+    assert u[0] == 0.5 * 2.0 ** -23
+    assert u[1] == u[0]                       # the low 9 bits are dropped
+    assert u[2] == 1.5 * 2.0 ** -23
+    assert u[3] == 1.0 - 2.0 ** -24
+    assert np.all((u > 0) & (u < 1))
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)   # exact in fp32
+
+
+def test_box_muller_closed_forms():
+    z0, z1 = philox.box_muller(np.array([math.exp(-0.5)]), np.array([0.0]))
+    assert abs(z0[0] - 1.0) < 1e-15 and abs(z1[0]) < 1e-15
+    z0, z1 = philox.box_muller(np.array([math.exp(-2.0)]), np.array([0.25]))
+    assert abs(z0[0]) < 1e-15 and abs(z1[0] - 2.0) < 1e-15
+    z0, z1 = philox.box_muller(np.array([math.exp(-4.5)]), np.array([0.5]))
+    assert abs(z0[0] + 3.0) < 1e-14 and abs(z1[0]) < 1e-14
+
+
+def test_box_muller_lane_pairing():
+    """z0, z1 come from (u0, u1) and z2, z3 from (u2, u3)."""
+    w = philox.philox_words(11, np.arange(4, dtype=np.uint64))
+    u = philox.words_to_uniform(w)
+    z = philox.normals_of_words(w)
+    r01 = np.sqrt(-2 * np.log(u[:, 0]))
+    r23 = np.sqrt(-2 * np.log(u[:, 2]))
+    np.testing.assert_allclose(z[:, 0] ** 2 + z[:, 1] ** 2, r01 ** 2, rtol=1e-12)
+    np.testing.assert_allclose(z[:, 2] ** 2 + z[:, 3] ** 2, r23 ** 2, rtol=1e-12)
+    np.testing.assert_allclose(np.arctan2(z[:, 1], z[:, 0]) % (2 * np.pi),
+                               (2 * np.pi * u[:, 1]) % (2 * np.pi), atol=1e-9)
+
+
+def test_gaussian_statistics():
+    from scipy import stats
+    z = philox.gaussian(0, 0, 2_000_000)
+    assert abs(z.mean()) < 5e-3
+    assert abs(z.var() - 1.0) < 5e-3
+    assert stats.kstest(z, "norm").pvalue > 1e-4
+    zz = z.reshape(-1, 2)
+    assert abs(np.corrcoef(zz[:, 0], zz[:, 1])[0, 1]) < 5e-3
+    # 23-bit uniforms cap |z| at sqrt(-2 ln 2**-24) ~ 5.77
+    assert np.abs(z).max() <= math.sqrt(-2 * math.log(0.5 * 2.0 ** -23)) + 1e-12
+
+
+def test_gaussian_scalar_matches_vector():
+    np.testing.assert_allclose(philox.gaussian_scalar(3, 17, 37), philox.gaussian(3, 17, 37),
+                               rtol=0, atol=1e-14)
+
+
+def test_gaussian_offset_concatenation():
+    n = 4 * 257
+    whole = philox.gaussian(42, 10, 2 * n)
+    first = philox.gaussian(42, 10, n)
+    second = philox.gaussian(42, 10 + philox.noise_blocks(n), n)
+    np.testing.assert_array_equal(whole, np.concatenate([first, second]))
+
+
+def test_gaussian_at_matches_gaussian():
+    full = philox.gaussian(9, 5, 1001)
+    idx = np.array([0, 1, 2, 3, 4, 999, 1000, 517])
+    np.testing.assert_array_equal(philox.gaussian_at(9, 5, idx), full[idx])
+
+
+# --------------------------------------------------------------------------
+# the clip-and-accumulate oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("masked", [False, True])
+def test_oracle_matches_brute_force(masked):
+    rng = np.random.default_rng(1)
+    X, G, mask = _rand_case(rng, 3, 4, 5, 4, masked)
+    C = 0.9
+    out, norms, c = dp_linear.oracle_linear(X, G, mask, C, 0.0, 0, 0, "f32")
+    S, bn = dp_linear.brute_force_linear(X.astype(np.float64).tolist(),
+                                         G.astype(np.float64).tolist(),
+                                         None if mask is None else mask.tolist(), C)
+    np.testing.assert_allclose(norms, bn, rtol=1e-12)
+    np.testing.assert_allclose(out * 3, np.array(S), rtol=1e-12, atol=1e-14)
+
+
+def test_t1_closed_form():
+    """T = 1: g_i is the outer product G_i X_i^T, so ||g_i|| = ||G_i|| ||X_i||."""
+    rng = np.random.default_rng(2)
+    X, G, _ = _rand_case(rng, 5, 1, 7, 6)
+    _, norms, _ = dp_linear.oracle_linear(X, G, None, 1.0, 0.0, 0, 0, "f32")
+    ref = np.linalg.norm(G.astype(np.float64)[:, 0, :], axis=1) * \
+        np.linalg.norm(X.astype(np.float64)[:, 0, :], axis=1)
+    np.testing.assert_allclose(norms, ref, rtol=1e-12)
+
+
+def test_gram_identity():
+    """||G^T X||_F^2 = <X X^T, G G^T>_F (the Gram-norm identity)."""
+    rng = np.random.default_rng(3)
+    X, G, mask = _rand_case(rng, 4, 9, 11, 13, masked=True)
+    _, norms, _ = dp_linear.oracle_linear(X, G, mask, 1.0, 0.0, 0, 0, "f32")
+    for i in range(4):
+        keep = mask[i].astype(bool)
+        x = X[i].astype(np.float64)[keep]
+        g = G[i].astype(np.float64)[keep]
+        gram = np.sum((x @ x.T) * (g @ g.T))
+        assert abs(norms[i] ** 2 - gram) <= 1e-12 * max(gram, 1e-300)
+
+
+def test_no_clip_no_noise_is_plain_gradient():
+    """C -> inf, sigma = 0: out = (sum over all rows of G~^T X~) / B, one big GEMM."""
+    rng = np.random.default_rng(4)
+    X, G, mask = _rand_case(rng, 3, 6, 8, 5, masked=True)
+    out, _, c = dp_linear.oracle_linear(X, G, mask, 1e30, 0.0, 0, 0, "f32")
+    assert np.all(c == 1.0)
+    keep = mask.reshape(-1).astype(bool)
+    Xf = X.reshape(-1, 8).astype(np.float64)[keep]
+    Gf = G.reshape(-1, 5).astype(np.float64)[keep]
+    np.testing.assert_allclose(out, Gf.T @ Xf / 3, rtol=1e-12, atol=1e-15)
+
+
+def test_clip_invariant():
+    rng = np.random.default_rng(5)
+    X, G, _ = _rand_case(rng, 8, 5, 6, 7)
+    G = G * (10.0 ** np.arange(-4, 4)[:, None, None]).astype(np.float32)
+    C = 0.7
+    _, norms, c = dp_linear.oracle_linear(X, G, None, C, 0.0, 0, 0, "f32")
+    assert np.all(c * norms <= C * (1 + 1e-12))
+    assert np.all((c == 1.0) == (norms <= C))
+    assert (c < 1).any() and (c == 1).any()
+
+
+def test_single_sample_clipped_norm():
+    """B = 1, sigma = 0: ||B out|| = min(n_1, C)."""
+    rng = np.random.default_rng(6)
+    X, G, _ = _rand_case(rng, 1, 7, 9, 4)
+    for C in (1e-3, 1e3):
+        out, norms, _ = dp_linear.oracle_linear(X, G, None, C, 0.0, 0, 0, "f32")
+        assert abs(np.linalg.norm(out) - min(norms[0], C)) <= 1e-12 * min(norms[0], C)
+
+
+def test_scale_invariance_of_clipped_sample():
+    rng = np.random.default_rng(7)
+    X, G, _ = _rand_case(rng, 3, 5, 6, 4)
+    C = 1e-2
+    out1, n1, c1 = dp_linear.oracle_linear(X, G, None, C, 0.0, 0, 0, "f32")
+    assert np.all(c1 < 1)
+    G2 = G.astype(np.float64)
+    G2[1] *= 8.0                               # exact in fp32
+    out2, _, _ = dp_linear.oracle_linear(X, G2.astype(np.float32), None, C, 0.0, 0, 0, "f32")
+    np.testing.assert_allclose(out2, out1, rtol=1e-12, atol=1e-16)
+
+
+def test_permutation_invariance():
+    rng = np.random.default_rng(8)
+    X, G, mask = _rand_case(rng, 5, 4, 6, 3, masked=True)
+    p = np.array([3, 0, 4, 1, 2])
+    o1, n1, _ = dp_linear.oracle_linear(X, G, mask, 0.5, 0.0, 0, 0, "f32")
+    o2, n2, _ = dp_linear.oracle_linear(X[p], G[p], mask[p], 0.5, 0.0, 0, 0, "f32")
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(n2, n1[p], rtol=1e-14)
+
+
+def test_batch_split_linearity():
+    rng = np.random.default_rng(9)
+    X, G, _ = _rand_case(rng, 6, 4, 5, 3)
+    C = 0.3
+    o_all, _, _ = dp_linear.oracle_linear(X, G, None, C, 0.0, 0, 0, "f32")
+    o_a, _, _ = dp_linear.oracle_linear(X[:2], G[:2], None, C, 0.0, 0, 0, "f32")
+    o_b, _, _ = dp_linear.oracle_linear(X[2:], G[2:], None, C, 0.0, 0, 0, "f32")
+    np.testing.assert_allclose(6 * o_all, 2 * o_a + 4 * o_b, rtol=1e-12, atol=1e-15)
+
+
+def test_mask_equals_unpadded_calls_and_ignores_padding():
+    rng = np.random.default_rng(10)
+    B, T, din, dout = 4, 9, 5, 6
+    X, G, _ = _rand_case(rng, B, T, din, dout)
+    lengths = np.array([9, 1, 4, 0])
+    mask = (np.arange(T)[None, :] < lengths[:, None]).astype(np.uint8)
+    C = 0.8
+    out, norms, _ = dp_linear.oracle_linear(X, G, mask, C, 0.0, 0, 0, "f32")
+    S = np.zeros((dout, din))
+    for i in range(B):
+        if lengths[i] == 0:
+            assert norms[i] == 0.0
+            continue
+        o_i, n_i, _ = dp_linear.oracle_linear(X[i:i + 1, :lengths[i]], G[i:i + 1, :lengths[i]],
+                                              None, C, 0.0, 0, 0, "f32")
+        S += o_i
+        assert abs(n_i[0] - norms[i]) <= 1e-13 * n_i[0]
+    np.testing.assert_allclose(out * B, S, rtol=1e-12, atol=1e-15)
+    Xn, Gn = X.copy(), G.copy()
+    Xn[mask == 0] = np.nan
+    Gn[mask == 0] = np.inf
+    out2, norms2, _ = dp_linear.oracle_linear(Xn, Gn, mask, C, 0.0, 0, 0, "f32")
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(norms2, norms)
+
+
+def test_projection_identity_reduces_to_dense():
+    rng = np.random.default_rng(11)
+    X, G, mask = _rand_case(rng, 3, 5, 6, 4, masked=True)
+    P = np.eye(6, dtype=np.float32)
+    o1, n1, _ = dp_linear.oracle_linear(X, G, mask, 0.5, 0.7, 3, 2, "f32")
+    o2, n2, _ = dp_linear.oracle_projected(X, G, mask, P, 0.5, 0.7, 3, 2, "f32")
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(n2, n1)
+
+
+def test_projection_associativity():
+    """h_i = G~_i^T (X~_i P) equals (G~_i^T X~_i) P, so n_i = ||g_i P||."""
+    rng = np.random.default_rng(12)
+    X, G, mask = _rand_case(rng, 3, 5, 8, 4, masked=True)
+    P = rng.standard_normal((8, 3)).astype(np.float32)
+    _, n_proj, _ = dp_linear.oracle_projected(X, G, mask, P, 1.0, 0.0, 0, 0, "f32")
+    for i in range(3):
+        keep = mask[i].astype(bool)
+        g = G[i].astype(np.float64)[keep].T @ X[i].astype(np.float64)[keep]
+        assert abs(np.linalg.norm(g @ P.astype(np.float64)) - n_proj[i]) <= 1e-12 * n_proj[i]
+
+
+def test_zero_activations_give_pure_noise():
+    """X = 0: every norm is 0, every c_i = 1, out = sigma C xi / B."""
+    B, T, din, dout = 3, 4, 6, 5
+    X = np.zeros((B, T, din), np.float32)
+    G = np.ones((B, T, dout), np.float32)
+    sigma, C, seed, off = 1.3, 0.4, 77, 1234
+    out, norms, c = dp_linear.oracle_linear(X, G, None, C, sigma, seed, off, "f32")
+    assert np.all(norms == 0) and np.all(c == 1)
+    xi = philox.gaussian(seed, off, din * dout).reshape(dout, din)
+    np.testing.assert_allclose(out, sigma * C * xi / B, rtol=1e-15)
+
+
+def test_entries_and_norms_helpers_agree_with_oracle():
+    rng = np.random.default_rng(13)
+    X, G, mask = _rand_case(rng, 4, 6, 10, 7, masked=True, dtype="bf16")
+    C, sigma = 0.05, 0.9
+    out, norms, c = dp_linear.oracle_linear(X, G, mask, C, sigma, 5, 3, "bf16")
+    rows = np.array([0, 6, 3, 2])
+    cols = np.array([9, 0, 4, 5])
+    ent = dp_linear.oracle_entries(X, G, mask, c, rows, cols, sigma, C, 5, 3, "bf16")
+    np.testing.assert_allclose(ent, out[rows, cols], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(dp_linear.oracle_norms(X, G, mask, "bf16", samples=[2, 0]),
+                               norms[[2, 0]], rtol=1e-14)
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(14)
+    a = np.concatenate([rng.standard_normal(10000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -2.0 ** -130, 3.0e38], np.float32)])
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(f32_to_bf16_bits(a), ref)
+    b = f32_to_bf16_bits(a)
+    np.testing.assert_array_equal(f32_to_bf16_bits(bf16_bits_to_f32(b)), b)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each must trip at least one pin
+# --------------------------------------------------------------------------
+def _pins_fail(fns):
+    for fn in fns:
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+_DENSE_PINS = [
+    lambda: test_oracle_matches_brute_force(True),
+    test_t1_closed_form, test_gram_identity, test_no_clip_no_noise_is_plain_gradient,
+    test_clip_invariant, test_single_sample_clipped_norm, test_mask_equals_unpadded_calls_and_ignores_padding,
+    test_zero_activations_give_pure_noise,
+]
+
+
+def test_planted_transposed_operand(monkeypatch):
+    monkeypatch.setattr(dp_linear, "per_sample_grad", lambda Xi, Gi: Xi.T @ Gi)
+    assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_clip_rule(monkeypatch):
+    monkeypatch.setattr(dp_linear, "clip_factor", lambda n, C: C / n if n > 0 else 1.0)
+    assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_mask_as_product(monkeypatch):
+    def mult(rows, mask_row):
+        return rows if mask_row is None else rows * np.asarray(mask_row)[:, None]
+    monkeypatch.setattr(dp_linear, "select_active", mult)
+    assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_noise_lane(monkeypatch):
+    orig = philox.normals_of_words
+    monkeypatch.setattr(philox, "normals_of_words", lambda w: orig(w)[:, [1, 0, 2, 3]])
+    assert _pins_fail([test_box_muller_lane_pairing, test_gaussian_statistics])
+
+
+def test_planted_philox_multiplier(monkeypatch, rocrand_ref):
+    monkeypatch.setattr(philox, "PHILOX_M1", 0xCD9E8D55)
+    assert _pins_fail([lambda: test_philox_scalar_matches_rocrand(rocrand_ref)])
+
+
+def test_planted_noise_offset(monkeypatch):
+    orig = dp_linear.noise_matrix
+    monkeypatch.setattr(dp_linear, "noise_matrix", lambda s, o, sh: orig(s, o + 1, sh))
+    assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_noise_without_clip_norm(monkeypatch):
+    # simulates out = (S + sigma xi) / B, i.e. the factor C dropped (C = 0.4 in the pin)
+    orig = dp_linear.noise_matrix
+    monkeypatch.setattr(dp_linear, "noise_matrix", lambda s, o, sh: orig(s, o, sh) / 0.4)
+    assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_dropped_sample(monkeypatch):
+    orig = dp_linear.clip_accumulate
+    monkeypatch.setattr(dp_linear, "clip_accumulate",
+                        lambda gs, C: orig(list(gs)[:-1] or [np.zeros((1, 1))], C))
+    assert _pins_fail(_DENSE_PINS)
