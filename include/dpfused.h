@@ -1,0 +1,198 @@
+/*
+ * dpfused: per-layer DP-SGD clip-and-accumulate for one linear layer, on
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the library computes (FlashDP: Private Training Large Language Models
+ * with Efficient DP-SGD, Abstract: per-sample gradient clipping done per
+ * layer, gradients computed once, in one fused task; Memory-Efficient
+ * Differentially Private Training with Gradient Random Projection, English
+ * explainer, Problem Statement and Methodology: clip each sample's gradient
+ * before the noise is added, and in the projected variant project first):
+ *
+ *   X~_i, G~_i   rows of sample i whose mask byte is 0 are taken as zero
+ *   g_i          = G~_i^T X~_i                        [dout, din]
+ *   n_i          = ||g_i||_F
+ *   c_i          = 1 if n_i <= C, else C / n_i
+ *   grad_out     = (sum_i c_i g_i + sigma * C * xi) / B
+ *   norms_out[i] = n_i   (before clipping)
+ *
+ * xi_e, for the row-major element index e of grad_out, is the standard normal
+ * number e mod 4 of Philox4x32-10 block (offset + floor(e/4)): key =
+ * (lo32(seed), hi32(seed)), counter = (lo32(block), hi32(block), 0, 0); the
+ * four words w give uniforms u = ((w >> 9) + 0.5) * 2^-23, and Box-Muller
+ * maps (u0,u1) -> (z0,z1) and (u2,u3) -> (z2,z3).  A call consumes
+ * dpfused_noise_blocks(dout*din) blocks: advance `offset` by that much
+ * between calls to draw fresh noise.
+ *
+ * No per-sample gradient is ever written to memory.  The per-sample norms come
+ * from the Gram identity ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> when T is short
+ * relative to the layer, or from the gradient tiles themselves otherwise;
+ * both give the same n_i up to rounding.
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller; the library
+ *     never keeps, frees or reallocates it.  Outputs are overwritten.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     queued on it asynchronously; temporary workspace is allocated and
+ *     released in stream order on the same stream.  Calls on different
+ *     streams may run concurrently.
+ *   - Arguments are checked before anything is queued: on any error nothing
+ *     is launched and nothing is written; the status says why and
+ *     dpfused_last_error() gives a message (per thread).
+ *   - Faults inside a kernel surface at the caller's next synchronisation.
+ *   - NaN or Inf in an ACTIVE row propagates to the outputs; masked rows are
+ *     never read into the arithmetic, whatever they hold.
+ *   - Results are bit-identical from run to run on the same device and build
+ *     (every reduction has a fixed order; no floating-point atomics).
+ */
+#ifndef DPFUSED_H
+#define DPFUSED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DPFUSED_ABI_VERSION 1
+
+typedef enum {
+  DPF_OK = 0,
+  DPF_ERR_INVALID_ARGUMENT = 1, /* a shape, value or pointer is not acceptable */
+  DPF_ERR_UNSUPPORTED = 2,      /* acceptable in principle, not handled (alignment, dtype mix) */
+  DPF_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed */
+  DPF_ERR_HIP = 4               /* the HIP runtime reported an error while queueing */
+} dpf_status;
+
+typedef enum { DPF_F32 = 0, DPF_BF16 = 1 } dpf_dtype;
+
+/* One [B, T, D] activation-like tensor in device memory.  The last dimension
+ * is contiguous; stride_b and stride_t are in ELEMENTS.  `data` must be
+ * 16-byte aligned, and for the vectorised loads also D * elemsize and both
+ * strides * elemsize should be multiples of 16 bytes (other layouts are
+ * accepted and run on a slower element-wise load path). */
+typedef struct {
+  const void* data;
+  int32_t dtype;     /* dpf_dtype */
+  int32_t reserved;  /* must be 0 */
+  int64_t B, T, D;
+  int64_t stride_b, stride_t;
+} dpf_act;
+
+/* The fused per-layer DP step for one linear layer (FlashDP abstract: one
+ * fused per-layer task; the clip rule, noise law and orientation follow the
+ * contract above).
+ *
+ *   X         activations        [B, T, din]   (bf16 or f32)
+ *   G         output gradients   [B, T, dout]  (same dtype as X, same B and T)
+ *   mask      [B, T] uint8, contiguous, 1 = active token; NULL = all active
+ *   C         clip norm, finite and > 0
+ *   sigma     noise multiplier, finite and >= 0 (0 = no noise, no Philox work)
+ *   seed, offset   Philox key and first block (see above)
+ *   grad_out  [dout, din] float32, row-major, overwritten
+ *   norms_out [B] float32, pre-clip n_i; may be NULL
+ *   stream    hipStream_t
+ *
+ * Errors: DPF_ERR_INVALID_ARGUMENT for NULL X/G data or grad_out, B/T/D < 1,
+ * X.B != G.B or X.T != G.T, C not finite or <= 0, sigma not finite or < 0,
+ * strides smaller than the row they step over; DPF_ERR_UNSUPPORTED for mixed
+ * dtypes, an unknown dtype, a non-zero reserved field or a data pointer not
+ * 16-byte aligned; DPF_ERR_OUT_OF_MEMORY if workspace cannot be allocated;
+ * DPF_ERR_HIP if a launch fails. */
+dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G,
+                                          const uint8_t* mask, float C, float sigma,
+                                          uint64_t seed, uint64_t offset,
+                                          float* grad_out, float* norms_out,
+                                          void* stream);
+
+/* Projected variant (Memory-Efficient Differentially Private Training with
+ * Gradient Random Projection, English explainer, Methodology: "Random
+ * Projection over SVD" and "Order of Operations").  Each sample's gradient is
+ * projected by a Gaussian matrix P before it is clipped and summed:
+ *
+ *   Y_i = X~_i P                 [T, r]  (rounded to X's dtype in workspace)
+ *   h_i = G~_i^T Y_i             [dout, r]
+ *   then clip, sum, noise and 1/B exactly as above, with r in place of din.
+ *
+ *   P         [din, r] row-major, same dtype as X, 16-byte aligned
+ *   r         projection rank >= 1
+ *   grad_out  [dout, r] float32, row-major, overwritten
+ *   norms_out [B] float32, pre-clip ||h_i||; may be NULL
+ *
+ * Errors as above, plus DPF_ERR_INVALID_ARGUMENT for NULL P or r < 1. */
+dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_act* G,
+                                                    const uint8_t* mask, const void* P,
+                                                    int64_t r, float C, float sigma,
+                                                    uint64_t seed, uint64_t offset,
+                                                    float* grad_out, float* norms_out,
+                                                    void* stream);
+
+/* Per-sample squared norms ||G~_i^T X~_i||^2 only, in float64, written to
+ * sqnorms_out[B] (device).  With accumulate != 0 the values are ADDED to what
+ * sqnorms_out holds (summing over several linears gives the squared norm of
+ * a sample's gradient across those layers).  Same argument rules as
+ * dpfused_linear_clip_accumulate. */
+dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                                      double* sqnorms_out, int32_t accumulate, void* stream);
+
+/* Clip factors from squared norms: c[i] = 1 if sqrt(sqnorms[i]) <= C else
+ * C / sqrt(sqnorms[i]) (float32), and norms_out[i] = sqrt(sqnorms[i]) when
+ * norms_out is not NULL.  All pointers are device memory; n >= 1. */
+dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float* c_out,
+                                float* norms_out, void* stream);
+
+/* grad_out = (sum_i c[i] G~_i^T X~_i + noise_std * xi) / B for given factors
+ * c[B] (device float32, each finite and > 0), with xi as above (noise_std = 0
+ * disables the noise).  Same argument rules as dpfused_linear_clip_accumulate;
+ * noise_std must be finite and >= 0. */
+dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                                     const float* c, float noise_std, uint64_t seed,
+                                     uint64_t offset, float* grad_out, void* stream);
+
+/* Raw Philox4x32-10 words: out[4*j + k] = word k of block (offset + j),
+ * j < nblocks, with the key/counter layout above.  out: device, 16-byte
+ * aligned, 4*nblocks uint32.  nblocks >= 0 (0 = nothing queued). */
+dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks,
+                                 uint32_t* out, void* stream);
+
+/* out[e] = scale * xi_e for e < n (xi as above: four normals per block,
+ * starting at block `offset`), stored as float32 or as bfloat16 rounded to
+ * nearest-even from the float32 product.  Used to draw the Gaussian
+ * projection P (entries N(0, 1/r): scale = 1/sqrt(r)).  out: device,
+ * 16-byte aligned.  n >= 0. */
+dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale,
+                                 int32_t dtype, void* out, void* stream);
+
+/* Philox blocks consumed by n noise elements: ceil(n / 4); 0 for n <= 0. */
+uint64_t dpfused_noise_blocks(int64_t n_elements);
+
+/* Library options (process-wide).  Names:
+ *   "norm_path"  0 = choose per call (Gram when max T is short relative to
+ *                din*dout/(din+dout), else direct), 1 = always Gram,
+ *                2 = always direct
+ *   "timing"     1 = record a HIP event pair around every kernel the library
+ *                launches, on the launch stream (see dpfused_timing_*); 0 = off
+ * Returns DPF_ERR_INVALID_ARGUMENT for an unknown name or value. */
+dpf_status dpfused_set_option(const char* name, int64_t value);
+int64_t dpfused_get_option(const char* name);
+
+/* Kernel timing, when the "timing" option is on.  dpfused_timing_collect()
+ * waits for every recorded event pair, adds its duration to a per-kernel
+ * total and returns the number of distinct kernels seen since the last
+ * reset; then entry k (k < that number) is read with the three accessors.
+ * Durations are in milliseconds.  Not thread-safe against concurrent calls. */
+void dpfused_timing_reset(void);
+int32_t dpfused_timing_collect(void);
+const char* dpfused_timing_name(int32_t k);
+double dpfused_timing_total_ms(int32_t k);
+int64_t dpfused_timing_launches(int32_t k);
+
+const char* dpfused_status_string(dpf_status s);
+const char* dpfused_last_error(void);
+int32_t dpfused_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPFUSED_H */

@@ -1,0 +1,211 @@
+"""Per-layer DP-SGD clip-and-accumulate for linear layers on AMD MI355X.
+
+Python binding of libdpfused (include/dpfused.h).  This module only
+marshals arguments: torch tensors provide device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+
+    grad, norms = linear_clip_accumulate(X, G, mask=None, C=1.0, sigma=1.0,
+                                         seed=0, offset=0)
+
+computes, for X [B, T, din] and G [B, T, dout] (bf16 or fp32, on the GPU),
+grad = (sum_i c_i G~_i^T X~_i + sigma C xi) / B with c_i = min(1, C/||g_i||),
+and the pre-clip per-sample norms.  See include/dpfused.h for the contract.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
+
+__all__ = [
+    "linear_clip_accumulate", "linear_clip_accumulate_projected", "per_sample_sqnorms",
+    "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
+    "set_option", "get_option", "timing_reset", "timing_collect", "DpfError", "load",
+]
+
+
+def load():
+    """Load libdpfused (raises ImportError if it has not been built)."""
+    return _lib.lib()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DPF_BF16
+    if t.dtype == torch.float32:
+        return DPF_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _act(t) -> DpfAct:
+    if t.dim() != 3:
+        raise ValueError("activations must be [B, T, D]")
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if t.stride(2) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    B, T, D = t.shape
+    return DpfAct(t.data_ptr(), _dtype_code(t), 0, B, T, D, t.stride(0), t.stride(1))
+
+
+def _stream(t, stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _mask_ptr(mask, B, T) -> Optional[int]:
+    if mask is None:
+        return None
+    torch = _torch()
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("mask must be uint8 or bool")
+    if tuple(mask.shape) != (B, T) or not mask.is_contiguous() or not mask.is_cuda:
+        raise ValueError("mask must be a contiguous [B, T] GPU tensor")
+    return mask.data_ptr()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def linear_clip_accumulate(X, G, mask=None, C: float = 1.0, sigma: float = 0.0, seed: int = 0,
+                           offset: int = 0, grad_out=None, norms_out=None, stream=None,
+                           want_norms: bool = True) -> Tuple[object, object]:
+    """Fused per-layer DP step; returns (grad_out [dout, din] fp32, norms [B] fp32 or None)."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if grad_out is None:
+        grad_out = torch.empty((G.shape[2], X.shape[2]), dtype=torch.float32, device=X.device)
+    if norms_out is None and want_norms:
+        norms_out = torch.empty((B,), dtype=torch.float32, device=X.device)
+    st = _lib.lib().dpfused_linear_clip_accumulate(
+        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), float(C), float(sigma),
+        int(seed), int(offset), grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
+    _lib.check(st)
+    return grad_out, norms_out
+
+
+def linear_clip_accumulate_projected(X, G, P, mask=None, C: float = 1.0, sigma: float = 0.0,
+                                     seed: int = 0, offset: int = 0, grad_out=None,
+                                     norms_out=None, stream=None, want_norms: bool = True):
+    """Projected variant: clip/sum/noise of G~_i^T (X~_i P); returns ([dout, r], norms)."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if P.dim() != 2 or not P.is_contiguous() or P.shape[0] != X.shape[2] or P.dtype != X.dtype:
+        raise ValueError("P must be a contiguous [din, r] tensor of X's dtype")
+    r = P.shape[1]
+    if grad_out is None:
+        grad_out = torch.empty((G.shape[2], r), dtype=torch.float32, device=X.device)
+    if norms_out is None and want_norms:
+        norms_out = torch.empty((B,), dtype=torch.float32, device=X.device)
+    st = _lib.lib().dpfused_linear_clip_accumulate_projected(
+        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), P.data_ptr(), int(r),
+        float(C), float(sigma), int(seed), int(offset), grad_out.data_ptr(), _ptr(norms_out),
+        _stream(X, stream))
+    _lib.check(st)
+    return grad_out, norms_out
+
+
+def per_sample_sqnorms(X, G, mask=None, out=None, accumulate: bool = False, stream=None):
+    """||G~_i^T X~_i||^2 per sample (fp64 [B]); with accumulate=True, added into ``out``."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an out tensor")
+        out = torch.empty((B,), dtype=torch.float64, device=X.device)
+    st = _lib.lib().dpfused_per_sample_sqnorms(ctypes.byref(xa), ctypes.byref(ga),
+                                               _mask_ptr(mask, B, T), out.data_ptr(),
+                                               1 if accumulate else 0, _stream(X, stream))
+    _lib.check(st)
+    return out
+
+
+def clip_factors(sqnorms, C: float, c_out=None, norms_out=None, stream=None):
+    """c = min(1, C / sqrt(sqnorms)) (fp32) and the norms, from fp64 squared norms."""
+    torch = _torch()
+    n = sqnorms.numel()
+    if c_out is None:
+        c_out = torch.empty((n,), dtype=torch.float32, device=sqnorms.device)
+    st = _lib.lib().dpfused_clip_factors(sqnorms.data_ptr(), int(n), float(C), c_out.data_ptr(),
+                                         _ptr(norms_out), _stream(sqnorms, stream))
+    _lib.check(st)
+    return c_out, norms_out
+
+
+def scaled_accumulate(X, G, c, mask=None, noise_std: float = 0.0, seed: int = 0, offset: int = 0,
+                      grad_out=None, stream=None):
+    """(sum_i c_i G~_i^T X~_i + noise_std xi) / B for given fp32 factors c [B]."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if grad_out is None:
+        grad_out = torch.empty((G.shape[2], X.shape[2]), dtype=torch.float32, device=X.device)
+    st = _lib.lib().dpfused_scaled_accumulate(ctypes.byref(xa), ctypes.byref(ga),
+                                              _mask_ptr(mask, B, T), c.data_ptr(),
+                                              float(noise_std), int(seed), int(offset),
+                                              grad_out.data_ptr(), _stream(X, stream))
+    _lib.check(st)
+    return grad_out
+
+
+def philox4x32_10(seed: int, offset: int, nblocks: int, out=None, device="cuda", stream=None):
+    """Raw Philox4x32-10 words as an int32 tensor [nblocks, 4] (bit patterns of uint32)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((max(nblocks, 0), 4), dtype=torch.int32, device=device)
+    st = _lib.lib().dpfused_philox4x32_10(int(seed), int(offset), int(nblocks), out.data_ptr(),
+                                          _stream(out, stream))
+    _lib.check(st)
+    return out
+
+
+def gaussian_fill(seed: int, offset: int, n: int, scale: float = 1.0, dtype=None, out=None,
+                  device="cuda", stream=None):
+    """scale * xi_e for e < n, as float32 or bfloat16 (rounded from the fp32 product)."""
+    torch = _torch()
+    dtype = torch.float32 if dtype is None else dtype
+    if out is None:
+        out = torch.empty((max(n, 0),), dtype=dtype, device=device)
+    st = _lib.lib().dpfused_gaussian_fill(int(seed), int(offset), int(n), float(scale),
+                                          _dtype_code(out), out.data_ptr(), _stream(out, stream))
+    _lib.check(st)
+    return out
+
+
+def noise_blocks(n_elements: int) -> int:
+    return int(_lib.lib().dpfused_noise_blocks(int(n_elements)))
+
+
+def set_option(name: str, value: int) -> None:
+    _lib.check(_lib.lib().dpfused_set_option(name.encode(), int(value)))
+
+
+def get_option(name: str) -> int:
+    return int(_lib.lib().dpfused_get_option(name.encode()))
+
+
+def timing_reset() -> None:
+    _lib.lib().dpfused_timing_reset()
+
+
+def timing_collect() -> dict:
+    """{kernel name: (total ms, launches)} of the event pairs recorded since the last reset."""
+    L = _lib.lib()
+    n = L.dpfused_timing_collect()
+    return {L.dpfused_timing_name(k).decode(): (L.dpfused_timing_total_ms(k),
+                                                 int(L.dpfused_timing_launches(k)))
+            for k in range(n)}

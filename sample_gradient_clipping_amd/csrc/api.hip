@@ -1,0 +1,488 @@
+// C ABI of libdpfused: argument checks, path choice, workspace, launches.
+//
+// Every entry point validates all of its arguments before queueing anything:
+// a failed check launches nothing and writes nothing.  Workspace (per-sample
+// norm partials, clip factors, mask tile flags, the projected activations) is
+// allocated with hipMallocAsync and released with hipFreeAsync on the call's
+// stream, so calls on different streams do not share state.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dpfused.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_norm_path{0};   // 0 auto, 1 gram, 2 direct
+std::atomic<int> g_timing{0};
+
+dpf_status fail(dpf_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+dpf_status ok() {
+  g_last_error.clear();
+  return DPF_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == DPF_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Timing registry
+// ---------------------------------------------------------------------------
+struct Pending {
+  std::string name;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+struct Total {
+  std::string name;
+  double ms = 0.0;
+  int64_t n = 0;
+};
+std::mutex g_tmu;
+std::vector<Pending> g_pending;
+std::vector<Total> g_totals;
+
+// ---------------------------------------------------------------------------
+// Argument checks
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+dpf_status check_act(const dpf_act* a, const char* name) {
+  if (a == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+  if (a->data == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, std::string(name) + ".data is NULL");
+  if (a->dtype != DPF_F32 && a->dtype != DPF_BF16)
+    return fail(DPF_ERR_UNSUPPORTED, std::string(name) + ".dtype is not DPF_F32 or DPF_BF16");
+  if (a->reserved != 0) return fail(DPF_ERR_UNSUPPORTED, std::string(name) + ".reserved must be 0");
+  if (a->B < 1 || a->T < 1 || a->D < 1)
+    return fail(DPF_ERR_INVALID_ARGUMENT, std::string(name) + ": B, T and D must be >= 1");
+  if (a->B > kMaxDim || a->T > kMaxDim || a->D > kMaxDim || a->B * a->T > ((int64_t)1 << 40))
+    return fail(DPF_ERR_UNSUPPORTED, std::string(name) + ": dimension too large");
+  if (a->stride_t < a->D)
+    return fail(DPF_ERR_INVALID_ARGUMENT, std::string(name) + ".stride_t < D (rows overlap)");
+  if (a->stride_b < (a->T - 1) * a->stride_t + a->D)
+    return fail(DPF_ERR_INVALID_ARGUMENT, std::string(name) + ".stride_b too small (samples overlap)");
+  if (!aligned16(a->data))
+    return fail(DPF_ERR_UNSUPPORTED, std::string(name) + ".data is not 16-byte aligned");
+  return DPF_OK;
+}
+
+dpf_status check_pair(const dpf_act* X, const dpf_act* G) {
+  dpf_status s = check_act(X, "X");
+  if (s != DPF_OK) return s;
+  s = check_act(G, "G");
+  if (s != DPF_OK) return s;
+  if (X->dtype != G->dtype) return fail(DPF_ERR_UNSUPPORTED, "X and G have different dtypes");
+  if (X->B != G->B || X->T != G->T)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "X and G disagree on B or T");
+  return DPF_OK;
+}
+
+bool vec_ok(const dpf_act* a) {
+  const size_t es = elem_size(a->dtype);
+  return aligned16(a->data) && (a->D * es) % 16 == 0 && (a->stride_t * es) % 16 == 0 &&
+         (a->stride_b * es) % 16 == 0;
+}
+
+dpf::Act to_act(const dpf_act* a) { return dpf::Act{a->data, a->stride_b, a->stride_t}; }
+
+dpf::NormPath choose_path(int64_t T, int64_t din, int64_t dout) {
+  const int forced = g_norm_path.load();
+  if (forced == 1) return dpf::NormPath::kGram;
+  if (forced == 2) return dpf::NormPath::kDirect;
+  // Gram costs T^2 (din + dout) per sample, the direct form 2 T din dout.
+  const double gram = (double)T * (double)T * (double)(din + dout);
+  const double direct = 2.0 * (double)T * (double)din * (double)dout;
+  return gram <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+}
+
+// Stream-ordered workspace carved into 256-byte aligned pieces.
+struct Workspace {
+  hipStream_t s;
+  void* base = nullptr;
+  size_t used = 0, size = 0;
+  explicit Workspace(hipStream_t st) : s(st) {}
+  ~Workspace() {
+    if (base) (void)hipFreeAsync(base, s);
+  }
+  size_t reserve(size_t bytes) {
+    const size_t at = (size + 255) & ~(size_t)255;
+    size = at + bytes;
+    return at;
+  }
+  bool allocate() {
+    if (size == 0) return true;
+    return hipMallocAsync(&base, size, s) == hipSuccess && base != nullptr;
+  }
+  template <class T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+};
+
+dpf_status hip_fail(hipError_t e, const char* where) {
+  return fail(DPF_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// Shared body of the dense and projected calls once X (or Y) is final.
+struct LayerPlan {
+  dpf::LayerArgs args{};
+  dpf::NormPath path = dpf::NormPath::kGram;
+  bool vec = false;
+  int np = 0;
+};
+
+LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
+  LayerPlan L;
+  L.args.X = to_act(X);
+  L.args.G = to_act(G);
+  L.args.dtype = X->dtype;
+  L.args.B = (int)X->B;
+  L.args.T = (int)X->T;
+  L.args.din = (int)X->D;
+  L.args.dout = (int)G->D;
+  L.args.mask = mask;
+  L.args.nflag = (int)((X->T + dpf::kFlagTokens - 1) / dpf::kFlagTokens);
+  L.path = choose_path(X->T, X->D, G->D);
+  L.vec = vec_ok(X) && vec_ok(G);
+  L.np = dpf::norm_partials_per_sample(L.path, L.args.T, L.args.din, L.args.dout);
+  return L;
+}
+
+// Queue flags (if masked) + norm partials.  ws offsets must be allocated.
+hipError_t queue_norm_partials(LayerPlan& L, uint8_t* flags, double* partials, hipStream_t s) {
+  L.args.partials = partials;
+  L.args.tile_flags = nullptr;
+  if (L.args.mask != nullptr) {
+    hipError_t e = dpf::launch_tile_flags(L.args.mask, L.args.B, L.args.T, flags, L.args.nflag, s);
+    if (e != hipSuccess) return e;
+    L.args.tile_flags = flags;
+  }
+  return dpf::launch_norm(L.args, L.path, L.vec, s);
+}
+
+dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
+                       float sigma, uint64_t seed, uint64_t offset, float* grad_out,
+                       float* norms_out, hipStream_t s, Workspace& ws) {
+  LayerPlan L = plan_layer(X, G, mask);
+  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
+  const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr,
+                                     ws.at<double>(off_part), s);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  float* c = ws.at<float>(off_c);
+  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  L.args.c = c;
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  e = dpf::launch_accumulate(L.args, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
+}
+
+dpf_status check_clip(float C, float sigma) {
+  if (!std::isfinite(C) || !(C > 0.0f)) return fail(DPF_ERR_INVALID_ARGUMENT, "C must be finite and > 0");
+  if (!std::isfinite(sigma) || sigma < 0.0f)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "sigma must be finite and >= 0");
+  if (!std::isfinite(sigma * C)) return fail(DPF_ERR_INVALID_ARGUMENT, "sigma * C overflows");
+  return DPF_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Timing hooks used by the launchers
+// ===========================================================================
+namespace dpf {
+void timing_begin(const char* name, hipStream_t s) {
+  if (!g_timing.load()) return;
+  Pending p;
+  p.name = name;
+  if (hipEventCreate(&p.start) != hipSuccess) return;
+  (void)hipEventRecord(p.start, s);
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_pending.push_back(p);
+}
+void timing_end(const char* name, hipStream_t s) {
+  if (!g_timing.load()) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto it = g_pending.rbegin(); it != g_pending.rend(); ++it) {
+    if (it->stop == nullptr && it->name == name) {
+      if (hipEventCreate(&it->stop) == hipSuccess) (void)hipEventRecord(it->stop, s);
+      return;
+    }
+  }
+}
+}  // namespace dpf
+
+// ===========================================================================
+// C entry points
+// ===========================================================================
+extern "C" {
+
+dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                                          float C, float sigma, uint64_t seed, uint64_t offset,
+                                          float* grad_out, float* norms_out, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  return fused_layer(X, G, mask, C, sigma, seed, offset, grad_out, norms_out, s, ws);
+}
+
+dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_act* G,
+                                                    const uint8_t* mask, const void* P, int64_t r,
+                                                    float C, float sigma, uint64_t seed,
+                                                    uint64_t offset, float* grad_out,
+                                                    float* norms_out, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (P == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "P is NULL");
+  if (r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "r must be >= 1");
+  if (r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "r too large");
+  if (!aligned16(P)) return fail(DPF_ERR_UNSUPPORTED, "P is not 16-byte aligned");
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t es = elem_size(X->dtype);
+
+  Workspace ws(s);
+  const size_t off_y = ws.reserve((size_t)X->B * X->T * r * es);
+  // Reserve the layer workspace now so that a single allocation covers both.
+  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
+  LayerPlan L = plan_layer(&Y, G, mask);
+  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
+  const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  Y.data = ws.at<void>(off_y);
+
+  dpf::ProjArgs pa{};
+  pa.X = to_act(X);
+  pa.P = P;
+  pa.Y = const_cast<void*>(Y.data);
+  pa.dtype = X->dtype;
+  pa.B = (int)X->B;
+  pa.T = (int)X->T;
+  pa.din = (int)X->D;
+  pa.r = (int)r;
+  pa.mask = mask;
+  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
+  hipError_t e = dpf::launch_project(pa, pvec, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+
+  L = plan_layer(&Y, G, mask);
+  e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr, ws.at<double>(off_part), s);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  float* c = ws.at<float>(off_c);
+  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  L.args.c = c;
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  e = dpf::launch_accumulate(L.args, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
+}
+
+dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                                      double* sqnorms_out, int32_t accumulate, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if (sqnorms_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms_out is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  LayerPlan L = plan_layer(X, G, mask);
+  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr,
+                                     ws.at<double>(off_part), s);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sqnorms_out, accumulate ? 1 : 0, 1.0f,
+                           nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  return ok();
+}
+
+dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float* c_out,
+                                float* norms_out, void* stream) {
+  if (sqnorms == nullptr || c_out == nullptr)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms and c_out must not be NULL");
+  if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
+  if (!std::isfinite(C) || !(C > 0.0f)) return fail(DPF_ERR_INVALID_ARGUMENT, "C must be finite and > 0");
+  hipError_t e = dpf::launch_clip_from_sq(sqnorms, n, C, c_out, norms_out,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "clip factor launch");
+  return ok();
+}
+
+dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                                     const float* c, float noise_std, uint64_t seed,
+                                     uint64_t offset, float* grad_out, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if (c == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "c is NULL");
+  if (!std::isfinite(noise_std) || noise_std < 0.0f)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "noise_std must be finite and >= 0");
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  LayerPlan L = plan_layer(X, G, mask);
+  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  if (mask) {
+    hipError_t e = dpf::launch_tile_flags(mask, L.args.B, L.args.T, ws.at<uint8_t>(off_flags),
+                                          L.args.nflag, s);
+    if (e != hipSuccess) return hip_fail(e, "tile flag launch");
+    L.args.tile_flags = ws.at<uint8_t>(off_flags);
+  }
+  L.args.c = c;
+  L.args.noise_std = noise_std;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  hipError_t e = dpf::launch_accumulate(L.args, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
+}
+
+dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
+                                 void* stream) {
+  if (nblocks < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "nblocks must be >= 0");
+  if (nblocks == 0) return ok();
+  if (out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned16(out)) return fail(DPF_ERR_UNSUPPORTED, "out is not 16-byte aligned");
+  hipError_t e = dpf::launch_philox_fill(seed, offset, nblocks, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "philox launch");
+  return ok();
+}
+
+dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale,
+                                 int32_t dtype, void* out, void* stream) {
+  if (n < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (dtype != DPF_F32 && dtype != DPF_BF16) return fail(DPF_ERR_UNSUPPORTED, "unknown dtype");
+  if (!std::isfinite(scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (n == 0) return ok();
+  if (out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned16(out)) return fail(DPF_ERR_UNSUPPORTED, "out is not 16-byte aligned");
+  hipError_t e = dpf::launch_gaussian_fill(seed, offset, n, scale, dtype, out,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gaussian fill launch");
+  return ok();
+}
+
+uint64_t dpfused_noise_blocks(int64_t n_elements) {
+  return n_elements <= 0 ? 0 : ((uint64_t)n_elements + 3) / 4;
+}
+
+dpf_status dpfused_set_option(const char* name, int64_t value) {
+  if (name == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "option name is NULL");
+  if (std::strcmp(name, "norm_path") == 0) {
+    if (value < 0 || value > 2) return fail(DPF_ERR_INVALID_ARGUMENT, "norm_path must be 0, 1 or 2");
+    g_norm_path.store((int)value);
+    return ok();
+  }
+  if (std::strcmp(name, "timing") == 0) {
+    if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "timing must be 0 or 1");
+    g_timing.store((int)value);
+    return ok();
+  }
+  return fail(DPF_ERR_INVALID_ARGUMENT, std::string("unknown option ") + name);
+}
+
+int64_t dpfused_get_option(const char* name) {
+  if (name == nullptr) return -1;
+  if (std::strcmp(name, "norm_path") == 0) return g_norm_path.load();
+  if (std::strcmp(name, "timing") == 0) return g_timing.load();
+  return -1;
+}
+
+void dpfused_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& p : g_pending) {
+    if (p.start) (void)hipEventDestroy(p.start);
+    if (p.stop) (void)hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+  g_totals.clear();
+}
+
+int32_t dpfused_timing_collect(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& p : g_pending) {
+    float ms = 0.f;
+    if (p.start && p.stop && hipEventSynchronize(p.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+      Total* t = nullptr;
+      for (auto& x : g_totals)
+        if (x.name == p.name) t = &x;
+      if (t == nullptr) {
+        g_totals.push_back(Total{p.name, 0.0, 0});
+        t = &g_totals.back();
+      }
+      t->ms += ms;
+      t->n += 1;
+    }
+    if (p.start) (void)hipEventDestroy(p.start);
+    if (p.stop) (void)hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+  return (int32_t)g_totals.size();
+}
+
+const char* dpfused_timing_name(int32_t k) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (k < 0 || k >= (int32_t)g_totals.size()) return "";
+  return g_totals[k].name.c_str();
+}
+
+double dpfused_timing_total_ms(int32_t k) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (k < 0 || k >= (int32_t)g_totals.size()) return 0.0;
+  return g_totals[k].ms;
+}
+
+int64_t dpfused_timing_launches(int32_t k) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (k < 0 || k >= (int32_t)g_totals.size()) return 0;
+  return g_totals[k].n;
+}
+
+const char* dpfused_status_string(dpf_status s) {
+  switch (s) {
+    case DPF_OK: return "DPF_OK";
+    case DPF_ERR_INVALID_ARGUMENT: return "DPF_ERR_INVALID_ARGUMENT";
+    case DPF_ERR_UNSUPPORTED: return "DPF_ERR_UNSUPPORTED";
+    case DPF_ERR_OUT_OF_MEMORY: return "DPF_ERR_OUT_OF_MEMORY";
+    case DPF_ERR_HIP: return "DPF_ERR_HIP";
+  }
+  return "DPF_UNKNOWN_STATUS";
+}
+
+const char* dpfused_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dpfused_abi_version(void) { return DPFUSED_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,564 @@
+// GEMM-shaped kernels of the per-layer DP step.
+//
+//  accumulate_kernel : grad = (sum_i c_i G~_i^T X~_i + noise_std * xi) / B
+//                      One GEMM whose K runs over every active token of every
+//                      sample; the clip factor is applied to the accumulator
+//                      at each sample boundary, so no per-sample gradient is
+//                      stored (FlashDP abstract: gradients computed once,
+//                      fused, per layer).
+//  direct_norm_kernel: per (output tile, sample) sum of squares of the tile of
+//                      g_i = G~_i^T X~_i, computed and dropped in registers.
+//  gram_norm_kernel  : per (sample, upper-triangular token-tile pair) partial
+//                      of <X~X~^T, G~G~^T> (the Gram form of ||g_i||^2).
+//  project_kernel    : Y = X~ P for the projected variant (DP-GRAPE explainer,
+//                      Methodology: project before clipping and noise).
+//
+// All four: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 2 x 2
+// blocks of 32 x 32 accumulators (a 128 x 128 workgroup tile), LDS double
+// buffered along K.  Partial results leave as fp64 per workgroup and are
+// summed in index order by finalize_kernel, so every reduction is fixed-order.
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace dpf {
+
+constexpr int kNT = 256;          // threads per workgroup
+constexpr int kWM = 2, kWN = 2;   // waves along the two tile dims
+constexpr int kBM = 2, kBN = 2;   // 32x32 blocks per wave along each dim
+constexpr int kTileM = kWM * kBM * 32;
+constexpr int kTileN = kWN * kBN * 32;
+
+template <class E> struct Cfg;
+template <> struct Cfg<BF16> { static constexpr int KT = 64; static constexpr int PAD = 16; };
+template <> struct Cfg<F32>  { static constexpr int KT = 32; static constexpr int PAD = 4; };
+
+// ===========================================================================
+// K-outer x K-outer main loop over a list of (sample, token-tile) steps.
+// MFMA operand "A" = X (rows along din), "B" = G (rows along dout), so the
+// accumulator block D[a][o] gives each lane 4 consecutive din columns of one
+// output row: one Philox block per lane-group and 16-byte stores.
+// ===========================================================================
+template <class E, bool VEC>
+struct KOuterGemm {
+  using S = typename E::storage;
+  static constexpr int KT = Cfg<E>::KT;
+  static constexpr int LDA = kTileM + Cfg<E>::PAD;
+  static constexpr int LDB = kTileN + Cfg<E>::PAD;
+  static constexpr int A_ELEMS = KT * LDA, B_ELEMS = KT * LDB;
+  static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * (int)sizeof(S);
+
+  f32x16 acc[kBM][kBN];
+  KOuterLoader<E, kTileM, KT, kNT, VEC> la;
+  KOuterLoader<E, kTileN, KT, kNT, VEC> lb;
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kBM; ++i)
+#pragma unroll
+      for (int j = 0; j < kBN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+
+  __device__ __forceinline__ void scale(float s) {
+#pragma unroll
+    for (int i = 0; i < kBM; ++i)
+#pragma unroll
+      for (int j = 0; j < kBN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= s;
+  }
+
+  __device__ __forceinline__ void fetch(const LayerArgs& p, int b, int kt, int a0, int o0) {
+    const S* xb = (const S*)p.X.data + (int64_t)b * p.X.stride_b;
+    const S* gb = (const S*)p.G.data + (int64_t)b * p.G.stride_b;
+    const uint8_t* mb = p.mask ? p.mask + (int64_t)b * p.T : nullptr;
+    la.load(xb, p.X.stride_t, p.T, mb, kt * KT, a0, p.din);
+    lb.load(gb, p.G.stride_t, p.T, mb, kt * KT, o0, p.dout);
+  }
+
+  __device__ __forceinline__ void stash(S* lds) const {
+    la.template store<LDA>(lds);
+    lb.template store<LDB>(lds + A_ELEMS);
+  }
+
+  __device__ __forceinline__ void compute(const S* lds) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / kWN, wn = wave % kWN;
+    const S* As = lds;
+    const S* Bs = lds + A_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < KT / E::kMfmaK; ++ks) {
+      typename Frag<E>::type fa[kBM], fb[kBN];
+#pragma unroll
+      for (int i = 0; i < kBM; ++i) fa[i] = frag_kouter<E, LDA>(As, (wm * kBM + i) * 32, ks);
+#pragma unroll
+      for (int j = 0; j < kBN; ++j) fb[j] = frag_kouter<E, LDB>(Bs, (wn * kBN + j) * 32, ks);
+#pragma unroll
+      for (int i = 0; i < kBM; ++i)
+#pragma unroll
+        for (int j = 0; j < kBN; ++j) acc[i][j] = mfma<E>(fa[i], fb[j], acc[i][j]);
+    }
+  }
+};
+
+// Step cursor over (sample, token tile) pairs in [b_begin, b_end), skipping
+// token tiles with no active row when per-tile flags are given.
+struct StepCursor {
+  int b, kt, b_end, nkt;
+  const uint8_t* flags;   // [B][nflag] or null (one flag per kFlagTokens tokens)
+  int nflag, kt_tokens;
+  __device__ __forceinline__ bool valid() const { return b < b_end; }
+  __device__ __forceinline__ bool active() const {
+    return flags == nullptr || flags[(int64_t)b * nflag + (kt * kt_tokens) / kFlagTokens] != 0;
+  }
+  __device__ __forceinline__ void skip_inactive() {
+    while (b < b_end && !active()) {
+      if (++kt == nkt) { kt = 0; ++b; }
+    }
+  }
+  __device__ __forceinline__ void advance() {
+    if (++kt == nkt) { kt = 0; ++b; }
+    skip_inactive();
+  }
+};
+
+template <class E, bool VEC, bool NORM>
+__device__ __forceinline__ void kouter_run(const LayerArgs& p, int b_begin, int b_end, int a0,
+                                           int o0, KOuterGemm<E, VEC>& g,
+                                           typename E::storage* lds, float* c_last) {
+  using S = typename E::storage;
+  using KG = KOuterGemm<E, VEC>;
+  const int nkt = (p.T + KG::KT - 1) / KG::KT;
+  static_assert(KG::KT <= kFlagTokens && kFlagTokens % KG::KT == 0, "flag granularity");
+  StepCursor cur{b_begin, 0, b_end, nkt, p.tile_flags, p.nflag, KG::KT};
+  cur.skip_inactive();
+  g.zero();
+  *c_last = 1.0f;
+  if (!cur.valid()) return;
+  int cur_b = cur.b;
+  if constexpr (!NORM) *c_last = p.c[cur_b];
+  g.fetch(p, cur.b, cur.kt, a0, o0);
+  g.stash(lds);
+  __syncthreads();
+  int buf = 0;
+  while (true) {
+    StepCursor nxt = cur;
+    nxt.advance();
+    if (nxt.valid()) g.fetch(p, nxt.b, nxt.kt, a0, o0);
+    g.compute(lds + buf * (KG::A_ELEMS + KG::B_ELEMS));
+    if (!nxt.valid()) break;
+    if constexpr (!NORM) {
+      if (nxt.b != cur_b) {
+        // acc holds sum_{j<=cur} (c_j / c_cur) g_j; re-express it in units
+        // of the next sample's factor before that sample's tiles are added.
+        const float c_next = p.c[nxt.b];
+        g.scale(*c_last / c_next);
+        *c_last = c_next;
+        cur_b = nxt.b;
+      }
+    }
+    g.stash(lds + (buf ^ 1) * (KG::A_ELEMS + KG::B_ELEMS));
+    __syncthreads();
+    buf ^= 1;
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ void __launch_bounds__(kNT) accumulate_kernel(LayerArgs p) {
+  using KG = KOuterGemm<E, VEC>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto* lds = (typename E::storage*)smem;
+  const int ntm = (p.din + kTileM - 1) / kTileM;
+  const int a0 = (blockIdx.x % ntm) * kTileM;
+  const int o0 = (blockIdx.x / ntm) * kTileN;
+  KG g;
+  float c_last;
+  kouter_run<E, VEC, false>(p, 0, p.B, a0, o0, g, lds, &c_last);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const float inv_scale = c_last;
+  const float fB = (float)p.B;
+  const bool vec_store = (p.din & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < kBM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      const int o = o0 + (wn * kBN + j) * 32 + acc_col(lane);
+      if (o >= p.dout) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = a0 + (wm * kBM + i) * 32 + acc_row(4 * q, lane);   // 4 consecutive a
+        if (a >= p.din) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = g.acc[i][j][4 * q + e] * inv_scale;
+        const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
+        if (p.noise_std != 0.0f) {
+          if (vec_store) {
+            const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
+            v[0] += p.noise_std * z.x; v[1] += p.noise_std * z.y;
+            v[2] += p.noise_std * z.z; v[3] += p.noise_std * z.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (a + e < p.din) v[e] += p.noise_std * normal_at(p.seed, p.offset, e0 + e);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v[e] / fB;
+        float* dst = p.out + e0;
+        if (vec_store) {
+          f32x4 w; w.x = v[0]; w.y = v[1]; w.z = v[2]; w.w = v[3];
+          *(f32x4*)dst = w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) if (a + e < p.din) dst[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ void __launch_bounds__(kNT) direct_norm_kernel(LayerArgs p) {
+  using KG = KOuterGemm<E, VEC>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto* lds = (typename E::storage*)smem;
+  __shared__ double red[kNT / 64];
+  const int ntm = (p.din + kTileM - 1) / kTileM;
+  const int ntiles = ntm * ((p.dout + kTileN - 1) / kTileN);
+  const int tile = blockIdx.x;
+  const int b = blockIdx.y;
+  const int a0 = (tile % ntm) * kTileM;
+  const int o0 = (tile / ntm) * kTileN;
+  KG g;
+  float unused;
+  kouter_run<E, VEC, true>(p, b, b + 1, a0, o0, g, lds, &unused);
+  // Out-of-range rows/columns loaded as zero, so their accumulators are 0.
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kBM; ++i)
+#pragma unroll
+    for (int j = 0; j < kBN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += g.acc[i][j][r] * g.acc[i][j][r];
+  const double tot = block_sum_f64((double)s, red);
+  if (threadIdx.x == 0) p.partials[(int64_t)b * ntiles + tile] = tot;
+}
+
+// ===========================================================================
+// Gram form of the per-sample norm:
+//   ||G~^T X~||^2 = sum_{s,t} (X~X~^T)[s,t] (G~G~^T)[s,t]
+// One workgroup per (sample, token-tile pair (S <= T)): the two 128 x 128
+// Gram tiles are accumulated one after the other (K = din, then K = dout)
+// and multiplied elementwise in registers; off-diagonal pairs count twice.
+// ===========================================================================
+template <class E, bool VEC>
+struct GramTile {
+  using S = typename E::storage;
+  static constexpr int KT = Cfg<E>::KT;
+  static constexpr int LD = KT + (sizeof(S) == 2 ? 8 : 4);
+  static constexpr int ELEMS = kTileM * LD;         // one operand tile
+  static constexpr int LDS_BYTES = 2 * 2 * ELEMS * (int)sizeof(S);
+  KInnerLoader<E, kTileM, KT, kNT, VEC> ls, lt;
+
+  __device__ __forceinline__ void run(const Act& A, int K, const LayerArgs& p, int b, int s0,
+                                      int t0, S* lds, f32x16 (&acc)[kBM][kBN]) {
+#pragma unroll
+    for (int i = 0; i < kBM; ++i)
+#pragma unroll
+      for (int j = 0; j < kBN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const S* base = (const S*)A.data + (int64_t)b * A.stride_b;
+    const uint8_t* mb = p.mask ? p.mask + (int64_t)b * p.T : nullptr;
+    const int nk = (K + KT - 1) / KT;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / kWN, wn = wave % kWN;
+    ls.load(base, A.stride_t, p.T, mb, s0, 0, K);
+    lt.load(base, A.stride_t, p.T, mb, t0, 0, K);
+    ls.template store<LD>(lds);
+    lt.template store<LD>(lds + ELEMS);
+    __syncthreads();
+    int buf = 0;
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool more = kk + 1 < nk;
+      if (more) {
+        ls.load(base, A.stride_t, p.T, mb, s0, (kk + 1) * KT, K);
+        lt.load(base, A.stride_t, p.T, mb, t0, (kk + 1) * KT, K);
+      }
+      const S* Ss = lds + buf * 2 * ELEMS;
+      const S* Ts = Ss + ELEMS;
+#pragma unroll
+      for (int ks = 0; ks < KT / E::kMfmaK; ++ks) {
+        typename Frag<E>::type fa[kBM], fb[kBN];
+#pragma unroll
+        for (int i = 0; i < kBM; ++i) fa[i] = frag_kinner<E, LD>(Ss, (wm * kBM + i) * 32, ks);
+#pragma unroll
+        for (int j = 0; j < kBN; ++j) fb[j] = frag_kinner<E, LD>(Ts, (wn * kBN + j) * 32, ks);
+#pragma unroll
+        for (int i = 0; i < kBM; ++i)
+#pragma unroll
+          for (int j = 0; j < kBN; ++j) acc[i][j] = mfma<E>(fa[i], fb[j], acc[i][j]);
+      }
+      if (!more) break;
+      S* nbuf = lds + (buf ^ 1) * 2 * ELEMS;
+      ls.template store<LD>(nbuf);
+      lt.template store<LD>(nbuf + ELEMS);
+      __syncthreads();
+      buf ^= 1;
+    }
+    __syncthreads();   // LDS is reused by the next phase
+  }
+};
+
+// Pair index p -> (S, T) token-tile indices with S <= T, row-major over S.
+__device__ __forceinline__ void pair_of_index(int pidx, int nt, int* s, int* t) {
+  int row = 0, start = 0;
+  while (pidx >= start + (nt - row)) { start += nt - row; ++row; }
+  *s = row;
+  *t = row + (pidx - start);
+}
+
+template <class E, bool VEC>
+__global__ void __launch_bounds__(kNT) gram_norm_kernel(LayerArgs p) {
+  using GT = GramTile<E, VEC>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto* lds = (typename E::storage*)smem;
+  __shared__ double red[kNT / 64];
+  const int nt = (p.T + kTileM - 1) / kTileM;
+  const int npairs = nt * (nt + 1) / 2;
+  const int pidx = blockIdx.x;
+  const int b = blockIdx.y;
+  int st, tt;
+  pair_of_index(pidx, nt, &st, &tt);
+  // Skip pairs whose token tiles hold no active row (flags are per 64 tokens).
+  bool live = true;
+  if (p.tile_flags != nullptr) {
+    const int fpt = kTileM / 64;
+    bool as = false, at = false;
+    for (int f = 0; f < fpt; ++f) {
+      const int fs = st * fpt + f, ft = tt * fpt + f;
+      if (fs < p.nflag) as |= p.tile_flags[(int64_t)b * p.nflag + fs] != 0;
+      if (ft < p.nflag) at |= p.tile_flags[(int64_t)b * p.nflag + ft] != 0;
+    }
+    live = as && at;
+  }
+  double tot = 0.0;
+  if (live) {
+    GT gt;
+    f32x16 ax[kBM][kBN], ag[kBM][kBN];
+    gt.run(p.X, p.din, p, b, st * kTileM, tt * kTileM, lds, ax);
+    gt.run(p.G, p.dout, p, b, st * kTileM, tt * kTileM, lds, ag);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBM; ++i)
+#pragma unroll
+      for (int j = 0; j < kBN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += ax[i][j][r] * ag[i][j][r];
+    tot = block_sum_f64((double)s, red);
+    if (st != tt) tot *= 2.0;
+  }
+  if (threadIdx.x == 0) p.partials[(int64_t)b * npairs + pidx] = tot;
+}
+
+// ===========================================================================
+// Projection Y = X~ P.  MFMA "A" = P^T (rows along r, K-outer in memory),
+// "B" = X (rows along tokens, K-inner).  Each lane ends with 4 consecutive r
+// of one token.  Y is [B, T, r] contiguous in X's dtype.
+// ===========================================================================
+template <class E, bool VEC>
+__global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
+  using S = typename E::storage;
+  constexpr int KT = Cfg<E>::KT;
+  constexpr int LDP = kTileM + Cfg<E>::PAD;        // P tile [KT][TileM] (r)
+  constexpr int LDX = KT + (sizeof(S) == 2 ? 8 : 4);  // X tile [TileN][KT]
+  constexpr int P_ELEMS = KT * LDP, X_ELEMS = kTileN * LDX;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  S* lds = (S*)smem;
+  const int ntr = (p.r + kTileM - 1) / kTileM;
+  const int j0 = (blockIdx.x % ntr) * kTileM;
+  const int64_t q0 = (int64_t)(blockIdx.x / ntr) * kTileN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / kWN, wn = wave % kWN;
+
+  KOuterLoader<E, kTileM, KT, kNT, VEC> lp;
+  KInnerLoader<E, kTileN, KT, kNT, VEC> lx;
+  f32x16 acc[kBM][kBN];
+#pragma unroll
+  for (int i = 0; i < kBM; ++i)
+#pragma unroll
+    for (int j = 0; j < kBN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const S* P = (const S*)p.P;
+  const S* Xd = (const S*)p.X.data;
+  const int nk = (p.din + KT - 1) / KT;
+  // P rows are "tokens" of the K-outer loader: row k of P, T = din, no mask.
+  lp.load(P, p.r, p.din, nullptr, 0, j0, p.r);
+  lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, 0, p.din);
+  lp.template store<LDP>(lds);
+  lx.template store<LDX>(lds + P_ELEMS);
+  __syncthreads();
+  int buf = 0;
+  for (int kk = 0; kk < nk; ++kk) {
+    const bool more = kk + 1 < nk;
+    if (more) {
+      lp.load(P, p.r, p.din, nullptr, (kk + 1) * KT, j0, p.r);
+      lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, (kk + 1) * KT, p.din);
+    }
+    const S* Ps = lds + buf * (P_ELEMS + X_ELEMS);
+    const S* Xs = Ps + P_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < KT / E::kMfmaK; ++ks) {
+      typename Frag<E>::type fa[kBM], fb[kBN];
+#pragma unroll
+      for (int i = 0; i < kBM; ++i) fa[i] = frag_kouter<E, LDP>(Ps, (wm * kBM + i) * 32, ks);
+#pragma unroll
+      for (int j = 0; j < kBN; ++j) fb[j] = frag_kinner<E, LDX>(Xs, (wn * kBN + j) * 32, ks);
+#pragma unroll
+      for (int i = 0; i < kBM; ++i)
+#pragma unroll
+        for (int j = 0; j < kBN; ++j) acc[i][j] = mfma<E>(fa[i], fb[j], acc[i][j]);
+    }
+    if (!more) break;
+    S* nb = lds + (buf ^ 1) * (P_ELEMS + X_ELEMS);
+    lp.template store<LDP>(nb);
+    lx.template store<LDX>(nb + P_ELEMS);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  const int64_t ntok = (int64_t)p.B * p.T;
+#pragma unroll
+  for (int i = 0; i < kBM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      const int64_t q = q0 + (wn * kBN + j) * 32 + acc_col(lane);
+      if (q >= ntok) continue;
+      S* yrow = (S*)p.Y + q * p.r;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int jj = j0 + (wm * kBM + i) * 32 + acc_row(4 * g, lane);
+        if (jj >= p.r) continue;
+        if constexpr (sizeof(S) == 2) {
+          u16x4 w;
+          w.s0 = f32_to_bf16_rne(acc[i][j][4 * g + 0]);
+          w.s1 = f32_to_bf16_rne(acc[i][j][4 * g + 1]);
+          w.s2 = f32_to_bf16_rne(acc[i][j][4 * g + 2]);
+          w.s3 = f32_to_bf16_rne(acc[i][j][4 * g + 3]);
+          if ((p.r & 3) == 0) {
+            *(u16x4*)(yrow + jj) = w;
+          } else {
+            const uint16_t ww[4] = {w.s0, w.s1, w.s2, w.s3};
+            for (int e = 0; e < 4; ++e) if (jj + e < p.r) yrow[jj + e] = ww[e];
+          }
+        } else {
+          for (int e = 0; e < 4; ++e) if (jj + e < p.r) yrow[jj + e] = acc[i][j][4 * g + e];
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Host-side launchers
+// ===========================================================================
+namespace {
+// Kernels here use more than the default 64 KiB of dynamic LDS; raise the
+// per-kernel limit once per instantiation.
+template <auto Kernel>
+hipError_t allow_lds(int bytes) {
+  static hipError_t once = hipFuncSetAttribute((const void*)Kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return once;
+}
+
+template <class E, bool VEC>
+hipError_t launch_accumulate_t(const LayerArgs& p, hipStream_t s) {
+  using KG = KOuterGemm<E, VEC>;
+  const int grid = ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
+  hipError_t e = allow_lds<accumulate_kernel<E, VEC>>(KG::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  timing_begin("accumulate", s);
+  hipLaunchKernelGGL((accumulate_kernel<E, VEC>), dim3(grid), dim3(kNT), KG::LDS_BYTES, s, p);
+  e = hipGetLastError();
+  timing_end("accumulate", s);
+  return e;
+}
+template <class E, bool VEC>
+hipError_t launch_direct_t(const LayerArgs& p, hipStream_t s) {
+  using KG = KOuterGemm<E, VEC>;
+  const int grid = ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
+  hipError_t e = allow_lds<direct_norm_kernel<E, VEC>>(KG::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  timing_begin("direct_norm", s);
+  hipLaunchKernelGGL((direct_norm_kernel<E, VEC>), dim3(grid, p.B), dim3(kNT), KG::LDS_BYTES, s, p);
+  e = hipGetLastError();
+  timing_end("direct_norm", s);
+  return e;
+}
+template <class E, bool VEC>
+hipError_t launch_gram_t(const LayerArgs& p, hipStream_t s) {
+  using GT = GramTile<E, VEC>;
+  const int nt = (p.T + kTileM - 1) / kTileM;
+  hipError_t e = allow_lds<gram_norm_kernel<E, VEC>>(GT::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  timing_begin("gram_norm", s);
+  hipLaunchKernelGGL((gram_norm_kernel<E, VEC>), dim3(nt * (nt + 1) / 2, p.B), dim3(kNT),
+                     GT::LDS_BYTES, s, p);
+  e = hipGetLastError();
+  timing_end("gram_norm", s);
+  return e;
+}
+template <class E, bool VEC>
+hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
+  using S = typename E::storage;
+  constexpr int KT = Cfg<E>::KT;
+  constexpr int bytes = 2 * (KT * (kTileM + Cfg<E>::PAD) + kTileN * (KT + (sizeof(S) == 2 ? 8 : 4))) *
+                        (int)sizeof(S);
+  const int64_t ntok = (int64_t)p.B * p.T;
+  const int64_t grid = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
+  hipError_t e = allow_lds<project_kernel<E, VEC>>(bytes);
+  if (e != hipSuccess) return e;
+  timing_begin("project", s);
+  hipLaunchKernelGGL((project_kernel<E, VEC>), dim3((unsigned)grid), dim3(kNT), bytes, s, p);
+  e = hipGetLastError();
+  timing_end("project", s);
+  return e;
+}
+}  // namespace
+
+int norm_partials_per_sample(NormPath path, int T, int din, int dout) {
+  if (path == NormPath::kGram) {
+    const int nt = (T + kTileM - 1) / kTileM;
+    return nt * (nt + 1) / 2;
+  }
+  return ((din + kTileM - 1) / kTileM) * ((dout + kTileN - 1) / kTileN);
+}
+
+hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s) {
+  if (p.dtype == kBF16) return vec ? launch_accumulate_t<BF16, true>(p, s) : launch_accumulate_t<BF16, false>(p, s);
+  return vec ? launch_accumulate_t<F32, true>(p, s) : launch_accumulate_t<F32, false>(p, s);
+}
+hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s) {
+  if (path == NormPath::kGram) {
+    if (p.dtype == kBF16) return vec ? launch_gram_t<BF16, true>(p, s) : launch_gram_t<BF16, false>(p, s);
+    return vec ? launch_gram_t<F32, true>(p, s) : launch_gram_t<F32, false>(p, s);
+  }
+  if (p.dtype == kBF16) return vec ? launch_direct_t<BF16, true>(p, s) : launch_direct_t<BF16, false>(p, s);
+  return vec ? launch_direct_t<F32, true>(p, s) : launch_direct_t<F32, false>(p, s);
+}
+hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s) {
+  if (p.dtype == kBF16) return vec ? launch_project_t<BF16, true>(p, s) : launch_project_t<BF16, false>(p, s);
+  return vec ? launch_project_t<F32, true>(p, s) : launch_project_t<F32, false>(p, s);
+}
+
+}  // namespace dpf

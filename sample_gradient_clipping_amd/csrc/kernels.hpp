@@ -1,0 +1,65 @@
+// Internal (C++) interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dpf {
+
+enum DType { kF32 = 0, kBF16 = 1 };
+enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2 };
+
+// Tokens covered by one entry of the per-sample activity flags.
+constexpr int kFlagTokens = 64;
+
+struct LayerArgs {
+  Act X, G;                 // [B, T, din] and [B, T, dout]
+  int dtype;                // DType
+  int B, T, din, dout;
+  const uint8_t* mask;      // [B, T] or null
+  const uint8_t* tile_flags;// [B, nflag]: any active token in each 64-token tile, or null
+  int nflag;
+  const float* c;           // [B] clip factors (accumulate only)
+  float noise_std;          // sigma * C (0 = no noise)
+  uint64_t seed, offset;
+  float* out;               // [dout, din]
+  double* partials;         // [B, norm_partials_per_sample] (norm kernels)
+};
+
+struct ProjArgs {
+  Act X;                    // [B, T, din]
+  const void* P;            // [din, r]
+  void* Y;                  // [B, T, r] contiguous, X's dtype
+  int dtype;
+  int B, T, din, r;
+  const uint8_t* mask;
+};
+
+// Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the
+// caller has checked alignment of every pointer, dimension and stride.
+hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
+hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
+hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
+int norm_partials_per_sample(NormPath path, int T, int din, int dout);
+
+// Small kernels (misc_kernels.hip).
+hipError_t launch_tile_flags(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag,
+                             hipStream_t s);
+// Per sample: sq = ordered sum of np partials; optionally added into sq_io;
+// then c = clip factor and norms = sqrt(sq) when c_out is given.
+hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,
+                           float C, float* c_out, float* norms_out, hipStream_t s);
+hipError_t launch_clip_from_sq(const double* sq, int64_t n, float C, float* c_out,
+                               float* norms_out, hipStream_t s);
+hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
+                              hipStream_t s);
+hipError_t launch_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale, int dtype,
+                                void* out, hipStream_t s);
+
+// Timing hooks (api.cpp): bracket one kernel launch on `s` when enabled.
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(const char* name, hipStream_t s);
+
+}  // namespace dpf

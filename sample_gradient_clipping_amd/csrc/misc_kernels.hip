@@ -1,0 +1,142 @@
+// Small kernels: Philox/Gaussian fills, mask tile flags, ordered finalize.
+#include "kernels.hpp"
+
+namespace dpf {
+
+// out[4j..4j+3] = Philox4x32-10 words of block offset + j.
+__global__ void philox_fill_kernel(uint64_t seed, uint64_t offset, int64_t nblocks, u32x4* out) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < nblocks) out[j] = philox_block(seed, offset + (uint64_t)j);
+}
+
+// out[e] = scale * xi_e, four elements (one Philox block) per thread.
+__global__ void gaussian_fill_kernel(uint64_t seed, uint64_t offset, int64_t n, float scale,
+                                     int dtype, void* out) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e0 = 4 * j;
+  if (e0 >= n) return;
+  const f32x4 z = normals_of_block(philox_block(seed, offset + (uint64_t)j));
+  const float v[4] = {scale * z.x, scale * z.y, scale * z.z, scale * z.w};
+  if (dtype == kF32) {
+    float* o = (float*)out + e0;
+    if (e0 + 4 <= n) {
+      f32x4 w; w.x = v[0]; w.y = v[1]; w.z = v[2]; w.w = v[3];
+      *(f32x4*)o = w;
+    } else {
+      for (int e = 0; e < 4 && e0 + e < n; ++e) o[e] = v[e];
+    }
+  } else {
+    uint16_t* o = (uint16_t*)out + e0;
+    if (e0 + 4 <= n) {
+      u16x4 w;
+      w.s0 = f32_to_bf16_rne(v[0]); w.s1 = f32_to_bf16_rne(v[1]);
+      w.s2 = f32_to_bf16_rne(v[2]); w.s3 = f32_to_bf16_rne(v[3]);
+      *(u16x4*)o = w;
+    } else {
+      for (int e = 0; e < 4 && e0 + e < n; ++e) o[e] = f32_to_bf16_rne(v[e]);
+    }
+  }
+}
+
+// flags[b, f] = 1 if any of tokens [64 f, 64 f + 64) of sample b is active.
+// One wave per (b, f).
+__global__ void tile_flags_kernel(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag) {
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (int64_t)B * nflag) return;
+  const int b = (int)(w / nflag), f = (int)(w % nflag);
+  const int t = f * kFlagTokens + lane;
+  const bool a = t < T && mask[(int64_t)b * T + t] != 0;
+  const uint64_t any = __ballot(a);
+  if (lane == 0) flags[w] = any != 0 ? 1 : 0;
+}
+
+__device__ __forceinline__ void clip_of_sq(double sq, float C, float* c, float* n) {
+  // Rounding can leave a tiny negative sum when g_i ~ 0; NaN must pass through.
+  const double nn = sqrt(sq < 0.0 ? 0.0 : sq);
+  *n = (float)nn;
+  *c = (nn <= (double)C) ? 1.0f : (float)((double)C / nn);
+}
+
+// One thread per sample; the partials of a sample are summed in index order.
+__global__ void finalize_kernel(const double* partials, int B, int np, double* sq_io,
+                                int accumulate, float C, float* c_out, float* norms_out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const double* row = partials + (int64_t)b * np;
+  double sq = 0.0;
+  for (int i = 0; i < np; ++i) sq += row[i];
+  if (sq_io != nullptr) {
+    if (accumulate) sq += sq_io[b];
+    sq_io[b] = sq;
+  }
+  if (c_out != nullptr) {
+    float c, n;
+    clip_of_sq(sq, C, &c, &n);
+    c_out[b] = c;
+    if (norms_out != nullptr) norms_out[b] = n;
+  }
+}
+
+__global__ void clip_from_sq_kernel(const double* sq, int64_t n, float C, float* c_out,
+                                    float* norms_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float c, nn;
+  clip_of_sq(sq[i], C, &c, &nn);
+  c_out[i] = c;
+  if (norms_out != nullptr) norms_out[i] = nn;
+}
+
+// ---------------------------------------------------------------------------
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
+                              hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  timing_begin("philox_fill", s);
+  hipLaunchKernelGGL(philox_fill_kernel, dim3(blocks_for(nblocks, 256)), dim3(256), 0, s, seed,
+                     offset, nblocks, (u32x4*)out);
+  timing_end("philox_fill", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale, int dtype,
+                                void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  timing_begin("gaussian_fill", s);
+  hipLaunchKernelGGL(gaussian_fill_kernel, dim3(blocks_for((n + 3) / 4, 256)), dim3(256), 0, s,
+                     seed, offset, n, scale, dtype, out);
+  timing_end("gaussian_fill", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_flags(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag,
+                             hipStream_t s) {
+  const int64_t waves = (int64_t)B * nflag;
+  timing_begin("tile_flags", s);
+  hipLaunchKernelGGL(tile_flags_kernel, dim3(blocks_for(waves, 4)), dim3(256), 0, s, mask, B, T,
+                     flags, nflag);
+  timing_end("tile_flags", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,
+                           float C, float* c_out, float* norms_out, hipStream_t s) {
+  timing_begin("finalize", s);
+  hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(B, 64)), dim3(64), 0, s, partials, B, np,
+                     sq_io, accumulate, C, c_out, norms_out);
+  timing_end("finalize", s);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip_from_sq(const double* sq, int64_t n, float C, float* c_out,
+                               float* norms_out, hipStream_t s) {
+  timing_begin("clip_factors", s);
+  hipLaunchKernelGGL(clip_from_sq_kernel, dim3(blocks_for(n, 64)), dim3(64), 0, s, sq, n, C,
+                     c_out, norms_out);
+  timing_end("clip_factors", s);
+  return hipGetLastError();
+}
+
+}  // namespace dpf

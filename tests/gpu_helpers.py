@@ -1,0 +1,69 @@
+"""Helpers for the GPU tests: uploading seeded numpy inputs and comparing with the oracle."""
+import numpy as np
+import pytest
+
+
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sample_gradient_clipping_amd as dp
+    dp.load()   # raises if the HIP library is missing: no fallback
+    return torch
+
+
+def to_dev(a: np.ndarray, dtype: str, torch):
+    """numpy float32 or uint16 (bf16 bits) -> GPU tensor of that dtype (bytes unchanged)."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def mask_dev(mask, torch):
+    return None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).cuda()
+
+
+def rel_fro(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_rel(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)))
+
+
+def run_dense(lin, torch, C=None, sigma=None, path=None, offset=None):
+    import sample_gradient_clipping_amd as dp
+    X = to_dev(lin.X, lin.dtype, torch)
+    G = to_dev(lin.G, lin.dtype, torch)
+    m = mask_dev(lin.mask, torch)
+    if path is not None:
+        dp.set_option("norm_path", path)
+    try:
+        out, norms = dp.linear_clip_accumulate(
+            X, G, m, C=lin.C if C is None else C, sigma=lin.sigma if sigma is None else sigma,
+            seed=lin.seed, offset=lin.offset if offset is None else offset)
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
+    return out.cpu().numpy(), norms.cpu().numpy()
+
+
+def random_linear(rng, B, T, din, dout, dtype="bf16", masked=False, C=1.0, sigma=0.0,
+                  g_scale=1e-2, lengths=None, seed=0, offset=0):
+    """Small seeded case with per-sample lognormal scales (mix of clipped/unclipped)."""
+    from workloads import Linear, f32_to_bf16_bits
+    X = rng.standard_normal((B, T, din), dtype=np.float32)
+    s = rng.lognormal(0.0, 1.0, B).astype(np.float32)
+    G = (rng.standard_normal((B, T, dout), dtype=np.float32) * (s * g_scale)[:, None, None]).astype(np.float32)
+    mask = None
+    if lengths is not None:
+        mask = (np.arange(T)[None, :] < np.asarray(lengths)[:, None]).astype(np.uint8)
+    elif masked:
+        mask = (rng.random((B, T)) < 0.7).astype(np.uint8)
+    if dtype == "bf16":
+        X, G = f32_to_bf16_bits(X), f32_to_bf16_bits(G)
+    return Linear("rand", X, G, mask, C, sigma, seed, offset, dtype)

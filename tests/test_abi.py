@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call is made."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sample_gradient_clipping_amd import _lib
+from sample_gradient_clipping_amd._lib import (DPF_BF16, DPF_ERR_INVALID_ARGUMENT,
+                                               DPF_ERR_UNSUPPORTED, DPF_F32, DPF_OK, DpfAct)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dpfused.h")
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdpfused.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dpfused_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dpfused_linear_clip_accumulate", "dpfused_linear_clip_accumulate_projected",
+                     "dpfused_philox4x32_10", "dpfused_gaussian_fill", "dpfused_noise_blocks",
+                     "dpfused_status_string", "dpfused_last_error", "dpfused_abi_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    assert set(declared_functions()) == set(_lib._SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_strings(L):
+    assert L.dpfused_abi_version() == 1
+    assert L.dpfused_status_string(DPF_OK) == b"DPF_OK"
+    assert L.dpfused_status_string(DPF_ERR_INVALID_ARGUMENT) == b"DPF_ERR_INVALID_ARGUMENT"
+    assert L.dpfused_status_string(99) == b"DPF_UNKNOWN_STATUS"
+
+
+def test_noise_blocks(L):
+    for n, want in [(0, 0), (-5, 0), (1, 1), (4, 1), (5, 2), (70778880, 17694720)]:
+        assert L.dpfused_noise_blocks(n) == want
+
+
+def test_options(L):
+    assert L.dpfused_set_option(b"norm_path", 2) == DPF_OK
+    assert L.dpfused_get_option(b"norm_path") == 2
+    assert L.dpfused_set_option(b"norm_path", 0) == DPF_OK
+    assert L.dpfused_set_option(b"norm_path", 3) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"bogus", 1) == DPF_ERR_INVALID_ARGUMENT
+    assert b"bogus" in L.dpfused_last_error()
+    assert L.dpfused_get_option(b"bogus") == -1
+    assert L.dpfused_set_option(b"timing", 0) == DPF_OK
+
+
+def _act(B=2, T=3, D=8, dtype=DPF_BF16, data=FAKE, reserved=0, sb=None, st=None):
+    st = D if st is None else st
+    sb = T * st if sb is None else sb
+    return DpfAct(data, dtype, reserved, B, T, D, sb, st)
+
+
+def _call(L, X, G, C=1.0, sigma=0.5, out=FAKE, mask=None):
+    return L.dpfused_linear_clip_accumulate(ctypes.byref(X) if X is not None else None,
+                                            ctypes.byref(G) if G is not None else None,
+                                            mask, C, sigma, 0, 0, out, None, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(X=None), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xdata=0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(out=0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xB=0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xT=0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xD=0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(gB=3), DPF_ERR_INVALID_ARGUMENT),
+    (dict(gT=4), DPF_ERR_INVALID_ARGUMENT),
+    (dict(C=0.0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(C=-1.0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(C=math.nan), DPF_ERR_INVALID_ARGUMENT),
+    (dict(C=math.inf), DPF_ERR_INVALID_ARGUMENT),
+    (dict(sigma=-0.1), DPF_ERR_INVALID_ARGUMENT),
+    (dict(sigma=math.nan), DPF_ERR_INVALID_ARGUMENT),
+    (dict(sigma=3e38, C=10.0), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xst=4), DPF_ERR_INVALID_ARGUMENT),
+    (dict(xsb=10), DPF_ERR_INVALID_ARGUMENT),
+    (dict(gdtype=DPF_F32), DPF_ERR_UNSUPPORTED),
+    (dict(xdtype=7, gdtype=7), DPF_ERR_UNSUPPORTED),
+    (dict(xreserved=1), DPF_ERR_UNSUPPORTED),
+    (dict(xdata=FAKE + 2), DPF_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 4), DPF_ERR_UNSUPPORTED),
+])
+def test_dense_argument_checks(L, case, status):
+    X = _act(B=case.get("xB", 2), T=case.get("xT", 3), D=case.get("xD", 8),
+             dtype=case.get("xdtype", DPF_BF16), data=case.get("xdata", FAKE),
+             reserved=case.get("xreserved", 0), sb=case.get("xsb"), st=case.get("xst"))
+    G = _act(B=case.get("gB", 2), T=case.get("gT", 3), D=16, dtype=case.get("gdtype", case.get("xdtype", DPF_BF16)))
+    got = _call(L, None if case.get("X", 1) is None else X, G, C=case.get("C", 1.0),
+                sigma=case.get("sigma", 0.5), out=case.get("out", FAKE))
+    assert got == status, L.dpfused_last_error()
+    assert L.dpfused_last_error() != b""
+
+
+def test_projected_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    f = L.dpfused_linear_clip_accumulate_projected
+    assert f(ctypes.byref(X), ctypes.byref(G), None, None, 4, 1.0, 1.0, 0, 0, FAKE, None, None) \
+        == DPF_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(X), ctypes.byref(G), None, FAKE, 0, 1.0, 1.0, 0, 0, FAKE, None, None) \
+        == DPF_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(X), ctypes.byref(G), None, FAKE + 8, 4, 1.0, 1.0, 0, 0, FAKE, None, None) \
+        == DPF_ERR_UNSUPPORTED
+    assert f(ctypes.byref(X), ctypes.byref(G), None, FAKE, 4, 0.0, 1.0, 0, 0, FAKE, None, None) \
+        == DPF_ERR_INVALID_ARGUMENT
+
+
+def test_building_block_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    assert L.dpfused_per_sample_sqnorms(ctypes.byref(X), ctypes.byref(G), None, None, 0, None) \
+        == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_clip_factors(None, 4, 1.0, FAKE, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_clip_factors(FAKE, 0, 1.0, FAKE, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_clip_factors(FAKE, 4, -1.0, FAKE, None, None) == DPF_ERR_INVALID_ARGUMENT
+    sa = L.dpfused_scaled_accumulate
+    assert sa(ctypes.byref(X), ctypes.byref(G), None, None, 0.0, 0, 0, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+    assert sa(ctypes.byref(X), ctypes.byref(G), None, FAKE, -1.0, 0, 0, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+
+
+def test_rng_argument_checks(L):
+    assert L.dpfused_philox4x32_10(0, 0, 0, None, None) == DPF_OK   # nothing to do
+    assert L.dpfused_philox4x32_10(0, 0, -1, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_philox4x32_10(0, 0, 5, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_philox4x32_10(0, 0, 5, FAKE + 4, None) == DPF_ERR_UNSUPPORTED
+    assert L.dpfused_gaussian_fill(0, 0, 0, 1.0, DPF_F32, None, None) == DPF_OK
+    assert L.dpfused_gaussian_fill(0, 0, -1, 1.0, DPF_F32, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_gaussian_fill(0, 0, 8, 1.0, 9, FAKE, None) == DPF_ERR_UNSUPPORTED
+    assert L.dpfused_gaussian_fill(0, 0, 8, math.inf, DPF_F32, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "sample_gradient_clipping_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,187 @@
+"""GPU invariants of the fused DP step that hold at any size (no oracle needed
+for most), plus the building-block entry points and error handling on the GPU."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dp_linear, philox
+from tests.gpu_helpers import mask_dev, max_rel, need_gpu, random_linear, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(lin, torch):
+    return to_dev(lin.X, lin.dtype, torch), to_dev(lin.G, lin.dtype, torch), mask_dev(lin.mask, torch)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_bitwise_determinism(path):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(20)
+    lin = random_linear(rng, 5, 333, 200, 264, masked=True)
+    X, G, m = _dev(lin, torch)
+    dp.set_option("norm_path", path)
+    try:
+        outs = [dp.linear_clip_accumulate(X, G, m, C=0.1, sigma=0.7, seed=3, offset=11) for _ in range(4)]
+    finally:
+        dp.set_option("norm_path", 0)
+    for o, n in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(n, outs[0][1])
+
+
+def test_masked_rows_never_read():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(21)
+    lin = random_linear(rng, 3, 200, 136, 128, lengths=[200, 77, 3])
+    X, G, m = _dev(lin, torch)
+    ref = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.5)
+    X2, G2 = X.clone(), G.clone()
+    pad = (m == 0)
+    X2[pad] = float("nan")
+    G2[pad] = float("inf")
+    got = dp.linear_clip_accumulate(X2, G2, m, C=0.05, sigma=0.5)
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+
+
+def test_active_nan_propagates():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(22)
+    lin = random_linear(rng, 2, 40, 64, 32)
+    X, G, _ = _dev(lin, torch)
+    X[1, 5, 7] = float("nan")
+    out, norms = dp.linear_clip_accumulate(X, G, None, C=1.0, sigma=0.0)
+    assert torch.isnan(norms[1]) and not torch.isnan(norms[0])
+    assert torch.isnan(out).any()
+
+
+def test_zero_activations_give_pure_noise():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout = 3, 50, 72, 40
+    X = torch.zeros((B, T, din), dtype=torch.bfloat16, device="cuda")
+    G = torch.randn((B, T, dout), device="cuda").to(torch.bfloat16)
+    sigma, C, seed, off = 1.3, 0.4, 77, 1234
+    out, norms = dp.linear_clip_accumulate(X, G, None, C=C, sigma=sigma, seed=seed, offset=off)
+    assert torch.all(norms == 0)
+    xi = philox.gaussian(seed, off, din * dout).reshape(dout, din)
+    assert np.max(np.abs(out.cpu().numpy() - sigma * C * xi / B)) <= 1e-5 * sigma * C
+
+
+@pytest.mark.parametrize("C", [1e-3, 1e3])
+def test_single_sample_clipped_norm(C):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(23)
+    lin = random_linear(rng, 1, 300, 200, 136)
+    X, G, _ = _dev(lin, torch)
+    out, norms = dp.linear_clip_accumulate(X, G, None, C=C, sigma=0.0)
+    n = float(norms[0])
+    assert abs(float(torch.linalg.norm(out.double())) - min(n, C)) <= 1e-5 * min(n, C)
+
+
+def test_unclipped_noiseless_is_plain_gemm():
+    """C huge, sigma = 0: out = G~^T X~ / B, compared with an fp32 GEMM in torch."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(24)
+    lin = random_linear(rng, 4, 257, 300, 136, lengths=[257, 100, 0, 31])
+    X, G, m = _dev(lin, torch)
+    out, _ = dp.linear_clip_accumulate(X, G, m, C=1e30, sigma=0.0)
+    keep = m.reshape(-1).bool()
+    Xf = X.reshape(-1, 300).float()[keep]
+    Gf = G.reshape(-1, 136).float()[keep]
+    ref = (Gf.t().contiguous() @ Xf) / 4
+    assert rel_fro(out.cpu().numpy(), ref.cpu().numpy()) <= 1e-5
+
+
+def test_scale_invariance_of_clipped_sample():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(25)
+    lin = random_linear(rng, 3, 90, 128, 64)
+    X, G, _ = _dev(lin, torch)
+    o1, n1 = dp.linear_clip_accumulate(X, G, None, C=1e-4, sigma=0.0)
+    G2 = G.clone()
+    G2[1] *= 8.0
+    o2, n2 = dp.linear_clip_accumulate(X, G2, None, C=1e-4, sigma=0.0)
+    assert abs(float(n2[1]) / float(n1[1]) - 8.0) < 1e-5
+    assert rel_fro(o2.cpu().numpy(), o1.cpu().numpy()) <= 1e-5
+
+
+def test_gram_and_direct_paths_agree():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(26)
+    lin = random_linear(rng, 4, 384, 256, 384, masked=True)
+    X, G, m = _dev(lin, torch)
+    res = {}
+    for path in (1, 2):
+        dp.set_option("norm_path", path)
+        try:
+            res[path] = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.0)
+        finally:
+            dp.set_option("norm_path", 0)
+    assert max_rel(res[1][1].cpu().numpy(), res[2][1].cpu().numpy()) <= 1e-4
+    assert rel_fro(res[1][0].cpu().numpy(), res[2][0].cpu().numpy()) <= 1e-4
+
+
+def test_sqnorms_accumulate_and_scaled_accumulate_compose():
+    """Building blocks reproduce the fused call and sum squared norms across linears."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(27)
+    a = random_linear(rng, 3, 100, 64, 136, masked=True)
+    b = random_linear(rng, 3, 100, 200, 72)
+    b.mask = a.mask
+    Xa, Ga, m = _dev(a, torch)
+    Xb, Gb, _ = _dev(b, torch)
+    sq = dp.per_sample_sqnorms(Xa, Ga, m)
+    sq_b = dp.per_sample_sqnorms(Xb, Gb, m)
+    tot = sq.clone()
+    dp.per_sample_sqnorms(Xb, Gb, m, out=tot, accumulate=True)
+    assert torch.allclose(tot, sq + sq_b, rtol=1e-14, atol=0)
+    _, ra, _ = dp_linear.oracle_linear(a.X, a.G, a.mask, 1.0, 0.0, 0, 0, "bf16")
+    assert max_rel(np.sqrt(sq.cpu().numpy()), ra) <= 1e-3
+    C = 0.05
+    c, norms = dp.clip_factors(sq, C, norms_out=torch.empty(3, device="cuda"))
+    fused, fnorms = dp.linear_clip_accumulate(Xa, Ga, m, C=C, sigma=0.8, seed=4, offset=9)
+    # the fused call forms sigma * C in float32
+    built = dp.scaled_accumulate(Xa, Ga, c, m, noise_std=float(np.float32(0.8) * np.float32(C)),
+                                 seed=4, offset=9)
+    assert torch.equal(fused, built)
+    assert torch.equal(fnorms, norms)
+
+
+def test_binding_raises_on_bad_arguments():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    X = torch.zeros((2, 3, 8), dtype=torch.bfloat16, device="cuda")
+    G = torch.zeros((2, 4, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dp.DpfError):
+        dp.linear_clip_accumulate(X, G, None, C=1.0)
+    with pytest.raises(dp.DpfError):
+        dp.linear_clip_accumulate(X, X, None, C=-1.0)
+    with pytest.raises(dp.DpfError):
+        dp.linear_clip_accumulate(X, X.float(), None, C=1.0)
+
+
+def test_kernel_timing_records_launches():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    X = torch.randn((2, 64, 128), device="cuda").to(torch.bfloat16)
+    G = torch.randn((2, 64, 128), device="cuda").to(torch.bfloat16)
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        for _ in range(3):
+            dp.linear_clip_accumulate(X, G, None, C=1.0, sigma=1.0)
+        t = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    assert t["accumulate"][1] == 3 and t["accumulate"][0] > 0
+    assert t["gram_norm"][1] == 3 and t["finalize"][1] == 3

@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Tolerances (stated for the method: per-sample norms within 1e-3 relative;
+the aggregated noisy gradient within 2e-2 relative Frobenius error for bf16
+inputs with fp32 accumulation).  Derived, tighter bounds used in addition:
+  * fp32 inputs: aggregate within 1e-4 relative Frobenius (fp32 MFMA, K small);
+  * sigma = 0 companions (the clipped sum alone, which the noise would
+    otherwise swamp): 1e-3 for bf16 -- the bf16 inputs are exact in the
+    oracle, so only fp32 accumulation order differs (error ~1e-6);
+  * projected variant: the GPU rounds Y = X P to bf16, adding ~2^-9 relative
+    error per Y entry, so its sigma = 0 companion is held to 1e-2.
+Shapes here are small enough for the oracle to finish in seconds but span
+several 128-wide tiles in every dimension and end in ragged tails.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import dp_linear
+from tests.gpu_helpers import (mask_dev, max_rel, need_gpu, random_linear, rel_fro, run_dense,
+                               to_dev)
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 1e-3
+AGG_TOL_BF16 = 2e-2
+AGG_TOL_F32 = 1e-4
+SUM_TOL_BF16 = 1e-3
+
+
+def _oracle(lin, C=None, sigma=None, offset=None):
+    return dp_linear.oracle_linear(lin.X, lin.G, lin.mask, lin.C if C is None else C,
+                                   lin.sigma if sigma is None else sigma, lin.seed,
+                                   lin.offset if offset is None else offset, lin.dtype)
+
+
+def _check(lin, path, sigma, C=None, agg_tol=None):
+    torch = need_gpu()
+    out, norms = run_dense(lin, torch, C=C, sigma=sigma, path=path)
+    ref, rnorms, _ = _oracle(lin, C=C, sigma=sigma)
+    assert max_rel(norms, rnorms) <= NORM_TOL, (max_rel(norms, rnorms), norms, rnorms)
+    tol = agg_tol if agg_tol is not None else (AGG_TOL_F32 if lin.dtype == "f32" else AGG_TOL_BF16)
+    err = rel_fro(out, ref)
+    assert err <= tol, err
+    return out, norms, ref, rnorms
+
+
+# ---------------------------------------------------------------------------
+# small multi-tile shapes with ragged tails, both norm paths, both dtypes
+# ---------------------------------------------------------------------------
+SHAPES = [
+    (3, 200, 264, 136),     # 2 token tiles (128 + 72), 3 x 2 output tiles with tails
+    (2, 130, 128, 256),     # exact tile widths, a 2-token tail
+    (1, 1, 8, 8),           # T = 1 outer product
+    (4, 16, 64, 32),        # the single-linear fp32 configuration's shape
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_dense_small_mixed_clip(dtype, path, shape):
+    B, T, din, dout = shape
+    rng = np.random.default_rng(hash((B, T, din, dout)) % 2**32)
+    lin = random_linear(rng, B, T, din, dout, dtype=dtype)
+    # clip norm at the median norm: some samples clip, some do not
+    _, rnorms, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rnorms)) * 1.0001 if B > 1 else float(rnorms[0]) * 0.5
+    tol = AGG_TOL_F32 if dtype == "f32" else SUM_TOL_BF16
+    _check(lin, path, sigma=0.0, C=C, agg_tol=tol)
+    _check(lin, path, sigma=0.9, C=C)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("path", [1, 2])
+def test_dense_odd_dims_scalar_loads(dtype, path):
+    rng = np.random.default_rng(5)
+    lin = random_linear(rng, 3, 45, 37, 19, dtype=dtype, masked=True)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn))
+    _check(lin, path, sigma=0.0, C=C, agg_tol=AGG_TOL_F32 if dtype == "f32" else SUM_TOL_BF16)
+    _check(lin, path, sigma=1.3, C=C)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_dense_ragged_prefix_masks(path):
+    rng = np.random.default_rng(6)
+    lengths = [300, 0, 1, 129, 64, 65]
+    lin = random_linear(rng, 6, 300, 192, 320, lengths=lengths)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    assert rn[1] == 0.0
+    C = float(np.median(rn[rn > 0]))
+    out, norms, _, _ = _check(lin, path, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+    assert norms[1] == 0.0
+    _check(lin, path, sigma=1.2, C=C)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_dense_random_mask(path):
+    rng = np.random.default_rng(7)
+    lin = random_linear(rng, 4, 257, 136, 72, masked=True)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    _check(lin, path, sigma=0.0, C=float(np.median(rn)), agg_tol=SUM_TOL_BF16)
+
+
+def test_strided_views():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(8)
+    lin = random_linear(rng, 3, 70, 96, 40, dtype="bf16")
+    Xb = np.zeros((3, 70, 96 + 24), np.uint16)
+    Xb[:, :, :96] = lin.X
+    Gb = np.zeros((3, 70 + 5, 40 + 8), np.uint16)
+    Gb[:, :70, :40] = lin.G
+    X = to_dev(Xb, "bf16", torch)[:, :, :96]
+    G = to_dev(Gb, "bf16", torch)[:, :70, :40]
+    out, norms = dp.linear_clip_accumulate(X, G, None, C=0.05, sigma=0.0)
+    ref, rn, _ = _oracle(lin, C=0.05, sigma=0.0)
+    assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+    assert rel_fro(out.cpu().numpy(), ref) <= SUM_TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# the five workload configurations
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("sigma", [0.0, 1.0])
+@pytest.mark.parametrize("path", [1, 2])
+def test_config_single_fp32_linear(sigma, path):
+    lin = workloads.config_c1(sigma).linears[0]
+    _check(lin, path, sigma=sigma)
+
+
+def test_config_gpt2_up_projection():
+    lin = workloads.config_c2().linears[0]
+    _, norms, ref, rn = _check(lin, 0, sigma=lin.sigma)
+    _check(lin, 0, sigma=0.0, agg_tol=SUM_TOL_BF16)
+    # mixed-clip supplement: C at the median oracle norm exercises c_i = 1
+    _check(lin, 0, sigma=0.0, C=float(np.median(rn)), agg_tol=SUM_TOL_BF16)
+
+
+def test_config_gpt2_up_projection_direct_path():
+    lin = workloads.config_c2().linears[0]
+    _check(lin, 2, sigma=0.0, agg_tol=SUM_TOL_BF16)
+
+
+@pytest.mark.parametrize("index", [0, 4, 5])
+def test_config_roberta_projected(index):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    from oracle import philox
+    lin = workloads.config_c5_linear(index)
+    r = 256
+    # P from the oracle's own Philox (seed 7), fed to both sides
+    P = workloads.f32_to_bf16_bits((philox.gaussian(7, 0, lin.din * r) / 16.0)
+                                   .astype(np.float32)).reshape(lin.din, r)
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    Pd = to_dev(P, "bf16", torch)
+    for sigma, tol in ((lin.sigma, AGG_TOL_BF16), (0.0, 1e-2)):
+        out, norms = dp.linear_clip_accumulate_projected(X, G, Pd, None, C=lin.C, sigma=sigma)
+        ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, sigma, 0, 0, "bf16")
+        assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+        assert rel_fro(out.cpu().numpy(), ref) <= tol
+    # end to end: P drawn on the GPU from Philox seed 7 (each side its own generator)
+    Pg = dp.gaussian_fill(7, 0, lin.din * r, 1.0 / 16, dtype=torch.bfloat16).view(lin.din, r)
+    out, norms = dp.linear_clip_accumulate_projected(X, G, Pg, None, C=lin.C, sigma=lin.sigma)
+    ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, lin.sigma, 0, 0, "bf16")
+    assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+    assert rel_fro(out.cpu().numpy(), ref) <= AGG_TOL_BF16
+
+
+def test_projected_small_masked_fp32_and_bf16():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(9)
+    for dtype in ("f32", "bf16"):
+        lin = random_linear(rng, 3, 150, 136, 72, dtype=dtype, lengths=[150, 20, 0])
+        Pf = (rng.standard_normal((136, 40)) / np.sqrt(40)).astype(np.float32)
+        P = workloads.f32_to_bf16_bits(Pf) if dtype == "bf16" else Pf
+        X, G = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch)
+        out, norms = dp.linear_clip_accumulate_projected(X, G, to_dev(P, dtype, torch),
+                                                         mask_dev(lin.mask, torch), C=0.02, sigma=0.0)
+        ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, lin.mask, P, 0.02, 0.0, 0, 0, dtype)
+        tol_n = NORM_TOL if dtype == "f32" else 5e-3
+        assert max_rel(norms.cpu().numpy()[rn > 0], rn[rn > 0]) <= tol_n
+        assert norms.cpu().numpy()[2] == 0.0
+        assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
