@@ -2,7 +2,7 @@
 //
 // Every entry point validates all of its arguments before queueing anything:
 // a failed check launches nothing and writes nothing.  Workspace (per-sample
-// norm partials, clip factors, mask tile flags, the projected activations) is
+// norm partials, clip factors, mask row-activity bits, the projected activations) is
 // allocated with hipMallocAsync and released with hipFreeAsync on the call's
 // stream, so calls on different streams do not share state.
 #include <hip/hip_runtime.h>
@@ -151,21 +151,21 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
   L.args.din = (int)X->D;
   L.args.dout = (int)G->D;
   L.args.mask = mask;
-  L.args.nflag = (int)((X->T + dpf::kFlagTokens - 1) / dpf::kFlagTokens);
+  L.args.nwords = (int)((X->T + dpf::kBitsTokens - 1) / dpf::kBitsTokens);
   L.path = choose_path(X->T, X->D, G->D);
   L.vec = vec_ok(X) && vec_ok(G);
-  L.np = dpf::norm_partials_per_sample(L.path, L.args.T, L.args.din, L.args.dout);
+  L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
   return L;
 }
 
-// Queue flags (if masked) + norm partials.  ws offsets must be allocated.
-hipError_t queue_norm_partials(LayerPlan& L, uint8_t* flags, double* partials, hipStream_t s) {
+// Queue row bits (if masked) + norm partials.  ws offsets must be allocated.
+hipError_t queue_norm_partials(LayerPlan& L, uint32_t* bits, double* partials, hipStream_t s) {
   L.args.partials = partials;
-  L.args.tile_flags = nullptr;
+  L.args.rowbits = nullptr;
   if (L.args.mask != nullptr) {
-    hipError_t e = dpf::launch_tile_flags(L.args.mask, L.args.B, L.args.T, flags, L.args.nflag, s);
+    hipError_t e = dpf::launch_row_bits(L.args.mask, L.args.B, L.args.T, bits, L.args.nwords, s);
     if (e != hipSuccess) return e;
-    L.args.tile_flags = flags;
+    L.args.rowbits = bits;
   }
   return dpf::launch_norm(L.args, L.path, L.vec, s);
 }
@@ -174,11 +174,11 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
                        float sigma, uint64_t seed, uint64_t offset, float* grad_out,
                        float* norms_out, hipStream_t s, Workspace& ws) {
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
   const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
   const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr,
+  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr,
                                      ws.at<double>(off_part), s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
   float* c = ws.at<float>(off_c);
@@ -269,7 +269,7 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   // Reserve the layer workspace now so that a single allocation covers both.
   dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
   LayerPlan L = plan_layer(&Y, G, mask);
-  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
   const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
   const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
@@ -290,7 +290,7 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
   L = plan_layer(&Y, G, mask);
-  e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr, ws.at<double>(off_part), s);
+  e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr, ws.at<double>(off_part), s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
   float* c = ws.at<float>(off_c);
   e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
@@ -313,10 +313,10 @@ dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace ws(s);
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
   const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint8_t>(off_flags) : nullptr,
+  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr,
                                      ws.at<double>(off_part), s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
   e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sqnorms_out, accumulate ? 1 : 0, 1.0f,
@@ -350,13 +350,13 @@ dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace ws(s);
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_flags = mask ? ws.reserve((size_t)L.args.B * L.args.nflag) : 0;
+  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   if (mask) {
-    hipError_t e = dpf::launch_tile_flags(mask, L.args.B, L.args.T, ws.at<uint8_t>(off_flags),
-                                          L.args.nflag, s);
-    if (e != hipSuccess) return hip_fail(e, "tile flag launch");
-    L.args.tile_flags = ws.at<uint8_t>(off_flags);
+    hipError_t e = dpf::launch_row_bits(mask, L.args.B, L.args.T, ws.at<uint32_t>(off_bits),
+                                        L.args.nwords, s);
+    if (e != hipSuccess) return hip_fail(e, "row bits launch");
+    L.args.rowbits = ws.at<uint32_t>(off_bits);
   }
   L.args.c = c;
   L.args.noise_std = noise_std;

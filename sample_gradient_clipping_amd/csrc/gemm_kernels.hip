@@ -104,13 +104,22 @@ struct KOuterGemm {
 
 // Step cursor over (sample, token tile) pairs in [b_begin, b_end), skipping
 // token tiles with no active row when per-tile flags are given.
+// Any active token among tokens [t0, t0 + n) of sample b (n a multiple of 32).
+__device__ __forceinline__ bool any_active(const uint32_t* bits, int nwords, int b, int t0, int n) {
+  if (bits == nullptr) return true;
+  const int w0 = t0 / kBitsTokens;
+  uint32_t acc = 0u;
+  for (int w = w0; w < w0 + n / kBitsTokens && w < nwords; ++w) acc |= bits[(int64_t)b * nwords + w];
+  return acc != 0u;
+}
+
 struct StepCursor {
   int b, kt, b_end, nkt;
-  const uint8_t* flags;   // [B][nflag] or null (one flag per kFlagTokens tokens)
-  int nflag, kt_tokens;
+  const uint32_t* bits;   // [B][nwords] row-activity bits or null
+  int nwords, kt_tokens;
   __device__ __forceinline__ bool valid() const { return b < b_end; }
   __device__ __forceinline__ bool active() const {
-    return flags == nullptr || flags[(int64_t)b * nflag + (kt * kt_tokens) / kFlagTokens] != 0;
+    return any_active(bits, nwords, b, kt * kt_tokens, kt_tokens);
   }
   __device__ __forceinline__ void skip_inactive() {
     while (b < b_end && !active()) {
@@ -130,8 +139,8 @@ __device__ __forceinline__ void kouter_run(const LayerArgs& p, int b_begin, int 
   using S = typename E::storage;
   using KG = KOuterGemm<E, VEC>;
   const int nkt = (p.T + KG::KT - 1) / KG::KT;
-  static_assert(KG::KT <= kFlagTokens && kFlagTokens % KG::KT == 0, "flag granularity");
-  StepCursor cur{b_begin, 0, b_end, nkt, p.tile_flags, p.nflag, KG::KT};
+  static_assert(KG::KT % kBitsTokens == 0, "row-bit granularity");
+  StepCursor cur{b_begin, 0, b_end, nkt, p.rowbits, p.nwords, KG::KT};
   cur.skip_inactive();
   g.zero();
   *c_last = 1.0f;
@@ -337,18 +346,9 @@ __global__ void __launch_bounds__(kNT) gram_norm_kernel(LayerArgs p) {
   const int b = blockIdx.y;
   int st, tt;
   pair_of_index(pidx, nt, &st, &tt);
-  // Skip pairs whose token tiles hold no active row (flags are per 64 tokens).
-  bool live = true;
-  if (p.tile_flags != nullptr) {
-    const int fpt = kTileM / 64;
-    bool as = false, at = false;
-    for (int f = 0; f < fpt; ++f) {
-      const int fs = st * fpt + f, ft = tt * fpt + f;
-      if (fs < p.nflag) as |= p.tile_flags[(int64_t)b * p.nflag + fs] != 0;
-      if (ft < p.nflag) at |= p.tile_flags[(int64_t)b * p.nflag + ft] != 0;
-    }
-    live = as && at;
-  }
+  // Skip pairs whose token tiles hold no active row.
+  const bool live = any_active(p.rowbits, p.nwords, b, st * kTileM, kTileM) &&
+                    any_active(p.rowbits, p.nwords, b, tt * kTileM, kTileM);
   double tot = 0.0;
   if (live) {
     GT gt;
@@ -536,15 +536,25 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
 }
 }  // namespace
 
-int norm_partials_per_sample(NormPath path, int T, int din, int dout) {
+// The large-tile kernels take bf16 inputs with 16-byte vector loads and
+// address one sample's rows with 32-bit buffer offsets (< 2 GiB per sample).
+static bool use_big(const LayerArgs& p, bool vec) {
+  const int64_t lim = (int64_t)1 << 30;   // elements: 2 GiB of bf16
+  return p.dtype == kBF16 && vec && (int64_t)(p.T - 1) * p.X.stride_t + p.din < lim &&
+         (int64_t)(p.T - 1) * p.G.stride_t + p.dout < lim;
+}
+
+int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
   if (path == NormPath::kGram) {
-    const int nt = (T + kTileM - 1) / kTileM;
+    const int nt = (p.T + kTileM - 1) / kTileM;
     return nt * (nt + 1) / 2;
   }
-  return ((din + kTileM - 1) / kTileM) * ((dout + kTileN - 1) / kTileN);
+  if (use_big(p, vec)) return big_tiles(p.din, p.dout);
+  return ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
 }
 
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s) {
+  if (use_big(p, vec)) return launch_accumulate_big(p, s);
   if (p.dtype == kBF16) return vec ? launch_accumulate_t<BF16, true>(p, s) : launch_accumulate_t<BF16, false>(p, s);
   return vec ? launch_accumulate_t<F32, true>(p, s) : launch_accumulate_t<F32, false>(p, s);
 }
@@ -553,6 +563,7 @@ hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t 
     if (p.dtype == kBF16) return vec ? launch_gram_t<BF16, true>(p, s) : launch_gram_t<BF16, false>(p, s);
     return vec ? launch_gram_t<F32, true>(p, s) : launch_gram_t<F32, false>(p, s);
   }
+  if (use_big(p, vec)) return launch_direct_norm_big(p, s);
   if (p.dtype == kBF16) return vec ? launch_direct_t<BF16, true>(p, s) : launch_direct_t<BF16, false>(p, s);
   return vec ? launch_direct_t<F32, true>(p, s) : launch_direct_t<F32, false>(p, s);
 }

@@ -11,16 +11,16 @@ namespace dpf {
 enum DType { kF32 = 0, kBF16 = 1 };
 enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2 };
 
-// Tokens covered by one entry of the per-sample activity flags.
-constexpr int kFlagTokens = 64;
+// Tokens covered by one word of the per-sample row-activity bits.
+constexpr int kBitsTokens = 32;
 
 struct LayerArgs {
   Act X, G;                 // [B, T, din] and [B, T, dout]
   int dtype;                // DType
   int B, T, din, dout;
   const uint8_t* mask;      // [B, T] or null
-  const uint8_t* tile_flags;// [B, nflag]: any active token in each 64-token tile, or null
-  int nflag;
+  const uint32_t* rowbits;  // [B, nwords]: bit r of word w = token 32 w + r is active; null = no mask
+  int nwords;               // ceil(T / 32)
   const float* c;           // [B] clip factors (accumulate only)
   float noise_std;          // sigma * C (0 = no noise)
   uint64_t seed, offset;
@@ -42,11 +42,17 @@ struct ProjArgs {
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
-int norm_partials_per_sample(NormPath path, int T, int din, int dout);
+// Partials per sample written by the norm kernel launch_norm picks for (p, path, vec).
+int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec);
+
+// Large-tile bf16 kernels (accum_big.hip).
+int big_tiles(int din, int dout);
+hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s);
+hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
 
 // Small kernels (misc_kernels.hip).
-hipError_t launch_tile_flags(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag,
-                             hipStream_t s);
+hipError_t launch_row_bits(const uint8_t* mask, int B, int T, uint32_t* bits, int nwords,
+                           hipStream_t s);
 // Per sample: sq = ordered sum of np partials; optionally added into sq_io;
 // then c = clip factor and norms = sqrt(sq) when c_out is given.
 hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,

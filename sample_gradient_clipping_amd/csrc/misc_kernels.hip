@@ -38,17 +38,21 @@ __global__ void gaussian_fill_kernel(uint64_t seed, uint64_t offset, int64_t n, 
   }
 }
 
-// flags[b, f] = 1 if any of tokens [64 f, 64 f + 64) of sample b is active.
-// One wave per (b, f).
-__global__ void tile_flags_kernel(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag) {
-  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+// bits[b, w] bit r = token 32 w + r of sample b is active (< T and mask != 0).
+// One wave per two words: lanes 0..31 -> word 2j, lanes 32..63 -> word 2j+1.
+__global__ void row_bits_kernel(const uint8_t* mask, int B, int T, uint32_t* bits, int nwords) {
+  const int64_t pair = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (w >= (int64_t)B * nflag) return;
-  const int b = (int)(w / nflag), f = (int)(w % nflag);
-  const int t = f * kFlagTokens + lane;
-  const bool a = t < T && mask[(int64_t)b * T + t] != 0;
-  const uint64_t any = __ballot(a);
-  if (lane == 0) flags[w] = any != 0 ? 1 : 0;
+  const int64_t wi = 2 * pair + (lane >> 5);
+  const int64_t total = (int64_t)B * nwords;
+  bool a = false;
+  if (wi < total) {
+    const int b = (int)(wi / nwords), w = (int)(wi % nwords);
+    const int t = w * kBitsTokens + (lane & 31);
+    a = t < T && mask[(int64_t)b * T + t] != 0;
+  }
+  const uint64_t ball = __ballot(a);
+  if (wi < total && (lane & 31) == 0) bits[wi] = (uint32_t)(ball >> (lane & 32));
 }
 
 __device__ __forceinline__ void clip_of_sq(double sq, float C, float* c, float* n) {
@@ -111,13 +115,13 @@ hipError_t launch_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float
   return hipGetLastError();
 }
 
-hipError_t launch_tile_flags(const uint8_t* mask, int B, int T, uint8_t* flags, int nflag,
-                             hipStream_t s) {
-  const int64_t waves = (int64_t)B * nflag;
-  timing_begin("tile_flags", s);
-  hipLaunchKernelGGL(tile_flags_kernel, dim3(blocks_for(waves, 4)), dim3(256), 0, s, mask, B, T,
-                     flags, nflag);
-  timing_end("tile_flags", s);
+hipError_t launch_row_bits(const uint8_t* mask, int B, int T, uint32_t* bits, int nwords,
+                           hipStream_t s) {
+  const int64_t waves = ((int64_t)B * nwords + 1) / 2;
+  timing_begin("row_bits", s);
+  hipLaunchKernelGGL(row_bits_kernel, dim3(blocks_for(waves, 4)), dim3(256), 0, s, mask, B, T,
+                     bits, nwords);
+  timing_end("row_bits", s);
   return hipGetLastError();
 }
 
