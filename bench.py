@@ -39,7 +39,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain copy of known size: reads and writes exactly 1 GiB per launch."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
+                      "launches": steps}), flush=True)
 
 
 def upload(a, torch):
@@ -86,6 +101,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU data parallelism is a design note, not built)"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     import torch
     import sample_gradient_clipping_amd as dp
     import workloads
