@@ -545,6 +545,7 @@ static bool use_big(const LayerArgs& p, bool vec) {
 }
 
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
+  if (path == NormPath::kGram && use_big(p, vec)) return gram_big_items_per_sample(p.T);
   if (path == NormPath::kGram) {
     const int nt = (p.T + kTileM - 1) / kTileM;
     return nt * (nt + 1) / 2;
@@ -560,6 +561,7 @@ hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s) {
 }
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s) {
   if (path == NormPath::kGram) {
+    if (use_big(p, vec)) return launch_gram_norm_big(p, s);
     if (p.dtype == kBF16) return vec ? launch_gram_t<BF16, true>(p, s) : launch_gram_t<BF16, false>(p, s);
     return vec ? launch_gram_t<F32, true>(p, s) : launch_gram_t<F32, false>(p, s);
   }

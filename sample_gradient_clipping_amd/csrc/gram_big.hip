@@ -1,0 +1,270 @@
+// Large-tile bf16 kernel for the Gram form of the per-sample squared norm:
+//
+//   ||G~_i^T X~_i||^2 = sum_{s,t} (X~_i X~_i^T)[s,t] (G~_i G~_i^T)[s,t]
+//
+// One workgroup per (sample, 256-token row block S, 128-token column block
+// Tb) with Tb >= 2S, i.e. every tile that touches the upper triangle s <= t.
+// Each element is weighted 2 above the diagonal, 1 on it and 0 below, so the
+// symmetric sum is counted once.  The X Gram tile (K = din) and the G Gram
+// tile (K = dout) accumulate one after the other in registers; their
+// elementwise product is reduced wave -> LDS -> one fp64 partial per
+// workgroup, summed in a fixed order later (finalize_kernel).
+//
+// Workgroup: 512 threads = 8 waves (4 along s, 2 along t; two per SIMD);
+// each wave owns 64 x 64 of both Gram tiles: 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators per Gram (128 fp32 per lane).
+// Operands are feature-contiguous ("K-inner"): each lane's MFMA fragment is
+// one 16-byte LDS read.  Data moves global -> LDS by 16-byte-per-lane buffer
+// loads that write LDS directly into a ring of three 48 KiB slots (64
+// features of 256 + 128 token rows); rows are 128 bytes with the 16-byte
+// chunk c of row r stored at c ^ ((r >> 1) & 7), which keeps both the DMA
+// writes and the fragment reads free of bank conflicts.  Masked tokens and
+// rows past T read through out-of-range buffer offsets (zeros).
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace dpf {
+namespace gram {
+
+constexpr int kNT = 512;
+constexpr int kWaveRows = 4, kWaveCols = 2;
+constexpr int kRowsS = 256, kRowsT = 128;
+constexpr int kKF = 64;                         // features per step
+constexpr int kRowBytes = kKF * 2;              // 128
+constexpr int kSBytes = kRowsS * kRowBytes;     // 32 KiB
+constexpr int kSlotBytes = kSBytes + kRowsT * kRowBytes;   // 48 KiB
+constexpr int kStages = 3;
+constexpr int kLdsBytes = kStages * kSlotBytes;            // 144 KiB
+constexpr int kDmaPerStep = kSlotBytes / 1024 / (kNT / 64);  // 6 per wave
+constexpr int kOOB = 0x7ffffff0;
+
+typedef __attribute__((address_space(4))) const uint32_t c_u32;
+
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds)
+               : "memory");
+}
+
+// Wait until at most `steps` of this wave's most recent DMA steps are in flight.
+__device__ __forceinline__ void wait_dma(int steps) {
+  static_assert(kDmaPerStep == 6, "wait_dma encodes 6 DMAs per step");
+  if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (steps == 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sample_rsrc(const Act& a, int b, int T, int D) {
+  const char* base = (const char*)a.data + (int64_t)b * a.stride_b * 2;
+  const int64_t bytes = ((int64_t)(T - 1) * a.stride_t + D) * 2;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                           (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                           0x00020000);
+}
+
+// Work items per sample for T tokens.
+__device__ __host__ __forceinline__ int items_per_sample(int T) {
+  const int nS = (T + kRowsS - 1) / kRowsS, nTb = (T + kRowsT - 1) / kRowsT;
+  int n = 0;
+  for (int S = 0; S < nS; ++S) n += (nTb - 2 * S > 0) ? nTb - 2 * S : 0;
+  return n;
+}
+
+// Per-lane DMA addressing for this workgroup's rows.  DMA j of wave w is
+// instruction q = 6 w + j of the slot: q < 32 fills s-rows 8q .. 8q+7, the
+// rest t-rows; lane l fills physical chunk l % 8 of row l / 8 of that group,
+// i.e. logical feature chunk (l % 8) ^ swizzle(row).
+struct DmaLane {
+  uint32_t xoff[kDmaPerStep], goff[kDmaPerStep];   // row offset + chunk, or kOOB
+  int cfeat[kDmaPerStep];                          // first feature of the chunk
+  __device__ __forceinline__ void init(const LayerArgs& p, int b, int S, int Tb) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < kDmaPerStep; ++j) {
+      const int q = kDmaPerStep * wave + j;
+      const bool sreg = q < kRowsS / 8;
+      const int row = (sreg ? 8 * q : 8 * (q - kRowsS / 8)) + (lane >> 3);
+      const int tok = sreg ? kRowsS * S + row : kRowsT * Tb + row;
+      bool active = tok < p.T;
+      if (active && p.rowbits != nullptr)
+        active = (p.rowbits[(int64_t)b * p.nwords + (tok >> 5)] >> (tok & 31)) & 1u;
+      const int c = swz(row, lane & 7);
+      cfeat[j] = c * 8;
+      xoff[j] = active ? (uint32_t)(((int64_t)tok * p.X.stride_t + c * 8) * 2) : (uint32_t)kOOB;
+      goff[j] = active ? (uint32_t)(((int64_t)tok * p.G.stride_t + c * 8) * 2) : (uint32_t)kOOB;
+    }
+  }
+};
+
+// Queue feature step `step` (X features for step < nkx, else G features).
+__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl,
+                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
+                                           int step, int nkx, uint32_t slot) {
+  const int wave = threadIdx.x >> 6;
+  const bool xs = step < nkx;
+  const int k0 = (xs ? step : step - nkx) * kKF;
+  const int D = xs ? p.din : p.dout;
+#pragma unroll
+  for (int j = 0; j < kDmaPerStep; ++j) {
+    const uint32_t base = xs ? dl.xoff[j] : dl.goff[j];
+    const int off = (k0 + dl.cfeat[j] < D) ? (int)(base + (uint32_t)k0 * 2) : kOOB;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (kDmaPerStep * wave + j) * 1024);
+    dma16(xs ? rx : rg, off, dst);
+  }
+}
+
+// MFMA operand for rows m0..m0+31 of a region, 16-feature substep ks.
+__device__ __forceinline__ u16x8 frag(const unsigned char* region, int m0, int ks) {
+  const int lane = threadIdx.x & 63;
+  const int row = m0 + (lane & 31);
+  const int c = 2 * ks + (lane >> 5);
+  return *(const u16x8*)(region + row * kRowBytes + swz(row, c) * 16);
+}
+
+struct Acc2 {
+  f32x16 v[2][2];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
+  }
+  // Keep the accumulators in accumulation registers (AGPRs): with two Gram
+  // tiles live, ordinary VGPRs would overflow.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(v[i][j]));
+  }
+  __device__ __forceinline__ void step(const unsigned char* slot) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / kWaveCols, wn = wave % kWaveCols;
+#pragma unroll
+    for (int ks = 0; ks < kKF / 16; ++ks) {
+      u16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = frag(slot, wm * 64 + i * 32, ks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = frag(slot + kSBytes, wn * 64 + j * 32, ks);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) v[i][j] = mfma_32x32x16(a[i], b[j], v[i][j]);
+    }
+  }
+};
+
+// Work item of workgroup `id`.  Workgroups are dealt to the 8 XCDs round
+// robin, so XCD x gets the contiguous item range [x*per, (x+1)*per): items
+// of one sample and row block S (sharing their s-rows) meet in one L2.
+// Item L = b * per_sample + (index of (S, Tb) within the sample).
+__device__ __forceinline__ bool item_of(int id, int per_sample, int B, int T, int* L_out, int* b,
+                                        int* S, int* Tb) {
+  const int total = B * per_sample;
+  const int per = (total + 7) / 8;
+  const int L = (id & 7) * per + (id >> 3);
+  if (L >= total) return false;
+  *L_out = L;
+  *b = L / per_sample;
+  int r = L % per_sample;
+  const int nTb = (T + kRowsT - 1) / kRowsT;
+  int s = 0;
+  while (r >= nTb - 2 * s) { r -= nTb - 2 * s; ++s; }
+  *S = s;
+  *Tb = 2 * s + r;
+  return true;
+}
+
+__global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int per_sample = items_per_sample(p.T);
+  int L, b, S, Tb;
+  if (!item_of(blockIdx.x, per_sample, p.B, p.T, &L, &b, &S, &Tb)) return;
+  const int nkx = (p.din + kKF - 1) / kKF, nkg = (p.dout + kKF - 1) / kKF;
+  const int n = nkx + nkg;
+  const __amdgpu_buffer_rsrc_t rx = sample_rsrc(p.X, b, p.T, p.din);
+  const __amdgpu_buffer_rsrc_t rg = sample_rsrc(p.G, b, p.T, p.dout);
+  DmaLane dl;
+  dl.init(p, b, S, Tb);
+  const uint32_t base = lds_addr(smem);
+#pragma unroll
+  for (int k = 0; k < kStages; ++k)
+    if (k < n) issue_step(p, dl, rx, rg, k, nkx, base + k * kSlotBytes);
+
+  Acc2 ax, ag;
+  ax.zero();
+  ag.zero();
+  int slot = 0;
+  // One pipelined step: wait for step i, refill the drained slot, compute.
+  // Issued so far: steps 0..2 before the loop, then step j+2 in iteration
+  // j >= 1.
+  auto step = [&](int i, Acc2& acc) {
+    wait_dma(i == 0 ? min(kStages - 1, n - 1) : min(kStages - 2, n - 1 - i));
+    __syncthreads();
+    if (i >= 1 && i + kStages - 1 < n) {
+      const int prev = (slot == 0) ? kStages - 1 : slot - 1;
+      issue_step(p, dl, rx, rg, i + kStages - 1, nkx, base + prev * kSlotBytes);
+    }
+    acc.step(smem + slot * kSlotBytes);
+    acc.pin();
+    slot = (slot + 1 == kStages) ? 0 : slot + 1;
+  };
+  int i = 0;
+  for (; i < nkx; ++i) step(i, ax);   // X Gram, K = din
+  for (; i < n; ++i) step(i, ag);     // G Gram, K = dout
+
+  // Weighted elementwise product.  Rows past T and masked rows are zero.
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / kWaveCols, wn = wave % kWaveCols;
+  const bool above = kRowsT * Tb >= kRowsS * (S + 1);   // whole tile has s < t
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float prod = ax.v[i][j][r] * ag.v[i][j][r];
+        if (above) {
+          sum += 2.0f * prod;
+        } else {
+          const int s = kRowsS * S + wm * 64 + i * 32 + acc_row(r, lane);
+          const int t = kRowsT * Tb + wn * 64 + j * 32 + acc_col(lane);
+          sum += (s < t) ? 2.0f * prod : ((s == t) ? prod : 0.0f);
+        }
+      }
+  __syncthreads();   // the slot ring is free: reuse it for the reduction
+  const double tot = block_sum_f64((double)sum, (double*)smem);
+  if (threadIdx.x == 0) p.partials[L] = tot;
+}
+
+}  // namespace gram
+
+int gram_big_items_per_sample(int T) { return gram::items_per_sample(T); }
+
+hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
+  static hipError_t once = hipFuncSetAttribute((const void*)gram::gram_norm_big_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               gram::kLdsBytes);
+  if (once != hipSuccess) return once;
+  const int total = p.B * gram::items_per_sample(p.T);
+  const int grid = 8 * ((total + 7) / 8);
+  timing_begin("gram_norm", s);
+  hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(grid), dim3(gram::kNT), gram::kLdsBytes, s,
+                     p);
+  hipError_t e = hipGetLastError();
+  timing_end("gram_norm", s);
+  return e;
+}
+
+}  // namespace dpf

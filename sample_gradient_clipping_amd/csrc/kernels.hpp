@@ -50,6 +50,10 @@ int big_tiles(int din, int dout);
 hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
 
+// Large-tile bf16 Gram-norm kernel (gram_big.hip).
+int gram_big_items_per_sample(int T);
+hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s);
+
 // Small kernels (misc_kernels.hip).
 hipError_t launch_row_bits(const uint8_t* mask, int B, int T, uint32_t* bits, int nwords,
                            hipStream_t s);
