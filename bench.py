@@ -13,6 +13,7 @@ resident in HBM before timing starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,19 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFMA peak"
+
+# HBM bytes per accumulate launch on this workload, from two rocprofv3 --pmc
+# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged
+# over the seven linears), each scaled by what the same counter reads for a
+# plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for
+# the kernel sources whose SHA-256 is stored here; reported as null otherwise.
+ACCUM_SOURCES = ("accum_big.hip", "common.hpp", "kernels.hpp")
+ACCUM_COUNTERS = {
+    "sources_sha256": "48cf033bc37af1dd98e68e19d8acf941455289136a18ae41711bdc23adfc6f6f",
+    "fetch_kib": 1292155.34, "fetch_scale": 2.0,
+    "write_kib": 177005.71, "write_scale": 1.0,
+    "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
+}
 
 
 def parse():
@@ -55,6 +69,20 @@ def copy_calibration(steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
                       "launches": steps}), flush=True)
+
+
+def accumulate_traffic(args):
+    """Counter-derived HBM bytes per accumulate launch, or None when the kernel
+    sources or the workload differ from the profiled ones."""
+    c = ACCUM_COUNTERS
+    h = hashlib.sha256()
+    for f in ACCUM_SOURCES:
+        with open(os.path.join(ROOT, "sample_gradient_clipping_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if (h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"] or args.seq != c["seq"]
+            or args.linears != c["linears"]):
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 
 
 def upload(a, torch):
@@ -169,6 +197,9 @@ def main():
     acc_achieved = acc_flops_per_launch / (acc_avg_ms * 1e-3) / 1e12 if acc_n else None
     gram_achieved = (gram / len(lins)) / ((gram_ms / max(gram_n, 1)) * 1e-3) / 1e12 if gram_n else None
 
+    traffic = accumulate_traffic(args)
+    algo_bytes = sum(2.0 * l.B * l.T * (l.din + l.dout) + 4.0 * l.din * l.dout for l in lins) / len(lins)
+
     per_linear = []
     for l in lins:
         f = 2.0 * l.B * l.T * l.din * l.dout
@@ -203,8 +234,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": None if acc_achieved is None else round(acc_achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic),
         },
+        "accumulate_bytes_per_launch": {"algorithmic": round(algo_bytes),
+                                        "hbm_counters": None if traffic is None else round(traffic)},
         "gram_norm_kernel_tflops": None if gram_achieved is None else round(gram_achieved, 2),
         "per_linear": per_linear,
         "wall_s_timed": round(wall, 3),
