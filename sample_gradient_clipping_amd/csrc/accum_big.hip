@@ -112,27 +112,51 @@ struct DmaLane {
   }
 };
 
-// Queue step (b, s) into the LDS slot at `stage`: X[tokens, a0:a0+256] and
-// G[tokens, o0:o0+256].  Inactive rows read through out-of-range offsets.
-template <bool MASK>
-__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl, int b, int s,
-                                           uint32_t stage) {
-  const __amdgpu_buffer_rsrc_t rx = sample_rsrc(p.X, b, p.T, p.din);
-  const __amdgpu_buffer_rsrc_t rg = sample_rsrc(p.G, b, p.T, p.dout);
-  const uint32_t bits = step_bits<MASK>(p, b, s);
-  const int t0 = s * kKT;
-  const uint32_t xs = (uint32_t)((int64_t)t0 * p.X.stride_t * 2);
-  const uint32_t gs = (uint32_t)((int64_t)t0 * p.G.stride_t * 2);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t wbase = stage + kRowsPerWave * wave * kRowBytes;
-  const uint32_t mine = bits >> (kRowsPerWave * wave);   // bit 2j + l/32 = row of DMA j
-#pragma unroll
-  for (int j = 0; j < kDmaPerOp; ++j) {
-    const bool act = (mine >> (2 * j + (lane >> 5))) & 1u;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(wbase + 2 * j * kRowBytes);
-    dma16(rx, act ? (int)(dl.xoff[j] + xs) : kOOB, dst);
-    dma16(rg, act ? (int)(dl.goff[j] + gs) : kOOB, dst + kOpBytes);
+// Buffer descriptors of one sample's X and G rows, rebuilt only when the
+// issuing cursor moves to another sample.
+struct SampleRsrc {
+  __amdgpu_buffer_rsrc_t rx, rg;
+  int b = -1;
+  __device__ __forceinline__ void at(const LayerArgs& p, int nb) {
+    if (nb != b) {
+      rx = sample_rsrc(p.X, nb, p.T, p.din);
+      rg = sample_rsrc(p.G, nb, p.T, p.dout);
+      b = nb;
+    }
   }
+};
+
+// Queue DMA pair j of step (b, s) into the LDS slot at `stage`: rows
+// 4 wave + 2 j + {0, 1} of X[tokens, a0:a0+256] and G[tokens, o0:o0+256].
+// With a mask, inactive rows read through out-of-range offsets.  Without
+// one, the rows past T of a tail step are already past the end of the
+// sample's buffer descriptor (row stride >= row length), so they read zeros
+// as they are.
+template <bool MASK>
+__device__ __forceinline__ void issue_pair(const LayerArgs& p, const DmaLane& dl, SampleRsrc& sr,
+                                           int b, int s, uint32_t stage, int j) {
+  sr.at(p, b);
+  const uint32_t t0 = (uint32_t)(s * kKT);
+  const uint32_t xs = t0 * (uint32_t)p.X.stride_t * 2u;   // < 2^31: span checked on the host
+  const uint32_t gs = t0 * (uint32_t)p.G.stride_t * 2u;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (kRowsPerWave * wave + 2 * j) * kRowBytes);
+  if constexpr (MASK) {
+    const uint32_t mine = step_bits<MASK>(p, b, s) >> (kRowsPerWave * wave);
+    const bool act = (mine >> (2 * j + (lane >> 5))) & 1u;
+    dma16(sr.rx, act ? (int)(dl.xoff[j] + xs) : kOOB, dst);
+    dma16(sr.rg, act ? (int)(dl.goff[j] + gs) : kOOB, dst + kOpBytes);
+  } else {
+    dma16(sr.rx, (int)(dl.xoff[j] + xs), dst);
+    dma16(sr.rg, (int)(dl.goff[j] + gs), dst + kOpBytes);
+  }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl, SampleRsrc& sr,
+                                           int b, int s, uint32_t stage) {
+#pragma unroll
+  for (int j = 0; j < kDmaPerOp; ++j) issue_pair<MASK>(p, dl, sr, b, s, stage, j);
 }
 
 // MFMA operands of one 16-token k-substep for this wave: 4 X blocks (din
@@ -168,6 +192,17 @@ __device__ __forceinline__ void read_frags(Frags& f, const unsigned char* stage,
   for (int j = 0; j < kBO; ++j) f.b[j] = frag(stage + kOpBytes, wn * (kBO * 32) + j * 32, ks);
 }
 
+// Fragment q of a k-substep: q = 0, 1 are the G blocks b[0], b[1]; q = 2..5
+// the X blocks a[0..3].  This is the order in which the MFMAs first need them.
+__device__ __forceinline__ void read_frag(Frags& f, const unsigned char* stage, int ks, int q) {
+  if (q < kBO) f.b[q] = frag(stage + kOpBytes, wave_col() * (kBO * 32) + q * 32, ks);
+  else f.a[q - kBO] = frag(stage, wave_row() * (kBA * 32) + (q - kBO) * 32, ks);
+}
+
+// Nothing is scheduled across this point: it fixes the interleaving of
+// MFMAs with LDS reads and DMA issue that the main loop spells out.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 struct Acc {
   f32x16 v[kBA][kBO];
   __device__ __forceinline__ void zero() {
@@ -193,6 +228,16 @@ struct Acc {
         asm volatile("" : "+a"(t));
         v[i][j] = t;
       }
+  }
+  // Keep every MFMA issued so far on this side of the statement (an
+  // ordering point; no instruction is emitted).
+  __device__ __forceinline__ void pin() {
+    asm volatile("" : "+a"(v[0][0]), "+a"(v[0][1]), "+a"(v[1][0]), "+a"(v[1][1]),
+                      "+a"(v[2][0]), "+a"(v[2][1]), "+a"(v[3][0]), "+a"(v[3][1]));
+  }
+  // MFMA k of a k-substep: block (k / kBO, k % kBO).
+  __device__ __forceinline__ void mma1(const Frags& f, int k) {
+    v[k / kBO][k % kBO] = mfma_32x32x16(f.a[k / kBO], f.b[k % kBO], v[k / kBO][k % kBO]);
   }
   __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
@@ -230,14 +275,39 @@ __device__ __forceinline__ int count_active(const LayerArgs& p, int b0, int b1, 
   return n;
 }
 
+// Workgroup barrier without a memory fence: the LDS reads still in flight
+// target a slot that no DMA refills before the next barrier, and the DMA
+// writes this barrier publishes were awaited explicitly (wait_dma).  The
+// empty asm statements keep the compiler from moving LDS accesses across.
+// All of this wave's LDS reads have returned.  Issued as the compiler's own
+// wait instruction, so that its bookkeeping of outstanding LDS reads (whose
+// counter tracks at most 15) starts again from zero: the reads issued next
+// are then waited for on their own, not together with older ones.
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+}
+
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Main loop over the active steps of samples [b0, b1).
 //
-// Five 32 KiB LDS slots.  A slot is refilled as soon as every wave's reads
-// of it are complete (the barrier of the next step), so the DMA of step i+4
-// is queued at the start of step i and has three steps to land: up to 128 KiB
-// per CU in flight, which is what it takes to keep the MFMAs fed through L2
-// misses.  Two waves share each SIMD, so one
-// wave's LDS-read and barrier waits are covered by the other's MFMAs.
+// Five 32 KiB LDS slots.  Barrier i (between the two k-substeps of step i)
+// certifies that step i+1 has landed for every wave and that every wave's
+// reads of step i-1 are complete; slot (i-1) is then refilled with step i+4.
+//
+// Both waves of a SIMD pass each barrier together, so neither can cover the
+// other's non-MFMA work: each wave interleaves its own.  Each k-substep is
+// eight MFMAs on fragments already in registers, with the LDS reads of the
+// other k-substep's fragments (and, after the barrier, the DMA of step i+4)
+// issued between them:
+//
+//   k-substep 0 of step i : MFMAs on f0, reads of f1 (step i, tokens 16..31)
+//   wait for f1, wait for step i+1's DMA, barrier
+//   k-substep 1 of step i : MFMAs on f1, DMA of step i+4, reads of f0 (step i+1)
 //
 // SCALE: rescale the accumulator at sample boundaries so that it ends as
 // sum_i (c_i / c_last) g_i; c_last is returned.
@@ -245,6 +315,7 @@ template <bool SCALE, bool MASK>
 __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0, int o0, Acc& acc,
                                      unsigned char* lds) {
   static_assert(kKT == kBitsTokens, "one row-bit word per step");
+  static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
   const int nsteps = (p.T + kKT - 1) / kKT;
   const int n = count_active<MASK>(p, b0, b1, nsteps);
   acc.zero();
@@ -252,6 +323,7 @@ __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0,
   const uint32_t base = lds_addr(lds);
   DmaLane dl;
   dl.init(p, a0, o0);
+  SampleRsrc sr;
 
   Cursor<MASK> ic{b0, 0, b1, nsteps};   // next step to issue
   ic.settle(p);
@@ -259,26 +331,19 @@ __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0,
 #pragma unroll
   for (int k = 0; k < kStages; ++k) {
     if (k < n) {
-      issue_step<MASK>(p, dl, ic.b, ic.s, base + k * kStageBytes);
+      issue_step<MASK>(p, dl, sr, ic.b, ic.s, base + k * kStageBytes);
       ic.advance(p);
     }
   }
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
   int cb = cc.b;
+  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
+  step_barrier();
+  Frags f0, f1;
+#pragma unroll
+  for (int q = 0; q < 6; ++q) read_frag(f0, lds, 0, q);
   int slot = 0;                        // i % kStages
   for (int i = 0; i < n; ++i) {
-    // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
-    // in iteration j >= 1, i.e. up to min(i+3, n-1) once i >= 1.  Wait until
-    // step i has landed for this wave; the barrier extends that to every
-    // wave and also certifies that all reads of step i-1 are complete.
-    wait_dma(i == 0 ? min(kStages - 1, n - 1) : min(kStages - 2, n - 1 - i));
-    __syncthreads();
-    if (i >= 1 && i + kStages - 1 < n) {
-      // refill slot (i-1) % kStages, drained before the barrier, with step i+4
-      const int prev = (slot == 0) ? kStages - 1 : slot - 1;
-      issue_step<MASK>(p, dl, ic.b, ic.s, base + prev * kStageBytes);
-      ic.advance(p);
-    }
     if (SCALE && cc.b != cb) {
       // acc holds sum_{j<=cb} (c_j / c_cb) g_j; re-express it in units of the
       // new sample's factor before its tiles are added.
@@ -288,13 +353,43 @@ __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0,
       cb = cc.b;
     }
     const unsigned char* st = lds + slot * kStageBytes;
-    Frags f;
-    read_frags(f, st, 0);
-    acc.mma(f);
-    read_frags(f, st, 1);
-    acc.mma(f);
-    cc.advance(p);
-    slot = (slot + 1 == kStages) ? 0 : slot + 1;
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc.mma1(f0, k);
+      sched_fence();
+      if (k < 6) read_frag(f1, st, 1, k);
+      sched_fence();
+    }
+    lds_reads_done();                  // f1 is in registers; slot i-1 is no longer read
+    const int next = (slot + 1 == kStages) ? 0 : slot + 1;
+    const unsigned char* sn = lds + next * kStageBytes;
+    if (i + 1 < n) {
+      // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
+      // at barrier j >= 1, i.e. up to max(4, i+3).  Wait for step i+1.
+      const int last = min(n - 1, i <= 1 ? kStages - 1 : i + kStages - 2);
+      wait_dma(last - (i + 1));
+      step_barrier();
+    }
+    // slot (i-1) % kStages is free: queue step i+4 into it, one DMA pair
+    // after each of the first two MFMAs.  The reads of f0 follow; on the last
+    // step they read the next slot's stale contents, which are never used.
+    const bool refill = i >= 1 && i + kStages - 1 < n;
+    const uint32_t prev = base + ((slot == 0) ? kStages - 1 : slot - 1) * kStageBytes;
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc.mma1(f1, k);
+      sched_fence();
+      if (k < kDmaPerOp && refill) issue_pair<MASK>(p, dl, sr, ic.b, ic.s, prev, k);
+      if (k == kDmaPerOp - 1) {
+        if (refill) ic.advance(p);
+        cc.advance(p);
+      }
+      if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
+      sched_fence();
+    }
+    slot = next;
   }
   return c_last;
 }

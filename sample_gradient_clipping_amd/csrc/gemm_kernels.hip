@@ -538,10 +538,15 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
 
 // The large-tile kernels take bf16 inputs with 16-byte vector loads and
 // address one sample's rows with 32-bit buffer offsets (< 2 GiB per sample).
+// The large-tile kernels address one sample's rows with 32-bit byte offsets,
+// including the rows of the last (partial) tile past T, which must land past
+// the end of the sample's buffer range rather than wrap around into it: the
+// padded span must stay below 2 GiB.
 static bool use_big(const LayerArgs& p, bool vec) {
   const int64_t lim = (int64_t)1 << 30;   // elements: 2 GiB of bf16
-  return p.dtype == kBF16 && vec && (int64_t)(p.T - 1) * p.X.stride_t + p.din < lim &&
-         (int64_t)(p.T - 1) * p.G.stride_t + p.dout < lim;
+  const int64_t Tp = ((int64_t)p.T + 255) / 256 * 256;
+  return p.dtype == kBF16 && vec && Tp * p.X.stride_t + p.din < lim &&
+         Tp * p.G.stride_t + p.dout < lim;
 }
 
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
