@@ -19,6 +19,8 @@
 // Output tiles are ordered so that the workgroups resident on one XCD at a
 // time cover a compact block of tiles (shared X and G strips stay in that
 // XCD's L2).
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -247,38 +249,38 @@ struct Acc {
   }
 };
 
-// (sample, step) cursor over the active steps of samples [b, b_end).
+// Cursor over the active (sample, 32-token step) pairs of a call, in order:
+// without a mask every step of every sample, with one the call's active-step
+// list.  k is the position in that sequence.
 template <bool MASK>
 struct Cursor {
-  int b, s, b_end, nsteps;
-  __device__ __forceinline__ bool active(const LayerArgs& p) const {
-    if constexpr (!MASK) return true;
-    else return ((c_u32*)p.rowbits)[(int64_t)b * p.nwords + s] != 0u;
-  }
-  __device__ __forceinline__ void settle(const LayerArgs& p) {
-    while (b < b_end && !active(p)) {
-      if (++s == nsteps) { s = 0; ++b; }
+  int k, b, s, nsteps;
+  const uint32_t* list;
+  __device__ __forceinline__ void load() {
+    if constexpr (MASK) {
+      const uint32_t v = ((c_u32*)list)[k];
+      b = (int)(v >> 16);
+      s = (int)(v & 0xffffu);
     }
   }
-  __device__ __forceinline__ void advance(const LayerArgs& p) {
-    if (++s == nsteps) { s = 0; ++b; }
-    settle(p);
+  __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
+    nsteps = (p.T + kKT - 1) / kKT;
+    k = k0;
+    if constexpr (MASK) {
+      list = p.steps + 2 + p.B;
+      load();
+    } else {
+      b = k0 / nsteps;
+      s = k0 - b * nsteps;
+    }
+  }
+  __device__ __forceinline__ void advance() {
+    ++k;
+    if constexpr (MASK) load();
+    else if (++s == nsteps) { s = 0; ++b; }
   }
 };
 
-template <bool MASK>
-__device__ __forceinline__ int count_active(const LayerArgs& p, int b0, int b1, int nsteps) {
-  if constexpr (!MASK) return (b1 - b0) * nsteps;
-  int n = 0;
-  Cursor<MASK> c{b0, 0, b1, nsteps};
-  for (c.settle(p); c.b < b1; c.advance(p)) ++n;
-  return n;
-}
-
-// Workgroup barrier without a memory fence: the LDS reads still in flight
-// target a slot that no DMA refills before the next barrier, and the DMA
-// writes this barrier publishes were awaited explicitly (wait_dma).  The
-// empty asm statements keep the compiler from moving LDS accesses across.
 // All of this wave's LDS reads have returned.  Issued as the compiler's own
 // wait instruction, so that its bookkeeping of outstanding LDS reads (whose
 // counter tracks at most 15) starts again from zero: the reads issued next
@@ -287,13 +289,16 @@ __device__ __forceinline__ void lds_reads_done() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
 }
 
+// Workgroup barrier without a memory fence: each wave has seen its LDS reads
+// return (lds_reads_done) and its DMA writes land (wait_dma) before it.  The
+// empty asm statements keep the compiler from moving LDS accesses across.
 __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Main loop over the active steps of samples [b0, b1).
+// Main loop over n active steps, from position k0 of the call's sequence.
 //
 // Five 32 KiB LDS slots.  Barrier i (between the two k-substeps of step i)
 // certifies that step i+1 has landed for every wave and that every wave's
@@ -312,27 +317,25 @@ __device__ __forceinline__ void step_barrier() {
 // SCALE: rescale the accumulator at sample boundaries so that it ends as
 // sum_i (c_i / c_last) g_i; c_last is returned.
 template <bool SCALE, bool MASK>
-__device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0, int o0, Acc& acc,
+__device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, int o0, Acc& acc,
                                      unsigned char* lds) {
   static_assert(kKT == kBitsTokens, "one row-bit word per step");
   static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
-  const int nsteps = (p.T + kKT - 1) / kKT;
-  const int n = count_active<MASK>(p, b0, b1, nsteps);
   acc.zero();
-  if (n == 0) return 1.0f;
+  if (n <= 0) return 1.0f;
   const uint32_t base = lds_addr(lds);
   DmaLane dl;
   dl.init(p, a0, o0);
   SampleRsrc sr;
 
-  Cursor<MASK> ic{b0, 0, b1, nsteps};   // next step to issue
-  ic.settle(p);
+  Cursor<MASK> ic;                       // next step to issue
+  ic.start(p, k0);
   Cursor<MASK> cc = ic;                  // step being consumed
 #pragma unroll
   for (int k = 0; k < kStages; ++k) {
     if (k < n) {
       issue_step<MASK>(p, dl, sr, ic.b, ic.s, base + k * kStageBytes);
-      ic.advance(p);
+      ic.advance();
     }
   }
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
@@ -383,8 +386,8 @@ __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0,
       sched_fence();
       if (k < kDmaPerOp && refill) issue_pair<MASK>(p, dl, sr, ic.b, ic.s, prev, k);
       if (k == kDmaPerOp - 1) {
-        if (refill) ic.advance(p);
-        cc.advance(p);
+        if (refill) ic.advance();
+        cc.advance();
       }
       if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
       sched_fence();
@@ -394,37 +397,34 @@ __device__ __forceinline__ float run(const LayerArgs& p, int b0, int b1, int a0,
   return c_last;
 }
 
-// Tile index for this workgroup: workgroups are dealt to the 8 XCDs round
-// robin, so give XCD x the contiguous range [x*per, (x+1)*per) of a grouped
-// raster order (kGroupRows tile-rows at a time).
-__device__ __forceinline__ bool tile_of(int id, int ntm, int ntn, int* tm, int* tn) {
-  const int ntiles = ntm * ntn;
-  const int per = (ntiles + 7) / 8;
-  const int L = (id & 7) * per + (id >> 3);
-  if (L >= ntiles) return false;
+// Grouped raster order of the output tiles: tile index L -> (tm, tn), kGroupRows
+// tile-rows at a time, so that consecutive tiles share X and G strips.
+__device__ __forceinline__ void raster(int L, int ntm, int ntn, int* tm, int* tn) {
   const int gsz = kGroupRows * ntn;
   const int g = L / gsz, r = L % gsz;
   const int rows = min(kGroupRows, ntm - g * kGroupRows);
   *tm = g * kGroupRows + r % rows;
   *tn = r / rows;
-  return true;
 }
 
-__global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
-  int tm, tn;
-  if (!tile_of(blockIdx.x, ntm, ntn, &tm, &tn)) return;
-  const int a0 = tm * kTile, o0 = tn * kTile;
-  Acc acc;
-  const float c_last = p.rowbits != nullptr ? run<true, true>(p, 0, p.B, a0, o0, acc, smem)
-                                            : run<true, false>(p, 0, p.B, a0, o0, acc, smem);
-  static_assert(256 * (64 + 4) * 4 <= kLdsBytes, "epilogue staging fits in the stage ring");
+// Workgroups are dealt to the 8 XCDs round robin; logical index of this
+// workgroup such that XCD x holds the contiguous range [x*G/8, (x+1)*G/8).
+__device__ __forceinline__ int logical_wg(int id, int G) {
+  return (G % 8 == 0) ? (id & 7) * (G / 8) + (id >> 3) : id;
+}
 
-  // Epilogue, one 32-row block-row (i) at a time: the waves park their
-  // accumulator blocks in LDS as [o][a] (o = dout index, 64 a values: 32 from
-  // each wave row), then every thread takes 4 consecutive a of one o -- one
-  // Philox block of noise and one 16-byte store.
+constexpr int kTileElems = kTile * kTile;
+
+// Store one output tile from the accumulator.  part == nullptr: the final
+// result (acc * c_last + noise) / B into p.out.  Otherwise the raw partial
+// acc * c_last into part[256 x 256] (row o - o0, column a - a0), which the
+// fixup kernel sums.  The waves park their accumulator blocks in LDS one
+// 32-row block-row (i) at a time as [o][a] (64 a values: 32 from each wave
+// row); every thread then takes 4 consecutive a of one o -- one Philox block
+// of noise and one 16-byte store.
+__device__ __forceinline__ void store_tile(const LayerArgs& p, const Acc& acc, float c_last, int a0,
+                                           int o0, float* part, unsigned char* smem) {
+  static_assert(256 * (64 + 4) * 4 <= kLdsBytes, "epilogue staging fits in the stage ring");
   const int lane = threadIdx.x & 63;
   const int wm = wave_row(), wn = wave_col();
   const float fB = (float)p.B;
@@ -450,11 +450,15 @@ __global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p) {
 #pragma unroll 1
     for (int e = threadIdx.x; e < 256 * 16; e += kNT) {
       const int ol = e >> 4, a4 = (e & 15) * 4;            // a4 in [0, 64)
-      const int o = o0 + ol;
-      const int a = a0 + (a4 >> 5) * (kBA * 32) + i * 32 + (a4 & 31);
+      const int al = (a4 >> 5) * (kBA * 32) + i * 32 + (a4 & 31);
+      f32x4 v = *(const f32x4*)(park + ol * kParkLd + a4);
+      v.x *= c_last; v.y *= c_last; v.z *= c_last; v.w *= c_last;
+      if (part != nullptr) {
+        *(f32x4*)(part + ol * kTile + al) = v;
+        continue;
+      }
+      const int o = o0 + ol, a = a0 + al;
       if (o < p.dout && a < p.din) {   // din % 8 == 0 on this path: a..a+3 all in range
-        f32x4 v = *(const f32x4*)(park + ol * kParkLd + a4);
-        v.x *= c_last; v.y *= c_last; v.z *= c_last; v.w *= c_last;
         const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
         if (noise) {
           const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
@@ -469,6 +473,89 @@ __global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p) {
   }
 }
 
+// Work plan of one accumulate launch (host-computed).  G persistent
+// workgroups, one per compute unit.  Tiles in grouped raster order; the first
+// D*G tiles go in D full rounds (tile d*G + L to workgroup L).  Each of the R
+// remaining tiles is split into P token chunks (P == 1: not split); piece
+// pi = c*R + r (chunk c of remaining tile r) goes to workgroup pi mod G, so
+// the workgroups running at the same time stream the same token rows and
+// share them in L2.  Pieces store partials; the fixup kernel sums them.
+struct SkPlan {
+  int G, D, R, P;
+  int ntm, ntn;
+};
+
+// Active steps per tile: all of them without a mask, else the list's count.
+__device__ __forceinline__ int active_steps(const LayerArgs& p) {
+  return p.steps != nullptr ? (int)((c_u32*)p.steps)[0] : p.B * ((p.T + kKT - 1) / kKT);
+}
+
+template <bool MASK>
+__device__ __forceinline__ void accumulate_body(const LayerArgs& p, const SkPlan& sk,
+                                                unsigned char* smem) {
+  const int n = active_steps(p);
+  const int L = logical_wg(blockIdx.x, sk.G);
+  Acc acc;
+  auto full_tile = [&](int t) {
+    int tm, tn;
+    raster(t, sk.ntm, sk.ntn, &tm, &tn);
+    const float c_last = run<true, MASK>(p, 0, n, tm * kTile, tn * kTile, acc, smem);
+    store_tile(p, acc, c_last, tm * kTile, tn * kTile, nullptr, smem);
+  };
+  for (int d = 0; d < sk.D; ++d) full_tile(d * sk.G + L);
+  if (sk.P == 1) {
+    if (L < sk.R) full_tile(sk.D * sk.G + L);
+    return;
+  }
+  for (int pi = L; pi < sk.R * sk.P; pi += sk.G) {
+    const int c = pi / sk.R, t = sk.D * sk.G + pi % sk.R;
+    const int k0 = (int)((int64_t)c * n / sk.P), k1 = (int)((int64_t)(c + 1) * n / sk.P);
+    int tm, tn;
+    raster(t, sk.ntm, sk.ntn, &tm, &tn);
+    const float c_last = run<true, MASK>(p, k0, k1 - k0, tm * kTile, tn * kTile, acc, smem);
+    store_tile(p, acc, c_last, tm * kTile, tn * kTile, p.skws + (int64_t)pi * kTileElems, smem);
+  }
+}
+
+__global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p, SkPlan sk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if (p.steps != nullptr) accumulate_body<true>(p, sk, smem);
+  else accumulate_body<false>(p, sk, smem);
+}
+
+// Split tiles: sum their P partials in chunk order, add the noise, divide by
+// B.  One workgroup per (split tile, 64-row quarter).
+constexpr int kFixThreads = 256;
+__global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs p, SkPlan sk) {
+  const int r = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  int tm, tn;
+  raster(sk.D * sk.G + r, sk.ntm, sk.ntn, &tm, &tn);
+  const int a0 = tm * kTile, o0 = tn * kTile;
+  const float fB = (float)p.B;
+  const bool noise = p.noise_std != 0.0f;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const int idx = j * kFixThreads + threadIdx.x;       // [0, 64 * 64)
+    const int ol = quarter * 64 + (idx >> 6), al = (idx & 63) * 4;
+    const int o = o0 + ol, a = a0 + al;
+    if (o >= p.dout || a >= p.din) continue;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < sk.P; ++c) {
+      const float* part = p.skws + (int64_t)(c * sk.R + r) * kTileElems;
+      const f32x4 w = *(const f32x4*)(part + ol * kTile + al);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
+    if (noise) {
+      const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
+      v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
+      v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
+    }
+    v.x = v.x / fB; v.y = v.y / fB; v.z = v.z / fB; v.w = v.w / fB;
+    *(f32x4*)(p.out + e0) = v;
+  }
+}
+
 __global__ void __launch_bounds__(kNT, 1) direct_norm_big_kernel(LayerArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
@@ -478,8 +565,13 @@ __global__ void __launch_bounds__(kNT, 1) direct_norm_big_kernel(LayerArgs p) {
   const int local = blockIdx.x % ntiles;
   const int tm = local % ntm, tn = local / ntm;
   Acc acc;
-  if (p.rowbits != nullptr) run<false, true>(p, b, b + 1, tm * kTile, tn * kTile, acc, smem);
-  else run<false, false>(p, b, b + 1, tm * kTile, tn * kTile, acc, smem);
+  if (p.steps != nullptr) {
+    const int k0 = (int)((c_u32*)p.steps)[1 + b], k1 = (int)((c_u32*)p.steps)[2 + b];
+    run<false, true>(p, k0, k1 - k0, tm * kTile, tn * kTile, acc, smem);
+  } else {
+    const int nsteps = (p.T + kKT - 1) / kKT;
+    run<false, false>(p, b * nsteps, nsteps, tm * kTile, tn * kTile, acc, smem);
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < kBA; ++i)
@@ -507,15 +599,62 @@ int big_tiles(int din, int dout) {
   return ((din + big::kTile - 1) / big::kTile) * ((dout + big::kTile - 1) / big::kTile);
 }
 
+namespace {
+// Pick the split of the last, partial round.  Cost model in microseconds,
+// from measurements on MI355X at the Llama-13B shapes: one 32-token step of a
+// 256 x 256 tile ~0.8 us, a piece's pipeline fill and epilogue ~16 us, the
+// fixup ~10 us plus 0.13 us per partial (256 KiB written, then read) and
+// 0.07 us per split tile (noise and store).
+big::SkPlan plan_accumulate(const LayerArgs& p) {
+  big::SkPlan sk{};
+  sk.ntm = (p.din + big::kTile - 1) / big::kTile;
+  sk.ntn = (p.dout + big::kTile - 1) / big::kTile;
+  const int ntiles = sk.ntm * sk.ntn;
+  const int cus = device_cus();
+  int G = std::min(cus, ntiles * 16);
+  if (G >= 8) G -= G % 8;
+  sk.G = G;
+  sk.D = ntiles / G;
+  sk.R = ntiles - sk.D * G;
+  sk.P = 1;
+  if (sk.R == 0) return sk;
+  const double n = (double)p.B * ((p.T + big::kKT - 1) / big::kKT);   // upper bound if masked
+  const double step_us = 0.8, piece_us = 16.0;
+  double best = n * step_us + piece_us;                                // P = 1: one more round
+  for (int P = 2; P <= 16; ++P) {
+    if (n / P < 16) break;                                             // pieces of >= 16 steps
+    const int S = (sk.R * P + G - 1) / G;
+    const double t = S * (n / P * step_us + piece_us) + 10.0 + 0.13 * sk.R * P + 0.07 * sk.R;
+    if (t < best) {
+      best = t;
+      sk.P = P;
+    }
+  }
+  if (sk.P == 1 && sk.D == 0) sk.G = sk.R;   // one tile per workgroup, no idle ones
+  return sk;
+}
+}  // namespace
+
+size_t accumulate_big_workspace_bytes(const LayerArgs& p) {
+  const big::SkPlan sk = plan_accumulate(p);
+  return sk.P == 1 ? 0 : (size_t)sk.R * sk.P * big::kTileElems * sizeof(float);
+}
+
 hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s) {
   hipError_t e = allow_lds_big<big::accumulate_big_kernel>(big::kLdsBytes);
   if (e != hipSuccess) return e;
-  const int nt = big_tiles(p.din, p.dout);
-  const int grid = 8 * ((nt + 7) / 8);
+  const big::SkPlan sk = plan_accumulate(p);
+  if (sk.P != 1 && p.skws == nullptr) return hipErrorInvalidValue;
   timing_begin("accumulate", s);
-  hipLaunchKernelGGL(big::accumulate_big_kernel, dim3(grid), dim3(big::kNT), big::kLdsBytes, s, p);
+  hipLaunchKernelGGL(big::accumulate_big_kernel, dim3(sk.G), dim3(big::kNT), big::kLdsBytes, s, p, sk);
   e = hipGetLastError();
   timing_end("accumulate", s);
+  if (e != hipSuccess || sk.P == 1) return e;
+  timing_begin("accumulate_fixup", s);
+  hipLaunchKernelGGL(big::accumulate_fixup_kernel, dim3(4 * sk.R), dim3(big::kFixThreads), 0, s, p,
+                     sk);
+  e = hipGetLastError();
+  timing_end("accumulate_fixup", s);
   return e;
 }
 

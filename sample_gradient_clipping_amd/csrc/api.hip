@@ -158,30 +158,64 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
   return L;
 }
 
-// Queue row bits (if masked) + norm partials.  ws offsets must be allocated.
-hipError_t queue_norm_partials(LayerPlan& L, uint32_t* bits, double* partials, hipStream_t s) {
-  L.args.partials = partials;
-  L.args.rowbits = nullptr;
-  if (L.args.mask != nullptr) {
-    hipError_t e = dpf::launch_row_bits(L.args.mask, L.args.B, L.args.T, bits, L.args.nwords, s);
-    if (e != hipSuccess) return e;
-    L.args.rowbits = bits;
+// Workspace pieces of one layer call (offsets into a Workspace).
+struct LayerWs {
+  size_t bits = 0, steps = 0, part = 0, c = 0, sk = 0;
+  bool has_steps = false, has_sk = false;
+};
+
+// Reserve what the call needs: row bits and the active-step list when
+// masked, norm partials, clip factors, split-tile accumulate partials.
+LayerWs reserve_layer(const LayerPlan& L, Workspace& ws, bool norm, bool clip, bool accum) {
+  LayerWs o;
+  const dpf::LayerArgs& a = L.args;
+  if (a.mask != nullptr) {
+    o.bits = ws.reserve((size_t)a.B * a.nwords * sizeof(uint32_t));
+    if (dpf::big_path(a, L.vec)) {
+      o.has_steps = true;
+      o.steps = ws.reserve(dpf::step_list_words(a.B, a.nwords) * sizeof(uint32_t));
+    }
   }
-  return dpf::launch_norm(L.args, L.path, L.vec, s);
+  if (norm) o.part = ws.reserve((size_t)a.B * L.np * sizeof(double));
+  if (clip) o.c = ws.reserve((size_t)a.B * sizeof(float));
+  if (accum) {
+    const size_t bytes = dpf::accumulate_workspace_bytes(a, L.vec);
+    if (bytes != 0) {
+      o.has_sk = true;
+      o.sk = ws.reserve(bytes);
+    }
+  }
+  return o;
+}
+
+// Once the workspace is allocated: point the layer at its pieces and queue
+// the row bits and the active-step list of a masked call.
+hipError_t bind_layer(LayerPlan& L, const Workspace& ws, const LayerWs& o, hipStream_t s) {
+  dpf::LayerArgs& a = L.args;
+  a.rowbits = nullptr;
+  a.steps = o.has_steps ? ws.at<uint32_t>(o.steps) : nullptr;
+  a.skws = o.has_sk ? ws.at<float>(o.sk) : nullptr;
+  if (a.mask == nullptr) return hipSuccess;
+  uint32_t* bits = ws.at<uint32_t>(o.bits);
+  hipError_t e = dpf::launch_row_bits(a.mask, a.B, a.T, bits, a.nwords, s);
+  if (e != hipSuccess) return e;
+  a.rowbits = bits;
+  if (o.has_steps) e = dpf::launch_step_list(bits, a.B, a.nwords, ws.at<uint32_t>(o.steps), s);
+  return e;
 }
 
 dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
                        float sigma, uint64_t seed, uint64_t offset, float* grad_out,
                        float* norms_out, hipStream_t s, Workspace& ws) {
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
-  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
-  const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
+  const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr,
-                                     ws.at<double>(off_part), s);
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.partials = ws.at<double>(o.part);
+  e = dpf::launch_norm(L.args, L.path, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-  float* c = ws.at<float>(off_c);
+  float* c = ws.at<float>(o.c);
   e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "finalize launch");
   L.args.c = c;
@@ -269,9 +303,7 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   // Reserve the layer workspace now so that a single allocation covers both.
   dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
   LayerPlan L = plan_layer(&Y, G, mask);
-  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
-  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
-  const size_t off_c = ws.reserve((size_t)L.args.B * sizeof(float));
+  const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   Y.data = ws.at<void>(off_y);
 
@@ -290,9 +322,12 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
   L = plan_layer(&Y, G, mask);
-  e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr, ws.at<double>(off_part), s);
+  e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.partials = ws.at<double>(o.part);
+  e = dpf::launch_norm(L.args, L.path, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-  float* c = ws.at<float>(off_c);
+  float* c = ws.at<float>(o.c);
   e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "finalize launch");
   L.args.c = c;
@@ -313,11 +348,12 @@ dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace ws(s);
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
-  const size_t off_part = ws.reserve((size_t)L.args.B * L.np * sizeof(double));
+  const LayerWs o = reserve_layer(L, ws, true, false, false);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = queue_norm_partials(L, mask ? ws.at<uint32_t>(off_bits) : nullptr,
-                                     ws.at<double>(off_part), s);
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.partials = ws.at<double>(o.part);
+  e = dpf::launch_norm(L.args, L.path, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
   e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sqnorms_out, accumulate ? 1 : 0, 1.0f,
                            nullptr, nullptr, s);
@@ -350,20 +386,16 @@ dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace ws(s);
   LayerPlan L = plan_layer(X, G, mask);
-  const size_t off_bits = mask ? ws.reserve((size_t)L.args.B * L.args.nwords * sizeof(uint32_t)) : 0;
+  const LayerWs o = reserve_layer(L, ws, false, false, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  if (mask) {
-    hipError_t e = dpf::launch_row_bits(mask, L.args.B, L.args.T, ws.at<uint32_t>(off_bits),
-                                        L.args.nwords, s);
-    if (e != hipSuccess) return hip_fail(e, "row bits launch");
-    L.args.rowbits = ws.at<uint32_t>(off_bits);
-  }
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
   L.args.c = c;
   L.args.noise_std = noise_std;
   L.args.seed = seed;
   L.args.offset = offset;
   L.args.out = grad_out;
-  hipError_t e = dpf::launch_accumulate(L.args, L.vec, s);
+  e = dpf::launch_accumulate(L.args, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
 }

@@ -542,11 +542,18 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
 // including the rows of the last (partial) tile past T, which must land past
 // the end of the sample's buffer range rather than wrap around into it: the
 // padded span must stay below 2 GiB.
+// Active-step entries pack the sample and the step into 16 bits each.
 static bool use_big(const LayerArgs& p, bool vec) {
   const int64_t lim = (int64_t)1 << 30;   // elements: 2 GiB of bf16
   const int64_t Tp = ((int64_t)p.T + 255) / 256 * 256;
   return p.dtype == kBF16 && vec && Tp * p.X.stride_t + p.din < lim &&
-         Tp * p.G.stride_t + p.dout < lim;
+         Tp * p.G.stride_t + p.dout < lim && p.B < 65536 && p.nwords < 65536;
+}
+
+bool big_path(const LayerArgs& p, bool vec) { return use_big(p, vec); }
+
+size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec) {
+  return use_big(p, vec) ? accumulate_big_workspace_bytes(p) : 0;
 }
 
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {

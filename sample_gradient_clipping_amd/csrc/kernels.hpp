@@ -26,7 +26,16 @@ struct LayerArgs {
   uint64_t seed, offset;
   float* out;               // [dout, din]
   double* partials;         // [B, norm_partials_per_sample] (norm kernels)
+  const uint32_t* steps;    // active-step list (large-tile kernels, masked calls) or null
+  float* skws;              // split-tile partials of the accumulate kernel, or null
 };
+
+// Active-step list of a masked call, built from the row bits:
+//   steps[0]          n, the number of (sample, 32-token step) pairs with an active token
+//   steps[1 + b]      index of sample b's first entry (b = 0..B; steps[1 + B] = n)
+//   steps[2 + B + k]  entry k = sample << 16 | step, sample-major (k < n), then one
+//                     spare zero entry, so that reading entry n stays in bounds.
+inline size_t step_list_words(int B, int nwords) { return (size_t)B * nwords + B + 3; }
 
 struct ProjArgs {
   Act X;                    // [B, T, din]
@@ -39,6 +48,12 @@ struct ProjArgs {
 
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the
 // caller has checked alignment of every pointer, dimension and stride.
+// True when (p, vec) runs on the large-tile bf16 kernels; a masked call on
+// them needs the active-step list (p.steps).
+bool big_path(const LayerArgs& p, bool vec);
+// Device workspace bytes launch_accumulate needs for (p, vec), passed in as
+// p.skws (0: none).
+size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec);
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
@@ -47,6 +62,7 @@ int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec);
 
 // Large-tile bf16 kernels (accum_big.hip).
 int big_tiles(int din, int dout);
+size_t accumulate_big_workspace_bytes(const LayerArgs& p);
 hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
 
@@ -57,6 +73,9 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s);
 // Small kernels (misc_kernels.hip).
 hipError_t launch_row_bits(const uint8_t* mask, int B, int T, uint32_t* bits, int nwords,
                            hipStream_t s);
+hipError_t launch_step_list(const uint32_t* bits, int B, int nwords, uint32_t* steps, hipStream_t s);
+// Compute units of the current device (cached per device).
+int device_cus();
 // Per sample: sq = ordered sum of np partials; optionally added into sq_io;
 // then c = clip factor and norms = sqrt(sq) when c_out is given.
 hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,

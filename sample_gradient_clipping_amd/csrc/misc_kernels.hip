@@ -1,4 +1,6 @@
 // Small kernels: Philox/Gaussian fills, mask tile flags, ordered finalize.
+#include <atomic>
+
 #include "kernels.hpp"
 
 namespace dpf {
@@ -53,6 +55,45 @@ __global__ void row_bits_kernel(const uint8_t* mask, int B, int T, uint32_t* bit
   }
   const uint64_t ball = __ballot(a);
   if (wi < total && (lane & 31) == 0) bits[wi] = (uint32_t)(ball >> (lane & 32));
+}
+
+// Active-step list (layout in kernels.hpp) from the row bits: one workgroup
+// walks the words in order, 1024 at a time; an entry's index is the number
+// of active words before it (ballot counts within a wave, then wave totals).
+constexpr int kListThreads = 1024;
+__global__ void __launch_bounds__(kListThreads) step_list_kernel(const uint32_t* bits, int B,
+                                                                 int nwords, uint32_t* steps) {
+  __shared__ uint32_t wave_count[kListThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t total = (int64_t)B * nwords;
+  uint32_t* entries = steps + 2 + B;
+  uint32_t base = 0;                  // active words before this chunk (same in every thread)
+  for (int64_t c0 = 0; c0 < total; c0 += kListThreads) {
+    const int64_t i = c0 + tid;
+    const bool act = i < total && bits[i] != 0u;
+    const uint64_t ball = __ballot(act);
+    const uint32_t below = (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_count[wave] = (uint32_t)__popcll(ball);
+    __syncthreads();
+    uint32_t before = 0, chunk = 0;
+    for (int w = 0; w < kListThreads / 64; ++w) {
+      if (w < wave) before += wave_count[w];
+      chunk += wave_count[w];
+    }
+    const uint32_t idx = base + before + below;
+    if (i < total) {
+      const int b = (int)(i / nwords), w = (int)(i % nwords);
+      if (w == 0) steps[1 + b] = idx;
+      if (act) entries[idx] = ((uint32_t)b << 16) | (uint32_t)w;
+    }
+    base += chunk;
+    __syncthreads();                  // wave_count is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    steps[0] = base;
+    steps[1 + B] = base;
+    entries[base] = 0u;               // spare entry
+  }
 }
 
 __device__ __forceinline__ void clip_of_sq(double sq, float C, float* c, float* n) {
@@ -123,6 +164,27 @@ hipError_t launch_row_bits(const uint8_t* mask, int B, int T, uint32_t* bits, in
                      bits, nwords);
   timing_end("row_bits", s);
   return hipGetLastError();
+}
+
+hipError_t launch_step_list(const uint32_t* bits, int B, int nwords, uint32_t* steps,
+                            hipStream_t s) {
+  timing_begin("step_list", s);
+  hipLaunchKernelGGL(step_list_kernel, dim3(1), dim3(kListThreads), 0, s, bits, B, nwords, steps);
+  timing_end("step_list", s);
+  return hipGetLastError();
+}
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  int n = cache[dev].load();
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    cache[dev].store(n);
+  }
+  return n;
 }
 
 hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,
