@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -178,12 +179,12 @@ LayerWs reserve_layer(const LayerPlan& L, Workspace& ws, bool norm, bool clip, b
   }
   if (norm) o.part = ws.reserve((size_t)a.B * L.np * sizeof(double));
   if (clip) o.c = ws.reserve((size_t)a.B * sizeof(float));
-  if (accum) {
-    const size_t bytes = dpf::accumulate_workspace_bytes(a, L.vec);
-    if (bytes != 0) {
-      o.has_sk = true;
-      o.sk = ws.reserve(bytes);
-    }
+  size_t bytes = 0;   // split-piece partials; the norm and accumulate phases share them
+  if (norm) bytes = dpf::norm_workspace_bytes(a, L.path, L.vec);
+  if (accum) bytes = std::max(bytes, dpf::accumulate_workspace_bytes(a, L.vec));
+  if (bytes != 0) {
+    o.has_sk = true;
+    o.sk = ws.reserve(bytes);
   }
   return o;
 }

@@ -556,6 +556,10 @@ size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec) {
   return use_big(p, vec) ? accumulate_big_workspace_bytes(p) : 0;
 }
 
+size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec) {
+  return (path == NormPath::kGram && use_big(p, vec)) ? gram_big_workspace_bytes(p) : 0;
+}
+
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
   if (path == NormPath::kGram && use_big(p, vec)) return gram_big_items_per_sample(p.T);
   if (path == NormPath::kGram) {

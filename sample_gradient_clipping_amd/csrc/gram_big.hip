@@ -20,6 +20,8 @@
 // chunk c of row r stored at c ^ ((r >> 1) & 7), which keeps both the DMA
 // writes and the fragment reads free of bank conflicts.  Masked tokens and
 // rows past T read through out-of-range buffer offsets (zeros).
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -164,17 +166,9 @@ struct Acc2 {
   }
 };
 
-// Work item of workgroup `id`.  Workgroups are dealt to the 8 XCDs round
-// robin, so XCD x gets the contiguous item range [x*per, (x+1)*per): items
-// of one sample and row block S (sharing their s-rows) meet in one L2.
-// Item L = b * per_sample + (index of (S, Tb) within the sample).
-__device__ __forceinline__ bool item_of(int id, int per_sample, int B, int T, int* L_out, int* b,
-                                        int* S, int* Tb) {
-  const int total = B * per_sample;
-  const int per = (total + 7) / 8;
-  const int L = (id & 7) * per + (id >> 3);
-  if (L >= total) return false;
-  *L_out = L;
+// Sample, row block S and column block Tb of item L (L = b * per_sample +
+// index of (S, Tb) within the sample, S-major).
+__device__ __forceinline__ void item_coords(int L, int per_sample, int T, int* b, int* S, int* Tb) {
   *b = L / per_sample;
   int r = L % per_sample;
   const int nTb = (T + kRowsT - 1) / kRowsT;
@@ -182,16 +176,21 @@ __device__ __forceinline__ bool item_of(int id, int per_sample, int B, int T, in
   while (r >= nTb - 2 * s) { r -= nTb - 2 * s; ++s; }
   *S = s;
   *Tb = 2 * s + r;
-  return true;
 }
 
-__global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int per_sample = items_per_sample(p.T);
-  int L, b, S, Tb;
-  if (!item_of(blockIdx.x, per_sample, p.B, p.T, &L, &b, &S, &Tb)) return;
-  const int nkx = (p.din + kKF - 1) / kKF, nkg = (p.dout + kKF - 1) / kKF;
-  const int n = nkx + nkg;
+// Workgroups are dealt to the 8 XCDs round robin; logical index of this
+// workgroup such that XCD x holds the contiguous range [x*G/8, (x+1)*G/8):
+// consecutive items (same sample, shared rows) meet in one L2.
+__device__ __forceinline__ int logical_wg(int id, int G) {
+  return (G % 8 == 0) ? (id & 7) * (G / 8) + (id >> 3) : id;
+}
+
+// Feature steps [k0, k1) of item (b, S, Tb) into ax (steps < nkx: X Gram)
+// and ag (the rest: G Gram).
+__device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int Tb, int k0, int k1,
+                                         Acc2& ax, Acc2& ag, unsigned char* smem) {
+  const int nkx = (p.din + kKF - 1) / kKF;
+  const int n = k1 - k0;
   const __amdgpu_buffer_rsrc_t rx = sample_rsrc(p.X, b, p.T, p.din);
   const __amdgpu_buffer_rsrc_t rg = sample_rsrc(p.G, b, p.T, p.dout);
   DmaLane dl;
@@ -199,31 +198,35 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p) {
   const uint32_t base = lds_addr(smem);
 #pragma unroll
   for (int k = 0; k < kStages; ++k)
-    if (k < n) issue_step(p, dl, rx, rg, k, nkx, base + k * kSlotBytes);
-
-  Acc2 ax, ag;
+    if (k < n) issue_step(p, dl, rx, rg, k0 + k, nkx, base + k * kSlotBytes);
   ax.zero();
   ag.zero();
   int slot = 0;
   // One pipelined step: wait for step i, refill the drained slot, compute.
-  // Issued so far: steps 0..2 before the loop, then step j+2 in iteration
-  // j >= 1.
+  // Issued so far: steps 0..2 (relative) before the loop, then step j+2 in
+  // iteration j >= 1.
   auto step = [&](int i, Acc2& acc) {
     wait_dma(i == 0 ? min(kStages - 1, n - 1) : min(kStages - 2, n - 1 - i));
     __syncthreads();
     if (i >= 1 && i + kStages - 1 < n) {
       const int prev = (slot == 0) ? kStages - 1 : slot - 1;
-      issue_step(p, dl, rx, rg, i + kStages - 1, nkx, base + prev * kSlotBytes);
+      issue_step(p, dl, rx, rg, k0 + i + kStages - 1, nkx, base + prev * kSlotBytes);
     }
     acc.step(smem + slot * kSlotBytes);
     acc.pin();
     slot = (slot + 1 == kStages) ? 0 : slot + 1;
   };
+  const int nx = max(0, min(k1, nkx) - k0);   // X steps of this range
   int i = 0;
-  for (; i < nkx; ++i) step(i, ax);   // X Gram, K = din
-  for (; i < n; ++i) step(i, ag);     // G Gram, K = dout
+  for (; i < nx; ++i) step(i, ax);   // X Gram, K = din
+  for (; i < n; ++i) step(i, ag);    // G Gram, K = dout
+  __syncthreads();                   // every wave is done with the slot ring
+}
 
-  // Weighted elementwise product.  Rows past T and masked rows are zero.
+// Weighted sum of ax .* ag over this thread's elements of item (S, Tb):
+// weight 2 above the diagonal (s < t), 1 on it, 0 below.  Rows past T and
+// masked rows are zero in both Grams.
+__device__ __forceinline__ float weighted_product(const Acc2& ax, const Acc2& ag, int S, int Tb) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / kWaveCols, wn = wave % kWaveCols;
   const bool above = kRowsT * Tb >= kRowsS * (S + 1);   // whole tile has s < t
@@ -243,27 +246,166 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p) {
           sum += (s < t) ? 2.0f * prod : ((s == t) ? prod : 0.0f);
         }
       }
-  __syncthreads();   // the slot ring is free: reuse it for the reduction
-  const double tot = block_sum_f64((double)sum, (double*)smem);
-  if (threadIdx.x == 0) p.partials[L] = tot;
+  return sum;
+}
+
+// Work plan (host-computed): G persistent workgroups; the first D*G items in
+// D full rounds (item d*G + L to workgroup L); each of the R remaining items
+// split into P chunks of its feature steps (P == 1: not split), piece
+// pi = c*R + r going to workgroup pi mod G.  A piece stores its partial
+// Grams; the fixup kernel finishes split items.
+struct GramPlan {
+  int G, D, R, P;
+};
+
+// A piece's partial Grams: 128 floats per thread (64 of X, then 64 of G),
+// stored as f32x4 q of thread tid at [q][tid] so that stores and loads of
+// consecutive threads are contiguous.
+constexpr int kPieceFloats = 128 * kNT;
+
+__device__ __forceinline__ void store_piece(float* dst, const Acc2& ax, const Acc2& ag) {
+  f32x4* d = (f32x4*)dst;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int x = (i * 2 + j) * 4 + q;
+        f32x4 v;
+        v.x = ax.v[i][j][4 * q]; v.y = ax.v[i][j][4 * q + 1];
+        v.z = ax.v[i][j][4 * q + 2]; v.w = ax.v[i][j][4 * q + 3];
+        d[x * kNT + threadIdx.x] = v;
+        v.x = ag.v[i][j][4 * q]; v.y = ag.v[i][j][4 * q + 1];
+        v.z = ag.v[i][j][4 * q + 2]; v.w = ag.v[i][j][4 * q + 3];
+        d[(16 + x) * kNT + threadIdx.x] = v;
+      }
+}
+
+__device__ __forceinline__ void add_piece(const float* src, Acc2& ax, Acc2& ag) {
+  const f32x4* d = (const f32x4*)src;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int x = (i * 2 + j) * 4 + q;
+        const f32x4 u = d[x * kNT + threadIdx.x], w = d[(16 + x) * kNT + threadIdx.x];
+        ax.v[i][j][4 * q] += u.x; ax.v[i][j][4 * q + 1] += u.y;
+        ax.v[i][j][4 * q + 2] += u.z; ax.v[i][j][4 * q + 3] += u.w;
+        ag.v[i][j][4 * q] += w.x; ag.v[i][j][4 * q + 1] += w.y;
+        ag.v[i][j][4 * q + 2] += w.z; ag.v[i][j][4 * q + 3] += w.w;
+      }
+}
+
+__global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, GramPlan gp,
+                                                               float* ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int per_sample = items_per_sample(p.T);
+  const int n = (p.din + kKF - 1) / kKF + (p.dout + kKF - 1) / kKF;
+  const int L = logical_wg(blockIdx.x, gp.G);
+  Acc2 ax, ag;
+  auto full_item = [&](int item) {
+    int b, S, Tb;
+    item_coords(item, per_sample, p.T, &b, &S, &Tb);
+    run_item(p, b, S, Tb, 0, n, ax, ag, smem);
+    const double tot = block_sum_f64((double)weighted_product(ax, ag, S, Tb), (double*)smem);
+    if (threadIdx.x == 0) p.partials[item] = tot;
+    __syncthreads();                 // the reduction scratch is the next item's ring
+  };
+  for (int d = 0; d < gp.D; ++d) full_item(d * gp.G + L);
+  if (gp.P == 1) {
+    if (L < gp.R) full_item(gp.D * gp.G + L);
+    return;
+  }
+  for (int pi = L; pi < gp.R * gp.P; pi += gp.G) {
+    const int c = pi / gp.R, item = gp.D * gp.G + pi % gp.R;
+    int b, S, Tb;
+    item_coords(item, per_sample, p.T, &b, &S, &Tb);
+    run_item(p, b, S, Tb, (int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), ax, ag,
+             smem);
+    store_piece(ws + (int64_t)pi * kPieceFloats, ax, ag);
+  }
+}
+
+// Split items: sum the P partial Grams in chunk order, then the weighted
+// product and its reduction, as for a whole item.  One workgroup per item,
+// with the main kernel's thread layout.
+__global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPlan gp,
+                                                            const float* ws) {
+  __shared__ double red[kNT / 64];
+  const int r = blockIdx.x, item = gp.D * gp.G + r;
+  int b, S, Tb;
+  item_coords(item, items_per_sample(p.T), p.T, &b, &S, &Tb);
+  Acc2 ax, ag;
+  ax.zero();
+  ag.zero();
+  for (int c = 0; c < gp.P; ++c) add_piece(ws + (int64_t)(c * gp.R + r) * kPieceFloats, ax, ag);
+  const double tot = block_sum_f64((double)weighted_product(ax, ag, S, Tb), red);
+  if (threadIdx.x == 0) p.partials[item] = tot;
 }
 
 }  // namespace gram
 
 int gram_big_items_per_sample(int T) { return gram::items_per_sample(T); }
 
+namespace {
+// Split of the last, partial round: same cost model as the accumulate
+// kernel's (a 64-feature step of a 256 x 128 item ~0.8 us; a piece's fill
+// and partial store ~10 us; the fixup ~10 us plus 0.13 us per piece).
+gram::GramPlan plan_gram(const LayerArgs& p) {
+  gram::GramPlan gp{};
+  const int items = p.B * gram::items_per_sample(p.T);
+  const int cus = device_cus();
+  int G = std::min(cus, items * 16);
+  if (G >= 8) G -= G % 8;
+  gp.G = G;
+  gp.D = items / G;
+  gp.R = items - gp.D * G;
+  gp.P = 1;
+  if (gp.R != 0) {
+    const double n = (p.din + gram::kKF - 1) / gram::kKF + (p.dout + gram::kKF - 1) / gram::kKF;
+    const double step_us = 0.8, piece_us = 10.0;
+    double best = n * step_us + piece_us;
+    for (int P = 2; P <= 16; ++P) {
+      if (n / P < 8) break;
+      const int S = (gp.R * P + G - 1) / G;
+      const double t = S * (n / P * step_us + piece_us) + 10.0 + 0.13 * gp.R * P;
+      if (t < best) {
+        best = t;
+        gp.P = P;
+      }
+    }
+  }
+  if (gp.P == 1 && gp.D == 0) gp.G = gp.R;
+  return gp;
+}
+}  // namespace
+
+size_t gram_big_workspace_bytes(const LayerArgs& p) {
+  const gram::GramPlan gp = plan_gram(p);
+  return gp.P == 1 ? 0 : (size_t)gp.R * gp.P * gram::kPieceFloats * sizeof(float);
+}
+
 hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   static hipError_t once = hipFuncSetAttribute((const void*)gram::gram_norm_big_kernel,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                gram::kLdsBytes);
   if (once != hipSuccess) return once;
-  const int total = p.B * gram::items_per_sample(p.T);
-  const int grid = 8 * ((total + 7) / 8);
+  const gram::GramPlan gp = plan_gram(p);
+  if (gp.P != 1 && p.skws == nullptr) return hipErrorInvalidValue;
   timing_begin("gram_norm", s);
-  hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(grid), dim3(gram::kNT), gram::kLdsBytes, s,
-                     p);
+  hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(gp.G), dim3(gram::kNT), gram::kLdsBytes, s, p,
+                     gp, p.skws);
   hipError_t e = hipGetLastError();
   timing_end("gram_norm", s);
+  if (e != hipSuccess || gp.P == 1) return e;
+  timing_begin("gram_fixup", s);
+  hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(gp.R), dim3(gram::kNT), 0, s, p, gp,
+                     (const float*)p.skws);
+  e = hipGetLastError();
+  timing_end("gram_fixup", s);
   return e;
 }
 

@@ -27,7 +27,7 @@ struct LayerArgs {
   float* out;               // [dout, din]
   double* partials;         // [B, norm_partials_per_sample] (norm kernels)
   const uint32_t* steps;    // active-step list (large-tile kernels, masked calls) or null
-  float* skws;              // split-tile partials of the accumulate kernel, or null
+  float* skws;              // partials of split tiles / items (large-tile kernels), or null
 };
 
 // Active-step list of a masked call, built from the row bits:
@@ -51,9 +51,11 @@ struct ProjArgs {
 // True when (p, vec) runs on the large-tile bf16 kernels; a masked call on
 // them needs the active-step list (p.steps).
 bool big_path(const LayerArgs& p, bool vec);
-// Device workspace bytes launch_accumulate needs for (p, vec), passed in as
-// p.skws (0: none).
+// Device workspace bytes launch_accumulate / launch_norm need for (p, vec),
+// passed in as p.skws (0: none).  The two phases run one after the other on
+// one stream and may share the buffer.
 size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec);
+size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec);
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
@@ -68,6 +70,7 @@ hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
 
 // Large-tile bf16 Gram-norm kernel (gram_big.hip).
 int gram_big_items_per_sample(int T);
+size_t gram_big_workspace_bytes(const LayerArgs& p);
 hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s);
 
 // Small kernels (misc_kernels.hip).
