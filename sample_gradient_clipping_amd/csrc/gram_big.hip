@@ -105,22 +105,46 @@ struct DmaLane {
   }
 };
 
-// Queue feature step `step` (X features for step < nkx, else G features).
-__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl,
-                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
-                                           int step, int nkx, uint32_t slot) {
+// Queue DMA j of feature step `step` (X features for step < nkx, else G
+// features) into the slot at LDS address `slot`.
+__device__ __forceinline__ void issue_dma(const LayerArgs& p, const DmaLane& dl,
+                                          __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
+                                          int step, int nkx, uint32_t slot, int j) {
   const int wave = threadIdx.x >> 6;
   const bool xs = step < nkx;
   const int k0 = (xs ? step : step - nkx) * kKF;
   const int D = xs ? p.din : p.dout;
-#pragma unroll
-  for (int j = 0; j < kDmaPerStep; ++j) {
-    const uint32_t base = xs ? dl.xoff[j] : dl.goff[j];
-    const int off = (k0 + dl.cfeat[j] < D) ? (int)(base + (uint32_t)k0 * 2) : kOOB;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (kDmaPerStep * wave + j) * 1024);
-    dma16(xs ? rx : rg, off, dst);
-  }
+  const uint32_t base = xs ? dl.xoff[j] : dl.goff[j];
+  const int off = (k0 + dl.cfeat[j] < D) ? (int)(base + (uint32_t)k0 * 2) : kOOB;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (kDmaPerStep * wave + j) * 1024);
+  dma16(xs ? rx : rg, off, dst);
 }
+
+__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl,
+                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
+                                           int step, int nkx, uint32_t slot) {
+#pragma unroll
+  for (int j = 0; j < kDmaPerStep; ++j) issue_dma(p, dl, rx, rg, step, nkx, slot, j);
+}
+
+// All of this wave's LDS reads have returned.  Issued as the compiler's own
+// wait instruction, so that its bookkeeping of outstanding LDS reads restarts
+// from zero.
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+}
+
+// Workgroup barrier without a memory fence: each wave has seen its LDS reads
+// return (lds_reads_done) and its DMA writes land (wait_dma) before it.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Nothing is scheduled across this point: it fixes the interleaving of
+// MFMAs with LDS reads and DMA issue that the main loop spells out.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // MFMA operand for rows m0..m0+31 of a region, 16-feature substep ks.
 __device__ __forceinline__ u16x8 frag(const unsigned char* region, int m0, int ks) {
@@ -148,23 +172,19 @@ struct Acc2 {
 #pragma unroll
       for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(v[i][j]));
   }
-  __device__ __forceinline__ void step(const unsigned char* slot) {
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave / kWaveCols, wn = wave % kWaveCols;
-#pragma unroll
-    for (int ks = 0; ks < kKF / 16; ++ks) {
-      u16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = frag(slot, wm * 64 + i * 32, ks);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = frag(slot + kSBytes, wn * 64 + j * 32, ks);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) v[i][j] = mfma_32x32x16(a[i], b[j], v[i][j]);
-    }
+  // MFMA k of a 16-feature substep: block (k / 2, k % 2).
+  __device__ __forceinline__ void mma1(const u16x8 (&f)[4], int k) {
+    v[k >> 1][k & 1] = mfma_32x32x16(f[k >> 1], f[2 + (k & 1)], v[k >> 1][k & 1]);
   }
 };
+
+// Fragment q of 16-feature substep ks of this wave: q = 0, 1 the s blocks
+// (rows wm*64 + 32q), q = 2, 3 the t blocks (rows wn*64 + 32(q-2)).
+__device__ __forceinline__ void read_frag(u16x8 (&f)[4], const unsigned char* slot, int ks, int q) {
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / kWaveCols, wn = wave % kWaveCols;
+  f[q] = q < 2 ? frag(slot, wm * 64 + q * 32, ks) : frag(slot + kSBytes, wn * 64 + (q - 2) * 32, ks);
+}
 
 // Sample, row block S and column block Tb of item L (L = b * per_sample +
 // index of (S, Tb) within the sample, S-major).
@@ -187,8 +207,17 @@ __device__ __forceinline__ int logical_wg(int id, int G) {
 
 // Feature steps [k0, k1) of item (b, S, Tb) into ax (steps < nkx: X Gram)
 // and ag (the rest: G Gram).
+//
+// Three 48 KiB slots of 64 features = four 16-feature substeps.  Fragments
+// are double-buffered: the MFMAs of one substep run on registers while the
+// next substep's fragments are read, one read between consecutive MFMAs.
+// Barrier i comes before the last substep of step i: it certifies that step
+// i+1 has landed for every wave and that every wave has read all of step i,
+// whose slot is then refilled with step i+3 (its DMAs interleaved with the
+// last substep's MFMAs), leaving two steps in flight.
 __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int Tb, int k0, int k1,
                                          Acc2& ax, Acc2& ag, unsigned char* smem) {
+  static_assert(kKF / 16 == 4 && kDmaPerStep == 6, "the interleave encodes 4 substeps, 6 DMAs");
   const int nkx = (p.din + kKF - 1) / kKF;
   const int n = k1 - k0;
   const __amdgpu_buffer_rsrc_t rx = sample_rsrc(p.X, b, p.T, p.din);
@@ -201,25 +230,74 @@ __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int T
     if (k < n) issue_step(p, dl, rx, rg, k0 + k, nkx, base + k * kSlotBytes);
   ax.zero();
   ag.zero();
+  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
+  step_barrier();
+  u16x8 f0[4], f1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) read_frag(f0, smem, 0, (q == 1) ? 2 : (q == 2) ? 3 : (q == 3) ? 1 : 0);
   int slot = 0;
-  // One pipelined step: wait for step i, refill the drained slot, compute.
-  // Issued so far: steps 0..2 (relative) before the loop, then step j+2 in
-  // iteration j >= 1.
-  auto step = [&](int i, Acc2& acc) {
-    wait_dma(i == 0 ? min(kStages - 1, n - 1) : min(kStages - 2, n - 1 - i));
-    __syncthreads();
-    if (i >= 1 && i + kStages - 1 < n) {
-      const int prev = (slot == 0) ? kStages - 1 : slot - 1;
-      issue_step(p, dl, rx, rg, k0 + i + kStages - 1, nkx, base + prev * kSlotBytes);
+  // Fragments in the order the MFMAs first need them: s block 0, t blocks
+  // 0 and 1, s block 1; two reads before a substep's first MFMA (the
+  // previous substep released their registers) and two after it.
+  constexpr int kNeed[4] = {0, 2, 3, 1};
+  auto substep = [&](Acc2& acc, const u16x8 (&f)[4], u16x8 (&g)[4], const unsigned char* st,
+                     int ks) {
+    read_frag(g, st, ks, kNeed[0]);
+    read_frag(g, st, ks, kNeed[1]);
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc.mma1(f, k);
+      sched_fence();
+      if (k == 0) {
+        read_frag(g, st, ks, kNeed[2]);
+        read_frag(g, st, ks, kNeed[3]);
+      }
+      sched_fence();
     }
-    acc.step(smem + slot * kSlotBytes);
-    acc.pin();
-    slot = (slot + 1 == kStages) ? 0 : slot + 1;
+  };
+  auto body = [&](int i, Acc2& acc) {
+    const unsigned char* st = smem + slot * kSlotBytes;
+    sched_fence();
+    substep(acc, f0, f1, st, 1);             // substep 0 on f0, read substep 1
+    substep(acc, f1, f0, st, 2);             // substep 1 on f1, read substep 2
+    substep(acc, f0, f1, st, 3);             // substep 2 on f0, read substep 3
+    lds_reads_done();                        // all of step i is in registers
+    const int next = (slot + 1 == kStages) ? 0 : slot + 1;
+    if (i + 1 < n) {
+      // Issued so far: steps 0..2 before the loop, then step j+3 at barrier
+      // j < i, i.e. up to i+2.  Wait for step i+1.
+      wait_dma(min(n - 1, i + kStages - 1) - (i + 1));
+      step_barrier();
+    }
+    const bool refill = i + kStages < n;
+    const uint32_t dst = base + slot * kSlotBytes;
+    const unsigned char* sn = smem + next * kSlotBytes;
+    // substep 3 on f1, reads of step i+1 (stale on the last step, never
+    // used), DMA of step i+3
+    read_frag(f0, sn, 0, kNeed[0]);
+    read_frag(f0, sn, 0, kNeed[1]);
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc.mma1(f1, k);
+      sched_fence();
+      if (k == 0) {
+        read_frag(f0, sn, 0, kNeed[2]);
+        read_frag(f0, sn, 0, kNeed[3]);
+      }
+      if (k >= 1 && refill) {
+        issue_dma(p, dl, rx, rg, k0 + i + kStages, nkx, dst, 2 * (k - 1));
+        issue_dma(p, dl, rx, rg, k0 + i + kStages, nkx, dst, 2 * (k - 1) + 1);
+      }
+      sched_fence();
+    }
+    slot = next;
   };
   const int nx = max(0, min(k1, nkx) - k0);   // X steps of this range
   int i = 0;
-  for (; i < nx; ++i) step(i, ax);   // X Gram, K = din
-  for (; i < n; ++i) step(i, ag);    // G Gram, K = dout
+  for (; i < nx; ++i) body(i, ax);   // X Gram, K = din
+  for (; i < n; ++i) body(i, ag);    // G Gram, K = dout
   __syncthreads();                   // every wave is done with the slot ring
 }
 
