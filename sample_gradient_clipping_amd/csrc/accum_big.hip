@@ -114,52 +114,88 @@ struct DmaLane {
   }
 };
 
-// Buffer descriptors of one sample's X and G rows, rebuilt only when the
-// issuing cursor moves to another sample.
-struct SampleRsrc {
+// Issue side of the pipeline: the next step to queue, with the buffer
+// descriptors of its sample (rebuilt only when the sample changes) and the
+// byte offsets of its first token row in X and G.  Without a mask, steps
+// run through every sample in order and the offsets advance by constant
+// increments; with one, the active-step list gives each step.
+template <bool MASK>
+struct Issue {
   __amdgpu_buffer_rsrc_t rx, rg;
-  int b = -1;
-  __device__ __forceinline__ void at(const LayerArgs& p, int nb) {
+  int b, s, k, nsteps;
+  uint32_t xs, gs, dx, dg;     // byte offsets of the step; per-step increments
+  const uint32_t* list;
+  __device__ __forceinline__ void rsrc(const LayerArgs& p) {
+    rx = sample_rsrc(p.X, b, p.T, p.din);
+    rg = sample_rsrc(p.G, b, p.T, p.dout);
+  }
+  __device__ __forceinline__ void load(const LayerArgs& p) {
+    const uint32_t v = ((c_u32*)list)[k];
+    const int nb = (int)(v >> 16);
+    s = (int)(v & 0xffffu);
+    xs = (uint32_t)s * dx;     // < 2^31: span checked on the host
+    gs = (uint32_t)s * dg;
     if (nb != b) {
-      rx = sample_rsrc(p.X, nb, p.T, p.din);
-      rg = sample_rsrc(p.G, nb, p.T, p.dout);
       b = nb;
+      rsrc(p);
     }
   }
-};
-
-// Queue DMA pair j of step (b, s) into the LDS slot at `stage`: rows
-// 4 wave + 2 j + {0, 1} of X[tokens, a0:a0+256] and G[tokens, o0:o0+256].
-// With a mask, inactive rows read through out-of-range offsets.  Without
-// one, the rows past T of a tail step are already past the end of the
-// sample's buffer descriptor (row stride >= row length), so they read zeros
-// as they are.
-template <bool MASK>
-__device__ __forceinline__ void issue_pair(const LayerArgs& p, const DmaLane& dl, SampleRsrc& sr,
-                                           int b, int s, uint32_t stage, int j) {
-  sr.at(p, b);
-  const uint32_t t0 = (uint32_t)(s * kKT);
-  const uint32_t xs = t0 * (uint32_t)p.X.stride_t * 2u;   // < 2^31: span checked on the host
-  const uint32_t gs = t0 * (uint32_t)p.G.stride_t * 2u;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (kRowsPerWave * wave + 2 * j) * kRowBytes);
-  if constexpr (MASK) {
-    const uint32_t mine = step_bits<MASK>(p, b, s) >> (kRowsPerWave * wave);
-    const bool act = (mine >> (2 * j + (lane >> 5))) & 1u;
-    dma16(sr.rx, act ? (int)(dl.xoff[j] + xs) : kOOB, dst);
-    dma16(sr.rg, act ? (int)(dl.goff[j] + gs) : kOOB, dst + kOpBytes);
-  } else {
-    dma16(sr.rx, (int)(dl.xoff[j] + xs), dst);
-    dma16(sr.rg, (int)(dl.goff[j] + gs), dst + kOpBytes);
+  __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
+    nsteps = (p.T + kKT - 1) / kKT;
+    dx = (uint32_t)kKT * (uint32_t)p.X.stride_t * 2u;
+    dg = (uint32_t)kKT * (uint32_t)p.G.stride_t * 2u;
+    k = k0;
+    if constexpr (MASK) {
+      list = p.steps + 2 + p.B;
+      b = -1;
+      load(p);
+    } else {
+      b = k0 / nsteps;
+      s = k0 - b * nsteps;
+      xs = (uint32_t)s * dx;
+      gs = (uint32_t)s * dg;
+      rsrc(p);
+    }
   }
-}
-
-template <bool MASK>
-__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl, SampleRsrc& sr,
-                                           int b, int s, uint32_t stage) {
+  // Only called while another step remains, so b stays a valid sample.
+  __device__ __forceinline__ void advance(const LayerArgs& p) {
+    ++k;
+    if constexpr (MASK) {
+      load(p);
+    } else if (++s == nsteps) {
+      s = 0;
+      xs = gs = 0u;
+      ++b;
+      rsrc(p);
+    } else {
+      xs += dx;
+      gs += dg;
+    }
+  }
+  // DMA `d` (0..3) of this step into the slot at LDS address `stage`: pair
+  // d / 2 (rows 4 wave + 2 (d / 2) + {0, 1}) of X (d even) or G (d odd).
+  // With a mask, inactive rows read through out-of-range offsets.  Without
+  // one, the rows past T of a tail step are already past the end of the
+  // sample's buffer descriptor (row stride >= row length), so they read
+  // zeros as they are.
+  __device__ __forceinline__ void dma(const LayerArgs& p, const DmaLane& dl, uint32_t stage,
+                                      int d) const {
+    const int j = d >> 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        stage + (kRowsPerWave * wave + 2 * j) * kRowBytes + (d & 1) * kOpBytes);
+    uint32_t off = (d & 1) ? dl.goff[j] + gs : dl.xoff[j] + xs;
+    if constexpr (MASK) {
+      const uint32_t mine = step_bits<MASK>(p, b, s) >> (kRowsPerWave * wave);
+      if (!((mine >> (2 * j + (lane >> 5))) & 1u)) off = (uint32_t)kOOB;
+    }
+    dma16((d & 1) ? rg : rx, (int)off, dst);
+  }
+  __device__ __forceinline__ void step(const LayerArgs& p, const DmaLane& dl, uint32_t stage) const {
 #pragma unroll
-  for (int j = 0; j < kDmaPerOp; ++j) issue_pair<MASK>(p, dl, sr, b, s, stage, j);
-}
+    for (int d = 0; d < 2 * kDmaPerOp; ++d) dma(p, dl, stage, d);
+  }
+};
 
 // MFMA operands of one 16-token k-substep for this wave: 4 X blocks (din
 // rows) and 2 G blocks (dout rows), each read with two transposing 8-byte
@@ -321,21 +357,24 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
                                      unsigned char* lds) {
   static_assert(kKT == kBitsTokens, "one row-bit word per step");
   static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
+  static_assert(2 * kDmaPerOp == 4, "one DMA after each of the first four MFMAs");
   acc.zero();
   if (n <= 0) return 1.0f;
   const uint32_t base = lds_addr(lds);
   DmaLane dl;
   dl.init(p, a0, o0);
-  SampleRsrc sr;
-
-  Cursor<MASK> ic;                       // next step to issue
-  ic.start(p, k0);
-  Cursor<MASK> cc = ic;                  // step being consumed
+  Issue<MASK> is;                        // next step to queue
+  is.start(p, k0);
+  // Consumer side: the sample of the step being consumed, and (without a
+  // mask) the steps left before the next sample starts.
+  Cursor<MASK> cc;
+  cc.start(p, k0);
+  int left = cc.nsteps - cc.s;
 #pragma unroll
   for (int k = 0; k < kStages; ++k) {
     if (k < n) {
-      issue_step<MASK>(p, dl, sr, ic.b, ic.s, base + k * kStageBytes);
-      ic.advance();
+      is.step(p, dl, base + k * kStageBytes);
+      if (k + 1 < n) is.advance(p);
     }
   }
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
@@ -362,33 +401,42 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
       acc.mma1(f0, k);
       sched_fence();
       if (k < 6) read_frag(f1, st, 1, k);
+      if (k == 7) {
+        // Consumer cursor to step i+1.
+        if constexpr (MASK) {
+          cc.advance();
+        } else if (--left == 0) {
+          left = cc.nsteps;
+          ++cc.b;
+        }
+      }
       sched_fence();
     }
     lds_reads_done();                  // f1 is in registers; slot i-1 is no longer read
     const int next = (slot + 1 == kStages) ? 0 : slot + 1;
     const unsigned char* sn = lds + next * kStageBytes;
-    if (i + 1 < n) {
-      // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
-      // at barrier j >= 1, i.e. up to max(4, i+3).  Wait for step i+1.
-      const int last = min(n - 1, i <= 1 ? kStages - 1 : i + kStages - 2);
-      wait_dma(last - (i + 1));
+    // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
+    // at barrier j >= 1, i.e. up to max(4, i+3).  Wait for step i+1: in the
+    // steady state that leaves two steps in flight.
+    const bool steady = i >= 1 && i + kStages - 1 < n;
+    if (steady) {
+      wait_dma(2);
+      step_barrier();
+    } else if (i + 1 < n) {
+      wait_dma(min(n - 1, i <= 1 ? kStages - 1 : i + kStages - 2) - (i + 1));
       step_barrier();
     }
-    // slot (i-1) % kStages is free: queue step i+4 into it, one DMA pair
-    // after each of the first two MFMAs.  The reads of f0 follow; on the last
-    // step they read the next slot's stale contents, which are never used.
-    const bool refill = i >= 1 && i + kStages - 1 < n;
+    // slot (i-1) % kStages is free: queue step i+4 into it, one DMA after
+    // each of the first four MFMAs.  The reads of f0 follow; on the last step
+    // they read the next slot's stale contents, which are never used.
     const uint32_t prev = base + ((slot == 0) ? kStages - 1 : slot - 1) * kStageBytes;
     sched_fence();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       acc.mma1(f1, k);
       sched_fence();
-      if (k < kDmaPerOp && refill) issue_pair<MASK>(p, dl, sr, ic.b, ic.s, prev, k);
-      if (k == kDmaPerOp - 1) {
-        if (refill) ic.advance();
-        cc.advance();
-      }
+      if (k < 4 && steady) is.dma(p, dl, prev, k);
+      if (k == 4 && steady && i + kStages < n) is.advance(p);
       if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
       sched_fence();
     }
