@@ -124,6 +124,7 @@ struct Issue {
   __amdgpu_buffer_rsrc_t rx, rg;
   int b, s, k, nsteps;
   uint32_t xs, gs, dx, dg;     // byte offsets of the step; per-step increments
+  uint32_t wdst;               // this wave's rows within a slot (LDS bytes)
   const uint32_t* list;
   __device__ __forceinline__ void rsrc(const LayerArgs& p) {
     rx = sample_rsrc(p.X, b, p.T, p.din);
@@ -144,6 +145,7 @@ struct Issue {
     nsteps = (p.T + kKT - 1) / kKT;
     dx = (uint32_t)kKT * (uint32_t)p.X.stride_t * 2u;
     dg = (uint32_t)kKT * (uint32_t)p.G.stride_t * 2u;
+    wdst = (uint32_t)(kRowsPerWave * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRowBytes);
     k = k0;
     if constexpr (MASK) {
       list = p.steps + 2 + p.B;
@@ -181,12 +183,11 @@ struct Issue {
   __device__ __forceinline__ void dma(const LayerArgs& p, const DmaLane& dl, uint32_t stage,
                                       int d) const {
     const int j = d >> 1;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        stage + (kRowsPerWave * wave + 2 * j) * kRowBytes + (d & 1) * kOpBytes);
+    const int lane = threadIdx.x & 63;
+    const uint32_t dst = stage + wdst + 2 * j * kRowBytes + (d & 1) * kOpBytes;
     uint32_t off = (d & 1) ? dl.goff[j] + gs : dl.xoff[j] + xs;
     if constexpr (MASK) {
-      const uint32_t mine = step_bits<MASK>(p, b, s) >> (kRowsPerWave * wave);
+      const uint32_t mine = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
       if (!((mine >> (2 * j + (lane >> 5))) & 1u)) off = (uint32_t)kOOB;
     }
     dma16((d & 1) ? rg : rx, (int)off, dst);

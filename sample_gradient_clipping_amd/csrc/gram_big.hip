@@ -44,10 +44,13 @@ typedef __attribute__((address_space(4))) const uint32_t c_u32;
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+// 16 bytes per lane from rsrc at voffset + soffset straight into LDS at
+// m0 + 16 * lane.  soffset is wave-uniform (the step's feature offset).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, uint32_t lds,
+                                      uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
-               : "v"(voffset), "s"(rsrc), "s"(lds)
+               : "v"(voffset), "s"(rsrc), "s"(lds), "s"(soffset)
                : "memory");
 }
 
@@ -105,26 +108,46 @@ struct DmaLane {
   }
 };
 
-// Queue DMA j of feature step `step` (X features for step < nkx, else G
-// features) into the slot at LDS address `slot`.
-__device__ __forceinline__ void issue_dma(const LayerArgs& p, const DmaLane& dl,
-                                          __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
-                                          int step, int nkx, uint32_t slot, int j) {
-  const int wave = threadIdx.x >> 6;
-  const bool xs = step < nkx;
-  const int k0 = (xs ? step : step - nkx) * kKF;
-  const int D = xs ? p.din : p.dout;
-  const uint32_t base = xs ? dl.xoff[j] : dl.goff[j];
-  const int off = (k0 + dl.cfeat[j] < D) ? (int)(base + (uint32_t)k0 * 2) : kOOB;
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (kDmaPerStep * wave + j) * 1024);
-  dma16(xs ? rx : rg, off, dst);
-}
-
-__device__ __forceinline__ void issue_step(const LayerArgs& p, const DmaLane& dl,
-                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
-                                           int step, int nkx, uint32_t slot) {
+// What the DMAs of one feature step need, computed once per step: the
+// descriptor and feature offset (the instruction's scalar offset) of the X
+// or G rows, and whether the step runs past D (then each lane tests its
+// chunk and sends the chunks past D out of range).
+// Steps are queued in order, X steps first: the lane's row offsets in dl.xoff
+// are replaced by its G offsets once, when the first G step is queued.
+struct StepDma {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t soff;
+  int k0, D;
+  bool tail;
+  __device__ __forceinline__ void at(const LayerArgs& p, DmaLane& dl, __amdgpu_buffer_rsrc_t rx,
+                                     __amdgpu_buffer_rsrc_t rg, int step, int nkx, bool& on_g) {
+    const bool xs = step < nkx;
+    if (!xs && !on_g) {
 #pragma unroll
-  for (int j = 0; j < kDmaPerStep; ++j) issue_dma(p, dl, rx, rg, step, nkx, slot, j);
+      for (int j = 0; j < kDmaPerStep; ++j) dl.xoff[j] = dl.goff[j];
+      on_g = true;
+    }
+    k0 = (xs ? step : step - nkx) * kKF;
+    D = xs ? p.din : p.dout;
+    r = xs ? rx : rg;
+    soff = (uint32_t)k0 * 2u;
+    tail = k0 + kKF > D;
+  }
+  // DMA j of the step into the slot whose address for this wave's DMAs is `dst`.
+  __device__ __forceinline__ void dma(const DmaLane& dl, uint32_t dst, int j) const {
+    int off = (int)dl.xoff[j];
+    if (tail && k0 + dl.cfeat[j] >= D) off = kOOB;
+    dma16(r, off, dst + (uint32_t)j * 1024u, soff);
+  }
+};
+
+__device__ __forceinline__ void issue_step(const LayerArgs& p, DmaLane& dl,
+                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
+                                           int step, int nkx, uint32_t dst, bool& on_g) {
+  StepDma sd;
+  sd.at(p, dl, rx, rg, step, nkx, on_g);
+#pragma unroll
+  for (int j = 0; j < kDmaPerStep; ++j) sd.dma(dl, dst, j);
 }
 
 // All of this wave's LDS reads have returned.  Issued as the compiler's own
@@ -225,9 +248,13 @@ __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int T
   DmaLane dl;
   dl.init(p, b, S, Tb);
   const uint32_t base = lds_addr(smem);
+  // This wave's DMAs fill kDmaPerStep consecutive KiB of a slot.
+  const uint32_t wdst =
+      base + (uint32_t)(kDmaPerStep * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 1024u;
+  bool on_g = false;
 #pragma unroll
   for (int k = 0; k < kStages; ++k)
-    if (k < n) issue_step(p, dl, rx, rg, k0 + k, nkx, base + k * kSlotBytes);
+    if (k < n) issue_step(p, dl, rx, rg, k0 + k, nkx, wdst + k * kSlotBytes, on_g);
   ax.zero();
   ag.zero();
   wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
@@ -271,7 +298,9 @@ __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int T
       step_barrier();
     }
     const bool refill = i + kStages < n;
-    const uint32_t dst = base + slot * kSlotBytes;
+    const uint32_t dst = wdst + slot * kSlotBytes;
+    StepDma sd;
+    if (refill) sd.at(p, dl, rx, rg, k0 + i + kStages, nkx, on_g);
     const unsigned char* sn = smem + next * kSlotBytes;
     // substep 3 on f1, reads of step i+1 (stale on the last step, never
     // used), DMA of step i+3
@@ -287,8 +316,8 @@ __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int T
         read_frag(f0, sn, 0, kNeed[3]);
       }
       if (k >= 1 && refill) {
-        issue_dma(p, dl, rx, rg, k0 + i + kStages, nkx, dst, 2 * (k - 1));
-        issue_dma(p, dl, rx, rg, k0 + i + kStages, nkx, dst, 2 * (k - 1) + 1);
+        sd.dma(dl, dst, 2 * (k - 1));
+        sd.dma(dl, dst, 2 * (k - 1) + 1);
       }
       sched_fence();
     }
