@@ -476,7 +476,8 @@ __device__ __forceinline__ void store_tile(const LayerArgs& p, const Acc& acc, f
   static_assert(256 * (64 + 4) * 4 <= kLdsBytes, "epilogue staging fits in the stage ring");
   const int lane = threadIdx.x & 63;
   const int wm = wave_row(), wn = wave_col();
-  const float fB = (float)p.B;
+  // 1/B: exact for a power-of-two B, else within one ulp of dividing.
+  const float rB = 1.0f / (float)p.B;
   const bool noise = p.noise_std != 0.0f;
   float* park = (float*)smem;
   constexpr int kParkLd = 64 + 4;     // floats per o row (padding against bank conflicts)
@@ -514,7 +515,7 @@ __device__ __forceinline__ void store_tile(const LayerArgs& p, const Acc& acc, f
           v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
           v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
         }
-        v.x = v.x / fB; v.y = v.y / fB; v.z = v.z / fB; v.w = v.w / fB;
+        v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
         *(f32x4*)(p.out + e0) = v;
       }
     }
@@ -580,7 +581,7 @@ __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs
   int tm, tn;
   raster(sk.D * sk.G + r, sk.ntm, sk.ntn, &tm, &tn);
   const int a0 = tm * kTile, o0 = tn * kTile;
-  const float fB = (float)p.B;
+  const float rB = 1.0f / (float)p.B;   // as in store_tile
   const bool noise = p.noise_std != 0.0f;
 #pragma unroll 1
   for (int j = 0; j < 16; ++j) {
@@ -600,7 +601,7 @@ __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs
       v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
       v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
     }
-    v.x = v.x / fB; v.y = v.y / fB; v.z = v.z / fB; v.w = v.w / fB;
+    v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
     *(f32x4*)(p.out + e0) = v;
   }
 }

@@ -97,8 +97,10 @@ __device__ __forceinline__ u32x4 philox_block(uint64_t seed, uint64_t block) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += kPhiloxW0; k1 += kPhiloxW1; }
-    const uint32_t lo0 = kPhiloxM0 * c0, hi0 = __umulhi(kPhiloxM0, c0);
-    const uint32_t lo1 = kPhiloxM1 * c2, hi1 = __umulhi(kPhiloxM1, c2);
+    // One 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32).
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0, p1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
   }
