@@ -358,7 +358,7 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
                                      unsigned char* lds) {
   static_assert(kKT == kBitsTokens, "one row-bit word per step");
   static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
-  static_assert(2 * kDmaPerOp == 4, "one DMA after each of the first four MFMAs");
+  static_assert(2 * kDmaPerOp == 4, "one DMA after every other one of eight MFMAs");
   acc.zero();
   if (n <= 0) return 1.0f;
   const uint32_t base = lds_addr(lds);
@@ -428,7 +428,7 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
       step_barrier();
     }
     // slot (i-1) % kStages is free: queue step i+4 into it, one DMA after
-    // each of the first four MFMAs.  The reads of f0 follow; on the last step
+    // every other MFMA.  The reads of f0 follow; on the last step
     // they read the next slot's stale contents, which are never used.
     const uint32_t prev = base + ((slot == 0) ? kStages - 1 : slot - 1) * kStageBytes;
     sched_fence();
@@ -436,8 +436,8 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
     for (int k = 0; k < 8; ++k) {
       acc.mma1(f1, k);
       sched_fence();
-      if (k < 4 && steady) is.dma(p, dl, prev, k);
-      if (k == 4 && steady && i + kStages < n) is.advance(p);
+      if ((k & 1) == 0 && steady) is.dma(p, dl, prev, k >> 1);
+      if (k == 7 && steady && i + kStages < n) is.advance(p);
       if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
       sched_fence();
     }
