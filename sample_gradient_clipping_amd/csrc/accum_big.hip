@@ -125,6 +125,7 @@ struct Issue {
   int b, s, k, nsteps;
   uint32_t xs, gs, dx, dg;     // byte offsets of the step; per-step increments
   uint32_t wdst;               // this wave's rows within a slot (LDS bytes)
+  uint32_t bits;               // with a mask: this wave's rows' activity bits of the step
   const uint32_t* list;
   __device__ __forceinline__ void rsrc(const LayerArgs& p) {
     rx = sample_rsrc(p.X, b, p.T, p.din);
@@ -140,6 +141,7 @@ struct Issue {
       b = nb;
       rsrc(p);
     }
+    bits = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
   }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
@@ -187,8 +189,7 @@ struct Issue {
     const uint32_t dst = stage + wdst + 2 * j * kRowBytes + (d & 1) * kOpBytes;
     uint32_t off = (d & 1) ? dl.goff[j] + gs : dl.xoff[j] + xs;
     if constexpr (MASK) {
-      const uint32_t mine = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
-      if (!((mine >> (2 * j + (lane >> 5))) & 1u)) off = (uint32_t)kOOB;
+      if (!((bits >> (2 * j + (lane >> 5))) & 1u)) off = (uint32_t)kOOB;
     }
     dma16((d & 1) ? rg : rx, (int)off, dst);
   }
