@@ -133,11 +133,23 @@ struct StepDma {
     soff = (uint32_t)k0 * 2u;
     tail = k0 + kKF > D;
   }
-  // DMA j of the step into the slot whose address for this wave's DMAs is `dst`.
-  __device__ __forceinline__ void dma(const DmaLane& dl, uint32_t dst, int j) const {
+  // DMA j of the step into the slot whose address for this wave's DMAs is
+  // `dst`; TAIL: the step runs past D.
+  template <bool TAIL>
+  __device__ __forceinline__ void dma_(const DmaLane& dl, uint32_t dst, int j) const {
     int off = (int)dl.xoff[j];
-    if (tail && k0 + dl.cfeat[j] >= D) off = kOOB;
+    if (TAIL && k0 + dl.cfeat[j] >= D) off = kOOB;
     dma16(r, off, dst + (uint32_t)j * 1024u, soff);
+  }
+  // DMAs j0 .. j0+cnt-1.  Tail steps (only when D is not a multiple of the
+  // step's 64 features) take a separate branch, so that the common path
+  // carries no per-lane test.
+  __device__ __forceinline__ void dmas(const DmaLane& dl, uint32_t dst, int j0, int cnt) const {
+    if (__builtin_expect(tail, 0)) {
+      for (int j = j0; j < j0 + cnt; ++j) dma_<true>(dl, dst, j);
+    } else {
+      for (int j = j0; j < j0 + cnt; ++j) dma_<false>(dl, dst, j);
+    }
   }
 };
 
@@ -146,8 +158,7 @@ __device__ __forceinline__ void issue_step(const LayerArgs& p, DmaLane& dl,
                                            int step, int nkx, uint32_t dst, bool& on_g) {
   StepDma sd;
   sd.at(p, dl, rx, rg, step, nkx, on_g);
-#pragma unroll
-  for (int j = 0; j < kDmaPerStep; ++j) sd.dma(dl, dst, j);
+  sd.dmas(dl, dst, 0, kDmaPerStep);
 }
 
 // All of this wave's LDS reads have returned.  Issued as the compiler's own
@@ -315,10 +326,7 @@ __device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int T
         read_frag(f0, sn, 0, kNeed[2]);
         read_frag(f0, sn, 0, kNeed[3]);
       }
-      if (k >= 1 && refill) {
-        sd.dma(dl, dst, 2 * (k - 1));
-        sd.dma(dl, dst, 2 * (k - 1) + 1);
-      }
+      if (k >= 1 && refill) sd.dmas(dl, dst, 2 * (k - 1), 2);
       sched_fence();
     }
     slot = next;
