@@ -55,7 +55,97 @@ def parse():
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="also measure the other workload configurations (fp32 single linear, "
+                         "GPT-2 MLP up-projection, ragged Llama-13B layer, RoBERTa projected)")
     return ap.parse_args()
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Average milliseconds per call of fn() over `steps` calls (events on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_configs(dp, torch, steps, warmup):
+    """Throughput of the other workload configurations, one fused call per linear."""
+    import workloads
+    out = {}
+
+    def to_device(a, dtype):
+        if dtype == "bf16":
+            return upload(a, torch)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def dense(makers, name, note):
+        dev, lins = [], []
+        for make in makers:
+            lin = make()
+            lins.append(lin)
+            print(f"# {name}: generated {lin.name}", file=sys.stderr, flush=True)
+            X, G = to_device(lin.X, lin.dtype), to_device(lin.G, lin.dtype)
+            mask = None if lin.mask is None else torch.from_numpy(np.ascontiguousarray(lin.mask)).cuda()
+            o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
+            nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+            dev.append((lin, X, G, mask, o, nrm))
+
+        def layer():
+            for lin, X, G, mask, o, nrm in dev:
+                dp.linear_clip_accumulate(X, G, mask, C=lin.C, sigma=lin.sigma, seed=lin.seed,
+                                          offset=lin.offset, grad_out=o, norms_out=nrm)
+        ms = time_calls(torch, layer, steps, warmup)
+        useful = sum(2.0 * l.active_tokens() * l.din * l.dout for l in lins)
+        B = lins[0].B
+        out[name] = {"note": note, "linears": len(lins), "ms": round(ms, 4),
+                     "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+                     "samples_per_s": round(B * len(lins) / (ms * 1e-3), 1),
+                     "tokens_per_s": round(sum(l.active_tokens() for l in lins) / (ms * 1e-3), 1)}
+        print(f"# {name}: {out[name]}", file=sys.stderr, flush=True)
+        del dev
+        torch.cuda.empty_cache()
+
+    dense([lambda: workloads.config_c1(sigma=1.0).linears[0]], "c1_fp32_B4_T16_64to32",
+          "one fp32 linear; launch-latency bound")
+    dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
+          "bf16, sigma 0.8")
+    dense([lambda i=i: workloads.config_c4_linear(i) for i in range(len(workloads.C4_LINEARS))],
+          "c4_llama13b_ragged_B16_T2048_7_linears",
+          "bf16, prefix masks T_i ~ U[128, 2048], C 0.5, sigma 1.2; useful flops over active tokens")
+
+    # projected variant: Y = X P with P from gaussian_fill(seed 7, offset 0, 1/sqrt(r)), r = 256
+    r = 256
+    dev, Ps = [], {}
+    lins = workloads.config_c5().linears
+    for lin in lins:
+        if lin.din not in Ps:
+            Ps[lin.din] = dp.gaussian_fill(7, 0, lin.din * r, 1.0 / 16.0,
+                                           dtype=torch.bfloat16).view(lin.din, r)
+        X, G = upload(lin.X, torch), upload(lin.G, torch)
+        o = torch.empty((lin.dout, r), dtype=torch.float32, device=X.device)
+        nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+        dev.append((lin, X, G, o, nrm))
+
+    def proj_layer():
+        for lin, X, G, o, nrm in dev:
+            dp.linear_clip_accumulate_projected(X, G, Ps[lin.din], C=lin.C, sigma=lin.sigma,
+                                                grad_out=o, norms_out=nrm)
+    ms = time_calls(torch, proj_layer, steps, warmup)
+    useful = sum(2.0 * l.B * l.T * (l.din + l.dout) * r for l in lins)
+    out["c5_roberta_large_projected_r256_6_linears"] = {
+        "note": "bf16, projection then clip in r space; useful flops 2*B*T*(din+dout)*r",
+        "linears": len(lins), "ms": round(ms, 4),
+        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+    return out
 
 
 def copy_calibration(steps):
@@ -185,6 +275,35 @@ def main():
     dp.set_option("timing", 0)
     dp.timing_reset()
 
+    # determinism: the outputs of two further steps must match bit for bit
+    step()
+    torch.cuda.synchronize()
+    first = [o.clone() for (_, _, o, _) in dev_in]
+    step()
+    torch.cuda.synchronize()
+    deterministic = all(torch.equal(a, o) for a, (_, _, o, _) in zip(first, dev_in))
+    del first
+
+    # per linear: the fused call alone, and a plain bf16 GEMM G^T X of the same
+    # shape (no clipping, no noise) as the non-DP reference
+    per_linear = []
+    for lin, (X, G, out, norms) in zip(lins, dev_in):
+        ms = time_calls(torch, lambda: dp.linear_clip_accumulate(
+            X, G, None, C=lin.C, sigma=lin.sigma, seed=lin.seed, offset=lin.offset,
+            grad_out=out, norms_out=norms), args.steps, 2)
+        Gt = G.reshape(-1, lin.dout).t().contiguous()
+        X2 = X.reshape(-1, lin.din)
+        ms_gemm = time_calls(torch, lambda: torch.matmul(Gt, X2), args.steps, 2)
+        del Gt
+        f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+        per_linear.append({"linear": lin.name, "din": lin.din, "dout": lin.dout,
+                           "useful_gflop": round(f / 1e9, 1), "ms": round(ms, 4),
+                           "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                           "samples_per_s": round(lin.B / (ms * 1e-3), 1),
+                           "tokens_per_s": round(lin.B * lin.T / (ms * 1e-3), 1),
+                           "plain_bf16_gemm_ms": round(ms_gemm, 4),
+                           "dp_over_plain_throughput": round(ms_gemm / ms, 3)})
+
     useful = sum(2.0 * l.B * l.T * l.din * l.dout for l in lins)
     gram = sum(float(l.B) * l.T * l.T * (l.din + l.dout) for l in lins)
     tflops = useful / (ms_step * 1e-3) / 1e12
@@ -203,11 +322,6 @@ def main():
     traffic = accumulate_traffic(args)
     algo_bytes = sum(2.0 * l.B * l.T * (l.din + l.dout) + 4.0 * l.din * l.dout for l in lins) / len(lins)
 
-    per_linear = []
-    for l in lins:
-        f = 2.0 * l.B * l.T * l.din * l.dout
-        per_linear.append({"linear": l.name, "din": l.din, "dout": l.dout,
-                           "useful_gflop": round(f / 1e9, 1)})
 
     res = {
         "metric": METRIC,
@@ -244,9 +358,14 @@ def main():
         "accumulate_with_fixup_tflops": None if acc_phase is None else round(acc_phase, 2),
         "gram_norm_kernel_tflops": None if gram_achieved is None else round(gram_achieved, 2),
         "per_linear": per_linear,
+        "bitwise_deterministic": bool(deterministic),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),
     }
+    if args.configs:
+        del dev_in
+        torch.cuda.empty_cache()
+        res["configs"] = measure_configs(dp, torch, args.steps, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(lins[0], args.cpu_budget_s)
     print(json.dumps(res), flush=True)
