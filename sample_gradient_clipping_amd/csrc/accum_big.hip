@@ -536,15 +536,43 @@ struct SkPlan {
   int ntm, ntn;
 };
 
+constexpr int kMaxSplit = 16;   // P never exceeds this
+
+// P for the R tiles of the last, partial round over n steps, at most maxP.
+// Cost model in microseconds, fitted to sweeps of P on MI355X at the
+// Llama-13B shapes (dense and ragged): one 32-token step of a 256 x 256 tile
+// ~0.8 us, a piece's pipeline fill and epilogue ~4 us (workgroups left alone
+// in a partly filled round run faster, which hides most of it), the fixup
+// ~5 us plus 0.06 us per partial (256 KiB written, then read).  Runs on the
+// host over every step, and on the device for masked calls, over the active
+// steps only the device knows.
+__host__ __device__ inline int split_tiles(int R, int G, int n, int maxP) {
+  if (R == 0) return 1;
+  const double step_us = 0.8, piece_us = 4.0;
+  double best = n * step_us + piece_us;   // P = 1: one more round
+  int bestP = 1;
+  for (int P = 2; P <= maxP; ++P) {
+    if ((double)n / P < 16.0) break;      // pieces of >= 16 steps
+    const int S = (R * P + G - 1) / G;
+    const double t = S * ((double)n / P * step_us + piece_us) + 5.0 + 0.06 * R * P;
+    if (t < best) {
+      best = t;
+      bestP = P;
+    }
+  }
+  return bestP;
+}
+
 // Active steps per tile: all of them without a mask, else the list's count.
 __device__ __forceinline__ int active_steps(const LayerArgs& p) {
   return p.steps != nullptr ? (int)((c_u32*)p.steps)[0] : p.B * ((p.T + kKT - 1) / kKT);
 }
 
 template <bool MASK>
-__device__ __forceinline__ void accumulate_body(const LayerArgs& p, const SkPlan& sk,
+__device__ __forceinline__ void accumulate_body(const LayerArgs& p, SkPlan sk,
                                                 unsigned char* smem) {
   const int n = active_steps(p);
+  if (MASK) sk.P = split_tiles(sk.R, sk.G, n, sk.P);   // the host's P is for every step
   const int L = logical_wg(blockIdx.x, sk.G);
   Acc acc;
   auto full_tile = [&](int t) {
@@ -575,36 +603,48 @@ __global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p, SkP
 }
 
 // Split tiles: sum their P partials in chunk order, add the noise, divide by
-// B.  One workgroup per (split tile, 64-row quarter).
+// B.  One thread per 4 consecutive outputs, one workgroup per 4 rows of a
+// split tile, so a 256 x 256 tile spreads over 64 workgroups.  Each thread
+// keeps the loads of up to kFixBatch partials in flight at once (indices past
+// P are clamped to the last partial and their values dropped).
 constexpr int kFixThreads = 256;
+constexpr int kFixRows = kFixThreads / (kTile / 4);     // 4 tile rows per workgroup
+constexpr int kFixBlocksPerTile = kTile / kFixRows;     // 64
+constexpr int kFixBatch = 8;
 __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs p, SkPlan sk) {
-  const int r = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  if (p.steps != nullptr) sk.P = split_tiles(sk.R, sk.G, (int)((c_u32*)p.steps)[0], sk.P);
+  if (sk.P == 1) return;            // masked: the active steps did not call for a split
+  const int r = blockIdx.x / kFixBlocksPerTile, rows = blockIdx.x % kFixBlocksPerTile;
   int tm, tn;
   raster(sk.D * sk.G + r, sk.ntm, sk.ntn, &tm, &tn);
-  const int a0 = tm * kTile, o0 = tn * kTile;
-  const float rB = 1.0f / (float)p.B;   // as in store_tile
-  const bool noise = p.noise_std != 0.0f;
+  const int ol = rows * kFixRows + (int)(threadIdx.x >> 6), al = (int)(threadIdx.x & 63) * 4;
+  const int o = tn * kTile + ol, a = tm * kTile + al;
+  if (o >= p.dout || a >= p.din) return;
+  const float* part = p.skws + (int64_t)r * kTileElems + ol * kTile + al;
+  const int64_t stride = (int64_t)sk.R * kTileElems;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-  for (int j = 0; j < 16; ++j) {
-    const int idx = j * kFixThreads + threadIdx.x;       // [0, 64 * 64)
-    const int ol = quarter * 64 + (idx >> 6), al = (idx & 63) * 4;
-    const int o = o0 + ol, a = a0 + al;
-    if (o >= p.dout || a >= p.din) continue;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < sk.P; ++c) {
-      const float* part = p.skws + (int64_t)(c * sk.R + r) * kTileElems;
-      const f32x4 w = *(const f32x4*)(part + ol * kTile + al);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  for (int c0 = 0; c0 < sk.P; c0 += kFixBatch) {
+    f32x4 w[kFixBatch];
+#pragma unroll
+    for (int j = 0; j < kFixBatch; ++j)
+      w[j] = *(const f32x4*)(part + (int64_t)min(c0 + j, sk.P - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < kFixBatch; ++j) {
+      if (c0 + j < sk.P) {
+        v.x += w[j].x; v.y += w[j].y; v.z += w[j].z; v.w += w[j].w;
+      }
     }
-    const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
-    if (noise) {
-      const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
-      v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
-      v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
-    }
-    v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
-    *(f32x4*)(p.out + e0) = v;
   }
+  const float rB = 1.0f / (float)p.B;   // as in store_tile
+  const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
+  if (p.noise_std != 0.0f) {
+    const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
+    v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
+    v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
+  }
+  v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+  *(f32x4*)(p.out + e0) = v;
 }
 
 __global__ void __launch_bounds__(kNT, 1) direct_norm_big_kernel(LayerArgs p) {
@@ -651,11 +691,6 @@ int big_tiles(int din, int dout) {
 }
 
 namespace {
-// Pick the split of the last, partial round.  Cost model in microseconds,
-// from measurements on MI355X at the Llama-13B shapes: one 32-token step of a
-// 256 x 256 tile ~0.8 us, a piece's pipeline fill and epilogue ~16 us, the
-// fixup ~10 us plus 0.13 us per partial (256 KiB written, then read) and
-// 0.07 us per split tile (noise and store).
 big::SkPlan plan_accumulate(const LayerArgs& p) {
   big::SkPlan sk{};
   sk.ntm = (p.din + big::kTile - 1) / big::kTile;
@@ -667,20 +702,8 @@ big::SkPlan plan_accumulate(const LayerArgs& p) {
   sk.G = G;
   sk.D = ntiles / G;
   sk.R = ntiles - sk.D * G;
-  sk.P = 1;
-  if (sk.R == 0) return sk;
-  const double n = (double)p.B * ((p.T + big::kKT - 1) / big::kKT);   // upper bound if masked
-  const double step_us = 0.8, piece_us = 16.0;
-  double best = n * step_us + piece_us;                                // P = 1: one more round
-  for (int P = 2; P <= 16; ++P) {
-    if (n / P < 16) break;                                             // pieces of >= 16 steps
-    const int S = (sk.R * P + G - 1) / G;
-    const double t = S * (n / P * step_us + piece_us) + 10.0 + 0.13 * sk.R * P + 0.07 * sk.R;
-    if (t < best) {
-      best = t;
-      sk.P = P;
-    }
-  }
+  const int n = p.B * ((p.T + big::kKT - 1) / big::kKT);   // every step (an upper bound if masked)
+  sk.P = big::split_tiles(sk.R, G, n, big::kMaxSplit);
   if (sk.P == 1 && sk.D == 0) sk.G = sk.R;   // one tile per workgroup, no idle ones
   return sk;
 }
@@ -702,8 +725,8 @@ hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s) {
   timing_end("accumulate", s);
   if (e != hipSuccess || sk.P == 1) return e;
   timing_begin("accumulate_fixup", s);
-  hipLaunchKernelGGL(big::accumulate_fixup_kernel, dim3(4 * sk.R), dim3(big::kFixThreads), 0, s, p,
-                     sk);
+  hipLaunchKernelGGL(big::accumulate_fixup_kernel, dim3(big::kFixBlocksPerTile * sk.R),
+                     dim3(big::kFixThreads), 0, s, p, sk);
   e = hipGetLastError();
   timing_end("accumulate_fixup", s);
   return e;

@@ -301,23 +301,26 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
 
   Workspace ws(s);
   const size_t off_y = ws.reserve((size_t)X->B * X->T * r * es);
-  // Reserve the layer workspace now so that a single allocation covers both.
-  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
-  LayerPlan L = plan_layer(&Y, G, mask);
-  const LayerWs o = reserve_layer(L, ws, true, true, true);
-  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  Y.data = ws.at<void>(off_y);
-
   dpf::ProjArgs pa{};
   pa.X = to_act(X);
   pa.P = P;
-  pa.Y = const_cast<void*>(Y.data);
   pa.dtype = X->dtype;
   pa.B = (int)X->B;
   pa.T = (int)X->T;
   pa.din = (int)X->D;
   pa.r = (int)r;
   pa.mask = mask;
+  pa.splits = dpf::project_splits(pa);
+  const size_t pbytes = dpf::project_workspace_bytes(pa);
+  const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
+  // Reserve the layer workspace now so that a single allocation covers both.
+  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
+  LayerPlan L = plan_layer(&Y, G, mask);
+  const LayerWs o = reserve_layer(L, ws, true, true, true);
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  Y.data = ws.at<void>(off_y);
+  pa.Y = const_cast<void*>(Y.data);
+  pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
   const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
   hipError_t e = dpf::launch_project(pa, pvec, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");

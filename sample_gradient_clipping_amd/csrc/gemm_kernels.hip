@@ -11,12 +11,16 @@
 //  gram_norm_kernel  : per (sample, upper-triangular token-tile pair) partial
 //                      of <X~X~^T, G~G~^T> (the Gram form of ||g_i||^2).
 //  project_kernel    : Y = X~ P for the projected variant (DP-GRAPE explainer,
-//                      Methodology: project before clipping and noise).
+//                      Methodology: project before clipping and noise),
+//                      optionally split along din into fp32 partials that
+//                      project_reduce_kernel sums in chunk order.
 //
 // All four: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 2 x 2
 // blocks of 32 x 32 accumulators (a 128 x 128 workgroup tile), LDS double
 // buffered along K.  Partial results leave as fp64 per workgroup and are
 // summed in index order by finalize_kernel, so every reduction is fixed-order.
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -371,7 +375,10 @@ __global__ void __launch_bounds__(kNT) gram_norm_kernel(LayerArgs p) {
 // ===========================================================================
 // Projection Y = X~ P.  MFMA "A" = P^T (rows along r, K-outer in memory),
 // "B" = X (rows along tokens, K-inner).  Each lane ends with 4 consecutive r
-// of one token.  Y is [B, T, r] contiguous in X's dtype.
+// of one token.  Y is [B, T, r] contiguous in X's dtype.  With p.splits > 1
+// the din range is cut into that many chunks, one workgroup per (output
+// tile, chunk), each storing its fp32 partial product; project_reduce_kernel
+// sums the chunks in order and rounds.
 // ===========================================================================
 template <class E, bool VEC>
 __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
@@ -382,9 +389,13 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
   constexpr int P_ELEMS = KT * LDP, X_ELEMS = kTileN * LDX;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   S* lds = (S*)smem;
+  const int64_t ntok = (int64_t)p.B * p.T;
   const int ntr = (p.r + kTileM - 1) / kTileM;
-  const int j0 = (blockIdx.x % ntr) * kTileM;
-  const int64_t q0 = (int64_t)(blockIdx.x / ntr) * kTileN;
+  const int64_t ntiles = (int64_t)ntr * ((ntok + kTileN - 1) / kTileN);
+  const int64_t tile = blockIdx.x % ntiles;
+  const int split = (int)(blockIdx.x / ntiles);
+  const int j0 = (int)(tile % ntr) * kTileM;
+  const int64_t q0 = (tile / ntr) * kTileN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / kWN, wn = wave % kWN;
 
@@ -400,15 +411,17 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
 
   const S* P = (const S*)p.P;
   const S* Xd = (const S*)p.X.data;
-  const int nk = (p.din + KT - 1) / KT;
+  const int nk_all = (p.din + KT - 1) / KT;
+  const int kb = (int)((int64_t)split * nk_all / p.splits);
+  const int nk = (int)((int64_t)(split + 1) * nk_all / p.splits);
   // P rows are "tokens" of the K-outer loader: row k of P, T = din, no mask.
-  lp.load(P, p.r, p.din, nullptr, 0, j0, p.r);
-  lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, 0, p.din);
+  lp.load(P, p.r, p.din, nullptr, kb * KT, j0, p.r);
+  lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, kb * KT, p.din);
   lp.template store<LDP>(lds);
   lx.template store<LDX>(lds + P_ELEMS);
   __syncthreads();
   int buf = 0;
-  for (int kk = 0; kk < nk; ++kk) {
+  for (int kk = kb; kk < nk; ++kk) {
     const bool more = kk + 1 < nk;
     if (more) {
       lp.load(P, p.r, p.din, nullptr, (kk + 1) * KT, j0, p.r);
@@ -436,7 +449,6 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
     buf ^= 1;
   }
 
-  const int64_t ntok = (int64_t)p.B * p.T;
 #pragma unroll
   for (int i = 0; i < kBM; ++i) {
 #pragma unroll
@@ -444,11 +456,20 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
       const int64_t q = q0 + (wn * kBN + j) * 32 + acc_col(lane);
       if (q >= ntok) continue;
       S* yrow = (S*)p.Y + q * p.r;
+      float* prow = p.part + ((int64_t)split * ntok + q) * p.r;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int jj = j0 + (wm * kBM + i) * 32 + acc_row(4 * g, lane);
         if (jj >= p.r) continue;
-        if constexpr (sizeof(S) == 2) {
+        if (p.splits > 1) {
+          if ((p.r & 3) == 0) {
+            f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                       acc[i][j][4 * g + 3]};
+            *(f32x4*)(prow + jj) = v;
+          } else {
+            for (int e = 0; e < 4; ++e) if (jj + e < p.r) prow[jj + e] = acc[i][j][4 * g + e];
+          }
+        } else if constexpr (sizeof(S) == 2) {
           u16x4 w;
           w.s0 = f32_to_bf16_rne(acc[i][j][4 * g + 0]);
           w.s1 = f32_to_bf16_rne(acc[i][j][4 * g + 1]);
@@ -465,6 +486,33 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
         }
       }
     }
+  }
+}
+
+// Y = sum of the p.splits partial products, chunk by chunk in order, rounded
+// to Y's dtype.  Four consecutive elements per thread.
+template <class E>
+__global__ void __launch_bounds__(256) project_reduce_kernel(ProjArgs p) {
+  using S = typename E::storage;
+  const int64_t n = (int64_t)p.B * p.T * p.r;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if ((n & 3) == 0) {
+    for (int c = 0; c < p.splits; ++c) {
+      const f32x4 w = *(const f32x4*)(p.part + c * n + i);
+      v[0] += w.x; v[1] += w.y; v[2] += w.z; v[3] += w.w;
+    }
+  } else {
+    for (int c = 0; c < p.splits; ++c)
+      for (int e = 0; e < 4; ++e)
+        if (i + e < n) v[e] += p.part[c * n + i + e];
+  }
+  S* y = (S*)p.Y + i;
+  for (int e = 0; e < 4; ++e) {
+    if (i + e >= n) break;
+    if constexpr (sizeof(S) == 2) y[e] = f32_to_bf16_rne(v[e]);
+    else y[e] = v[e];
   }
 }
 
@@ -525,13 +573,22 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
   constexpr int bytes = 2 * (KT * (kTileM + Cfg<E>::PAD) + kTileN * (KT + (sizeof(S) == 2 ? 8 : 4))) *
                         (int)sizeof(S);
   const int64_t ntok = (int64_t)p.B * p.T;
-  const int64_t grid = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
+  const int64_t tiles = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
+  if (p.splits < 1 || (p.splits > 1 && p.part == nullptr)) return hipErrorInvalidValue;
   hipError_t e = allow_lds<project_kernel<E, VEC>>(bytes);
   if (e != hipSuccess) return e;
   timing_begin("project", s);
-  hipLaunchKernelGGL((project_kernel<E, VEC>), dim3((unsigned)grid), dim3(kNT), bytes, s, p);
+  hipLaunchKernelGGL((project_kernel<E, VEC>), dim3((unsigned)(tiles * p.splits)), dim3(kNT), bytes,
+                     s, p);
   e = hipGetLastError();
   timing_end("project", s);
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t n = ntok * p.r;
+  timing_begin("project_reduce", s);
+  hipLaunchKernelGGL((project_reduce_kernel<E>), dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0,
+                     s, p);
+  e = hipGetLastError();
+  timing_end("project_reduce", s);
   return e;
 }
 }  // namespace
@@ -585,6 +642,22 @@ hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t 
   if (p.dtype == kBF16) return vec ? launch_direct_t<BF16, true>(p, s) : launch_direct_t<BF16, false>(p, s);
   return vec ? launch_direct_t<F32, true>(p, s) : launch_direct_t<F32, false>(p, s);
 }
+// din chunks of the projection: enough (output tile, chunk) workgroups for
+// one per compute unit, each chunk at least 4 K-steps long, at most 8 chunks.
+int project_splits(const ProjArgs& p) {
+  const int KT = p.dtype == kBF16 ? Cfg<BF16>::KT : Cfg<F32>::KT;
+  const int64_t ntok = (int64_t)p.B * p.T;
+  const int64_t tiles = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
+  const int nk = (p.din + KT - 1) / KT;
+  const int64_t want = (device_cus() + tiles - 1) / tiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, 8, nk / 4}));
+}
+
+size_t project_workspace_bytes(const ProjArgs& p) {
+  const int sp = project_splits(p);
+  return sp == 1 ? 0 : (size_t)sp * p.B * p.T * p.r * sizeof(float);
+}
+
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s) {
   if (p.dtype == kBF16) return vec ? launch_project_t<BF16, true>(p, s) : launch_project_t<BF16, false>(p, s);
   return vec ? launch_project_t<F32, true>(p, s) : launch_project_t<F32, false>(p, s);

@@ -373,6 +373,31 @@ struct GramPlan {
   int G, D, R, P;
 };
 
+constexpr int kMaxSplit = 16;
+
+// D, R and P for `items` items of n feature steps on G workgroups, with at
+// most `cap` pieces.  Cost model from measurements on MI355X: a 64-feature
+// step of a 256 x 128 item ~0.8 us; a piece's fill and partial store ~10 us;
+// the fixup ~10 us plus 0.13 us per piece.  Runs on the host, and on the
+// device for masked calls, where only the device knows how many items hold
+// an active token.
+__host__ __device__ inline GramPlan split_items(int items, int G, int n, int cap) {
+  GramPlan gp{G, items / G, items % G, 1};
+  if (gp.R == 0) return gp;
+  const double step_us = 0.8, piece_us = 10.0;
+  double best = n * step_us + piece_us;
+  for (int P = 2; P <= kMaxSplit; ++P) {
+    if ((double)n / P < 8.0 || gp.R * P > cap) break;
+    const int S = (gp.R * P + G - 1) / G;
+    const double t = S * ((double)n / P * step_us + piece_us) + 10.0 + 0.13 * gp.R * P;
+    if (t < best) {
+      best = t;
+      gp.P = P;
+    }
+  }
+  return gp;
+}
+
 // A piece's partial Grams: 128 floats per thread (64 of X, then 64 of G),
 // stored as f32x4 q of thread tid at [q][tid] so that stores and loads of
 // consecutive threads are contiguous.
@@ -414,12 +439,19 @@ __device__ __forceinline__ void add_piece(const float* src, Acc2& ax, Acc2& ag) 
       }
 }
 
+// Masked calls: live[0] = n, the number of items with an active token in
+// both of their row blocks, live[1 .. n] their indices in increasing order.
+// The other items are exactly zero; the list kernel stores their partials.
+// The plan over the n live items is made here, with at most `cap` pieces.
 __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, GramPlan gp,
+                                                               const uint32_t* live, int cap,
                                                                float* ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int per_sample = items_per_sample(p.T);
   const int n = (p.din + kKF - 1) / kKF + (p.dout + kKF - 1) / kKF;
   const int L = logical_wg(blockIdx.x, gp.G);
+  if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, n, cap);
+  auto item_at = [&](int i) { return live != nullptr ? (int)((c_u32*)live)[1 + i] : i; };
   Acc2 ax, ag;
   auto full_item = [&](int item) {
     int b, S, Tb;
@@ -429,13 +461,13 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, Gram
     if (threadIdx.x == 0) p.partials[item] = tot;
     __syncthreads();                 // the reduction scratch is the next item's ring
   };
-  for (int d = 0; d < gp.D; ++d) full_item(d * gp.G + L);
+  for (int d = 0; d < gp.D; ++d) full_item(item_at(d * gp.G + L));
   if (gp.P == 1) {
-    if (L < gp.R) full_item(gp.D * gp.G + L);
+    if (L < gp.R) full_item(item_at(gp.D * gp.G + L));
     return;
   }
   for (int pi = L; pi < gp.R * gp.P; pi += gp.G) {
-    const int c = pi / gp.R, item = gp.D * gp.G + pi % gp.R;
+    const int c = pi / gp.R, item = item_at(gp.D * gp.G + pi % gp.R);
     int b, S, Tb;
     item_coords(item, per_sample, p.T, &b, &S, &Tb);
     run_item(p, b, S, Tb, (int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), ax, ag,
@@ -446,11 +478,18 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, Gram
 
 // Split items: sum the P partial Grams in chunk order, then the weighted
 // product and its reduction, as for a whole item.  One workgroup per item,
-// with the main kernel's thread layout.
+// with the main kernel's thread layout.  Masked calls launch one workgroup
+// per possible split item and make the plan as the main kernel does.
 __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPlan gp,
+                                                            const uint32_t* live, int cap,
                                                             const float* ws) {
   __shared__ double red[kNT / 64];
-  const int r = blockIdx.x, item = gp.D * gp.G + r;
+  const int n = (p.din + kKF - 1) / kKF + (p.dout + kKF - 1) / kKF;
+  if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, n, cap);
+  const int r = blockIdx.x;
+  if (gp.P == 1 || r >= gp.R) return;
+  const int i = gp.D * gp.G + r;
+  const int item = live != nullptr ? (int)((c_u32*)live)[1 + i] : i;
   int b, S, Tb;
   item_coords(item, items_per_sample(p.T), p.T, &b, &S, &Tb);
   Acc2 ax, ag;
@@ -461,45 +500,74 @@ __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPla
   if (threadIdx.x == 0) p.partials[item] = tot;
 }
 
+// Live-item list of a masked call (layout at gram_norm_big_kernel) from the
+// row bits; items with no active token in one of their row blocks get a zero
+// partial here.  One workgroup walks the items in order, 1024 at a time; an
+// entry's index is the number of live items before it.
+constexpr int kListThreads = 1024;
+__global__ void __launch_bounds__(kListThreads) live_items_kernel(LayerArgs p, uint32_t* live) {
+  __shared__ uint32_t wave_count[kListThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per_sample = items_per_sample(p.T);
+  const int64_t total = (int64_t)p.B * per_sample;
+  uint32_t base = 0;
+  for (int64_t c0 = 0; c0 < total; c0 += kListThreads) {
+    const int64_t i = c0 + tid;
+    bool act = false;
+    if (i < total) {
+      int b, S, Tb;
+      item_coords((int)i, per_sample, p.T, &b, &S, &Tb);
+      const uint32_t* w = p.rowbits + (int64_t)b * p.nwords;
+      uint32_t ws = 0, wt = 0;
+      for (int k = S * (kRowsS / 32); k < min((S + 1) * (kRowsS / 32), p.nwords); ++k) ws |= w[k];
+      for (int k = Tb * (kRowsT / 32); k < min((Tb + 1) * (kRowsT / 32), p.nwords); ++k) wt |= w[k];
+      act = ws != 0u && wt != 0u;
+      if (!act) p.partials[i] = 0.0;
+    }
+    const uint64_t ball = __ballot(act);
+    const uint32_t below = (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_count[wave] = (uint32_t)__popcll(ball);
+    __syncthreads();
+    uint32_t before = 0, chunk = 0;
+    for (int w = 0; w < kListThreads / 64; ++w) {
+      if (w < wave) before += wave_count[w];
+      chunk += wave_count[w];
+    }
+    if (act) live[1 + base + before + below] = (uint32_t)i;
+    base += chunk;
+    __syncthreads();                  // wave_count is rewritten by the next chunk
+  }
+  if (tid == 0) live[0] = base;
+}
+
 }  // namespace gram
 
 int gram_big_items_per_sample(int T) { return gram::items_per_sample(T); }
 
 namespace {
-// Split of the last, partial round: same cost model as the accumulate
-// kernel's (a 64-feature step of a 256 x 128 item ~0.8 us; a piece's fill
-// and partial store ~10 us; the fixup ~10 us plus 0.13 us per piece).
 gram::GramPlan plan_gram(const LayerArgs& p) {
-  gram::GramPlan gp{};
   const int items = p.B * gram::items_per_sample(p.T);
   const int cus = device_cus();
   int G = std::min(cus, items * 16);
   if (G >= 8) G -= G % 8;
-  gp.G = G;
-  gp.D = items / G;
-  gp.R = items - gp.D * G;
-  gp.P = 1;
-  if (gp.R != 0) {
-    const double n = (p.din + gram::kKF - 1) / gram::kKF + (p.dout + gram::kKF - 1) / gram::kKF;
-    const double step_us = 0.8, piece_us = 10.0;
-    double best = n * step_us + piece_us;
-    for (int P = 2; P <= 16; ++P) {
-      if (n / P < 8) break;
-      const int S = (gp.R * P + G - 1) / G;
-      const double t = S * (n / P * step_us + piece_us) + 10.0 + 0.13 * gp.R * P;
-      if (t < best) {
-        best = t;
-        gp.P = P;
-      }
-    }
-  }
+  const int n = (p.din + gram::kKF - 1) / gram::kKF + (p.dout + gram::kKF - 1) / gram::kKF;
+  gram::GramPlan gp = gram::split_items(items, G, n, 1 << 30);
   if (gp.P == 1 && gp.D == 0) gp.G = gp.R;
   return gp;
+}
+
+// Workspace of a masked call: the live-item list, then room for G pieces
+// (the device-side plan never splits into more).
+size_t live_list_bytes(const LayerArgs& p) {
+  const size_t b = ((size_t)p.B * gram::items_per_sample(p.T) + 1) * sizeof(uint32_t);
+  return (b + 255) & ~(size_t)255;
 }
 }  // namespace
 
 size_t gram_big_workspace_bytes(const LayerArgs& p) {
   const gram::GramPlan gp = plan_gram(p);
+  if (p.mask != nullptr)
+    return live_list_bytes(p) + (size_t)gp.G * gram::kPieceFloats * sizeof(float);
   return gp.P == 1 ? 0 : (size_t)gp.R * gp.P * gram::kPieceFloats * sizeof(float);
 }
 
@@ -509,16 +577,29 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
                                                gram::kLdsBytes);
   if (once != hipSuccess) return once;
   const gram::GramPlan gp = plan_gram(p);
-  if (gp.P != 1 && p.skws == nullptr) return hipErrorInvalidValue;
+  const bool masked = p.rowbits != nullptr;
+  if ((masked || gp.P != 1) && p.skws == nullptr) return hipErrorInvalidValue;
+  uint32_t* live = nullptr;
+  float* pieces = p.skws;
+  hipError_t e;
+  if (masked) {
+    live = reinterpret_cast<uint32_t*>(p.skws);
+    pieces = p.skws + live_list_bytes(p) / sizeof(float);
+    timing_begin("live_items", s);
+    hipLaunchKernelGGL(gram::live_items_kernel, dim3(1), dim3(gram::kListThreads), 0, s, p, live);
+    e = hipGetLastError();
+    timing_end("live_items", s);
+    if (e != hipSuccess) return e;
+  }
   timing_begin("gram_norm", s);
   hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(gp.G), dim3(gram::kNT), gram::kLdsBytes, s, p,
-                     gp, p.skws);
-  hipError_t e = hipGetLastError();
+                     gp, (const uint32_t*)live, gp.G, pieces);
+  e = hipGetLastError();
   timing_end("gram_norm", s);
-  if (e != hipSuccess || gp.P == 1) return e;
+  if (e != hipSuccess || (!masked && gp.P == 1)) return e;
   timing_begin("gram_fixup", s);
-  hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(gp.R), dim3(gram::kNT), 0, s, p, gp,
-                     (const float*)p.skws);
+  hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(masked ? gp.G : gp.R), dim3(gram::kNT), 0, s, p,
+                     gp, (const uint32_t*)live, gp.G, (const float*)pieces);
   e = hipGetLastError();
   timing_end("gram_fixup", s);
   return e;

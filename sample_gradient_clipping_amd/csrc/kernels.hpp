@@ -44,6 +44,8 @@ struct ProjArgs {
   int dtype;
   int B, T, din, r;
   const uint8_t* mask;
+  float* part;              // [splits, B*T, r] fp32 partial products when splits > 1
+  int splits;               // din chunks, one workgroup each per output tile
 };
 
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the
@@ -59,6 +61,10 @@ size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec);
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
+// Number of din chunks launch_project splits Y = X P into, and the fp32
+// partial buffer (p.part) that takes when above 1.
+int project_splits(const ProjArgs& p);
+size_t project_workspace_bytes(const ProjArgs& p);
 // Partials per sample written by the norm kernel launch_norm picks for (p, path, vec).
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec);
 

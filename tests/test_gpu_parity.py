@@ -184,3 +184,49 @@ def test_projected_small_masked_fp32_and_bf16():
         assert max_rel(norms.cpu().numpy()[rn > 0], rn[rn > 0]) <= tol_n
         assert norms.cpu().numpy()[2] == 0.0
         assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_masked_gram_dead_row_blocks(path):
+    """Masks that leave whole 256- and 128-token row blocks empty.
+
+    The Gram kernel works on (256-token block, 128-token block) items of a
+    sample and skips those with an empty block.  Sample 0 has tokens only
+    in [300, 512) (its first 256-token block is empty), sample 1 one token at
+    129, sample 2 none (norm 0), sample 3 every other token.  With
+    din + dout = 5120 features and few live items, the items also split over
+    several workgroups.
+    """
+    rng = np.random.default_rng(11)
+    lin = random_linear(rng, 4, 512, 2048, 3072)
+    mask = np.zeros((4, 512), np.uint8)
+    mask[0, 300:] = 1
+    mask[1, 129] = 1
+    mask[3, ::2] = 1
+    lin.mask = mask
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    assert rn[2] == 0.0 and (rn[[0, 1, 3]] > 0).all()
+    C = float(np.median(rn[[0, 1, 3]]))
+    out, norms, _, _ = _check(lin, path, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+    assert norms[2] == 0.0
+    _check(lin, path, sigma=0.7, C=C)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(2, 100, 1000, 72), (3, 33, 1000, 70)])
+def test_projected_split_along_din(dtype, shape):
+    """din = 1000 is long enough for the projection to split along din into
+    fp32 chunks summed in order; din, r and B*T*r all end in ragged tails."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, r = shape
+    rng = np.random.default_rng(12)
+    lin = random_linear(rng, B, T, din, 96, dtype=dtype, lengths=[T - 7] + [T] * (B - 1))
+    Pf = (rng.standard_normal((din, r)) / np.sqrt(r)).astype(np.float32)
+    P = workloads.f32_to_bf16_bits(Pf) if dtype == "bf16" else Pf
+    X, G = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch)
+    out, norms = dp.linear_clip_accumulate_projected(X, G, to_dev(P, dtype, torch),
+                                                     mask_dev(lin.mask, torch), C=0.05, sigma=0.0)
+    ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, lin.mask, P, 0.05, 0.0, 0, 0, dtype)
+    assert max_rel(norms.cpu().numpy(), rn) <= (NORM_TOL if dtype == "f32" else 5e-3)
+    assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
