@@ -98,14 +98,22 @@ bool vec_ok(const dpf_act* a) {
 
 dpf::Act to_act(const dpf_act* a) { return dpf::Act{a->data, a->stride_b, a->stride_t}; }
 
-dpf::NormPath choose_path(int64_t T, int64_t din, int64_t dout) {
+dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec) {
   const int forced = g_norm_path.load();
   if (forced == 1) return dpf::NormPath::kGram;
   if (forced == 2) return dpf::NormPath::kDirect;
+  const double T = a.T, din = a.din, dout = a.dout;
+  const double direct = 2.0 * T * din * dout;   // flops per sample
+  if (dpf::big_path(a, vec)) {
+    // The large-tile Gram kernel works on 256 x 256 token blocks (padded),
+    // at about three quarters of the direct kernel's rate per flop and with
+    // a fixed cost per block (two pipeline fills, a parked X Gram): measured
+    // on MI355X it wins once it needs at most half the direct kernel's flops.
+    const double gram = 2.0 * dpf::gram_big_items_per_sample(a.T) * 65536.0 * (din + dout);
+    return 2.0 * gram <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+  }
   // Gram costs T^2 (din + dout) per sample, the direct form 2 T din dout.
-  const double gram = (double)T * (double)T * (double)(din + dout);
-  const double direct = 2.0 * (double)T * (double)din * (double)dout;
-  return gram <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+  return T * T * (din + dout) <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
 }
 
 // Stream-ordered workspace carved into 256-byte aligned pieces.
@@ -153,8 +161,8 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
   L.args.dout = (int)G->D;
   L.args.mask = mask;
   L.args.nwords = (int)((X->T + dpf::kBitsTokens - 1) / dpf::kBitsTokens);
-  L.path = choose_path(X->T, X->D, G->D);
   L.vec = vec_ok(X) && vec_ok(G);
+  L.path = choose_path(L.args, L.vec);
   L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
   return L;
 }

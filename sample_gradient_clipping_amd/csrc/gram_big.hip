@@ -2,24 +2,32 @@
 //
 //   ||G~_i^T X~_i||^2 = sum_{s,t} (X~_i X~_i^T)[s,t] (G~_i G~_i^T)[s,t]
 //
-// One workgroup per (sample, 256-token row block S, 128-token column block
-// Tb) with Tb >= 2S, i.e. every tile that touches the upper triangle s <= t.
-// Each element is weighted 2 above the diagonal, 1 on it and 0 below, so the
-// symmetric sum is counted once.  The X Gram tile (K = din) and the G Gram
-// tile (K = dout) accumulate one after the other in registers; their
-// elementwise product is reduced wave -> LDS -> one fp64 partial per
-// workgroup, summed in a fixed order later (finalize_kernel).
+// Work item: (sample, 256-token row block S, 256-token column block Tb) with
+// S <= Tb, i.e. every block that touches the upper triangle s <= t.  Each
+// element is weighted 2 above the diagonal, 1 on it and 0 below, so the
+// symmetric sum is counted once (for a diagonal item that is the plain sum
+// of its block, which is symmetric).
 //
-// Workgroup: 512 threads = 8 waves (4 along s, 2 along t; two per SIMD);
-// each wave owns 64 x 64 of both Gram tiles: 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 accumulators per Gram (128 fp32 per lane).
+// Workgroup: 512 threads = 8 waves (2 along s, 4 along t; two per SIMD);
+// each wave owns 128 x 64 of the item's Gram tile: 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators (128 fp32 per lane), the shape of
+// the accumulate kernel's wave tile.  Only one Gram fits in registers, so an
+// item runs in two phases: the X Gram (K = din) is computed and parked in a
+// per-workgroup scratch buffer (256 KiB, thread-major, read back only by the
+// thread that wrote it), then the G Gram (K = dout); the epilogue multiplies
+// the two elementwise, weights and reduces wave -> LDS -> one fp64 partial per
+// item, summed in a fixed order later (finalize_kernel).
+//
 // Operands are feature-contiguous ("K-inner"): each lane's MFMA fragment is
-// one 16-byte LDS read.  Data moves global -> LDS by 16-byte-per-lane buffer
-// loads that write LDS directly into a ring of three 48 KiB slots (64
-// features of 256 + 128 token rows); rows are 128 bytes with the 16-byte
-// chunk c of row r stored at c ^ ((r >> 1) & 7), which keeps both the DMA
-// writes and the fragment reads free of bank conflicts.  Masked tokens and
-// rows past T read through out-of-range buffer offsets (zeros).
+// one 16-byte LDS read.  A phase streams 32-feature steps of the item's 256 s
+// rows and 256 t rows (32 KiB) from global memory into a ring of five LDS
+// slots with 16-byte-per-lane buffer loads that write LDS directly; rows are
+// 64 bytes with the 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3),
+// which keeps the fragment reads free of bank conflicts.  The main loop has
+// the accumulate kernel's structure: two 16-feature substeps of eight MFMAs
+// per step, fragments double-buffered and read between MFMAs, one barrier
+// per step, each step's DMAs issued four steps ahead.  Masked tokens and rows
+// past T read through out-of-range buffer offsets (zeros).
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -29,20 +37,35 @@ namespace dpf {
 namespace gram {
 
 constexpr int kNT = 512;
-constexpr int kWaveRows = 4, kWaveCols = 2;
-constexpr int kRowsS = 256, kRowsT = 128;
-constexpr int kKF = 64;                         // features per step
-constexpr int kRowBytes = kKF * 2;              // 128
-constexpr int kSBytes = kRowsS * kRowBytes;     // 32 KiB
-constexpr int kSlotBytes = kSBytes + kRowsT * kRowBytes;   // 48 KiB
-constexpr int kStages = 3;
-constexpr int kLdsBytes = kStages * kSlotBytes;            // 144 KiB
-constexpr int kDmaPerStep = kSlotBytes / 1024 / (kNT / 64);  // 6 per wave
+constexpr int kWaveRows = 2, kWaveCols = 4;    // wave grid: 2 along s, 4 along t
+constexpr int kBA = 4, kBO = 2;                // 32x32 blocks per wave: 128 (s) x 64 (t)
+constexpr int kRows = 256;                     // token rows on each side of an item
+constexpr int kKF = 32;                        // features per step
+constexpr int kRowBytes = kKF * 2;             // 64
+constexpr int kSideBytes = kRows * kRowBytes;  // 16 KiB
+constexpr int kStageBytes = 2 * kSideBytes;    // 32 KiB: the s rows, then the t rows
+constexpr int kStages = 5;
+constexpr int kLdsBytes = kStages * kStageBytes;   // 160 KiB: all of gfx950's LDS
+constexpr int kWaves = kNT / 64;
+constexpr int kDmaPerStep = kStageBytes / 1024 / kWaves;   // 4 per wave, 16 rows each
 constexpr int kOOB = 0x7ffffff0;
+constexpr int kAccFloats = kBA * kBO * 16;            // 128 per lane
+constexpr int kGramFloats = kAccFloats * kNT;         // one Gram tile, thread-major
+constexpr int kMaxSplit = 16;
 
 typedef __attribute__((address_space(4))) const uint32_t c_u32;
 
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// The thread index, hidden from the optimiser: addressing derived from it
+// is then computed where it is used, once per item, instead of being hoisted
+// out of the item loop and kept live (in registers it does not have) across
+// the whole kernel.
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // 16 bytes per lane from rsrc at voffset + soffset straight into LDS at
 // m0 + 16 * lane.  soffset is wave-uniform (the step's feature offset).
@@ -56,10 +79,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, 
 
 // Wait until at most `steps` of this wave's most recent DMA steps are in flight.
 __device__ __forceinline__ void wait_dma(int steps) {
-  static_assert(kDmaPerStep == 6, "wait_dma encodes 6 DMAs per step");
+  static_assert(kDmaPerStep == 4, "wait_dma encodes 4 DMAs per step");
   if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (steps == 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (steps == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (steps == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (steps == 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -74,92 +99,70 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sample_rsrc(const Act& a, int 
                                            0x00020000);
 }
 
-// Work items per sample for T tokens.
+// Work items per sample for T tokens: the upper triangle (with the diagonal)
+// of nB x nB blocks of 256 tokens.
 __device__ __host__ __forceinline__ int items_per_sample(int T) {
-  const int nS = (T + kRowsS - 1) / kRowsS, nTb = (T + kRowsT - 1) / kRowsT;
-  int n = 0;
-  for (int S = 0; S < nS; ++S) n += (nTb - 2 * S > 0) ? nTb - 2 * S : 0;
-  return n;
+  const int nB = (T + kRows - 1) / kRows;
+  return nB * (nB + 1) / 2;
 }
 
-// Per-lane DMA addressing for this workgroup's rows.  DMA j of wave w is
-// instruction q = 6 w + j of the slot: q < 32 fills s-rows 8q .. 8q+7, the
-// rest t-rows; lane l fills physical chunk l % 8 of row l / 8 of that group,
-// i.e. logical feature chunk (l % 8) ^ swizzle(row).
+// Sample, row block S and column block Tb >= S of item L (L = b * per_sample
+// + index of (S, Tb) within the sample, S-major).
+__device__ __forceinline__ void item_coords(int L, int per_sample, int T, int* b, int* S, int* Tb) {
+  *b = L / per_sample;
+  int r = L % per_sample;
+  const int nB = (T + kRows - 1) / kRows;
+  int s = 0;
+  while (r >= nB - s) { r -= nB - s; ++s; }
+  *S = s;
+  *Tb = s + r;
+}
+
+// Per-lane DMA addressing of one side (X or G) of an item.  DMA j of wave w
+// fills stage rows 16 (4 w + j) .. +15 (rows < 256: the s rows, the rest the
+// t rows); lane l fills physical chunk l % 4 of row l / 4 of that group, i.e.
+// logical feature chunk swz(row, l % 4).
 struct DmaLane {
-  uint32_t xoff[kDmaPerStep], goff[kDmaPerStep];   // row offset + chunk, or kOOB
-  int cfeat[kDmaPerStep];                          // first feature of the chunk
-  __device__ __forceinline__ void init(const LayerArgs& p, int b, int S, int Tb) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t off[kDmaPerStep];   // token row offset + chunk offset (bytes), or kOOB
+  int cfeat[kDmaPerStep];      // first feature of the lane's chunk within a step
+  __device__ __forceinline__ void init(const LayerArgs& p, const Act& a, int b, int S, int Tb,
+                                       int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int j = 0; j < kDmaPerStep; ++j) {
-      const int q = kDmaPerStep * wave + j;
-      const bool sreg = q < kRowsS / 8;
-      const int row = (sreg ? 8 * q : 8 * (q - kRowsS / 8)) + (lane >> 3);
-      const int tok = sreg ? kRowsS * S + row : kRowsT * Tb + row;
+      const int row = 16 * (kDmaPerStep * wave + j) + (lane >> 2);
+      const int c = swz(row, lane & 3);
+      const int tok = row < kRows ? kRows * S + row : kRows * Tb + (row - kRows);
       bool active = tok < p.T;
       if (active && p.rowbits != nullptr)
         active = (p.rowbits[(int64_t)b * p.nwords + (tok >> 5)] >> (tok & 31)) & 1u;
-      const int c = swz(row, lane & 7);
-      cfeat[j] = c * 8;
-      xoff[j] = active ? (uint32_t)(((int64_t)tok * p.X.stride_t + c * 8) * 2) : (uint32_t)kOOB;
-      goff[j] = active ? (uint32_t)(((int64_t)tok * p.G.stride_t + c * 8) * 2) : (uint32_t)kOOB;
+      cfeat[j] = 8 * c;
+      off[j] = active ? (uint32_t)(((int64_t)tok * a.stride_t + 8 * c) * 2) : (uint32_t)kOOB;
     }
   }
 };
 
-// What the DMAs of one feature step need, computed once per step: the
-// descriptor and feature offset (the instruction's scalar offset) of the X
-// or G rows, and whether the step runs past D (then each lane tests its
-// chunk and sends the chunks past D out of range).
-// Steps are queued in order, X steps first: the lane's row offsets in dl.xoff
-// are replaced by its G offsets once, when the first G step is queued.
+// The DMAs of one 32-feature step k of a side with D features: the
+// feature offset rides in the instruction's scalar offset; only a step that
+// runs past D tests each lane's chunk (D is a multiple of 8 on this path, so
+// a chunk is wholly inside or wholly past the end).
 struct StepDma {
-  __amdgpu_buffer_rsrc_t r;
   uint32_t soff;
   int k0, D;
   bool tail;
-  __device__ __forceinline__ void at(const LayerArgs& p, DmaLane& dl, __amdgpu_buffer_rsrc_t rx,
-                                     __amdgpu_buffer_rsrc_t rg, int step, int nkx, bool& on_g) {
-    const bool xs = step < nkx;
-    if (!xs && !on_g) {
-#pragma unroll
-      for (int j = 0; j < kDmaPerStep; ++j) dl.xoff[j] = dl.goff[j];
-      on_g = true;
-    }
-    k0 = (xs ? step : step - nkx) * kKF;
-    D = xs ? p.din : p.dout;
-    r = xs ? rx : rg;
+  __device__ __forceinline__ void at(int k, int Dd) {
+    k0 = k * kKF;
+    D = Dd;
     soff = (uint32_t)k0 * 2u;
     tail = k0 + kKF > D;
   }
-  // DMA j of the step into the slot whose address for this wave's DMAs is
-  // `dst`; TAIL: the step runs past D.
-  template <bool TAIL>
-  __device__ __forceinline__ void dma_(const DmaLane& dl, uint32_t dst, int j) const {
-    int off = (int)dl.xoff[j];
-    if (TAIL && k0 + dl.cfeat[j] >= D) off = kOOB;
+  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const DmaLane& dl, uint32_t dst,
+                                      int j) const {
+    int off = (int)dl.off[j];
+    if (__builtin_expect(tail, 0) && k0 + dl.cfeat[j] >= D) off = kOOB;
     dma16(r, off, dst + (uint32_t)j * 1024u, soff);
   }
-  // DMAs j0 .. j0+cnt-1.  Tail steps (only when D is not a multiple of the
-  // step's 64 features) take a separate branch, so that the common path
-  // carries no per-lane test.
-  __device__ __forceinline__ void dmas(const DmaLane& dl, uint32_t dst, int j0, int cnt) const {
-    if (__builtin_expect(tail, 0)) {
-      for (int j = j0; j < j0 + cnt; ++j) dma_<true>(dl, dst, j);
-    } else {
-      for (int j = j0; j < j0 + cnt; ++j) dma_<false>(dl, dst, j);
-    }
-  }
 };
-
-__device__ __forceinline__ void issue_step(const LayerArgs& p, DmaLane& dl,
-                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rg,
-                                           int step, int nkx, uint32_t dst, bool& on_g) {
-  StepDma sd;
-  sd.at(p, dl, rx, rg, step, nkx, on_g);
-  sd.dmas(dl, dst, 0, kDmaPerStep);
-}
 
 // All of this wave's LDS reads have returned.  Issued as the compiler's own
 // wait instruction, so that its bookkeeping of outstanding LDS reads restarts
@@ -180,56 +183,215 @@ __device__ __forceinline__ void step_barrier() {
 // MFMAs with LDS reads and DMA issue that the main loop spells out.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// MFMA operand for rows m0..m0+31 of a region, 16-feature substep ks.
-__device__ __forceinline__ u16x8 frag(const unsigned char* region, int m0, int ks) {
+// MFMA operand for rows m0..m0+31 of a side, 16-feature substep ks.
+__device__ __forceinline__ u16x8 frag(const unsigned char* side, int m0, int ks) {
   const int lane = threadIdx.x & 63;
   const int row = m0 + (lane & 31);
   const int c = 2 * ks + (lane >> 5);
-  return *(const u16x8*)(region + row * kRowBytes + swz(row, c) * 16);
+  return *(const u16x8*)(side + row * kRowBytes + swz(row, c) * 16);
 }
 
-struct Acc2 {
-  f32x16 v[2][2];
+struct Frags {
+  u16x8 a[kBA], b[kBO];
+};
+
+__device__ __forceinline__ int wave_row() { return (threadIdx.x >> 6) / kWaveCols; }
+__device__ __forceinline__ int wave_col() { return (threadIdx.x >> 6) % kWaveCols; }
+
+// Fragment q of a substep: q = 0, 1 the t blocks b[0], b[1]; q = 2..5 the s
+// blocks a[0..3] -- the order in which the MFMAs first need them.
+__device__ __forceinline__ void read_frag(Frags& f, const unsigned char* stage, int ks, int q) {
+  if (q < kBO) f.b[q] = frag(stage + kSideBytes, wave_col() * (kBO * 32) + q * 32, ks);
+  else f.a[q - kBO] = frag(stage, wave_row() * (kBA * 32) + (q - kBO) * 32, ks);
+}
+
+struct Acc {
+  f32x16 v[kBA][kBO];
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBA; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kBO; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
   }
-  // Keep the accumulators in accumulation registers (AGPRs): with two Gram
-  // tiles live, ordinary VGPRs would overflow.
+  // Keep the accumulators in accumulation registers (AGPRs), which the MFMAs
+  // read and write directly; in ordinary VGPRs they would not fit beside the
+  // fragments and addresses.
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBA; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(v[i][j]));
+      for (int j = 0; j < kBO; ++j) asm volatile("" : "+a"(v[i][j]));
   }
-  // MFMA k of a 16-feature substep: block (k / 2, k % 2).
-  __device__ __forceinline__ void mma1(const u16x8 (&f)[4], int k) {
-    v[k >> 1][k & 1] = mfma_32x32x16(f[k >> 1], f[2 + (k & 1)], v[k >> 1][k & 1]);
+  // MFMA k of a substep: block (k / kBO, k % kBO).
+  __device__ __forceinline__ void mma1(const Frags& f, int k) {
+    v[k / kBO][k % kBO] = mfma_32x32x16(f.a[k / kBO], f.b[k % kBO], v[k / kBO][k % kBO]);
   }
 };
 
-// Fragment q of 16-feature substep ks of this wave: q = 0, 1 the s blocks
-// (rows wm*64 + 32q), q = 2, 3 the t blocks (rows wn*64 + 32(q-2)).
-__device__ __forceinline__ void read_frag(u16x8 (&f)[4], const unsigned char* slot, int ks, int q) {
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / kWaveCols, wn = wave % kWaveCols;
-  f[q] = q < 2 ? frag(slot, wm * 64 + q * 32, ks) : frag(slot + kSBytes, wn * 64 + (q - 2) * 32, ks);
+// Steps k0 .. k0+n-1 (32 features each) of one side (a: X or G, D features)
+// of item (b, S, Tb) into acc.
+//
+// Five 32 KiB LDS slots.  Barrier i (between the two substeps of step i)
+// certifies that step i+1 has landed for every wave and that every wave's
+// reads of step i-1 are complete; slot (i-1) is then refilled with step i+4:
+//
+//   substep 0 of step i : MFMAs on f0, reads of f1 (step i, features 16..31)
+//   wait for f1, wait for step i+1's DMA, barrier
+//   substep 1 of step i : MFMAs on f1, DMA of step i+4, reads of f0 (step i+1)
+__device__ __forceinline__ void run(const LayerArgs& p, const Act& a, int D, int b, int S, int Tb,
+                                    int k0, int n, Acc& acc, unsigned char* lds) {
+  static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
+  acc.zero();
+  if (n <= 0) return;
+  const __amdgpu_buffer_rsrc_t r = sample_rsrc(a, b, p.T, D);
+  const int tid = opaque_tid();
+  DmaLane dl;
+  dl.init(p, a, b, S, Tb, tid);
+  const uint32_t base = lds_addr(lds);
+  // This wave's DMAs fill kDmaPerStep consecutive KiB of a slot.
+  const uint32_t wdst = (uint32_t)(kDmaPerStep * __builtin_amdgcn_readfirstlane(tid >> 6)) * 1024u;
+#pragma unroll
+  for (int k = 0; k < kStages; ++k) {
+    if (k < n) {
+      StepDma sd;
+      sd.at(k0 + k, D);
+#pragma unroll
+      for (int j = 0; j < kDmaPerStep; ++j) sd.dma(r, dl, base + k * kStageBytes + wdst, j);
+    }
+  }
+  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
+  step_barrier();
+  Frags f0, f1;
+#pragma unroll
+  for (int q = 0; q < 6; ++q) read_frag(f0, lds, 0, q);
+  int slot = 0;                        // i % kStages
+  for (int i = 0; i < n; ++i) {
+    const unsigned char* st = lds + slot * kStageBytes;
+    acc.pin();
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc.mma1(f0, k);
+      sched_fence();
+      if (k < 6) read_frag(f1, st, 1, k);
+      sched_fence();
+    }
+    lds_reads_done();                  // f1 is in registers; slot i-1 is no longer read
+    const int next = (slot + 1 == kStages) ? 0 : slot + 1;
+    const unsigned char* sn = lds + next * kStageBytes;
+    // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
+    // at barrier j >= 1, i.e. up to max(4, i+3).  Wait for step i+1: in the
+    // steady state that leaves two steps in flight.
+    const bool steady = i >= 1 && i + kStages - 1 < n;
+    if (steady) {
+      wait_dma(2);
+      step_barrier();
+    } else if (i + 1 < n) {
+      wait_dma(min(n - 1, i <= 1 ? kStages - 1 : i + kStages - 2) - (i + 1));
+      step_barrier();
+    }
+    // slot (i-1) % kStages is free: queue step i+4 into it, one DMA after
+    // every other MFMA.  The reads of f0 follow; on the last step they read
+    // the next slot's stale contents, which are never used.
+    const uint32_t prev = base + ((slot == 0) ? kStages - 1 : slot - 1) * kStageBytes + wdst;
+    StepDma sd;
+    if (steady) sd.at(k0 + i + kStages - 1, D);   // step i+4 of this side
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc.mma1(f1, k);
+      sched_fence();
+      if ((k & 1) == 0 && steady) sd.dma(r, dl, prev, k >> 1);
+      if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
+      sched_fence();
+    }
+    slot = next;
+  }
+  __syncthreads();                     // every wave is done with the slot ring
 }
 
-// Sample, row block S and column block Tb of item L (L = b * per_sample +
-// index of (S, Tb) within the sample, S-major).
-__device__ __forceinline__ void item_coords(int L, int per_sample, int T, int* b, int* S, int* Tb) {
-  *b = L / per_sample;
-  int r = L % per_sample;
-  const int nTb = (T + kRowsT - 1) / kRowsT;
-  int s = 0;
-  while (r >= nTb - 2 * s) { r -= nTb - 2 * s; ++s; }
-  *S = s;
-  *Tb = 2 * s + r;
+// A Gram tile's accumulators, thread-major: f32x4 x of thread tid at
+// [x][tid], so that the stores and loads of consecutive threads are
+// contiguous.  Quad x = (i * kBO + j) * 4 + q holds block (i, j) registers
+// 4q .. 4q+3.
+__device__ __forceinline__ void store_gram(float* dst, const Acc& acc) {
+  const int tid = opaque_tid();
+  f32x4* d = (f32x4*)dst + tid;
+#pragma unroll
+  for (int i = 0; i < kBA; ++i)
+#pragma unroll
+    for (int j = 0; j < kBO; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+        v.x = acc.v[i][j][4 * q]; v.y = acc.v[i][j][4 * q + 1];
+        v.z = acc.v[i][j][4 * q + 2]; v.w = acc.v[i][j][4 * q + 3];
+        d[((i * kBO + j) * 4 + q) * kNT] = v;
+        if (q == 3) sched_fence();   // one block's registers at a time
+      }
+}
+
+// Weight of an item's elements in the symmetric sum.  Off the diagonal
+// (S < Tb) every element has s < t: weight 2.  A diagonal item (S == Tb)
+// pairs the same 256 tokens on both sides, so both of its Gram blocks are
+// symmetric and the sum above its diagonal equals the sum below: weighting
+// 2 above, 1 on and 0 below gives the plain sum of the whole block.
+__device__ __forceinline__ float item_weight(int S, int Tb) { return S < Tb ? 2.0f : 1.0f; }
+
+// Sum over this thread's elements of xg * gg, with xg a thread-major Gram
+// tile (layout at store_gram) and gg the accumulators.
+__device__ __forceinline__ float product_sum(const float* xg, const Acc& gg) {
+  const int tid = opaque_tid();
+  const f32x4* dx = (const f32x4*)xg + tid;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kBA; ++i)
+#pragma unroll
+    for (int j = 0; j < kBO; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 u = dx[((i * kBO + j) * 4 + q) * kNT];
+        sum += u.x * gg.v[i][j][4 * q] + u.y * gg.v[i][j][4 * q + 1] +
+               u.z * gg.v[i][j][4 * q + 2] + u.w * gg.v[i][j][4 * q + 3];
+      }
+      if (j == kBO - 1) sched_fence();   // 8 loaded quads at a time
+    }
+  return sum;
+}
+
+// Work plan: G persistent workgroups; the first D*G items in D full rounds
+// (item d*G + L to workgroup L); each of the R remaining items split into P
+// chunks of its feature steps (X steps first, then G steps; P == 1: not
+// split), piece pi = c*R + r going to workgroup pi mod G.  A piece stores
+// the partial Gram of each side it touches; the fixup kernel finishes split
+// items.
+struct GramPlan {
+  int G, D, R, P;
+};
+
+// D, R and P for `items` items of n feature steps on G workgroups, with at
+// most `cap` pieces.  Cost model in microseconds from measurements on MI355X:
+// a 32-feature step of a 256 x 256 item ~0.8 us; a piece's pipeline fill and
+// partial store ~8 us; the fixup ~10 us plus 0.1 us per piece.  Runs on the
+// host, and on the device for masked calls, where only the device knows how
+// many items hold an active token.
+__host__ __device__ inline GramPlan split_items(int items, int G, int n, int cap) {
+  GramPlan gp{G, items / G, items % G, 1};
+  if (gp.R == 0) return gp;
+  const double step_us = 0.8, piece_us = 8.0;
+  double best = n * step_us + piece_us;
+  for (int P = 2; P <= kMaxSplit; ++P) {
+    if ((double)n / P < 8.0 || gp.R * P > cap) break;
+    const int S = (gp.R * P + G - 1) / G;
+    const double t = S * ((double)n / P * step_us + piece_us) + 10.0 + 0.1 * gp.R * P;
+    if (t < best) {
+      best = t;
+      gp.P = P;
+    }
+  }
+  return gp;
 }
 
 // Workgroups are dealt to the 8 XCDs round robin; logical index of this
@@ -239,265 +401,133 @@ __device__ __forceinline__ int logical_wg(int id, int G) {
   return (G % 8 == 0) ? (id & 7) * (G / 8) + (id >> 3) : id;
 }
 
-// Feature steps [k0, k1) of item (b, S, Tb) into ax (steps < nkx: X Gram)
-// and ag (the rest: G Gram).
-//
-// Three 48 KiB slots of 64 features = four 16-feature substeps.  Fragments
-// are double-buffered: the MFMAs of one substep run on registers while the
-// next substep's fragments are read, one read between consecutive MFMAs.
-// Barrier i comes before the last substep of step i: it certifies that step
-// i+1 has landed for every wave and that every wave has read all of step i,
-// whose slot is then refilled with step i+3 (its DMAs interleaved with the
-// last substep's MFMAs), leaving two steps in flight.
-__device__ __forceinline__ void run_item(const LayerArgs& p, int b, int S, int Tb, int k0, int k1,
-                                         Acc2& ax, Acc2& ag, unsigned char* smem) {
-  static_assert(kKF / 16 == 4 && kDmaPerStep == 6, "the interleave encodes 4 substeps, 6 DMAs");
-  const int nkx = (p.din + kKF - 1) / kKF;
-  const int n = k1 - k0;
-  const __amdgpu_buffer_rsrc_t rx = sample_rsrc(p.X, b, p.T, p.din);
-  const __amdgpu_buffer_rsrc_t rg = sample_rsrc(p.G, b, p.T, p.dout);
-  DmaLane dl;
-  dl.init(p, b, S, Tb);
-  const uint32_t base = lds_addr(smem);
-  // This wave's DMAs fill kDmaPerStep consecutive KiB of a slot.
-  const uint32_t wdst =
-      base + (uint32_t)(kDmaPerStep * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 1024u;
-  bool on_g = false;
-#pragma unroll
-  for (int k = 0; k < kStages; ++k)
-    if (k < n) issue_step(p, dl, rx, rg, k0 + k, nkx, wdst + k * kSlotBytes, on_g);
-  ax.zero();
-  ag.zero();
-  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
-  step_barrier();
-  u16x8 f0[4], f1[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) read_frag(f0, smem, 0, (q == 1) ? 2 : (q == 2) ? 3 : (q == 3) ? 1 : 0);
-  int slot = 0;
-  // Fragments in the order the MFMAs first need them: s block 0, t blocks
-  // 0 and 1, s block 1; two reads before a substep's first MFMA (the
-  // previous substep released their registers) and two after it.
-  constexpr int kNeed[4] = {0, 2, 3, 1};
-  auto substep = [&](Acc2& acc, const u16x8 (&f)[4], u16x8 (&g)[4], const unsigned char* st,
-                     int ks) {
-    read_frag(g, st, ks, kNeed[0]);
-    read_frag(g, st, ks, kNeed[1]);
-    sched_fence();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc.mma1(f, k);
-      sched_fence();
-      if (k == 0) {
-        read_frag(g, st, ks, kNeed[2]);
-        read_frag(g, st, ks, kNeed[3]);
-      }
-      sched_fence();
-    }
-  };
-  auto body = [&](int i, Acc2& acc) {
-    const unsigned char* st = smem + slot * kSlotBytes;
-    sched_fence();
-    substep(acc, f0, f1, st, 1);             // substep 0 on f0, read substep 1
-    substep(acc, f1, f0, st, 2);             // substep 1 on f1, read substep 2
-    substep(acc, f0, f1, st, 3);             // substep 2 on f0, read substep 3
-    lds_reads_done();                        // all of step i is in registers
-    const int next = (slot + 1 == kStages) ? 0 : slot + 1;
-    if (i + 1 < n) {
-      // Issued so far: steps 0..2 before the loop, then step j+3 at barrier
-      // j < i, i.e. up to i+2.  Wait for step i+1.
-      wait_dma(min(n - 1, i + kStages - 1) - (i + 1));
-      step_barrier();
-    }
-    const bool refill = i + kStages < n;
-    const uint32_t dst = wdst + slot * kSlotBytes;
-    StepDma sd;
-    if (refill) sd.at(p, dl, rx, rg, k0 + i + kStages, nkx, on_g);
-    const unsigned char* sn = smem + next * kSlotBytes;
-    // substep 3 on f1, reads of step i+1 (stale on the last step, never
-    // used), DMA of step i+3
-    read_frag(f0, sn, 0, kNeed[0]);
-    read_frag(f0, sn, 0, kNeed[1]);
-    sched_fence();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc.mma1(f1, k);
-      sched_fence();
-      if (k == 0) {
-        read_frag(f0, sn, 0, kNeed[2]);
-        read_frag(f0, sn, 0, kNeed[3]);
-      }
-      if (k >= 1 && refill) sd.dmas(dl, dst, 2 * (k - 1), 2);
-      sched_fence();
-    }
-    slot = next;
-  };
-  const int nx = max(0, min(k1, nkx) - k0);   // X steps of this range
-  int i = 0;
-  for (; i < nx; ++i) body(i, ax);   // X Gram, K = din
-  for (; i < n; ++i) body(i, ag);    // G Gram, K = dout
-  __syncthreads();                   // every wave is done with the slot ring
-}
-
-// Weighted sum of ax .* ag over this thread's elements of item (S, Tb):
-// weight 2 above the diagonal (s < t), 1 on it, 0 below.  Rows past T and
-// masked rows are zero in both Grams.
-__device__ __forceinline__ float weighted_product(const Acc2& ax, const Acc2& ag, int S, int Tb) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave / kWaveCols, wn = wave % kWaveCols;
-  const bool above = kRowsT * Tb >= kRowsS * (S + 1);   // whole tile has s < t
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float prod = ax.v[i][j][r] * ag.v[i][j][r];
-        if (above) {
-          sum += 2.0f * prod;
-        } else {
-          const int s = kRowsS * S + wm * 64 + i * 32 + acc_row(r, lane);
-          const int t = kRowsT * Tb + wn * 64 + j * 32 + acc_col(lane);
-          sum += (s < t) ? 2.0f * prod : ((s == t) ? prod : 0.0f);
-        }
-      }
-  return sum;
-}
-
-// Work plan (host-computed): G persistent workgroups; the first D*G items in
-// D full rounds (item d*G + L to workgroup L); each of the R remaining items
-// split into P chunks of its feature steps (P == 1: not split), piece
-// pi = c*R + r going to workgroup pi mod G.  A piece stores its partial
-// Grams; the fixup kernel finishes split items.
-struct GramPlan {
-  int G, D, R, P;
-};
-
-constexpr int kMaxSplit = 16;
-
-// D, R and P for `items` items of n feature steps on G workgroups, with at
-// most `cap` pieces.  Cost model from measurements on MI355X: a 64-feature
-// step of a 256 x 128 item ~0.8 us; a piece's fill and partial store ~10 us;
-// the fixup ~10 us plus 0.13 us per piece.  Runs on the host, and on the
-// device for masked calls, where only the device knows how many items hold
-// an active token.
-__host__ __device__ inline GramPlan split_items(int items, int G, int n, int cap) {
-  GramPlan gp{G, items / G, items % G, 1};
-  if (gp.R == 0) return gp;
-  const double step_us = 0.8, piece_us = 10.0;
-  double best = n * step_us + piece_us;
-  for (int P = 2; P <= kMaxSplit; ++P) {
-    if ((double)n / P < 8.0 || gp.R * P > cap) break;
-    const int S = (gp.R * P + G - 1) / G;
-    const double t = S * ((double)n / P * step_us + piece_us) + 10.0 + 0.13 * gp.R * P;
-    if (t < best) {
-      best = t;
-      gp.P = P;
-    }
+// Feature steps [c0, c1) of the concatenated sequence (X steps, then G
+// steps) split into the X part [x0, x1) and the G part [g0, g1).
+struct Parts {
+  int x0, x1, g0, g1;
+  __device__ __forceinline__ Parts(int c0, int c1, int nkx) {
+    x0 = min(c0, nkx);
+    x1 = min(c1, nkx);
+    g0 = max(c0, nkx) - nkx;
+    g1 = max(c1, nkx) - nkx;
   }
-  return gp;
-}
-
-// A piece's partial Grams: 128 floats per thread (64 of X, then 64 of G),
-// stored as f32x4 q of thread tid at [q][tid] so that stores and loads of
-// consecutive threads are contiguous.
-constexpr int kPieceFloats = 128 * kNT;
-
-__device__ __forceinline__ void store_piece(float* dst, const Acc2& ax, const Acc2& ag) {
-  f32x4* d = (f32x4*)dst;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int x = (i * 2 + j) * 4 + q;
-        f32x4 v;
-        v.x = ax.v[i][j][4 * q]; v.y = ax.v[i][j][4 * q + 1];
-        v.z = ax.v[i][j][4 * q + 2]; v.w = ax.v[i][j][4 * q + 3];
-        d[x * kNT + threadIdx.x] = v;
-        v.x = ag.v[i][j][4 * q]; v.y = ag.v[i][j][4 * q + 1];
-        v.z = ag.v[i][j][4 * q + 2]; v.w = ag.v[i][j][4 * q + 3];
-        d[(16 + x) * kNT + threadIdx.x] = v;
-      }
-}
-
-__device__ __forceinline__ void add_piece(const float* src, Acc2& ax, Acc2& ag) {
-  const f32x4* d = (const f32x4*)src;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int x = (i * 2 + j) * 4 + q;
-        const f32x4 u = d[x * kNT + threadIdx.x], w = d[(16 + x) * kNT + threadIdx.x];
-        ax.v[i][j][4 * q] += u.x; ax.v[i][j][4 * q + 1] += u.y;
-        ax.v[i][j][4 * q + 2] += u.z; ax.v[i][j][4 * q + 3] += u.w;
-        ag.v[i][j][4 * q] += w.x; ag.v[i][j][4 * q + 1] += w.y;
-        ag.v[i][j][4 * q + 2] += w.z; ag.v[i][j][4 * q + 3] += w.w;
-      }
-}
+};
 
 // Masked calls: live[0] = n, the number of items with an active token in
 // both of their row blocks, live[1 .. n] their indices in increasing order.
 // The other items are exactly zero; the list kernel stores their partials.
 // The plan over the n live items is made here, with at most `cap` pieces.
+// Workspace: xs = one X Gram per workgroup; pieces = two Gram tiles (X part,
+// G part) per piece.
 __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, GramPlan gp,
                                                                const uint32_t* live, int cap,
-                                                               float* ws) {
+                                                               float* xs, float* pieces) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int per_sample = items_per_sample(p.T);
-  const int n = (p.din + kKF - 1) / kKF + (p.dout + kKF - 1) / kKF;
+  const int nkx = (p.din + kKF - 1) / kKF, nkg = (p.dout + kKF - 1) / kKF;
+  const int n = nkx + nkg;
   const int L = logical_wg(blockIdx.x, gp.G);
   if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, n, cap);
   auto item_at = [&](int i) { return live != nullptr ? (int)((c_u32*)live)[1 + i] : i; };
-  Acc2 ax, ag;
-  auto full_item = [&](int item) {
+  // This workgroup's units: whole items d*G + L, then pieces L, L+G, ...
+  const int nfull = gp.D + ((gp.P == 1 && L < gp.R) ? 1 : 0);
+  const int npiece = gp.P == 1 ? 0 : (gp.R * gp.P - L + gp.G - 1) / gp.G;
+  float* mine = xs + (int64_t)L * kGramFloats;   // this workgroup's X Gram
+  Acc acc;
+  // Whole items: the X Gram to scratch, then the G Gram, multiplied with the
+  // X Gram read back by the threads that stored it.
+#pragma unroll 1
+  for (int u = 0; u < nfull; ++u) {
+    const int item = item_at(u * gp.G + L);
     int b, S, Tb;
     item_coords(item, per_sample, p.T, &b, &S, &Tb);
-    run_item(p, b, S, Tb, 0, n, ax, ag, smem);
-    const double tot = block_sum_f64((double)weighted_product(ax, ag, S, Tb), (double*)smem);
+    run(p, p.X, p.din, b, S, Tb, 0, nkx, acc, smem);
+    store_gram(mine, acc);
+    run(p, p.G, p.dout, b, S, Tb, 0, nkg, acc, smem);
+    const double tot =
+        block_sum_f64((double)(item_weight(S, Tb) * product_sum(mine, acc)), (double*)smem);
     if (threadIdx.x == 0) p.partials[item] = tot;
-    __syncthreads();                 // the reduction scratch is the next item's ring
-  };
-  for (int d = 0; d < gp.D; ++d) full_item(item_at(d * gp.G + L));
-  if (gp.P == 1) {
-    if (L < gp.R) full_item(item_at(gp.D * gp.G + L));
-    return;
+    __syncthreads();                 // the reduction scratch is the next unit's ring
   }
-  for (int pi = L; pi < gp.R * gp.P; pi += gp.G) {
-    const int c = pi / gp.R, item = item_at(gp.D * gp.G + pi % gp.R);
+  // Pieces: the partial Gram of each side the piece touches.
+#pragma unroll 1
+  for (int u = 0; u < npiece; ++u) {
+    const int pi = L + u * gp.G;
+    const int c = pi / gp.R;
+    const int item = item_at(gp.D * gp.G + pi % gp.R);
     int b, S, Tb;
     item_coords(item, per_sample, p.T, &b, &S, &Tb);
-    run_item(p, b, S, Tb, (int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), ax, ag,
-             smem);
-    store_piece(ws + (int64_t)pi * kPieceFloats, ax, ag);
+    const Parts pt((int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), nkx);
+    float* dst = pieces + (int64_t)pi * 2 * kGramFloats;
+#pragma unroll 1
+    for (int side = 0; side < 2; ++side) {
+      const int k0 = side ? pt.g0 : pt.x0, k1 = side ? pt.g1 : pt.x1;
+      if (k1 <= k0) continue;
+      run(p, side ? p.G : p.X, side ? p.dout : p.din, b, S, Tb, k0, k1 - k0, acc, smem);
+      store_gram(dst + side * kGramFloats, acc);
+    }
   }
 }
 
-// Split items: sum the P partial Grams in chunk order, then the weighted
-// product and its reduction, as for a whole item.  One workgroup per item,
-// with the main kernel's thread layout.  Masked calls launch one workgroup
-// per possible split item and make the plan as the main kernel does.
+// Split items: sum the partial X and G Grams of the P pieces in chunk order,
+// then the weighted product and its reduction, as for a whole item.  Each
+// item spreads over kFixParts workgroups (with the main kernel's thread
+// layout), workgroup h taking quads [h, h+1) * kAccFloats / 4 / kFixParts of
+// every thread; their fp64 sums go to part[r][h], which gram_fixup_sum_kernel
+// adds in order.  Masked calls launch workgroups for every possible split
+// item and make the plan as the main kernel does.
+constexpr int kFixParts = 8;
+constexpr int kFixQuads = kAccFloats / 4 / kFixParts;   // 4
 __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPlan gp,
                                                             const uint32_t* live, int cap,
-                                                            const float* ws) {
+                                                            const float* pieces, double* part) {
   __shared__ double red[kNT / 64];
-  const int n = (p.din + kKF - 1) / kKF + (p.dout + kKF - 1) / kKF;
+  const int nkx = (p.din + kKF - 1) / kKF, nkg = (p.dout + kKF - 1) / kKF;
+  const int n = nkx + nkg;
   if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, n, cap);
-  const int r = blockIdx.x;
+  const int r = blockIdx.x / kFixParts, h = blockIdx.x % kFixParts;
   if (gp.P == 1 || r >= gp.R) return;
   const int i = gp.D * gp.G + r;
   const int item = live != nullptr ? (int)((c_u32*)live)[1 + i] : i;
   int b, S, Tb;
   item_coords(item, items_per_sample(p.T), p.T, &b, &S, &Tb);
-  Acc2 ax, ag;
-  ax.zero();
-  ag.zero();
-  for (int c = 0; c < gp.P; ++c) add_piece(ws + (int64_t)(c * gp.R + r) * kPieceFloats, ax, ag);
-  const double tot = block_sum_f64((double)weighted_product(ax, ag, S, Tb), red);
-  if (threadIdx.x == 0) p.partials[item] = tot;
+  f32x4 sx[kFixQuads], sg[kFixQuads];
+#pragma unroll
+  for (int x = 0; x < kFixQuads; ++x) {
+    sx[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int c = 0; c < gp.P; ++c) {
+    const Parts pt((int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), nkx);
+    const f32x4* src = (const f32x4*)(pieces + (int64_t)(c * gp.R + r) * 2 * kGramFloats) +
+                       (h * kFixQuads) * kNT + threadIdx.x;
+#pragma unroll
+    for (int x = 0; x < kFixQuads; ++x) {
+      if (pt.x1 > pt.x0) sx[x] += src[x * kNT];
+      if (pt.g1 > pt.g0) sg[x] += src[kGramFloats / 4 + x * kNT];
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int x = 0; x < kFixQuads; ++x)
+    sum += sx[x].x * sg[x].x + sx[x].y * sg[x].y + sx[x].z * sg[x].z + sx[x].w * sg[x].w;
+  const double tot = block_sum_f64((double)(item_weight(S, Tb) * sum), red);
+  if (threadIdx.x == 0) part[r * kFixParts + h] = tot;
+}
+
+// partials[item] = sum over h of part[r][h], in order; one thread per split
+// item.
+__global__ void gram_fixup_sum_kernel(LayerArgs p, GramPlan gp, const uint32_t* live, int cap,
+                                      const double* part) {
+  const int nkx = (p.din + kKF - 1) / kKF, nkg = (p.dout + kKF - 1) / kKF;
+  if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, nkx + nkg, cap);
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gp.P == 1 || r >= gp.R) return;
+  const int i = gp.D * gp.G + r;
+  const int item = live != nullptr ? (int)((c_u32*)live)[1 + i] : i;
+  double s = 0.0;
+  for (int h = 0; h < kFixParts; ++h) s += part[r * kFixParts + h];
+  p.partials[item] = s;
 }
 
 // Live-item list of a masked call (layout at gram_norm_big_kernel) from the
@@ -510,6 +540,7 @@ __global__ void __launch_bounds__(kListThreads) live_items_kernel(LayerArgs p, u
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per_sample = items_per_sample(p.T);
   const int64_t total = (int64_t)p.B * per_sample;
+  constexpr int kWords = kRows / 32;   // row-bit words per block
   uint32_t base = 0;
   for (int64_t c0 = 0; c0 < total; c0 += kListThreads) {
     const int64_t i = c0 + tid;
@@ -519,8 +550,8 @@ __global__ void __launch_bounds__(kListThreads) live_items_kernel(LayerArgs p, u
       item_coords((int)i, per_sample, p.T, &b, &S, &Tb);
       const uint32_t* w = p.rowbits + (int64_t)b * p.nwords;
       uint32_t ws = 0, wt = 0;
-      for (int k = S * (kRowsS / 32); k < min((S + 1) * (kRowsS / 32), p.nwords); ++k) ws |= w[k];
-      for (int k = Tb * (kRowsT / 32); k < min((Tb + 1) * (kRowsT / 32), p.nwords); ++k) wt |= w[k];
+      for (int k = S * kWords; k < min((S + 1) * kWords, p.nwords); ++k) ws |= w[k];
+      for (int k = Tb * kWords; k < min((Tb + 1) * kWords, p.nwords); ++k) wt |= w[k];
       act = ws != 0u && wt != 0u;
       if (!act) p.partials[i] = 0.0;
     }
@@ -556,20 +587,28 @@ gram::GramPlan plan_gram(const LayerArgs& p) {
   return gp;
 }
 
-// Workspace of a masked call: the live-item list, then room for G pieces
-// (the device-side plan never splits into more).
-size_t live_list_bytes(const LayerArgs& p) {
-  const size_t b = ((size_t)p.B * gram::items_per_sample(p.T) + 1) * sizeof(uint32_t);
-  return (b + 255) & ~(size_t)255;
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace layout: [live-item list (masked calls)] [one X Gram per
+// workgroup] [two Gram tiles per piece] [fixup sums].  A masked call reserves room for G
+// pieces: the device-side plan never splits into more.
+struct GramWs {
+  size_t xs = 0, pieces = 0, part = 0, total = 0;
+};
+GramWs gram_ws(const LayerArgs& p, const gram::GramPlan& gp) {
+  GramWs w;
+  const size_t tile = (size_t)gram::kGramFloats * sizeof(float);
+  if (p.mask != nullptr) w.xs = round256(((size_t)p.B * gram::items_per_sample(p.T) + 1) * 4);
+  w.pieces = w.xs + (size_t)gp.G * tile;
+  const size_t npieces = p.mask != nullptr ? (size_t)gp.G : (gp.P == 1 ? 0 : (size_t)gp.R * gp.P);
+  w.part = w.pieces + npieces * 2 * tile;
+  // fixup sums: one row per possible split item (R < G)
+  w.total = w.part + round256((size_t)gp.G * gram::kFixParts * sizeof(double));
+  return w;
 }
 }  // namespace
 
-size_t gram_big_workspace_bytes(const LayerArgs& p) {
-  const gram::GramPlan gp = plan_gram(p);
-  if (p.mask != nullptr)
-    return live_list_bytes(p) + (size_t)gp.G * gram::kPieceFloats * sizeof(float);
-  return gp.P == 1 ? 0 : (size_t)gp.R * gp.P * gram::kPieceFloats * sizeof(float);
-}
+size_t gram_big_workspace_bytes(const LayerArgs& p) { return gram_ws(p, plan_gram(p)).total; }
 
 hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   static hipError_t once = hipFuncSetAttribute((const void*)gram::gram_norm_big_kernel,
@@ -578,13 +617,15 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   if (once != hipSuccess) return once;
   const gram::GramPlan gp = plan_gram(p);
   const bool masked = p.rowbits != nullptr;
-  if ((masked || gp.P != 1) && p.skws == nullptr) return hipErrorInvalidValue;
-  uint32_t* live = nullptr;
-  float* pieces = p.skws;
+  if (p.skws == nullptr) return hipErrorInvalidValue;
+  const GramWs w = gram_ws(p, gp);
+  char* base = reinterpret_cast<char*>(p.skws);
+  uint32_t* live = masked ? reinterpret_cast<uint32_t*>(base) : nullptr;
+  float* xs = reinterpret_cast<float*>(base + w.xs);
+  float* pieces = reinterpret_cast<float*>(base + w.pieces);
+  double* part = reinterpret_cast<double*>(base + w.part);
   hipError_t e;
   if (masked) {
-    live = reinterpret_cast<uint32_t*>(p.skws);
-    pieces = p.skws + live_list_bytes(p) / sizeof(float);
     timing_begin("live_items", s);
     hipLaunchKernelGGL(gram::live_items_kernel, dim3(1), dim3(gram::kListThreads), 0, s, p, live);
     e = hipGetLastError();
@@ -593,14 +634,19 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   }
   timing_begin("gram_norm", s);
   hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(gp.G), dim3(gram::kNT), gram::kLdsBytes, s, p,
-                     gp, (const uint32_t*)live, gp.G, pieces);
+                     gp, (const uint32_t*)live, gp.G, xs, pieces);
   e = hipGetLastError();
   timing_end("gram_norm", s);
   if (e != hipSuccess || (!masked && gp.P == 1)) return e;
+  const int nfix = masked ? gp.G : gp.R;   // items that may be split
   timing_begin("gram_fixup", s);
-  hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(masked ? gp.G : gp.R), dim3(gram::kNT), 0, s, p,
-                     gp, (const uint32_t*)live, gp.G, (const float*)pieces);
+  hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(nfix * gram::kFixParts), dim3(gram::kNT), 0, s,
+                     p, gp, (const uint32_t*)live, gp.G, (const float*)pieces, part);
   e = hipGetLastError();
+  if (e == hipSuccess)
+    hipLaunchKernelGGL(gram::gram_fixup_sum_kernel, dim3((nfix + 63) / 64), dim3(64), 0, s, p, gp,
+                       (const uint32_t*)live, gp.G, (const double*)part);
+  if (e == hipSuccess) e = hipGetLastError();
   timing_end("gram_fixup", s);
   return e;
 }

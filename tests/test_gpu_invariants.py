@@ -176,12 +176,14 @@ def test_kernel_timing_records_launches():
     G = torch.randn((2, 64, 128), device="cuda").to(torch.bfloat16)
     dp.timing_reset()
     dp.set_option("timing", 1)
+    dp.set_option("norm_path", 1)      # the Gram kernel, whatever the automatic choice
     try:
         for _ in range(3):
             dp.linear_clip_accumulate(X, G, None, C=1.0, sigma=1.0)
         t = dp.timing_collect()
     finally:
         dp.set_option("timing", 0)
+        dp.set_option("norm_path", 0)
         dp.timing_reset()
     assert t["accumulate"][1] == 3 and t["accumulate"][0] > 0
     assert t["gram_norm"][1] == 3 and t["finalize"][1] == 3
