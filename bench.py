@@ -145,6 +145,19 @@ def measure_configs(dp, torch, steps, warmup):
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
         "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+
+    # the same, with P drawn from its seed inside the projection (never stored)
+    def seeded_layer():
+        for lin, X, G, o, nrm in dev:
+            dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7, p_offset=0,
+                                                       C=lin.C, sigma=lin.sigma, grad_out=o,
+                                                       norms_out=nrm)
+    ms = time_calls(torch, seeded_layer, steps, warmup)
+    out["c5_roberta_large_projected_seeded_r256_6_linears"] = {
+        "note": "as above, P regenerated from Philox seed 7 inside the projection kernel",
+        "linears": len(lins), "ms": round(ms, 4),
+        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
     return out
 
 
@@ -363,6 +376,21 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     if args.configs:
+        # group clipping: one clip factor per sample over the seven linears
+        Xs = [X for (X, _, _, _) in dev_in]
+        Gs = [G for (_, G, _, _) in dev_in]
+        outs = [o for (_, _, o, _) in dev_in]
+        offs, at = [], 0
+        for l in lins:
+            offs.append(at)
+            at += (l.din * l.dout + 3) // 4
+        ms_group = time_calls(torch, lambda: dp.group_clip_accumulate(
+            Xs, Gs, None, C=1.0, sigma=1.0, offsets=offs, grad_outs=outs), args.steps, 2)
+        res["group_clip_layer"] = {
+            "note": "the same seven linears, clipped jointly (one c_i per sample over the layer)",
+            "ms": round(ms_group, 4), "useful_tflops": round(useful / (ms_group * 1e-3) / 1e12, 2),
+            "samples_per_s": round(args.batch / (ms_group * 1e-3), 1)}
+        del Xs, Gs, outs
         del dev_in
         torch.cuda.empty_cache()
         res["configs"] = measure_configs(dp, torch, args.steps, 2)

@@ -127,6 +127,29 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
                                                     float* grad_out, float* norms_out,
                                                     void* stream);
 
+/* Projected variant with the projection regenerated from a seed instead of
+ * stored (same explainer, Methodology, "Random Projection over SVD": the
+ * random matrices need not be kept, since they can be drawn again from their
+ * seed).  Identical to dpfused_linear_clip_accumulate_projected with
+ *
+ *   P[d][j] = p_scale * xi_{d*r + j}   (d < din, j < r)
+ *
+ * rounded to X's dtype, xi from Philox4x32-10 (p_seed, p_offset) as above --
+ * i.e. with the P that dpfused_gaussian_fill(p_seed, p_offset, din*r,
+ * p_scale, X's dtype) writes -- but P never exists in memory: the projection
+ * kernel draws each element where it needs it.  p_scale = 1/sqrt(r) gives
+ * the N(0, 1/r) entries of the method.
+ *
+ *   r         projection rank, a positive multiple of 8
+ *   p_scale   finite
+ *
+ * Errors as for the projected variant; r not a multiple of 8 gives
+ * DPF_ERR_UNSUPPORTED. */
+dpf_status dpfused_linear_clip_accumulate_projected_seeded(
+    const dpf_act* X, const dpf_act* G, const uint8_t* mask, int64_t r, uint64_t p_seed,
+    uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
+    float* grad_out, float* norms_out, void* stream);
+
 /* Per-sample squared norms ||G~_i^T X~_i||^2 only, in float64, written to
  * sqnorms_out[B] (device).  With accumulate != 0 the values are ADDED to what
  * sqnorms_out holds (summing over several linears gives the squared norm of
@@ -148,6 +171,35 @@ dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float
 dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                      const float* c, float noise_std, uint64_t seed,
                                      uint64_t offset, float* grad_out, void* stream);
+
+/* Group (joint) clipping over n linears that see the same samples, e.g. the
+ * seven linears of one decoder layer.  The FlashDP pages clip per layer
+ * (FlashDP, Abstract: per-layer DP-SGD, gradients computed once); this is the
+ * same step with the clipping norm taken over a group of layers instead of
+ * one, the form standard (flat) DP-SGD uses for the whole model:
+ *
+ *   n_i^2           = sum_l ||G~_il^T X~_il||_F^2
+ *   c_i             = 1 if n_i <= C, else C / n_i
+ *   grad_out[l]     = (sum_i c_i G~_il^T X~_il + sigma * C * xi^(l)) / B
+ *   norms_out[i]    = n_i (the group norm, before clipping)
+ *
+ * xi^(l) is the noise of the dense call with (seed, offsets[l]).  With n = 1
+ * it is dpfused_linear_clip_accumulate.
+ *
+ *   n          number of linears, >= 1
+ *   X, G       HOST arrays of n descriptors; every linear has the same B and T
+ *   mask       [B, T] or NULL, shared by the linears
+ *   offsets    HOST array of n Philox offsets
+ *   grad_out   HOST array of n DEVICE pointers, grad_out[l] [dout_l, din_l]
+ *   norms_out  [B] float32 or NULL
+ *
+ * Errors as for dpfused_linear_clip_accumulate, checked for every linear
+ * before anything is queued; B or T differing between linears gives
+ * DPF_ERR_INVALID_ARGUMENT. */
+dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_act* G,
+                                         const uint8_t* mask, float C, float sigma, uint64_t seed,
+                                         const uint64_t* offsets, float* const* grad_out,
+                                         float* norms_out, void* stream);
 
 /* Raw Philox4x32-10 words: out[4*j + k] = word k of block (offset + j),
  * j < nblocks, with the key/counter layout above.  out: device, 16-byte

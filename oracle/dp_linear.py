@@ -108,6 +108,61 @@ def oracle_linear(X, G, mask, C: float, sigma: float, seed: int, offset: int,
     return out / B, norms, c
 
 
+def oracle_group(linears, mask, C: float, sigma: float, seed: int, offsets,
+                 dtype: str = "bf16", with_noise: bool = True):
+    """Group (joint) clipping over linears that see the same samples.
+
+    The FlashDP abstract frames the method as per-layer clipping; clipping
+    over a group of layers is the same procedure with sample i's gradient
+    taken as the tuple (g_i^1, ..., g_i^L) of its per-layer gradients, whose
+    norm is that of the tuple flattened into one vector -- standard (flat)
+    DP-SGD restricted to those layers.  Steps 3-5 run on that vector; the
+    sum is split back per linear, and linear l gets the noise of
+    (seed, offsets[l]).
+
+    linears: list of (X, G) pairs in the storage dtype, same B and T.
+    Returns ([out_l [dout_l, din_l] f64], norms [B] f64, c [B] f64)."""
+    widened = [(widen(X, dtype), widen(G, dtype)) for X, G in linears]
+    B = widened[0][0].shape[0]
+    shapes = [(Gw.shape[2], Xw.shape[2]) for Xw, Gw in widened]
+
+    def flat_grads():
+        for i in range(B):
+            m = None if mask is None else mask[i]
+            yield np.concatenate([
+                per_sample_grad(select_active(Xw[i], m), select_active(Gw[i], m)).ravel()
+                for Xw, Gw in widened])
+
+    S, norms, c = clip_accumulate(flat_grads(), C)
+    outs, at = [], 0
+    for l, shape in enumerate(shapes):
+        n = shape[0] * shape[1]
+        o = S[at:at + n].reshape(shape).copy()
+        at += n
+        if with_noise and sigma != 0.0:
+            o = o + sigma * C * noise_matrix(seed, offsets[l], shape)
+        outs.append(o / B)
+    return outs, norms, c
+
+
+def projection_matrix(seed: int, offset: int, din: int, r: int, scale: float,
+                      dtype: str = "bf16") -> np.ndarray:
+    """P[d, j] = scale * xi_{d*r+j}(seed, offset) in the storage dtype (bf16
+    bits rounded to nearest even, or float32): the seeded projection of the
+    DP-GRAPE explainer (Methodology, random projections drawn again from their
+    seed rather than stored).  The normals are this module's float64 ones
+    rounded to float32 and scaled in float32, so a float32 generator may round
+    a few entries to the neighbouring bf16 value; comparisons against one use
+    a tolerance."""
+    v = (np.float32(scale) * philox.gaussian(seed, offset, din * r).astype(np.float32))
+    v = v.astype(np.float32).reshape(din, r)
+    if dtype == "f32":
+        return v
+    u = v.view(np.uint32)
+    out = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16))
+    return out.astype(np.uint16)
+
+
 def project_rows(Xi: np.ndarray, Pw: np.ndarray) -> np.ndarray:
     """Y_i = X~_i P (float64)."""
     return Xi @ Pw

@@ -14,13 +14,15 @@ and the pre-clip per-sample norms.  See include/dpfused.h for the contract.
 from __future__ import annotations
 
 import ctypes
+import math
 from typing import Optional, Tuple
 
 from . import _lib
 from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
 
 __all__ = [
-    "linear_clip_accumulate", "linear_clip_accumulate_projected", "per_sample_sqnorms",
+    "linear_clip_accumulate", "linear_clip_accumulate_projected",
+    "linear_clip_accumulate_projected_seeded", "group_clip_accumulate", "per_sample_sqnorms",
     "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
     "set_option", "get_option", "timing_reset", "timing_collect", "DpfError", "load",
 ]
@@ -116,6 +118,58 @@ def linear_clip_accumulate_projected(X, G, P, mask=None, C: float = 1.0, sigma: 
         _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
+
+
+def linear_clip_accumulate_projected_seeded(X, G, r: int, mask=None, p_seed: int = 0,
+                                            p_offset: int = 0, p_scale=None, C: float = 1.0,
+                                            sigma: float = 0.0, seed: int = 0, offset: int = 0,
+                                            grad_out=None, norms_out=None, stream=None,
+                                            want_norms: bool = True):
+    """Projected variant with P[d, j] = p_scale * xi_{d*r+j}(p_seed, p_offset) drawn inside
+    the projection (never stored); p_scale defaults to 1/sqrt(r)."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if p_scale is None:
+        p_scale = 1.0 / math.sqrt(r)
+    if grad_out is None:
+        grad_out = torch.empty((G.shape[2], r), dtype=torch.float32, device=X.device)
+    if norms_out is None and want_norms:
+        norms_out = torch.empty((B,), dtype=torch.float32, device=X.device)
+    st = _lib.lib().dpfused_linear_clip_accumulate_projected_seeded(
+        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), int(r), int(p_seed),
+        int(p_offset), float(p_scale), float(C), float(sigma), int(seed), int(offset),
+        grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
+    _lib.check(st)
+    return grad_out, norms_out
+
+
+def group_clip_accumulate(Xs, Gs, mask=None, C: float = 1.0, sigma: float = 0.0, seed: int = 0,
+                          offsets=None, grad_outs=None, norms_out=None, stream=None,
+                          want_norms: bool = True):
+    """Joint clipping over linears that see the same samples: one c_i from the norm of
+    sample i's gradient over all of them; returns ([grad_out per linear], norms)."""
+    torch = _torch()
+    n = len(Xs)
+    if n < 1 or len(Gs) != n:
+        raise ValueError("Xs and Gs must be non-empty lists of the same length")
+    acts = (DpfAct * n)(*[_act(x) for x in Xs])
+    gacts = (DpfAct * n)(*[_act(g) for g in Gs])
+    B, T = Xs[0].shape[0], Xs[0].shape[1]
+    if offsets is None:
+        offsets = [0] * n
+    if grad_outs is None:
+        grad_outs = [torch.empty((g.shape[2], x.shape[2]), dtype=torch.float32, device=x.device)
+                     for x, g in zip(Xs, Gs)]
+    if norms_out is None and want_norms:
+        norms_out = torch.empty((B,), dtype=torch.float32, device=Xs[0].device)
+    offs = (ctypes.c_uint64 * n)(*[int(o) for o in offsets])
+    outs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in grad_outs])
+    st = _lib.lib().dpfused_group_clip_accumulate(
+        n, acts, gacts, _mask_ptr(mask, B, T), float(C), float(sigma), int(seed), offs, outs,
+        _ptr(norms_out), _stream(Xs[0], stream))
+    _lib.check(st)
+    return grad_outs, norms_out
 
 
 def per_sample_sqnorms(X, G, mask=None, out=None, accumulate: bool = False, stream=None):

@@ -245,6 +245,102 @@ dpf_status check_clip(float C, float sigma) {
   return DPF_OK;
 }
 
+// Shared body of the projected calls: P read from memory (gen == 0) or
+// regenerated from (p_seed, p_offset, p_scale) inside the projection.
+dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, const void* P,
+                           int gen, uint64_t p_seed, uint64_t p_offset, float p_scale, int64_t r,
+                           float C, float sigma, uint64_t seed, uint64_t offset, float* grad_out,
+                           float* norms_out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t es = elem_size(X->dtype);
+
+  Workspace ws(s);
+  const size_t off_y = ws.reserve((size_t)X->B * X->T * r * es);
+  dpf::ProjArgs pa{};
+  pa.X = to_act(X);
+  pa.P = P;
+  pa.dtype = X->dtype;
+  pa.B = (int)X->B;
+  pa.T = (int)X->T;
+  pa.din = (int)X->D;
+  pa.r = (int)r;
+  pa.mask = mask;
+  pa.gen = gen;
+  pa.p_seed = p_seed;
+  pa.p_offset = p_offset;
+  pa.p_scale = p_scale;
+  pa.splits = dpf::project_splits(pa);
+  const size_t pbytes = dpf::project_workspace_bytes(pa);
+  const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
+  // Reserve the layer workspace now so that a single allocation covers both.
+  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
+  LayerPlan L = plan_layer(&Y, G, mask);
+  const LayerWs o = reserve_layer(L, ws, true, true, true);
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  Y.data = ws.at<void>(off_y);
+  pa.Y = const_cast<void*>(Y.data);
+  pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
+  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
+  hipError_t e = dpf::launch_project(pa, pvec, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+
+  L = plan_layer(&Y, G, mask);
+  e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.partials = ws.at<double>(o.part);
+  e = dpf::launch_norm(L.args, L.path, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  float* c = ws.at<float>(o.c);
+  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  L.args.c = c;
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  e = dpf::launch_accumulate(L.args, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
+}
+
+// Norm phase of one linear into sq[B] (added when accumulate != 0).
+dpf_status sqnorms_into(const dpf_act* X, const dpf_act* G, const uint8_t* mask, double* sq,
+                        int accumulate, hipStream_t s) {
+  Workspace ws(s);
+  LayerPlan L = plan_layer(X, G, mask);
+  const LayerWs o = reserve_layer(L, ws, true, false, false);
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.partials = ws.at<double>(o.part);
+  e = dpf::launch_norm(L.args, L.path, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sq, accumulate ? 1 : 0, 1.0f, nullptr,
+                           nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  return ok();
+}
+
+// Accumulate phase of one linear with given clip factors c[B].
+dpf_status accumulate_with(const dpf_act* X, const dpf_act* G, const uint8_t* mask, const float* c,
+                           float noise_std, uint64_t seed, uint64_t offset, float* grad_out,
+                           hipStream_t s) {
+  Workspace ws(s);
+  LayerPlan L = plan_layer(X, G, mask);
+  const LayerWs o = reserve_layer(L, ws, false, false, true);
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  L.args.c = c;
+  L.args.noise_std = noise_std;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  e = dpf::launch_accumulate(L.args, L.vec, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -304,52 +400,25 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   if (!aligned16(P)) return fail(DPF_ERR_UNSUPPORTED, "P is not 16-byte aligned");
   if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
   if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t es = elem_size(X->dtype);
+  return projected_layer(X, G, mask, P, 0, 0, 0, 0.0f, r, C, sigma, seed, offset, grad_out,
+                         norms_out, stream);
+}
 
-  Workspace ws(s);
-  const size_t off_y = ws.reserve((size_t)X->B * X->T * r * es);
-  dpf::ProjArgs pa{};
-  pa.X = to_act(X);
-  pa.P = P;
-  pa.dtype = X->dtype;
-  pa.B = (int)X->B;
-  pa.T = (int)X->T;
-  pa.din = (int)X->D;
-  pa.r = (int)r;
-  pa.mask = mask;
-  pa.splits = dpf::project_splits(pa);
-  const size_t pbytes = dpf::project_workspace_bytes(pa);
-  const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
-  // Reserve the layer workspace now so that a single allocation covers both.
-  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
-  LayerPlan L = plan_layer(&Y, G, mask);
-  const LayerWs o = reserve_layer(L, ws, true, true, true);
-  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  Y.data = ws.at<void>(off_y);
-  pa.Y = const_cast<void*>(Y.data);
-  pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
-  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
-  hipError_t e = dpf::launch_project(pa, pvec, s);
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
-
-  L = plan_layer(&Y, G, mask);
-  e = bind_layer(L, ws, o, s);
-  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  L.args.partials = ws.at<double>(o.part);
-  e = dpf::launch_norm(L.args, L.path, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-  float* c = ws.at<float>(o.c);
-  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize launch");
-  L.args.c = c;
-  L.args.noise_std = sigma * C;
-  L.args.seed = seed;
-  L.args.offset = offset;
-  L.args.out = grad_out;
-  e = dpf::launch_accumulate(L.args, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
-  return ok();
+dpf_status dpfused_linear_clip_accumulate_projected_seeded(
+    const dpf_act* X, const dpf_act* G, const uint8_t* mask, int64_t r, uint64_t p_seed,
+    uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
+    float* grad_out, float* norms_out, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "r must be >= 1");
+  if (r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "r too large");
+  if (r % 8 != 0) return fail(DPF_ERR_UNSUPPORTED, "r must be a multiple of 8");
+  if (!std::isfinite(p_scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "p_scale must be finite");
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  return projected_layer(X, G, mask, nullptr, 1, p_seed, p_offset, p_scale, r, C, sigma, seed,
+                         offset, grad_out, norms_out, stream);
 }
 
 dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
@@ -357,20 +426,7 @@ dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const 
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if (sqnorms_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms_out is NULL");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Workspace ws(s);
-  LayerPlan L = plan_layer(X, G, mask);
-  const LayerWs o = reserve_layer(L, ws, true, false, false);
-  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = bind_layer(L, ws, o, s);
-  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  L.args.partials = ws.at<double>(o.part);
-  e = dpf::launch_norm(L.args, L.path, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sqnorms_out, accumulate ? 1 : 0, 1.0f,
-                           nullptr, nullptr, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize launch");
-  return ok();
+  return sqnorms_into(X, G, mask, sqnorms_out, accumulate, static_cast<hipStream_t>(stream));
 }
 
 dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float* c_out,
@@ -395,20 +451,45 @@ dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const u
     return fail(DPF_ERR_INVALID_ARGUMENT, "noise_std must be finite and >= 0");
   if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
   if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  return accumulate_with(X, G, mask, c, noise_std, seed, offset, grad_out,
+                         static_cast<hipStream_t>(stream));
+}
+
+dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_act* G,
+                                         const uint8_t* mask, float C, float sigma, uint64_t seed,
+                                         const uint64_t* offsets, float* const* grad_out,
+                                         float* norms_out, void* stream) {
+  if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
+  if (X == nullptr || G == nullptr || offsets == nullptr || grad_out == nullptr)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "X, G, offsets and grad_out must not be NULL");
+  dpf_status st = check_clip(C, sigma);
+  if (st != DPF_OK) return st;
+  for (int32_t l = 0; l < n; ++l) {
+    if ((st = check_pair(&X[l], &G[l])) != DPF_OK) return st;
+    if (X[l].B != X[0].B || X[l].T != X[0].T)
+      return fail(DPF_ERR_INVALID_ARGUMENT, "every linear must have the same B and T");
+    if (grad_out[l] == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out[l] is NULL");
+    if (!aligned16(grad_out[l]))
+      return fail(DPF_ERR_UNSUPPORTED, "grad_out[l] is not 16-byte aligned");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t B = X[0].B;
   Workspace ws(s);
-  LayerPlan L = plan_layer(X, G, mask);
-  const LayerWs o = reserve_layer(L, ws, false, false, true);
+  const size_t off_sq = ws.reserve((size_t)B * sizeof(double));
+  const size_t off_c = ws.reserve((size_t)B * sizeof(float));
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  hipError_t e = bind_layer(L, ws, o, s);
-  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  L.args.c = c;
-  L.args.noise_std = noise_std;
-  L.args.seed = seed;
-  L.args.offset = offset;
-  L.args.out = grad_out;
-  e = dpf::launch_accumulate(L.args, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  double* sq = ws.at<double>(off_sq);
+  float* c = ws.at<float>(off_c);
+  // norm phase of every linear: n_i^2 summed over the group
+  for (int32_t l = 0; l < n; ++l)
+    if ((st = sqnorms_into(&X[l], &G[l], mask, sq, l > 0, s)) != DPF_OK) return st;
+  hipError_t e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "clip factor launch");
+  // accumulate phase of every linear with the group's factors
+  for (int32_t l = 0; l < n; ++l)
+    if ((st = accumulate_with(&X[l], &G[l], mask, c, sigma * C, seed, offsets[l], grad_out[l], s)) !=
+        DPF_OK)
+      return st;
   return ok();
 }
 

@@ -380,7 +380,31 @@ __global__ void __launch_bounds__(kNT) gram_norm_kernel(LayerArgs p) {
 // tile, chunk), each storing its fp32 partial product; project_reduce_kernel
 // sums the chunks in order and rounds.
 // ===========================================================================
-template <class E, bool VEC>
+// One loader chunk of P regenerated instead of read: P[d][c .. c+kVec) =
+// p_scale * xi_e for e = d*r + c .., rounded to the storage type exactly as
+// gaussian_fill writes it.  r is a multiple of 8, so a chunk covers whole
+// Philox blocks (two for bf16, one for fp32).
+template <class E>
+__device__ __forceinline__ u32x4 gen_p_chunk(const ProjArgs& p, int d, int c) {
+  if (d >= p.din || c >= p.r) return u32x4{0u, 0u, 0u, 0u};
+  const uint64_t blk = p.p_offset + (((uint64_t)d * (uint64_t)p.r + (uint64_t)c) >> 2);
+  if constexpr (sizeof(typename E::storage) == 2) {
+    const f32x4 z0 = normals_of_block(philox_block(p.p_seed, blk));
+    const f32x4 z1 = normals_of_block(philox_block(p.p_seed, blk + 1));
+    const float v[8] = {p.p_scale * z0.x, p.p_scale * z0.y, p.p_scale * z0.z, p.p_scale * z0.w,
+                        p.p_scale * z1.x, p.p_scale * z1.y, p.p_scale * z1.z, p.p_scale * z1.w};
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e]);
+    return __builtin_bit_cast(u32x4, h);
+  } else {
+    const f32x4 z = normals_of_block(philox_block(p.p_seed, blk));
+    const float v[4] = {p.p_scale * z.x, p.p_scale * z.y, p.p_scale * z.z, p.p_scale * z.w};
+    return __builtin_bit_cast(u32x4, v);
+  }
+}
+
+template <class E, bool VEC, bool GEN>
 __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
   using S = typename E::storage;
   constexpr int KT = Cfg<E>::KT;
@@ -415,7 +439,19 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
   const int kb = (int)((int64_t)split * nk_all / p.splits);
   const int nk = (int)((int64_t)(split + 1) * nk_all / p.splits);
   // P rows are "tokens" of the K-outer loader: row k of P, T = din, no mask.
-  lp.load(P, p.r, p.din, nullptr, kb * KT, j0, p.r);
+  using LP = decltype(lp);
+  auto load_p = [&](int k0) {
+    if constexpr (GEN) {
+#pragma unroll
+      for (int i = 0; i < LP::N; ++i) {
+        const int q = threadIdx.x + kNT * i;
+        lp.r[i] = gen_p_chunk<E>(p, k0 + q / LP::CPR, j0 + (q % LP::CPR) * E::kVec);
+      }
+    } else {
+      lp.load(P, p.r, p.din, nullptr, k0, j0, p.r);
+    }
+  };
+  load_p(kb * KT);
   lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, kb * KT, p.din);
   lp.template store<LDP>(lds);
   lx.template store<LDX>(lds + P_ELEMS);
@@ -424,7 +460,7 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
   for (int kk = kb; kk < nk; ++kk) {
     const bool more = kk + 1 < nk;
     if (more) {
-      lp.load(P, p.r, p.din, nullptr, (kk + 1) * KT, j0, p.r);
+      load_p((kk + 1) * KT);
       lx.load_flat(Xd, p.X.stride_b, p.X.stride_t, p.B, p.T, p.mask, q0, (kk + 1) * KT, p.din);
     }
     const S* Ps = lds + buf * (P_ELEMS + X_ELEMS);
@@ -566,7 +602,7 @@ hipError_t launch_gram_t(const LayerArgs& p, hipStream_t s) {
   timing_end("gram_norm", s);
   return e;
 }
-template <class E, bool VEC>
+template <class E, bool VEC, bool GEN>
 hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
   using S = typename E::storage;
   constexpr int KT = Cfg<E>::KT;
@@ -575,11 +611,11 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
   const int64_t ntok = (int64_t)p.B * p.T;
   const int64_t tiles = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
   if (p.splits < 1 || (p.splits > 1 && p.part == nullptr)) return hipErrorInvalidValue;
-  hipError_t e = allow_lds<project_kernel<E, VEC>>(bytes);
+  hipError_t e = allow_lds<project_kernel<E, VEC, GEN>>(bytes);
   if (e != hipSuccess) return e;
   timing_begin("project", s);
-  hipLaunchKernelGGL((project_kernel<E, VEC>), dim3((unsigned)(tiles * p.splits)), dim3(kNT), bytes,
-                     s, p);
+  hipLaunchKernelGGL((project_kernel<E, VEC, GEN>), dim3((unsigned)(tiles * p.splits)), dim3(kNT),
+                     bytes, s, p);
   e = hipGetLastError();
   timing_end("project", s);
   if (e != hipSuccess || p.splits == 1) return e;
@@ -659,8 +695,14 @@ size_t project_workspace_bytes(const ProjArgs& p) {
 }
 
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s) {
-  if (p.dtype == kBF16) return vec ? launch_project_t<BF16, true>(p, s) : launch_project_t<BF16, false>(p, s);
-  return vec ? launch_project_t<F32, true>(p, s) : launch_project_t<F32, false>(p, s);
+  if (p.gen) {
+    if (p.dtype == kBF16)
+      return vec ? launch_project_t<BF16, true, true>(p, s) : launch_project_t<BF16, false, true>(p, s);
+    return vec ? launch_project_t<F32, true, true>(p, s) : launch_project_t<F32, false, true>(p, s);
+  }
+  if (p.dtype == kBF16)
+    return vec ? launch_project_t<BF16, true, false>(p, s) : launch_project_t<BF16, false, false>(p, s);
+  return vec ? launch_project_t<F32, true, false>(p, s) : launch_project_t<F32, false, false>(p, s);
 }
 
 }  // namespace dpf

@@ -46,6 +46,11 @@ struct ProjArgs {
   const uint8_t* mask;
   float* part;              // [splits, B*T, r] fp32 partial products when splits > 1
   int splits;               // din chunks, one workgroup each per output tile
+  // gen != 0: P is not read but regenerated, P[d][j] = p_scale * xi_{d*r+j}
+  // from Philox (p_seed, p_offset), rounded to X's dtype (as gaussian_fill).
+  int gen;
+  uint64_t p_seed, p_offset;
+  float p_scale;
 };
 
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the

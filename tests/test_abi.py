@@ -128,6 +128,40 @@ def test_projected_argument_checks(L):
         == DPF_ERR_INVALID_ARGUMENT
 
 
+def test_seeded_projected_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    f = L.dpfused_linear_clip_accumulate_projected_seeded
+    args = lambda r=8, scale=0.25, C=1.0, out=FAKE: (ctypes.byref(X), ctypes.byref(G), None, r, 7, 0,
+                                                      scale, C, 1.0, 0, 0, out, None, None)
+    assert f(*args(r=0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(r=12)) == DPF_ERR_UNSUPPORTED             # not a multiple of 8
+    assert f(*args(scale=math.nan)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(C=0.0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(out=0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(out=FAKE + 4)) == DPF_ERR_UNSUPPORTED
+
+
+def test_group_argument_checks(L):
+    n = 2
+    Xs = (DpfAct * n)(_act(), _act(D=16))
+    Gs = (DpfAct * n)(_act(D=16), _act(D=8))
+    offs = (ctypes.c_uint64 * n)(0, 32)
+    outs = (ctypes.c_void_p * n)(FAKE, FAKE)
+    f = L.dpfused_group_clip_accumulate
+    assert f(0, Xs, Gs, None, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, None, Gs, None, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, 1.0, 1.0, 0, None, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, -1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    bad_t = (DpfAct * n)(_act(), _act(T=5, D=16))
+    bad_tg = (DpfAct * n)(_act(D=16), _act(T=5, D=8))
+    assert f(n, bad_t, bad_tg, None, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert b"same B and T" in L.dpfused_last_error()
+    bad_out = (ctypes.c_void_p * n)(FAKE, FAKE + 4)
+    assert f(n, Xs, Gs, None, 1.0, 1.0, 0, offs, bad_out, None, None) == DPF_ERR_UNSUPPORTED
+    null_out = (ctypes.c_void_p * n)(FAKE, None)
+    assert f(n, Xs, Gs, None, 1.0, 1.0, 0, offs, null_out, None, None) == DPF_ERR_INVALID_ARGUMENT
+
+
 def test_building_block_argument_checks(L):
     X, G = _act(), _act(D=16)
     assert L.dpfused_per_sample_sqnorms(ctypes.byref(X), ctypes.byref(G), None, None, 0, None) \

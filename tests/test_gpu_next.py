@@ -1,0 +1,133 @@
+"""GPU parity for the two widenings of the hot path: the projection drawn from
+its seed inside the projection kernel (P never stored), and group (joint)
+clipping over several linears that see the same samples.
+
+Tolerances as for the dense and projected calls: norms 1e-3 relative;
+aggregates 2e-2 relative Frobenius with noise; sigma = 0 companions 1e-3
+(dense, bf16 inputs exact in the oracle) or 1e-2 (projected: Y rounded to
+bf16 on the GPU).  The seeded projection is also checked bit for bit against
+the stored-P call fed with the P that dpfused_gaussian_fill draws from the
+same seed: both must run the same arithmetic on the same values.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import dp_linear
+from tests.gpu_helpers import mask_dev, max_rel, need_gpu, random_linear, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 1e-3
+AGG_TOL_BF16 = 2e-2
+SUM_TOL_BF16 = 1e-3
+
+
+# ---------------------------------------------------------------------------
+# seeded projection
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 150, 1000, 136, 72), (2, 64, 136, 200, 256)])
+def test_seeded_projection_equals_stored_projection(dtype, shape):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout, r = shape
+    rng = np.random.default_rng(41)
+    lin = random_linear(rng, B, T, din, dout, dtype=dtype, lengths=[T] + [T // 3] * (B - 1))
+    X, G, m = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch), mask_dev(lin.mask, torch)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    scale = 1.0 / math.sqrt(r)
+    P = dp.gaussian_fill(9, 3, din * r, scale, dtype=tdt).view(din, r)
+    o1, n1 = dp.linear_clip_accumulate_projected(X, G, P, m, C=0.05, sigma=0.7, seed=1, offset=2)
+    o2, n2 = dp.linear_clip_accumulate_projected_seeded(X, G, r, m, p_seed=9, p_offset=3,
+                                                        p_scale=scale, C=0.05, sigma=0.7, seed=1,
+                                                        offset=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(n1, n2)
+
+
+@pytest.mark.parametrize("index", [0, 5])
+def test_seeded_projection_roberta_vs_oracle(index):
+    """RoBERTa-large shapes, r = 256, P from Philox seed 7 with entries
+    N(0, 1/r): the GPU draws P inside the projection, the oracle with its own
+    generator."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    lin = workloads.config_c5_linear(index)
+    r = 256
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    P = dp_linear.projection_matrix(7, 0, lin.din, r, 1.0 / 16.0, "bf16")
+    for sigma, tol in ((lin.sigma, AGG_TOL_BF16), (0.0, 1e-2)):
+        out, norms = dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7,
+                                                                p_offset=0, C=lin.C, sigma=sigma)
+        ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, sigma, 0, 0, "bf16")
+        assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+        assert rel_fro(out.cpu().numpy(), ref) <= tol
+
+
+# ---------------------------------------------------------------------------
+# group clipping
+# ---------------------------------------------------------------------------
+def _group_case(rng, B, T, dims, lengths, dtype="bf16"):
+    lins = [random_linear(rng, B, T, din, dout, dtype=dtype, lengths=lengths) for din, dout in dims]
+    return lins, lins[0].mask
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_group_clip_matches_oracle(dtype):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(42)
+    dims = [(512, 640), (640, 512), (256, 1024)] if dtype == "bf16" else [(64, 40), (24, 72)]
+    B, T = 3, 300
+    lins, mask = _group_case(rng, B, T, dims, [300, 150, 37], dtype)
+    pairs = [(l.X, l.G) for l in lins]
+    offsets = [0, 1000, 5000]
+    _, rn, _ = dp_linear.oracle_group(pairs, mask, 1.0, 0.0, 0, offsets, dtype)
+    C = float(np.median(rn))               # some samples clip, some do not
+    Xs = [to_dev(l.X, dtype, torch) for l in lins]
+    Gs = [to_dev(l.G, dtype, torch) for l in lins]
+    m = mask_dev(mask, torch)
+    sum_tol = SUM_TOL_BF16 if dtype == "bf16" else 1e-4
+    for sigma, tol in ((0.0, sum_tol), (1.1, AGG_TOL_BF16 if dtype == "bf16" else 1e-4)):
+        outs, norms = dp.group_clip_accumulate(Xs, Gs, m, C=C, sigma=sigma, seed=3,
+                                               offsets=offsets[:len(lins)])
+        refs, rn, rc = dp_linear.oracle_group(pairs, mask, C, sigma, 3, offsets, dtype)
+        assert (rc == 1).any() and (rc < 1).any()
+        assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+        for o, ref in zip(outs, refs):
+            assert rel_fro(o.cpu().numpy(), ref) <= tol
+
+
+def test_group_of_one_is_the_dense_call_bitwise():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(43)
+    lin = random_linear(rng, 4, 257, 264, 136, masked=True)
+    X, G, m = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch), mask_dev(lin.mask, torch)
+    o1, n1 = dp.linear_clip_accumulate(X, G, m, C=0.01, sigma=0.9, seed=5, offset=17)
+    (o2,), n2 = dp.group_clip_accumulate([X], [G], m, C=0.01, sigma=0.9, seed=5, offsets=[17])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(n1, n2)
+
+
+def test_group_row_split_reproduces_whole_layer():
+    """Two linears that are the output-row halves of one linear: group
+    clipping of the halves gives the whole linear's per-layer result."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(44)
+    B, T, din, dout, d1 = 4, 200, 512, 768, 256
+    lin = random_linear(rng, B, T, din, dout, lengths=[200, 90, 200, 13])
+    X, G, m = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch), mask_dev(lin.mask, torch)
+    whole, nw = dp.linear_clip_accumulate(X, G, m, C=0.02, sigma=0.6, seed=2, offset=8)
+    G1 = G[:, :, :d1].contiguous()
+    G2 = G[:, :, d1:].contiguous()
+    (h1, h2), ng = dp.group_clip_accumulate([X, X], [G1, G2], m, C=0.02, sigma=0.6, seed=2,
+                                            offsets=[8, 8 + d1 * din // 4])
+    assert max_rel(ng.cpu().numpy(), nw.cpu().numpy()) <= 1e-4
+    assert rel_fro(torch.cat([h1, h2]).cpu().numpy(), whole.cpu().numpy()) <= 1e-4

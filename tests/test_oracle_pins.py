@@ -282,6 +282,52 @@ def test_mask_equals_unpadded_calls_and_ignores_padding():
     np.testing.assert_array_equal(norms2, norms)
 
 
+def test_group_of_one_is_per_layer():
+    rng = np.random.default_rng(30)
+    X, G, mask = _rand_case(rng, 4, 5, 6, 3, masked=True)
+    outs, n_g, c_g = dp_linear.oracle_group([(X, G)], mask, 0.4, 0.9, 5, [7], "f32")
+    o, n, c = dp_linear.oracle_linear(X, G, mask, 0.4, 0.9, 5, 7, "f32")
+    np.testing.assert_allclose(outs[0], o, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(n_g, n, rtol=1e-14)
+    np.testing.assert_array_equal(c_g == 1.0, c == 1.0)
+
+
+def test_group_row_split_reproduces_whole_layer():
+    """Cutting one linear's output rows into two linears with the same input:
+    the group norm of the two halves is the norm of the whole gradient, so
+    group clipping of the halves equals per-layer clipping of the whole (the
+    noise follows the row-major element index, so the second half's offset
+    is the first half's element count / 4)."""
+    rng = np.random.default_rng(31)
+    B, T, din, dout, d1 = 4, 6, 8, 10, 4
+    X, G, mask = _rand_case(rng, B, T, din, dout, masked=True)
+    C, sigma, seed, off = 0.3, 0.8, 11, 5
+    whole, n_w, c_w = dp_linear.oracle_linear(X, G, mask, C, sigma, seed, off, "f32")
+    outs, n_g, c_g = dp_linear.oracle_group([(X, G[:, :, :d1]), (X, G[:, :, d1:])], mask, C,
+                                            sigma, seed, [off, off + d1 * din // 4], "f32")
+    assert (c_w < 1).any()
+    np.testing.assert_allclose(np.concatenate(outs, axis=0), whole, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(n_g, n_w, rtol=1e-13)
+
+
+def test_group_clip_bounds_the_group_norm():
+    rng = np.random.default_rng(32)
+    lin = []
+    for din, dout in ((5, 3), (4, 7), (6, 2)):
+        X, G, _ = _rand_case(rng, 5, 4, din, dout)
+        lin.append((X, G))
+    C = 0.2
+    _, norms, c = dp_linear.oracle_group(lin, None, C, 0.0, 0, [0, 0, 0], "f32")
+    Xw = [dp_linear.widen(x, "f32") for x, _ in lin]
+    Gw = [dp_linear.widen(g, "f32") for _, g in lin]
+    for i in range(5):
+        sq = sum(float(np.sum((Gw[l][i].T @ Xw[l][i]) ** 2)) for l in range(3))
+        assert abs(math.sqrt(sq) - norms[i]) <= 1e-12 * norms[i]
+        assert c[i] * norms[i] <= C * (1 + 1e-12)
+        # each layer's norm alone would have clipped less
+        assert c[i] <= min(1.0, C / math.sqrt(float(np.sum((Gw[0][i].T @ Xw[0][i]) ** 2))))
+
+
 def test_projection_identity_reduces_to_dense():
     rng = np.random.default_rng(11)
     X, G, mask = _rand_case(rng, 3, 5, 6, 4, masked=True)
