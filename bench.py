@@ -158,6 +158,29 @@ def measure_configs(dp, torch, steps, warmup):
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
         "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+
+    # projected Adam step on the privatised projected gradients (moments in
+    # r-space, weight update W -= lr U P^T with P drawn from its seed)
+    states = []
+    for lin, X, G, o, nrm in dev:
+        states.append((o, torch.zeros_like(o), torch.zeros_like(o),
+                       torch.zeros((lin.dout, lin.din), dtype=torch.float32, device=o.device)))
+    seeded_layer()
+    step_no = [0]
+
+    def adam_layer():
+        step_no[0] += 1
+        for h, m, v, W in states:
+            dp.projected_adam_step(h, m, v, W, step_no[0], 1e-4, P=None, p_seed=7, p_offset=0)
+    ms = time_calls(torch, adam_layer, steps, warmup)
+    flops = sum(2.0 * l.dout * l.din * r for l in lins)
+    bytes_ = sum(4.0 * (6 * l.dout * r + 2 * l.dout * l.din) for l in lins)
+    out["c5_roberta_large_projected_adam_step_6_linears"] = {
+        "note": "moments + U P^T update (fp32 MFMA), P drawn from its seed; flops 2*dout*din*r, "
+                "bytes: h, m, v, U in r-space and W read+written",
+        "linears": len(lins), "ms": round(ms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "gb_per_s": round(bytes_ / (ms * 1e-3) / 1e9, 1)}
     return out
 
 

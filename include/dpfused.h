@@ -201,6 +201,40 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
                                          const uint64_t* offsets, float* const* grad_out,
                                          float* norms_out, void* stream);
 
+/* One step of the projected Adam optimizer (Memory-Efficient Differentially
+ * Private Training with Gradient Random Projection, English explainer,
+ * Methodology, "Projected Optimizer States": the Adam moments are kept in the
+ * projected space, and the update goes back to the weight through the
+ * projection).  With h = grad, the privatised projected gradient of a linear
+ * (the grad_out of a projected call):
+ *
+ *   m <- beta1 m + (1 - beta1) h,   v <- beta2 v + (1 - beta2) h*h
+ *   U  = (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ *   W <- W - lr * U P^T
+ *
+ * (plain Adam, no weight decay; elementwise in float32, U P^T with float32
+ * MFMA).
+ *
+ *   grad       [dout, r] float32 (device), read
+ *   m, v       [dout, r] float32 (device), updated in place
+ *   W          [dout, din] float32 row-major (device), updated in place
+ *   r, din     multiples of 4
+ *   step       >= 1, the number of this update (1 for the first)
+ *   beta1, beta2 in [0, 1); eps finite and > 0; lr finite
+ *   P          [din, r] row-major, p_dtype (DPF_F32 or DPF_BF16), 16-byte
+ *              aligned -- or NULL: then P[d][j] = p_scale * xi_{d*r+j} from
+ *              Philox (p_seed, p_offset) rounded to p_dtype, the P of
+ *              dpfused_linear_clip_accumulate_projected_seeded, drawn again
+ *              inside the kernel
+ *
+ * All pointers 16-byte aligned.  Errors as above; nothing is written on
+ * error.  m, v and W must not overlap each other or grad. */
+dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, float* W,
+                                       int64_t dout, int64_t din, int64_t r, int64_t step,
+                                       float lr, float beta1, float beta2, float eps,
+                                       const void* P, int32_t p_dtype, uint64_t p_seed,
+                                       uint64_t p_offset, float p_scale, void* stream);
+
 /* Raw Philox4x32-10 words: out[4*j + k] = word k of block (offset + j),
  * j < nblocks, with the key/counter layout above.  out: device, 16-byte
  * aligned, 4*nblocks uint32.  nblocks >= 0 (0 = nothing queued). */

@@ -22,7 +22,8 @@ from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
 
 __all__ = [
     "linear_clip_accumulate", "linear_clip_accumulate_projected",
-    "linear_clip_accumulate_projected_seeded", "group_clip_accumulate", "per_sample_sqnorms",
+    "linear_clip_accumulate_projected_seeded", "group_clip_accumulate", "projected_adam_step",
+    "per_sample_sqnorms",
     "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
     "set_option", "get_option", "timing_reset", "timing_collect", "DpfError", "load",
 ]
@@ -170,6 +171,38 @@ def group_clip_accumulate(Xs, Gs, mask=None, C: float = 1.0, sigma: float = 0.0,
         _ptr(norms_out), _stream(Xs[0], stream))
     _lib.check(st)
     return grad_outs, norms_out
+
+
+def projected_adam_step(grad, m, v, W, step: int, lr: float, beta1: float = 0.9,
+                        beta2: float = 0.999, eps: float = 1e-8, P=None, p_seed: int = 0,
+                        p_offset: int = 0, p_scale=None, p_dtype=None, stream=None):
+    """One projected Adam step: m, v ([dout, r] fp32) and W ([dout, din] fp32) are updated
+    in place from the privatised projected gradient ``grad`` [dout, r]; P [din, r], or
+    None to draw it from (p_seed, p_offset, p_scale) in p_dtype (default bf16)."""
+    torch = _torch()
+    dout, r = grad.shape
+    din = W.shape[1]
+    for t, name in ((grad, "grad"), (m, "m"), (v, "v"), (W, "W")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if tuple(m.shape) != (dout, r) or tuple(v.shape) != (dout, r) or W.shape[0] != dout:
+        raise ValueError("m and v must be [dout, r] and W [dout, din]")
+    if P is not None:
+        if P.dim() != 2 or tuple(P.shape) != (din, r) or not P.is_contiguous():
+            raise ValueError("P must be a contiguous [din, r] tensor")
+        pdt = _dtype_code(P)
+        pptr = P.data_ptr()
+    else:
+        pdt = _dtype_code(torch.empty(0, dtype=p_dtype or torch.bfloat16))
+        pptr = None
+        if p_scale is None:
+            p_scale = 1.0 / math.sqrt(r)
+    st = _lib.lib().dpfused_projected_adam_step(
+        grad.data_ptr(), m.data_ptr(), v.data_ptr(), W.data_ptr(), int(dout), int(din), int(r),
+        int(step), float(lr), float(beta1), float(beta2), float(eps), pptr, int(pdt),
+        int(p_seed), int(p_offset), float(p_scale or 0.0), _stream(grad, stream))
+    _lib.check(st)
+    return m, v, W
 
 
 def per_sample_sqnorms(X, G, mask=None, out=None, accumulate: bool = False, stream=None):

@@ -60,6 +60,11 @@ _SIGNATURES = {
         ctypes.c_int32, ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p,
         ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
         ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p]),
+    "dpfused_projected_adam_step": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64,
+        ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p]),
     "dpfused_per_sample_sqnorms": (ctypes.c_int, [
         ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_void_p]),

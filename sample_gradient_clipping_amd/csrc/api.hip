@@ -493,6 +493,60 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
   return ok();
 }
 
+dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, float* W,
+                                       int64_t dout, int64_t din, int64_t r, int64_t step,
+                                       float lr, float beta1, float beta2, float eps,
+                                       const void* P, int32_t p_dtype, uint64_t p_seed,
+                                       uint64_t p_offset, float p_scale, void* stream) {
+  if (grad == nullptr || m == nullptr || v == nullptr || W == nullptr)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "grad, m, v and W must not be NULL");
+  if (dout < 1 || din < 1 || r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "dout, din, r must be >= 1");
+  if (dout > kMaxDim || din > kMaxDim || r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "dimension too large");
+  if (r % 4 != 0 || din % 4 != 0)
+    return fail(DPF_ERR_UNSUPPORTED, "r and din must be multiples of 4");
+  if (step < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "step must be >= 1");
+  if (!std::isfinite(lr)) return fail(DPF_ERR_INVALID_ARGUMENT, "lr must be finite");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(DPF_ERR_INVALID_ARGUMENT, "beta1 and beta2 must be in [0, 1)");
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return fail(DPF_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+  if (p_dtype != DPF_F32 && p_dtype != DPF_BF16) return fail(DPF_ERR_UNSUPPORTED, "unknown P dtype");
+  if (P == nullptr && !std::isfinite(p_scale))
+    return fail(DPF_ERR_INVALID_ARGUMENT, "p_scale must be finite");
+  if (!aligned16(grad) || !aligned16(m) || !aligned16(v) || !aligned16(W) ||
+      (P != nullptr && !aligned16(P)))
+    return fail(DPF_ERR_UNSUPPORTED, "grad, m, v, W and P must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  const size_t off_u = ws.reserve((size_t)dout * r * sizeof(float));
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  dpf::AdamArgs a{};
+  a.grad = grad;
+  a.m = m;
+  a.v = v;
+  a.u = ws.at<float>(off_u);
+  a.W = W;
+  a.dout = dout;
+  a.din = din;
+  a.r = r;
+  a.lr = lr;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+  a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+  if (!(a.bc1 > 0.0f) || !(a.bc2 > 0.0f))
+    return fail(DPF_ERR_INVALID_ARGUMENT, "bias corrections underflow (beta^step == 1)");
+  a.P = P;
+  a.p_dtype = p_dtype;
+  a.gen = P == nullptr ? 1 : 0;
+  a.p_seed = p_seed;
+  a.p_offset = p_offset;
+  a.p_scale = p_scale;
+  hipError_t e = dpf::launch_projected_adam(a, s);
+  if (e != hipSuccess) return hip_fail(e, "projected Adam launch");
+  return ok();
+}
+
 dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
                                  void* stream) {
   if (nblocks < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "nblocks must be >= 0");

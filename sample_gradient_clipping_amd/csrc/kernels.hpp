@@ -53,6 +53,23 @@ struct ProjArgs {
   float p_scale;
 };
 
+// One projected Adam step (optim.hip).
+struct AdamArgs {
+  const float* grad;        // [dout, r] privatised projected gradient
+  float* m;                 // [dout, r] first moment, updated in place
+  float* v;                 // [dout, r] second moment, updated in place
+  float* u;                 // [dout, r] workspace: the bias-corrected direction
+  float* W;                 // [dout, din] float32 weight, updated in place
+  int64_t dout, din, r;
+  float lr, beta1, beta2, eps, bc1, bc2;   // bc_k = 1 - beta_k^step
+  const void* P;            // [din, r] of p_dtype, unless gen
+  int p_dtype;
+  int gen;                  // P[d][j] = p_scale * xi_{d*r+j}(p_seed, p_offset), rounded to p_dtype
+  uint64_t p_seed, p_offset;
+  float p_scale;
+};
+hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s);
+
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the
 // caller has checked alignment of every pointer, dimension and stride.
 // True when (p, vec) runs on the large-tile bf16 kernels; a masked call on

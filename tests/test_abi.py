@@ -162,6 +162,30 @@ def test_group_argument_checks(L):
     assert f(n, Xs, Gs, None, 1.0, 1.0, 0, offs, null_out, None, None) == DPF_ERR_INVALID_ARGUMENT
 
 
+def test_projected_adam_argument_checks(L):
+    f = L.dpfused_projected_adam_step
+    ok = dict(grad=FAKE, m=FAKE, v=FAKE, W=FAKE, dout=4, din=8, r=8, step=1, lr=1e-3, b1=0.9,
+              b2=0.999, eps=1e-8, P=FAKE, pdt=DPF_BF16, scale=0.25)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["grad"], a["m"], a["v"], a["W"], a["dout"], a["din"], a["r"], a["step"],
+                 a["lr"], a["b1"], a["b2"], a["eps"], a["P"], a["pdt"], 0, 0, a["scale"], None)
+    assert call(grad=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(W=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(r=0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(r=6) == DPF_ERR_UNSUPPORTED
+    assert call(din=10) == DPF_ERR_UNSUPPORTED
+    assert call(step=0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(b1=1.0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(b2=-0.1) == DPF_ERR_INVALID_ARGUMENT
+    assert call(eps=0.0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(lr=math.inf) == DPF_ERR_INVALID_ARGUMENT
+    assert call(pdt=9) == DPF_ERR_UNSUPPORTED
+    assert call(P=None, scale=math.nan) == DPF_ERR_INVALID_ARGUMENT
+    assert call(m=FAKE + 4) == DPF_ERR_UNSUPPORTED
+
+
 def test_building_block_argument_checks(L):
     X, G = _act(), _act(D=16)
     assert L.dpfused_per_sample_sqnorms(ctypes.byref(X), ctypes.byref(G), None, None, 0, None) \

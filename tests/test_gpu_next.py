@@ -1,6 +1,7 @@
-"""GPU parity for the two widenings of the hot path: the projection drawn from
-its seed inside the projection kernel (P never stored), and group (joint)
-clipping over several linears that see the same samples.
+"""GPU parity for the widenings of the hot path: the projection drawn from its
+seed inside the projection kernel (P never stored), group (joint) clipping
+over several linears that see the same samples, and the projected Adam step
+that consumes the privatised projected gradient.
 
 Tolerances as for the dense and projected calls: norms 1e-3 relative;
 aggregates 2e-2 relative Frobenius with noise; sigma = 0 companions 1e-3
@@ -131,3 +132,94 @@ def test_group_row_split_reproduces_whole_layer():
                                             offsets=[8, 8 + d1 * din // 4])
     assert max_rel(ng.cpu().numpy(), nw.cpu().numpy()) <= 1e-4
     assert rel_fro(torch.cat([h1, h2]).cpu().numpy(), whole.cpu().numpy()) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# projected Adam step
+# ---------------------------------------------------------------------------
+def _adam_case(rng, dout, din, r):
+    h = (rng.standard_normal((dout, r)) * 0.01).astype(np.float32)
+    m = (rng.standard_normal((dout, r)) * 0.005).astype(np.float32)
+    v = (rng.random((dout, r)) * 1e-4).astype(np.float32)
+    W = rng.standard_normal((dout, din)).astype(np.float32)
+    return h, m, v, W
+
+
+@pytest.mark.parametrize("pdtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(200, 136, 72), (1024, 4096, 256)])
+def test_projected_adam_step_matches_oracle(pdtype, shape):
+    """Elementwise moments in float32 against float64: 1e-6 relative; the
+    weight change lr * U P^T (float32 MFMA over r) within 1e-5 of the
+    oracle's change."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    from oracle import optim
+    dout, din, r = shape
+    rng = np.random.default_rng(45)
+    h, m, v, W = _adam_case(rng, dout, din, r)
+    Pf = (rng.standard_normal((din, r)) / np.sqrt(r)).astype(np.float32)
+    P = workloads.f32_to_bf16_bits(Pf) if pdtype == "bf16" else Pf
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    hd, md, vd, Wd = dev(h), dev(m), dev(v), dev(W)
+    Pd = to_dev(P, pdtype, torch)
+    step, lr, b1, b2, eps = 7, 1e-3, 0.9, 0.999, 1e-8
+    dp.projected_adam_step(hd, md, vd, Wd, step, lr, b1, b2, eps, P=Pd)
+    rm, rv, rW = optim.projected_adam_step(h, m, v, W, step, lr, b1, b2, eps,
+                                           dp_linear.widen(P, pdtype))
+    assert rel_fro(md.cpu().numpy(), rm) <= 1e-6
+    assert rel_fro(vd.cpu().numpy(), rv) <= 1e-6
+    dW_ref = rW - W.astype(np.float64)
+    dW = Wd.cpu().numpy().astype(np.float64) - W.astype(np.float64)
+    assert np.linalg.norm(dW - dW_ref) <= 1e-5 * np.linalg.norm(dW_ref) + 1e-7 * np.linalg.norm(W)
+
+
+def test_projected_adam_seeded_equals_stored():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    dout, din, r = 300, 520, 64
+    rng = np.random.default_rng(46)
+    h, m, v, W = _adam_case(rng, dout, din, r)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    P = dp.gaussian_fill(5, 11, din * r, 0.125, dtype=torch.bfloat16).view(din, r)
+    outs = []
+    for seeded in (False, True):
+        md, vd, Wd = dev(m), dev(v), dev(W)
+        if seeded:
+            dp.projected_adam_step(dev(h), md, vd, Wd, 2, 1e-2, P=None, p_seed=5, p_offset=11,
+                                   p_scale=0.125, p_dtype=torch.bfloat16)
+        else:
+            dp.projected_adam_step(dev(h), md, vd, Wd, 2, 1e-2, P=P)
+        outs.append((md, vd, Wd))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_projected_dp_step_end_to_end_roberta():
+    """The projected call (P drawn from its seed) followed by the projected
+    Adam step on one RoBERTa-large linear, against the oracles chained."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    from oracle import optim
+    lin = workloads.config_c5_linear(4)          # fc1: 1024 -> 4096
+    r = 256
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    h, _ = dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7, p_offset=0,
+                                                      C=lin.C, sigma=lin.sigma)
+    rng = np.random.default_rng(47)
+    W = rng.standard_normal((lin.dout, lin.din)).astype(np.float32)
+    Wd = torch.from_numpy(W).cuda()
+    md = torch.zeros((lin.dout, r), dtype=torch.float32, device="cuda")
+    vd = torch.zeros_like(md)
+    dp.projected_adam_step(h, md, vd, Wd, 1, 1e-3, P=None, p_seed=7, p_offset=0)
+    P = dp_linear.projection_matrix(7, 0, lin.din, r, 1.0 / 16.0, "bf16")
+    href, _, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, lin.sigma, 0, 0, "bf16")
+    assert rel_fro(h.cpu().numpy(), href) <= AGG_TOL_BF16
+    # the step from the GPU's own h (the privatised gradient is the input of the step)
+    _, _, rW = optim.projected_adam_step(h.cpu().numpy(), np.zeros((lin.dout, r)),
+                                         np.zeros((lin.dout, r)), W, 1, 1e-3, 0.9, 0.999, 1e-8,
+                                         dp_linear.widen(P, "bf16"))
+    dW_ref = rW - W.astype(np.float64)
+    dW = Wd.cpu().numpy().astype(np.float64) - W.astype(np.float64)
+    # a few P entries may round to the neighbouring bf16 value on either side
+    assert np.linalg.norm(dW - dW_ref) <= 2e-3 * np.linalg.norm(dW_ref)

@@ -14,7 +14,7 @@ import subprocess
 import numpy as np
 import pytest
 
-from oracle import dp_linear, philox
+from oracle import dp_linear, optim, philox
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -326,6 +326,45 @@ def test_group_clip_bounds_the_group_norm():
         assert c[i] * norms[i] <= C * (1 + 1e-12)
         # each layer's norm alone would have clipped less
         assert c[i] <= min(1.0, C / math.sqrt(float(np.sum((Gw[0][i].T @ Xw[0][i]) ** 2))))
+
+
+def test_projected_adam_first_step_closed_form():
+    """m = v = 0, t = 1: m_hat = h, v_hat = h^2, so U = h / (|h| + eps)."""
+    rng = np.random.default_rng(33)
+    dout, din, r = 5, 7, 3
+    h = rng.standard_normal((dout, r))
+    W = rng.standard_normal((dout, din))
+    P = rng.standard_normal((din, r))
+    eps, lr = 1e-3, 0.05
+    m, v, W1 = optim.projected_adam_step(h, np.zeros_like(h), np.zeros_like(h), W, 1, lr, 0.9,
+                                         0.999, eps, P)
+    np.testing.assert_allclose(W1, W - lr * (h / (np.abs(h) + eps)) @ P.T, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(m, 0.1 * h, rtol=1e-15)
+    np.testing.assert_allclose(v, 0.001 * h * h, rtol=1e-12)
+
+
+def test_projected_adam_identity_projection_is_torch_adam():
+    """With P = I (r = din) the projected step is plain Adam: compare several
+    steps against torch.optim.Adam (float64, CPU)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(34)
+    dout, din = 4, 6
+    W0 = rng.standard_normal((dout, din))
+    p = torch.nn.Parameter(torch.tensor(W0, dtype=torch.float64))
+    opt = torch.optim.Adam([p], lr=0.01, betas=(0.8, 0.95), eps=1e-6, foreach=False)
+    m = np.zeros((dout, din))
+    v = np.zeros((dout, din))
+    W = W0.copy()
+    I = np.eye(din)
+    for t in range(1, 6):
+        g = rng.standard_normal((dout, din)) * (0.1 * t)
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        m, v, W = optim.projected_adam_step(g, m, v, W, t, 0.01, 0.8, 0.95, 1e-6, I)
+        np.testing.assert_allclose(W, p.detach().numpy(), rtol=1e-12, atol=1e-14)
+        st = opt.state[p]
+        np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-15)
 
 
 def test_projection_identity_reduces_to_dense():
