@@ -117,6 +117,23 @@ def measure_configs(dp, torch, steps, warmup):
           "one fp32 linear; launch-latency bound")
     dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
           "bf16, sigma 0.8")
+
+    # the same layer with its bias (weight and bias clipped together)
+    lin = workloads.config_c2().linears[0]
+    X, G = upload(lin.X, torch), upload(lin.G, torch)
+    o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
+    ob = torch.empty((lin.dout,), dtype=torch.float32, device=X.device)
+    nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+    ms = time_calls(torch, lambda: dp.linear_clip_accumulate_bias(
+        X, G, None, C=lin.C, sigma=lin.sigma, grad_out=o, bias_grad_out=ob, norms_out=nrm),
+        steps, warmup)
+    f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+    out["c2_gpt2_up_with_bias"] = {
+        "note": "as c2, plus the bias gradient (column sums of G) in the clipping norm and sum",
+        "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+        "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
+    del X, G, o, ob, nrm
+    torch.cuda.empty_cache()
     dense([lambda i=i: workloads.config_c4_linear(i) for i in range(len(workloads.C4_LINEARS))],
           "c4_llama13b_ragged_B16_T2048_7_linears",
           "bf16, prefix masks T_i ~ U[128, 2048], C 0.5, sigma 1.2; useful flops over active tokens")

@@ -172,6 +172,32 @@ dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const u
                                      const float* c, float noise_std, uint64_t seed,
                                      uint64_t offset, float* grad_out, void* stream);
 
+/* The dense step for a linear layer with a bias, y = x W^T + b: the layer's
+ * parameters are W and b, so sample i's gradient is the pair (g_i, gb_i) and
+ * both parts are clipped by the norm of the pair (the per-layer clipping of
+ * the FlashDP abstract, applied to the whole layer):
+ *
+ *   gb_i             = sum over the active tokens t of G~_i[t]       [dout]
+ *   n_i              = sqrt(||g_i||_F^2 + ||gb_i||^2)
+ *   grad_out         = (sum_i c_i g_i  + sigma * C * xi) / B          [dout, din]
+ *   bias_grad_out    = (sum_i c_i gb_i + sigma * C * xi') / B         [dout]
+ *
+ * xi as for dpfused_linear_clip_accumulate (offset); xi' continues the same
+ * Philox stream after it: element o of the bias uses block
+ * offset + dpfused_noise_blocks(dout*din) + floor(o/4), lane o mod 4.  A call
+ * consumes dpfused_noise_blocks(dout*din) + dpfused_noise_blocks(dout) blocks.
+ * Equivalently: the dense call on the input [X, 1] (a constant-one column
+ * whose weight is the bias), up to the noise layout.
+ *
+ *   bias_grad_out  [dout] float32 (device), 4-byte aligned, overwritten
+ *
+ * Other arguments and errors as for dpfused_linear_clip_accumulate. */
+dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* G,
+                                               const uint8_t* mask, float C, float sigma,
+                                               uint64_t seed, uint64_t offset, float* grad_out,
+                                               float* bias_grad_out, float* norms_out,
+                                               void* stream);
+
 /* Group (joint) clipping over n linears that see the same samples, e.g. the
  * seven linears of one decoder layer.  The FlashDP pages clip per layer
  * (FlashDP, Abstract: per-layer DP-SGD, gradients computed once); this is the

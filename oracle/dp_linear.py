@@ -108,6 +108,37 @@ def oracle_linear(X, G, mask, C: float, sigma: float, seed: int, offset: int,
     return out / B, norms, c
 
 
+def oracle_linear_bias(X, G, mask, C: float, sigma: float, seed: int, offset: int,
+                       dtype: str = "bf16", with_noise: bool = True):
+    """Dense variant for a linear with a bias, y = x W^T + b.
+
+    The per-layer clipping of the FlashDP abstract applies to the layer's
+    whole gradient, here the pair (g_i, gb_i) with gb_i = sum of the active
+    rows of G_i (the weight gradient of a constant-one input).  Steps 3-5 run
+    on the pair flattened into one vector.  Noise: the weight's xi from
+    `offset`, the bias's continuing the stream at offset + ceil(dout*din/4).
+
+    Returns (out_W [dout, din], out_b [dout], norms [B], c [B]), all float64."""
+    Xw = widen(X, dtype)
+    Gw = widen(G, dtype)
+    B, din, dout = Xw.shape[0], Xw.shape[2], Gw.shape[2]
+
+    def flat_grads():
+        for i in range(B):
+            m = None if mask is None else mask[i]
+            Gi = select_active(Gw[i], m)
+            g = per_sample_grad(select_active(Xw[i], m), Gi)
+            yield np.concatenate([g.ravel(), Gi.sum(axis=0)])
+
+    S, norms, c = clip_accumulate(flat_grads(), C)
+    out_w = S[:dout * din].reshape(dout, din).copy()
+    out_b = S[dout * din:].copy()
+    if with_noise and sigma != 0.0:
+        out_w = out_w + sigma * C * noise_matrix(seed, offset, (dout, din))
+        out_b = out_b + sigma * C * philox.gaussian(seed, offset + (dout * din + 3) // 4, dout)
+    return out_w / B, out_b / B, norms, c
+
+
 def oracle_group(linears, mask, C: float, sigma: float, seed: int, offsets,
                  dtype: str = "bf16", with_noise: bool = True):
     """Group (joint) clipping over linears that see the same samples.

@@ -22,7 +22,8 @@ from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
 
 __all__ = [
     "linear_clip_accumulate", "linear_clip_accumulate_projected",
-    "linear_clip_accumulate_projected_seeded", "group_clip_accumulate", "projected_adam_step",
+    "linear_clip_accumulate_projected_seeded", "linear_clip_accumulate_bias",
+    "group_clip_accumulate", "projected_adam_step",
     "per_sample_sqnorms",
     "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
     "set_option", "get_option", "timing_reset", "timing_collect", "DpfError", "load",
@@ -143,6 +144,28 @@ def linear_clip_accumulate_projected_seeded(X, G, r: int, mask=None, p_seed: int
         grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
+
+
+def linear_clip_accumulate_bias(X, G, mask=None, C: float = 1.0, sigma: float = 0.0,
+                                seed: int = 0, offset: int = 0, grad_out=None, bias_grad_out=None,
+                                norms_out=None, stream=None, want_norms: bool = True):
+    """Dense step for a linear with a bias: weight and bias gradients clipped together;
+    returns (grad_out [dout, din], bias_grad_out [dout], norms [B])."""
+    torch = _torch()
+    xa, ga = _act(X), _act(G)
+    B, T = X.shape[0], X.shape[1]
+    if grad_out is None:
+        grad_out = torch.empty((G.shape[2], X.shape[2]), dtype=torch.float32, device=X.device)
+    if bias_grad_out is None:
+        bias_grad_out = torch.empty((G.shape[2],), dtype=torch.float32, device=X.device)
+    if norms_out is None and want_norms:
+        norms_out = torch.empty((B,), dtype=torch.float32, device=X.device)
+    st = _lib.lib().dpfused_linear_clip_accumulate_bias(
+        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), float(C), float(sigma),
+        int(seed), int(offset), grad_out.data_ptr(), bias_grad_out.data_ptr(), _ptr(norms_out),
+        _stream(X, stream))
+    _lib.check(st)
+    return grad_out, bias_grad_out, norms_out
 
 
 def group_clip_accumulate(Xs, Gs, mask=None, C: float = 1.0, sigma: float = 0.0, seed: int = 0,

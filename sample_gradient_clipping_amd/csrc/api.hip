@@ -455,6 +455,46 @@ dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const u
                          static_cast<hipStream_t>(stream));
 }
 
+dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* G,
+                                               const uint8_t* mask, float C, float sigma,
+                                               uint64_t seed, uint64_t offset, float* grad_out,
+                                               float* bias_grad_out, float* norms_out,
+                                               void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (grad_out == nullptr || bias_grad_out == nullptr)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out and bias_grad_out must not be NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(bias_grad_out) & 3u) != 0)
+    return fail(DPF_ERR_UNSUPPORTED, "bias_grad_out is not 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t B = X->B, dout = G->D;
+  Workspace ws(s);
+  const size_t off_sq = ws.reserve((size_t)B * sizeof(double));
+  const size_t off_c = ws.reserve((size_t)B * sizeof(float));
+  const size_t off_gb = ws.reserve((size_t)B * dout * sizeof(float));
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  double* sq = ws.at<double>(off_sq);
+  float* c = ws.at<float>(off_c);
+  float* gb = ws.at<float>(off_gb);
+  // ||g_i||^2 of the weight, then + ||gb_i||^2 of the bias
+  if ((st = sqnorms_into(X, G, mask, sq, 0, s)) != DPF_OK) return st;
+  hipError_t e = dpf::launch_bias_grads(to_act(G), G->dtype, (int)B, (int)G->T, (int)dout, mask,
+                                        gb, sq, s);
+  if (e != hipSuccess) return hip_fail(e, "bias gradient launch");
+  e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "clip factor launch");
+  if ((st = accumulate_with(X, G, mask, c, sigma * C, seed, offset, grad_out, s)) != DPF_OK)
+    return st;
+  // the bias noise continues the weight's Philox stream
+  const uint64_t boff = offset + (uint64_t)((dout * X->D + 3) / 4);
+  e = dpf::launch_bias_accumulate(gb, c, (int)B, (int)dout, sigma * C, seed, boff, bias_grad_out,
+                                  s);
+  if (e != hipSuccess) return hip_fail(e, "bias accumulate launch");
+  return ok();
+}
+
 dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_act* G,
                                          const uint8_t* mask, float C, float sigma, uint64_t seed,
                                          const uint64_t* offsets, float* const* grad_out,

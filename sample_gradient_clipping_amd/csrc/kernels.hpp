@@ -53,6 +53,14 @@ struct ProjArgs {
   float p_scale;
 };
 
+// Bias gradients (bias.hip): gb[b][o] = sum of the active rows of G_b, and
+// sq[b] += ||gb[b]||^2; then out[o] = (sum_b c[b] gb[b][o] + noise_std xi_o) / B.
+hipError_t launch_bias_grads(const Act& G, int dtype, int B, int T, int dout, const uint8_t* mask,
+                             float* gb, double* sq, hipStream_t s);
+hipError_t launch_bias_accumulate(const float* gb, const float* c, int B, int dout,
+                                  float noise_std, uint64_t seed, uint64_t offset, float* out,
+                                  hipStream_t s);
+
 // One projected Adam step (optim.hip).
 struct AdamArgs {
   const float* grad;        // [dout, r] privatised projected gradient

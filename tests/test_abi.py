@@ -141,6 +141,18 @@ def test_seeded_projected_argument_checks(L):
     assert f(*args(out=FAKE + 4)) == DPF_ERR_UNSUPPORTED
 
 
+def test_bias_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    f = L.dpfused_linear_clip_accumulate_bias
+    call = lambda out=FAKE, bout=FAKE, C=1.0: f(ctypes.byref(X), ctypes.byref(G), None, C, 1.0, 0,
+                                                 0, out, bout, None, None)
+    assert call(bout=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(out=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(bout=FAKE + 2) == DPF_ERR_UNSUPPORTED
+    assert call(out=FAKE + 4) == DPF_ERR_UNSUPPORTED
+    assert call(C=-1.0) == DPF_ERR_INVALID_ARGUMENT
+
+
 def test_group_argument_checks(L):
     n = 2
     Xs = (DpfAct * n)(_act(), _act(D=16))

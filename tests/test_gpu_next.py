@@ -223,3 +223,43 @@ def test_projected_dp_step_end_to_end_roberta():
     dW = Wd.cpu().numpy().astype(np.float64) - W.astype(np.float64)
     # a few P entries may round to the neighbouring bf16 value on either side
     assert np.linalg.norm(dW - dW_ref) <= 2e-3 * np.linalg.norm(dW_ref)
+
+
+# ---------------------------------------------------------------------------
+# bias gradients
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 300, 264, 136), (4, 16, 64, 32)])
+def test_bias_matches_oracle(dtype, shape):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout = shape
+    rng = np.random.default_rng(48)
+    lin = random_linear(rng, B, T, din, dout, dtype=dtype, lengths=[T] + [T // 2] * (B - 1))
+    X, G, m = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch), mask_dev(lin.mask, torch)
+    _, _, rn, _ = dp_linear.oracle_linear_bias(lin.X, lin.G, lin.mask, 1.0, 0.0, 0, 0, dtype)
+    C = float(np.median(rn))
+    sum_tol = SUM_TOL_BF16 if dtype == "bf16" else 1e-4
+    for sigma, tol in ((0.0, sum_tol), (0.9, AGG_TOL_BF16 if dtype == "bf16" else 1e-4)):
+        ow, ob, norms = dp.linear_clip_accumulate_bias(X, G, m, C=C, sigma=sigma, seed=4, offset=6)
+        rw, rb, rn, rc = dp_linear.oracle_linear_bias(lin.X, lin.G, lin.mask, C, sigma, 4, 6, dtype)
+        assert (rc == 1).any() and (rc < 1).any()
+        assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+        assert rel_fro(ow.cpu().numpy(), rw) <= tol
+        assert rel_fro(ob.cpu().numpy(), rb) <= tol
+
+
+def test_bias_is_the_weight_of_a_constant_input_on_gpu():
+    """The bias call against the dense call on [X, 1] (sigma = 0)."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(49)
+    B, T, din, dout = 4, 257, 263, 136
+    lin = random_linear(rng, B, T, din, dout, lengths=[257, 100, 3, 257])
+    X, G, m = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch), mask_dev(lin.mask, torch)
+    Xa = torch.cat([X, torch.ones((B, T, 1), dtype=X.dtype, device=X.device)], dim=2).contiguous()
+    ow, ob, nb = dp.linear_clip_accumulate_bias(X, G, m, C=0.05, sigma=0.0)
+    oa, na = dp.linear_clip_accumulate(Xa, G, m, C=0.05, sigma=0.0)
+    assert max_rel(nb.cpu().numpy(), na.cpu().numpy()) <= 1e-4
+    assert rel_fro(ow.cpu().numpy(), oa[:, :din].cpu().numpy()) <= 1e-4
+    assert rel_fro(ob.cpu().numpy(), oa[:, din].cpu().numpy()) <= 1e-4

@@ -282,6 +282,37 @@ def test_mask_equals_unpadded_calls_and_ignores_padding():
     np.testing.assert_array_equal(norms2, norms)
 
 
+def test_bias_is_the_weight_of_a_constant_input():
+    """Appending a constant-one column to X turns the bias into one more weight
+    column: without noise the bias variant equals the dense oracle on [X, 1]
+    (the masked rows of the extra column are selected away like the rest)."""
+    rng = np.random.default_rng(35)
+    B, T, din, dout = 4, 6, 5, 3
+    X, G, mask = _rand_case(rng, B, T, din, dout, masked=True)
+    Xa = np.concatenate([X, np.ones((B, T, 1), np.float32)], axis=2)
+    C = 0.4
+    ow, ob, n, c = dp_linear.oracle_linear_bias(X, G, mask, C, 0.0, 0, 0, "f32")
+    oa, na, ca = dp_linear.oracle_linear(Xa, G, mask, C, 0.0, 0, 0, "f32")
+    assert (c < 1).any()
+    np.testing.assert_allclose(ow, oa[:, :din], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(ob, oa[:, din], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(n, na, rtol=1e-13)
+
+
+def test_bias_noise_continues_the_weight_stream():
+    """X = 0 and G = 0: both outputs are pure noise, the bias's drawn from the
+    blocks right after the weight's."""
+    B, T, din, dout = 2, 3, 6, 5          # 30 weight elements: 8 blocks (the last one partly used)
+    X = np.zeros((B, T, din), np.float32)
+    G = np.zeros((B, T, dout), np.float32)
+    ow, ob, n, c = dp_linear.oracle_linear_bias(X, G, None, 0.5, 2.0, 9, 4, "f32")
+    assert (n == 0).all() and (c == 1).all()
+    z = philox.gaussian_scalar(9, 4, 30)
+    zb = philox.gaussian_scalar(9, 4 + 8, dout)
+    np.testing.assert_allclose(ow.ravel(), 2.0 * 0.5 * np.array(z) / B, rtol=1e-12)
+    np.testing.assert_allclose(ob, 2.0 * 0.5 * np.array(zb) / B, rtol=1e-12)
+
+
 def test_group_of_one_is_per_layer():
     rng = np.random.default_rng(30)
     X, G, mask = _rand_case(rng, 4, 5, 6, 3, masked=True)
