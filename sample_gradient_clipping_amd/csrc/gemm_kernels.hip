@@ -1,4 +1,6 @@
-// GEMM-shaped kernels of the per-layer DP step.
+// GEMM-shaped kernels of the per-layer DP step for fp32 inputs and for the
+// shapes the large-tile bf16 kernels (accum_big.hip, gram_big.hip) do not
+// take, plus the projection of the projected variant for every shape.
 //
 //  accumulate_kernel : grad = (sum_i c_i G~_i^T X~_i + noise_std * xi) / B
 //                      One GEMM whose K runs over every active token of every
@@ -13,7 +15,8 @@
 //  project_kernel    : Y = X~ P for the projected variant (DP-GRAPE explainer,
 //                      Methodology: project before clipping and noise),
 //                      optionally split along din into fp32 partials that
-//                      project_reduce_kernel sums in chunk order.
+//                      project_reduce_kernel sums in chunk order; P is read,
+//                      or (GEN) drawn from its seed where it is loaded.
 //
 // All four: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 2 x 2
 // blocks of 32 x 32 accumulators (a 128 x 128 workgroup tile), LDS double
@@ -630,12 +633,11 @@ hipError_t launch_project_t(const ProjArgs& p, hipStream_t s) {
 }  // namespace
 
 // The large-tile kernels take bf16 inputs with 16-byte vector loads and
-// address one sample's rows with 32-bit buffer offsets (< 2 GiB per sample).
-// The large-tile kernels address one sample's rows with 32-bit byte offsets,
-// including the rows of the last (partial) tile past T, which must land past
-// the end of the sample's buffer range rather than wrap around into it: the
-// padded span must stay below 2 GiB.
-// Active-step entries pack the sample and the step into 16 bits each.
+// address one sample's rows with 32-bit byte offsets, including the rows of
+// the last (partial) tile past T, which must land past the end of the
+// sample's buffer range rather than wrap around into it: the padded span must
+// stay below 2 GiB.  Active-step entries pack the sample and the step into
+// 16 bits each.
 static bool use_big(const LayerArgs& p, bool vec) {
   const int64_t lim = (int64_t)1 << 30;   // elements: 2 GiB of bf16
   const int64_t Tp = ((int64_t)p.T + 255) / 256 * 256;
