@@ -4,8 +4,10 @@ A step is one pass of the whole hot path over the seven linears of one
 Llama-13B-shaped decoder layer (q, k, v, o: 5120x5120; gate, up: 5120->13824;
 down: 13824->5120) at B = 8, T = 2048, bf16 inputs, fp32 accumulation, each
 linear clipped on its own (C = 1) with Philox noise (sigma = 1, seed 0,
-offset 0): per linear, the Gram norm phase, the ordered reduction to clip
-factors and the scaled-accumulate GEMM with the noise epilogue.
+offset 0): per linear, the norm phase the library picks for the shape (at
+these shapes the staged form: each per-sample gradient tile computed once,
+its sum of squares taken and the tile stored in HBM), the ordered reduction
+to clip factors, and the clipped sum with the noise epilogue.
 
 Inputs are seeded synthetic Gaussians (no dataset) generated on the host and
 resident in HBM before timing starts.  Prints one JSON line.
@@ -29,17 +31,18 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFMA peak"
 
-# HBM bytes per accumulate launch on this workload, from two rocprofv3 --pmc
-# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged
-# over the seven linears), each scaled by what the same counter reads for a
-# plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for
-# the kernel sources whose SHA-256 is stored here; reported as null otherwise.
-ACCUM_SOURCES = ("accum_big.hip", "common.hpp", "kernels.hpp")
-ACCUM_COUNTERS = {
-    "sources_sha256": "7745646934953e039b637b4e4f7a685ca95c7acd55ea57b85785d98f134d7bb6",
-    "fetch_kib": 1130232.65, "fetch_scale": 2.0,
-    "write_kib": 279698.29, "write_scale": 1.0,
+# HBM bytes per launch of the dominant kernels on this workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch, averaged over the seven linears), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE
+# x1.0).  Valid only for the kernel sources whose SHA-256 is stored here and
+# the default workload; reported as null otherwise.
+COUNTER_SOURCES = ("accum_big.hip", "common.hpp", "kernels.hpp")
+KERNEL_COUNTERS = {
+    "sources_sha256": None,
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
+    "fetch_scale": 2.0, "write_scale": 1.0,
+    "kernels": {},
 }
 
 
@@ -171,9 +174,12 @@ def measure_configs(dp, torch, steps, warmup):
                 dp.linear_clip_accumulate(X, G, mask, C=lin.C, sigma=lin.sigma, seed=lin.seed,
                                           offset=lin.offset, grad_out=o, norms_out=nrm)
         ms = time_calls(torch, layer, steps, warmup)
+        paths = sorted({norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate(
+            d[1], d[2], d[3], C=d[0].C, sigma=d[0].sigma, seed=d[0].seed, offset=d[0].offset,
+            grad_out=d[4], norms_out=d[5])) for d in dev})
         useful = sum(2.0 * l.active_tokens() * l.din * l.dout for l in lins)
         B = lins[0].B
-        out[name] = {"note": note, "linears": len(lins), "ms": round(ms, 4),
+        out[name] = {"note": note, "norm_path": ",".join(paths), "linears": len(lins), "ms": round(ms, 4),
                      "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
                      "samples_per_s": round(B * len(lins) / (ms * 1e-3), 1),
                      "tokens_per_s": round(sum(l.active_tokens() for l in lins) / (ms * 1e-3), 1)}
@@ -247,9 +253,13 @@ def measure_configs(dp, torch, steps, warmup):
             dp.linear_clip_accumulate_projected(X, G, Ps[lin.din], C=lin.C, sigma=lin.sigma,
                                                 grad_out=o, norms_out=nrm)
     ms = time_calls(torch, proj_layer, steps, warmup)
+    paths = sorted({norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate_projected(
+        d[1], d[2], Ps[d[0].din], C=d[0].C, sigma=d[0].sigma, grad_out=d[3], norms_out=d[4]))
+        for d in dev})
     useful = sum(2.0 * l.B * l.T * (l.din + l.dout) * r for l in lins)
     out["c5_roberta_large_projected_r256_6_linears"] = {
         "note": "bf16, projection then clip in r space; useful flops 2*B*T*(din+dout)*r",
+        "norm_path": ",".join(paths),
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
         "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
@@ -305,18 +315,41 @@ def copy_calibration(steps):
                       "launches": steps}), flush=True)
 
 
-def accumulate_traffic(args):
-    """Counter-derived HBM bytes per accumulate launch, or None when the kernel
+def kernel_traffic(args, kernel):
+    """Counter-derived HBM bytes per launch of `kernel`, or None when the kernel
     sources or the workload differ from the profiled ones."""
-    c = ACCUM_COUNTERS
+    c = KERNEL_COUNTERS
     h = hashlib.sha256()
-    for f in ACCUM_SOURCES:
+    for f in COUNTER_SOURCES:
         with open(os.path.join(ROOT, "sample_gradient_clipping_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if (h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"] or args.seq != c["seq"]
-            or args.linears != c["linears"]):
+    k = c["kernels"].get(kernel)
+    if (k is None or h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"]
+            or args.seq != c["seq"] or args.linears != c["linears"]):
         return None
-    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+    return (k["fetch_kib"] * c["fetch_scale"] + k["write_kib"] * c["write_scale"]) * 1024.0
+
+
+def norm_path_of(dp, call):
+    """Which norm path the library took for one call (from its kernel timing)."""
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        call()
+        names = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    for key, path in (("staged_norm", "staged"), ("gram_norm", "gram"), ("direct_norm", "direct")):
+        if key in names:
+            return path
+    return "unknown"
+
+
+def staged_bytes(l):
+    """Staged per-sample tiles of one linear (256 x 256 fp32 tiles, padded)."""
+    tiles = -(-l.din // 256) * -(-l.dout // 256)
+    return 4.0 * l.B * tiles * 65536
 
 
 def upload(a, torch):
@@ -432,16 +465,20 @@ def main():
     # per linear: the fused call alone, and a plain bf16 GEMM G^T X of the same
     # shape (no clipping, no noise) as the non-DP reference
     per_linear = []
+    paths = []
     for lin, (X, G, out, norms) in zip(lins, dev_in):
-        ms = time_calls(torch, lambda: dp.linear_clip_accumulate(
+        call = lambda: dp.linear_clip_accumulate(
             X, G, None, C=lin.C, sigma=lin.sigma, seed=lin.seed, offset=lin.offset,
-            grad_out=out, norms_out=norms), args.steps, 2)
+            grad_out=out, norms_out=norms)
+        paths.append(norm_path_of(dp, call))
+        ms = time_calls(torch, call, args.steps, 2)
         Gt = G.reshape(-1, lin.dout).t().contiguous()
         X2 = X.reshape(-1, lin.din)
         ms_gemm = time_calls(torch, lambda: torch.matmul(Gt, X2), args.steps, 2)
         del Gt
         f = 2.0 * lin.B * lin.T * lin.din * lin.dout
         per_linear.append({"linear": lin.name, "din": lin.din, "dout": lin.dout,
+                           "norm_path": paths[-1],
                            "useful_gflop": round(f / 1e9, 1), "ms": round(ms, 4),
                            "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
                            "samples_per_s": round(lin.B / (ms * 1e-3), 1),
@@ -450,23 +487,65 @@ def main():
                            "dp_over_plain_throughput": round(ms_gemm / ms, 3)})
 
     useful = sum(2.0 * l.B * l.T * l.din * l.dout for l in lins)
-    gram = sum(float(l.B) * l.T * l.T * (l.din + l.dout) for l in lins)
+    contraction = lambda l: 2.0 * l.B * l.T * l.din * l.dout
+    gram_flops = lambda l: float(l.B) * l.T * l.T * (l.din + l.dout)
+    executed = sum(contraction(l) + (gram_flops(l) if p == "gram" else contraction(l) if p == "direct"
+                                     else 0.0) for l, p in zip(lins, paths))
     tflops = useful / (ms_step * 1e-3) / 1e12
     samples_per_s = sum(l.B for l in lins) / (ms_step * 1e-3)
 
-    acc_ms, acc_n = ktimes.get("accumulate", (0.0, 0))
-    fix_ms, _ = ktimes.get("accumulate_fixup", (0.0, 0))
-    gram_ms, gram_n = ktimes.get("gram_norm", (0.0, 0))
-    acc_avg_ms = acc_ms / max(acc_n, 1)
-    acc_flops_per_launch = useful / len(lins)
-    acc_achieved = acc_flops_per_launch / (acc_avg_ms * 1e-3) / 1e12 if acc_n else None
-    gram_achieved = (gram / len(lins)) / ((gram_ms / max(gram_n, 1)) * 1e-3) / 1e12 if gram_n else None
-    # the accumulate step including the pass that sums split tiles' partials
-    acc_phase = useful / ((acc_ms + fix_ms) / args.steps * 1e-3) / 1e12 if acc_n else None
+    # MFMA kernels and the flops each does per linear; the dominant one (most
+    # time per step) is the roofline kernel.
+    mfma_flops = {
+        "staged_norm": lambda l, p: contraction(l) if p == "staged" else 0.0,
+        "direct_norm": lambda l, p: contraction(l) if p == "direct" else 0.0,
+        "gram_norm": lambda l, p: gram_flops(l) if p == "gram" else 0.0,
+        "accumulate": lambda l, p: contraction(l) if p != "staged" else 0.0,
+    }
+    kernel_desc = {
+        "staged_norm": "staged_norm (per-sample gradient tiles by MFMA, their sums of squares, "
+                       "tiles stored once for the combine pass)",
+        "direct_norm": "direct_norm (per-sample gradient tiles by MFMA, sums of squares)",
+        "gram_norm": "gram_norm (per-sample Gram blocks by MFMA, weighted product sum)",
+        "accumulate": "accumulate (scaled-accumulate GEMM + noise epilogue)",
+    }
 
-    traffic = accumulate_traffic(args)
-    algo_bytes = sum(2.0 * l.B * l.T * (l.din + l.dout) + 4.0 * l.din * l.dout for l in lins) / len(lins)
+    def achieved_tflops(k):
+        ms, n = ktimes.get(k, (0.0, 0))
+        if n == 0:
+            return None
+        f = sum(mfma_flops[k](l, p) for l, p in zip(lins, paths)) * args.steps
+        return f / (ms * 1e-3) / 1e12
 
+    dom = max((k for k in mfma_flops if k in ktimes), key=lambda k: ktimes[k][0])
+    dom_n = ktimes[dom][1]
+    dom_flops = sum(mfma_flops[dom](l, p) for l, p in zip(lins, paths)) * args.steps / dom_n
+    dom_avg_ms = ktimes[dom][0] / dom_n
+    dom_achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    # algorithmic bytes per launch of the dominant kernel: X and G read once
+    # (bf16), plus what it must write -- the staged tiles (staged_norm) or the
+    # fp32 result (accumulate)
+    users = [(l, p) for l, p in zip(lins, paths) if mfma_flops[dom](l, p) > 0]
+    dom_algo_bytes = sum(2.0 * l.B * l.T * (l.din + l.dout)
+                         + (staged_bytes(l) if dom == "staged_norm" else
+                            4.0 * l.din * l.dout if dom == "accumulate" else 0.0)
+                         for l, _ in users) / max(len(users), 1)
+    traffic = kernel_traffic(args, dom)
+
+    # the combine pass of the staged path is bound by HBM: staged tiles read
+    # once, the fp32 result written once
+    comb_ms, comb_n = ktimes.get("staged_combine", (0.0, 0))
+    comb = None
+    if comb_n:
+        st = [l for l, p in zip(lins, paths) if p == "staged"]
+        comb_bytes = sum(staged_bytes(l) + 4.0 * l.din * l.dout for l in st) / len(st)
+        comb_gbs = comb_bytes / ((comb_ms / comb_n) * 1e-3) / 1e9
+        comb = {"kernel": "staged_combine (sum_i c_i g_i + noise, / B, from the staged tiles)",
+                "bound": "hbm", "achieved": round(comb_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(comb_gbs / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": round(comb_bytes),
+                "traffic": None if kernel_traffic(args, "staged_combine") is None
+                else round(kernel_traffic(args, "staged_combine"))}
 
     res = {
         "metric": METRIC,
@@ -483,25 +562,27 @@ def main():
         "data": "synthetic (seeded Gaussian X, lognormal-scaled G; no dataset)",
         "config": {"workload": "llama13b_decoder_layer_7_linears_B8_T2048_bf16",
                    "batch": args.batch, "seq_len": args.seq, "linears": names,
-                   "C": 1.0, "sigma": 1.0, "norm_path": "auto (Gram for all seven)",
+                   "C": 1.0, "sigma": 1.0,
+                   "norm_path": "auto: " + ", ".join(f"{l.name} {p}" for l, p in zip(lins, paths)),
                    "parallelism": "none (1 GPU)"},
         "samples_per_s": round(samples_per_s, 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "executed_tflops": round((useful + gram) / (ms_step * 1e-3) / 1e12, 2),
+        "executed_tflops": round(executed / (ms_step * 1e-3) / 1e12, 2),
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in ktimes.items()},
         "roofline": {
-            "kernel": "accumulate (scaled-accumulate GEMM + noise epilogue)",
+            "kernel": kernel_desc[dom],
             "bound": "mfma",
-            "achieved": None if acc_achieved is None else round(acc_achieved, 2),
+            "achieved": round(dom_achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": None if acc_achieved is None else round(acc_achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dom_achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None if traffic is None else round(traffic),
         },
-        "accumulate_bytes_per_launch": {"algorithmic": round(algo_bytes),
-                                        "hbm_counters": None if traffic is None else round(traffic)},
-        "accumulate_with_fixup_tflops": None if acc_phase is None else round(acc_phase, 2),
-        "gram_norm_kernel_tflops": None if gram_achieved is None else round(gram_achieved, 2),
+        "roofline_kernel_bytes_per_launch": {"algorithmic": round(dom_algo_bytes),
+                                             "hbm_counters": None if traffic is None else round(traffic)},
+        "combine_roofline": comb,
+        "mfma_kernel_tflops": {k: round(achieved_tflops(k), 2) for k in mfma_flops
+                               if achieved_tflops(k) is not None},
         "per_linear": per_linear,
         "bitwise_deterministic": bool(deterministic),
         "gpu_sclk_during_timed_steps": clock.summary(),

@@ -24,10 +24,16 @@
  * dpfused_noise_blocks(dout*din) blocks: advance `offset` by that much
  * between calls to draw fresh noise.
  *
- * No per-sample gradient is ever written to memory.  The per-sample norms come
- * from the Gram identity ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> when T is short
- * relative to the layer, or from the gradient tiles themselves otherwise;
- * both give the same n_i up to rounding.
+ * Each call picks one of three ways to the norms, all giving the same n_i
+ * and grad_out up to rounding: the Gram identity
+ * ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> (T short relative to the layer), the
+ * per-sample gradient tiles computed and dropped (a second contraction then
+ * forms the clipped sum), or -- for the single-layer calls on bf16 -- those
+ * tiles computed once and staged in a device workspace (fp32, B * dout * din
+ * values rounded up to 256 x 256 tiles, at most 16 GiB) that the clipped sum
+ * then reads back.  The staged form trades the second contraction for one
+ * pass over HBM; the choice is made per call from measured rates (see the
+ * "norm_path" option).  Staged tiles live only for the duration of the call.
  *
  * Conventions for every entry point
  *   - Every data pointer is DEVICE memory owned by the caller; the library
@@ -279,11 +285,16 @@ dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, floa
 uint64_t dpfused_noise_blocks(int64_t n_elements);
 
 /* Library options (process-wide).  Names:
- *   "norm_path"  0 = choose per call (Gram when max T is short relative to
- *                din*dout/(din+dout), else direct), 1 = always Gram,
- *                2 = always direct
+ *   "norm_path"  0 = choose per call; 1 = always Gram; 2 = always direct
+ *                (gradient tiles computed and dropped, then a second
+ *                contraction); 3 = staged where the call allows it (bf16
+ *                single-layer calls whose staged tiles fit in 16 GiB), else
+ *                direct
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
+ *   "workspace_keep_bytes"  bytes of freed workspace the library's per-device
+ *                memory pool keeps reserved for later calls (default 16 GiB;
+ *                setting it trims the pools to that size)
  * Returns DPF_ERR_INVALID_ARGUMENT for an unknown name or value. */
 dpf_status dpfused_set_option(const char* name, int64_t value);
 int64_t dpfused_get_option(const char* name);

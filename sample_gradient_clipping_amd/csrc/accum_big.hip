@@ -2,6 +2,10 @@
 //
 //   accumulate_big_kernel : grad = (sum_i c_i G~_i^T X~_i + noise_std xi) / B
 //   direct_norm_big_kernel: per (output tile, sample) sum of squares of g_i's tile
+//   staged_norm_big_kernel: the same, and g_i's tile itself stored (fp32) in a
+//                           workspace; staged_combine_kernel then forms
+//                           (sum_i c_i g_i + noise_std xi) / B from those tiles,
+//                           so each per-sample gradient is computed only once
 //
 // Workgroup: 512 threads = 8 waves (2 x 4, two per SIMD); workgroup tile 256
 // (din) x 256 (dout); each wave owns 128 x 64 = 4 x 2 blocks of
@@ -675,6 +679,116 @@ __global__ void __launch_bounds__(kNT, 1) direct_norm_big_kernel(LayerArgs p) {
   if (threadIdx.x == 0) p.partials[(int64_t)b * ntiles + local] = tot;
 }
 
+// Staged per-sample gradients.  Unit u = b * ntiles + L is sample b's output
+// tile L (grouped raster order); its 256 x 256 fp32 tile is stored at
+// skws + u * 65536 as the accumulator's register image: 16-byte chunk
+// (w * 32 + k) * 64 + lane holds v[i][j][4g .. 4g+3] of lane `lane` of wave
+// w, with k = (i * kBO + j) * 4 + g.  Each store instruction writes 1 KiB
+// contiguously and needs no LDS; the combine kernel decodes the image.
+constexpr int kImgChunks = kBA * kBO * 4;   // 16-byte chunks per lane
+
+// Persistent: G workgroups (one per compute unit) take units u = L, L + G,
+// ... (L the XCD-aware logical index), so the workgroups resident on one XCD
+// work on neighbouring tiles of one sample at a time and share its X and G
+// strips in that XCD's L2; a unit's tile stores then overlap the next unit's
+// pipeline fill.  Each wave writes its own fp64 partial (np = 8 per tile), so
+// no LDS is needed between units.
+constexpr int kStagedParts = kWaves;
+
+__global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, int G) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
+  const int ntiles = ntm * ntn;
+  const int N = ntiles * p.B;
+  const int nsteps = (p.T + kKT - 1) / kKT;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  Acc acc;
+  for (int u = logical_wg(blockIdx.x, G); u < N; u += G) {
+    const int b = u / ntiles, L = u - b * ntiles;
+    int tm, tn;
+    raster(L, ntm, ntn, &tm, &tn);
+    if (p.steps != nullptr) {
+      const int k0 = (int)((c_u32*)p.steps)[1 + b], k1 = (int)((c_u32*)p.steps)[2 + b];
+      run<false, true>(p, k0, k1 - k0, tm * kTile, tn * kTile, acc, smem);
+    } else {
+      run<false, false>(p, b * nsteps, nsteps, tm * kTile, tn * kTile, acc, smem);
+    }
+    float* img = p.skws + (int64_t)u * kTileElems + ((int64_t)wave * kImgChunks * 64 + lane) * 4;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBA; ++i)
+#pragma unroll
+      for (int j = 0; j < kBO; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+          v.x = acc.v[i][j][4 * g + 0]; v.y = acc.v[i][j][4 * g + 1];
+          v.z = acc.v[i][j][4 * g + 2]; v.w = acc.v[i][j][4 * g + 3];
+          s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          // read once, by the combine kernel: stream it past the caches
+          __builtin_nontemporal_store(v, (f32x4*)(img + ((i * kBO + j) * 4 + g) * 256));
+        }
+    const double tot = wave_sum_f64((double)s);
+    if (lane == 0) p.partials[((int64_t)b * ntiles + L) * kStagedParts + wave] = tot;
+    // Every wave's LDS reads of this unit have returned before any wave's
+    // next DMA refills the ring; the stores stay in flight.
+    lds_reads_done();
+    step_barrier();
+  }
+}
+
+// out = (sum_b c_b g_b + noise_std xi) / B from the staged tiles: one thread
+// per 16-byte chunk of a tile image, i.e. 4 consecutive din columns of one
+// output row; samples summed in order, kCombBatch loads in flight (indices
+// past B clamped to the last sample and their values dropped).
+constexpr int kCombThreads = 256;
+constexpr int kCombBlocksPerTile = kTileElems / 4 / kCombThreads;   // 64
+constexpr int kCombBatch = 8;
+
+__global__ void __launch_bounds__(kCombThreads) staged_combine_kernel(LayerArgs p) {
+  const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
+  const int ntiles = ntm * ntn;
+  const int L = blockIdx.x / kCombBlocksPerTile;
+  const int chunk = (blockIdx.x % kCombBlocksPerTile) * kCombThreads + (int)threadIdx.x;
+  const int lane = chunk & 63, k = (chunk >> 6) % kImgChunks, wave = (chunk >> 6) / kImgChunks;
+  const int g = k & 3, j = (k >> 2) % kBO, i = (k >> 2) / kBO;
+  int tm, tn;
+  raster(L, ntm, ntn, &tm, &tn);
+  const int a = tm * kTile + (wave / kWaveCols) * (kBA * 32) + i * 32 + acc_row(4 * g, lane);
+  const int o = tn * kTile + (wave % kWaveCols) * (kBO * 32) + j * 32 + acc_col(lane);
+  if (o >= p.dout || a >= p.din) return;   // din % 8 == 0 on this path: a..a+3 all in range
+  const float* src = p.skws + (int64_t)L * kTileElems + (int64_t)chunk * 4;
+  const int64_t stride = (int64_t)ntiles * kTileElems;   // one sample's tiles
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int b0 = 0; b0 < p.B; b0 += kCombBatch) {
+    f32x4 w[kCombBatch];
+    float cb[kCombBatch];
+#pragma unroll
+    for (int q = 0; q < kCombBatch; ++q) {
+      const int b = min(b0 + q, p.B - 1);
+      w[q] = __builtin_nontemporal_load((const f32x4*)(src + (int64_t)b * stride));
+      cb[q] = p.c[b];
+    }
+#pragma unroll
+    for (int q = 0; q < kCombBatch; ++q) {
+      if (b0 + q < p.B) {
+        v.x += cb[q] * w[q].x; v.y += cb[q] * w[q].y;
+        v.z += cb[q] * w[q].z; v.w += cb[q] * w[q].w;
+      }
+    }
+  }
+  const float rB = 1.0f / (float)p.B;   // as in store_tile
+  const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
+  if (p.noise_std != 0.0f) {
+    const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
+    v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
+    v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
+  }
+  v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+  *(f32x4*)(p.out + e0) = v;
+}
+
 }  // namespace big
 
 namespace {
@@ -729,6 +843,40 @@ hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s) {
                      dim3(big::kFixThreads), 0, s, p, sk);
   e = hipGetLastError();
   timing_end("accumulate_fixup", s);
+  return e;
+}
+
+size_t staged_big_workspace_bytes(const LayerArgs& p) {
+  return (size_t)p.B * big_tiles(p.din, p.dout) * big::kTileElems * sizeof(float);
+}
+
+int staged_big_partials_per_sample(const LayerArgs& p) {
+  return big_tiles(p.din, p.dout) * big::kStagedParts;
+}
+
+hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s) {
+  hipError_t e = allow_lds_big<big::staged_norm_big_kernel>(big::kLdsBytes);
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)big_tiles(p.din, p.dout) * p.B;
+  if (p.skws == nullptr || units > 0x7fffffff) return hipErrorInvalidValue;
+  int G = (int)std::min<int64_t>(device_cus(), units);
+  if (G >= 8) G -= G % 8;
+  timing_begin("staged_norm", s);
+  hipLaunchKernelGGL(big::staged_norm_big_kernel, dim3((unsigned)G), dim3(big::kNT),
+                     big::kLdsBytes, s, p, G);
+  e = hipGetLastError();
+  timing_end("staged_norm", s);
+  return e;
+}
+
+hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s) {
+  const int64_t blocks = (int64_t)big_tiles(p.din, p.dout) * big::kCombBlocksPerTile;
+  if (p.skws == nullptr || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  timing_begin("staged_combine", s);
+  hipLaunchKernelGGL(big::staged_combine_kernel, dim3((unsigned)blocks), dim3(big::kCombThreads),
+                     0, s, p);
+  const hipError_t e = hipGetLastError();
+  timing_end("staged_combine", s);
   return e;
 }
 

@@ -2,8 +2,9 @@
 //
 // Every entry point validates all of its arguments before queueing anything:
 // a failed check launches nothing and writes nothing.  Workspace (per-sample
-// norm partials, clip factors, mask row-activity bits, the projected activations) is
-// allocated with hipMallocAsync and released with hipFreeAsync on the call's
+// norm partials, clip factors, mask row-activity bits, the projected
+// activations, staged per-sample gradient tiles) is allocated in stream order
+// from a per-device memory pool and released with hipFreeAsync on the call's
 // stream, so calls on different streams do not share state.
 #include <hip/hip_runtime.h>
 
@@ -22,7 +23,7 @@
 namespace {
 
 thread_local std::string g_last_error;
-std::atomic<int> g_norm_path{0};   // 0 auto, 1 gram, 2 direct
+std::atomic<int> g_norm_path{0};   // 0 auto, 1 gram, 2 direct, 3 staged
 std::atomic<int> g_timing{0};
 
 dpf_status fail(dpf_status s, const std::string& msg) {
@@ -98,22 +99,112 @@ bool vec_ok(const dpf_act* a) {
 
 dpf::Act to_act(const dpf_act* a) { return dpf::Act{a->data, a->stride_b, a->stride_t}; }
 
-dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec) {
+// Largest staged workspace (B per-sample gradient tiles, fp32) a call may use.
+constexpr double kStagedMaxBytes = 16.0 * (1ull << 30);
+
+// Rates used to price the norm paths against each other on the large-tile
+// path, measured on MI355X at the Llama-13B, GPT-2 and RoBERTa shapes (flops
+// or bytes per microsecond): the direct and staged norm kernels run the
+// token contraction at ~1.25 PFLOP/s, the accumulate kernel at ~1.15, the
+// Gram kernel at ~1.05 plus ~25 us of fills and fixup; the staged tiles
+// cost ~1/10 us per MB to store (beyond the contraction) and are read back
+// at ~5 TB/s.
+constexpr double kNormPerUs = 1.25e9, kAccPerUs = 1.15e9, kGramPerUs = 1.05e9;
+constexpr double kStorePerUs = 10.0e6, kCombinePerUs = 5.0e6;
+constexpr double kGramFixedUs = 25.0, kAccFixedUs = 15.0, kCombineFixedUs = 5.0;
+
+// allow_staged: the caller runs the accumulate phase right after the norm
+// phase on the same workspace (the single-layer calls), so the per-sample
+// tiles can be staged in between.
+dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) {
+  const bool big = dpf::big_path(a, vec);
+  const double staged_bytes = (double)dpf::staged_big_workspace_bytes(a);
+  const bool staged_ok = allow_staged && big && staged_bytes <= kStagedMaxBytes &&
+                         (double)a.B * dpf::big_tiles(a.din, a.dout) < 2147483647.0;
   const int forced = g_norm_path.load();
   if (forced == 1) return dpf::NormPath::kGram;
   if (forced == 2) return dpf::NormPath::kDirect;
+  if (forced == 3) return staged_ok ? dpf::NormPath::kStaged : dpf::NormPath::kDirect;
   const double T = a.T, din = a.din, dout = a.dout;
   const double direct = 2.0 * T * din * dout;   // flops per sample
-  if (dpf::big_path(a, vec)) {
+  if (big) {
     // The large-tile Gram kernel works on 256 x 256 token blocks (padded),
-    // at about three quarters of the direct kernel's rate per flop and with
-    // a fixed cost per block (two pipeline fills, a parked X Gram): measured
-    // on MI355X it wins once it needs at most half the direct kernel's flops.
+    // with a fixed cost per block (two pipeline fills, a parked X Gram):
+    // measured on MI355X it beats the direct kernel once it needs at most
+    // half the direct kernel's flops.
     const double gram = 2.0 * dpf::gram_big_items_per_sample(a.T) * 65536.0 * (din + dout);
-    return 2.0 * gram <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+    const bool use_gram = 2.0 * gram <= direct;
+    const dpf::NormPath two_pass = use_gram ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+    // Staged: the direct kernel, storing its tiles, then a read of them in
+    // place of the accumulate kernel's second contraction.  Masked calls
+    // keep the two-pass paths: the host does not know their active tokens.
+    if (staged_ok && a.mask == nullptr) {
+      const double acc = a.B * direct;   // the contraction both forms run once
+      const double t_two_pass =
+          (use_gram ? a.B * gram / kGramPerUs + kGramFixedUs : acc / kNormPerUs) +
+          acc / kAccPerUs + kAccFixedUs;
+      const double t_staged = acc / kNormPerUs + staged_bytes / kStorePerUs +
+                              staged_bytes / kCombinePerUs + kCombineFixedUs;
+      if (t_staged < t_two_pass) return dpf::NormPath::kStaged;
+    }
+    return two_pass;
   }
   // Gram costs T^2 (din + dout) per sample, the direct form 2 T din dout.
   return T * T * (din + dout) <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
+}
+
+// Per-device stream-ordered memory pool for workspace.  It keeps up to
+// g_keep_bytes reserved across synchronisations (the default pool returns
+// freed memory at every synchronisation), so a call that needs gigabytes --
+// the staged path -- does not map them afresh on every step.
+std::atomic<int64_t> g_keep_bytes{(int64_t)16 << 30};
+std::mutex g_pool_mu;
+constexpr int kMaxDevices = 64;
+hipMemPool_t g_pools[kMaxDevices] = {};
+bool g_pool_tried[kMaxDevices] = {};
+
+int stream_device(hipStream_t s) {
+  int dev = -1;
+  if (s != nullptr) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(s, &d) == hipSuccess) dev = (int)d;
+  }
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) dev = -1;
+  return dev;
+}
+
+hipMemPool_t workspace_pool(hipStream_t s) {
+  const int dev = stream_device(s);
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (!g_pool_tried[dev]) {
+    g_pool_tried[dev] = true;
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+      uint64_t keep = (uint64_t)g_keep_bytes.load();
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      g_pools[dev] = pool;
+    } else {
+      (void)hipGetLastError();   // fall back to hipMallocAsync's default pool
+    }
+  }
+  return g_pools[dev];
+}
+
+void set_keep_bytes(int64_t keep) {
+  g_keep_bytes.store(keep);
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (g_pools[d] == nullptr) continue;
+    uint64_t k = (uint64_t)keep;
+    (void)hipMemPoolSetAttribute(g_pools[d], hipMemPoolAttrReleaseThreshold, &k);
+    (void)hipMemPoolTrimTo(g_pools[d], (size_t)keep);
+  }
 }
 
 // Stream-ordered workspace carved into 256-byte aligned pieces.
@@ -132,7 +223,10 @@ struct Workspace {
   }
   bool allocate() {
     if (size == 0) return true;
-    return hipMallocAsync(&base, size, s) == hipSuccess && base != nullptr;
+    hipMemPool_t pool = workspace_pool(s);
+    const hipError_t e = pool != nullptr ? hipMallocFromPoolAsync(&base, size, pool, s)
+                                         : hipMallocAsync(&base, size, s);
+    return e == hipSuccess && base != nullptr;
   }
   template <class T>
   T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
@@ -150,7 +244,8 @@ struct LayerPlan {
   int np = 0;
 };
 
-LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
+LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                     bool allow_staged = false) {
   LayerPlan L;
   L.args.X = to_act(X);
   L.args.G = to_act(G);
@@ -162,7 +257,7 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask) {
   L.args.mask = mask;
   L.args.nwords = (int)((X->T + dpf::kBitsTokens - 1) / dpf::kBitsTokens);
   L.vec = vec_ok(X) && vec_ok(G);
-  L.path = choose_path(L.args, L.vec);
+  L.path = choose_path(L.args, L.vec, allow_staged);
   L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
   return L;
 }
@@ -213,10 +308,17 @@ hipError_t bind_layer(LayerPlan& L, const Workspace& ws, const LayerWs& o, hipSt
   return e;
 }
 
+// Accumulate phase of a single-layer call: the staged path combines the
+// tiles its norm phase stored; the others run the scaled contraction.
+hipError_t accumulate_phase(const LayerPlan& L, hipStream_t s) {
+  if (L.path == dpf::NormPath::kStaged) return dpf::launch_staged_combine(L.args, s);
+  return dpf::launch_accumulate(L.args, L.vec, s);
+}
+
 dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
                        float sigma, uint64_t seed, uint64_t offset, float* grad_out,
                        float* norms_out, hipStream_t s, Workspace& ws) {
-  LayerPlan L = plan_layer(X, G, mask);
+  LayerPlan L = plan_layer(X, G, mask, true);
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
@@ -232,7 +334,7 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
   L.args.seed = seed;
   L.args.offset = offset;
   L.args.out = grad_out;
-  e = dpf::launch_accumulate(L.args, L.vec, s);
+  e = accumulate_phase(L, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
 }
@@ -274,7 +376,7 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
   // Reserve the layer workspace now so that a single allocation covers both.
   dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
-  LayerPlan L = plan_layer(&Y, G, mask);
+  LayerPlan L = plan_layer(&Y, G, mask, true);
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   Y.data = ws.at<void>(off_y);
@@ -284,7 +386,7 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   hipError_t e = dpf::launch_project(pa, pvec, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
-  L = plan_layer(&Y, G, mask);
+  L = plan_layer(&Y, G, mask, true);
   e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
   L.args.partials = ws.at<double>(o.part);
@@ -298,7 +400,7 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   L.args.seed = seed;
   L.args.offset = offset;
   L.args.out = grad_out;
-  e = dpf::launch_accumulate(L.args, L.vec, s);
+  e = accumulate_phase(L, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
 }
@@ -336,7 +438,7 @@ dpf_status accumulate_with(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   L.args.seed = seed;
   L.args.offset = offset;
   L.args.out = grad_out;
-  e = dpf::launch_accumulate(L.args, L.vec, s);
+  e = accumulate_phase(L, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
 }
@@ -619,8 +721,14 @@ uint64_t dpfused_noise_blocks(int64_t n_elements) {
 dpf_status dpfused_set_option(const char* name, int64_t value) {
   if (name == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "option name is NULL");
   if (std::strcmp(name, "norm_path") == 0) {
-    if (value < 0 || value > 2) return fail(DPF_ERR_INVALID_ARGUMENT, "norm_path must be 0, 1 or 2");
+    if (value < 0 || value > 3)
+      return fail(DPF_ERR_INVALID_ARGUMENT, "norm_path must be 0, 1, 2 or 3");
     g_norm_path.store((int)value);
+    return ok();
+  }
+  if (std::strcmp(name, "workspace_keep_bytes") == 0) {
+    if (value < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "workspace_keep_bytes must be >= 0");
+    set_keep_bytes(value);
     return ok();
   }
   if (std::strcmp(name, "timing") == 0) {
@@ -635,6 +743,7 @@ int64_t dpfused_get_option(const char* name) {
   if (name == nullptr) return -1;
   if (std::strcmp(name, "norm_path") == 0) return g_norm_path.load();
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
+  if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
   return -1;
 }
 

@@ -652,7 +652,9 @@ size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec) {
 }
 
 size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec) {
-  return (path == NormPath::kGram && use_big(p, vec)) ? gram_big_workspace_bytes(p) : 0;
+  if (!use_big(p, vec)) return 0;
+  if (path == NormPath::kGram) return gram_big_workspace_bytes(p);
+  return path == NormPath::kStaged ? staged_big_workspace_bytes(p) : 0;
 }
 
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
@@ -661,6 +663,7 @@ int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
     const int nt = (p.T + kTileM - 1) / kTileM;
     return nt * (nt + 1) / 2;
   }
+  if (path == NormPath::kStaged && use_big(p, vec)) return staged_big_partials_per_sample(p);
   if (use_big(p, vec)) return big_tiles(p.din, p.dout);
   return ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
 }
@@ -670,7 +673,14 @@ hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s) {
   if (p.dtype == kBF16) return vec ? launch_accumulate_t<BF16, true>(p, s) : launch_accumulate_t<BF16, false>(p, s);
   return vec ? launch_accumulate_t<F32, true>(p, s) : launch_accumulate_t<F32, false>(p, s);
 }
+hipError_t launch_staged_combine(const LayerArgs& p, hipStream_t s) {
+  return launch_staged_combine_big(p, s);
+}
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s) {
+  if (path == NormPath::kStaged) {
+    if (!use_big(p, vec)) return hipErrorInvalidValue;
+    return launch_staged_norm_big(p, s);
+  }
   if (path == NormPath::kGram) {
     if (use_big(p, vec)) return launch_gram_norm_big(p, s);
     if (p.dtype == kBF16) return vec ? launch_gram_t<BF16, true>(p, s) : launch_gram_t<BF16, false>(p, s);

@@ -9,7 +9,10 @@
 namespace dpf {
 
 enum DType { kF32 = 0, kBF16 = 1 };
-enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2 };
+// kStaged (large-tile path only): the direct kernel also stores every
+// per-sample gradient tile (fp32) in the workspace, and the accumulate phase
+// is launch_staged_combine over those tiles instead of a second contraction.
+enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2, kStaged = 3 };
 
 // Tokens covered by one word of the per-sample row-activity bits.
 constexpr int kBitsTokens = 32;
@@ -89,6 +92,8 @@ bool big_path(const LayerArgs& p, bool vec);
 size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec);
 size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec);
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s);
+// Accumulate phase of the staged path: out from the tiles launch_norm stored.
+hipError_t launch_staged_combine(const LayerArgs& p, hipStream_t s);
 hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t s);
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
 // Number of din chunks launch_project splits Y = X P into, and the fp32
@@ -103,6 +108,10 @@ int big_tiles(int din, int dout);
 size_t accumulate_big_workspace_bytes(const LayerArgs& p);
 hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
+size_t staged_big_workspace_bytes(const LayerArgs& p);
+int staged_big_partials_per_sample(const LayerArgs& p);
+hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s);
+hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s);
 
 // Large-tile bf16 Gram-norm kernel (gram_big.hip).
 int gram_big_items_per_sample(int T);

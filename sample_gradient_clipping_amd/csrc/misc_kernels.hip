@@ -103,14 +103,21 @@ __device__ __forceinline__ void clip_of_sq(double sq, float C, float* c, float* 
   *c = (nn <= (double)C) ? 1.0f : (float)((double)C / nn);
 }
 
-// One thread per sample; the partials of a sample are summed in index order.
-__global__ void finalize_kernel(const double* partials, int B, int np, double* sq_io,
-                                int accumulate, float C, float* c_out, float* norms_out) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
+// One workgroup per sample.  Thread t sums partials t, t + 256, ... in index
+// order; the 256 sums are then combined by the fixed tree of block_sum_f64,
+// so the result does not depend on timing.
+constexpr int kFinThreads = 256;
+__global__ void __launch_bounds__(kFinThreads) finalize_kernel(const double* partials, int np,
+                                                               double* sq_io, int accumulate,
+                                                               float C, float* c_out,
+                                                               float* norms_out) {
+  __shared__ double red[kFinThreads / 64];
+  const int b = blockIdx.x;
   const double* row = partials + (int64_t)b * np;
-  double sq = 0.0;
-  for (int i = 0; i < np; ++i) sq += row[i];
+  double part = 0.0;
+  for (int i = threadIdx.x; i < np; i += kFinThreads) part += row[i];
+  double sq = block_sum_f64(part, red);
+  if (threadIdx.x != 0) return;
   if (sq_io != nullptr) {
     if (accumulate) sq += sq_io[b];
     sq_io[b] = sq;
@@ -190,7 +197,7 @@ int device_cus() {
 hipError_t launch_finalize(const double* partials, int B, int np, double* sq_io, int accumulate,
                            float C, float* c_out, float* norms_out, hipStream_t s) {
   timing_begin("finalize", s);
-  hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(B, 64)), dim3(64), 0, s, partials, B, np,
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)B), dim3(kFinThreads), 0, s, partials, np,
                      sq_io, accumulate, C, c_out, norms_out);
   timing_end("finalize", s);
   return hipGetLastError();

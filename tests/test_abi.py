@@ -61,7 +61,17 @@ def test_options(L):
     assert L.dpfused_set_option(b"norm_path", 2) == DPF_OK
     assert L.dpfused_get_option(b"norm_path") == 2
     assert L.dpfused_set_option(b"norm_path", 0) == DPF_OK
-    assert L.dpfused_set_option(b"norm_path", 3) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"norm_path", 3) == DPF_OK
+    assert L.dpfused_get_option(b"norm_path") == 3
+    assert L.dpfused_set_option(b"norm_path", 0) == DPF_OK
+    assert L.dpfused_set_option(b"norm_path", 4) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"norm_path", -1) == DPF_ERR_INVALID_ARGUMENT
+    keep = L.dpfused_get_option(b"workspace_keep_bytes")
+    assert keep == 16 << 30
+    assert L.dpfused_set_option(b"workspace_keep_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"workspace_keep_bytes", 1 << 20) == DPF_OK
+    assert L.dpfused_get_option(b"workspace_keep_bytes") == 1 << 20
+    assert L.dpfused_set_option(b"workspace_keep_bytes", keep) == DPF_OK
     assert L.dpfused_set_option(b"bogus", 1) == DPF_ERR_INVALID_ARGUMENT
     assert b"bogus" in L.dpfused_last_error()
     assert L.dpfused_get_option(b"bogus") == -1

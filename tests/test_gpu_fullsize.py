@@ -21,13 +21,13 @@ AGG_TOL = 2e-2
 SUM_TOL = 1e-3
 
 
-def _compare(lin, torch):
-    out, norms = run_dense(lin, torch)
+def _compare(lin, torch, path=None):
+    out, norms = run_dense(lin, torch, path=path)
     ref, rnorms, rc = dp_linear.oracle_linear(lin.X, lin.G, lin.mask, lin.C, lin.sigma, lin.seed,
                                               lin.offset, lin.dtype)
     assert max_rel(norms, rnorms) <= NORM_TOL
     assert rel_fro(out, ref) <= AGG_TOL
-    out0, _ = run_dense(lin, torch, sigma=0.0)
+    out0, _ = run_dense(lin, torch, sigma=0.0, path=path)
     ref0 = ref - lin.sigma * lin.C * dp_linear.noise_matrix(lin.seed, lin.offset, ref.shape) / lin.B
     err0 = rel_fro(out0, ref0)
     assert err0 <= SUM_TOL, err0
@@ -39,6 +39,23 @@ def test_llama13b_layer_linear(index):
     torch = need_gpu()
     lin = workloads.config_c3_linear(index)
     _compare(lin, torch)
+
+
+# Each norm path forced on one linear of each shape (q: 5120 -> 5120, gate:
+# 5120 -> 13824, down: 13824 -> 5120), whichever the automatic choice is:
+# 1 Gram, 3 staged per-sample tiles.
+@pytest.mark.parametrize("path", [1, 3])
+@pytest.mark.parametrize("index", [0, 4, 6])
+def test_llama13b_layer_linear_forced_path(index, path):
+    torch = need_gpu()
+    lin = workloads.config_c3_linear(index)
+    _compare(lin, torch, path=path)
+
+
+def test_llama13b_ragged_q_staged():
+    torch = need_gpu()
+    lin = workloads.config_c4_linear(0)
+    _compare(lin, torch, path=3)
 
 
 @pytest.mark.parametrize("index", range(7))

@@ -15,7 +15,7 @@ def _dev(lin, torch):
     return to_dev(lin.X, lin.dtype, torch), to_dev(lin.G, lin.dtype, torch), mask_dev(lin.mask, torch)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_bitwise_determinism(path):
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
@@ -112,21 +112,64 @@ def test_scale_invariance_of_clipped_sample():
     assert rel_fro(o2.cpu().numpy(), o1.cpu().numpy()) <= 1e-5
 
 
-def test_gram_and_direct_paths_agree():
+def test_gram_direct_and_staged_paths_agree():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
     rng = np.random.default_rng(26)
     lin = random_linear(rng, 4, 384, 256, 384, masked=True)
     X, G, m = _dev(lin, torch)
     res = {}
-    for path in (1, 2):
+    for path in (1, 2, 3):
         dp.set_option("norm_path", path)
         try:
             res[path] = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.0)
         finally:
             dp.set_option("norm_path", 0)
-    assert max_rel(res[1][1].cpu().numpy(), res[2][1].cpu().numpy()) <= 1e-4
-    assert rel_fro(res[1][0].cpu().numpy(), res[2][0].cpu().numpy()) <= 1e-4
+    for path in (2, 3):
+        assert max_rel(res[1][1].cpu().numpy(), res[path][1].cpu().numpy()) <= 1e-4
+        assert rel_fro(res[1][0].cpu().numpy(), res[path][0].cpu().numpy()) <= 1e-4
+
+
+@pytest.mark.parametrize("shape,expect", [
+    ((8, 2048, 5120, 5120), "staged_norm"),   # Llama-13B q: staging the tiles beats a second pass
+    ((8, 512, 5120, 5120), "gram_norm"),      # short sequences: the Gram phase is cheap
+    ((32, 512, 768, 3072), "direct_norm"),    # GPT-2 MLP: direct, then a second contraction
+])
+def test_automatic_norm_path_choice(shape, expect):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout = shape
+    X = torch.randn((B, T, din), device="cuda").to(torch.bfloat16)
+    G = torch.randn((B, T, dout), device="cuda").to(torch.bfloat16)
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        dp.linear_clip_accumulate(X, G, None, C=1.0, sigma=1.0)
+        t = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    assert expect in t, sorted(t)
+
+
+def test_staged_path_launches_its_kernels():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    X = torch.randn((2, 64, 256), device="cuda").to(torch.bfloat16)
+    G = torch.randn((2, 64, 128), device="cuda").to(torch.bfloat16)
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    dp.set_option("norm_path", 3)
+    try:
+        for _ in range(2):
+            dp.linear_clip_accumulate(X, G, None, C=1.0, sigma=1.0)
+        t = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.set_option("norm_path", 0)
+        dp.timing_reset()
+    assert t["staged_norm"][1] == 2 and t["staged_combine"][1] == 2
+    assert "accumulate" not in t and "gram_norm" not in t
 
 
 def test_sqnorms_accumulate_and_scaled_accumulate_compose():

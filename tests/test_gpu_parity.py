@@ -56,8 +56,10 @@ SHAPES = [
 ]
 
 
+# norm paths: 1 Gram, 2 direct (tiles dropped, second contraction), 3 staged
+# (bf16 large-tile calls: tiles stored once, then combined; elsewhere direct)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_dense_small_mixed_clip(dtype, path, shape):
     B, T, din, dout = shape
@@ -82,7 +84,7 @@ def test_dense_odd_dims_scalar_loads(dtype, path):
     _check(lin, path, sigma=1.3, C=C)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_dense_ragged_prefix_masks(path):
     rng = np.random.default_rng(6)
     lengths = [300, 0, 1, 129, 64, 65]
@@ -95,12 +97,28 @@ def test_dense_ragged_prefix_masks(path):
     _check(lin, path, sigma=1.2, C=C)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_dense_random_mask(path):
     rng = np.random.default_rng(7)
     lin = random_linear(rng, 4, 257, 136, 72, masked=True)
     _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
     _check(lin, path, sigma=0.0, C=float(np.median(rn)), agg_tol=SUM_TOL_BF16)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_staged_multi_tile_ragged_edges(masked):
+    """Staged path over 3 x 4 output tiles whose last row and column are
+    partial, 10 token steps with a ragged tail, and (masked) a sample with
+    no active token, whose staged tiles are all zero."""
+    rng = np.random.default_rng(31)
+    lengths = [300, 0, 77, 300] if masked else None
+    lin = random_linear(rng, 4, 300, 520, 776, lengths=lengths)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn[rn > 0]))
+    out, norms, _, _ = _check(lin, 3, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+    if masked:
+        assert norms[1] == 0.0
+    _check(lin, 3, sigma=1.1, C=C)
 
 
 def test_strided_views():
@@ -138,9 +156,10 @@ def test_config_gpt2_up_projection():
     _check(lin, 0, sigma=0.0, C=float(np.median(rn)), agg_tol=SUM_TOL_BF16)
 
 
-def test_config_gpt2_up_projection_direct_path():
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_config_gpt2_up_projection_forced_paths(path):
     lin = workloads.config_c2().linears[0]
-    _check(lin, 2, sigma=0.0, agg_tol=SUM_TOL_BF16)
+    _check(lin, path, sigma=0.0, agg_tol=SUM_TOL_BF16)
 
 
 @pytest.mark.parametrize("index", [0, 4, 5])
