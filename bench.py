@@ -37,12 +37,16 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE
 # x1.0).  Valid only for the kernel sources whose SHA-256 is stored here and
 # the default workload; reported as null otherwise.
-COUNTER_SOURCES = ("accum_big.hip", "common.hpp", "kernels.hpp")
+COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": None,
+    "sources_sha256": "0d31a054410a2a6d76931b5fae4add5c395c75200b24d2874a10c9ffaf7dc6a7",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "kernels": {},
+    # per --norm-path value: kernel -> KiB per dispatch
+    "runs": {
+        "0": {"staged_norm": {"fetch_kib": 1213016.07, "write_kib": 1416805.65}, "staged_combine": {"fetch_kib": 708063.02, "write_kib": 177418.34}},
+        "1": {"accumulate": {"fetch_kib": 1130427.26, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 418924.59, "write_kib": 152505.33}},
+    },
 }
 
 
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down")
+    ap.add_argument("--norm-path", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="0: the library's per-call choice (default); 1 Gram, 2 direct, 3 staged")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     ap.add_argument("--configs", action="store_true",
@@ -323,7 +329,7 @@ def kernel_traffic(args, kernel):
     for f in COUNTER_SOURCES:
         with open(os.path.join(ROOT, "sample_gradient_clipping_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    k = c["kernels"].get(kernel)
+    k = c["runs"].get(str(args.norm_path), {}).get(kernel)
     if (k is None or h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"]
             or args.seq != c["seq"] or args.linears != c["linears"]):
         return None
@@ -404,6 +410,7 @@ def main():
     import workloads
 
     dp.load()
+    dp.set_option("norm_path", args.norm_path)
     dev = torch.device("cuda:0")
     names = [n.strip() for n in args.linears.split(",")]
     idx = [i for i, (n, _, _) in enumerate(workloads.C3_LINEARS) if n in names]
@@ -563,7 +570,8 @@ def main():
         "config": {"workload": "llama13b_decoder_layer_7_linears_B8_T2048_bf16",
                    "batch": args.batch, "seq_len": args.seq, "linears": names,
                    "C": 1.0, "sigma": 1.0,
-                   "norm_path": "auto: " + ", ".join(f"{l.name} {p}" for l, p in zip(lins, paths)),
+                   "norm_path": ("auto: " if args.norm_path == 0 else "forced: ")
+                                + ", ".join(f"{l.name} {p}" for l, p in zip(lins, paths)),
                    "parallelism": "none (1 GPU)"},
         "samples_per_s": round(samples_per_s, 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

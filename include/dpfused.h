@@ -28,10 +28,10 @@
  * and grad_out up to rounding: the Gram identity
  * ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> (T short relative to the layer), the
  * per-sample gradient tiles computed and dropped (a second contraction then
- * forms the clipped sum), or -- for the single-layer calls on bf16 -- those
- * tiles computed once and staged in a device workspace (fp32, B * dout * din
- * values rounded up to 256 x 256 tiles, at most 16 GiB) that the clipped sum
- * then reads back.  The staged form trades the second contraction for one
+ * forms the clipped sum), or -- for unmasked bf16 calls of the single-layer
+ * and group entry points -- those tiles computed once and staged in a device
+ * workspace (fp32, B * dout * din values rounded up to 256 x 256 tiles, at
+ * most 16 GiB per call) that the clipped sum then reads back.  The staged form trades the second contraction for one
  * pass over HBM; the choice is made per call from measured rates (see the
  * "norm_path" option).  Staged tiles live only for the duration of the call.
  *
@@ -288,8 +288,8 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *   "norm_path"  0 = choose per call; 1 = always Gram; 2 = always direct
  *                (gradient tiles computed and dropped, then a second
  *                contraction); 3 = staged where the call allows it (bf16
- *                single-layer calls whose staged tiles fit in 16 GiB), else
- *                direct
+ *                single-layer and group calls whose staged tiles fit in
+ *                16 GiB), else direct
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
  *   "workspace_keep_bytes"  bytes of freed workspace the library's per-device

@@ -686,6 +686,7 @@ __global__ void __launch_bounds__(kNT, 1) direct_norm_big_kernel(LayerArgs p) {
 // w, with k = (i * kBO + j) * 4 + g.  Each store instruction writes 1 KiB
 // contiguously and needs no LDS; the combine kernel decodes the image.
 constexpr int kImgChunks = kBA * kBO * 4;   // 16-byte chunks per lane
+constexpr int64_t kImgStride = kTileElems;   // floats from one unit's image to the next
 
 // Persistent: G workgroups (one per compute unit) take units u = L, L + G,
 // ... (L the XCD-aware logical index), so the workgroups resident on one XCD
@@ -713,7 +714,7 @@ __global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, in
     } else {
       run<false, false>(p, b * nsteps, nsteps, tm * kTile, tn * kTile, acc, smem);
     }
-    float* img = p.skws + (int64_t)u * kTileElems + ((int64_t)wave * kImgChunks * 64 + lane) * 4;
+    float* img = p.skws + (int64_t)u * kImgStride + ((int64_t)wave * kImgChunks * 64 + lane) * 4;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < kBA; ++i)
@@ -757,8 +758,8 @@ __global__ void __launch_bounds__(kCombThreads) staged_combine_kernel(LayerArgs 
   const int a = tm * kTile + (wave / kWaveCols) * (kBA * 32) + i * 32 + acc_row(4 * g, lane);
   const int o = tn * kTile + (wave % kWaveCols) * (kBO * 32) + j * 32 + acc_col(lane);
   if (o >= p.dout || a >= p.din) return;   // din % 8 == 0 on this path: a..a+3 all in range
-  const float* src = p.skws + (int64_t)L * kTileElems + (int64_t)chunk * 4;
-  const int64_t stride = (int64_t)ntiles * kTileElems;   // one sample's tiles
+  const float* src = p.skws + (int64_t)L * kImgStride + (int64_t)chunk * 4;
+  const int64_t stride = (int64_t)ntiles * kImgStride;   // one sample's tiles
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int b0 = 0; b0 < p.B; b0 += kCombBatch) {
@@ -847,7 +848,7 @@ hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s) {
 }
 
 size_t staged_big_workspace_bytes(const LayerArgs& p) {
-  return (size_t)p.B * big_tiles(p.din, p.dout) * big::kTileElems * sizeof(float);
+  return (size_t)p.B * big_tiles(p.din, p.dout) * big::kImgStride * sizeof(float);
 }
 
 int staged_big_partials_per_sample(const LayerArgs& p) {

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -622,16 +623,64 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   double* sq = ws.at<double>(off_sq);
   float* c = ws.at<float>(off_c);
+  // A linear on the staged path keeps its per-sample tiles, in a workspace of
+  // its own, from its norm phase until its accumulate phase (after the
+  // group's clip factors exist).  The group's staged tiles stay within the
+  // per-call limit; the linears past it take their two-pass path.
+  struct StagedLinear {
+    LayerPlan L;
+    std::unique_ptr<Workspace> ws;
+    bool on = false;
+  };
+  std::vector<StagedLinear> lin((size_t)n);
+  double staged_total = 0.0;
+  for (int32_t l = 0; l < n; ++l) {
+    StagedLinear& z = lin[(size_t)l];
+    z.L = plan_layer(&X[l], &G[l], mask, true);
+    if (z.L.path != dpf::NormPath::kStaged) continue;
+    const double bytes = (double)dpf::staged_big_workspace_bytes(z.L.args);
+    if (staged_total + bytes > kStagedMaxBytes) continue;
+    staged_total += bytes;
+    z.ws.reset(new Workspace(s));
+    const LayerWs o = reserve_layer(z.L, *z.ws, true, false, false);
+    if (!z.ws->allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+    hipError_t e = bind_layer(z.L, *z.ws, o, s);
+    if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+    z.L.args.partials = z.ws->at<double>(o.part);
+    z.on = true;
+  }
   // norm phase of every linear: n_i^2 summed over the group
-  for (int32_t l = 0; l < n; ++l)
-    if ((st = sqnorms_into(&X[l], &G[l], mask, sq, l > 0, s)) != DPF_OK) return st;
+  for (int32_t l = 0; l < n; ++l) {
+    StagedLinear& z = lin[(size_t)l];
+    if (!z.on) {
+      if ((st = sqnorms_into(&X[l], &G[l], mask, sq, l > 0, s)) != DPF_OK) return st;
+      continue;
+    }
+    hipError_t e = dpf::launch_norm(z.L.args, z.L.path, z.L.vec, s);
+    if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+    e = dpf::launch_finalize(z.L.args.partials, z.L.args.B, z.L.np, sq, l > 0 ? 1 : 0, 1.0f,
+                             nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  }
   hipError_t e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "clip factor launch");
   // accumulate phase of every linear with the group's factors
-  for (int32_t l = 0; l < n; ++l)
-    if ((st = accumulate_with(&X[l], &G[l], mask, c, sigma * C, seed, offsets[l], grad_out[l], s)) !=
-        DPF_OK)
-      return st;
+  for (int32_t l = 0; l < n; ++l) {
+    StagedLinear& z = lin[(size_t)l];
+    if (!z.on) {
+      if ((st = accumulate_with(&X[l], &G[l], mask, c, sigma * C, seed, offsets[l], grad_out[l],
+                                s)) != DPF_OK)
+        return st;
+      continue;
+    }
+    z.L.args.c = c;
+    z.L.args.noise_std = sigma * C;
+    z.L.args.seed = seed;
+    z.L.args.offset = offsets[l];
+    z.L.args.out = grad_out[l];
+    e = dpf::launch_staged_combine(z.L.args, s);
+    if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  }
   return ok();
 }
 

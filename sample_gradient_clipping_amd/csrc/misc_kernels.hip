@@ -103,10 +103,10 @@ __device__ __forceinline__ void clip_of_sq(double sq, float C, float* c, float* 
   *c = (nn <= (double)C) ? 1.0f : (float)((double)C / nn);
 }
 
-// One workgroup per sample.  Thread t sums partials t, t + 256, ... in index
-// order; the 256 sums are then combined by the fixed tree of block_sum_f64,
-// so the result does not depend on timing.
-constexpr int kFinThreads = 256;
+// One workgroup per sample.  Thread t sums partials t, t + 1024, ... in index
+// order (four loads in flight at a time); the 1024 sums are then combined by
+// the fixed tree of block_sum_f64, so the result does not depend on timing.
+constexpr int kFinThreads = 1024;
 __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const double* partials, int np,
                                                                double* sq_io, int accumulate,
                                                                float C, float* c_out,
@@ -115,7 +115,16 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const double* par
   const int b = blockIdx.x;
   const double* row = partials + (int64_t)b * np;
   double part = 0.0;
-  for (int i = threadIdx.x; i < np; i += kFinThreads) part += row[i];
+  int i = threadIdx.x;
+  for (; i + 3 * kFinThreads < np; i += 4 * kFinThreads) {
+    const double v0 = row[i], v1 = row[i + kFinThreads];
+    const double v2 = row[i + 2 * kFinThreads], v3 = row[i + 3 * kFinThreads];
+    part += v0;
+    part += v1;
+    part += v2;
+    part += v3;
+  }
+  for (; i < np; i += kFinThreads) part += row[i];
   double sq = block_sum_f64(part, red);
   if (threadIdx.x != 0) return;
   if (sq_io != nullptr) {

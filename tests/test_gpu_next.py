@@ -116,6 +116,54 @@ def test_group_of_one_is_the_dense_call_bitwise():
     assert torch.equal(n1, n2)
 
 
+@pytest.mark.parametrize("path", [0, 3])
+def test_group_clip_unmasked_matches_oracle(path):
+    """Unmasked bf16 group over the large-tile path: automatic choice, and
+    every linear forced onto the staged path (per-sample tiles kept from
+    each linear's norm phase until the group's clip factors exist)."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(45)
+    dims = [(512, 640), (640, 512), (256, 1024)]
+    lins, mask = _group_case(rng, 3, 300, dims, None)
+    pairs = [(l.X, l.G) for l in lins]
+    offsets = [0, 1000, 5000]
+    _, rn, _ = dp_linear.oracle_group(pairs, None, 1.0, 0.0, 0, offsets, "bf16")
+    C = float(np.median(rn))
+    Xs = [to_dev(l.X, "bf16", torch) for l in lins]
+    Gs = [to_dev(l.G, "bf16", torch) for l in lins]
+    dp.set_option("norm_path", path)
+    try:
+        for sigma, tol in ((0.0, SUM_TOL_BF16), (1.1, AGG_TOL_BF16)):
+            outs, norms = dp.group_clip_accumulate(Xs, Gs, None, C=C, sigma=sigma, seed=3,
+                                                   offsets=offsets)
+            refs, rn, rc = dp_linear.oracle_group(pairs, None, C, sigma, 3, offsets, "bf16")
+            assert (rc == 1).any() and (rc < 1).any()
+            assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+            for o, ref in zip(outs, refs):
+                assert rel_fro(o.cpu().numpy(), ref) <= tol
+    finally:
+        dp.set_option("norm_path", 0)
+
+
+def test_group_of_one_is_the_staged_dense_call_bitwise():
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(46)
+    lin = random_linear(rng, 4, 257, 264, 136)
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    dp.set_option("norm_path", 3)
+    try:
+        o1, n1 = dp.linear_clip_accumulate(X, G, None, C=0.01, sigma=0.9, seed=5, offset=17)
+        (o2,), n2 = dp.group_clip_accumulate([X], [G], None, C=0.01, sigma=0.9, seed=5,
+                                             offsets=[17])
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
+    assert torch.equal(o1, o2)
+    assert torch.equal(n1, n2)
+
+
 def test_group_row_split_reproduces_whole_layer():
     """Two linears that are the output-row halves of one linear: group
     clipping of the halves gives the whole linear's per-layer result."""
