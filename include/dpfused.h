@@ -41,7 +41,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     queued on it asynchronously; temporary workspace is allocated and
  *     released in stream order on the same stream.  Calls on different
- *     streams may run concurrently.
+ *     streams may run concurrently, except that calls on the staged path
+ *     take the device's staged-tile buffer in turn (each call's stream waits,
+ *     on the GPU, for the previous holder's last use).
  *   - Arguments are checked before anything is queued: on any error nothing
  *     is launched and nothing is written; the status says why and
  *     dpfused_last_error() gives a message (per thread).
@@ -292,9 +294,14 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                16 GiB), else direct
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
- *   "workspace_keep_bytes"  bytes of freed workspace the library's per-device
- *                memory pool keeps reserved for later calls (default 16 GiB;
- *                setting it trims the pools to that size)
+ *   "workspace_keep_bytes"  bytes the library keeps reserved for later calls
+ *                (default 16 GiB): freed workspace in its per-device memory
+ *                pool, and the per-device buffer of staged per-sample tiles
+ *                (freed after each call when larger).  Setting it trims both;
+ *                trimming the staged buffer waits for its last user.
+ * Read-only (dpfused_get_option): "workspace_reserved_bytes" and
+ * "workspace_reserved_high", what the current device's pool holds now and at
+ * most (-1 without a pool).
  * Returns DPF_ERR_INVALID_ARGUMENT for an unknown name or value. */
 dpf_status dpfused_set_option(const char* name, int64_t value);
 int64_t dpfused_get_option(const char* name);

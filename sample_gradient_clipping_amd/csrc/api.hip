@@ -197,14 +197,96 @@ hipMemPool_t workspace_pool(hipStream_t s) {
   return g_pools[dev];
 }
 
+// The staged per-sample tiles (up to gigabytes) live in one buffer per device
+// that the library keeps and grows, not in the pool: pool allocations of that
+// size, freed and made again by calls on several streams, were measured to
+// stall for tens of milliseconds on MI355X.  Calls on any stream take the
+// buffer in turn: each one's stream first waits (on the GPU) for the event
+// recorded after the previous holder's last use, and records its own after
+// its last launch.  A buffer larger than g_keep_bytes is freed after use.
+struct StagedBuffer {
+  std::mutex mu;
+  void* ptr = nullptr;
+  size_t size = 0;
+  hipEvent_t last = nullptr;
+  bool recorded = false;
+};
+StagedBuffer g_staged[kMaxDevices];
+
+class StagedLease {
+ public:
+  ~StagedLease() { release(); }
+  // Holds the calling thread's device buffer of at least `bytes` for work
+  // queued on `s` until release(); false if it cannot be had.
+  bool acquire(hipStream_t s, size_t bytes) {
+    const int dev = stream_device(s);
+    if (dev < 0 || dev >= kMaxDevices) return false;
+    buf_ = &g_staged[dev];
+    lk_ = std::unique_lock<std::mutex>(buf_->mu);
+    s_ = s;
+    if (buf_->last == nullptr &&
+        hipEventCreateWithFlags(&buf_->last, hipEventDisableTiming) != hipSuccess) {
+      buf_->last = nullptr;
+      return fail_acquire();
+    }
+    if (buf_->recorded && hipStreamWaitEvent(s, buf_->last, 0) != hipSuccess) return fail_acquire();
+    if (buf_->size < bytes) {
+      if (buf_->ptr != nullptr) (void)hipFreeAsync(buf_->ptr, s);
+      buf_->ptr = nullptr;
+      buf_->size = 0;
+      if (hipMallocAsync(&buf_->ptr, bytes, s) != hipSuccess || buf_->ptr == nullptr) {
+        buf_->ptr = nullptr;
+        return fail_acquire();
+      }
+      buf_->size = bytes;
+    }
+    held_ = true;
+    return true;
+  }
+  void* ptr() const { return held_ ? buf_->ptr : nullptr; }
+  void release() {
+    if (!held_) return;
+    held_ = false;
+    if (hipEventRecord(buf_->last, s_) == hipSuccess) buf_->recorded = true;
+    if ((int64_t)buf_->size > g_keep_bytes.load()) {
+      (void)hipFreeAsync(buf_->ptr, s_);
+      buf_->ptr = nullptr;
+      buf_->size = 0;
+    }
+    lk_.unlock();
+  }
+
+ private:
+  bool fail_acquire() {
+    (void)hipGetLastError();
+    lk_.unlock();
+    return false;
+  }
+  StagedBuffer* buf_ = nullptr;
+  std::unique_lock<std::mutex> lk_;
+  hipStream_t s_ = nullptr;
+  bool held_ = false;
+};
+
 void set_keep_bytes(int64_t keep) {
   g_keep_bytes.store(keep);
-  std::lock_guard<std::mutex> lk(g_pool_mu);
+  {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    for (int d = 0; d < kMaxDevices; ++d) {
+      if (g_pools[d] == nullptr) continue;
+      uint64_t k = (uint64_t)keep;
+      (void)hipMemPoolSetAttribute(g_pools[d], hipMemPoolAttrReleaseThreshold, &k);
+      (void)hipMemPoolTrimTo(g_pools[d], (size_t)keep);
+    }
+  }
   for (int d = 0; d < kMaxDevices; ++d) {
-    if (g_pools[d] == nullptr) continue;
-    uint64_t k = (uint64_t)keep;
-    (void)hipMemPoolSetAttribute(g_pools[d], hipMemPoolAttrReleaseThreshold, &k);
-    (void)hipMemPoolTrimTo(g_pools[d], (size_t)keep);
+    StagedBuffer& b = g_staged[d];
+    std::lock_guard<std::mutex> lk(b.mu);
+    if (b.ptr == nullptr || (int64_t)b.size <= keep) continue;
+    if (b.recorded) (void)hipEventSynchronize(b.last);   // its last user is done with it
+    (void)hipFreeAsync(b.ptr, nullptr);
+    b.ptr = nullptr;
+    b.size = 0;
   }
 }
 
@@ -267,6 +349,7 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
 struct LayerWs {
   size_t bits = 0, steps = 0, part = 0, c = 0, sk = 0;
   bool has_steps = false, has_sk = false;
+  size_t staged = 0;   // staged path: bytes of per-sample tiles (held in a StagedLease)
 };
 
 // Reserve what the call needs: row bits and the active-step list when
@@ -283,6 +366,10 @@ LayerWs reserve_layer(const LayerPlan& L, Workspace& ws, bool norm, bool clip, b
   }
   if (norm) o.part = ws.reserve((size_t)a.B * L.np * sizeof(double));
   if (clip) o.c = ws.reserve((size_t)a.B * sizeof(float));
+  if (L.path == dpf::NormPath::kStaged) {
+    o.staged = dpf::norm_workspace_bytes(a, L.path, L.vec);
+    return o;
+  }
   size_t bytes = 0;   // split-piece partials; the norm and accumulate phases share them
   if (norm) bytes = dpf::norm_workspace_bytes(a, L.path, L.vec);
   if (accum) bytes = std::max(bytes, dpf::accumulate_workspace_bytes(a, L.vec));
@@ -324,6 +411,12 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
+  if (L.path == dpf::NormPath::kStaged) {
+    if (!lease.acquire(s, o.staged))
+      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
+    L.args.skws = static_cast<float*>(lease.ptr());
+  }
   L.args.partials = ws.at<double>(o.part);
   e = dpf::launch_norm(L.args, L.path, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
@@ -390,6 +483,13 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   L = plan_layer(&Y, G, mask, true);
   e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
+  if (L.path == dpf::NormPath::kStaged) {
+    if (!lease.acquire(s, o.staged))
+      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
+    L.args.skws = static_cast<float*>(lease.ptr());
+  }
+
   L.args.partials = ws.at<double>(o.part);
   e = dpf::launch_norm(L.args, L.path, L.vec, s);
   if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
@@ -630,17 +730,19 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
   struct StagedLinear {
     LayerPlan L;
     std::unique_ptr<Workspace> ws;
+    size_t at = 0;   // offset of its tiles in the staged buffer
     bool on = false;
   };
   std::vector<StagedLinear> lin((size_t)n);
-  double staged_total = 0.0;
+  size_t staged_total = 0;
   for (int32_t l = 0; l < n; ++l) {
     StagedLinear& z = lin[(size_t)l];
     z.L = plan_layer(&X[l], &G[l], mask, true);
     if (z.L.path != dpf::NormPath::kStaged) continue;
-    const double bytes = (double)dpf::staged_big_workspace_bytes(z.L.args);
-    if (staged_total + bytes > kStagedMaxBytes) continue;
-    staged_total += bytes;
+    const size_t bytes = dpf::staged_big_workspace_bytes(z.L.args);
+    if ((double)(staged_total + bytes) > kStagedMaxBytes) continue;
+    z.at = staged_total;
+    staged_total = (staged_total + bytes + 255) & ~(size_t)255;
     z.ws.reset(new Workspace(s));
     const LayerWs o = reserve_layer(z.L, *z.ws, true, false, false);
     if (!z.ws->allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
@@ -648,6 +750,13 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
     if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
     z.L.args.partials = z.ws->at<double>(o.part);
     z.on = true;
+  }
+  StagedLease lease;
+  if (staged_total != 0) {
+    if (!lease.acquire(s, staged_total))
+      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
+    for (auto& z : lin)
+      if (z.on) z.L.args.skws = reinterpret_cast<float*>(static_cast<char*>(lease.ptr()) + z.at);
   }
   // norm phase of every linear: n_i^2 summed over the group
   for (int32_t l = 0; l < n; ++l) {
@@ -793,6 +902,16 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "norm_path") == 0) return g_norm_path.load();
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
   if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
+  // Read-only: memory the current device's workspace pool holds now, and the
+  // most it has held (-1 when there is no pool).
+  const bool now = std::strcmp(name, "workspace_reserved_bytes") == 0;
+  if (now || std::strcmp(name, "workspace_reserved_high") == 0) {
+    hipMemPool_t pool = workspace_pool(nullptr);
+    uint64_t v = 0;
+    const hipMemPoolAttr attr = now ? hipMemPoolAttrReservedMemCurrent : hipMemPoolAttrReservedMemHigh;
+    if (pool == nullptr || hipMemPoolGetAttribute(pool, attr, &v) != hipSuccess) return -1;
+    return (int64_t)v;
+  }
   return -1;
 }
 
