@@ -152,6 +152,46 @@ def test_automatic_norm_path_choice(shape, expect):
     assert expect in t, sorted(t)
 
 
+@pytest.mark.parametrize("keep", [16 << 30, 0])
+def test_staged_calls_alternating_streams_match_one_stream(keep):
+    """Calls on two streams share the device's staged-tile buffer in turn:
+    results equal the one-stream results bit for bit, also when the buffer
+    is freed after every call (keep = 0)."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(27)
+    shapes = [(3, 300, 520, 776), (2, 130, 256, 1024), (3, 300, 776, 520), (4, 64, 264, 136)]
+    data = []
+    for B, T, din, dout in shapes:
+        lin = random_linear(rng, B, T, din, dout)
+        data.append((to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)))
+    old_keep = dp.get_option("workspace_keep_bytes")
+    dp.set_option("norm_path", 3)
+    dp.set_option("workspace_keep_bytes", keep)
+    try:
+        ref = [dp.linear_clip_accumulate(X, G, None, C=0.05, sigma=0.7, seed=9, offset=i)
+               for i, (X, G) in enumerate(data)]
+        torch.cuda.synchronize()
+        main = torch.cuda.current_stream()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for _ in range(3):
+            start = torch.cuda.Event()
+            start.record(main)
+            outs = []
+            for i, (X, G) in enumerate(data):
+                st = streams[i % 2]
+                st.wait_event(start)
+                with torch.cuda.stream(st):
+                    outs.append(dp.linear_clip_accumulate(X, G, None, C=0.05, sigma=0.7, seed=9,
+                                                          offset=i))
+            torch.cuda.synchronize()
+            for (o, n), (ro, rn) in zip(outs, ref):
+                assert torch.equal(o, ro) and torch.equal(n, rn)
+    finally:
+        dp.set_option("norm_path", 0)
+        dp.set_option("workspace_keep_bytes", old_keep)
+
+
 def test_staged_path_launches_its_kernels():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
