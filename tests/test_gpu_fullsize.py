@@ -76,3 +76,72 @@ def test_llama13b_q_mixed_clip():
     assert (rc == 1).any() and (rc < 1).any()
     assert max_rel(norms, rnorms) <= NORM_TOL
     assert rel_fro(out, ref) <= SUM_TOL
+
+
+# ---------------------------------------------------------------------------
+# the staged path's 16 GiB limit (inputs drawn on the GPU: no oracle at these
+# sizes; the paths are compared with each other)
+# ---------------------------------------------------------------------------
+def _kernels_of(dp, call):
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        call()
+        return dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+
+
+def _bf16_normal(torch, shape, scale, gen):
+    return (torch.randn(shape, device="cuda", generator=gen) * scale).to(torch.bfloat16)
+
+
+def test_staged_limit_falls_back_to_direct():
+    """B = 168 at 5120 x 5120: the staged tiles would take 17.6 GB > 16 GiB, so
+    even a forced staged call runs the direct path; its result matches the
+    Gram path's."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    g = torch.Generator(device="cuda").manual_seed(5)
+    B, T, D = 168, 256, 5120
+    X = _bf16_normal(torch, (B, T, D), 1.0, g)
+    G = _bf16_normal(torch, (B, T, D), 1e-3, g)
+    res = {}
+    for path in (3, 1):
+        dp.set_option("norm_path", path)
+        try:
+            t = _kernels_of(dp, lambda: res.__setitem__(
+                path, dp.linear_clip_accumulate(X, G, None, C=0.5, sigma=0.0)))
+        finally:
+            dp.set_option("norm_path", 0)
+        if path == 3:
+            assert "direct_norm" in t and "staged_norm" not in t, sorted(t)
+    assert max_rel(res[3][1].cpu().numpy(), res[1][1].cpu().numpy()) <= 1e-4
+    assert rel_fro(res[3][0].cpu().numpy(), res[1][0].cpu().numpy()) <= 1e-4
+
+
+def test_group_past_staged_limit_mixes_paths():
+    """Three linears whose staged tiles take 6.7 GB each: the first two are
+    staged and the third, past the 16 GiB limit, takes its two-pass path;
+    the group result matches the all-Gram group."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    g = torch.Generator(device="cuda").manual_seed(6)
+    B, T, D = 64, 256, 5120
+    Xs = [_bf16_normal(torch, (B, T, D), 1.0, g) for _ in range(3)]
+    Gs = [_bf16_normal(torch, (B, T, D), 1e-3, g) for _ in range(3)]
+    res = {}
+    for path in (3, 1):
+        dp.set_option("norm_path", path)
+        try:
+            t = _kernels_of(dp, lambda: res.__setitem__(path, dp.group_clip_accumulate(
+                Xs, Gs, None, C=0.5, sigma=0.0, offsets=[0, 0, 0])))
+        finally:
+            dp.set_option("norm_path", 0)
+        if path == 3:
+            assert t["staged_norm"][1] == 2 and t["direct_norm"][1] == 1, t
+    (o3, n3), (o1, n1) = res[3], res[1]
+    assert max_rel(n3.cpu().numpy(), n1.cpu().numpy()) <= 1e-4
+    for a, b in zip(o3, o1):
+        assert rel_fro(a.cpu().numpy(), b.cpu().numpy()) <= 1e-4
