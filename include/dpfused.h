@@ -113,6 +113,30 @@ dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G,
                                           float* grad_out, float* norms_out,
                                           void* stream);
 
+/* The same step with an explicit denominator, added into grad_out on request:
+ *
+ *   grad_out = beta * grad_out + (sum_i c_i g_i + sigma * C * xi) / denom,
+ *   beta = accumulate (0 or 1)
+ *
+ * For gradient accumulation over micro-batches of one logical batch, and for
+ * a batch split across devices: each part is called with the logical batch
+ * size as denom and sigma = 0 except for one part, which adds the noise.  The
+ * per-sample clipping is unchanged (each sample is clipped on its own,
+ * FlashDP abstract: per-layer clipping of each sample's gradient), so the
+ * parts add up to the call on the whole batch.  With denom = B and
+ * accumulate = 0 the result is dpfused_linear_clip_accumulate's, bit for bit.
+ *
+ *   denom       finite and > 0
+ *   accumulate  0: grad_out is overwritten; 1: the result is added to it
+ *               (grad_out must then hold finite values)
+ *   other arguments, layouts and errors as dpfused_linear_clip_accumulate;
+ *   a bad denom or accumulate gives DPF_ERR_INVALID_ARGUMENT. */
+dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
+                                             const uint8_t* mask, float C, float sigma,
+                                             uint64_t seed, uint64_t offset, float denom,
+                                             int32_t accumulate, float* grad_out,
+                                             float* norms_out, void* stream);
+
 /* Projected variant (Memory-Efficient Differentially Private Training with
  * Gradient Random Projection, English explainer, Methodology: "Random
  * Projection over SVD" and "Order of Operations").  Each sample's gradient is

@@ -90,11 +90,19 @@ def clip_accumulate(per_sample, C: float):
 
 
 def oracle_linear(X, G, mask, C: float, sigma: float, seed: int, offset: int,
-                  dtype: str = "bf16", with_noise: bool = True):
-    """Dense variant.  Returns (out [dout, din] f64, norms [B] f64, c [B] f64)."""
+                  dtype: str = "bf16", with_noise: bool = True, denom=None, out0=None):
+    """Dense variant.  Returns (out [dout, din] f64, norms [B] f64, c [B] f64).
+
+    out = (S + sigma C xi) / denom, denom = B unless given; with out0 (the
+    buffer's previous contents) the result is added to it.  Each sample is
+    still clipped on its own (FlashDP abstract: per-layer clipping of each
+    sample's gradient), so the calls on the parts of a batch, each with the
+    whole batch's size as denom and the noise in one of them, add up to the
+    call on the whole batch."""
     Xw = widen(X, dtype)
     Gw = widen(G, dtype)
     B = Xw.shape[0]
+    d = float(B if denom is None else denom)
 
     def grads():
         for i in range(B):
@@ -105,7 +113,10 @@ def oracle_linear(X, G, mask, C: float, sigma: float, seed: int, offset: int,
     out = S.copy()
     if with_noise and sigma != 0.0:
         out = out + sigma * C * noise_matrix(seed, offset, S.shape)
-    return out / B, norms, c
+    out = out / d
+    if out0 is not None:
+        out = np.asarray(out0, dtype=np.float64) + out
+    return out, norms, c
 
 
 def oracle_linear_bias(X, G, mask, C: float, sigma: float, seed: int, offset: int,

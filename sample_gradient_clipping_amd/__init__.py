@@ -84,18 +84,30 @@ def _ptr(t) -> Optional[int]:
 
 def linear_clip_accumulate(X, G, mask=None, C: float = 1.0, sigma: float = 0.0, seed: int = 0,
                            offset: int = 0, grad_out=None, norms_out=None, stream=None,
-                           want_norms: bool = True) -> Tuple[object, object]:
-    """Fused per-layer DP step; returns (grad_out [dout, din] fp32, norms [B] fp32 or None)."""
+                           want_norms: bool = True, denom: Optional[float] = None,
+                           accumulate: bool = False) -> Tuple[object, object]:
+    """Fused per-layer DP step; returns (grad_out [dout, din] fp32, norms [B] fp32 or None).
+
+    denom (default B) divides the noisy clipped sum; accumulate=True adds the
+    result into grad_out (which must then be given) instead of overwriting it."""
     torch = _torch()
     xa, ga = _act(X), _act(G)
     B, T = X.shape[0], X.shape[1]
+    if accumulate and grad_out is None:
+        raise ValueError("accumulate=True needs grad_out")
     if grad_out is None:
         grad_out = torch.empty((G.shape[2], X.shape[2]), dtype=torch.float32, device=X.device)
     if norms_out is None and want_norms:
         norms_out = torch.empty((B,), dtype=torch.float32, device=X.device)
-    st = _lib.lib().dpfused_linear_clip_accumulate(
-        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), float(C), float(sigma),
-        int(seed), int(offset), grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
+    if denom is None and not accumulate:
+        st = _lib.lib().dpfused_linear_clip_accumulate(
+            ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), float(C), float(sigma),
+            int(seed), int(offset), grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
+    else:
+        st = _lib.lib().dpfused_linear_clip_accumulate_ex(
+            ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T), float(C), float(sigma),
+            int(seed), int(offset), float(B if denom is None else denom), int(bool(accumulate)),
+            grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
 

@@ -470,7 +470,7 @@ __device__ __forceinline__ int logical_wg(int id, int G) {
 constexpr int kTileElems = kTile * kTile;
 
 // Store one output tile from the accumulator.  part == nullptr: the final
-// result (acc * c_last + noise) / B into p.out.  Otherwise the raw partial
+// result (acc * c_last + noise) / denom into p.out (added to it when beta).  Otherwise the raw partial
 // acc * c_last into part[256 x 256] (row o - o0, column a - a0), which the
 // fixup kernel sums.  The waves park their accumulator blocks in LDS one
 // 32-row block-row (i) at a time as [o][a] (64 a values: 32 from each wave
@@ -481,8 +481,8 @@ __device__ __forceinline__ void store_tile(const LayerArgs& p, const Acc& acc, f
   static_assert(256 * (64 + 4) * 4 <= kLdsBytes, "epilogue staging fits in the stage ring");
   const int lane = threadIdx.x & 63;
   const int wm = wave_row(), wn = wave_col();
-  // 1/B: exact for a power-of-two B, else within one ulp of dividing.
-  const float rB = 1.0f / (float)p.B;
+  // 1/denom: exact for a power of two, else within one ulp of dividing.
+  const float rB = 1.0f / p.denom;
   const bool noise = p.noise_std != 0.0f;
   float* park = (float*)smem;
   constexpr int kParkLd = 64 + 4;     // floats per o row (padding against bank conflicts)
@@ -521,6 +521,10 @@ __device__ __forceinline__ void store_tile(const LayerArgs& p, const Acc& acc, f
           v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
         }
         v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+        if (p.beta) {
+          const f32x4 old = *(const f32x4*)(p.out + e0);
+          v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+        }
         *(f32x4*)(p.out + e0) = v;
       }
     }
@@ -640,7 +644,7 @@ __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs
       }
     }
   }
-  const float rB = 1.0f / (float)p.B;   // as in store_tile
+  const float rB = 1.0f / p.denom;   // as in store_tile
   const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
   if (p.noise_std != 0.0f) {
     const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
@@ -648,6 +652,10 @@ __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs
     v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
   }
   v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+  if (p.beta) {
+    const f32x4 old = *(const f32x4*)(p.out + e0);
+    v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+  }
   *(f32x4*)(p.out + e0) = v;
 }
 
@@ -779,7 +787,7 @@ __global__ void __launch_bounds__(kCombThreads) staged_combine_kernel(LayerArgs 
       }
     }
   }
-  const float rB = 1.0f / (float)p.B;   // as in store_tile
+  const float rB = 1.0f / p.denom;   // as in store_tile
   const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
   if (p.noise_std != 0.0f) {
     const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
@@ -787,6 +795,10 @@ __global__ void __launch_bounds__(kCombThreads) staged_combine_kernel(LayerArgs 
     v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
   }
   v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+  if (p.beta) {
+    const f32x4 old = *(const f32x4*)(p.out + e0);
+    v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+  }
   *(f32x4*)(p.out + e0) = v;
 }
 

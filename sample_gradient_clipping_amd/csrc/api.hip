@@ -339,6 +339,8 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
   L.args.dout = (int)G->D;
   L.args.mask = mask;
   L.args.nwords = (int)((X->T + dpf::kBitsTokens - 1) / dpf::kBitsTokens);
+  L.args.denom = (float)X->B;
+  L.args.beta = 0;
   L.vec = vec_ok(X) && vec_ok(G);
   L.path = choose_path(L.args, L.vec, allow_staged);
   L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
@@ -404,9 +406,11 @@ hipError_t accumulate_phase(const LayerPlan& L, hipStream_t s) {
 }
 
 dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
-                       float sigma, uint64_t seed, uint64_t offset, float* grad_out,
-                       float* norms_out, hipStream_t s, Workspace& ws) {
+                       float sigma, uint64_t seed, uint64_t offset, float denom, int beta,
+                       float* grad_out, float* norms_out, hipStream_t s, Workspace& ws) {
   LayerPlan L = plan_layer(X, G, mask, true);
+  L.args.denom = denom;
+  L.args.beta = beta;
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
@@ -586,7 +590,28 @@ dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G, co
   if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace ws(s);
-  return fused_layer(X, G, mask, C, sigma, seed, offset, grad_out, norms_out, s, ws);
+  return fused_layer(X, G, mask, C, sigma, seed, offset, (float)X->B, 0, grad_out, norms_out, s,
+                     ws);
+}
+
+dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
+                                             const uint8_t* mask, float C, float sigma,
+                                             uint64_t seed, uint64_t offset, float denom,
+                                             int32_t accumulate, float* grad_out,
+                                             float* norms_out, void* stream) {
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (!std::isfinite(denom) || !(denom > 0.0f))
+    return fail(DPF_ERR_INVALID_ARGUMENT, "denom must be finite and > 0");
+  if (accumulate != 0 && accumulate != 1)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  return fused_layer(X, G, mask, C, sigma, seed, offset, denom, accumulate, grad_out, norms_out,
+                     s, ws);
 }
 
 dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_act* G,

@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(kNT) accumulate_kernel(LayerArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const float inv_scale = c_last;
-  const float fB = (float)p.B;
+  const float denom = p.denom;
   const bool vec_store = (p.din & 3) == 0;
 #pragma unroll
   for (int i = 0; i < kBM; ++i) {
@@ -225,14 +225,19 @@ __global__ void __launch_bounds__(kNT) accumulate_kernel(LayerArgs p) {
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = v[e] / fB;
+        for (int e = 0; e < 4; ++e) v[e] = v[e] / denom;
         float* dst = p.out + e0;
         if (vec_store) {
           f32x4 w; w.x = v[0]; w.y = v[1]; w.z = v[2]; w.w = v[3];
+          if (p.beta) {
+            const f32x4 old = *(const f32x4*)dst;
+            w.x += old.x; w.y += old.y; w.z += old.z; w.w += old.w;
+          }
           *(f32x4*)dst = w;
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) if (a + e < p.din) dst[e] = v[e];
+          for (int e = 0; e < 4; ++e)
+            if (a + e < p.din) dst[e] = p.beta ? dst[e] + v[e] : v[e];
         }
       }
     }

@@ -27,6 +27,8 @@ struct LayerArgs {
   const float* c;           // [B] clip factors (accumulate only)
   float noise_std;          // sigma * C (0 = no noise)
   uint64_t seed, offset;
+  float denom;              // the sum is divided by this (B unless the caller gives another)
+  int beta;                 // 1: out += result; 0: out = result
   float* out;               // [dout, din]
   double* partials;         // [B, norm_partials_per_sample] (norm kernels)
   const uint32_t* steps;    // active-step list (large-tile kernels, masked calls) or null

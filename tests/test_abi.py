@@ -138,6 +138,23 @@ def test_projected_argument_checks(L):
         == DPF_ERR_INVALID_ARGUMENT
 
 
+def test_ex_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    f = L.dpfused_linear_clip_accumulate_ex
+    args = lambda denom=2.0, acc=0, C=1.0, out=FAKE: (ctypes.byref(X), ctypes.byref(G), None, C, 0.5,
+                                                      0, 0, denom, acc, out, None, None)
+    assert f(*args(denom=0.0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(denom=-1.0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(denom=math.nan)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(denom=math.inf)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(acc=2)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(acc=-1)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(C=0.0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(out=0)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(out=FAKE + 4)) == DPF_ERR_UNSUPPORTED
+    assert b"" != L.dpfused_last_error()
+
+
 def test_seeded_projected_argument_checks(L):
     X, G = _act(), _act(D=16)
     f = L.dpfused_linear_clip_accumulate_projected_seeded

@@ -311,3 +311,63 @@ def test_bias_is_the_weight_of_a_constant_input_on_gpu():
     assert max_rel(nb.cpu().numpy(), na.cpu().numpy()) <= 1e-4
     assert rel_fro(ow.cpu().numpy(), oa[:, :din].cpu().numpy()) <= 1e-4
     assert rel_fro(ob.cpu().numpy(), oa[:, din].cpu().numpy()) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# f4: explicit denominator, accumulation into grad_out
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,path", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("f32", 2)])
+def test_ex_accumulates_into_grad_out_against_oracle(dtype, path):
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(47)
+    lin = random_linear(rng, 3, 300, 520, 264, dtype=dtype) if dtype == "bf16" else \
+        random_linear(rng, 3, 40, 72, 56, dtype=dtype)
+    _, rn, _ = dp_linear.oracle_linear(lin.X, lin.G, None, 1.0, 0.0, 0, 0, dtype)
+    C = float(np.median(rn))
+    s0, _, _ = dp_linear.oracle_linear(lin.X, lin.G, None, C, 0.0, 0, 0, dtype, denom=10.0)
+    out0 = (rng.standard_normal(s0.shape) * np.abs(s0).mean()).astype(np.float32)
+    X, G = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch)
+    dp.set_option("norm_path", path)
+    try:
+        for sigma in (0.0, 0.9):
+            ref, rnorms, _ = dp_linear.oracle_linear(lin.X, lin.G, None, C, sigma, 5, 17, dtype,
+                                                     denom=10.0, out0=out0)
+            grad = torch.from_numpy(out0.copy()).cuda()
+            _, norms = dp.linear_clip_accumulate(X, G, None, C=C, sigma=sigma, seed=5, offset=17,
+                                                 grad_out=grad, denom=10.0, accumulate=True)
+            assert max_rel(norms.cpu().numpy(), rnorms) <= NORM_TOL
+            # the part this call adds, free of out0
+            got = grad.cpu().numpy().astype(np.float64) - out0
+            tol = (SUM_TOL_BF16 if sigma == 0.0 else AGG_TOL_BF16) if dtype == "bf16" else 1e-4
+            assert rel_fro(got, ref - out0) <= tol
+    finally:
+        dp.set_option("norm_path", 0)
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_micro_batches_add_up_to_the_whole_batch(path):
+    """Three micro-batches of a batch of 6, each divided by 6, the noise in
+    the first, accumulated into one buffer: the whole batch's result."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(48)
+    lin = random_linear(rng, 6, 300, 520, 264)
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    C = 0.02
+    dp.set_option("norm_path", path)
+    try:
+        whole, wn = dp.linear_clip_accumulate(X, G, None, C=C, sigma=0.8, seed=3, offset=4)
+        acc = torch.empty_like(whole)
+        parts = [(0, 2, 0.8, False), (2, 5, 0.0, True), (5, 6, 0.0, True)]
+        norms = []
+        for a, b, sigma, add in parts:
+            _, n = dp.linear_clip_accumulate(X[a:b].contiguous(), G[a:b].contiguous(), None, C=C,
+                                             sigma=sigma, seed=3, offset=4, grad_out=acc,
+                                             denom=6.0, accumulate=add)
+            norms.append(n)
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
+    assert max_rel(torch.cat(norms).cpu().numpy(), wn.cpu().numpy()) <= 1e-6
+    assert rel_fro(acc.cpu().numpy(), whole.cpu().numpy()) <= 1e-5

@@ -256,6 +256,33 @@ def test_batch_split_linearity():
     np.testing.assert_allclose(6 * o_all, 2 * o_a + 4 * o_b, rtol=1e-12, atol=1e-15)
 
 
+def test_parts_with_the_whole_batch_denominator_add_up():
+    """Micro-batches (or per-device shares) called with the whole batch's
+    size as the denominator, the noise in one of them and the results added
+    into one buffer, give the call on the whole batch: clipping stays per
+    sample, so the split changes nothing."""
+    rng = np.random.default_rng(11)
+    X, G, _ = _rand_case(rng, 6, 4, 5, 3)
+    C, sigma = 0.3, 0.7
+    whole, _, _ = dp_linear.oracle_linear(X, G, None, C, sigma, 4, 9, "f32")
+    acc, _, _ = dp_linear.oracle_linear(X[:2], G[:2], None, C, sigma, 4, 9, "f32", denom=6)
+    acc, _, _ = dp_linear.oracle_linear(X[2:5], G[2:5], None, C, 0.0, 4, 9, "f32", denom=6,
+                                        out0=acc)
+    acc, _, _ = dp_linear.oracle_linear(X[5:], G[5:], None, C, 0.0, 4, 9, "f32", denom=6,
+                                        out0=acc)
+    np.testing.assert_allclose(acc, whole, rtol=1e-12, atol=1e-15)
+
+
+def test_denominator_defaults_to_the_batch_size():
+    rng = np.random.default_rng(12)
+    X, G, _ = _rand_case(rng, 3, 4, 5, 3)
+    o1, _, _ = dp_linear.oracle_linear(X, G, None, 0.3, 0.5, 1, 2, "f32")
+    o2, _, _ = dp_linear.oracle_linear(X, G, None, 0.3, 0.5, 1, 2, "f32", denom=3)
+    o3, _, _ = dp_linear.oracle_linear(X, G, None, 0.3, 0.5, 1, 2, "f32", denom=6)
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(o3, o1 / 2)
+
+
 def test_mask_equals_unpadded_calls_and_ignores_padding():
     rng = np.random.default_rng(10)
     B, T, din, dout = 4, 9, 5, 6
