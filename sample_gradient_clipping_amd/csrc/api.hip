@@ -702,6 +702,7 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
   const size_t off_sq = ws.reserve((size_t)B * sizeof(double));
   const size_t off_c = ws.reserve((size_t)B * sizeof(float));
   const size_t off_gb = ws.reserve((size_t)B * dout * sizeof(float));
+  const size_t off_part = ws.reserve(dpf::bias_workspace_bytes((int)B, (int)G->T, (int)dout));
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   double* sq = ws.at<double>(off_sq);
   float* c = ws.at<float>(off_c);
@@ -709,7 +710,7 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
   // ||g_i||^2 of the weight, then + ||gb_i||^2 of the bias
   if ((st = sqnorms_into(X, G, mask, sq, 0, s)) != DPF_OK) return st;
   hipError_t e = dpf::launch_bias_grads(to_act(G), G->dtype, (int)B, (int)G->T, (int)dout, mask,
-                                        gb, sq, s);
+                                        ws.at<float>(off_part), gb, sq, s);
   if (e != hipSuccess) return hip_fail(e, "bias gradient launch");
   e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "clip factor launch");

@@ -60,8 +60,10 @@ struct ProjArgs {
 
 // Bias gradients (bias.hip): gb[b][o] = sum of the active rows of G_b, and
 // sq[b] += ||gb[b]||^2; then out[o] = (sum_b c[b] gb[b][o] + noise_std xi_o) / B.
+// part: bias_workspace_bytes(B, T, dout) of scratch for the token-chunk sums.
+size_t bias_workspace_bytes(int B, int T, int dout);
 hipError_t launch_bias_grads(const Act& G, int dtype, int B, int T, int dout, const uint8_t* mask,
-                             float* gb, double* sq, hipStream_t s);
+                             float* part, float* gb, double* sq, hipStream_t s);
 hipError_t launch_bias_accumulate(const float* gb, const float* c, int B, int dout,
                                   float noise_std, uint64_t seed, uint64_t offset, float* out,
                                   hipStream_t s);

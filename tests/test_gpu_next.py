@@ -277,7 +277,10 @@ def test_projected_dp_step_end_to_end_roberta():
 # bias gradients
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(3, 300, 264, 136), (4, 16, 64, 32)])
+# dout 136 and 3072: 8 bf16 columns per thread, token chunks; dout 37: one
+# column per thread
+@pytest.mark.parametrize("shape", [(3, 300, 264, 136), (4, 16, 64, 32), (3, 300, 40, 37),
+                                   (2, 70, 64, 3072)])
 def test_bias_matches_oracle(dtype, shape):
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
