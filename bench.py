@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "c5ab81bfe1bd54c810c36a122878e9fbdfd89f4d0cc720c39ca878bb8e6144a7",
+    "sources_sha256": "b59e91e357f67ca0628a1a98333bc015b7e5478db742d8152c7fe61ed3c71cab",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1251111.95, "write_kib": 1416772.26}, "staged_combine": {"fetch_kib": 708059.3, "write_kib": 177177.82}},
-        "1": {"accumulate": {"fetch_kib": 1129312.75, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 419921.26, "write_kib": 152505.44}},
+        "0": {"staged_norm": {"fetch_kib": 1273151.28, "write_kib": 1416819.0}, "staged_combine": {"fetch_kib": 708059.29, "write_kib": 177202.89}},
+        "1": {"accumulate": {"fetch_kib": 1130881.3, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 417606.47, "write_kib": 152505.34}},
     },
 }
 

@@ -114,9 +114,9 @@ constexpr double kNormPerUs = 1.25e9, kAccPerUs = 1.15e9, kGramPerUs = 1.05e9;
 constexpr double kStorePerUs = 10.0e6, kCombinePerUs = 5.0e6;
 constexpr double kGramFixedUs = 25.0, kAccFixedUs = 15.0, kCombineFixedUs = 5.0;
 
-// allow_staged: the caller runs the accumulate phase right after the norm
-// phase on the same workspace (the single-layer calls), so the per-sample
-// tiles can be staged in between.
+// allow_staged: the caller keeps the per-sample tiles from the norm phase to
+// the accumulate phase (the single-layer calls, and group clipping, which
+// holds every linear's tiles until the group's clip factors exist).
 dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) {
   const bool big = dpf::big_path(a, vec);
   const double staged_bytes = (double)dpf::staged_big_workspace_bytes(a);
@@ -154,10 +154,11 @@ dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) 
   return T * T * (din + dout) <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
 }
 
-// Per-device stream-ordered memory pool for workspace.  It keeps up to
+// Per-device stream-ordered memory pool for workspace (everything but the
+// staged tiles, which have a buffer of their own below).  It keeps up to
 // g_keep_bytes reserved across synchronisations (the default pool returns
-// freed memory at every synchronisation), so a call that needs gigabytes --
-// the staged path -- does not map them afresh on every step.
+// freed memory at every synchronisation), so workspace is not mapped afresh
+// on every step.
 std::atomic<int64_t> g_keep_bytes{(int64_t)16 << 30};
 std::mutex g_pool_mu;
 constexpr int kMaxDevices = 64;
