@@ -362,37 +362,34 @@ def upload(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def cpu_baseline(lin, budget_s):
-    """The fp64 oracle (untuned) on a bounded sample of one linear's work."""
+def cpu_baseline(lins, budget_s):
+    """The fp64 oracle (untuned) on a bounded sample of the step: whole
+    linears (all samples) in the step's order until about budget_s of CPU
+    work has been done."""
     from oracle import dp_linear
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    B = lin.B
-    nsamp = 1
-    best = None
-    while True:
-        Xs, Gs = lin.X[:nsamp], lin.G[:nsamp]
-        t0 = time.perf_counter()
-        dp_linear.oracle_linear(Xs, Gs, None, lin.C, lin.sigma, lin.seed, lin.offset, "bf16")
-        dt = time.perf_counter() - t0
-        flops = 2.0 * nsamp * lin.T * lin.din * lin.dout
-        best = (nsamp, dt, flops)
-        if dt * 2 > budget_s or nsamp >= B:
+    done, dt, flops = [], 0.0, 0.0
+    for lin in lins:
+        if done and dt >= budget_s:
             break
-        nsamp = min(B, nsamp * 2)
-    nsamp, dt, flops = best
+        t0 = time.perf_counter()
+        dp_linear.oracle_linear(lin.X, lin.G, None, lin.C, lin.sigma, lin.seed, lin.offset, "bf16")
+        dt += time.perf_counter() - t0
+        flops += 2.0 * lin.B * lin.T * lin.din * lin.dout
+        done.append(lin.name)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle (per-sample g_i materialised, clip, sum, Philox noise) on "
-                   f"{nsamp} of {B} samples of the '{lin.name}' linear "
-                   f"({lin.din}->{lin.dout}, T={lin.T}); {dt:.1f} s wall; host os.cpu_count()="
-                   f"{os.cpu_count()}"),
+                   f"{len(done)} of the step's {len(lins)} linears ({', '.join(done)}), all "
+                   f"{lins[0].B} samples each, T={lins[0].T}; {dt:.1f} s wall; host "
+                   f"os.cpu_count()={os.cpu_count()}"),
     }
 
 
@@ -617,7 +614,7 @@ def main():
         torch.cuda.empty_cache()
         res["configs"] = measure_configs(dp, torch, args.steps, 2)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(lins[0], args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline(lins, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
 
 
