@@ -29,7 +29,8 @@
  * ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> (T short relative to the layer), the
  * per-sample gradient tiles computed and dropped (a second contraction then
  * forms the clipped sum), or -- for unmasked bf16 calls of the single-layer
- * and group entry points -- those tiles computed once and staged in a device
+ * (dense, bias, projected) and group entry points -- those tiles computed
+ * once and staged in a device
  * workspace (fp32, B * dout * din values rounded up to 256 x 256 tiles, at
  * most 16 GiB per call) that the clipped sum then reads back.  The staged form trades the second contraction for one
  * pass over HBM; the choice is made per call from measured rates (see the

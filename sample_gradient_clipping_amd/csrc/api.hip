@@ -108,10 +108,10 @@ constexpr double kStagedMaxBytes = 16.0 * (1ull << 30);
 // or bytes per microsecond): the direct and staged norm kernels run the
 // token contraction at ~1.25 PFLOP/s, the accumulate kernel at ~1.15, the
 // Gram kernel at ~1.05 plus ~25 us of fills and fixup; the staged tiles
-// cost ~1/10 us per MB to store (beyond the contraction) and are read back
-// at ~5 TB/s.
+// cost ~1/20 us per MB to store (beyond the contraction: the persistent
+// kernel's stores overlap the next unit's fill) and are read back at ~5 TB/s.
 constexpr double kNormPerUs = 1.25e9, kAccPerUs = 1.15e9, kGramPerUs = 1.05e9;
-constexpr double kStorePerUs = 10.0e6, kCombinePerUs = 5.0e6;
+constexpr double kStorePerUs = 20.0e6, kCombinePerUs = 5.0e6;
 constexpr double kGramFixedUs = 25.0, kAccFixedUs = 15.0, kCombineFixedUs = 5.0;
 
 // allow_staged: the caller keeps the per-sample tiles from the norm phase to
@@ -708,15 +708,46 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
   double* sq = ws.at<double>(off_sq);
   float* c = ws.at<float>(off_c);
   float* gb = ws.at<float>(off_gb);
+  // On the staged path the weight's per-sample tiles are kept until the
+  // clip factors (which need the bias's norms too) exist.
+  LayerPlan L = plan_layer(X, G, mask, true);
+  const bool staged = L.path == dpf::NormPath::kStaged;
+  Workspace lws(s);
+  StagedLease lease;
+  hipError_t e = hipSuccess;
   // ||g_i||^2 of the weight, then + ||gb_i||^2 of the bias
-  if ((st = sqnorms_into(X, G, mask, sq, 0, s)) != DPF_OK) return st;
-  hipError_t e = dpf::launch_bias_grads(to_act(G), G->dtype, (int)B, (int)G->T, (int)dout, mask,
-                                        ws.at<float>(off_part), gb, sq, s);
+  if (staged) {
+    const LayerWs o = reserve_layer(L, lws, true, false, false);
+    if (!lws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+    if ((e = bind_layer(L, lws, o, s)) != hipSuccess) return hip_fail(e, "mask preparation launch");
+    if (!lease.acquire(s, o.staged))
+      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
+    L.args.skws = static_cast<float*>(lease.ptr());
+    L.args.partials = lws.at<double>(o.part);
+    if ((e = dpf::launch_norm(L.args, L.path, L.vec, s)) != hipSuccess)
+      return hip_fail(e, "norm kernel launch");
+    e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sq, 0, 1.0f, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  } else if ((st = sqnorms_into(X, G, mask, sq, 0, s)) != DPF_OK) {
+    return st;
+  }
+  e = dpf::launch_bias_grads(to_act(G), G->dtype, (int)B, (int)G->T, (int)dout, mask,
+                             ws.at<float>(off_part), gb, sq, s);
   if (e != hipSuccess) return hip_fail(e, "bias gradient launch");
   e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "clip factor launch");
-  if ((st = accumulate_with(X, G, mask, c, sigma * C, seed, offset, grad_out, s)) != DPF_OK)
+  if (staged) {
+    L.args.c = c;
+    L.args.noise_std = sigma * C;
+    L.args.seed = seed;
+    L.args.offset = offset;
+    L.args.out = grad_out;
+    if ((e = dpf::launch_staged_combine(L.args, s)) != hipSuccess)
+      return hip_fail(e, "accumulate launch");
+  } else if ((st = accumulate_with(X, G, mask, c, sigma * C, seed, offset, grad_out, s)) !=
+             DPF_OK) {
     return st;
+  }
   // the bias noise continues the weight's Philox stream
   const uint64_t boff = offset + (uint64_t)((dout * X->D + 3) / 4);
   e = dpf::launch_bias_accumulate(gb, c, (int)B, (int)dout, sigma * C, seed, boff, bias_grad_out,

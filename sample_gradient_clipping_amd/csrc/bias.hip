@@ -78,10 +78,23 @@ __global__ void __launch_bounds__(kCols) bias_accumulate_kernel(const float* gb,
   const int64_t e0 = 4 * j;
   if (e0 >= dout) return;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < B; ++b) {
-    const float cb = c[b];
-    for (int k = 0; k < 4; ++k)
-      if (e0 + k < dout) v[k] += cb * gb[(int64_t)b * dout + e0 + k];
+  const int nk = (int)min((int64_t)4, dout - e0);
+  // samples in order, eight at a time with their loads in flight together
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    float w[8][4], cb[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int b = min(b0 + q, B - 1);
+      cb[q] = c[b];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[q][k] = k < nk ? gb[(int64_t)b * dout + e0 + k] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (b0 + q < B) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] += cb[q] * w[q][k];
+      }
   }
   const float rB = 1.0f / (float)B;   // as the weight epilogue
   f32x4 z = {0.f, 0.f, 0.f, 0.f};

@@ -133,7 +133,8 @@ def test_gram_direct_and_staged_paths_agree():
 @pytest.mark.parametrize("shape,expect", [
     ((8, 2048, 5120, 5120), "staged_norm"),   # Llama-13B q: staging the tiles beats a second pass
     ((8, 512, 5120, 5120), "gram_norm"),      # short sequences: the Gram phase is cheap
-    ((32, 512, 768, 3072), "direct_norm"),    # GPT-2 MLP: direct, then a second contraction
+    ((32, 512, 768, 3072), "staged_norm"),    # GPT-2 MLP
+    ((32, 128, 256, 4096), "direct_norm"),    # RoBERTa fc1 in r-space: few flops per staged byte
 ])
 def test_automatic_norm_path_choice(shape, expect):
     torch = need_gpu()

@@ -300,6 +300,32 @@ def test_bias_matches_oracle(dtype, shape):
         assert rel_fro(ob.cpu().numpy(), rb) <= tol
 
 
+@pytest.mark.parametrize("path", [0, 1, 3])
+def test_bias_unmasked_matches_oracle(path):
+    """Unmasked bf16 over the large-tile kernels: the automatic choice (the
+    staged path at this shape), Gram, and staged forced."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(50)
+    lin = random_linear(rng, 4, 300, 520, 264)
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    _, _, rn, _ = dp_linear.oracle_linear_bias(lin.X, lin.G, None, 1.0, 0.0, 0, 0, "bf16")
+    C = float(np.median(rn))
+    dp.set_option("norm_path", path)
+    try:
+        for sigma, tol in ((0.0, SUM_TOL_BF16), (0.9, AGG_TOL_BF16)):
+            ow, ob, norms = dp.linear_clip_accumulate_bias(X, G, None, C=C, sigma=sigma, seed=4,
+                                                           offset=6)
+            rw, rb, rn, rc = dp_linear.oracle_linear_bias(lin.X, lin.G, None, C, sigma, 4, 6,
+                                                          "bf16")
+            assert (rc == 1).any() and (rc < 1).any()
+            assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
+            assert rel_fro(ow.cpu().numpy(), rw) <= tol
+            assert rel_fro(ob.cpu().numpy(), rb) <= tol
+    finally:
+        dp.set_option("norm_path", 0)
+
+
 def test_bias_is_the_weight_of_a_constant_input_on_gpu():
     """The bias call against the dense call on [X, 1] (sigma = 0)."""
     torch = need_gpu()
