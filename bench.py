@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "b59e91e357f67ca0628a1a98333bc015b7e5478db742d8152c7fe61ed3c71cab",
+    "sources_sha256": "c95af885aaa2b2324d46b80c3a9cfafcecd424d662822e7a602793f474f5e021",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1273151.28, "write_kib": 1416819.0}, "staged_combine": {"fetch_kib": 708059.29, "write_kib": 177202.89}},
-        "1": {"accumulate": {"fetch_kib": 1130881.3, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 417606.47, "write_kib": 152505.34}},
+        "0": {"staged_norm": {"fetch_kib": 1406607.86, "write_kib": 1416485.46}, "staged_combine": {"fetch_kib": 708059.31, "write_kib": 177186.68}},
+        "1": {"accumulate": {"fetch_kib": 1132039.78, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 419048.28, "write_kib": 152505.33}},
     },
 }
 
