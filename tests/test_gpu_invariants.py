@@ -271,3 +271,41 @@ def test_kernel_timing_records_launches():
         dp.timing_reset()
     assert t["accumulate"][1] == 3 and t["accumulate"][0] > 0
     assert t["gram_norm"][1] == 3 and t["finalize"][1] == 3
+
+
+CANARY = 0x7FC0DEAD   # a quiet-NaN bit pattern no kernel writes
+
+
+def _guarded(torch, n, guard=1024):
+    """A float32 view of n elements with `guard` canary words on each side
+    (16-byte aligned), and the whole buffer."""
+    buf = torch.full((n + 2 * guard,), CANARY, dtype=torch.int32, device="cuda")
+    return buf[guard:guard + n].view(torch.float32), buf, guard
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("shape", [(3, 300, 520, 776), (2, 45, 40, 24), (5, 70, 264, 136)])
+def test_outputs_stay_inside_their_buffers(path, masked, shape):
+    """Canary words around grad_out and norms_out survive every norm path,
+    ragged tiles and masked rows: no kernel writes outside its outputs."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout = shape
+    rng = np.random.default_rng(28)
+    lin = random_linear(rng, B, T, din, dout, lengths=[T] + [T // 3] * (B - 1) if masked else None)
+    X, G, m = _dev(lin, torch)
+    out, obuf, og = _guarded(torch, dout * din)
+    nrm, nbuf, ng = _guarded(torch, B)
+    dp.set_option("norm_path", path)
+    try:
+        dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.5, grad_out=out.view(dout, din),
+                                  norms_out=nrm)
+        dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.5, grad_out=out.view(dout, din),
+                                  norms_out=nrm, denom=7.0, accumulate=True)
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
+    for buf, g in ((obuf, og), (nbuf, ng)):
+        assert bool((buf[:g] == CANARY).all()) and bool((buf[-g:] == CANARY).all())
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(nrm).all())
