@@ -346,7 +346,8 @@ def norm_path_of(dp, call):
     finally:
         dp.set_option("timing", 0)
         dp.timing_reset()
-    for key, path in (("staged_norm", "staged"), ("gram_norm", "gram"), ("direct_norm", "direct")):
+    for key, path in (("staged_norm", "staged"), ("gram_norm", "gram"), ("direct_norm", "direct"),
+                      ("tiny_layer", "one workgroup")):
         if key in names:
             return path
     return "unknown"

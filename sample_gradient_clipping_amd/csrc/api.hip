@@ -412,6 +412,17 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
   LayerPlan L = plan_layer(X, G, mask, true);
   L.args.denom = denom;
   L.args.beta = beta;
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  // A tiny layer runs the whole step in one workgroup (unless a norm path is
+  // forced): one launch, no workspace.
+  if (g_norm_path.load() == 0 && dpf::tiny_eligible(L.args)) {
+    const hipError_t e = dpf::launch_tiny_layer(L.args, C, norms_out, s);
+    if (e != hipSuccess) return hip_fail(e, "tiny layer launch");
+    return ok();
+  }
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);

@@ -68,6 +68,16 @@ hipError_t launch_bias_accumulate(const float* gb, const float* c, int B, int do
                                   float noise_std, uint64_t seed, uint64_t offset, float* out,
                                   hipStream_t s);
 
+// The whole step in one workgroup for tiny layers (tiny.hip): eligible when
+// B <= kTinyMaxB, one thread per 2 x 4 block of outputs fits the workgroup,
+// every sample's X and G rows fit kTinyLdsBytes as float32, and the call is
+// at most kTinyMaxFlops.  Writes out and norms_out.
+constexpr int kTinyMaxB = 8;
+constexpr int kTinyLdsBytes = 64 * 1024;
+constexpr double kTinyMaxFlops = 4.0e6;
+bool tiny_eligible(const LayerArgs& p);
+hipError_t launch_tiny_layer(const LayerArgs& p, float C, float* norms_out, hipStream_t s);
+
 // One projected Adam step (optim.hip).
 struct AdamArgs {
   const float* grad;        // [dout, r] privatised projected gradient

@@ -15,7 +15,7 @@ def _dev(lin, torch):
     return to_dev(lin.X, lin.dtype, torch), to_dev(lin.G, lin.dtype, torch), mask_dev(lin.mask, torch)
 
 
-@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("path", [0, 1, 2, 3])
 def test_bitwise_determinism(path):
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
@@ -44,6 +44,31 @@ def test_masked_rows_never_read():
     G2[pad] = float("inf")
     got = dp.linear_clip_accumulate(X2, G2, m, C=0.05, sigma=0.5)
     assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+
+
+def test_tiny_layer_masked_rows_never_read_and_deterministic():
+    """The one-workgroup kernel: NaN/Inf in masked rows change no bit, and
+    repeated calls agree bit for bit."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(29)
+    lin = random_linear(rng, 3, 40, 48, 32, lengths=[40, 17, 3])
+    X, G, m = _dev(lin, torch)
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        ref = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.5)
+        assert "tiny_layer" in dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    X2, G2 = X.clone(), G.clone()
+    pad = (m == 0)
+    X2[pad] = float("nan")
+    G2[pad] = float("inf")
+    for _ in range(3):
+        got = dp.linear_clip_accumulate(X2, G2, m, C=0.05, sigma=0.5)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
 
 
 def test_active_nan_propagates():
@@ -135,6 +160,7 @@ def test_gram_direct_and_staged_paths_agree():
     ((8, 512, 5120, 5120), "gram_norm"),      # short sequences: the Gram phase is cheap
     ((32, 512, 768, 3072), "staged_norm"),    # GPT-2 MLP
     ((32, 128, 256, 4096), "direct_norm"),    # RoBERTa fc1 in r-space: few flops per staged byte
+    ((4, 16, 64, 32), "tiny_layer"),          # one workgroup does the whole step
 ])
 def test_automatic_norm_path_choice(shape, expect):
     torch = need_gpu()
@@ -283,7 +309,7 @@ def _guarded(torch, n, guard=1024):
     return buf[guard:guard + n].view(torch.float32), buf, guard
 
 
-@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("path", [0, 1, 2, 3])
 @pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("shape", [(3, 300, 520, 776), (2, 45, 40, 24), (5, 70, 264, 136)])
 def test_outputs_stay_inside_their_buffers(path, masked, shape):

@@ -121,6 +121,36 @@ def test_staged_multi_tile_ragged_edges(masked):
     _check(lin, 3, sigma=1.1, C=C)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(4, 16, 64, 32), (5, 33, 24, 40), (1, 1, 8, 8), (3, 30, 96, 64),
+                                   (8, 9, 37, 19)])
+def test_tiny_layer_kernel(dtype, shape):
+    """The one-workgroup kernel (taken automatically for these shapes): masks
+    with a fully masked sample, mixed clipping, noise, against the oracle."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    B, T, din, dout = shape
+    X = torch.zeros((B, T, din), device="cuda")
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        dp.linear_clip_accumulate(X, torch.zeros((B, T, dout), device="cuda"), None, C=1.0)
+        assert "tiny_layer" in dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    rng = np.random.default_rng(sum(shape))
+    lengths = [T] + [0] + [max(1, T // 2)] * (B - 2) if B > 2 else None
+    lin = random_linear(rng, B, T, din, dout, dtype=dtype, lengths=lengths)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn[rn > 0])) * 1.0001 if (rn > 0).sum() > 1 else float(rn.max()) * 0.5
+    tol = AGG_TOL_F32 if dtype == "f32" else SUM_TOL_BF16
+    _, norms, _, _ = _check(lin, 0, sigma=0.0, C=C, agg_tol=tol)
+    if lengths is not None:
+        assert norms[1] == 0.0
+    _check(lin, 0, sigma=0.7, C=C)
+
+
 def test_strided_views():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
@@ -142,7 +172,7 @@ def test_strided_views():
 # the five workload configurations
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("sigma", [0.0, 1.0])
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [0, 1, 2])   # 0: the automatic choice, the one-workgroup kernel
 def test_config_single_fp32_linear(sigma, path):
     lin = workloads.config_c1(sigma).linears[0]
     _check(lin, path, sigma=sigma)
