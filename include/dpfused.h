@@ -30,11 +30,14 @@
  * per-sample gradient tiles computed and dropped (a second contraction then
  * forms the clipped sum), or -- for unmasked bf16 calls of the single-layer
  * (dense, bias, projected) and group entry points -- those tiles computed
- * once and staged in a device
- * workspace (fp32, B * dout * din values rounded up to 256 x 256 tiles, at
- * most 16 GiB per call) that the clipped sum then reads back.  The staged form trades the second contraction for one
- * pass over HBM; the choice is made per call from measured rates (see the
+ * once and staged in a device workspace (fp32, B * dout * din values rounded
+ * up to 256 x 256 tiles, at most 16 GiB per call) that the clipped sum then
+ * reads back.  The staged form trades the second contraction for one pass
+ * over HBM; the choice is made per call from measured rates (see the
  * "norm_path" option).  Staged tiles live only for the duration of the call.
+ * Tiny dense calls (B <= 8, about 8192 outputs, every sample's rows within
+ * 64 KiB as float32, at most 4 MFLOP) run the whole step in one workgroup
+ * instead: one launch, the per-sample gradients never leave the chip.
  *
  * Conventions for every entry point
  *   - Every data pointer is DEVICE memory owned by the caller; the library
