@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "c95af885aaa2b2324d46b80c3a9cfafcecd424d662822e7a602793f474f5e021",
+    "sources_sha256": "8ddef15f3c87d629d6f16aa012c09ec01116f363cdf277f9803d7a1a050f2316",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1406607.86, "write_kib": 1416485.46}, "staged_combine": {"fetch_kib": 708059.31, "write_kib": 177186.68}},
-        "1": {"accumulate": {"fetch_kib": 1132039.78, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 419048.28, "write_kib": 152505.33}},
+        "0": {"staged_norm": {"fetch_kib": 1344513.1, "write_kib": 1416491.48}, "staged_combine": {"fetch_kib": 708059.32, "write_kib": 177166.29}},
+        "1": {"accumulate": {"fetch_kib": 1129749.09, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 419009.47, "write_kib": 152505.26}},
     },
 }
 
