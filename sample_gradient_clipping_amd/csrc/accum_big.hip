@@ -358,34 +358,77 @@ __device__ __forceinline__ void step_barrier() {
 //
 // SCALE: rescale the accumulator at sample boundaries so that it ends as
 // sum_i (c_i / c_last) g_i; c_last is returned.
-template <bool SCALE, bool MASK>
-__device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, int o0, Acc& acc,
-                                     unsigned char* lds) {
-  static_assert(kKT == kBitsTokens, "one row-bit word per step");
-  static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
-  static_assert(2 * kDmaPerOp == 4, "one DMA after every other one of eight MFMAs");
-  acc.zero();
-  if (n <= 0) return 1.0f;
-  const uint32_t base = lds_addr(lds);
+// Pipeline state of one run over an output tile: the lanes' DMA offsets,
+// the issue side, and the consumer side (the sample of the step being
+// consumed and, without a mask, the steps left before the next sample).
+template <bool MASK>
+struct Pipe {
   DmaLane dl;
-  dl.init(p, a0, o0);
-  Issue<MASK> is;                        // next step to queue
-  is.start(p, k0);
-  // Consumer side: the sample of the step being consumed, and (without a
-  // mask) the steps left before the next sample starts.
+  Issue<MASK> is;
   Cursor<MASK> cc;
-  cc.start(p, k0);
-  int left = cc.nsteps - cc.s;
+  int left, n;
+};
+
+// Queue the first min(kStages, n) steps of a run into the slot ring.
+template <bool MASK>
+__device__ __forceinline__ void prologue(const LayerArgs& p, int k0, int n, int a0, int o0,
+                                         Pipe<MASK>& ps, uint32_t base) {
+  ps.n = n;
+  if (n <= 0) return;
+  ps.dl.init(p, a0, o0);
+  ps.is.start(p, k0);
+  ps.cc.start(p, k0);
+  ps.left = ps.cc.nsteps - ps.cc.s;
 #pragma unroll
   for (int k = 0; k < kStages; ++k) {
     if (k < n) {
-      is.step(p, dl, base + k * kStageBytes);
-      if (k + 1 < n) is.advance(p);
+      ps.is.step(p, ps.dl, base + k * kStageBytes);
+      if (k + 1 < n) ps.is.advance(p);
     }
   }
+}
+
+// Wait until step 0 of a run has landed for this wave, `steps` of its DMA
+// steps having been queued after step 0.  after_stores: at least 32 vector
+// memory stores were issued after the whole prologue (the previous unit's
+// tile, in the staged kernel).  Loads complete in order among themselves, so
+// allowing for those stores (and no more than their minimum count) still
+// guarantees step 0; allowing for fewer would only wait longer.
+__device__ __forceinline__ void wait_first(int steps, bool after_stores) {
+  if (!after_stores) {
+    wait_dma(steps);
+  } else if (steps <= 0) {
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  } else if (steps == 1) {
+    asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+  } else if (steps == 2) {
+    asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
+  } else if (steps == 3) {
+    asm volatile("s_waitcnt vmcnt(44)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  }
+}
+
+// The run whose first steps `prologue` queued: the main loop below.
+template <bool SCALE, bool MASK>
+__device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, Acc& acc,
+                                            unsigned char* lds, bool after_stores) {
+  static_assert(kKT == kBitsTokens, "one row-bit word per step");
+  static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
+  static_assert(2 * kDmaPerOp == 4, "one DMA after every other one of eight MFMAs");
+  static_assert(kDmaPerStep * (kStages - 1) + 32 <= 63, "vmcnt field");
+  acc.zero();
+  const int n = ps.n;
+  if (n <= 0) return 1.0f;
+  const uint32_t base = lds_addr(lds);
+  const DmaLane& dl = ps.dl;
+  Issue<MASK>& is = ps.is;               // next step to queue
+  Cursor<MASK>& cc = ps.cc;
+  int left = ps.left;
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
   int cb = cc.b;
-  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
+  wait_first(min(kStages - 1, n - 1), after_stores);   // step 0 has landed for this wave
   step_barrier();
   Frags f0, f1;
 #pragma unroll
@@ -449,6 +492,15 @@ __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, 
     slot = next;
   }
   return c_last;
+}
+
+// One run over n steps from position k0 of the call's sequence.
+template <bool SCALE, bool MASK>
+__device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, int o0, Acc& acc,
+                                     unsigned char* lds) {
+  Pipe<MASK> ps;
+  prologue<MASK>(p, k0, n, a0, o0, ps, lds_addr(lds));
+  return run_queued<SCALE, MASK>(p, ps, acc, lds, false);
 }
 
 // Grouped raster order of the output tiles: tile index L -> (tm, tn), kGroupRows
@@ -699,28 +751,51 @@ constexpr int64_t kImgStride = kTileElems;   // floats from one unit's image to 
 // Persistent: G workgroups (one per compute unit) take units u = L, L + G,
 // ... (L the XCD-aware logical index), so the workgroups resident on one XCD
 // work on neighbouring tiles of one sample at a time and share its X and G
-// strips in that XCD's L2; a unit's tile stores then overlap the next unit's
-// pipeline fill.  Each wave writes its own fp64 partial (np = 8 per tile), so
-// no LDS is needed between units.
+// strips in that XCD's L2.  Once every wave is done with a unit's LDS slots,
+// the next unit's first steps are queued before this unit's tile is stored,
+// so the stores overlap the next unit's pipeline fill.  Each wave writes its
+// own fp64 partial (np = 8 per tile), so no LDS is needed between units.
 constexpr int kStagedParts = kWaves;
 
-__global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, int G) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+template <bool MASK>
+__device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned char* smem) {
   const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
   const int ntiles = ntm * ntn;
   const int N = ntiles * p.B;
   const int nsteps = (p.T + kKT - 1) / kKT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  Acc acc;
-  for (int u = logical_wg(blockIdx.x, G); u < N; u += G) {
+  const uint32_t base = lds_addr(smem);
+  // queue the first steps of unit u
+  auto queue = [&](int u, Pipe<MASK>& ps) {
     const int b = u / ntiles, L = u - b * ntiles;
     int tm, tn;
     raster(L, ntm, ntn, &tm, &tn);
-    if (p.steps != nullptr) {
-      const int k0 = (int)((c_u32*)p.steps)[1 + b], k1 = (int)((c_u32*)p.steps)[2 + b];
-      run<false, true>(p, k0, k1 - k0, tm * kTile, tn * kTile, acc, smem);
+    int k0, n;
+    if constexpr (MASK) {
+      k0 = (int)((c_u32*)p.steps)[1 + b];
+      n = (int)((c_u32*)p.steps)[2 + b] - k0;
     } else {
-      run<false, false>(p, b * nsteps, nsteps, tm * kTile, tn * kTile, acc, smem);
+      k0 = b * nsteps;
+      n = nsteps;
+    }
+    prologue<MASK>(p, k0, n, tm * kTile, tn * kTile, ps, base);
+  };
+  Acc acc;
+  Pipe<MASK> ps;
+  int u = logical_wg(blockIdx.x, G);
+  if (u < N) queue(u, ps);
+  bool after_stores = false;
+  for (; u < N; u += G) {
+    const int b = u / ntiles, L = u - b * ntiles;
+    run_queued<false, MASK>(p, ps, acc, smem, after_stores);
+    // Every wave's LDS reads of this unit have returned before any wave
+    // refills the ring; then the next unit's first steps go out.
+    lds_reads_done();
+    step_barrier();
+    after_stores = false;
+    if (u + G < N) {
+      queue(u + G, ps);
+      after_stores = ps.n > 0;
     }
     float* img = p.skws + (int64_t)u * kImgStride + ((int64_t)wave * kImgChunks * 64 + lane) * 4;
     float s = 0.f;
@@ -742,11 +817,13 @@ __global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, in
         }
     const double tot = wave_sum_f64((double)s);
     if (lane == 0) p.partials[((int64_t)b * ntiles + L) * kStagedParts + wave] = tot;
-    // Every wave's LDS reads of this unit have returned before any wave's
-    // next DMA refills the ring; the stores stay in flight.
-    lds_reads_done();
-    step_barrier();
   }
+}
+
+__global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, int G) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if (p.steps != nullptr) staged_units<true>(p, G, smem);
+  else staged_units<false>(p, G, smem);
 }
 
 // out = (sum_b c_b g_b + noise_std xi) / B from the staged tiles: one thread
