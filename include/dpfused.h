@@ -327,6 +327,18 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                pool, and the per-device buffer of staged per-sample tiles
  *                (freed after each call when larger).  Setting it trims both;
  *                trimming the staged buffer waits for its last user.
+ *   "workspace_limit_bytes"  a workspace request larger than this (one
+ *                call's pool allocation, or its staged tile buffer) fails
+ *                with DPF_ERR_OUT_OF_MEMORY before any output is written, as a
+ *                failed hipMallocAsync would; 0 (default) = no limit
+ *   "trace"      1 = push a roctx range named after the entry point around
+ *                every call, for rocprofv3 --marker-trace; 0 = off (default)
+ *   "debug"      1 = synchronise the launch stream after every kernel and
+ *                print the kernel's name and the HIP error to stderr if it
+ *                failed; slow, for finding a failing launch; 0 = off (default)
+ * Defaults are read from the environment when the library is loaded:
+ * DPFUSED_NORM_PATH ("auto", "gram", "direct", "staged" or 0-3),
+ * DPFUSED_TRACE and DPFUSED_DEBUG (0/1), DPFUSED_WS_LIMIT (bytes).
  * Read-only (dpfused_get_option): "workspace_reserved_bytes" and
  * "workspace_reserved_high", what the current device's pool holds now and at
  * most (-1 without a pool).

@@ -20,6 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdpfused.so")
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 # Packed-fp32 instructions are disabled for every HIP translation unit; the
 # host pass warns that it does not know the feature, which is harmless.
@@ -31,7 +32,7 @@ HIP_FLAGS = [
 
 
 def _hipcc() -> str:
-    h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    h = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     if not os.path.exists(h):
         raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libdpfused")
     return h
@@ -61,7 +62,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
+           "-L", os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     if verbose:
         print(" ".join(cmd), flush=True)
     _run(cmd)

@@ -12,11 +12,15 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "dpfused.h"
 #include "kernels.hpp"
@@ -26,6 +30,45 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<int> g_norm_path{0};   // 0 auto, 1 gram, 2 direct, 3 staged
 std::atomic<int> g_timing{0};
+std::atomic<int> g_trace{0};        // roctx range around every entry point
+std::atomic<int> g_debug{0};        // synchronise after every launch, report errors
+std::atomic<int64_t> g_ws_limit{0};   // workspace requests above this fail (0: no limit)
+
+// Defaults from the environment, read once when the library is loaded:
+// DPFUSED_NORM_PATH (auto, gram, direct, staged or 0-3), DPFUSED_TRACE,
+// DPFUSED_DEBUG (0/1), DPFUSED_WS_LIMIT (bytes).
+bool read_env() {
+  if (const char* v = std::getenv("DPFUSED_NORM_PATH")) {
+    const std::string t(v);
+    const int path = t == "gram" ? 1 : t == "direct" ? 2 : t == "staged" ? 3
+                   : (t.size() == 1 && t[0] >= '0' && t[0] <= '3') ? t[0] - '0' : 0;
+    g_norm_path.store(path);
+  }
+  if (const char* v = std::getenv("DPFUSED_TRACE")) g_trace.store(std::atoi(v) != 0);
+  if (const char* v = std::getenv("DPFUSED_DEBUG")) g_debug.store(std::atoi(v) != 0);
+  if (const char* v = std::getenv("DPFUSED_WS_LIMIT")) {
+    const long long n = std::atoll(v);
+    g_ws_limit.store(n > 0 ? (int64_t)n : 0);
+  }
+  return true;
+}
+const bool g_env_read = read_env();
+
+bool over_limit(size_t bytes) {
+  const int64_t lim = g_ws_limit.load();
+  return lim > 0 && (int64_t)bytes > lim;
+}
+
+// A roctx range named after the entry point, when the trace option is on.
+struct TraceRange {
+  bool on;
+  explicit TraceRange(const char* name) : on(g_trace.load() != 0) {
+    if (on) roctxRangePushA(name);
+  }
+  ~TraceRange() {
+    if (on) roctxRangePop();
+  }
+};
 
 dpf_status fail(dpf_status s, const std::string& msg) {
   g_last_error = msg;
@@ -222,6 +265,7 @@ class StagedLease {
   bool acquire(hipStream_t s, size_t bytes) {
     const int dev = stream_device(s);
     if (dev < 0 || dev >= kMaxDevices) return false;
+    if (over_limit(bytes)) return false;
     buf_ = &g_staged[dev];
     lk_ = std::unique_lock<std::mutex>(buf_->mu);
     s_ = s;
@@ -307,6 +351,7 @@ struct Workspace {
   }
   bool allocate() {
     if (size == 0) return true;
+    if (over_limit(size)) return false;
     hipMemPool_t pool = workspace_pool(s);
     const hipError_t e = pool != nullptr ? hipMallocFromPoolAsync(&base, size, pool, s)
                                          : hipMallocAsync(&base, size, s);
@@ -576,6 +621,12 @@ void timing_begin(const char* name, hipStream_t s) {
   g_pending.push_back(p);
 }
 void timing_end(const char* name, hipStream_t s) {
+  if (g_debug.load()) {
+    // debugging: wait for the kernel and report a failure by its name
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) std::fprintf(stderr, "dpfused: kernel %s failed: %s\n", name, hipGetErrorString(e));
+  }
   if (!g_timing.load()) return;
   std::lock_guard<std::mutex> lk(g_tmu);
   for (auto it = g_pending.rbegin(); it != g_pending.rend(); ++it) {
@@ -595,6 +646,7 @@ extern "C" {
 dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                           float C, float sigma, uint64_t seed, uint64_t offset,
                                           float* grad_out, float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_linear_clip_accumulate");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -611,6 +663,7 @@ dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
                                              uint64_t seed, uint64_t offset, float denom,
                                              int32_t accumulate, float* grad_out,
                                              float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_linear_clip_accumulate_ex");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -631,6 +684,7 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
                                                     float C, float sigma, uint64_t seed,
                                                     uint64_t offset, float* grad_out,
                                                     float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_linear_clip_accumulate_projected");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -648,6 +702,7 @@ dpf_status dpfused_linear_clip_accumulate_projected_seeded(
     const dpf_act* X, const dpf_act* G, const uint8_t* mask, int64_t r, uint64_t p_seed,
     uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
     float* grad_out, float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_linear_clip_accumulate_projected_seeded");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -663,6 +718,7 @@ dpf_status dpfused_linear_clip_accumulate_projected_seeded(
 
 dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                       double* sqnorms_out, int32_t accumulate, void* stream) {
+  TraceRange trace_("dpfused_per_sample_sqnorms");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if (sqnorms_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms_out is NULL");
@@ -671,6 +727,7 @@ dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const 
 
 dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float* c_out,
                                 float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_clip_factors");
   if (sqnorms == nullptr || c_out == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms and c_out must not be NULL");
   if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
@@ -684,6 +741,7 @@ dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float
 dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                      const float* c, float noise_std, uint64_t seed,
                                      uint64_t offset, float* grad_out, void* stream) {
+  TraceRange trace_("dpfused_scaled_accumulate");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if (c == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "c is NULL");
@@ -700,6 +758,7 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
                                                uint64_t seed, uint64_t offset, float* grad_out,
                                                float* bias_grad_out, float* norms_out,
                                                void* stream) {
+  TraceRange trace_("dpfused_linear_clip_accumulate_bias");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -771,6 +830,7 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
                                          const uint8_t* mask, float C, float sigma, uint64_t seed,
                                          const uint64_t* offsets, float* const* grad_out,
                                          float* norms_out, void* stream) {
+  TraceRange trace_("dpfused_group_clip_accumulate");
   if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
   if (X == nullptr || G == nullptr || offsets == nullptr || grad_out == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "X, G, offsets and grad_out must not be NULL");
@@ -867,6 +927,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
                                        float lr, float beta1, float beta2, float eps,
                                        const void* P, int32_t p_dtype, uint64_t p_seed,
                                        uint64_t p_offset, float p_scale, void* stream) {
+  TraceRange trace_("dpfused_projected_adam_step");
   if (grad == nullptr || m == nullptr || v == nullptr || W == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "grad, m, v and W must not be NULL");
   if (dout < 1 || din < 1 || r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "dout, din, r must be >= 1");
@@ -918,6 +979,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
 
 dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
                                  void* stream) {
+  TraceRange trace_("dpfused_philox4x32_10");
   if (nblocks < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "nblocks must be >= 0");
   if (nblocks == 0) return ok();
   if (out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -929,6 +991,7 @@ dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks
 
 dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale,
                                  int32_t dtype, void* out, void* stream) {
+  TraceRange trace_("dpfused_gaussian_fill");
   if (n < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 0");
   if (dtype != DPF_F32 && dtype != DPF_BF16) return fail(DPF_ERR_UNSUPPORTED, "unknown dtype");
   if (!std::isfinite(scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -958,6 +1021,16 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
     set_keep_bytes(value);
     return ok();
   }
+  if (std::strcmp(name, "workspace_limit_bytes") == 0) {
+    if (value < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "workspace_limit_bytes must be >= 0");
+    g_ws_limit.store(value);
+    return ok();
+  }
+  if (std::strcmp(name, "trace") == 0 || std::strcmp(name, "debug") == 0) {
+    if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "trace and debug must be 0 or 1");
+    (name[0] == 't' ? g_trace : g_debug).store((int)value);
+    return ok();
+  }
   if (std::strcmp(name, "timing") == 0) {
     if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "timing must be 0 or 1");
     g_timing.store((int)value);
@@ -971,6 +1044,9 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "norm_path") == 0) return g_norm_path.load();
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
   if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
+  if (std::strcmp(name, "workspace_limit_bytes") == 0) return g_ws_limit.load();
+  if (std::strcmp(name, "trace") == 0) return g_trace.load();
+  if (std::strcmp(name, "debug") == 0) return g_debug.load();
   // Read-only: memory the current device's workspace pool holds now, and the
   // most it has held (-1 when there is no pool).
   const bool now = std::strcmp(name, "workspace_reserved_bytes") == 0;

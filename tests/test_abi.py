@@ -76,6 +76,38 @@ def test_options(L):
     assert b"bogus" in L.dpfused_last_error()
     assert L.dpfused_get_option(b"bogus") == -1
     assert L.dpfused_set_option(b"timing", 0) == DPF_OK
+    for name in (b"trace", b"debug"):
+        assert L.dpfused_set_option(name, 1) == DPF_OK
+        assert L.dpfused_get_option(name) == 1
+        assert L.dpfused_set_option(name, 0) == DPF_OK
+        assert L.dpfused_get_option(name) == 0
+        assert L.dpfused_set_option(name, 2) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_get_option(b"workspace_limit_bytes") == 0
+    assert L.dpfused_set_option(b"workspace_limit_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"workspace_limit_bytes", 4096) == DPF_OK
+    assert L.dpfused_get_option(b"workspace_limit_bytes") == 4096
+    assert L.dpfused_set_option(b"workspace_limit_bytes", 0) == DPF_OK
+
+
+@pytest.mark.parametrize("env,want", [
+    ({"DPFUSED_NORM_PATH": "staged"}, {"norm_path": 3}),
+    ({"DPFUSED_NORM_PATH": "gram", "DPFUSED_TRACE": "1"}, {"norm_path": 1, "trace": 1}),
+    ({"DPFUSED_NORM_PATH": "2", "DPFUSED_DEBUG": "1"}, {"norm_path": 2, "debug": 1}),
+    ({"DPFUSED_NORM_PATH": "bogus", "DPFUSED_WS_LIMIT": "123456"},
+     {"norm_path": 0, "workspace_limit_bytes": 123456, "trace": 0, "debug": 0}),
+])
+def test_options_from_environment(env, want):
+    # read once when the library is loaded, so each case loads it in a fresh process
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; L = ctypes.CDLL(sys.argv[1]); "
+            "L.dpfused_get_option.restype = ctypes.c_int64; "
+            "print(' '.join(str(L.dpfused_get_option(n.encode())) for n in sys.argv[2:]))")
+    names = list(want)
+    out = subprocess.run([sys.executable, "-c", code, _lib.LIB_PATH, *names],
+                         env={**os.environ, **env}, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert [int(v) for v in out.stdout.split()] == [want[n] for n in names]
 
 
 def _act(B=2, T=3, D=8, dtype=DPF_BF16, data=FAKE, reserved=0, sb=None, st=None):

@@ -15,16 +15,19 @@ def _dev(lin, torch):
     return to_dev(lin.X, lin.dtype, torch), to_dev(lin.G, lin.dtype, torch), mask_dev(lin.mask, torch)
 
 
+@pytest.mark.parametrize("masked", [True, False])
 @pytest.mark.parametrize("path", [0, 1, 2, 3])
-def test_bitwise_determinism(path):
+def test_bitwise_determinism(path, masked):
+    """Ten repeats agree bit for bit: no reduction depends on timing (masked
+    calls never take the staged path, so path 3 runs direct there)."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
     rng = np.random.default_rng(20)
-    lin = random_linear(rng, 5, 333, 200, 264, masked=True)
+    lin = random_linear(rng, 5, 333, 200, 264, masked=masked)
     X, G, m = _dev(lin, torch)
     dp.set_option("norm_path", path)
     try:
-        outs = [dp.linear_clip_accumulate(X, G, m, C=0.1, sigma=0.7, seed=3, offset=11) for _ in range(4)]
+        outs = [dp.linear_clip_accumulate(X, G, m, C=0.1, sigma=0.7, seed=3, offset=11) for _ in range(10)]
     finally:
         dp.set_option("norm_path", 0)
     for o, n in outs[1:]:
