@@ -278,7 +278,7 @@ def measure_configs(dp, torch, steps, warmup):
                                                        norms_out=nrm)
     ms = time_calls(torch, seeded_layer, steps, warmup)
     out["c5_roberta_large_projected_seeded_r256_6_linears"] = {
-        "note": "as above, P regenerated from Philox seed 7 inside the projection kernel",
+        "note": "as above, P drawn from Philox seed 7 in each call (once into workspace), never kept",
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
         "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}

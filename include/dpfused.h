@@ -172,9 +172,12 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
  *
  * rounded to X's dtype, xi from Philox4x32-10 (p_seed, p_offset) as above --
  * i.e. with the P that dpfused_gaussian_fill(p_seed, p_offset, din*r,
- * p_scale, X's dtype) writes -- but P never exists in memory: the projection
- * kernel draws each element where it needs it.  p_scale = 1/sqrt(r) gives
- * the N(0, 1/r) entries of the method.
+ * p_scale, X's dtype) writes -- but P is not kept: with one tile of tokens
+ * (B*T <= 128) the projection kernel draws each element where it needs it;
+ * with more, P is drawn once into the call's workspace (din*r elements,
+ * released with it) and read from there, which is cheaper than drawing it
+ * again in every token tile.  p_scale = 1/sqrt(r) gives the N(0, 1/r)
+ * entries of the method.
  *
  *   r         projection rank, a positive multiple of 8
  *   p_scale   finite
@@ -287,7 +290,9 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
  *              aligned -- or NULL: then P[d][j] = p_scale * xi_{d*r+j} from
  *              Philox (p_seed, p_offset) rounded to p_dtype, the P of
  *              dpfused_linear_clip_accumulate_projected_seeded, drawn again
- *              inside the kernel
+ *              inside the kernel, or once into workspace (din*r elements of
+ *              p_dtype, for this call only) when W has more than one row of
+ *              the kernel's tiles
  *
  * All pointers 16-byte aligned.  Errors as above; nothing is written on
  * error.  m, v and W must not overlap each other or grad. */
@@ -323,10 +328,14 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
  *   "workspace_keep_bytes"  bytes the library keeps reserved for later calls
- *                (default 16 GiB): freed workspace in its per-device memory
- *                pool, and the per-device buffer of staged per-sample tiles
- *                (freed after each call when larger).  Setting it trims both;
- *                trimming the staged buffer waits for its last user.
+ *                (default 16 GiB), each of: workspace blocks freed by calls
+ *                and kept for reuse (a later call's stream waits on the GPU
+ *                for the block's last use, so blocks move between streams
+ *                safely), freed memory in the per-device pool behind them,
+ *                and the per-device buffer of staged per-sample tiles (freed
+ *                after each call when larger).  Setting it trims all three;
+ *                trimming kept blocks and the staged buffer waits for their
+ *                last users.
  *   "workspace_limit_bytes"  a workspace request larger than this (one
  *                call's pool allocation, or its staged tile buffer) fails
  *                with DPF_ERR_OUT_OF_MEMORY before any output is written, as a

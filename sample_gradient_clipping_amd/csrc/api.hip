@@ -3,9 +3,9 @@
 // Every entry point validates all of its arguments before queueing anything:
 // a failed check launches nothing and writes nothing.  Workspace (per-sample
 // norm partials, clip factors, mask row-activity bits, the projected
-// activations, staged per-sample gradient tiles) is allocated in stream order
-// from a per-device memory pool and released with hipFreeAsync on the call's
-// stream, so calls on different streams do not share state.
+// activations) comes from a per-device cache of blocks, each ordered after
+// its previous use by an event, backed by a per-device memory pool; the
+// staged per-sample gradient tiles have a per-device buffer of their own.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -313,8 +313,44 @@ class StagedLease {
   bool held_ = false;
 };
 
+// Freed workspace blocks are kept for later calls: a pool allocation and its
+// free cost more host time than a small call's kernel launches.  A kept block
+// carries an event recorded on the stream of its last use; the next user's
+// stream waits for that event on the GPU, so a block may move between streams.
+// Each device keeps at most g_keep_bytes of blocks (oldest freed first).
+struct CachedBlock {
+  void* ptr;
+  size_t size;
+  hipEvent_t ev;
+};
+struct BlockCache {
+  std::mutex mu;
+  std::vector<CachedBlock> blocks;   // oldest first
+  size_t bytes = 0;
+  std::vector<hipEvent_t> spare;     // events of blocks given back to the pool
+};
+BlockCache g_cache[kMaxDevices];
+
+// Frees cached blocks until at most `keep` bytes remain, on stream `s` after
+// each block's last use (s == nullptr: wait for it on the host first).
+void trim_cache(BlockCache& c, size_t keep, hipStream_t s) {
+  while (c.bytes > keep && !c.blocks.empty()) {
+    CachedBlock b = c.blocks.front();
+    c.blocks.erase(c.blocks.begin());
+    c.bytes -= b.size;
+    if (s != nullptr) (void)hipStreamWaitEvent(s, b.ev, 0);
+    else (void)hipEventSynchronize(b.ev);
+    (void)hipFreeAsync(b.ptr, s);
+    c.spare.push_back(b.ev);
+  }
+}
+
 void set_keep_bytes(int64_t keep) {
   g_keep_bytes.store(keep);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    std::lock_guard<std::mutex> lk(g_cache[d].mu);
+    trim_cache(g_cache[d], (size_t)keep, nullptr);
+  }
   {
     std::lock_guard<std::mutex> lk(g_pool_mu);
     for (int d = 0; d < kMaxDevices; ++d) {
@@ -335,14 +371,38 @@ void set_keep_bytes(int64_t keep) {
   }
 }
 
-// Stream-ordered workspace carved into 256-byte aligned pieces.
+// Stream-ordered workspace carved into 256-byte aligned pieces: a kept block
+// of at least the size (and at most about twice it), else a new one from the
+// pool.  Given back to the cache when the call's launches are queued.
 struct Workspace {
   hipStream_t s;
   void* base = nullptr;
-  size_t used = 0, size = 0;
+  size_t size = 0, cap = 0;
+  hipEvent_t ev = nullptr;
+  int dev = -1;
   explicit Workspace(hipStream_t st) : s(st) {}
   ~Workspace() {
-    if (base) (void)hipFreeAsync(base, s);
+    if (base == nullptr) return;
+    if (dev < 0 || dev >= kMaxDevices) {
+      (void)hipFreeAsync(base, s);
+      return;
+    }
+    BlockCache& c = g_cache[dev];
+    std::lock_guard<std::mutex> lk(c.mu);
+    if (ev == nullptr && !c.spare.empty()) {
+      ev = c.spare.back();
+      c.spare.pop_back();
+    }
+    if (ev == nullptr && hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
+    if (ev == nullptr || hipEventRecord(ev, s) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFreeAsync(base, s);
+      if (ev != nullptr) c.spare.push_back(ev);
+      return;
+    }
+    c.blocks.push_back(CachedBlock{base, cap, ev});
+    c.bytes += cap;
+    trim_cache(c, (size_t)g_keep_bytes.load(), s);
   }
   size_t reserve(size_t bytes) {
     const size_t at = (size + 255) & ~(size_t)255;
@@ -352,10 +412,42 @@ struct Workspace {
   bool allocate() {
     if (size == 0) return true;
     if (over_limit(size)) return false;
+    dev = stream_device(s);
+    if (dev >= 0 && dev < kMaxDevices) {
+      BlockCache& c = g_cache[dev];
+      std::lock_guard<std::mutex> lk(c.mu);
+      int best = -1;
+      for (int i = 0; i < (int)c.blocks.size(); ++i) {
+        const size_t b = c.blocks[(size_t)i].size;
+        if (b >= size && b <= 2 * size + ((size_t)1 << 20) &&
+            (best < 0 || b < c.blocks[(size_t)best].size))
+          best = i;
+      }
+      if (best >= 0) {
+        const CachedBlock b = c.blocks[(size_t)best];
+        c.blocks.erase(c.blocks.begin() + best);
+        c.bytes -= b.size;
+        if (hipStreamWaitEvent(s, b.ev, 0) == hipSuccess) {
+          base = b.ptr;
+          cap = b.size;
+          ev = b.ev;
+          return true;
+        }
+        (void)hipGetLastError();   // cannot order after its last use: give it back
+        (void)hipEventSynchronize(b.ev);
+        (void)hipFreeAsync(b.ptr, s);
+        c.spare.push_back(b.ev);
+      }
+    }
     hipMemPool_t pool = workspace_pool(s);
     const hipError_t e = pool != nullptr ? hipMallocFromPoolAsync(&base, size, pool, s)
                                          : hipMallocAsync(&base, size, s);
-    return e == hipSuccess && base != nullptr;
+    if (e != hipSuccess || base == nullptr) {
+      base = nullptr;
+      return false;
+    }
+    cap = size;
+    return true;
   }
   template <class T>
   T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
@@ -946,14 +1038,10 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
       (P != nullptr && !aligned16(P)))
     return fail(DPF_ERR_UNSUPPORTED, "grad, m, v, W and P must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Workspace ws(s);
-  const size_t off_u = ws.reserve((size_t)dout * r * sizeof(float));
-  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   dpf::AdamArgs a{};
   a.grad = grad;
   a.m = m;
   a.v = v;
-  a.u = ws.at<float>(off_u);
   a.W = W;
   a.dout = dout;
   a.din = din;
@@ -972,6 +1060,13 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
   a.p_seed = p_seed;
   a.p_offset = p_offset;
   a.p_scale = p_scale;
+  Workspace ws(s);
+  const size_t off_u = ws.reserve((size_t)dout * r * sizeof(float));
+  const bool pbuf = dpf::adam_draws_p_once(a);
+  const size_t off_p = pbuf ? ws.reserve((size_t)din * r * elem_size(p_dtype)) : 0;
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  a.u = ws.at<float>(off_u);
+  a.pbuf = pbuf ? ws.at<void>(off_p) : nullptr;
   hipError_t e = dpf::launch_projected_adam(a, s);
   if (e != hipSuccess) return hip_fail(e, "projected Adam launch");
   return ok();

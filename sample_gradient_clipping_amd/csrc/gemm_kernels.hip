@@ -706,12 +706,38 @@ int project_splits(const ProjArgs& p) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, 8, nk / 4}));
 }
 
+// A projection drawn from its seed regenerates its slice of P in every token
+// tile.  With more than one token tile it is cheaper to draw P once into the
+// call's workspace (din*r elements, after the split partials) with the
+// gaussian fill, whose values are the ones the kernel would draw, and read
+// it like a stored P.  P still lives only for the call.
+static bool project_draws_p_once(const ProjArgs& p) {
+  const int64_t ntok = (int64_t)p.B * p.T;
+  return p.gen != 0 && (ntok + kTileN - 1) / kTileN > 1;
+}
+
+static size_t project_split_bytes(const ProjArgs& p, int sp) {
+  const size_t b = sp == 1 ? 0 : (size_t)sp * p.B * p.T * p.r * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
 size_t project_workspace_bytes(const ProjArgs& p) {
   const int sp = project_splits(p);
-  return sp == 1 ? 0 : (size_t)sp * p.B * p.T * p.r * sizeof(float);
+  if (!project_draws_p_once(p)) return project_split_bytes(p, sp);
+  return project_split_bytes(p, sp) + (size_t)p.din * p.r * (p.dtype == kBF16 ? 2 : 4);
 }
 
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s) {
+  if (project_draws_p_once(p)) {
+    if (p.part == nullptr) return hipErrorInvalidValue;
+    ProjArgs q = p;
+    q.P = reinterpret_cast<char*>(p.part) + project_split_bytes(p, p.splits);
+    q.gen = 0;
+    hipError_t e = launch_gaussian_fill(p.p_seed, p.p_offset, (int64_t)p.din * p.r, p.p_scale,
+                                        p.dtype, const_cast<void*>(q.P), s);
+    if (e != hipSuccess) return e;
+    return launch_project(q, vec, s);
+  }
   if (p.gen) {
     if (p.dtype == kBF16)
       return vec ? launch_project_t<BF16, true, true>(p, s) : launch_project_t<BF16, false, true>(p, s);

@@ -92,7 +92,11 @@ struct AdamArgs {
   int gen;                  // P[d][j] = p_scale * xi_{d*r+j}(p_seed, p_offset), rounded to p_dtype
   uint64_t p_seed, p_offset;
   float p_scale;
+  void* pbuf;               // [din, r] of p_dtype, workspace when adam_draws_p_once(a)
 };
+// True when a seeded P is drawn once into a.pbuf (gaussian fill) and read
+// from there, rather than drawn again by every row of W tiles.
+bool adam_draws_p_once(const AdamArgs& a);
 hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s);
 
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the

@@ -10,9 +10,12 @@
 //
 //  adam_moments_kernel : the elementwise part, 4 elements per thread
 //  adam_update_kernel  : W -= lr * U P^T, fp32 MFMA (v_mfma_f32_32x32x2f32)
-//                        on 128 x 128 tiles of W; P is read (bf16 or fp32) or
-//                        drawn again from its seed exactly as gaussian_fill
-//                        writes it, then widened to fp32.
+//                        on 128 x 128 tiles of W, or 64 x 64 when the larger
+//                        tiles would leave compute units idle; P is read
+//                        (bf16 or fp32) or drawn again from its seed exactly
+//                        as gaussian_fill writes it, then widened to fp32.
+//                        With more than one row of W tiles a seeded P is drawn
+//                        once into workspace by the gaussian fill instead.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -20,11 +23,11 @@ namespace dpf {
 namespace optim {
 
 constexpr int kNT = 256;                 // 4 waves, 2 x 2
-constexpr int kTile = 128;               // W tile: 128 (din) x 128 (dout)
 constexpr int kKT = 32;                  // r per LDS step
 constexpr int kLD = kKT + 4;             // LDS row (floats), padded against bank conflicts
-constexpr int kTileFloats = kTile * kLD;
-constexpr int kLdsBytes = 2 * 2 * kTileFloats * (int)sizeof(float);   // P and U, double-buffered
+// W tile: TILE (din) x TILE (dout); P and U slices double-buffered in LDS
+template <int TILE>
+constexpr int lds_bytes() { return 2 * 2 * TILE * kLD * (int)sizeof(float); }
 
 __global__ void __launch_bounds__(256) adam_moments_kernel(AdamArgs a) {
   const int64_t n = a.dout * a.r;
@@ -72,19 +75,23 @@ __device__ __forceinline__ f32x4 u_chunk(const AdamArgs& a, int64_t o, int j) {
 
 // One W tile.  MFMA "A" = P rows (din), "B" = U rows (dout), both with r
 // contiguous ("K-inner"), so D[d][o] gives each lane 4 consecutive din
-// columns of one W row: a 16-byte read-modify-write.
+// columns of one W row: a 16-byte read-modify-write.  Each wave owns NB x NB
+// blocks of 32 x 32.
+template <int TILE>
 __global__ void __launch_bounds__(kNT) adam_update_kernel(AdamArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int ntd = (int)((a.din + kTile - 1) / kTile);
-  const int64_t d0 = (int64_t)(blockIdx.x % ntd) * kTile, o0 = (int64_t)(blockIdx.x / ntd) * kTile;
+  constexpr int NB = TILE / 64;
+  constexpr int kTileFloats = TILE * kLD;
+  const int ntd = (int)((a.din + TILE - 1) / TILE);
+  const int64_t d0 = (int64_t)(blockIdx.x % ntd) * TILE, o0 = (int64_t)(blockIdx.x / ntd) * TILE;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  constexpr int kChunks = kTile * (kKT / 4) / kNT;   // 4 chunks of each operand per thread
-  f32x16 acc[2][2];
+  constexpr int kChunks = TILE * (kKT / 4) / kNT;   // chunks of each operand per thread
+  f32x16 acc[NB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   f32x4 pr[kChunks], ur[kChunks];
@@ -117,29 +124,29 @@ __global__ void __launch_bounds__(kNT) adam_update_kernel(AdamArgs a) {
     const float* Us = Ps + kTileFloats;
 #pragma unroll
     for (int ks = 0; ks < kKT / 2; ++ks) {
-      float fa[2], fb[2];
+      float fa[NB], fb[NB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = frag_kinner<F32, kLD>(Ps, (wm * 2 + i) * 32, ks);
+      for (int i = 0; i < NB; ++i) fa[i] = frag_kinner<F32, kLD>(Ps, (wm * NB + i) * 32, ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = frag_kinner<F32, kLD>(Us, (wn * 2 + j) * 32, ks);
+      for (int j = 0; j < NB; ++j) fb[j] = frag_kinner<F32, kLD>(Us, (wn * NB + j) * 32, ks);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma<F32>(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma<F32>(fa[i], fb[j], acc[i][j]);
     }
     if (!more) break;
     stash(lds + ((kk + 1) & 1) * 2 * kTileFloats);
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t o = o0 + (wn * 2 + j) * 32 + acc_col(lane);
+    for (int j = 0; j < NB; ++j) {
+      const int64_t o = o0 + (wn * NB + j) * 32 + acc_col(lane);
       if (o >= a.dout) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t d = d0 + (wm * 2 + i) * 32 + acc_row(4 * g, lane);
+        const int64_t d = d0 + (wm * NB + i) * 32 + acc_row(4 * g, lane);
         if (d >= a.din) continue;   // din % 4 == 0: d .. d+3 all in range
         f32x4* w = (f32x4*)(a.W + o * a.din + d);
         f32x4 x = *w;
@@ -154,26 +161,51 @@ __global__ void __launch_bounds__(kNT) adam_update_kernel(AdamArgs a) {
 
 }  // namespace optim
 
-hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s) {
-  static hipError_t once = hipFuncSetAttribute((const void*)optim::adam_update_kernel,
+namespace {
+template <int TILE>
+hipError_t launch_update(const AdamArgs& a, hipStream_t s) {
+  static hipError_t once = hipFuncSetAttribute((const void*)optim::adam_update_kernel<TILE>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               optim::kLdsBytes);
+                                               optim::lds_bytes<TILE>());
   if (once != hipSuccess) return once;
+  const int64_t tiles = ((a.din + TILE - 1) / TILE) * ((a.dout + TILE - 1) / TILE);
+  timing_begin("adam_update", s);
+  hipLaunchKernelGGL(optim::adam_update_kernel<TILE>, dim3((unsigned)tiles), dim3(optim::kNT),
+                     optim::lds_bytes<TILE>(), s, a);
+  const hipError_t e = hipGetLastError();
+  timing_end("adam_update", s);
+  return e;
+}
+
+// 128 x 128 W tiles unless that leaves fewer workgroups than compute units.
+bool small_tiles(const AdamArgs& a) {
+  return ((a.din + 127) / 128) * ((a.dout + 127) / 128) < device_cus();
+}
+}  // namespace
+
+bool adam_draws_p_once(const AdamArgs& a) {
+  const int tile = small_tiles(a) ? 64 : 128;
+  return a.gen != 0 && a.dout > tile;
+}
+
+hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s) {
+  AdamArgs q = a;
+  if (adam_draws_p_once(a)) {
+    if (a.pbuf == nullptr) return hipErrorInvalidValue;
+    hipError_t e = launch_gaussian_fill(a.p_seed, a.p_offset, a.din * a.r, a.p_scale, a.p_dtype,
+                                        a.pbuf, s);
+    if (e != hipSuccess) return e;
+    q.P = a.pbuf;
+    q.gen = 0;
+  }
   const int64_t n = a.dout * a.r;
   timing_begin("adam_moments", s);
   hipLaunchKernelGGL(optim::adam_moments_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256),
-                     0, s, a);
+                     0, s, q);
   hipError_t e = hipGetLastError();
   timing_end("adam_moments", s);
   if (e != hipSuccess) return e;
-  const int64_t tiles = ((a.din + optim::kTile - 1) / optim::kTile) *
-                        ((a.dout + optim::kTile - 1) / optim::kTile);
-  timing_begin("adam_update", s);
-  hipLaunchKernelGGL(optim::adam_update_kernel, dim3((unsigned)tiles), dim3(optim::kNT),
-                     optim::kLdsBytes, s, a);
-  e = hipGetLastError();
-  timing_end("adam_update", s);
-  return e;
+  return small_tiles(q) ? launch_update<64>(q, s) : launch_update<128>(q, s);
 }
 
 }  // namespace dpf

@@ -222,6 +222,43 @@ def test_staged_calls_alternating_streams_match_one_stream(keep):
         dp.set_option("workspace_keep_bytes", old_keep)
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_workspace_blocks_move_between_streams(path):
+    """Workspace freed by a call on one stream is kept and handed to the next
+    call, here on another stream that is not otherwise ordered after the
+    first: that stream waits for the block's last use, so every result still
+    equals the one-stream result bit for bit."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(28)
+    data = []
+    for i in range(6):
+        lin = random_linear(rng, 4, 700, 520, 776, masked=True)
+        data.append(_dev(lin, torch))
+    dp.set_option("norm_path", path)
+    try:
+        ref = [dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9, offset=i)
+               for i, (X, G, m) in enumerate(data)]
+        torch.cuda.synchronize()
+        main = torch.cuda.current_stream()
+        streams = [torch.cuda.Stream() for _ in range(3)]
+        for _ in range(3):
+            start = torch.cuda.Event()
+            start.record(main)
+            outs = []
+            for i, (X, G, m) in enumerate(data):
+                st = streams[i % 3]
+                st.wait_event(start)
+                with torch.cuda.stream(st):
+                    outs.append(dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9,
+                                                          offset=i))
+            torch.cuda.synchronize()
+            for (o, n), (ro, rn) in zip(outs, ref):
+                assert torch.equal(o, ro) and torch.equal(n, rn)
+    finally:
+        dp.set_option("norm_path", 0)
+
+
 def test_staged_path_launches_its_kernels():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
