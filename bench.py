@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "3a41c058da5a5dfbaaee7b82f4ba7942d668628c3c30a1e74de519de58d7e7fc",
+    "sources_sha256": "277b5a4bc4824b0fdbf3c2804a8546957f93af972dfaef49bd8472dc5e56b01e",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1455496.12, "write_kib": 1416511.96}, "staged_combine": {"fetch_kib": 708059.29, "write_kib": 177214.74}},
-        "1": {"accumulate": {"fetch_kib": 1139913.01, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 420234.3, "write_kib": 152505.34}},
+        "0": {"staged_norm": {"fetch_kib": 1415101.16, "write_kib": 1416514.01}, "staged_combine": {"fetch_kib": 708059.32, "write_kib": 177206.37}},
+        "1": {"accumulate": {"fetch_kib": 1128929.82, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 420833.99, "write_kib": 152505.28}},
     },
 }
 
