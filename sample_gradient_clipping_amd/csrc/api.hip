@@ -379,7 +379,7 @@ struct Workspace {
   void* base = nullptr;
   size_t size = 0, cap = 0;
   hipEvent_t ev = nullptr;
-  int dev = -1;
+  int dev = -1;   // -1: not from (and not returned to) the cache
   explicit Workspace(hipStream_t st) : s(st) {}
   ~Workspace() {
     if (base == nullptr) return;
@@ -412,7 +412,14 @@ struct Workspace {
   bool allocate() {
     if (size == 0) return true;
     if (over_limit(size)) return false;
-    dev = stream_device(s);
+    // A stream being captured into a graph (or one whose state cannot be
+    // read) gets plain stream-ordered pool memory: kept blocks are ordered by
+    // events recorded outside any capture.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    bool cacheable = false;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess) cacheable = cs == hipStreamCaptureStatusNone;
+    else (void)hipGetLastError();
+    dev = cacheable ? stream_device(s) : -1;
     if (dev >= 0 && dev < kMaxDevices) {
       BlockCache& c = g_cache[dev];
       std::lock_guard<std::mutex> lk(c.mu);
