@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "277b5a4bc4824b0fdbf3c2804a8546957f93af972dfaef49bd8472dc5e56b01e",
+    "sources_sha256": "8f73e64db902a9ec81794083bf9040f1d8b6a6dad3ad68b1217aa020bf7db579",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1415101.16, "write_kib": 1416514.01}, "staged_combine": {"fetch_kib": 708059.32, "write_kib": 177206.37}},
-        "1": {"accumulate": {"fetch_kib": 1128929.82, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 420833.99, "write_kib": 152505.28}},
+        "0": {"staged_norm": {"fetch_kib": 1427278.02, "write_kib": 1416514.31}, "staged_combine": {"fetch_kib": 708059.32, "write_kib": 177180.15}},
+        "1": {"accumulate": {"fetch_kib": 1129802.82, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 421323.76, "write_kib": 152505.45}},
     },
 }
 
@@ -279,6 +279,16 @@ def measure_configs(dp, torch, steps, warmup):
     ms = time_calls(torch, seeded_layer, steps, warmup)
     out["c5_roberta_large_projected_seeded_r256_6_linears"] = {
         "note": "as above, P drawn from Philox seed 7 in each call (once into workspace), never kept",
+        "linears": len(lins), "ms": round(ms, 4),
+        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+    dp.set_option("p_in_kernels", 1)
+    try:
+        ms = time_calls(torch, seeded_layer, steps, warmup)
+    finally:
+        dp.set_option("p_in_kernels", 0)
+    out["c5_roberta_large_projected_seeded_in_kernel_r256_6_linears"] = {
+        "note": "as above, P drawn inside the projection kernel in every token tile; no P tensor",
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
         "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}

@@ -173,11 +173,12 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
  * rounded to X's dtype, xi from Philox4x32-10 (p_seed, p_offset) as above --
  * i.e. with the P that dpfused_gaussian_fill(p_seed, p_offset, din*r,
  * p_scale, X's dtype) writes -- but P is not kept: with one tile of tokens
- * (B*T <= 128) the projection kernel draws each element where it needs it;
- * with more, P is drawn once into the call's workspace (din*r elements,
- * released with it) and read from there, which is cheaper than drawing it
- * again in every token tile.  p_scale = 1/sqrt(r) gives the N(0, 1/r)
- * entries of the method.
+ * (B*T <= 128), or with the "p_in_kernels" option on, the projection kernel
+ * draws each element where it needs it and P never exists in memory; with
+ * more, P is drawn once into the call's workspace (din*r elements, released
+ * with it) and read from there, which is cheaper than drawing it again in
+ * every token tile.  Both give the same bits.  p_scale = 1/sqrt(r) gives
+ * the N(0, 1/r) entries of the method.
  *
  *   r         projection rank, a positive multiple of 8
  *   p_scale   finite
@@ -292,7 +293,7 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
  *              dpfused_linear_clip_accumulate_projected_seeded, drawn again
  *              inside the kernel, or once into workspace (din*r elements of
  *              p_dtype, for this call only) when W has more than one row of
- *              the kernel's tiles
+ *              the kernel's tiles and the "p_in_kernels" option is off
  *
  * All pointers 16-byte aligned.  Errors as above; nothing is written on
  * error.  m, v and W must not overlap each other or grad. */
@@ -340,6 +341,10 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                call's pool allocation, or its staged tile buffer) fails
  *                with DPF_ERR_OUT_OF_MEMORY before any output is written, as a
  *                failed hipMallocAsync would; 0 (default) = no limit
+ *   "p_in_kernels"  1 = a P given by its seed is always drawn inside the
+ *                kernels that use it, never stored (slower at many token
+ *                tiles); 0 (default) = drawn once per call into workspace
+ *                where that is cheaper.  Results are identical.
  *   "trace"      1 = push a roctx range named after the entry point around
  *                every call, for rocprofv3 --marker-trace; 0 = off (default)
  *   "debug"      1 = synchronise the launch stream after every kernel and

@@ -1128,6 +1128,11 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
     g_ws_limit.store(value);
     return ok();
   }
+  if (std::strcmp(name, "p_in_kernels") == 0) {
+    if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "p_in_kernels must be 0 or 1");
+    dpf::set_p_in_kernels(value != 0);
+    return ok();
+  }
   if (std::strcmp(name, "trace") == 0 || std::strcmp(name, "debug") == 0) {
     if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "trace and debug must be 0 or 1");
     (name[0] == 't' ? g_trace : g_debug).store((int)value);
@@ -1147,6 +1152,7 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
   if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
   if (std::strcmp(name, "workspace_limit_bytes") == 0) return g_ws_limit.load();
+  if (std::strcmp(name, "p_in_kernels") == 0) return dpf::p_in_kernels() ? 1 : 0;
   if (std::strcmp(name, "trace") == 0) return g_trace.load();
   if (std::strcmp(name, "debug") == 0) return g_debug.load();
   // Read-only: memory the current device's workspace pool holds now, and the

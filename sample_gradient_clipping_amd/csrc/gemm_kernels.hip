@@ -24,6 +24,8 @@
 // summed in index order by finalize_kernel, so every reduction is fixed-order.
 #include <algorithm>
 
+#include <atomic>
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -711,9 +713,13 @@ int project_splits(const ProjArgs& p) {
 // call's workspace (din*r elements, after the split partials) with the
 // gaussian fill, whose values are the ones the kernel would draw, and read
 // it like a stored P.  P still lives only for the call.
+static std::atomic<int> g_p_in_kernels{0};
+void set_p_in_kernels(bool on) { g_p_in_kernels.store(on ? 1 : 0); }
+bool p_in_kernels() { return g_p_in_kernels.load() != 0; }
+
 static bool project_draws_p_once(const ProjArgs& p) {
   const int64_t ntok = (int64_t)p.B * p.T;
-  return p.gen != 0 && (ntok + kTileN - 1) / kTileN > 1;
+  return p.gen != 0 && !p_in_kernels() && (ntok + kTileN - 1) / kTileN > 1;
 }
 
 static size_t project_split_bytes(const ProjArgs& p, int sp) {

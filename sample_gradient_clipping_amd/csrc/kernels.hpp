@@ -97,6 +97,10 @@ struct AdamArgs {
 // True when a seeded P is drawn once into a.pbuf (gaussian fill) and read
 // from there, rather than drawn again by every row of W tiles.
 bool adam_draws_p_once(const AdamArgs& a);
+// Process-wide: when on, a seeded P is always drawn inside the projection
+// and update kernels where it is used, and never exists in memory.
+void set_p_in_kernels(bool on);
+bool p_in_kernels();
 hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s);
 
 // Launchers (gemm_kernels.hip).  `vec` selects 16-byte vector loads; the

@@ -185,7 +185,7 @@ bool small_tiles(const AdamArgs& a) {
 
 bool adam_draws_p_once(const AdamArgs& a) {
   const int tile = small_tiles(a) ? 64 : 128;
-  return a.gen != 0 && a.dout > tile;
+  return a.gen != 0 && !p_in_kernels() && a.dout > tile;
 }
 
 hipError_t launch_projected_adam(const AdamArgs& a, hipStream_t s) {

@@ -76,7 +76,7 @@ def test_options(L):
     assert b"bogus" in L.dpfused_last_error()
     assert L.dpfused_get_option(b"bogus") == -1
     assert L.dpfused_set_option(b"timing", 0) == DPF_OK
-    for name in (b"trace", b"debug"):
+    for name in (b"trace", b"debug", b"p_in_kernels"):
         assert L.dpfused_set_option(name, 1) == DPF_OK
         assert L.dpfused_get_option(name) == 1
         assert L.dpfused_set_option(name, 0) == DPF_OK

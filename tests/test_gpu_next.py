@@ -29,11 +29,22 @@ SUM_TOL_BF16 = 1e-3
 # ---------------------------------------------------------------------------
 # seeded projection
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("in_kernel", [0, 1])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(3, 150, 1000, 136, 72), (2, 64, 136, 200, 256)])
-def test_seeded_projection_equals_stored_projection(dtype, shape):
+def test_seeded_projection_equals_stored_projection(dtype, shape, in_kernel):
+    """P drawn inside the projection kernel (one token tile, or p_in_kernels
+    on) or once into workspace: the stored-P call's bits either way."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
+    dp.set_option("p_in_kernels", in_kernel)
+    try:
+        _seeded_vs_stored(torch, dp, dtype, shape)
+    finally:
+        dp.set_option("p_in_kernels", 0)
+
+
+def _seeded_vs_stored(torch, dp, dtype, shape):
     B, T, din, dout, r = shape
     rng = np.random.default_rng(41)
     lin = random_linear(rng, B, T, din, dout, dtype=dtype, lengths=[T] + [T // 3] * (B - 1))
@@ -221,12 +232,22 @@ def test_projected_adam_step_matches_oracle(pdtype, shape):
     assert np.linalg.norm(dW - dW_ref) <= 1e-5 * np.linalg.norm(dW_ref) + 1e-7 * np.linalg.norm(W)
 
 
+@pytest.mark.parametrize("in_kernel", [0, 1])
 @pytest.mark.parametrize("dout", [300, 1024, 60])
-def test_projected_adam_seeded_equals_stored(dout):
+def test_projected_adam_seeded_equals_stored(dout, in_kernel):
     """P drawn once into workspace (dout 300, 1024) or inside the update
-    kernel (dout 60: one row of W tiles) gives the stored-P step bit for bit."""
+    kernel (dout 60: one row of W tiles; or p_in_kernels on) gives the
+    stored-P step bit for bit."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
+    dp.set_option("p_in_kernels", in_kernel)
+    try:
+        _adam_seeded_vs_stored(torch, dp, dout)
+    finally:
+        dp.set_option("p_in_kernels", 0)
+
+
+def _adam_seeded_vs_stored(torch, dp, dout):
     din, r = 520, 64
     rng = np.random.default_rng(46)
     h, m, v, W = _adam_case(rng, dout, din, r)
