@@ -145,3 +145,31 @@ def test_group_past_staged_limit_mixes_paths():
     assert max_rel(n3.cpu().numpy(), n1.cpu().numpy()) <= 1e-4
     for a, b in zip(o3, o1):
         assert rel_fro(a.cpu().numpy(), b.cpu().numpy()) <= 1e-4
+
+
+def test_offsets_past_two_gib_take_the_generic_kernels():
+    """X rows 8192 elements apart (a view into a 4 GiB buffer), T = 131072:
+    a sample spans 2^30 elements, past what the large-tile kernels address
+    with 32-bit offsets, so the call runs the generic kernels (64-bit
+    addressing).  Against the oracle on the 64 columns in use; the other
+    columns hold NaN, which must never be read."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    from tests.gpu_helpers import random_linear, to_dev
+    B, T, din, dout, pitch = 2, 131072, 64, 64, 8192
+    lin = random_linear(np.random.default_rng(33), B, T, din, dout)
+    _, rn, _ = dp_linear.oracle_linear(lin.X, lin.G, None, 1.0, 0.0, 0, 0, "bf16")
+    C = float(np.mean(rn))
+    big = torch.full((B, T, pitch), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big[:, :, :din].copy_(to_dev(lin.X, "bf16", torch))
+    X = big[:, :, :din]
+    assert X.stride(1) * 131072 >= 1 << 30
+    G = to_dev(lin.G, "bf16", torch)
+    out, norms = dp.linear_clip_accumulate(X, G, None, C=C, sigma=0.8, seed=4, offset=9)
+    out0, _ = dp.linear_clip_accumulate(X, G, None, C=C, sigma=0.0)
+    torch.cuda.synchronize()
+    ref, rnorms, _ = dp_linear.oracle_linear(lin.X, lin.G, None, C, 0.8, 4, 9, "bf16")
+    ref0, _, _ = dp_linear.oracle_linear(lin.X, lin.G, None, C, 0.0, 0, 0, "bf16")
+    assert max_rel(norms.cpu().numpy(), rnorms) <= NORM_TOL
+    assert rel_fro(out.cpu().numpy(), ref) <= AGG_TOL
+    assert rel_fro(out0.cpu().numpy(), ref0) <= SUM_TOL
