@@ -43,11 +43,12 @@
  *   - Every data pointer is DEVICE memory owned by the caller; the library
  *     never keeps, frees or reallocates it.  Outputs are overwritten.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
- *     queued on it asynchronously; temporary workspace is allocated and
- *     released in stream order on the same stream.  Calls on different
- *     streams may run concurrently, except that calls on the staged path
- *     take the device's staged-tile buffer in turn (each call's stream waits,
- *     on the GPU, for the previous holder's last use).
+ *     queued on it asynchronously; temporary workspace is taken and given
+ *     back in stream order: a block kept from an earlier call is used only
+ *     after that call's last use of it (the stream waits for it on the GPU).
+ *     Calls on different streams may run concurrently, except that calls on
+ *     the staged path take the device's staged-tile buffer in turn (each
+ *     call's stream waits, on the GPU, for the previous holder's last use).
  *   - Arguments are checked before anything is queued: on any error nothing
  *     is launched and nothing is written; the status says why and
  *     dpfused_last_error() gives a message (per thread).

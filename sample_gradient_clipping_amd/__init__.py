@@ -139,8 +139,8 @@ def linear_clip_accumulate_projected_seeded(X, G, r: int, mask=None, p_seed: int
                                             sigma: float = 0.0, seed: int = 0, offset: int = 0,
                                             grad_out=None, norms_out=None, stream=None,
                                             want_norms: bool = True):
-    """Projected variant with P[d, j] = p_scale * xi_{d*r+j}(p_seed, p_offset) drawn inside
-    the projection (never stored); p_scale defaults to 1/sqrt(r)."""
+    """Projected variant with P[d, j] = p_scale * xi_{d*r+j}(p_seed, p_offset) drawn in the
+    call and not kept (see the "p_in_kernels" option); p_scale defaults to 1/sqrt(r)."""
     torch = _torch()
     xa, ga = _act(X), _act(G)
     B, T = X.shape[0], X.shape[1]
