@@ -259,6 +259,36 @@ def test_workspace_blocks_move_between_streams(path):
         dp.set_option("norm_path", 0)
 
 
+def test_trimming_kept_workspace_between_streams():
+    """Blocks kept from calls on three streams are trimmed (keep = 0) while
+    those calls may still run, then calls resume with a fresh cache: every
+    result equals the one-stream result."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(29)
+    data = [_dev(random_linear(rng, 3, 500, 264, 520, masked=True), torch) for _ in range(6)]
+    old_keep = dp.get_option("workspace_keep_bytes")
+    dp.set_option("norm_path", 2)
+    try:
+        ref = [dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9, offset=i)
+               for i, (X, G, m) in enumerate(data)]
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream() for _ in range(3)]
+        for keep in (0, old_keep, 0, old_keep):
+            outs = []
+            for i, (X, G, m) in enumerate(data):
+                with torch.cuda.stream(streams[i % 3]):
+                    outs.append(dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9,
+                                                          offset=i))
+            dp.set_option("workspace_keep_bytes", keep)
+            torch.cuda.synchronize()
+            for (o, n), (ro, rn) in zip(outs, ref):
+                assert torch.equal(o, ro) and torch.equal(n, rn)
+    finally:
+        dp.set_option("norm_path", 0)
+        dp.set_option("workspace_keep_bytes", old_keep)
+
+
 def test_staged_path_launches_its_kernels():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
