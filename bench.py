@@ -39,13 +39,13 @@ METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFM
 # the default workload; reported as null otherwise.
 COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
 KERNEL_COUNTERS = {
-    "sources_sha256": "8f73e64db902a9ec81794083bf9040f1d8b6a6dad3ad68b1217aa020bf7db579",
+    "sources_sha256": "23951e013c3dc85a37e3b81f3fc25951d69e211f22fe95bf533fcfb8de3ae012",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1427278.02, "write_kib": 1416514.31}, "staged_combine": {"fetch_kib": 708059.32, "write_kib": 177180.15}},
-        "1": {"accumulate": {"fetch_kib": 1129802.82, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 421323.76, "write_kib": 152505.45}},
+        "0": {"staged_norm": {"fetch_kib": 1284089.86, "write_kib": 1416510.64}, "staged_combine": {"fetch_kib": 708059.38, "write_kib": 177198.16}},
+        "1": {"accumulate": {"fetch_kib": 1135114.01, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 418247.31, "write_kib": 152505.33}},
     },
 }
 

@@ -757,7 +757,7 @@ constexpr int64_t kImgStride = kTileElems;   // floats from one unit's image to 
 // own fp64 partial (np = 8 per tile), so no LDS is needed between units.
 constexpr int kStagedParts = kWaves;
 
-template <bool MASK>
+template <bool MASK, bool NT>
 __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned char* smem) {
   const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
   const int ntiles = ntm * ntn;
@@ -809,21 +809,25 @@ __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned
           v.x = acc.v[i][j][4 * g + 0]; v.y = acc.v[i][j][4 * g + 1];
           v.z = acc.v[i][j][4 * g + 2]; v.w = acc.v[i][j][4 * g + 3];
           s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-          // Plain (cached) stores: the most recently written tiles are still
-          // in the 256 MB MALL when the combine kernel reads them, which
-          // measured 13% faster combines at 5120 x 5120 than non-temporal
-          // stores; larger layers neither gain nor lose.
-          *(f32x4*)(img + ((i * kBO + j) * 4 + g) * 256) = v;
+          // Plain (cached) stores leave the most recently written tiles in
+          // the 256 MB MALL for the combine kernel: 13% faster combines at
+          // 5120 x 5120.  Non-temporal stores (NT) suit the calls whose tiles
+          // mostly leave the MALL anyway, or whose short units store so often
+          // that cached stores crowd out the operands of the next units.
+          f32x4* dst = (f32x4*)(img + ((i * kBO + j) * 4 + g) * 256);
+          if constexpr (NT) __builtin_nontemporal_store(v, dst);
+          else *dst = v;
         }
     const double tot = wave_sum_f64((double)s);
     if (lane == 0) p.partials[((int64_t)b * ntiles + L) * kStagedParts + wave] = tot;
   }
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, int G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  if (p.steps != nullptr) staged_units<true>(p, G, smem);
-  else staged_units<false>(p, G, smem);
+  if (p.steps != nullptr) staged_units<true, NT>(p, G, smem);
+  else staged_units<false, NT>(p, G, smem);
 }
 
 // out = (sum_b c_b g_b + noise_std xi) / B from the staged tiles: one thread
@@ -947,19 +951,34 @@ int staged_big_partials_per_sample(const LayerArgs& p) {
   return big_tiles(p.din, p.dout) * big::kStagedParts;
 }
 
-hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s) {
-  hipError_t e = allow_lds_big<big::staged_norm_big_kernel>(big::kLdsBytes);
+// Non-temporal tile stores where measured faster on MI355X: units of at most
+// 16 token steps (GPT-2 MLP, T = 512: 7% faster calls), or more than 1.5 GB
+// of tiles (Llama-13B gate/up/down, 2.3 GB: 1%).  Cached stores otherwise
+// (q/k/v/o, 0.84 GB: the combine reads recent tiles from the MALL, 2% faster).
+static bool staged_nontemporal(const LayerArgs& p) {
+  const int nsteps = (p.T + big::kKT - 1) / big::kKT;
+  return nsteps <= 16 || (double)staged_big_workspace_bytes(p) > 1.5e9;
+}
+
+template <bool NT>
+static hipError_t launch_staged_norm_t(const LayerArgs& p, int G, hipStream_t s) {
+  hipError_t e = allow_lds_big<big::staged_norm_big_kernel<NT>>(big::kLdsBytes);
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)big_tiles(p.din, p.dout) * p.B;
-  if (p.skws == nullptr || units > 0x7fffffff) return hipErrorInvalidValue;
-  int G = (int)std::min<int64_t>(device_cus(), units);
-  if (G >= 8) G -= G % 8;
   timing_begin("staged_norm", s);
-  hipLaunchKernelGGL(big::staged_norm_big_kernel, dim3((unsigned)G), dim3(big::kNT),
+  hipLaunchKernelGGL(big::staged_norm_big_kernel<NT>, dim3((unsigned)G), dim3(big::kNT),
                      big::kLdsBytes, s, p, G);
   e = hipGetLastError();
   timing_end("staged_norm", s);
   return e;
+}
+
+hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s) {
+  const int64_t units = (int64_t)big_tiles(p.din, p.dout) * p.B;
+  if (p.skws == nullptr || units > 0x7fffffff) return hipErrorInvalidValue;
+  int G = (int)std::min<int64_t>(device_cus(), units);
+  if (G >= 8) G -= G % 8;
+  return staged_nontemporal(p) ? launch_staged_norm_t<true>(p, G, s)
+                               : launch_staged_norm_t<false>(p, G, s);
 }
 
 hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s) {
