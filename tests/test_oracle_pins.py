@@ -483,6 +483,75 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(f32_to_bf16_bits(bf16_bits_to_f32(b)), b)
 
 
+def test_widen_bf16_matches_torch_on_every_bit_pattern():
+    """widen(bits, "bf16") against torch's own bfloat16 -> float64 conversion,
+    over all 65536 patterns (zeros, subnormals, infinities and NaNs included)."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = dp_linear.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127   # exponent all ones with a non-zero fraction, both signs
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_widen_f32_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(15)
+    a = np.concatenate([rng.standard_normal(4096).astype(np.float32) * 1e3,
+                        np.array([0.0, -0.0, 1e-45, -3.4e38, np.inf, -np.inf], np.float32)])
+    got = dp_linear.widen(a, "f32")
+    ref = torch.from_numpy(a).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def _bf16_bits_by_torch(v32: np.ndarray) -> np.ndarray:
+    torch = pytest.importorskip("torch")
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def test_projection_matrix_entries_follow_the_row_major_stream():
+    """P[d, j] is normal number d*r + j of the (seed, offset) stream, computed
+    here by the pure-Python scalar generator (itself pinned against rocRAND),
+    scaled in float32, and for bf16 rounded by torch's conversion.  Reading of
+    the DP-GRAPE explainer, Methodology, "Random Projection over SVD": the
+    projection is drawn again from its seed, row-major over [din, r]."""
+    seed, off, din, r = 7, 5, 37, 24
+    scale = 1.0 / math.sqrt(r)
+    z = philox.gaussian_scalar(seed, off, din * r)
+    P32 = dp_linear.projection_matrix(seed, off, din, r, scale, "f32")
+    P16 = dp_linear.projection_matrix(seed, off, din, r, scale, "bf16")
+    assert P32.shape == (din, r) and P32.dtype == np.float32
+    assert P16.shape == (din, r) and P16.dtype == np.uint16
+    rng = np.random.default_rng(16)
+    picks = [(0, 0), (0, 1), (1, 0), (din - 1, r - 1), (din - 1, 0), (0, r - 1)]
+    picks += [(int(d), int(j)) for d, j in zip(rng.integers(0, din, 40), rng.integers(0, r, 40))]
+    want32 = np.array([np.float32(scale) * np.float32(z[d * r + j]) for d, j in picks], np.float32)
+    got32 = np.array([P32[d, j] for d, j in picks], np.float32)
+    np.testing.assert_array_equal(got32, want32)
+    np.testing.assert_array_equal(np.array([P16[d, j] for d, j in picks], np.uint16),
+                                  _bf16_bits_by_torch(want32))
+    # the whole matrix, bf16 against torch's rounding of the float32 matrix
+    np.testing.assert_array_equal(P16, _bf16_bits_by_torch(P32))
+
+
+def test_projection_matrix_moments():
+    """Entries N(0, scale^2): sample mean and variance over 2^17 entries."""
+    din, r = 512, 256
+    s = 1.0 / math.sqrt(r)
+    P = dp_linear.projection_matrix(7, 0, din, r, s, "f32").astype(np.float64)
+    n = P.size
+    assert abs(P.mean()) < 5.0 * s / math.sqrt(n)
+    assert abs(P.var() / s ** 2 - 1.0) < 5.0 * math.sqrt(2.0 / n)
+    # rows are not copies of each other and columns are uncorrelated
+    c = np.corrcoef(P[:, 0], P[:, 1])[0, 1]
+    assert abs(c) < 5.0 / math.sqrt(din)
+
+
 # --------------------------------------------------------------------------
 # planted mistakes: each must trip at least one pin
 # --------------------------------------------------------------------------
@@ -549,3 +618,22 @@ def test_planted_dropped_sample(monkeypatch):
     monkeypatch.setattr(dp_linear, "clip_accumulate",
                         lambda gs, C: orig(list(gs)[:-1] or [np.zeros((1, 1))], C))
     assert _pins_fail(_DENSE_PINS)
+
+
+def test_planted_widen_shift(monkeypatch):
+    def wrong(a, dtype):
+        a = np.asarray(a)
+        if dtype == "bf16":
+            return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    monkeypatch.setattr(dp_linear, "widen", wrong)
+    assert _pins_fail([test_widen_bf16_matches_torch_on_every_bit_pattern])
+
+
+def test_planted_transposed_projection(monkeypatch):
+    def transposed(seed, offset, din, r, scale, dtype="bf16"):
+        z = philox.gaussian(seed, offset, din * r).astype(np.float32)
+        v = (np.float32(scale) * z).astype(np.float32).reshape(r, din).T.copy()
+        return v if dtype == "f32" else _bf16_bits_by_torch(v)
+    monkeypatch.setattr(dp_linear, "projection_matrix", transposed)
+    assert _pins_fail([test_projection_matrix_entries_follow_the_row_major_stream])
