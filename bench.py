@@ -5,9 +5,16 @@ Llama-13B-shaped decoder layer (q, k, v, o: 5120x5120; gate, up: 5120->13824;
 down: 13824->5120) at B = 8, T = 2048, bf16 inputs, fp32 accumulation, each
 linear clipped on its own (C = 1) with Philox noise (sigma = 1, seed 0,
 offset 0): per linear, the norm phase the library picks for the shape (at
-these shapes the staged form: each per-sample gradient tile computed once,
-its sum of squares taken and the tile stored in HBM), the ordered reduction
-to clip factors, and the clipped sum with the noise epilogue.
+these shapes the Gram identity: per-sample Gram blocks of X and G by MFMA,
+no per-sample gradient stored), the ordered reduction to clip factors, and
+the clipped sum as one scaled-accumulate GEMM with the noise epilogue.
+
+Beside the headline the same line reports the staged form (each per-sample
+gradient tile stored in device memory once, then combined) as a labelled
+comparison with its extra device memory, and the other workloads: one fp32
+linear, the GPT-2 MLP up-projection (with its inputs in and out of the
+Infinity Cache), the ragged Llama-13B batch, and the RoBERTa-large projected
+variant.
 
 Inputs are seeded synthetic Gaussians (no dataset) generated on the host and
 resident in HBM before timing starts.  Prints one JSON line.
@@ -28,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFMA peak"
 
@@ -44,9 +52,11 @@ KERNEL_COUNTERS = {
     "fetch_scale": 2.0, "write_scale": 1.0,
     # per --norm-path value: kernel -> KiB per dispatch
     "runs": {
-        "0": {"staged_norm": {"fetch_kib": 1284089.86, "write_kib": 1416510.64}, "staged_combine": {"fetch_kib": 708059.38, "write_kib": 177198.16}},
         "1": {"accumulate": {"fetch_kib": 1135114.01, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 418247.31, "write_kib": 152505.33}},
+        "3": {"staged_norm": {"fetch_kib": 1284089.86, "write_kib": 1416510.64}, "staged_combine": {"fetch_kib": 708059.38, "write_kib": 177198.16}},
     },
+    # --norm-path 0 takes the Gram path on all seven linears: the same kernels
+    "same_as": {"0": "1"},
 }
 
 
@@ -64,9 +74,11 @@ def parse():
                     help="0: the library's per-call choice (default); 1 Gram, 2 direct, 3 staged")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
-    ap.add_argument("--configs", action="store_true",
-                    help="also measure the other workload configurations (fp32 single linear, "
-                         "GPT-2 MLP up-projection, ragged Llama-13B layer, RoBERTa projected)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload configurations (fp32 single linear, GPT-2 MLP "
+                         "up-projection, ragged Llama-13B layer, RoBERTa projected)")
+    ap.add_argument("--no-staged", action="store_true",
+                    help="skip the staged-path comparison of the headline step")
     return ap.parse_args()
 
 
@@ -153,8 +165,15 @@ def time_calls(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def call_memory(dp):
+    """Resets the library's record of the most device memory one call took
+    beyond its inputs and outputs; returns a reader of it."""
+    dp.set_option("workspace_call_high", 0)
+    return lambda: int(dp.get_option("workspace_call_high"))
+
+
 def measure_configs(dp, torch, steps, warmup):
-    """Throughput of the other workload configurations, one fused call per linear."""
+    """The other workloads, one fused call per linear, on the automatic path."""
     import workloads
     out = {}
 
@@ -163,7 +182,7 @@ def measure_configs(dp, torch, steps, warmup):
             return upload(a, torch)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    def dense(makers, name, note):
+    def dense(makers, name, note, peak=PEAK_BF16_TFLOPS):
         dev, lins = [], []
         for make in makers:
             lin = make()
@@ -179,25 +198,34 @@ def measure_configs(dp, torch, steps, warmup):
             for lin, X, G, mask, o, nrm in dev:
                 dp.linear_clip_accumulate(X, G, mask, C=lin.C, sigma=lin.sigma, seed=lin.seed,
                                           offset=lin.offset, grad_out=o, norms_out=nrm)
+        mem = call_memory(dp)
         ms = time_calls(torch, layer, steps, warmup)
-        paths = sorted({norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate(
+        paths = [norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate(
             d[1], d[2], d[3], C=d[0].C, sigma=d[0].sigma, seed=d[0].seed, offset=d[0].offset,
-            grad_out=d[4], norms_out=d[5])) for d in dev})
+            grad_out=d[4], norms_out=d[5])) for d in dev]
         useful = sum(2.0 * l.active_tokens() * l.din * l.dout for l in lins)
         B = lins[0].B
-        out[name] = {"note": note, "norm_path": ",".join(paths), "linears": len(lins), "ms": round(ms, 4),
-                     "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-                     "samples_per_s": round(B * len(lins) / (ms * 1e-3), 1),
-                     "tokens_per_s": round(sum(l.active_tokens() for l in lins) / (ms * 1e-3), 1)}
+        tf = useful / (ms * 1e-3) / 1e12
+        out[name] = {"note": note,
+                     "norm_path": ", ".join(f"{l.name} {p}" for l, p in zip(lins, paths)),
+                     "linears": len(lins), "ms": round(ms, 4),
+                     "useful_tflops": round(tf, 3), "peak_tflops": peak,
+                     "frac_of_peak": round(tf / peak, 5),
+                     "samples_per_s": round(B / (ms * 1e-3), 1),
+                     "tokens_per_s": round(sum(l.active_tokens() for l in lins) / len(lins)
+                                           / (ms * 1e-3), 1),
+                     "extra_device_bytes_per_call_max": mem()}
         print(f"# {name}: {out[name]}", file=sys.stderr, flush=True)
         del dev
         torch.cuda.empty_cache()
 
     dense([lambda: workloads.config_c1(sigma=1.0).linears[0]], "c1_fp32_B4_T16_64to32",
-          "one fp32 linear; launch-latency bound")
+          "one fp32 linear, sigma 1; launch-latency bound; peak = fp32 vector 157.3 TFLOP/s",
+          peak=PEAK_FP32_TFLOPS)
+    dense([lambda: workloads.config_c1(sigma=0.0).linears[0]], "c1_fp32_B4_T16_64to32_sigma0",
+          "as above, sigma 0", peak=PEAK_FP32_TFLOPS)
     dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
-          "bf16, sigma 0.8")
-
+          "bf16, sigma 0.8; inputs (126 MB) resident in the Infinity Cache across calls")
     # the same layer with its bias (weight and bias clipped together)
     lin = workloads.config_c2().linears[0]
     X, G = upload(lin.X, torch), upload(lin.G, torch)
@@ -222,6 +250,7 @@ def measure_configs(dp, torch, steps, warmup):
     out["c2_gpt2_up_B32_T512_768to3072_flushed"] = {
         "note": "as c2, each call after a 512 MB write that evicts the inputs from the cache",
         "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
         "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
     del flush
     o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
@@ -234,6 +263,7 @@ def measure_configs(dp, torch, steps, warmup):
     out["c2_gpt2_up_with_bias"] = {
         "note": "as c2, plus the bias gradient (column sums of G) in the clipping norm and sum",
         "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
         "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
     del X, G, o, ob, nrm
     torch.cuda.empty_cache()
@@ -268,7 +298,8 @@ def measure_configs(dp, torch, steps, warmup):
         "norm_path": ",".join(paths),
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+        "frac_of_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
 
     # the same, with P drawn from its seed inside the projection (never stored)
     def seeded_layer():
@@ -281,7 +312,7 @@ def measure_configs(dp, torch, steps, warmup):
         "note": "as above, P drawn from Philox seed 7 in each call (once into workspace), never kept",
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
     dp.set_option("p_in_kernels", 1)
     try:
         ms = time_calls(torch, seeded_layer, steps, warmup)
@@ -291,7 +322,7 @@ def measure_configs(dp, torch, steps, warmup):
         "note": "as above, P drawn inside the projection kernel in every token tile; no P tensor",
         "linears": len(lins), "ms": round(ms, 4),
         "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "samples_per_s": round(lins[0].B * len(lins) / (ms * 1e-3), 1)}
+        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
 
     # projected Adam step on the privatised projected gradients (moments in
     # r-space, weight update W -= lr U P^T with P drawn from its seed)
@@ -339,11 +370,23 @@ def kernel_traffic(args, kernel):
     for f in COUNTER_SOURCES:
         with open(os.path.join(ROOT, "sample_gradient_clipping_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    k = c["runs"].get(str(args.norm_path), {}).get(kernel)
+    run = c.get("same_as", {}).get(str(args.norm_path), str(args.norm_path))
+    k = c["runs"].get(run, {}).get(kernel)
     if (k is None or h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"]
             or args.seq != c["seq"] or args.linears != c["linears"]):
         return None
     return (k["fetch_kib"] * c["fetch_scale"] + k["write_kib"] * c["write_scale"]) * 1024.0
+
+
+def kernel_counter(args, kernel, name):
+    """A per-kernel counter figure (e.g. MFMA-busy %) from the committed
+    rocprofv3 --pmc summary of this workload, or None when the kernel sources
+    or the workload differ from the profiled ones."""
+    c = KERNEL_COUNTERS
+    if kernel_traffic(args, kernel) is None:
+        return None
+    run = c.get("same_as", {}).get(str(args.norm_path), str(args.norm_path))
+    return c["runs"].get(run, {}).get(kernel, {}).get(name)
 
 
 def norm_path_of(dp, call):
@@ -443,7 +486,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # whole-step wall time
+    # whole-step wall time; the library's record of the device memory each
+    # call takes beyond its inputs and outputs is reset first
+    mem = call_memory(dp)
     s0 = torch.cuda.Event(enable_timing=True)
     s1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -456,6 +501,8 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     ms_step = s0.elapsed_time(s1) / args.steps
+    extra_bytes = mem()
+    pool_high = int(dp.get_option("workspace_reserved_high"))
 
     # per-kernel durations: HIP events recorded by the library on the launch
     # stream around every kernel, over a second pass of the same K steps
@@ -507,7 +554,7 @@ def main():
     executed = sum(contraction(l) + (gram_flops(l) if p == "gram" else contraction(l) if p == "direct"
                                      else 0.0) for l, p in zip(lins, paths))
     tflops = useful / (ms_step * 1e-3) / 1e12
-    samples_per_s = sum(l.B for l in lins) / (ms_step * 1e-3)
+    samples_per_s = args.batch / (ms_step * 1e-3)   # a step is one layer over the batch
 
     # MFMA kernels and the flops each does per linear; the dominant one (most
     # time per step) is the roofline kernel.
@@ -582,7 +629,10 @@ def main():
                                 + ", ".join(f"{l.name} {p}" for l, p in zip(lins, paths)),
                    "parallelism": "none (1 GPU)"},
         "samples_per_s": round(samples_per_s, 1),
+        "samples_per_s_note": "batch / step time: one step clips the whole layer for B samples",
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "extra_device_bytes_per_call_max": extra_bytes,
+        "workspace_pool_reserved_high_bytes": pool_high,
         "executed_tflops": round(executed / (ms_step * 1e-3) / 1e12, 2),
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in ktimes.items()},
         "roofline": {
@@ -593,6 +643,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(dom_achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None if traffic is None else round(traffic),
+            "avg_launch_ms": round(dom_avg_ms, 4),
+            "flops_per_launch": round(dom_flops),
+            "mfma_busy_pct": kernel_counter(args, dom, "mfma_busy_pct"),
         },
         "roofline_kernel_bytes_per_launch": {"algorithmic": round(dom_algo_bytes),
                                              "hbm_counters": None if traffic is None else round(traffic)},
@@ -605,22 +658,46 @@ def main():
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),
     }
-    if args.configs:
-        # group clipping: one clip factor per sample over the seven linears
-        Xs = [X for (X, _, _, _) in dev_in]
-        Gs = [G for (_, G, _, _) in dev_in]
-        outs = [o for (_, _, o, _) in dev_in]
-        offs, at = [], 0
-        for l in lins:
-            offs.append(at)
-            at += (l.din * l.dout + 3) // 4
-        ms_group = time_calls(torch, lambda: dp.group_clip_accumulate(
-            Xs, Gs, None, C=1.0, sigma=1.0, offsets=offs, grad_outs=outs), args.steps, 2)
-        res["group_clip_layer"] = {
-            "note": "the same seven linears, clipped jointly (one c_i per sample over the layer)",
-            "ms": round(ms_group, 4), "useful_tflops": round(useful / (ms_group * 1e-3) / 1e12, 2),
-            "samples_per_s": round(args.batch / (ms_group * 1e-3), 1)}
-        del Xs, Gs, outs
+    if not args.no_staged and args.norm_path != 3:
+        # The staged form, for comparison only: every per-sample gradient tile
+        # computed once and stored in device memory (the explicit storage the
+        # FlashDP abstract sets its method against), then combined.
+        dp.set_option("norm_path", 3)
+        try:
+            smem = call_memory(dp)
+            ms_staged = time_calls(torch, step, args.steps, 2)
+            staged_extra = smem()
+            spaths = [norm_path_of(dp, lambda l=l, d=d: dp.linear_clip_accumulate(
+                d[0], d[1], None, C=l.C, sigma=l.sigma, seed=l.seed, offset=l.offset,
+                grad_out=d[2], norms_out=d[3])) for l, d in zip(lins, dev_in)]
+        finally:
+            dp.set_option("norm_path", args.norm_path)
+        res["staged_path_comparison"] = {
+            "note": "opt-in staged form (norm_path 3): per-sample gradient tiles stored in device "
+                    "memory once, then combined; not the method's form, which keeps no "
+                    "per-sample gradient",
+            "norm_path": ", ".join(f"{l.name} {p}" for l, p in zip(lins, spaths)),
+            "ms_per_step": round(ms_staged, 4),
+            "useful_tflops": round(useful / (ms_staged * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(useful / (ms_staged * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "samples_per_s": round(args.batch / (ms_staged * 1e-3), 1),
+            "extra_device_bytes_per_call_max": staged_extra}
+    # group clipping: one clip factor per sample over the seven linears
+    Xs = [X for (X, _, _, _) in dev_in]
+    Gs = [G for (_, G, _, _) in dev_in]
+    outs = [o for (_, _, o, _) in dev_in]
+    offs = dp.consecutive_offsets([(l.dout, l.din) for l in lins])
+    gmem = call_memory(dp)
+    ms_group = time_calls(torch, lambda: dp.group_clip_accumulate(
+        Xs, Gs, None, C=1.0, sigma=1.0, offsets=offs, grad_outs=outs), args.steps, 2)
+    res["group_clip_layer"] = {
+        "note": "the same seven linears, clipped jointly (one c_i per sample over the layer)",
+        "ms": round(ms_group, 4), "useful_tflops": round(useful / (ms_group * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(useful / (ms_group * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "samples_per_s": round(args.batch / (ms_group * 1e-3), 1),
+        "extra_device_bytes_per_call_max": gmem()}
+    del Xs, Gs, outs
+    if not args.no_configs:
         del dev_in
         torch.cuda.empty_cache()
         res["configs"] = measure_configs(dp, torch, args.steps, 2)

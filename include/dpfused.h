@@ -24,17 +24,17 @@
  * dpfused_noise_blocks(dout*din) blocks: advance `offset` by that much
  * between calls to draw fresh noise.
  *
- * Each call picks one of three ways to the norms, all giving the same n_i
- * and grad_out up to rounding: the Gram identity
- * ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> (T short relative to the layer), the
- * per-sample gradient tiles computed and dropped (a second contraction then
- * forms the clipped sum), or -- for unmasked bf16 calls of the single-layer
- * (dense, bias, projected) and group entry points -- those tiles computed
- * once and staged in a device workspace (fp32, B * dout * din values rounded
- * up to 256 x 256 tiles, at most 16 GiB per call) that the clipped sum then
- * reads back.  The staged form trades the second contraction for one pass
- * over HBM; the choice is made per call from measured rates (see the
- * "norm_path" option).  Staged tiles live only for the duration of the call.
+ * Each call picks one of two ways to the norms, both giving the same n_i and
+ * grad_out up to rounding, and neither storing a per-sample gradient: the
+ * Gram identity ||G~^T X~||^2 = <X~ X~^T, G~ G~^T> (T short relative to the
+ * layer), or the per-sample gradient tiles computed and dropped (a second
+ * contraction then forms the clipped sum).  A third way, on request only
+ * (the "norm_path" option set to 3), computes each tile once and stages it
+ * in device memory (fp32, B * dout * din values rounded up to 256 x 256
+ * tiles, at most 16 GiB per call) for the clipped sum to read back; that is
+ * the explicit per-sample storage the FlashDP abstract sets its method
+ * against, kept for comparison.  Staged tiles are given back at the end of
+ * the call unless the "staged_keep_bytes" option keeps them.
  * Tiny dense calls (B <= 8, about 8192 outputs, every sample's rows within
  * 64 KiB as float32, at most 4 MFLOP) run the whole step in one workgroup
  * instead: one launch, the per-sample gradients never leave the chip.
@@ -46,9 +46,10 @@
  *     queued on it asynchronously; temporary workspace is taken and given
  *     back in stream order: a block kept from an earlier call is used only
  *     after that call's last use of it (the stream waits for it on the GPU).
- *     Calls on different streams may run concurrently, except that calls on
- *     the staged path take the device's staged-tile buffer in turn (each
- *     call's stream waits, on the GPU, for the previous holder's last use).
+ *     Calls on different streams may run concurrently, except that staged
+ *     calls take a kept staged-tile buffer in turn when the
+ *     "staged_keep_bytes" option keeps one (each call's stream waits, on the
+ *     GPU, for the previous holder's last use).
  *   - Arguments are checked before anything is queued: on any error nothing
  *     is launched and nothing is written; the status says why and
  *     dpfused_last_error() gives a message (per thread).
@@ -57,6 +58,11 @@
  *     never read into the arithmetic, whatever they hold.
  *   - Results are bit-identical from run to run on the same device and build
  *     (every reduction has a fixed order; no floating-point atomics).
+ *   - Noise: two outputs must never draw the same Philox block under one
+ *     seed.  Shared normals cancel when the two outputs are subtracted, and
+ *     the privacy the noise buys is lost.  Advance `offset` by
+ *     dpfused_noise_blocks(n) after each call; the group call and the seeded
+ *     projected call reject overlapping ranges that they can see.
  */
 #ifndef DPFUSED_H
 #define DPFUSED_H
@@ -178,14 +184,20 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
  * draws each element where it needs it and P never exists in memory; with
  * more, P is drawn once into the call's workspace (din*r elements, released
  * with it) and read from there, which is cheaper than drawing it again in
- * every token tile.  Both give the same bits.  p_scale = 1/sqrt(r) gives
- * the N(0, 1/r) entries of the method.
+ * every token tile.  Both give the same bits.
  *
  *   r         projection rank, a positive multiple of 8
- *   p_scale   finite
+ *   p_scale   the entries' standard deviation; NaN or <= 0 selects the
+ *             method's N(0, 1/r) entries, p_scale = 1/sqrt(r) (same
+ *             explainer and section: Gaussian entries whose variance is
+ *             the inverse of the rank)
  *
  * Errors as for the projected variant; r not a multiple of 8 gives
- * DPF_ERR_UNSUPPORTED. */
+ * DPF_ERR_UNSUPPORTED; an infinite p_scale gives DPF_ERR_INVALID_ARGUMENT;
+ * with sigma > 0 and seed == p_seed, noise blocks [offset, offset +
+ * dpfused_noise_blocks(dout*r)) that overlap P's blocks [p_offset, p_offset +
+ * dpfused_noise_blocks(din*r)) give DPF_ERR_INVALID_ARGUMENT (the noise would
+ * be a scaled copy of P's entries, known to anyone who can draw P again). */
 dpf_status dpfused_linear_clip_accumulate_projected_seeded(
     const dpf_act* X, const dpf_act* G, const uint8_t* mask, int64_t r, uint64_t p_seed,
     uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
@@ -251,7 +263,11 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
  *   norms_out[i]    = n_i (the group norm, before clipping)
  *
  * xi^(l) is the noise of the dense call with (seed, offsets[l]).  With n = 1
- * it is dpfused_linear_clip_accumulate.
+ * it is dpfused_linear_clip_accumulate.  With sigma > 0 the block ranges
+ * [offsets[l], offsets[l] + dpfused_noise_blocks(dout_l * din_l)) must be
+ * pairwise disjoint, else DPF_ERR_INVALID_ARGUMENT (consecutive ranges,
+ * offsets[l+1] = offsets[l] + dpfused_noise_blocks(dout_l * din_l), are the
+ * usual choice).
  *
  *   n          number of linears, >= 1
  *   X, G       HOST arrays of n descriptors; every linear has the same B and T
@@ -291,7 +307,8 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
  *   P          [din, r] row-major, p_dtype (DPF_F32 or DPF_BF16), 16-byte
  *              aligned -- or NULL: then P[d][j] = p_scale * xi_{d*r+j} from
  *              Philox (p_seed, p_offset) rounded to p_dtype, the P of
- *              dpfused_linear_clip_accumulate_projected_seeded, drawn again
+ *              dpfused_linear_clip_accumulate_projected_seeded (NaN or <= 0
+ *              p_scale: 1/sqrt(r), as there), drawn again
  *              inside the kernel, or once into workspace (din*r elements of
  *              p_dtype, for this call only) when W has more than one row of
  *              the kernel's tiles and the "p_in_kernels" option is off
@@ -304,40 +321,56 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
                                        const void* P, int32_t p_dtype, uint64_t p_seed,
                                        uint64_t p_offset, float p_scale, void* stream);
 
-/* Raw Philox4x32-10 words: out[4*j + k] = word k of block (offset + j),
- * j < nblocks, with the key/counter layout above.  out: device, 16-byte
- * aligned, 4*nblocks uint32.  nblocks >= 0 (0 = nothing queued). */
+/* Raw Philox4x32-10 words of the noise generator (the noise added after
+ * clipping in the FlashDP abstract and in the DP-GRAPE explainer,
+ * Methodology, is drawn from this counter-based generator; Salmon, Moraes,
+ * Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11):
+ * out[4*j + k] = word k of block (offset + j), j < nblocks, with the
+ * key/counter layout above.  For checking the generator and for callers
+ * that draw their own noise.  out: device, 16-byte aligned, 4*nblocks
+ * uint32.  nblocks >= 0 (0 = nothing queued).  Errors: NULL or misaligned
+ * out, negative nblocks. */
 dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks,
                                  uint32_t* out, void* stream);
 
-/* out[e] = scale * xi_e for e < n (xi as above: four normals per block,
- * starting at block `offset`), stored as float32 or as bfloat16 rounded to
- * nearest-even from the float32 product.  Used to draw the Gaussian
- * projection P (entries N(0, 1/r): scale = 1/sqrt(r)).  out: device,
- * 16-byte aligned.  n >= 0. */
+/* Gaussian numbers of the noise law above: out[e] = scale * xi_e for e < n
+ * (four normals per block, starting at block `offset`), stored as float32
+ * or as bfloat16 rounded to nearest-even from the float32 product.  Draws
+ * the Gaussian projection P of the DP-GRAPE explainer (Methodology, "Random
+ * Projection over SVD": random Gaussian matrices, drawn again from their
+ * seed; entries N(0, 1/r): scale = 1/sqrt(r)), and the noise
+ * sigma * C * xi of the FlashDP abstract's noise step on its own.  out:
+ * device, 16-byte aligned.  n >= 0.  Errors: unknown dtype, infinite scale,
+ * NULL or misaligned out, negative n. */
 dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale,
                                  int32_t dtype, void* out, void* stream);
 
-/* Philox blocks consumed by n noise elements: ceil(n / 4); 0 for n <= 0. */
+/* Philox blocks consumed by n noise elements (four normals per block, by
+ * the noise layout above): ceil(n / 4); 0 for n <= 0.  Advance `offset` by
+ * this much between calls so that no two outputs share noise. */
 uint64_t dpfused_noise_blocks(int64_t n_elements);
 
 /* Library options (process-wide).  Names:
- *   "norm_path"  0 = choose per call; 1 = always Gram; 2 = always direct
- *                (gradient tiles computed and dropped, then a second
- *                contraction); 3 = staged where the call allows it (bf16
- *                single-layer and group calls whose staged tiles fit in
- *                16 GiB), else direct
+ *   "norm_path"  0 = choose per call between Gram and direct (default);
+ *                1 = always Gram; 2 = always direct (gradient tiles
+ *                computed and dropped, then a second contraction); 3 =
+ *                staged where the call allows it (bf16 single-layer and
+ *                group calls whose staged tiles fit in 16 GiB), else direct
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
- *   "workspace_keep_bytes"  bytes the library keeps reserved for later calls
- *                (default 16 GiB), each of: workspace blocks freed by calls
- *                and kept for reuse (a later call's stream waits on the GPU
- *                for the block's last use, so blocks move between streams
- *                safely), freed memory in the per-device pool behind them,
- *                and the per-device buffer of staged per-sample tiles (freed
- *                after each call when larger).  Setting it trims all three;
- *                trimming kept blocks and the staged buffer waits for their
- *                last users.
+ *   "workspace_keep_bytes"  bytes of workspace the library keeps reserved
+ *                for later calls (default 512 MiB, about twice the largest
+ *                Llama-13B-layer call's workspace), each of: workspace
+ *                blocks freed by calls and kept for reuse (a later call's
+ *                stream waits on the GPU for the block's last use, so blocks
+ *                move between streams safely), and freed memory in the
+ *                per-device pool behind them.  Setting it trims both;
+ *                trimming kept blocks waits for their last users.
+ *   "staged_keep_bytes"  staged path only: a per-device buffer of staged
+ *                tiles up to this size is kept for the next call (calls on
+ *                any stream then take it in turn, the stream waiting on the
+ *                GPU for its previous holder); 0 (default) = the tiles are
+ *                taken and given back within each call, stream-ordered
  *   "workspace_limit_bytes"  a workspace request larger than this (one
  *                call's pool allocation, or its staged tile buffer) fails
  *                with DPF_ERR_OUT_OF_MEMORY before any output is written, as a
@@ -356,7 +389,11 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  * DPFUSED_TRACE and DPFUSED_DEBUG (0/1), DPFUSED_WS_LIMIT (bytes).
  * Read-only (dpfused_get_option): "workspace_reserved_bytes" and
  * "workspace_reserved_high", what the current device's pool holds now and at
- * most (-1 without a pool).
+ * most (-1 without a pool); "workspace_call_bytes", the device memory the
+ * last call on this thread took beyond its inputs and outputs (workspace
+ * plus staged tiles), and "workspace_call_high", the most any call took
+ * since the library was loaded or since dpfused_set_option(
+ * "workspace_call_high", 0).
  * Returns DPF_ERR_INVALID_ARGUMENT for an unknown name or value. */
 dpf_status dpfused_set_option(const char* name, int64_t value);
 int64_t dpfused_get_option(const char* name);

@@ -146,29 +146,26 @@ dpf::Act to_act(const dpf_act* a) { return dpf::Act{a->data, a->stride_b, a->str
 // Largest staged workspace (B per-sample gradient tiles, fp32) a call may use.
 constexpr double kStagedMaxBytes = 16.0 * (1ull << 30);
 
-// Rates used to price the norm paths against each other on the large-tile
-// path, measured on MI355X at the Llama-13B, GPT-2 and RoBERTa shapes (flops
-// or bytes per microsecond): the direct and staged norm kernels run the
-// token contraction at ~1.25 PFLOP/s, the accumulate kernel at ~1.15, the
-// Gram kernel at ~1.05 plus ~25 us of fills and fixup; the staged tiles
-// cost ~1/20 us per MB to store (beyond the contraction: the persistent
-// kernel's stores overlap the next unit's fill) and are read back at ~5 TB/s.
-constexpr double kNormPerUs = 1.25e9, kAccPerUs = 1.15e9, kGramPerUs = 1.05e9;
-constexpr double kStorePerUs = 20.0e6, kCombinePerUs = 5.0e6;
-constexpr double kGramFixedUs = 25.0, kAccFixedUs = 15.0, kCombineFixedUs = 5.0;
-
-// allow_staged: the caller keeps the per-sample tiles from the norm phase to
-// the accumulate phase (the single-layer calls, and group clipping, which
+// The norm path of one call.  The automatic choice is always one of the two
+// forms that never store a per-sample gradient: the Gram identity or the
+// direct form (each g_i tile computed and dropped).  The staged form, which
+// keeps every g_i tile in device memory between the norm and accumulate
+// phases, runs only when the "norm_path" option asks for it.
+//
+// allow_staged: the caller can keep the per-sample tiles from the norm phase
+// to the accumulate phase (the single-layer calls, and group clipping, which
 // holds every linear's tiles until the group's clip factors exist).
 dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) {
   const bool big = dpf::big_path(a, vec);
-  const double staged_bytes = (double)dpf::staged_big_workspace_bytes(a);
-  const bool staged_ok = allow_staged && big && staged_bytes <= kStagedMaxBytes &&
-                         (double)a.B * dpf::big_tiles(a.din, a.dout) < 2147483647.0;
   const int forced = g_norm_path.load();
   if (forced == 1) return dpf::NormPath::kGram;
   if (forced == 2) return dpf::NormPath::kDirect;
-  if (forced == 3) return staged_ok ? dpf::NormPath::kStaged : dpf::NormPath::kDirect;
+  if (forced == 3) {
+    const bool staged_ok = allow_staged && big &&
+                           (double)dpf::staged_big_workspace_bytes(a) <= kStagedMaxBytes &&
+                           (double)a.B * dpf::big_tiles(a.din, a.dout) < 2147483647.0;
+    return staged_ok ? dpf::NormPath::kStaged : dpf::NormPath::kDirect;
+  }
   const double T = a.T, din = a.din, dout = a.dout;
   const double direct = 2.0 * T * din * dout;   // flops per sample
   if (big) {
@@ -177,32 +174,41 @@ dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) 
     // measured on MI355X it beats the direct kernel once it needs at most
     // half the direct kernel's flops.
     const double gram = 2.0 * dpf::gram_big_items_per_sample(a.T) * 65536.0 * (din + dout);
-    const bool use_gram = 2.0 * gram <= direct;
-    const dpf::NormPath two_pass = use_gram ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
-    // Staged: the direct kernel, storing its tiles, then a read of them in
-    // place of the accumulate kernel's second contraction.  Masked calls
-    // keep the two-pass paths: the host does not know their active tokens.
-    if (staged_ok && a.mask == nullptr) {
-      const double acc = a.B * direct;   // the contraction both forms run once
-      const double t_two_pass =
-          (use_gram ? a.B * gram / kGramPerUs + kGramFixedUs : acc / kNormPerUs) +
-          acc / kAccPerUs + kAccFixedUs;
-      const double t_staged = acc / kNormPerUs + staged_bytes / kStorePerUs +
-                              staged_bytes / kCombinePerUs + kCombineFixedUs;
-      if (t_staged < t_two_pass) return dpf::NormPath::kStaged;
-    }
-    return two_pass;
+    return 2.0 * gram <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
   }
   // Gram costs T^2 (din + dout) per sample, the direct form 2 T din dout.
   return T * T * (din + dout) <= direct ? dpf::NormPath::kGram : dpf::NormPath::kDirect;
 }
 
 // Per-device stream-ordered memory pool for workspace (everything but the
-// staged tiles, which have a buffer of their own below).  It keeps up to
+// staged tiles, which are taken apart from it below).  It keeps up to
 // g_keep_bytes reserved across synchronisations (the default pool returns
 // freed memory at every synchronisation), so workspace is not mapped afresh
-// on every step.
-std::atomic<int64_t> g_keep_bytes{(int64_t)16 << 30};
+// on every step.  The default, 512 MiB, is about twice the workspace of the
+// largest Llama-13B-layer call (a 5120 x 5120 linear at B = 8, T = 2048:
+// split-tile partials of the accumulate and Gram kernels plus the norm
+// partials), so the calls of one layer step reuse blocks.
+std::atomic<int64_t> g_keep_bytes{(int64_t)512 << 20};
+// Bytes of staged per-sample tiles kept for the next call; 0 (the default):
+// the tiles are given back at the end of every call.
+std::atomic<int64_t> g_staged_keep{0};
+// Device memory one call takes beyond its inputs and outputs (workspace plus
+// staged tiles): the last call on this thread, and the most since reset.
+thread_local int64_t t_call_bytes = 0;
+std::atomic<int64_t> g_call_high{0};
+void note_call_bytes(size_t bytes) {
+  t_call_bytes += (int64_t)bytes;
+  int64_t h = g_call_high.load();
+  while (t_call_bytes > h && !g_call_high.compare_exchange_weak(h, t_call_bytes)) {
+  }
+}
+
+// Starts the per-call memory count, and the roctx range of the entry point
+// when the trace option is on.
+struct CallScope {
+  TraceRange range;
+  explicit CallScope(const char* name) : range(name) { t_call_bytes = 0; }
+};
 std::mutex g_pool_mu;
 constexpr int kMaxDevices = 64;
 hipMemPool_t g_pools[kMaxDevices] = {};
@@ -216,6 +222,15 @@ int stream_device(hipStream_t s) {
   }
   if (dev < 0 && hipGetDevice(&dev) != hipSuccess) dev = -1;
   return dev;
+}
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;   // state unknown: take the path that is safe under capture
+  }
+  return cs != hipStreamCaptureStatusNone;
 }
 
 hipMemPool_t workspace_pool(hipStream_t s) {
@@ -241,13 +256,17 @@ hipMemPool_t workspace_pool(hipStream_t s) {
   return g_pools[dev];
 }
 
-// The staged per-sample tiles (up to gigabytes) live in one buffer per device
-// that the library keeps and grows, not in the pool: pool allocations of that
-// size, freed and made again by calls on several streams, were measured to
-// stall for tens of milliseconds on MI355X.  Calls on any stream take the
-// buffer in turn: each one's stream first waits (on the GPU) for the event
-// recorded after the previous holder's last use, and records its own after
-// its last launch.  A buffer larger than g_keep_bytes is freed after use.
+// The staged per-sample tiles (up to gigabytes, staged path only) are taken
+// for one call and given back at its end: stream-ordered hipMallocAsync /
+// hipFreeAsync on the call's stream.  With the "staged_keep_bytes" option
+// above 0 a buffer of up to that size is kept per device for the next call
+// instead (pool allocations of that size, freed and made again by calls on
+// several streams, were measured to stall for tens of milliseconds on
+// MI355X).  Calls on any stream take a kept buffer in turn: each one's
+// stream first waits (on the GPU) for the event recorded after the previous
+// holder's last use, and records its own after its last launch.  A stream
+// being captured into a graph never uses the kept buffer (its events are
+// recorded outside the capture): it takes capture-local memory.
 struct StagedBuffer {
   std::mutex mu;
   void* ptr = nullptr;
@@ -260,15 +279,25 @@ StagedBuffer g_staged[kMaxDevices];
 class StagedLease {
  public:
   ~StagedLease() { release(); }
-  // Holds the calling thread's device buffer of at least `bytes` for work
-  // queued on `s` until release(); false if it cannot be had.
+  // Holds at least `bytes` of staged tiles for work queued on `s` until
+  // release(); false if they cannot be had.
   bool acquire(hipStream_t s, size_t bytes) {
-    const int dev = stream_device(s);
-    if (dev < 0 || dev >= kMaxDevices) return false;
     if (over_limit(bytes)) return false;
+    s_ = s;
+    const int dev = stream_device(s);
+    if (g_staged_keep.load() <= 0 || (int64_t)bytes > g_staged_keep.load() || dev < 0 ||
+        dev >= kMaxDevices || stream_capturing(s)) {
+      if (hipMallocAsync(&local_, bytes, s) != hipSuccess || local_ == nullptr) {
+        (void)hipGetLastError();
+        local_ = nullptr;
+        return false;
+      }
+      held_ = true;
+      note_call_bytes(bytes);
+      return true;
+    }
     buf_ = &g_staged[dev];
     lk_ = std::unique_lock<std::mutex>(buf_->mu);
-    s_ = s;
     if (buf_->last == nullptr &&
         hipEventCreateWithFlags(&buf_->last, hipEventDisableTiming) != hipSuccess) {
       buf_->last = nullptr;
@@ -286,14 +315,20 @@ class StagedLease {
       buf_->size = bytes;
     }
     held_ = true;
+    note_call_bytes(bytes);
     return true;
   }
-  void* ptr() const { return held_ ? buf_->ptr : nullptr; }
+  void* ptr() const { return !held_ ? nullptr : local_ != nullptr ? local_ : buf_->ptr; }
   void release() {
     if (!held_) return;
     held_ = false;
+    if (local_ != nullptr) {
+      (void)hipFreeAsync(local_, s_);
+      local_ = nullptr;
+      return;
+    }
     if (hipEventRecord(buf_->last, s_) == hipSuccess) buf_->recorded = true;
-    if ((int64_t)buf_->size > g_keep_bytes.load()) {
+    if ((int64_t)buf_->size > g_staged_keep.load()) {
       (void)hipFreeAsync(buf_->ptr, s_);
       buf_->ptr = nullptr;
       buf_->size = 0;
@@ -308,6 +343,7 @@ class StagedLease {
     return false;
   }
   StagedBuffer* buf_ = nullptr;
+  void* local_ = nullptr;
   std::unique_lock<std::mutex> lk_;
   hipStream_t s_ = nullptr;
   bool held_ = false;
@@ -360,6 +396,10 @@ void set_keep_bytes(int64_t keep) {
       (void)hipMemPoolTrimTo(g_pools[d], (size_t)keep);
     }
   }
+}
+
+void set_staged_keep(int64_t keep) {
+  g_staged_keep.store(keep);
   for (int d = 0; d < kMaxDevices; ++d) {
     StagedBuffer& b = g_staged[d];
     std::lock_guard<std::mutex> lk(b.mu);
@@ -412,14 +452,22 @@ struct Workspace {
   bool allocate() {
     if (size == 0) return true;
     if (over_limit(size)) return false;
+    note_call_bytes(size);
     // A stream being captured into a graph (or one whose state cannot be
-    // read) gets plain stream-ordered pool memory: kept blocks are ordered by
-    // events recorded outside any capture.
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    bool cacheable = false;
-    if (hipStreamIsCapturing(s, &cs) == hipSuccess) cacheable = cs == hipStreamCaptureStatusNone;
-    else (void)hipGetLastError();
-    dev = cacheable ? stream_device(s) : -1;
+    // read) gets plain stream-ordered memory, which the capture records as
+    // the graph's own allocation and free: kept blocks are ordered by events
+    // recorded outside any capture, and the pool is not the graph's.
+    if (stream_capturing(s)) {
+      dev = -1;
+      if (hipMallocAsync(&base, size, s) != hipSuccess || base == nullptr) {
+        (void)hipGetLastError();
+        base = nullptr;
+        return false;
+      }
+      cap = size;
+      return true;
+    }
+    dev = stream_device(s);
     if (dev >= 0 && dev < kMaxDevices) {
       BlockCache& c = g_cache[dev];
       std::lock_guard<std::mutex> lk(c.mu);
@@ -492,62 +540,101 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
   return L;
 }
 
-// Workspace pieces of one layer call (offsets into a Workspace).
+// Workspace pieces of one or more layer calls (offsets into a Workspace).
 struct LayerWs {
   size_t bits = 0, steps = 0, part = 0, c = 0, sk = 0;
-  bool has_steps = false, has_sk = false;
-  size_t staged = 0;   // staged path: bytes of per-sample tiles (held in a StagedLease)
+  bool has_bits = false, has_steps = false, has_part = false, has_sk = false;
+  size_t staged = 0;   // staged path (one layer): bytes of per-sample tiles (a StagedLease)
 };
 
-// Reserve what the call needs: row bits and the active-step list when
-// masked, norm partials, clip factors, split-tile accumulate partials.
-LayerWs reserve_layer(const LayerPlan& L, Workspace& ws, bool norm, bool clip, bool accum) {
+// Reserve, in one workspace, what the layers need when their launches
+// follow one another on one stream: row bits and the active-step list when
+// masked (the layers share B, T and the mask), norm partials, clip factors,
+// and the split-tile partials that the norm and accumulate kernels of a
+// layer use one after the other.  Pieces that no two launches use at the
+// same time are shared between the layers at the size of the largest.
+LayerWs reserve_layers(const LayerPlan* const* Ls, int n, Workspace& ws, bool norm, bool clip,
+                       bool accum) {
   LayerWs o;
-  const dpf::LayerArgs& a = L.args;
-  if (a.mask != nullptr) {
-    o.bits = ws.reserve((size_t)a.B * a.nwords * sizeof(uint32_t));
-    if (dpf::big_path(a, L.vec)) {
+  const dpf::LayerArgs& a0 = Ls[0]->args;
+  bool any_big = false;
+  size_t part = 0, sk = 0;
+  for (int l = 0; l < n; ++l) {
+    const LayerPlan& L = *Ls[l];
+    const dpf::LayerArgs& a = L.args;
+    if (dpf::big_path(a, L.vec)) any_big = true;
+    if (norm) part = std::max(part, (size_t)a.B * L.np * sizeof(double));
+    if (L.path == dpf::NormPath::kStaged) continue;   // no split partials: its tiles are staged
+    if (norm) sk = std::max(sk, dpf::norm_workspace_bytes(a, L.path, L.vec));
+    if (accum) sk = std::max(sk, dpf::accumulate_workspace_bytes(a, L.vec));
+  }
+  if (a0.mask != nullptr) {
+    o.has_bits = true;
+    o.bits = ws.reserve((size_t)a0.B * a0.nwords * sizeof(uint32_t));
+    if (any_big) {
       o.has_steps = true;
-      o.steps = ws.reserve(dpf::step_list_words(a.B, a.nwords) * sizeof(uint32_t));
+      o.steps = ws.reserve(dpf::step_list_words(a0.B, a0.nwords) * sizeof(uint32_t));
     }
   }
-  if (norm) o.part = ws.reserve((size_t)a.B * L.np * sizeof(double));
-  if (clip) o.c = ws.reserve((size_t)a.B * sizeof(float));
-  if (L.path == dpf::NormPath::kStaged) {
-    o.staged = dpf::norm_workspace_bytes(a, L.path, L.vec);
-    return o;
+  if (norm) {
+    o.has_part = true;
+    o.part = ws.reserve(part);
   }
-  size_t bytes = 0;   // split-piece partials; the norm and accumulate phases share them
-  if (norm) bytes = dpf::norm_workspace_bytes(a, L.path, L.vec);
-  if (accum) bytes = std::max(bytes, dpf::accumulate_workspace_bytes(a, L.vec));
-  if (bytes != 0) {
+  if (clip) o.c = ws.reserve((size_t)a0.B * sizeof(float));
+  if (sk != 0) {
     o.has_sk = true;
-    o.sk = ws.reserve(bytes);
+    o.sk = ws.reserve(sk);
   }
+  if (n == 1 && Ls[0]->path == dpf::NormPath::kStaged)
+    o.staged = dpf::norm_workspace_bytes(a0, dpf::NormPath::kStaged, Ls[0]->vec);
   return o;
 }
 
-// Once the workspace is allocated: point the layer at its pieces and queue
-// the row bits and the active-step list of a masked call.
-hipError_t bind_layer(LayerPlan& L, const Workspace& ws, const LayerWs& o, hipStream_t s) {
-  dpf::LayerArgs& a = L.args;
-  a.rowbits = nullptr;
-  a.steps = o.has_steps ? ws.at<uint32_t>(o.steps) : nullptr;
-  a.skws = o.has_sk ? ws.at<float>(o.sk) : nullptr;
+LayerWs reserve_layer(const LayerPlan& L, Workspace& ws, bool norm, bool clip, bool accum) {
+  const LayerPlan* one = &L;
+  return reserve_layers(&one, 1, ws, norm, clip, accum);
+}
+
+// Once the workspace is allocated: queue the row bits and the active-step
+// list of a masked call (once for all the layers that share them).
+hipError_t prepare_mask(const dpf::LayerArgs& a, const Workspace& ws, const LayerWs& o,
+                        hipStream_t s) {
   if (a.mask == nullptr) return hipSuccess;
   uint32_t* bits = ws.at<uint32_t>(o.bits);
   hipError_t e = dpf::launch_row_bits(a.mask, a.B, a.T, bits, a.nwords, s);
-  if (e != hipSuccess) return e;
-  a.rowbits = bits;
-  if (o.has_steps) e = dpf::launch_step_list(bits, a.B, a.nwords, ws.at<uint32_t>(o.steps), s);
+  if (e == hipSuccess && o.has_steps)
+    e = dpf::launch_step_list(bits, a.B, a.nwords, ws.at<uint32_t>(o.steps), s);
   return e;
 }
 
-// Accumulate phase of a single-layer call: the staged path combines the
-// tiles its norm phase stored; the others run the scaled contraction.
+// Point a layer at its workspace pieces.
+void point_layer(LayerPlan& L, const Workspace& ws, const LayerWs& o) {
+  dpf::LayerArgs& a = L.args;
+  a.rowbits = o.has_bits ? ws.at<uint32_t>(o.bits) : nullptr;
+  a.steps = o.has_steps && dpf::big_path(a, L.vec) ? ws.at<uint32_t>(o.steps) : nullptr;
+  a.skws = o.has_sk ? ws.at<float>(o.sk) : nullptr;
+  a.partials = o.has_part ? ws.at<double>(o.part) : nullptr;
+}
+
+hipError_t bind_layer(LayerPlan& L, const Workspace& ws, const LayerWs& o, hipStream_t s) {
+  point_layer(L, ws, o);
+  return prepare_mask(L.args, ws, o, s);
+}
+
+// Accumulate phase of a layer: the staged path combines the tiles its norm
+// phase stored; the others run the scaled contraction.
 hipError_t accumulate_phase(const LayerPlan& L, hipStream_t s) {
   if (L.path == dpf::NormPath::kStaged) return dpf::launch_staged_combine(L.args, s);
   return dpf::launch_accumulate(L.args, L.vec, s);
+}
+
+// Norm phase of a bound layer: partials, then their ordered sum into sq
+// (added when accumulate != 0) or, with c != nullptr, the clip factors.
+hipError_t norm_phase(const LayerPlan& L, double* sq, int accumulate, float C, float* c,
+                      float* norms_out, hipStream_t s) {
+  hipError_t e = dpf::launch_norm(L.args, L.path, L.vec, s);
+  if (e != hipSuccess) return e;
+  return dpf::launch_finalize(L.args.partials, L.args.B, L.np, sq, accumulate, C, c, norms_out, s);
 }
 
 dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
@@ -569,25 +656,16 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
   }
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
+  if (L.path == dpf::NormPath::kStaged && !lease.acquire(s, o.staged))
+    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
-  if (L.path == dpf::NormPath::kStaged) {
-    if (!lease.acquire(s, o.staged))
-      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
-    L.args.skws = static_cast<float*>(lease.ptr());
-  }
-  L.args.partials = ws.at<double>(o.part);
-  e = dpf::launch_norm(L.args, L.path, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(lease.ptr());
   float* c = ws.at<float>(o.c);
-  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "norm phase launch");
   L.args.c = c;
-  L.args.noise_std = sigma * C;
-  L.args.seed = seed;
-  L.args.offset = offset;
-  L.args.out = grad_out;
   e = accumulate_phase(L, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
@@ -599,6 +677,20 @@ dpf_status check_clip(float C, float sigma) {
     return fail(DPF_ERR_INVALID_ARGUMENT, "sigma must be finite and >= 0");
   if (!std::isfinite(sigma * C)) return fail(DPF_ERR_INVALID_ARGUMENT, "sigma * C overflows");
   return DPF_OK;
+}
+
+// Philox block ranges [o1, o1 + n1) and [o2, o2 + n2) of one key share a
+// block (the block index wraps modulo 2^64).
+bool blocks_overlap(uint64_t o1, uint64_t n1, uint64_t o2, uint64_t n2) {
+  if (n1 == 0 || n2 == 0) return false;
+  return (uint64_t)(o2 - o1) < n1 || (uint64_t)(o1 - o2) < n2;
+}
+
+uint64_t noise_blocks_of(int64_t n) { return n <= 0 ? 0 : ((uint64_t)n + 3) / 4; }
+
+// Default scale of a seeded projection: entries N(0, 1/r).
+float projection_scale(float p_scale, int64_t r) {
+  return (std::isnan(p_scale) || p_scale <= 0.0f) ? (float)(1.0 / std::sqrt((double)r)) : p_scale;
 }
 
 // Shared body of the projected calls: P read from memory (gen == 0) or
@@ -633,6 +725,9 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   LayerPlan L = plan_layer(&Y, G, mask, true);
   const LayerWs o = reserve_layer(L, ws, true, true, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
+  if (L.path == dpf::NormPath::kStaged && !lease.acquire(s, o.staged))
+    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
   Y.data = ws.at<void>(off_y);
   pa.Y = const_cast<void*>(Y.data);
   pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
@@ -643,19 +738,10 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   L = plan_layer(&Y, G, mask, true);
   e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
-  if (L.path == dpf::NormPath::kStaged) {
-    if (!lease.acquire(s, o.staged))
-      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
-    L.args.skws = static_cast<float*>(lease.ptr());
-  }
-
-  L.args.partials = ws.at<double>(o.part);
-  e = dpf::launch_norm(L.args, L.path, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
+  if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(lease.ptr());
   float* c = ws.at<float>(o.c);
-  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, nullptr, 0, C, c, norms_out, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "norm phase launch");
   L.args.c = c;
   L.args.noise_std = sigma * C;
   L.args.seed = seed;
@@ -675,12 +761,8 @@ dpf_status sqnorms_into(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  L.args.partials = ws.at<double>(o.part);
-  e = dpf::launch_norm(L.args, L.path, L.vec, s);
-  if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-  e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sq, accumulate ? 1 : 0, 1.0f, nullptr,
-                           nullptr, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  e = norm_phase(L, sq, accumulate ? 1 : 0, 1.0f, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "norm phase launch");
   return ok();
 }
 
@@ -745,7 +827,7 @@ extern "C" {
 dpf_status dpfused_linear_clip_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                           float C, float sigma, uint64_t seed, uint64_t offset,
                                           float* grad_out, float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_linear_clip_accumulate");
+  CallScope call_("dpfused_linear_clip_accumulate");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -762,7 +844,7 @@ dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
                                              uint64_t seed, uint64_t offset, float denom,
                                              int32_t accumulate, float* grad_out,
                                              float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_linear_clip_accumulate_ex");
+  CallScope call_("dpfused_linear_clip_accumulate_ex");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -783,7 +865,7 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
                                                     float C, float sigma, uint64_t seed,
                                                     uint64_t offset, float* grad_out,
                                                     float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_linear_clip_accumulate_projected");
+  CallScope call_("dpfused_linear_clip_accumulate_projected");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -801,23 +883,29 @@ dpf_status dpfused_linear_clip_accumulate_projected_seeded(
     const dpf_act* X, const dpf_act* G, const uint8_t* mask, int64_t r, uint64_t p_seed,
     uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
     float* grad_out, float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_linear_clip_accumulate_projected_seeded");
+  CallScope call_("dpfused_linear_clip_accumulate_projected_seeded");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
   if (r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "r must be >= 1");
   if (r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "r too large");
   if (r % 8 != 0) return fail(DPF_ERR_UNSUPPORTED, "r must be a multiple of 8");
-  if (!std::isfinite(p_scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "p_scale must be finite");
+  if (std::isinf(p_scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "p_scale must be finite");
   if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
   if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
-  return projected_layer(X, G, mask, nullptr, 1, p_seed, p_offset, p_scale, r, C, sigma, seed,
-                         offset, grad_out, norms_out, stream);
+  // Noise drawn from the projection's own blocks would be a copy of P's
+  // entries (scaled): anyone who can draw P again would know the noise.
+  if (sigma > 0.0f && seed == p_seed &&
+      blocks_overlap(offset, noise_blocks_of(G->D * r), p_offset, noise_blocks_of(X->D * r)))
+    return fail(DPF_ERR_INVALID_ARGUMENT,
+                "the noise blocks overlap the projection's blocks under the same seed");
+  return projected_layer(X, G, mask, nullptr, 1, p_seed, p_offset, projection_scale(p_scale, r),
+                         r, C, sigma, seed, offset, grad_out, norms_out, stream);
 }
 
 dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                       double* sqnorms_out, int32_t accumulate, void* stream) {
-  TraceRange trace_("dpfused_per_sample_sqnorms");
+  CallScope call_("dpfused_per_sample_sqnorms");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if (sqnorms_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms_out is NULL");
@@ -826,7 +914,7 @@ dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const 
 
 dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float* c_out,
                                 float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_clip_factors");
+  CallScope call_("dpfused_clip_factors");
   if (sqnorms == nullptr || c_out == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "sqnorms and c_out must not be NULL");
   if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
@@ -840,7 +928,7 @@ dpf_status dpfused_clip_factors(const double* sqnorms, int64_t n, float C, float
 dpf_status dpfused_scaled_accumulate(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
                                      const float* c, float noise_std, uint64_t seed,
                                      uint64_t offset, float* grad_out, void* stream) {
-  TraceRange trace_("dpfused_scaled_accumulate");
+  CallScope call_("dpfused_scaled_accumulate");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if (c == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "c is NULL");
@@ -857,7 +945,7 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
                                                uint64_t seed, uint64_t offset, float* grad_out,
                                                float* bias_grad_out, float* norms_out,
                                                void* stream) {
-  TraceRange trace_("dpfused_linear_clip_accumulate_bias");
+  CallScope call_("dpfused_linear_clip_accumulate_bias");
   dpf_status st = check_pair(X, G);
   if (st != DPF_OK) return st;
   if ((st = check_clip(C, sigma)) != DPF_OK) return st;
@@ -868,57 +956,43 @@ dpf_status dpfused_linear_clip_accumulate_bias(const dpf_act* X, const dpf_act* 
     return fail(DPF_ERR_UNSUPPORTED, "bias_grad_out is not 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t B = X->B, dout = G->D;
+  // Everything the call needs is reserved, and allocated, before the first
+  // launch: a failed allocation leaves every output untouched.
   Workspace ws(s);
   const size_t off_sq = ws.reserve((size_t)B * sizeof(double));
   const size_t off_c = ws.reserve((size_t)B * sizeof(float));
   const size_t off_gb = ws.reserve((size_t)B * dout * sizeof(float));
   const size_t off_part = ws.reserve(dpf::bias_workspace_bytes((int)B, (int)G->T, (int)dout));
+  LayerPlan L = plan_layer(X, G, mask, true);
+  const LayerWs o = reserve_layer(L, ws, true, false, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  // On the staged path the weight's per-sample tiles are kept until the
+  // clip factors (which need the bias's norms too) exist.
+  StagedLease lease;
+  if (L.path == dpf::NormPath::kStaged && !lease.acquire(s, o.staged))
+    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
   double* sq = ws.at<double>(off_sq);
   float* c = ws.at<float>(off_c);
   float* gb = ws.at<float>(off_gb);
-  // On the staged path the weight's per-sample tiles are kept until the
-  // clip factors (which need the bias's norms too) exist.
-  LayerPlan L = plan_layer(X, G, mask, true);
-  const bool staged = L.path == dpf::NormPath::kStaged;
-  Workspace lws(s);
-  StagedLease lease;
-  hipError_t e = hipSuccess;
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(lease.ptr());
   // ||g_i||^2 of the weight, then + ||gb_i||^2 of the bias
-  if (staged) {
-    const LayerWs o = reserve_layer(L, lws, true, false, false);
-    if (!lws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-    if ((e = bind_layer(L, lws, o, s)) != hipSuccess) return hip_fail(e, "mask preparation launch");
-    if (!lease.acquire(s, o.staged))
-      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
-    L.args.skws = static_cast<float*>(lease.ptr());
-    L.args.partials = lws.at<double>(o.part);
-    if ((e = dpf::launch_norm(L.args, L.path, L.vec, s)) != hipSuccess)
-      return hip_fail(e, "norm kernel launch");
-    e = dpf::launch_finalize(L.args.partials, L.args.B, L.np, sq, 0, 1.0f, nullptr, nullptr, s);
-    if (e != hipSuccess) return hip_fail(e, "finalize launch");
-  } else if ((st = sqnorms_into(X, G, mask, sq, 0, s)) != DPF_OK) {
-    return st;
-  }
+  if ((e = norm_phase(L, sq, 0, 1.0f, nullptr, nullptr, s)) != hipSuccess)
+    return hip_fail(e, "norm phase launch");
   e = dpf::launch_bias_grads(to_act(G), G->dtype, (int)B, (int)G->T, (int)dout, mask,
                              ws.at<float>(off_part), gb, sq, s);
   if (e != hipSuccess) return hip_fail(e, "bias gradient launch");
   e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "clip factor launch");
-  if (staged) {
-    L.args.c = c;
-    L.args.noise_std = sigma * C;
-    L.args.seed = seed;
-    L.args.offset = offset;
-    L.args.out = grad_out;
-    if ((e = dpf::launch_staged_combine(L.args, s)) != hipSuccess)
-      return hip_fail(e, "accumulate launch");
-  } else if ((st = accumulate_with(X, G, mask, c, sigma * C, seed, offset, grad_out, s)) !=
-             DPF_OK) {
-    return st;
-  }
+  L.args.c = c;
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  if ((e = accumulate_phase(L, s)) != hipSuccess) return hip_fail(e, "accumulate launch");
   // the bias noise continues the weight's Philox stream
-  const uint64_t boff = offset + (uint64_t)((dout * X->D + 3) / 4);
+  const uint64_t boff = offset + noise_blocks_of(dout * X->D);
   e = dpf::launch_bias_accumulate(gb, c, (int)B, (int)dout, sigma * C, seed, boff, bias_grad_out,
                                   s);
   if (e != hipSuccess) return hip_fail(e, "bias accumulate launch");
@@ -929,7 +1003,7 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
                                          const uint8_t* mask, float C, float sigma, uint64_t seed,
                                          const uint64_t* offsets, float* const* grad_out,
                                          float* norms_out, void* stream) {
-  TraceRange trace_("dpfused_group_clip_accumulate");
+  CallScope call_("dpfused_group_clip_accumulate");
   if (n < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 1");
   if (X == nullptr || G == nullptr || offsets == nullptr || grad_out == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "X, G, offsets and grad_out must not be NULL");
@@ -943,80 +1017,78 @@ dpf_status dpfused_group_clip_accumulate(int32_t n, const dpf_act* X, const dpf_
     if (!aligned16(grad_out[l]))
       return fail(DPF_ERR_UNSUPPORTED, "grad_out[l] is not 16-byte aligned");
   }
+  // With noise, two linears drawing the same Philox blocks would carry the
+  // same normals, which cancel when their outputs are subtracted.
+  if (sigma > 0.0f) {
+    for (int32_t l = 0; l < n; ++l)
+      for (int32_t m = l + 1; m < n; ++m)
+        if (blocks_overlap(offsets[l], noise_blocks_of(X[l].D * G[l].D), offsets[m],
+                           noise_blocks_of(X[m].D * G[m].D)))
+          return fail(DPF_ERR_INVALID_ARGUMENT,
+                      "the noise block ranges of two linears overlap (offsets[l] .. offsets[l] + "
+                      "dpfused_noise_blocks(dout_l * din_l) must be disjoint)");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t B = X[0].B;
+  // Plan every linear.  A linear on the staged path keeps its per-sample
+  // tiles, at its own place in one staged buffer, from its norm phase until
+  // its accumulate phase (after the group's clip factors exist).  The group's
+  // staged tiles stay within the per-call limit; the linears past it take
+  // their two-pass path.
+  std::vector<LayerPlan> lin((size_t)n);
+  std::vector<size_t> at((size_t)n, 0);
+  size_t staged_total = 0;
+  for (int32_t l = 0; l < n; ++l) {
+    LayerPlan& L = lin[(size_t)l];
+    L = plan_layer(&X[l], &G[l], mask, true);
+    if (L.path != dpf::NormPath::kStaged) continue;
+    const size_t bytes = dpf::staged_big_workspace_bytes(L.args);
+    if ((double)(staged_total + bytes) > kStagedMaxBytes) {
+      L = plan_layer(&X[l], &G[l], mask, false);
+      continue;
+    }
+    at[(size_t)l] = staged_total;
+    staged_total = (staged_total + bytes + 255) & ~(size_t)255;
+  }
+  // One workspace for the whole group, taken before the first launch: a
+  // failed allocation leaves every output untouched.
   Workspace ws(s);
   const size_t off_sq = ws.reserve((size_t)B * sizeof(double));
   const size_t off_c = ws.reserve((size_t)B * sizeof(float));
+  std::vector<const LayerPlan*> plans((size_t)n);
+  for (int32_t l = 0; l < n; ++l) plans[(size_t)l] = &lin[(size_t)l];
+  const LayerWs o = reserve_layers(plans.data(), n, ws, true, false, true);
   if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  StagedLease lease;
+  if (staged_total != 0 && !lease.acquire(s, staged_total))
+    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
   double* sq = ws.at<double>(off_sq);
   float* c = ws.at<float>(off_c);
-  // A linear on the staged path keeps its per-sample tiles, in a workspace of
-  // its own, from its norm phase until its accumulate phase (after the
-  // group's clip factors exist).  The group's staged tiles stay within the
-  // per-call limit; the linears past it take their two-pass path.
-  struct StagedLinear {
-    LayerPlan L;
-    std::unique_ptr<Workspace> ws;
-    size_t at = 0;   // offset of its tiles in the staged buffer
-    bool on = false;
-  };
-  std::vector<StagedLinear> lin((size_t)n);
-  size_t staged_total = 0;
+  hipError_t e = prepare_mask(lin[0].args, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
   for (int32_t l = 0; l < n; ++l) {
-    StagedLinear& z = lin[(size_t)l];
-    z.L = plan_layer(&X[l], &G[l], mask, true);
-    if (z.L.path != dpf::NormPath::kStaged) continue;
-    const size_t bytes = dpf::staged_big_workspace_bytes(z.L.args);
-    if ((double)(staged_total + bytes) > kStagedMaxBytes) continue;
-    z.at = staged_total;
-    staged_total = (staged_total + bytes + 255) & ~(size_t)255;
-    z.ws.reset(new Workspace(s));
-    const LayerWs o = reserve_layer(z.L, *z.ws, true, false, false);
-    if (!z.ws->allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-    hipError_t e = bind_layer(z.L, *z.ws, o, s);
-    if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-    z.L.args.partials = z.ws->at<double>(o.part);
-    z.on = true;
-  }
-  StagedLease lease;
-  if (staged_total != 0) {
-    if (!lease.acquire(s, staged_total))
-      return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
-    for (auto& z : lin)
-      if (z.on) z.L.args.skws = reinterpret_cast<float*>(static_cast<char*>(lease.ptr()) + z.at);
+    LayerPlan& L = lin[(size_t)l];
+    point_layer(L, ws, o);
+    if (L.path == dpf::NormPath::kStaged)
+      L.args.skws = reinterpret_cast<float*>(static_cast<char*>(lease.ptr()) + at[(size_t)l]);
   }
   // norm phase of every linear: n_i^2 summed over the group
   for (int32_t l = 0; l < n; ++l) {
-    StagedLinear& z = lin[(size_t)l];
-    if (!z.on) {
-      if ((st = sqnorms_into(&X[l], &G[l], mask, sq, l > 0, s)) != DPF_OK) return st;
-      continue;
-    }
-    hipError_t e = dpf::launch_norm(z.L.args, z.L.path, z.L.vec, s);
-    if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
-    e = dpf::launch_finalize(z.L.args.partials, z.L.args.B, z.L.np, sq, l > 0 ? 1 : 0, 1.0f,
-                             nullptr, nullptr, s);
-    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    if ((e = norm_phase(lin[(size_t)l], sq, l > 0 ? 1 : 0, 1.0f, nullptr, nullptr, s)) !=
+        hipSuccess)
+      return hip_fail(e, "norm phase launch");
   }
-  hipError_t e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
+  e = dpf::launch_clip_from_sq(sq, B, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "clip factor launch");
   // accumulate phase of every linear with the group's factors
   for (int32_t l = 0; l < n; ++l) {
-    StagedLinear& z = lin[(size_t)l];
-    if (!z.on) {
-      if ((st = accumulate_with(&X[l], &G[l], mask, c, sigma * C, seed, offsets[l], grad_out[l],
-                                s)) != DPF_OK)
-        return st;
-      continue;
-    }
-    z.L.args.c = c;
-    z.L.args.noise_std = sigma * C;
-    z.L.args.seed = seed;
-    z.L.args.offset = offsets[l];
-    z.L.args.out = grad_out[l];
-    e = dpf::launch_staged_combine(z.L.args, s);
-    if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+    LayerPlan& L = lin[(size_t)l];
+    L.args.c = c;
+    L.args.noise_std = sigma * C;
+    L.args.seed = seed;
+    L.args.offset = offsets[l];
+    L.args.out = grad_out[l];
+    if ((e = accumulate_phase(L, s)) != hipSuccess) return hip_fail(e, "accumulate launch");
   }
   return ok();
 }
@@ -1026,7 +1098,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
                                        float lr, float beta1, float beta2, float eps,
                                        const void* P, int32_t p_dtype, uint64_t p_seed,
                                        uint64_t p_offset, float p_scale, void* stream) {
-  TraceRange trace_("dpfused_projected_adam_step");
+  CallScope call_("dpfused_projected_adam_step");
   if (grad == nullptr || m == nullptr || v == nullptr || W == nullptr)
     return fail(DPF_ERR_INVALID_ARGUMENT, "grad, m, v and W must not be NULL");
   if (dout < 1 || din < 1 || r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "dout, din, r must be >= 1");
@@ -1039,7 +1111,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
     return fail(DPF_ERR_INVALID_ARGUMENT, "beta1 and beta2 must be in [0, 1)");
   if (!std::isfinite(eps) || !(eps > 0.0f)) return fail(DPF_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
   if (p_dtype != DPF_F32 && p_dtype != DPF_BF16) return fail(DPF_ERR_UNSUPPORTED, "unknown P dtype");
-  if (P == nullptr && !std::isfinite(p_scale))
+  if (P == nullptr && std::isinf(p_scale))
     return fail(DPF_ERR_INVALID_ARGUMENT, "p_scale must be finite");
   if (!aligned16(grad) || !aligned16(m) || !aligned16(v) || !aligned16(W) ||
       (P != nullptr && !aligned16(P)))
@@ -1066,7 +1138,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
   a.gen = P == nullptr ? 1 : 0;
   a.p_seed = p_seed;
   a.p_offset = p_offset;
-  a.p_scale = p_scale;
+  a.p_scale = P == nullptr ? projection_scale(p_scale, r) : p_scale;
   Workspace ws(s);
   const size_t off_u = ws.reserve((size_t)dout * r * sizeof(float));
   const bool pbuf = dpf::adam_draws_p_once(a);
@@ -1081,7 +1153,7 @@ dpf_status dpfused_projected_adam_step(const float* grad, float* m, float* v, fl
 
 dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks, uint32_t* out,
                                  void* stream) {
-  TraceRange trace_("dpfused_philox4x32_10");
+  CallScope call_("dpfused_philox4x32_10");
   if (nblocks < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "nblocks must be >= 0");
   if (nblocks == 0) return ok();
   if (out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -1093,7 +1165,7 @@ dpf_status dpfused_philox4x32_10(uint64_t seed, uint64_t offset, int64_t nblocks
 
 dpf_status dpfused_gaussian_fill(uint64_t seed, uint64_t offset, int64_t n, float scale,
                                  int32_t dtype, void* out, void* stream) {
-  TraceRange trace_("dpfused_gaussian_fill");
+  CallScope call_("dpfused_gaussian_fill");
   if (n < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be >= 0");
   if (dtype != DPF_F32 && dtype != DPF_BF16) return fail(DPF_ERR_UNSUPPORTED, "unknown dtype");
   if (!std::isfinite(scale)) return fail(DPF_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -1123,9 +1195,19 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
     set_keep_bytes(value);
     return ok();
   }
+  if (std::strcmp(name, "staged_keep_bytes") == 0) {
+    if (value < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "staged_keep_bytes must be >= 0");
+    set_staged_keep(value);
+    return ok();
+  }
   if (std::strcmp(name, "workspace_limit_bytes") == 0) {
     if (value < 0) return fail(DPF_ERR_INVALID_ARGUMENT, "workspace_limit_bytes must be >= 0");
     g_ws_limit.store(value);
+    return ok();
+  }
+  if (std::strcmp(name, "workspace_call_high") == 0) {
+    if (value != 0) return fail(DPF_ERR_INVALID_ARGUMENT, "workspace_call_high can only be reset to 0");
+    g_call_high.store(0);
     return ok();
   }
   if (std::strcmp(name, "p_in_kernels") == 0) {
@@ -1152,6 +1234,9 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
   if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
   if (std::strcmp(name, "workspace_limit_bytes") == 0) return g_ws_limit.load();
+  if (std::strcmp(name, "staged_keep_bytes") == 0) return g_staged_keep.load();
+  if (std::strcmp(name, "workspace_call_bytes") == 0) return t_call_bytes;
+  if (std::strcmp(name, "workspace_call_high") == 0) return g_call_high.load();
   if (std::strcmp(name, "p_in_kernels") == 0) return dpf::p_in_kernels() ? 1 : 0;
   if (std::strcmp(name, "trace") == 0) return g_trace.load();
   if (std::strcmp(name, "debug") == 0) return g_debug.load();

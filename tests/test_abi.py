@@ -5,6 +5,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sample_gradient_clipping_amd import _lib
@@ -67,7 +68,7 @@ def test_options(L):
     assert L.dpfused_set_option(b"norm_path", 4) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"norm_path", -1) == DPF_ERR_INVALID_ARGUMENT
     keep = L.dpfused_get_option(b"workspace_keep_bytes")
-    assert keep == 16 << 30
+    assert keep == 512 << 20
     assert L.dpfused_set_option(b"workspace_keep_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"workspace_keep_bytes", 1 << 20) == DPF_OK
     assert L.dpfused_get_option(b"workspace_keep_bytes") == 1 << 20
@@ -194,7 +195,8 @@ def test_seeded_projected_argument_checks(L):
                                                       scale, C, 1.0, 0, 0, out, None, None)
     assert f(*args(r=0)) == DPF_ERR_INVALID_ARGUMENT
     assert f(*args(r=12)) == DPF_ERR_UNSUPPORTED             # not a multiple of 8
-    assert f(*args(scale=math.nan)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(scale=math.inf)) == DPF_ERR_INVALID_ARGUMENT
+    assert f(*args(scale=-math.inf)) == DPF_ERR_INVALID_ARGUMENT
     assert f(*args(C=0.0)) == DPF_ERR_INVALID_ARGUMENT
     assert f(*args(out=0)) == DPF_ERR_INVALID_ARGUMENT
     assert f(*args(out=FAKE + 4)) == DPF_ERR_UNSUPPORTED
@@ -253,7 +255,7 @@ def test_projected_adam_argument_checks(L):
     assert call(eps=0.0) == DPF_ERR_INVALID_ARGUMENT
     assert call(lr=math.inf) == DPF_ERR_INVALID_ARGUMENT
     assert call(pdt=9) == DPF_ERR_UNSUPPORTED
-    assert call(P=None, scale=math.nan) == DPF_ERR_INVALID_ARGUMENT
+    assert call(P=None, scale=math.inf) == DPF_ERR_INVALID_ARGUMENT
     assert call(m=FAKE + 4) == DPF_ERR_UNSUPPORTED
 
 
@@ -295,3 +297,89 @@ def test_product_path_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_seeded_projection_rejects_noise_drawn_from_its_blocks(L):
+    """With sigma > 0 the noise must not reuse the projection's Philox blocks under the
+    same seed: the noise would then be a scaled copy of P's entries."""
+    X, G = _act(D=16), _act(D=8)                 # din = 16, dout = 8, r = 8
+    f = L.dpfused_linear_clip_accumulate_projected_seeded
+
+    def call(p_seed, p_off, seed, off, sigma=1.0):
+        return f(ctypes.byref(X), ctypes.byref(G), None, 8, p_seed, p_off, math.nan, 1.0, sigma,
+                 seed, off, FAKE, None, None)
+    # P uses blocks [p_off, p_off + 32); the noise [off, off + 16)
+    assert call(7, 0, 7, 0) == DPF_ERR_INVALID_ARGUMENT
+    assert b"overlap" in L.dpfused_last_error()
+    assert call(7, 0, 7, 31) == DPF_ERR_INVALID_ARGUMENT
+    assert call(7, 20, 7, 5) == DPF_ERR_INVALID_ARGUMENT
+    assert call(0, 0, 0, 0) == DPF_ERR_INVALID_ARGUMENT      # the all-default seeds
+    # the range wraps modulo 2^64
+    assert call(7, 2 ** 64 - 4, 7, 10) == DPF_ERR_INVALID_ARGUMENT
+
+
+def test_group_rejects_overlapping_noise_ranges(L):
+    n = 3
+    Xs = (DpfAct * n)(_act(D=16), _act(D=16), _act(D=8))
+    Gs = (DpfAct * n)(_act(D=16), _act(D=8), _act(D=8))       # 64, 32 and 16 noise blocks
+    outs = (ctypes.c_void_p * n)(FAKE, FAKE, FAKE)
+    f = L.dpfused_group_clip_accumulate
+    for bad in ([0, 0, 200], [0, 63, 200], [0, 64, 95], [100, 0, 20], [0, 2 ** 64 - 8, 500]):
+        offs = (ctypes.c_uint64 * n)(*bad)
+        assert f(n, Xs, Gs, None, 1.0, 0.5, 0, offs, outs, None, None) == \
+            DPF_ERR_INVALID_ARGUMENT, bad
+        assert b"overlap" in L.dpfused_last_error()
+
+
+def test_binding_default_group_offsets_are_disjoint():
+    import sample_gradient_clipping_amd as dp
+    shapes = [(5120, 5120), (13824, 5120), (7, 3), (1, 1), (2, 2)]
+    offs = dp.consecutive_offsets(shapes)
+    assert offs[0] == 0
+    for l in range(1, len(shapes)):
+        assert offs[l] == offs[l - 1] + dp_noise_blocks(shapes[l - 1][0] * shapes[l - 1][1])
+    assert dp.consecutive_offsets([(3, 3)], start=9) == [9]
+
+
+def dp_noise_blocks(n):
+    return (n + 3) // 4
+
+
+def test_binding_checks_caller_outputs():
+    """Outputs the caller passes are written through raw pointers: the binding checks
+    dtype, exact shape, contiguity and device before any call."""
+    torch = pytest.importorskip("torch")
+    import sample_gradient_clipping_amd as dp
+    chk = dp._check_out
+    dev = torch.device("cpu")
+    good = torch.empty((4, 6), dtype=torch.float32)
+    chk(good, (4, 6), "grad_out", dev)
+    with pytest.raises(ValueError, match="float32"):
+        chk(good.to(torch.bfloat16), (4, 6), "grad_out", dev)
+    with pytest.raises(ValueError, match="shape"):
+        chk(good, (6, 4), "grad_out", dev)
+    with pytest.raises(ValueError, match="shape"):
+        chk(good.reshape(24), (4, 6), "grad_out", dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        chk(torch.empty((6, 4)).t(), (4, 6), "grad_out", dev)
+    with pytest.raises(ValueError, match="on"):
+        chk(torch.empty((4, 6), device="meta"), (4, 6), "grad_out", dev)
+    with pytest.raises(TypeError):
+        chk(np.zeros((4, 6), np.float32), (4, 6), "grad_out", dev)
+    with pytest.raises(ValueError, match="float64"):
+        chk(torch.empty(4), (4,), "out", dev, torch.float64)
+    with pytest.raises(ValueError, match="on"):
+        dp._same_device(torch.empty(2, device="meta"), dev, "G")
+
+
+def test_memory_options(L):
+    assert L.dpfused_get_option(b"staged_keep_bytes") == 0
+    assert L.dpfused_get_option(b"workspace_keep_bytes") == 512 << 20
+    assert L.dpfused_set_option(b"staged_keep_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"workspace_call_high", 5) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"workspace_call_high", 0) == DPF_OK
+    assert L.dpfused_get_option(b"workspace_call_high") == 0
+    assert L.dpfused_get_option(b"workspace_call_bytes") >= 0
+    assert L.dpfused_set_option(b"staged_keep_bytes", 1 << 30) == DPF_OK
+    assert L.dpfused_get_option(b"staged_keep_bytes") == 1 << 30
+    assert L.dpfused_set_option(b"staged_keep_bytes", 0) == DPF_OK

@@ -159,13 +159,14 @@ def test_gram_direct_and_staged_paths_agree():
 
 
 @pytest.mark.parametrize("shape,expect", [
-    ((8, 2048, 5120, 5120), "staged_norm"),   # Llama-13B q: staging the tiles beats a second pass
+    ((8, 2048, 5120, 5120), "gram_norm"),     # Llama-13B q: T^2 (din + dout) < T din dout
     ((8, 512, 5120, 5120), "gram_norm"),      # short sequences: the Gram phase is cheap
-    ((32, 512, 768, 3072), "staged_norm"),    # GPT-2 MLP
-    ((32, 128, 256, 4096), "direct_norm"),    # RoBERTa fc1 in r-space: few flops per staged byte
+    ((32, 512, 768, 3072), "direct_norm"),    # GPT-2 MLP: padded Gram blocks cost more
+    ((32, 128, 256, 4096), "direct_norm"),    # RoBERTa fc1 in r-space
     ((4, 16, 64, 32), "tiny_layer"),          # one workgroup does the whole step
 ])
 def test_automatic_norm_path_choice(shape, expect):
+    """The automatic choice is always a form that stores no per-sample gradient."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
     B, T, din, dout = shape
@@ -180,13 +181,15 @@ def test_automatic_norm_path_choice(shape, expect):
         dp.set_option("timing", 0)
         dp.timing_reset()
     assert expect in t, sorted(t)
+    assert "staged_norm" not in t and "staged_combine" not in t
 
 
 @pytest.mark.parametrize("keep", [16 << 30, 0])
 def test_staged_calls_alternating_streams_match_one_stream(keep):
-    """Calls on two streams share the device's staged-tile buffer in turn:
-    results equal the one-stream results bit for bit, also when the buffer
-    is freed after every call (keep = 0)."""
+    """Staged calls on two streams: with a kept buffer (keep = 16 GiB) they
+    share it in turn; with none (keep = 0, the default) each call takes and
+    gives back its own tiles.  Results equal the one-stream results bit for
+    bit either way."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
     rng = np.random.default_rng(27)
@@ -195,9 +198,9 @@ def test_staged_calls_alternating_streams_match_one_stream(keep):
     for B, T, din, dout in shapes:
         lin = random_linear(rng, B, T, din, dout)
         data.append((to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)))
-    old_keep = dp.get_option("workspace_keep_bytes")
+    old_keep = dp.get_option("staged_keep_bytes")
     dp.set_option("norm_path", 3)
-    dp.set_option("workspace_keep_bytes", keep)
+    dp.set_option("staged_keep_bytes", keep)
     try:
         ref = [dp.linear_clip_accumulate(X, G, None, C=0.05, sigma=0.7, seed=9, offset=i)
                for i, (X, G) in enumerate(data)]
@@ -219,7 +222,48 @@ def test_staged_calls_alternating_streams_match_one_stream(keep):
                 assert torch.equal(o, ro) and torch.equal(n, rn)
     finally:
         dp.set_option("norm_path", 0)
-        dp.set_option("workspace_keep_bytes", old_keep)
+        dp.set_option("staged_keep_bytes", old_keep)
+
+
+@pytest.mark.parametrize("path", [0, 3])
+def test_graph_capture_replays_match_eager(path):
+    """A call captured into a HIP graph (the library then takes
+    graph-owned workspace and, on the staged path, graph-owned tiles) and
+    replayed several times, with eager calls on the same data in between:
+    every replay equals the eager result bit for bit."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(31)
+    lin = random_linear(rng, 3, 300, 520, 776, masked=(path == 0))
+    X, G, m = _dev(lin, torch)
+    dp.set_option("norm_path", path)
+    try:
+        ref, ref_n = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9, offset=4)
+        out = torch.empty_like(ref)
+        norms = torch.empty_like(ref_n)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9, offset=4,
+                                          grad_out=out, norms_out=norms)
+        torch.cuda.synchronize()
+        for it in range(3):
+            out.fill_(float(it) - 5.0)
+            norms.fill_(-1.0)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref) and torch.equal(norms, ref_n), it
+            eager, eager_n = dp.linear_clip_accumulate(X, G, m, C=0.05, sigma=0.7, seed=9,
+                                                       offset=4)
+            torch.cuda.synchronize()
+            assert torch.equal(eager, ref) and torch.equal(eager_n, ref_n)
+        del graph
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
 
 
 @pytest.mark.parametrize("path", [1, 2])

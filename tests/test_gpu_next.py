@@ -97,7 +97,7 @@ def test_group_clip_matches_oracle(dtype):
     B, T = 3, 300
     lins, mask = _group_case(rng, B, T, dims, [300, 150, 37], dtype)
     pairs = [(l.X, l.G) for l in lins]
-    offsets = [0, 1000, 5000]
+    offsets = dp.consecutive_offsets([(dout, din) for din, dout in dims], start=1000)
     _, rn, _ = dp_linear.oracle_group(pairs, mask, 1.0, 0.0, 0, offsets, dtype)
     C = float(np.median(rn))               # some samples clip, some do not
     Xs = [to_dev(l.X, dtype, torch) for l in lins]
@@ -106,7 +106,7 @@ def test_group_clip_matches_oracle(dtype):
     sum_tol = SUM_TOL_BF16 if dtype == "bf16" else 1e-4
     for sigma, tol in ((0.0, sum_tol), (1.1, AGG_TOL_BF16 if dtype == "bf16" else 1e-4)):
         outs, norms = dp.group_clip_accumulate(Xs, Gs, m, C=C, sigma=sigma, seed=3,
-                                               offsets=offsets[:len(lins)])
+                                               offsets=offsets)
         refs, rn, rc = dp_linear.oracle_group(pairs, mask, C, sigma, 3, offsets, dtype)
         assert (rc == 1).any() and (rc < 1).any()
         assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
@@ -138,7 +138,7 @@ def test_group_clip_unmasked_matches_oracle(path):
     dims = [(512, 640), (640, 512), (256, 1024)]
     lins, mask = _group_case(rng, 3, 300, dims, None)
     pairs = [(l.X, l.G) for l in lins]
-    offsets = [0, 1000, 5000]
+    offsets = dp.consecutive_offsets([(dout, din) for din, dout in dims])
     _, rn, _ = dp_linear.oracle_group(pairs, None, 1.0, 0.0, 0, offsets, "bf16")
     C = float(np.median(rn))
     Xs = [to_dev(l.X, "bf16", torch) for l in lins]

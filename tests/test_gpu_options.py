@@ -79,6 +79,50 @@ def test_workspace_limit_group_and_bias():
         _group_and_bias(torch, dp)
 
 
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_workspace_limit_just_below_the_call_leaves_outputs(path):
+    """Masked group and bias calls on the two-pass paths: a limit one byte
+    below what the call takes fails before anything is written (the call
+    takes all its workspace before its first launch), and a limit equal to
+    it lets the call run."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    X, G = _inputs(torch)
+    X2, G2 = _inputs(torch, seed=6, shape=(4, 256, 768, 256))
+    mask = torch.ones(X.shape[:2], dtype=torch.uint8, device="cuda")
+    mask[1, 100:] = 0
+    mask[3, :] = 0
+    offs = dp.consecutive_offsets([(768, 768), (256, 768)])
+    calls = {
+        "group": lambda outs: dp.group_clip_accumulate(
+            [X, X2], [G, G2], mask, C=0.5, sigma=0.3, seed=3, offsets=offs,
+            grad_outs=outs[:2], norms_out=outs[2]),
+        "bias": lambda outs: dp.linear_clip_accumulate_bias(
+            X, G, mask, C=0.5, sigma=0.3, seed=3, grad_out=outs[0], bias_grad_out=outs[1],
+            norms_out=outs[2]),
+    }
+    with _Options(norm_path=path):
+        for name, call in calls.items():
+            shapes = [(768, 768), (256, 768), (4,)] if name == "group" else \
+                [(768, 768), (768,), (4,)]
+            ref = [torch.empty(sh, device="cuda") for sh in shapes]
+            call(ref)
+            torch.cuda.synchronize()
+            need = dp.get_option("workspace_call_bytes")
+            assert need > 0
+            outs = [torch.full(sh, 7.0, device="cuda") for sh in shapes]
+            with _Options(workspace_limit_bytes=need - 1):
+                with pytest.raises(dp.DpfError) as e:
+                    call(outs)
+                assert e.value.status == DPF_ERR_OUT_OF_MEMORY
+            torch.cuda.synchronize()
+            assert all(torch.all(o == 7.0) for o in outs), name
+            with _Options(workspace_limit_bytes=need):
+                call(outs)
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(outs, ref)), name
+
+
 def _group_and_bias(torch, dp):
     X, G = _inputs(torch)
     X2, G2 = _inputs(torch, seed=6, shape=(4, 256, 768, 256))
