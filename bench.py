@@ -150,19 +150,33 @@ class ClockSampler:
                 "max_mhz": max(self.mhz), "mean_mhz": round(sum(self.mhz) / len(self.mhz))}
 
 
-def time_calls(torch, fn, steps, warmup):
-    """Average milliseconds per call of fn() over `steps` calls (events on the current stream)."""
+def time_calls(torch, fn, steps, warmup, min_ms=20.0, warm_ms=100.0):
+    """Average milliseconds per call of fn() (events on the current stream).
+
+    Warm-up: `warmup` calls, then more until about warm_ms of wall time has
+    passed, so that a GPU idle before (clock down) has reached its working
+    clock.  Timed: `steps` calls, or more for short calls, so that the timed
+    region spans at least min_ms."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_warm = 0
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(16):
+            fn()
+        n_warm += 16
+        torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) * 1e3 / n_warm
+    reps = max(steps, int(min_ms / max(per_call, 1e-4)) + 1)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
+    for _ in range(reps):
         fn()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / reps
 
 
 def call_memory(dp):
@@ -533,10 +547,10 @@ def main():
             X, G, None, C=lin.C, sigma=lin.sigma, seed=lin.seed, offset=lin.offset,
             grad_out=out, norms_out=norms)
         paths.append(norm_path_of(dp, call))
-        ms = time_calls(torch, call, args.steps, 2)
+        ms = time_calls(torch, call, args.steps, 2, warm_ms=0.0)
         Gt = G.reshape(-1, lin.dout).t().contiguous()
         X2 = X.reshape(-1, lin.din)
-        ms_gemm = time_calls(torch, lambda: torch.matmul(Gt, X2), args.steps, 2)
+        ms_gemm = time_calls(torch, lambda: torch.matmul(Gt, X2), args.steps, 2, warm_ms=0.0)
         del Gt
         f = 2.0 * lin.B * lin.T * lin.din * lin.dout
         per_linear.append({"linear": lin.name, "din": lin.din, "dout": lin.dout,
@@ -665,7 +679,7 @@ def main():
         dp.set_option("norm_path", 3)
         try:
             smem = call_memory(dp)
-            ms_staged = time_calls(torch, step, args.steps, 2)
+            ms_staged = time_calls(torch, step, args.steps, 2, warm_ms=0.0)
             staged_extra = smem()
             spaths = [norm_path_of(dp, lambda l=l, d=d: dp.linear_clip_accumulate(
                 d[0], d[1], None, C=l.C, sigma=l.sigma, seed=l.seed, offset=l.offset,
@@ -689,7 +703,7 @@ def main():
     offs = dp.consecutive_offsets([(l.dout, l.din) for l in lins])
     gmem = call_memory(dp)
     ms_group = time_calls(torch, lambda: dp.group_clip_accumulate(
-        Xs, Gs, None, C=1.0, sigma=1.0, offsets=offs, grad_outs=outs), args.steps, 2)
+        Xs, Gs, None, C=1.0, sigma=1.0, offsets=offs, grad_outs=outs), args.steps, 2, warm_ms=0.0)
     res["group_clip_layer"] = {
         "note": "the same seven linears, clipped jointly (one c_i per sample over the layer)",
         "ms": round(ms_group, 4), "useful_tflops": round(useful / (ms_group * 1e-3) / 1e12, 2),

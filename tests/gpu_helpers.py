@@ -67,3 +67,40 @@ def random_linear(rng, B, T, din, dout, dtype="bf16", masked=False, C=1.0, sigma
     if dtype == "bf16":
         X, G = f32_to_bf16_bits(X), f32_to_bf16_bits(G)
     return Linear("rand", X, G, mask, C, sigma, seed, offset, dtype)
+
+
+# Element-wise bounds (in addition to the stated relative-Frobenius ones):
+# a sigma = 0 output against the oracle, max|got - ref| <= tol * max|ref|,
+# with tol 1e-3 for bf16 inputs (exact in the oracle: only the fp32
+# accumulation order differs) and 1e-5 for fp32 inputs; and the noise, taken
+# as out(sigma) - out(0) of two GPU calls that differ only in sigma, against
+# sigma * C * xi / denom with xi from the oracle's own Philox + Box-Muller,
+# to 1e-5 * sigma * C / denom absolute (fp32 normals are within 7e-7 of the
+# fp64 ones for |z| <= 5.8; the fp32 roundings of the epilogue add ~1e-7).
+SUM_ELEM_TOL = {"bf16": 1e-3, "f32": 1e-5}
+NOISE_ELEM_TOL = 1e-5
+
+
+def assert_elementwise(got, ref, tol, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)))
+    assert np.isfinite(err) and err <= tol * scale, (
+        f"{what}: max|got - ref| = {err:.3e} > {tol:g} * max|ref| = {tol * scale:.3e}")
+    return err / scale if scale > 0 else 0.0
+
+
+def assert_noise(out_sigma, out_zero, sigma, C, seed, offset, denom, what="", xi=None):
+    """out(sigma) - out(0) = sigma C xi / denom, element by element."""
+    d = np.asarray(out_sigma, np.float64) - np.asarray(out_zero, np.float64)
+    if xi is None:
+        from oracle import philox
+        xi = philox.gaussian(seed, offset, d.size).reshape(d.shape)
+    want = sigma * C * np.asarray(xi, np.float64) / denom
+    err = float(np.max(np.abs(d - want)))
+    tol = NOISE_ELEM_TOL * sigma * C / denom
+    assert np.isfinite(err) and err <= tol, (
+        f"{what}: max|noise - sigma C xi / denom| = {err:.3e} > {tol:.3e}")
+    return err

@@ -12,7 +12,8 @@ import pytest
 
 import workloads
 from oracle import dp_linear
-from tests.gpu_helpers import max_rel, need_gpu, rel_fro, run_dense
+from tests.gpu_helpers import (assert_elementwise, assert_noise, max_rel, need_gpu, rel_fro,
+                               run_dense)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -28,9 +29,13 @@ def _compare(lin, torch, path=None):
     assert max_rel(norms, rnorms) <= NORM_TOL
     assert rel_fro(out, ref) <= AGG_TOL
     out0, _ = run_dense(lin, torch, sigma=0.0, path=path)
-    ref0 = ref - lin.sigma * lin.C * dp_linear.noise_matrix(lin.seed, lin.offset, ref.shape) / lin.B
+    xi = dp_linear.noise_matrix(lin.seed, lin.offset, ref.shape)
+    ref0 = ref - lin.sigma * lin.C * xi / lin.B
     err0 = rel_fro(out0, ref0)
     assert err0 <= SUM_TOL, err0
+    # element by element: the clipped sum, and the noise out(sigma) - out(0)
+    assert_elementwise(out0, ref0, SUM_TOL, "sigma = 0 companion")
+    assert_noise(out, out0, lin.sigma, lin.C, lin.seed, lin.offset, lin.B, "noise", xi=xi)
     return rnorms, rc
 
 
@@ -76,6 +81,7 @@ def test_llama13b_q_mixed_clip():
     assert (rc == 1).any() and (rc < 1).any()
     assert max_rel(norms, rnorms) <= NORM_TOL
     assert rel_fro(out, ref) <= SUM_TOL
+    assert_elementwise(out, ref, SUM_TOL, "mixed clip, sigma = 0")
 
 
 # ---------------------------------------------------------------------------
@@ -173,3 +179,5 @@ def test_offsets_past_two_gib_take_the_generic_kernels():
     assert max_rel(norms.cpu().numpy(), rnorms) <= NORM_TOL
     assert rel_fro(out.cpu().numpy(), ref) <= AGG_TOL
     assert rel_fro(out0.cpu().numpy(), ref0) <= SUM_TOL
+    assert_elementwise(out0.cpu().numpy(), ref0, SUM_TOL, "generic kernels, sigma = 0")
+    assert_noise(out.cpu().numpy(), out0.cpu().numpy(), 0.8, C, 4, 9, B, "generic kernels noise")

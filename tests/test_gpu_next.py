@@ -17,7 +17,8 @@ import pytest
 
 import workloads
 from oracle import dp_linear
-from tests.gpu_helpers import mask_dev, max_rel, need_gpu, random_linear, rel_fro, to_dev
+from tests.gpu_helpers import (SUM_ELEM_TOL, assert_elementwise, assert_noise, mask_dev, max_rel,
+                               need_gpu, random_linear, rel_fro, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,12 +73,17 @@ def test_seeded_projection_roberta_vs_oracle(index):
     r = 256
     X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
     P = dp_linear.projection_matrix(7, 0, lin.din, r, 1.0 / 16.0, "bf16")
+    outs = {}
     for sigma, tol in ((lin.sigma, AGG_TOL_BF16), (0.0, 1e-2)):
         out, norms = dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7,
                                                                 p_offset=0, C=lin.C, sigma=sigma)
         ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, sigma, 0, 0, "bf16")
         assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
         assert rel_fro(out.cpu().numpy(), ref) <= tol
+        outs[sigma] = out.cpu().numpy()
+    # element by element (Y rounded to bf16 on the GPU: 1e-2 of the largest entry)
+    assert_elementwise(outs[0.0], ref, 1e-2, "seeded projected sigma = 0")
+    assert_noise(outs[lin.sigma], outs[0.0], lin.sigma, lin.C, 0, 0, lin.B, "seeded noise")
 
 
 # ---------------------------------------------------------------------------
@@ -104,6 +110,7 @@ def test_group_clip_matches_oracle(dtype):
     Gs = [to_dev(l.G, dtype, torch) for l in lins]
     m = mask_dev(mask, torch)
     sum_tol = SUM_TOL_BF16 if dtype == "bf16" else 1e-4
+    got = {}
     for sigma, tol in ((0.0, sum_tol), (1.1, AGG_TOL_BF16 if dtype == "bf16" else 1e-4)):
         outs, norms = dp.group_clip_accumulate(Xs, Gs, m, C=C, sigma=sigma, seed=3,
                                                offsets=offsets)
@@ -112,6 +119,18 @@ def test_group_clip_matches_oracle(dtype):
         assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
         for o, ref in zip(outs, refs):
             assert rel_fro(o.cpu().numpy(), ref) <= tol
+        got[sigma] = ([o.cpu().numpy() for o in outs], refs)
+    _group_elementwise(got, 1.1, C, 3, offsets, B, dtype)
+
+
+def _group_elementwise(got, sigma, C, seed, offsets, B, dtype):
+    """Each linear's sigma = 0 output against the oracle, and its noise
+    out(sigma) - out(0) against its own stream (seed, offsets[l])."""
+    outs0, refs0 = got[0.0]
+    outs1, _ = got[sigma]
+    for l, (o0, r0, o1) in enumerate(zip(outs0, refs0, outs1)):
+        assert_elementwise(o0, r0, SUM_ELEM_TOL[dtype], f"group linear {l}, sigma = 0")
+        assert_noise(o1, o0, sigma, C, seed, offsets[l], B, f"group linear {l} noise")
 
 
 def test_group_of_one_is_the_dense_call_bitwise():
@@ -145,6 +164,7 @@ def test_group_clip_unmasked_matches_oracle(path):
     Gs = [to_dev(l.G, "bf16", torch) for l in lins]
     dp.set_option("norm_path", path)
     try:
+        got = {}
         for sigma, tol in ((0.0, SUM_TOL_BF16), (1.1, AGG_TOL_BF16)):
             outs, norms = dp.group_clip_accumulate(Xs, Gs, None, C=C, sigma=sigma, seed=3,
                                                    offsets=offsets)
@@ -153,6 +173,8 @@ def test_group_clip_unmasked_matches_oracle(path):
             assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
             for o, ref in zip(outs, refs):
                 assert rel_fro(o.cpu().numpy(), ref) <= tol
+            got[sigma] = ([o.cpu().numpy() for o in outs], refs)
+        _group_elementwise(got, 1.1, C, 3, offsets, 3, "bf16")
     finally:
         dp.set_option("norm_path", 0)
 
@@ -315,6 +337,7 @@ def test_bias_matches_oracle(dtype, shape):
     _, _, rn, _ = dp_linear.oracle_linear_bias(lin.X, lin.G, lin.mask, 1.0, 0.0, 0, 0, dtype)
     C = float(np.median(rn))
     sum_tol = SUM_TOL_BF16 if dtype == "bf16" else 1e-4
+    got = {}
     for sigma, tol in ((0.0, sum_tol), (0.9, AGG_TOL_BF16 if dtype == "bf16" else 1e-4)):
         ow, ob, norms = dp.linear_clip_accumulate_bias(X, G, m, C=C, sigma=sigma, seed=4, offset=6)
         rw, rb, rn, rc = dp_linear.oracle_linear_bias(lin.X, lin.G, lin.mask, C, sigma, 4, 6, dtype)
@@ -322,6 +345,19 @@ def test_bias_matches_oracle(dtype, shape):
         assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
         assert rel_fro(ow.cpu().numpy(), rw) <= tol
         assert rel_fro(ob.cpu().numpy(), rb) <= tol
+        got[sigma] = (ow.cpu().numpy(), ob.cpu().numpy(), rw, rb)
+    _bias_elementwise(got, 0.9, C, 4, 6, B, din, dout, dtype)
+
+
+def _bias_elementwise(got, sigma, C, seed, offset, B, din, dout, dtype):
+    """Weight and bias outputs at sigma = 0 against the oracle; the noise of
+    each: the weight's from `offset`, the bias's continuing the stream."""
+    w0, b0, rw0, rb0 = got[0.0]
+    w1, b1, _, _ = got[sigma]
+    assert_elementwise(w0, rw0, SUM_ELEM_TOL[dtype], "bias call weight, sigma = 0")
+    assert_elementwise(b0, rb0, SUM_ELEM_TOL[dtype], "bias call bias, sigma = 0")
+    assert_noise(w1, w0, sigma, C, seed, offset, B, "bias call weight noise")
+    assert_noise(b1, b0, sigma, C, seed, offset + (din * dout + 3) // 4, B, "bias noise")
 
 
 @pytest.mark.parametrize("path", [0, 1, 3])
@@ -337,6 +373,7 @@ def test_bias_unmasked_matches_oracle(path):
     C = float(np.median(rn))
     dp.set_option("norm_path", path)
     try:
+        got = {}
         for sigma, tol in ((0.0, SUM_TOL_BF16), (0.9, AGG_TOL_BF16)):
             ow, ob, norms = dp.linear_clip_accumulate_bias(X, G, None, C=C, sigma=sigma, seed=4,
                                                            offset=6)
@@ -346,6 +383,8 @@ def test_bias_unmasked_matches_oracle(path):
             assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
             assert rel_fro(ow.cpu().numpy(), rw) <= tol
             assert rel_fro(ob.cpu().numpy(), rb) <= tol
+            got[sigma] = (ow.cpu().numpy(), ob.cpu().numpy(), rw, rb)
+        _bias_elementwise(got, 0.9, C, 4, 6, 4, 520, 264, "bf16")
     finally:
         dp.set_option("norm_path", 0)
 
@@ -383,6 +422,7 @@ def test_ex_accumulates_into_grad_out_against_oracle(dtype, path):
     X, G = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch)
     dp.set_option("norm_path", path)
     try:
+        grads = {}
         for sigma in (0.0, 0.9):
             ref, rnorms, _ = dp_linear.oracle_linear(lin.X, lin.G, None, C, sigma, 5, 17, dtype,
                                                      denom=10.0, out0=out0)
@@ -394,6 +434,13 @@ def test_ex_accumulates_into_grad_out_against_oracle(dtype, path):
             got = grad.cpu().numpy().astype(np.float64) - out0
             tol = (SUM_TOL_BF16 if sigma == 0.0 else AGG_TOL_BF16) if dtype == "bf16" else 1e-4
             assert rel_fro(got, ref - out0) <= tol
+            grads[sigma] = (grad.cpu().numpy(), ref)
+        # element by element: grad_out after the sigma = 0 call against the
+        # oracle, and the noise the sigma = 0.9 call added on top of the same
+        # prior contents, divided by the explicit denominator
+        assert_elementwise(grads[0.0][0].astype(np.float64) - out0, grads[0.0][1] - out0,
+                           SUM_ELEM_TOL[dtype], "accumulated sigma = 0")
+        assert_noise(grads[0.9][0], grads[0.0][0], 0.9, C, 5, 17, 10.0, "accumulated noise")
     finally:
         dp.set_option("norm_path", 0)
 

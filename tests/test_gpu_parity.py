@@ -17,8 +17,8 @@ import pytest
 
 import workloads
 from oracle import dp_linear
-from tests.gpu_helpers import (mask_dev, max_rel, need_gpu, random_linear, rel_fro, run_dense,
-                               to_dev)
+from tests.gpu_helpers import (SUM_ELEM_TOL, assert_elementwise, assert_noise, mask_dev, max_rel,
+                               need_gpu, random_linear, rel_fro, run_dense, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,10 @@ NORM_TOL = 1e-3
 AGG_TOL_BF16 = 2e-2
 AGG_TOL_F32 = 1e-4
 SUM_TOL_BF16 = 1e-3
+# projected sigma = 0, element-wise against max|ref|: Y = X P is stored in the
+# inputs' dtype on the GPU and kept in fp64 by the oracle (bf16: 2^-9 relative
+# per Y entry; fp32: two chained fp32 contractions)
+PROJ_ELEM_TOL = {"bf16": 1e-2, "f32": 1e-4}
 
 
 def _oracle(lin, C=None, sigma=None, offset=None):
@@ -35,13 +39,25 @@ def _oracle(lin, C=None, sigma=None, offset=None):
 
 
 def _check(lin, path, sigma, C=None, agg_tol=None):
+    """The call against the oracle: norms, the aggregate (relative Frobenius),
+    and element by element the clipped sum (sigma = 0) and, for sigma > 0,
+    the noise out(sigma) - out(0)."""
     torch = need_gpu()
+    Cv = lin.C if C is None else C
     out, norms = run_dense(lin, torch, C=C, sigma=sigma, path=path)
     ref, rnorms, _ = _oracle(lin, C=C, sigma=sigma)
     assert max_rel(norms, rnorms) <= NORM_TOL, (max_rel(norms, rnorms), norms, rnorms)
     tol = agg_tol if agg_tol is not None else (AGG_TOL_F32 if lin.dtype == "f32" else AGG_TOL_BF16)
     err = rel_fro(out, ref)
     assert err <= tol, err
+    if sigma == 0.0:
+        assert_elementwise(out, ref, SUM_ELEM_TOL[lin.dtype], "sigma = 0")
+    else:
+        out0, _ = run_dense(lin, torch, C=C, sigma=0.0, path=path)
+        xi = dp_linear.noise_matrix(lin.seed, lin.offset, ref.shape)
+        ref0 = ref - sigma * Cv * xi / lin.B
+        assert_elementwise(out0, ref0, SUM_ELEM_TOL[lin.dtype], "sigma = 0 companion")
+        assert_noise(out, out0, sigma, Cv, lin.seed, lin.offset, lin.B, "noise", xi=xi)
     return out, norms, ref, rnorms
 
 
@@ -204,11 +220,17 @@ def test_config_roberta_projected(index):
                                    .astype(np.float32)).reshape(lin.din, r)
     X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
     Pd = to_dev(P, "bf16", torch)
+    outs = {}
     for sigma, tol in ((lin.sigma, AGG_TOL_BF16), (0.0, 1e-2)):
         out, norms = dp.linear_clip_accumulate_projected(X, G, Pd, None, C=lin.C, sigma=sigma)
         ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, sigma, 0, 0, "bf16")
         assert max_rel(norms.cpu().numpy(), rn) <= NORM_TOL
         assert rel_fro(out.cpu().numpy(), ref) <= tol
+        outs[sigma] = out.cpu().numpy()
+    # element by element: the clipped sum (Y is rounded to bf16 on the GPU,
+    # 2^-9 relative per entry, hence 1e-2 of the largest entry) and the noise
+    assert_elementwise(outs[0.0], ref, PROJ_ELEM_TOL["bf16"], "projected sigma = 0")
+    assert_noise(outs[lin.sigma], outs[0.0], lin.sigma, lin.C, 0, 0, lin.B, "projected noise")
     # end to end: P drawn on the GPU from Philox seed 7 (each side its own generator)
     Pg = dp.gaussian_fill(7, 0, lin.din * r, 1.0 / 16, dtype=torch.bfloat16).view(lin.din, r)
     out, norms = dp.linear_clip_accumulate_projected(X, G, Pg, None, C=lin.C, sigma=lin.sigma)
@@ -233,6 +255,7 @@ def test_projected_small_masked_fp32_and_bf16():
         assert max_rel(norms.cpu().numpy()[rn > 0], rn[rn > 0]) <= tol_n
         assert norms.cpu().numpy()[2] == 0.0
         assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
+        assert_elementwise(out.cpu().numpy(), ref, PROJ_ELEM_TOL[dtype], f"projected {dtype}")
 
 
 @pytest.mark.parametrize("path", [0, 1])
@@ -279,3 +302,4 @@ def test_projected_split_along_din(dtype, shape):
     ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, lin.mask, P, 0.05, 0.0, 0, 0, dtype)
     assert max_rel(norms.cpu().numpy(), rn) <= (NORM_TOL if dtype == "f32" else 5e-3)
     assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
+    assert_elementwise(out.cpu().numpy(), ref, PROJ_ELEM_TOL[dtype], f"projected split {dtype}")
