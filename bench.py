@@ -167,8 +167,10 @@ def time_calls(torch, fn, steps, warmup, min_ms=20.0, warm_ms=100.0):
             fn()
         n_warm += 16
         torch.cuda.synchronize()
-    per_call = (time.perf_counter() - t0) * 1e3 / n_warm
-    reps = max(steps, int(min_ms / max(per_call, 1e-4)) + 1)
+    reps = steps
+    if n_warm:
+        per_call = (time.perf_counter() - t0) * 1e3 / n_warm
+        reps = max(steps, int(min_ms / max(per_call, 1e-4)) + 1)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
