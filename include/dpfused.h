@@ -148,6 +148,34 @@ dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
                                              int32_t accumulate, float* grad_out,
                                              float* norms_out, void* stream);
 
+/* dpfused_linear_clip_accumulate for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The call allocates nothing -- no hipMalloc, hipFree or
+ * pool allocation.  Its workspace is a static device array of 80 MiB that
+ * the library holds on each GPU it runs on until the process ends.
+ *
+ * Same arguments, result and errors as dpfused_linear_clip_accumulate.  The
+ * norm path is that call's automatic choice (or the "norm_path" option's
+ * Gram or direct; never the staged form).  When that plan's workspace is
+ * larger than the scratch, the call runs without split tiles (same path),
+ * then, for the Gram path, the direct form: results then equal the
+ * allocating call's up to fp32 summation order, not bit for bit.
+ *
+ * Extra error: DPF_ERR_UNSUPPORTED when even that workspace (norm partials
+ * B * tiles * 8 bytes, mask bits and lists) exceeds 80 MiB; nothing is then
+ * launched or written.
+ *
+ * Every call on one GPU uses that GPU's one scratch array, and a call
+ * leaves its contents behind (every kernel writes what it later reads, so
+ * nothing needs clearing).  Calls that overlap in time on one GPU -- on two
+ * streams, or from two threads without ordering -- race on it and give
+ * wrong results; order them (one stream, or events). */
+dpf_status dpfused_linear_clip_accumulate_noalloc(const dpf_act* X, const dpf_act* G,
+                                                  const uint8_t* mask, float C, float sigma,
+                                                  uint64_t seed, uint64_t offset,
+                                                  float* grad_out, float* norms_out,
+                                                  void* stream);
+
 /* Projected variant (Memory-Efficient Differentially Private Training with
  * Gradient Random Projection, English explainer, Methodology: "Random
  * Projection over SVD" and "Order of Operations").  Each sample's gradient is

@@ -21,7 +21,7 @@ from . import _lib
 from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
 
 __all__ = [
-    "linear_clip_accumulate", "linear_clip_accumulate_projected",
+    "linear_clip_accumulate", "linear_clip_accumulate_noalloc", "linear_clip_accumulate_projected",
     "linear_clip_accumulate_projected_seeded", "linear_clip_accumulate_bias",
     "group_clip_accumulate", "consecutive_offsets", "projected_adam_step",
     "per_sample_sqnorms",
@@ -145,6 +145,27 @@ def linear_clip_accumulate(X, G, mask=None, C: float = 1.0, sigma: float = 0.0, 
             ctypes.byref(xa), ctypes.byref(ga), mp, float(C), float(sigma),
             int(seed), int(offset), float(B if denom is None else denom), int(bool(accumulate)),
             grad_out.data_ptr(), _ptr(norms_out), _stream(X, stream))
+    _lib.check(st)
+    return grad_out, norms_out
+
+
+def linear_clip_accumulate_noalloc(X, G, grad_out, mask=None, C: float = 1.0,
+                                   sigma: float = 0.0, seed: int = 0, offset: int = 0,
+                                   norms_out=None, stream=None):
+    """linear_clip_accumulate without any device allocation, for code under graph
+    capture or loops that must not allocate: the library works in its static per-GPU
+    scratch, and this wrapper allocates nothing either (grad_out [dout, din] fp32 must
+    be given; norms_out [B] fp32 or None).  Calls that overlap in time on one GPU race
+    on the scratch: keep them ordered."""
+    xa, ga = _pair(X, G)
+    B, T = X.shape[0], X.shape[1]
+    _check_out(grad_out, (G.shape[2], X.shape[2]), "grad_out", X.device)
+    if norms_out is not None:
+        _check_out(norms_out, (B,), "norms_out", X.device)
+    st = _lib.lib().dpfused_linear_clip_accumulate_noalloc(
+        ctypes.byref(xa), ctypes.byref(ga), _mask_ptr(mask, B, T, X.device), float(C),
+        float(sigma), int(seed), int(offset), grad_out.data_ptr(), _ptr(norms_out),
+        _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
 

@@ -52,6 +52,10 @@ _SIGNATURES = {
         ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_float,
         ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dpfused_linear_clip_accumulate_noalloc": (ctypes.c_int, [
+        ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
     "dpfused_linear_clip_accumulate_projected": (ctypes.c_int, [
         ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,

@@ -914,7 +914,7 @@ big::SkPlan plan_accumulate(const LayerArgs& p) {
   sk.D = ntiles / G;
   sk.R = ntiles - sk.D * G;
   const int n = p.B * ((p.T + big::kKT - 1) / big::kKT);   // every step (an upper bound if masked)
-  sk.P = big::split_tiles(sk.R, G, n, big::kMaxSplit);
+  sk.P = big::split_tiles(sk.R, G, n, p.max_split == 1 ? 1 : big::kMaxSplit);
   if (sk.P == 1 && sk.D == 0) sk.G = sk.R;   // one tile per workgroup, no idle ones
   return sk;
 }

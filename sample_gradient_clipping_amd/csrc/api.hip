@@ -25,6 +25,15 @@
 #include "dpfused.h"
 #include "kernels.hpp"
 
+// Static scratch of dpfused_linear_clip_accumulate_noalloc, for callers that
+// cannot allocate (graph capture, tight serving loops): 80 MiB, which holds
+// a Llama-13B-sized linear's workspace without split tiles (the Gram
+// kernel's parked blocks, 64 MiB on 256 compute units, plus norm partials,
+// clip factors and mask bits).  Each device holds its own copy, at its own
+// address, until the process ends.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -420,9 +429,10 @@ struct Workspace {
   size_t size = 0, cap = 0;
   hipEvent_t ev = nullptr;
   int dev = -1;   // -1: not from (and not returned to) the cache
+  bool external = false;   // memory the workspace does not own (the static scratch)
   explicit Workspace(hipStream_t st) : s(st) {}
   ~Workspace() {
-    if (base == nullptr) return;
+    if (base == nullptr || external) return;
     if (dev < 0 || dev >= kMaxDevices) {
       (void)hipFreeAsync(base, s);
       return;
@@ -502,6 +512,14 @@ struct Workspace {
       return false;
     }
     cap = size;
+    return true;
+  }
+  // Carve the pieces from memory the caller holds instead of allocating.
+  bool use_external(void* p, size_t bytes) {
+    if (size > bytes) return false;
+    base = p;
+    cap = bytes;
+    external = true;
     return true;
   }
   template <class T>
@@ -766,6 +784,43 @@ dpf_status sqnorms_into(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of dpfused_linear_clip_accumulate_noalloc
+// ---------------------------------------------------------------------------
+// The call's workspace lives in the file-scope array `scratch` (top of this
+// file) instead of the pool.  Host code never passes the array's name to a
+// kernel (in host code it only stands for the symbol): it takes the device
+// address once per device with hipGetSymbolAddress and uses that.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of device dev's copy of `scratch`, taken on its first
+// use with dev current; nullptr (and the reason) if it cannot be had.
+void* scratch_ptr(int dev, std::string* why) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] != nullptr) return g_scratch_ptr[dev];
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+  void* p = nullptr;
+  if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    *why = std::string("no address for the static scratch: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  g_scratch_ptr[dev] = p;
+  return p;
+}
+
+// Workspace bytes a dense call on plan L takes (nothing is allocated).
+size_t layer_ws_bytes(const LayerPlan& L, hipStream_t s) {
+  Workspace dry(s);
+  (void)reserve_layer(L, dry, true, true, true);
+  return dry.size;
+}
+
 // Accumulate phase of one linear with given clip factors c[B].
 dpf_status accumulate_with(const dpf_act* X, const dpf_act* G, const uint8_t* mask, const float* c,
                            float noise_std, uint64_t seed, uint64_t offset, float* grad_out,
@@ -858,6 +913,66 @@ dpf_status dpfused_linear_clip_accumulate_ex(const dpf_act* X, const dpf_act* G,
   Workspace ws(s);
   return fused_layer(X, G, mask, C, sigma, seed, offset, denom, accumulate, grad_out, norms_out,
                      s, ws);
+}
+
+dpf_status dpfused_linear_clip_accumulate_noalloc(const dpf_act* X, const dpf_act* G,
+                                                  const uint8_t* mask, float C, float sigma,
+                                                  uint64_t seed, uint64_t offset,
+                                                  float* grad_out, float* norms_out,
+                                                  void* stream) {
+  CallScope call_("dpfused_linear_clip_accumulate_noalloc");
+  dpf_status st = check_pair(X, G);
+  if (st != DPF_OK) return st;
+  if ((st = check_clip(C, sigma)) != DPF_OK) return st;
+  if (grad_out == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+  if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dev = stream_device(s);
+  if (dev < 0 || dev >= kMaxDevices) return fail(DPF_ERR_HIP, "cannot tell the stream's device");
+  // Never the staged form: its tiles are far larger than the scratch.
+  LayerPlan L = plan_layer(X, G, mask, false);
+  L.args.noise_std = sigma * C;
+  L.args.seed = seed;
+  L.args.offset = offset;
+  L.args.out = grad_out;
+  if (g_norm_path.load() == 0 && dpf::tiny_eligible(L.args)) {
+    const hipError_t e = dpf::launch_tiny_layer(L.args, C, norms_out, s);
+    if (e != hipSuccess) return hip_fail(e, "tiny layer launch");
+    return ok();
+  }
+  // The call's own plan if its workspace fits the scratch; else the same
+  // norm path without split tiles or items (no split partials); else, for
+  // the Gram path, the direct form without splits (no parked Gram blocks).
+  size_t need = layer_ws_bytes(L, s);
+  if (need > kScratchBytes) {
+    L.args.max_split = 1;
+    need = layer_ws_bytes(L, s);
+  }
+  if (need > kScratchBytes && L.path == dpf::NormPath::kGram && g_norm_path.load() != 1) {
+    L.path = dpf::NormPath::kDirect;
+    L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
+    need = layer_ws_bytes(L, s);
+  }
+  if (need > kScratchBytes)
+    return fail(DPF_ERR_UNSUPPORTED,
+                "the call needs " + std::to_string(need) + " bytes of workspace, more than the " +
+                    std::to_string(kScratchBytes) + " bytes of static scratch");
+  std::string why;
+  void* base = scratch_ptr(dev, &why);
+  if (base == nullptr) return fail(DPF_ERR_HIP, why);
+  Workspace ws(s);
+  const LayerWs o = reserve_layer(L, ws, true, true, true);
+  if (!ws.use_external(base, kScratchBytes))
+    return fail(DPF_ERR_UNSUPPORTED, "workspace larger than the static scratch");
+  hipError_t e = bind_layer(L, ws, o, s);
+  if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  float* c = ws.at<float>(o.c);
+  e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
+  if (e != hipSuccess) return hip_fail(e, "norm phase launch");
+  L.args.c = c;
+  e = accumulate_phase(L, s);
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  return ok();
 }
 
 dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_act* G,

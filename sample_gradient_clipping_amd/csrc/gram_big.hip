@@ -582,7 +582,7 @@ gram::GramPlan plan_gram(const LayerArgs& p) {
   int G = std::min(cus, items * 16);
   if (G >= 8) G -= G % 8;
   const int n = (p.din + gram::kKF - 1) / gram::kKF + (p.dout + gram::kKF - 1) / gram::kKF;
-  gram::GramPlan gp = gram::split_items(items, G, n, 1 << 30);
+  gram::GramPlan gp = gram::split_items(items, G, n, p.max_split == 1 ? 0 : 1 << 30);
   if (gp.P == 1 && gp.D == 0) gp.G = gp.R;
   return gp;
 }
@@ -600,7 +600,8 @@ GramWs gram_ws(const LayerArgs& p, const gram::GramPlan& gp) {
   const size_t tile = (size_t)gram::kGramFloats * sizeof(float);
   if (p.mask != nullptr) w.xs = round256(((size_t)p.B * gram::items_per_sample(p.T) + 1) * 4);
   w.pieces = w.xs + (size_t)gp.G * tile;
-  const size_t npieces = p.mask != nullptr ? (size_t)gp.G : (gp.P == 1 ? 0 : (size_t)gp.R * gp.P);
+  const size_t npieces = p.max_split == 1 ? 0
+                        : p.mask != nullptr ? (size_t)gp.G : (gp.P == 1 ? 0 : (size_t)gp.R * gp.P);
   w.part = w.pieces + npieces * 2 * tile;
   // fixup sums: one row per possible split item (R < G)
   w.total = w.part + round256((size_t)gp.G * gram::kFixParts * sizeof(double));
@@ -624,6 +625,8 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   float* xs = reinterpret_cast<float*>(base + w.xs);
   float* pieces = reinterpret_cast<float*>(base + w.pieces);
   double* part = reinterpret_cast<double*>(base + w.part);
+  // pieces the device-side plan of a masked call may use (0: no split)
+  const int cap = p.max_split == 1 ? 0 : gp.G;
   hipError_t e;
   if (masked) {
     timing_begin("live_items", s);
@@ -634,18 +637,18 @@ hipError_t launch_gram_norm_big(const LayerArgs& p, hipStream_t s) {
   }
   timing_begin("gram_norm", s);
   hipLaunchKernelGGL(gram::gram_norm_big_kernel, dim3(gp.G), dim3(gram::kNT), gram::kLdsBytes, s, p,
-                     gp, (const uint32_t*)live, gp.G, xs, pieces);
+                     gp, (const uint32_t*)live, cap, xs, pieces);
   e = hipGetLastError();
   timing_end("gram_norm", s);
   if (e != hipSuccess || (!masked && gp.P == 1)) return e;
   const int nfix = masked ? gp.G : gp.R;   // items that may be split
   timing_begin("gram_fixup", s);
   hipLaunchKernelGGL(gram::gram_fixup_kernel, dim3(nfix * gram::kFixParts), dim3(gram::kNT), 0, s,
-                     p, gp, (const uint32_t*)live, gp.G, (const float*)pieces, part);
+                     p, gp, (const uint32_t*)live, cap, (const float*)pieces, part);
   e = hipGetLastError();
   if (e == hipSuccess)
     hipLaunchKernelGGL(gram::gram_fixup_sum_kernel, dim3((nfix + 63) / 64), dim3(64), 0, s, p, gp,
-                       (const uint32_t*)live, gp.G, (const double*)part);
+                       (const uint32_t*)live, cap, (const double*)part);
   if (e == hipSuccess) e = hipGetLastError();
   timing_end("gram_fixup", s);
   return e;

@@ -33,6 +33,8 @@ struct LayerArgs {
   double* partials;         // [B, norm_partials_per_sample] (norm kernels)
   const uint32_t* steps;    // active-step list (large-tile kernels, masked calls) or null
   float* skws;              // partials of split tiles / items (large-tile kernels), or null
+  int max_split;            // 1: never split a tile or Gram item (no split partials in
+                            // skws); 0: as the cost model picks
 };
 
 // Active-step list of a masked call, built from the row bits:

@@ -383,3 +383,17 @@ def test_memory_options(L):
     assert L.dpfused_set_option(b"staged_keep_bytes", 1 << 30) == DPF_OK
     assert L.dpfused_get_option(b"staged_keep_bytes") == 1 << 30
     assert L.dpfused_set_option(b"staged_keep_bytes", 0) == DPF_OK
+
+
+def test_noalloc_argument_checks(L):
+    X, G = _act(), _act(D=16)
+    f = L.dpfused_linear_clip_accumulate_noalloc
+    call = lambda out=FAKE, C=1.0, sigma=1.0: f(ctypes.byref(X), ctypes.byref(G), None, C, sigma,
+                                                 0, 0, out, None, None)
+    assert call(out=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(out=FAKE + 4) == DPF_ERR_UNSUPPORTED
+    assert call(C=0.0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(sigma=-1.0) == DPF_ERR_INVALID_ARGUMENT
+    bad = _act(T=5)
+    assert f(ctypes.byref(bad), ctypes.byref(G), None, 1.0, 1.0, 0, 0, FAKE, None, None) == \
+        DPF_ERR_INVALID_ARGUMENT
