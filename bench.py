@@ -39,24 +39,30 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "fused DP clip+accumulate TFLOP/s and samples/s per linear layer; % MFMA peak"
 
-# HBM bytes per launch of the dominant kernels on this workload, from two
-# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
-# dispatch, averaged over the seven linears), each scaled by what the same
-# counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE
-# x1.0).  Valid only for the kernel sources whose SHA-256 is stored here and
-# the default workload; reported as null otherwise.
-COUNTER_SOURCES = ("accum_big.hip", "gram_big.hip", "common.hpp", "kernels.hpp")
+# Figures per launch of the dominant kernels on this workload (the automatic
+# path: Gram on all seven linears), from rocprofv3 runs of this script
+# (profiles/gram_accumulate_llama13b_layer_B8_T2048_*.md): HBM bytes from two
+# --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged over
+# the seven linears) scaled by what the same counters read for a plain 1 GiB
+# device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); MfmaUtil (MFMA-busy cycles
+# per SIMD cycle, percent); and the kernel-trace average duration.  Each
+# kernel's figures hold only for the sources whose SHA-256 is stored with them
+# and the default workload; they are reported as null otherwise.
+KERNEL_SOURCES = {"accumulate": ("accum_big.hip", "common.hpp"),
+                  "gram_norm": ("gram_big.hip", "common.hpp")}
 KERNEL_COUNTERS = {
-    "sources_sha256": "23951e013c3dc85a37e3b81f3fc25951d69e211f22fe95bf533fcfb8de3ae012",
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
-    # per --norm-path value: kernel -> KiB per dispatch
-    "runs": {
-        "1": {"accumulate": {"fetch_kib": 1135114.01, "write_kib": 279698.29}, "gram_norm": {"fetch_kib": 418247.31, "write_kib": 152505.33}},
-        "3": {"staged_norm": {"fetch_kib": 1284089.86, "write_kib": 1416510.64}, "staged_combine": {"fetch_kib": 708059.38, "write_kib": 177198.16}},
+    "kernels": {
+        "accumulate": {"sources_sha256": "653aa1b0b5cba054cba5a34c86255f191b3e2e3262c3d1720655a1fe6587a6ff",
+                       "fetch_kib": 1129826.69, "write_kib": 279698.29, "mfma_busy_pct": 59.49,
+                       "trace_avg_us": 1299.4},
+        "gram_norm": {"sources_sha256": "a22f5cd2595a5c58255194bb6fda470b276f620ce31f9b99869ede600f370a06",
+                      "fetch_kib": 422855.55, "write_kib": 152505.42, "mfma_busy_pct": 50.23,
+                      "trace_avg_us": 511.9},
     },
-    # --norm-path 0 takes the Gram path on all seven linears: the same kernels
-    "same_as": {"0": "1"},
+    # --norm-path values that run these kernels on every linear of the workload
+    "paths": ("0", "1"),
 }
 
 
@@ -378,31 +384,34 @@ def copy_calibration(steps):
                       "launches": steps}), flush=True)
 
 
-def kernel_traffic(args, kernel):
-    """Counter-derived HBM bytes per launch of `kernel`, or None when the kernel
-    sources or the workload differ from the profiled ones."""
+def kernel_record(args, kernel):
+    """The committed profile figures of `kernel`, or None when its sources or
+    the workload differ from the profiled ones."""
     c = KERNEL_COUNTERS
+    k = c["kernels"].get(kernel)
+    if k is None or str(args.norm_path) not in c["paths"] or args.batch != c["batch"] \
+            or args.seq != c["seq"] or args.linears != c["linears"]:
+        return None
     h = hashlib.sha256()
-    for f in COUNTER_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sample_gradient_clipping_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    run = c.get("same_as", {}).get(str(args.norm_path), str(args.norm_path))
-    k = c["runs"].get(run, {}).get(kernel)
-    if (k is None or h.hexdigest() != c["sources_sha256"] or args.batch != c["batch"]
-            or args.seq != c["seq"] or args.linears != c["linears"]):
+    return k if h.hexdigest() == k["sources_sha256"] else None
+
+
+def kernel_traffic(args, kernel):
+    """Counter-derived HBM bytes per launch of `kernel`, or None."""
+    k = kernel_record(args, kernel)
+    if k is None:
         return None
+    c = KERNEL_COUNTERS
     return (k["fetch_kib"] * c["fetch_scale"] + k["write_kib"] * c["write_scale"]) * 1024.0
 
 
 def kernel_counter(args, kernel, name):
-    """A per-kernel counter figure (e.g. MFMA-busy %) from the committed
-    rocprofv3 --pmc summary of this workload, or None when the kernel sources
-    or the workload differ from the profiled ones."""
-    c = KERNEL_COUNTERS
-    if kernel_traffic(args, kernel) is None:
-        return None
-    run = c.get("same_as", {}).get(str(args.norm_path), str(args.norm_path))
-    return c["runs"].get(run, {}).get(kernel, {}).get(name)
+    """A per-kernel figure (MFMA-busy %, trace average) from the committed profile, or None."""
+    k = kernel_record(args, kernel)
+    return None if k is None else k.get(name)
 
 
 def norm_path_of(dp, call):
@@ -662,6 +671,13 @@ def main():
             "avg_launch_ms": round(dom_avg_ms, 4),
             "flops_per_launch": round(dom_flops),
             "mfma_busy_pct": kernel_counter(args, dom, "mfma_busy_pct"),
+            "committed_trace_avg_ms": None if kernel_counter(args, dom, "trace_avg_us") is None
+            else kernel_counter(args, dom, "trace_avg_us") / 1e3,
+            "committed_trace_frac": None if kernel_counter(args, dom, "trace_avg_us") is None
+            else round(dom_flops / (kernel_counter(args, dom, "trace_avg_us") * 1e-6) / 1e12
+                       / PEAK_BF16_TFLOPS, 4),
+            "note": "achieved from this run's HIP events on the launch stream; committed_trace_* "
+                    "from the rocprofv3 kernel trace in profiles/ (boxes differ by ~5% in clock)",
         },
         "roofline_kernel_bytes_per_launch": {"algorithmic": round(dom_algo_bytes),
                                              "hbm_counters": None if traffic is None else round(traffic)},
