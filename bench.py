@@ -425,7 +425,7 @@ def norm_path_of(dp, call):
         dp.set_option("timing", 0)
         dp.timing_reset()
     for key, path in (("staged_norm", "staged"), ("gram_norm", "gram"), ("direct_norm", "direct"),
-                      ("tiny_layer", "one workgroup")):
+                      ("onepass", "one pass"), ("tiny_layer", "one workgroup")):
         if key in names:
             return path
     return "unknown"
@@ -584,12 +584,15 @@ def main():
     # MFMA kernels and the flops each does per linear; the dominant one (most
     # time per step) is the roofline kernel.
     mfma_flops = {
+        "onepass": lambda l, p: contraction(l) if p == "one pass" else 0.0,
         "staged_norm": lambda l, p: contraction(l) if p == "staged" else 0.0,
         "direct_norm": lambda l, p: contraction(l) if p == "direct" else 0.0,
         "gram_norm": lambda l, p: gram_flops(l) if p == "gram" else 0.0,
-        "accumulate": lambda l, p: contraction(l) if p != "staged" else 0.0,
+        "accumulate": lambda l, p: contraction(l) if p not in ("staged", "one pass") else 0.0,
     }
     kernel_desc = {
+        "onepass": "onepass (per-sample gradient tiles once, cross-workgroup norm reduction, "
+                   "clipped running sum in registers)",
         "staged_norm": "staged_norm (per-sample gradient tiles by MFMA, their sums of squares, "
                        "tiles stored once for the combine pass)",
         "direct_norm": "direct_norm (per-sample gradient tiles by MFMA, sums of squares)",

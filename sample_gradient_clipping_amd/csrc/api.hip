@@ -42,6 +42,8 @@ std::atomic<int> g_timing{0};
 std::atomic<int> g_trace{0};        // roctx range around every entry point
 std::atomic<int> g_debug{0};        // synchronise after every launch, report errors
 std::atomic<int64_t> g_ws_limit{0};   // workspace requests above this fail (0: no limit)
+std::atomic<int> g_onepass_spin{1 << 20};   // single pass: tries of a blocking wait
+std::atomic<int> g_onepass_never{0};        // single pass: testing, every wait gives up
 
 // Defaults from the environment, read once when the library is loaded:
 // DPFUSED_NORM_PATH (auto, gram, direct, staged or 0-3), DPFUSED_TRACE,
@@ -50,7 +52,8 @@ bool read_env() {
   if (const char* v = std::getenv("DPFUSED_NORM_PATH")) {
     const std::string t(v);
     const int path = t == "gram" ? 1 : t == "direct" ? 2 : t == "staged" ? 3
-                   : (t.size() == 1 && t[0] >= '0' && t[0] <= '3') ? t[0] - '0' : 0;
+                   : t == "onepass" ? 4
+                   : (t.size() == 1 && t[0] >= '0' && t[0] <= '4') ? t[0] - '0' : 0;
     g_norm_path.store(path);
   }
   if (const char* v = std::getenv("DPFUSED_TRACE")) g_trace.store(std::atoi(v) != 0);
@@ -164,9 +167,19 @@ constexpr double kStagedMaxBytes = 16.0 * (1ull << 30);
 // allow_staged: the caller can keep the per-sample tiles from the norm phase
 // to the accumulate phase (the single-layer calls, and group clipping, which
 // holds every linear's tiles until the group's clip factors exist).
-dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged) {
+// The single-pass kernel runs one workgroup per 128 x 128 output tile, all
+// resident at once (a cooperative launch), on the large-tile layout.
+bool onepass_ok(const dpf::LayerArgs& a, bool vec) {
+  if (!dpf::big_path(a, vec) || a.B > 65535) return false;
+  const int nt = dpf::onepass_tiles(a.din, a.dout);
+  return nt <= 256 && nt <= dpf::onepass_resident_limit();
+}
+
+dpf::NormPath choose_path(const dpf::LayerArgs& a, bool vec, bool allow_staged,
+                          bool allow_onepass = false) {
   const bool big = dpf::big_path(a, vec);
   const int forced = g_norm_path.load();
+  if (forced == 4 && allow_onepass && onepass_ok(a, vec)) return dpf::NormPath::kOnePass;
   if (forced == 1) return dpf::NormPath::kGram;
   if (forced == 2) return dpf::NormPath::kDirect;
   if (forced == 3) {
@@ -539,7 +552,7 @@ struct LayerPlan {
 };
 
 LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
-                     bool allow_staged = false) {
+                     bool allow_staged = false, bool allow_onepass = false) {
   LayerPlan L;
   L.args.X = to_act(X);
   L.args.G = to_act(G);
@@ -553,7 +566,7 @@ LayerPlan plan_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask,
   L.args.denom = (float)X->B;
   L.args.beta = 0;
   L.vec = vec_ok(X) && vec_ok(G);
-  L.path = choose_path(L.args, L.vec, allow_staged);
+  L.path = choose_path(L.args, L.vec, allow_staged, allow_onepass);
   L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
   return L;
 }
@@ -582,7 +595,8 @@ LayerWs reserve_layers(const LayerPlan* const* Ls, int n, Workspace& ws, bool no
     const dpf::LayerArgs& a = L.args;
     if (dpf::big_path(a, L.vec)) any_big = true;
     if (norm) part = std::max(part, (size_t)a.B * L.np * sizeof(double));
-    if (L.path == dpf::NormPath::kStaged) continue;   // no split partials: its tiles are staged
+    // no split partials: staged tiles, or the single pass (no separate phases)
+    if (L.path == dpf::NormPath::kStaged || L.path == dpf::NormPath::kOnePass) continue;
     if (norm) sk = std::max(sk, dpf::norm_workspace_bytes(a, L.path, L.vec));
     if (accum) sk = std::max(sk, dpf::accumulate_workspace_bytes(a, L.vec));
   }
@@ -658,7 +672,9 @@ hipError_t norm_phase(const LayerPlan& L, double* sq, int accumulate, float C, f
 dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, float C,
                        float sigma, uint64_t seed, uint64_t offset, float denom, int beta,
                        float* grad_out, float* norms_out, hipStream_t s, Workspace& ws) {
-  LayerPlan L = plan_layer(X, G, mask, true);
+  // The single pass needs a cooperative launch, which a graph capture does
+  // not take: captured calls keep the two-phase paths.
+  LayerPlan L = plan_layer(X, G, mask, true, !stream_capturing(s));
   L.args.denom = denom;
   L.args.beta = beta;
   L.args.noise_std = sigma * C;
@@ -679,6 +695,11 @@ dpf_status fused_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, 
     return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
   hipError_t e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  if (L.path == dpf::NormPath::kOnePass) {
+    e = dpf::launch_onepass(L.args, C, norms_out, s);
+    if (e != hipSuccess) return hip_fail(e, "single-pass launch");
+    return ok();
+  }
   if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(lease.ptr());
   float* c = ws.at<float>(o.c);
   e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
@@ -929,8 +950,9 @@ dpf_status dpfused_linear_clip_accumulate_noalloc(const dpf_act* X, const dpf_ac
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dev = stream_device(s);
   if (dev < 0 || dev >= kMaxDevices) return fail(DPF_ERR_HIP, "cannot tell the stream's device");
-  // Never the staged form: its tiles are far larger than the scratch.
-  LayerPlan L = plan_layer(X, G, mask, false);
+  // Never the staged form: its tiles are far larger than the scratch.  The
+  // single pass (small workspace) when not under graph capture.
+  LayerPlan L = plan_layer(X, G, mask, false, !stream_capturing(s));
   L.args.noise_std = sigma * C;
   L.args.seed = seed;
   L.args.offset = offset;
@@ -966,6 +988,11 @@ dpf_status dpfused_linear_clip_accumulate_noalloc(const dpf_act* X, const dpf_ac
     return fail(DPF_ERR_UNSUPPORTED, "workspace larger than the static scratch");
   hipError_t e = bind_layer(L, ws, o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
+  if (L.path == dpf::NormPath::kOnePass) {
+    e = dpf::launch_onepass(L.args, C, norms_out, s);
+    if (e != hipSuccess) return hip_fail(e, "single-pass launch");
+    return ok();
+  }
   float* c = ws.at<float>(o.c);
   e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "norm phase launch");
@@ -1300,9 +1327,23 @@ uint64_t dpfused_noise_blocks(int64_t n_elements) {
 dpf_status dpfused_set_option(const char* name, int64_t value) {
   if (name == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "option name is NULL");
   if (std::strcmp(name, "norm_path") == 0) {
-    if (value < 0 || value > 3)
-      return fail(DPF_ERR_INVALID_ARGUMENT, "norm_path must be 0, 1, 2 or 3");
+    if (value < 0 || value > 4)
+      return fail(DPF_ERR_INVALID_ARGUMENT, "norm_path must be 0, 1, 2, 3 or 4");
     g_norm_path.store((int)value);
+    return ok();
+  }
+  if (std::strcmp(name, "onepass_spin_limit") == 0) {
+    if (value < 0 || value > (1 << 30))
+      return fail(DPF_ERR_INVALID_ARGUMENT, "onepass_spin_limit must be in [0, 2^30]");
+    g_onepass_spin.store((int)value);
+    dpf::set_onepass_testing(g_onepass_spin.load(), g_onepass_never.load());
+    return ok();
+  }
+  if (std::strcmp(name, "onepass_never_ready") == 0) {
+    if (value != 0 && value != 1)
+      return fail(DPF_ERR_INVALID_ARGUMENT, "onepass_never_ready must be 0 or 1");
+    g_onepass_never.store((int)value);
+    dpf::set_onepass_testing(g_onepass_spin.load(), g_onepass_never.load());
     return ok();
   }
   if (std::strcmp(name, "workspace_keep_bytes") == 0) {
@@ -1346,6 +1387,8 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
 int64_t dpfused_get_option(const char* name) {
   if (name == nullptr) return -1;
   if (std::strcmp(name, "norm_path") == 0) return g_norm_path.load();
+  if (std::strcmp(name, "onepass_spin_limit") == 0) return g_onepass_spin.load();
+  if (std::strcmp(name, "onepass_never_ready") == 0) return g_onepass_never.load();
   if (std::strcmp(name, "timing") == 0) return g_timing.load();
   if (std::strcmp(name, "workspace_keep_bytes") == 0) return g_keep_bytes.load();
   if (std::strcmp(name, "workspace_limit_bytes") == 0) return g_ws_limit.load();

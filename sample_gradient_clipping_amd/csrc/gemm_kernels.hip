@@ -659,12 +659,13 @@ size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec) {
 }
 
 size_t norm_workspace_bytes(const LayerArgs& p, NormPath path, bool vec) {
-  if (!use_big(p, vec)) return 0;
+  if (!use_big(p, vec) || path == NormPath::kOnePass) return 0;
   if (path == NormPath::kGram) return gram_big_workspace_bytes(p);
   return path == NormPath::kStaged ? staged_big_workspace_bytes(p) : 0;
 }
 
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
+  if (path == NormPath::kOnePass) return onepass_tiles(p.din, p.dout);
   if (path == NormPath::kGram && use_big(p, vec)) return gram_big_items_per_sample(p.T);
   if (path == NormPath::kGram) {
     const int nt = (p.T + kTileM - 1) / kTileM;

@@ -12,7 +12,11 @@ enum DType { kF32 = 0, kBF16 = 1 };
 // kStaged (large-tile path only): the direct kernel also stores every
 // per-sample gradient tile (fp32) in the workspace, and the accumulate phase
 // is launch_staged_combine over those tiles instead of a second contraction.
-enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2, kStaged = 3 };
+// kOnePass (large-tile layout, single-layer calls only): one cooperative
+// kernel computes each per-sample gradient tile once, reduces the per-sample
+// norms across workgroups and adds c_i g_i to a running sum in registers
+// (launch_onepass); no separate norm or accumulate phase.
+enum class NormPath { kAuto = 0, kGram = 1, kDirect = 2, kStaged = 3, kOnePass = 4 };
 
 // Tokens covered by one word of the per-sample row-activity bits.
 constexpr int kBitsTokens = 32;
@@ -136,6 +140,20 @@ size_t staged_big_workspace_bytes(const LayerArgs& p);
 int staged_big_partials_per_sample(const LayerArgs& p);
 hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s);
+
+// Single-pass fused kernel (onepass.hip): one workgroup per 128 x 128 output
+// tile, all resident at once.  p.partials: onepass_workspace_bytes(p) of
+// per-(sample, tile) slots.  Writes p.out (with noise, / denom, beta) and
+// norms_out.  hipErrorCooperativeLaunchTooLarge when the tiles cannot all
+// be resident.
+int onepass_tiles(int din, int dout);
+int onepass_resident_limit();
+size_t onepass_workspace_bytes(const LayerArgs& p);
+hipError_t launch_onepass(const LayerArgs& p, float C, float* norms_out, hipStream_t s);
+// Testing hooks of the single-pass kernel's bounded waits: tries of a
+// blocking poll (default 2^20), and never_ready != 0 to treat every fetch of
+// partials as incomplete (every bounded wait then gives up: NaN outputs).
+void set_onepass_testing(int spin_limit, int never_ready);
 
 // Large-tile bf16 Gram-norm kernel (gram_big.hip).
 int gram_big_items_per_sample(int T);

@@ -157,7 +157,9 @@ int main(void) {
   /* options */
   EXPECT(dpfused_set_option("bogus", 1), DPF_ERR_INVALID_ARGUMENT);
   EXPECT(dpfused_set_option(NULL, 1), DPF_ERR_INVALID_ARGUMENT);
-  EXPECT(dpfused_set_option("norm_path", 4), DPF_ERR_INVALID_ARGUMENT);
+  EXPECT(dpfused_set_option("norm_path", 5), DPF_ERR_INVALID_ARGUMENT);
+  EXPECT(dpfused_set_option("norm_path", 4), DPF_OK);
+  EXPECT(dpfused_set_option("onepass_never_ready", 2), DPF_ERR_INVALID_ARGUMENT);
   EXPECT(dpfused_set_option("norm_path", 3), DPF_OK);
   if (dpfused_get_option("norm_path") != 3) ++g_failures;
   EXPECT(dpfused_set_option("norm_path", 0), DPF_OK);

@@ -65,7 +65,17 @@ def test_options(L):
     assert L.dpfused_set_option(b"norm_path", 3) == DPF_OK
     assert L.dpfused_get_option(b"norm_path") == 3
     assert L.dpfused_set_option(b"norm_path", 0) == DPF_OK
-    assert L.dpfused_set_option(b"norm_path", 4) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"norm_path", 4) == DPF_OK
+    assert L.dpfused_get_option(b"norm_path") == 4
+    assert L.dpfused_set_option(b"norm_path", 0) == DPF_OK
+    assert L.dpfused_set_option(b"norm_path", 5) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"onepass_spin_limit", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"onepass_never_ready", 2) == DPF_ERR_INVALID_ARGUMENT
+    spin = L.dpfused_get_option(b"onepass_spin_limit")
+    assert spin == 1 << 20 and L.dpfused_get_option(b"onepass_never_ready") == 0
+    assert L.dpfused_set_option(b"onepass_spin_limit", 7) == DPF_OK
+    assert L.dpfused_get_option(b"onepass_spin_limit") == 7
+    assert L.dpfused_set_option(b"onepass_spin_limit", spin) == DPF_OK
     assert L.dpfused_set_option(b"norm_path", -1) == DPF_ERR_INVALID_ARGUMENT
     keep = L.dpfused_get_option(b"workspace_keep_bytes")
     assert keep == 512 << 20
