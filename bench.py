@@ -248,6 +248,32 @@ def measure_configs(dp, torch, steps, warmup):
           "as above, sigma 0", peak=PEAK_FP32_TFLOPS)
     dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
           "bf16, sigma 0.8; inputs (126 MB) resident in the Infinity Cache across calls")
+    # the GPT-2 layer on each norm path, one after another on the same inputs:
+    # Gram, direct, the single pass (each per-sample gradient once, on chip)
+    # and the opt-in staged form
+    lin = workloads.config_c2().linears[0]
+    X, G = upload(lin.X, torch), upload(lin.G, torch)
+    o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
+    nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+    f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+    by_path = {}
+    for path, name in ((1, "gram"), (2, "direct"), (4, "one pass"), (3, "staged")):
+        dp.set_option("norm_path", path)
+        try:
+            call = lambda: dp.linear_clip_accumulate(X, G, None, C=lin.C, sigma=lin.sigma,
+                                                     grad_out=o, norms_out=nrm)
+            mem = call_memory(dp)
+            ms = time_calls(torch, call, steps, warmup)
+            taken = norm_path_of(dp, call)
+            by_path[name] = {"ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                             "norm_path_taken": taken, "extra_device_bytes_per_call_max": mem()}
+        finally:
+            dp.set_option("norm_path", 0)
+    out["c2_gpt2_up_by_norm_path"] = {
+        "note": "as c2, each norm path forced in turn (the automatic choice is listed above)",
+        **by_path}
+    del X, G, o, nrm
+
     # the same layer with its bias (weight and bias clipped together)
     lin = workloads.config_c2().linears[0]
     X, G = upload(lin.X, torch), upload(lin.G, torch)

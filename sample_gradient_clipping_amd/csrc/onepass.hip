@@ -30,7 +30,7 @@
 // accumulators, in four sets (running sum, two waiting samples, current).
 // Operands are token-major ("K-outer") as in the large-tile accumulate
 // kernel: 32-token steps of the tile's 128 X columns and 128 G columns
-// (16 KiB) go from global memory into a ring of six LDS slots by 16-byte
+// (16 KiB) go from global memory into a ring of nine LDS slots by 16-byte
 // buffer loads that write LDS directly; rows are 256 bytes, the 16-byte chunk
 // c of row k at chunk c ^ 4 (k mod 4), read back with gfx950's transposing
 // LDS read.  Waves 4..7 issue all the loads; waves 0..3 issue none, so wave 0
@@ -52,8 +52,8 @@ constexpr int kKT = 32;                       // tokens per step
 constexpr int kRowBytes = kTile * 2;          // one token row of one operand, bf16
 constexpr int kOpBytes = kKT * kRowBytes;     // 8 KiB
 constexpr int kStageBytes = 2 * kOpBytes;     // 16 KiB: the X rows, then the G rows
-constexpr int kStages = 6;
-constexpr int kRingBytes = kStages * kStageBytes;   // 96 KiB
+constexpr int kStages = 9;
+constexpr int kRingBytes = kStages * kStageBytes;   // 144 KiB
 constexpr int kRedBytes = 256;                      // wave sums, factor, flags
 constexpr int kLdsBytes = kRingBytes + kRedBytes;
 constexpr int kFirstDmaWave = 4;                    // waves 4..7 load the operands
@@ -95,12 +95,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, 
 // Wait until at most `steps` of this wave's most recent DMA steps are in flight.
 __device__ __forceinline__ void wait_dma(int steps) {
   static_assert(kDmaPerWave == 4, "wait_dma encodes 4 DMAs per step");
-  if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (steps == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if (steps == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (steps == 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if (steps == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  static_assert(kStages <= 9, "wait_dma encodes at most 8 steps in flight");
+  switch (steps) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+  }
 }
 
 __device__ __forceinline__ void lds_reads_done() {
@@ -484,8 +490,11 @@ __device__ void body(const LayerArgs& p, const Params& q, unsigned char* smem) {
       }
       if (lane == 0) sh->ready = rdy;
     }
+    // Barriers here are plain (no memory fence): the waves exchange data
+    // through LDS only, and a fence would make the loading waves wait for
+    // every operand load in flight.
     lds_reads_done();
-    __syncthreads();
+    step_barrier();
     if (wave == 0 && lane == 0) {
       double tot = 0.0;
 #pragma unroll
@@ -496,9 +505,11 @@ __device__ void body(const LayerArgs& p, const Params& q, unsigned char* smem) {
     if (sh->ready) fold();
     // both waiting places full: the oldest must be folded before b can wait
     if (b - fold_next == 2) {
-      __syncthreads();                  // every wave has read sh->ready / sh->fac
+      lds_reads_done();                 // every wave has read sh->ready / sh->fac
+      step_barrier();
       if (wave == 0) fetch_blocking(fold_next);
-      __syncthreads();
+      lds_reads_done();
+      step_barrier();
       fold();
     }
     if ((b & 1) == 0) copy(w0, cur);
@@ -520,9 +531,11 @@ __device__ void body(const LayerArgs& p, const Params& q, unsigned char* smem) {
 #pragma unroll 1
   while (fold_next < p.B) {
     if (wave == 0) fetch_blocking(fold_next);
-    __syncthreads();
+    lds_reads_done();
+    step_barrier();
     fold();
-    __syncthreads();
+    lds_reads_done();
+    step_barrier();
   }
 
   // ---- epilogue: (run + noise_std xi) / denom, from the registers
