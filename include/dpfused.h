@@ -231,6 +231,30 @@ dpf_status dpfused_linear_clip_accumulate_projected_seeded(
     uint64_t p_offset, float p_scale, float C, float sigma, uint64_t seed, uint64_t offset,
     float* grad_out, float* norms_out, void* stream);
 
+/* The projection step of the projected variant alone (same explainer,
+ * Methodology, "Order of Operations": the activations are projected before
+ * the per-sample gradient is formed, clipped and noised):
+ *
+ *   Y[b][t][j] = sum_d X~[b][t][d] P[d][j]     (X~: X with masked rows zero)
+ *
+ * accumulated in float32 and rounded to X's dtype (round to nearest even for
+ * bf16) -- exactly the Y that the projected calls form in their workspace.
+ *
+ *   X     as for the dense call (bf16 or float32)
+ *   mask  [B, T] uint8 or NULL; masked rows of Y are zero
+ *   P     [din, r] row-major, X's dtype, 16-byte aligned
+ *   r     >= 1
+ *   Y     [B, T, r] row-major, contiguous, X's dtype, 16-byte aligned;
+ *         owned by the caller, overwritten
+ *
+ * Errors: DPF_ERR_INVALID_ARGUMENT for NULL P or Y or r < 1; as for the
+ * dense call for X; DPF_ERR_UNSUPPORTED for unaligned P or Y or r too large;
+ * DPF_ERR_OUT_OF_MEMORY when the split-K workspace of the fallback tiles
+ * (used for float32 and for shapes the bf16 kernel does not take) cannot be
+ * allocated. */
+dpf_status dpfused_project(const dpf_act* X, const uint8_t* mask, const void* P, int64_t r,
+                           void* Y, void* stream);
+
 /* Per-sample squared norms ||G~_i^T X~_i||^2 only, in float64, written to
  * sqnorms_out[B] (device).  With accumulate != 0 the values are ADDED to what
  * sqnorms_out holds (summing over several linears gives the squared norm of
@@ -383,7 +407,21 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                1 = always Gram; 2 = always direct (gradient tiles
  *                computed and dropped, then a second contraction); 3 =
  *                staged where the call allows it (bf16 single-layer and
- *                group calls whose staged tiles fit in 16 GiB), else direct
+ *                group calls whose staged tiles fit in 16 GiB), else direct;
+ *                4 = single pass where the call allows it (the dense
+ *                single-layer calls, bf16 on the large-tile layout, at most
+ *                256 output tiles of 128 x 128 that can all be resident at
+ *                once, not under graph capture: one cooperative kernel that
+ *                computes each per-sample gradient tile once and reduces the
+ *                norms across workgroups while the next sample is
+ *                contracted), else the automatic choice
+ *   "onepass_spin_limit"  single pass: tries of a blocked wait for another
+ *                workgroup's partial norms before the call gives up and
+ *                writes NaN to its outputs (default 2^20; 0..2^30)
+ *   "onepass_never_ready"  testing only: 1 = every fetch of partials in the
+ *                single pass counts as incomplete, so every blocked wait
+ *                gives up after "onepass_spin_limit" tries (the kernel still
+ *                exits; the outputs are NaN); 0 (default) = normal
  *   "timing"     1 = record a HIP event pair around every kernel the library
  *                launches, on the launch stream (see dpfused_timing_*); 0 = off
  *   "workspace_keep_bytes"  bytes of workspace the library keeps reserved
@@ -413,7 +451,7 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                print the kernel's name and the HIP error to stderr if it
  *                failed; slow, for finding a failing launch; 0 = off (default)
  * Defaults are read from the environment when the library is loaded:
- * DPFUSED_NORM_PATH ("auto", "gram", "direct", "staged" or 0-3),
+ * DPFUSED_NORM_PATH ("auto", "gram", "direct", "staged", "onepass" or 0-4),
  * DPFUSED_TRACE and DPFUSED_DEBUG (0/1), DPFUSED_WS_LIMIT (bytes).
  * Read-only (dpfused_get_option): "workspace_reserved_bytes" and
  * "workspace_reserved_high", what the current device's pool holds now and at

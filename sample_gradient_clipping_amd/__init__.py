@@ -22,7 +22,7 @@ from ._lib import DpfAct, DpfError, DPF_BF16, DPF_F32  # noqa: F401
 
 __all__ = [
     "linear_clip_accumulate", "linear_clip_accumulate_noalloc", "linear_clip_accumulate_projected",
-    "linear_clip_accumulate_projected_seeded", "linear_clip_accumulate_bias",
+    "linear_clip_accumulate_projected_seeded", "linear_clip_accumulate_bias", "project",
     "group_clip_accumulate", "consecutive_offsets", "projected_adam_step",
     "per_sample_sqnorms",
     "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
@@ -194,6 +194,25 @@ def linear_clip_accumulate_projected(X, G, P, mask=None, C: float = 1.0, sigma: 
         _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
+
+
+def project(X, P, mask=None, out=None, stream=None):
+    """The projection step alone: Y = X~ P ([B, T, r], X's dtype; masked rows zero),
+    as the projected calls form it."""
+    torch = _torch()
+    xa = _act(X)
+    B, T = X.shape[0], X.shape[1]
+    if P.dim() != 2 or not P.is_contiguous() or P.shape[0] != X.shape[2] or P.dtype != X.dtype:
+        raise ValueError("P must be a contiguous [din, r] tensor of X's dtype")
+    _same_device(P, X.device, "P")
+    r = P.shape[1]
+    if out is None:
+        out = torch.empty((B, T, r), dtype=X.dtype, device=X.device)
+    _check_out(out, (B, T, r), "out", X.device, dtype=X.dtype)
+    st = _lib.lib().dpfused_project(ctypes.byref(xa), _mask_ptr(mask, B, T, X.device), P.data_ptr(),
+                                    int(r), out.data_ptr(), _stream(X, stream))
+    _lib.check(st)
+    return out
 
 
 def linear_clip_accumulate_projected_seeded(X, G, r: int, mask=None, p_seed: int = 0,

@@ -97,6 +97,8 @@ _SIGNATURES = {
     "dpfused_timing_reset": (None, []),
     "dpfused_timing_collect": (ctypes.c_int32, []),
     "dpfused_timing_name": (ctypes.c_char_p, [ctypes.c_int32]),
+    "dpfused_project": (ctypes.c_int, [ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "dpfused_timing_total_ms": (ctypes.c_double, [ctypes.c_int32]),
     "dpfused_timing_launches": (ctypes.c_int64, [ctypes.c_int32]),
     "dpfused_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -603,16 +603,19 @@ constexpr int kMaxSplit = 16;   // P never exceeds this
 // Llama-13B shapes (dense and ragged): one 32-token step of a 256 x 256 tile
 // ~0.8 us, a piece's pipeline fill and epilogue ~4 us (workgroups left alone
 // in a partly filled round run faster, which hides most of it), the fixup
-// ~5 us plus 0.06 us per partial (256 KiB written, then read).  Runs on the
-// host over every step, and on the device for masked calls, over the active
-// steps only the device knows.
+// ~5 us plus 0.06 us per partial (256 KiB written, then read).  Pieces are
+// at least 4 steps long: layers with a handful of tiles (the RoBERTa
+// r-space calls: 4 tiles, 128 steps) then spread over 64 workgroups instead
+// of 32; at the Llama and GPT-2 shapes the model's choice is the same as
+// with a 16-step minimum.  Runs on the host over every step, and on the
+// device for masked calls, over the active steps only the device knows.
 __host__ __device__ inline int split_tiles(int R, int G, int n, int maxP) {
   if (R == 0) return 1;
   const double step_us = 0.8, piece_us = 4.0;
   double best = n * step_us + piece_us;   // P = 1: one more round
   int bestP = 1;
   for (int P = 2; P <= maxP; ++P) {
-    if ((double)n / P < 16.0) break;      // pieces of >= 16 steps
+    if ((double)n / P < 4.0) break;       // pieces of >= 4 steps
     const int S = (R * P + G - 1) / G;
     const double t = S * ((double)n / P * step_us + piece_us) + 5.0 + 0.06 * R * P;
     if (t < best) {

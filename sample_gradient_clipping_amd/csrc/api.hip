@@ -46,7 +46,7 @@ std::atomic<int> g_onepass_spin{1 << 20};   // single pass: tries of a blocking 
 std::atomic<int> g_onepass_never{0};        // single pass: testing, every wait gives up
 
 // Defaults from the environment, read once when the library is loaded:
-// DPFUSED_NORM_PATH (auto, gram, direct, staged or 0-3), DPFUSED_TRACE,
+// DPFUSED_NORM_PATH (auto, gram, direct, staged, onepass or 0-4), DPFUSED_TRACE,
 // DPFUSED_DEBUG (0/1), DPFUSED_WS_LIMIT (bytes).
 bool read_env() {
   if (const char* v = std::getenv("DPFUSED_NORM_PATH")) {
@@ -756,8 +756,9 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   pa.p_seed = p_seed;
   pa.p_offset = p_offset;
   pa.p_scale = p_scale;
-  pa.splits = dpf::project_splits(pa);
-  const size_t pbytes = dpf::project_workspace_bytes(pa);
+  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
+  pa.splits = dpf::project_splits(pa, pvec);
+  const size_t pbytes = dpf::project_workspace_bytes(pa, pvec);
   const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
   // Reserve the layer workspace now so that a single allocation covers both.
   dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
@@ -770,7 +771,6 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   Y.data = ws.at<void>(off_y);
   pa.Y = const_cast<void*>(Y.data);
   pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
-  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
   hipError_t e = dpf::launch_project(pa, pvec, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
@@ -1043,6 +1043,41 @@ dpf_status dpfused_linear_clip_accumulate_projected_seeded(
                 "the noise blocks overlap the projection's blocks under the same seed");
   return projected_layer(X, G, mask, nullptr, 1, p_seed, p_offset, projection_scale(p_scale, r),
                          r, C, sigma, seed, offset, grad_out, norms_out, stream);
+}
+
+dpf_status dpfused_project(const dpf_act* X, const uint8_t* mask, const void* P, int64_t r,
+                           void* Y, void* stream) {
+  CallScope call_("dpfused_project");
+  dpf_status st = check_act(X, "X");
+  if (st != DPF_OK) return st;
+  if (P == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "P is NULL");
+  if (Y == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "Y is NULL");
+  if (r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "r must be >= 1");
+  if (r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "r too large");
+  if (!aligned16(P)) return fail(DPF_ERR_UNSUPPORTED, "P is not 16-byte aligned");
+  if (!aligned16(Y)) return fail(DPF_ERR_UNSUPPORTED, "Y is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t es = elem_size(X->dtype);
+  dpf::ProjArgs pa{};
+  pa.X = to_act(X);
+  pa.P = P;
+  pa.Y = Y;
+  pa.dtype = X->dtype;
+  pa.B = (int)X->B;
+  pa.T = (int)X->T;
+  pa.din = (int)X->D;
+  pa.r = (int)r;
+  pa.mask = mask;
+  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
+  pa.splits = dpf::project_splits(pa, pvec);
+  const size_t pbytes = dpf::project_workspace_bytes(pa, pvec);
+  Workspace ws(s);
+  const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
+  const hipError_t e = dpf::launch_project(pa, pvec, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return ok();
 }
 
 dpf_status dpfused_per_sample_sqnorms(const dpf_act* X, const dpf_act* G, const uint8_t* mask,

@@ -390,30 +390,6 @@ __global__ void __launch_bounds__(kNT) gram_norm_kernel(LayerArgs p) {
 // tile, chunk), each storing its fp32 partial product; project_reduce_kernel
 // sums the chunks in order and rounds.
 // ===========================================================================
-// One loader chunk of P regenerated instead of read: P[d][c .. c+kVec) =
-// p_scale * xi_e for e = d*r + c .., rounded to the storage type exactly as
-// gaussian_fill writes it.  r is a multiple of 8, so a chunk covers whole
-// Philox blocks (two for bf16, one for fp32).
-template <class E>
-__device__ __forceinline__ u32x4 gen_p_chunk(const ProjArgs& p, int d, int c) {
-  if (d >= p.din || c >= p.r) return u32x4{0u, 0u, 0u, 0u};
-  const uint64_t blk = p.p_offset + (((uint64_t)d * (uint64_t)p.r + (uint64_t)c) >> 2);
-  if constexpr (sizeof(typename E::storage) == 2) {
-    const f32x4 z0 = normals_of_block(philox_block(p.p_seed, blk));
-    const f32x4 z1 = normals_of_block(philox_block(p.p_seed, blk + 1));
-    const float v[8] = {p.p_scale * z0.x, p.p_scale * z0.y, p.p_scale * z0.z, p.p_scale * z0.w,
-                        p.p_scale * z1.x, p.p_scale * z1.y, p.p_scale * z1.z, p.p_scale * z1.w};
-    uint16_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e]);
-    return __builtin_bit_cast(u32x4, h);
-  } else {
-    const f32x4 z = normals_of_block(philox_block(p.p_seed, blk));
-    const float v[4] = {p.p_scale * z.x, p.p_scale * z.y, p.p_scale * z.z, p.p_scale * z.w};
-    return __builtin_bit_cast(u32x4, v);
-  }
-}
-
 template <class E, bool VEC, bool GEN>
 __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
   using S = typename E::storage;
@@ -455,7 +431,8 @@ __global__ void __launch_bounds__(kNT) project_kernel(ProjArgs p) {
 #pragma unroll
       for (int i = 0; i < LP::N; ++i) {
         const int q = threadIdx.x + kNT * i;
-        lp.r[i] = gen_p_chunk<E>(p, k0 + q / LP::CPR, j0 + (q % LP::CPR) * E::kVec);
+        lp.r[i] = gen_p_chunk<E>(p.p_seed, p.p_offset, p.p_scale, p.din, p.r, k0 + q / LP::CPR,
+                                 j0 + (q % LP::CPR) * E::kVec);
       }
     } else {
       lp.load(P, p.r, p.din, nullptr, k0, j0, p.r);
@@ -698,17 +675,6 @@ hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t 
   if (p.dtype == kBF16) return vec ? launch_direct_t<BF16, true>(p, s) : launch_direct_t<BF16, false>(p, s);
   return vec ? launch_direct_t<F32, true>(p, s) : launch_direct_t<F32, false>(p, s);
 }
-// din chunks of the projection: enough (output tile, chunk) workgroups for
-// one per compute unit, each chunk at least 4 K-steps long, at most 8 chunks.
-int project_splits(const ProjArgs& p) {
-  const int KT = p.dtype == kBF16 ? Cfg<BF16>::KT : Cfg<F32>::KT;
-  const int64_t ntok = (int64_t)p.B * p.T;
-  const int64_t tiles = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
-  const int nk = (p.din + KT - 1) / KT;
-  const int64_t want = (device_cus() + tiles - 1) / tiles;
-  return (int)std::max<int64_t>(1, std::min<int64_t>({want, 8, nk / 4}));
-}
-
 // A projection drawn from its seed regenerates its slice of P in every token
 // tile.  With more than one token tile it is cheaper to draw P once into the
 // call's workspace (din*r elements, after the split partials) with the
@@ -723,13 +689,31 @@ static bool project_draws_p_once(const ProjArgs& p) {
   return p.gen != 0 && !p_in_kernels() && (ntok + kTileN - 1) / kTileN > 1;
 }
 
+// din chunks of the projection.  One wherever the bf16 projection kernel
+// (proj_big.hip, never split) takes the shape; it also draws P in its own
+// tiles when asked, so a P drawn in the kernel, drawn once into workspace or
+// stored meets the same arithmetic and gives the same bits.  Otherwise (the
+// generic tiles) enough (output tile, chunk) workgroups for one per compute
+// unit, each chunk at least 4 K-steps long, at most 8 chunks.
+int project_splits(const ProjArgs& p, bool vec) {
+  ProjArgs q = p;
+  q.gen = 0;
+  if (project_big_shape_ok(q, vec)) return 1;
+  const int KT = p.dtype == kBF16 ? Cfg<BF16>::KT : Cfg<F32>::KT;
+  const int64_t ntok = (int64_t)p.B * p.T;
+  const int64_t tiles = ((p.r + kTileM - 1) / kTileM) * ((ntok + kTileN - 1) / kTileN);
+  const int nk = (p.din + KT - 1) / KT;
+  const int64_t want = (device_cus() + tiles - 1) / tiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, 8, nk / 4}));
+}
+
 static size_t project_split_bytes(const ProjArgs& p, int sp) {
   const size_t b = sp == 1 ? 0 : (size_t)sp * p.B * p.T * p.r * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
 
-size_t project_workspace_bytes(const ProjArgs& p) {
-  const int sp = project_splits(p);
+size_t project_workspace_bytes(const ProjArgs& p, bool vec) {
+  const int sp = project_splits(p, vec);
   if (!project_draws_p_once(p)) return project_split_bytes(p, sp);
   return project_split_bytes(p, sp) + (size_t)p.din * p.r * (p.dtype == kBF16 ? 2 : 4);
 }
@@ -745,6 +729,7 @@ hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s) {
     if (e != hipSuccess) return e;
     return launch_project(q, vec, s);
   }
+  if (p.splits == 1 && project_big_eligible(p, vec)) return launch_project_big(p, s);
   if (p.gen) {
     if (p.dtype == kBF16)
       return vec ? launch_project_t<BF16, true, true>(p, s) : launch_project_t<BF16, false, true>(p, s);

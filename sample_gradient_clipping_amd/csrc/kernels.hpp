@@ -126,8 +126,13 @@ hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t 
 hipError_t launch_project(const ProjArgs& p, bool vec, hipStream_t s);
 // Number of din chunks launch_project splits Y = X P into, and the fp32
 // partial buffer (p.part) that takes when above 1.
-int project_splits(const ProjArgs& p);
-size_t project_workspace_bytes(const ProjArgs& p);
+int project_splits(const ProjArgs& p, bool vec);
+size_t project_workspace_bytes(const ProjArgs& p, bool vec);
+// The bf16 projection kernel (proj_big.hip): the shape conditions alone, and
+// with the pointers of a call (P 16-byte, Y 8-byte aligned).
+bool project_big_shape_ok(const ProjArgs& p, bool vec);
+bool project_big_eligible(const ProjArgs& p, bool vec);
+hipError_t launch_project_big(const ProjArgs& p, hipStream_t s);
 // Partials per sample written by the norm kernel launch_norm picks for (p, path, vec).
 int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec);
 

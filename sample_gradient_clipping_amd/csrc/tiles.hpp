@@ -163,4 +163,31 @@ __device__ __forceinline__ f32x16 mfma(const typename Frag<E>::type& a,
   else return mfma_32x32x2(a, b, c);
 }
 
+// One 16-byte chunk of a projection P regenerated instead of read:
+// P[d][c .. c + 16/sizeof(storage)) = scale * xi_e for e = d*r + c ..,
+// xi from Philox4x32-10 (seed, offset) and Box-Muller, rounded to the storage
+// type exactly as the Gaussian fill writes it; zero for d >= din or c >= r.
+// r is a multiple of 8, so a chunk covers whole Philox blocks (two for bf16,
+// one for fp32).
+template <class E>
+__device__ __forceinline__ u32x4 gen_p_chunk(uint64_t seed, uint64_t offset, float scale, int din,
+                                             int r, int d, int c) {
+  if (d >= din || c >= r) return u32x4{0u, 0u, 0u, 0u};
+  const uint64_t blk = offset + (((uint64_t)d * (uint64_t)r + (uint64_t)c) >> 2);
+  if constexpr (sizeof(typename E::storage) == 2) {
+    const f32x4 z0 = normals_of_block(philox_block(seed, blk));
+    const f32x4 z1 = normals_of_block(philox_block(seed, blk + 1));
+    const float v[8] = {scale * z0.x, scale * z0.y, scale * z0.z, scale * z0.w,
+                        scale * z1.x, scale * z1.y, scale * z1.z, scale * z1.w};
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e]);
+    return __builtin_bit_cast(u32x4, h);
+  } else {
+    const f32x4 z = normals_of_block(philox_block(seed, blk));
+    const float v[4] = {scale * z.x, scale * z.y, scale * z.z, scale * z.w};
+    return __builtin_bit_cast(u32x4, v);
+  }
+}
+
 }  // namespace dpf

@@ -181,6 +181,27 @@ def test_projected_argument_checks(L):
         == DPF_ERR_INVALID_ARGUMENT
 
 
+def test_project_argument_checks(L):
+    X = _act()
+    f = L.dpfused_project
+    ok_args = dict(P=FAKE, r=4, Y=FAKE)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return f(ctypes.byref(X), None, a["P"], a["r"], a["Y"], None)
+
+    assert call(P=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(Y=None) == DPF_ERR_INVALID_ARGUMENT
+    assert call(r=0) == DPF_ERR_INVALID_ARGUMENT
+    assert call(r=-3) == DPF_ERR_INVALID_ARGUMENT
+    assert call(P=FAKE + 8) == DPF_ERR_UNSUPPORTED
+    assert call(Y=FAKE + 8) == DPF_ERR_UNSUPPORTED
+    assert call(r=1 << 40) == DPF_ERR_UNSUPPORTED
+    bad = _act(B=0)
+    assert f(ctypes.byref(bad), None, FAKE, 4, FAKE, None) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_last_error() != b""
+
+
 def test_ex_argument_checks(L):
     X, G = _act(), _act(D=16)
     f = L.dpfused_linear_clip_accumulate_ex
