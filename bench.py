@@ -54,12 +54,12 @@ KERNEL_COUNTERS = {
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     "kernels": {
-        "accumulate": {"sources_sha256": "653aa1b0b5cba054cba5a34c86255f191b3e2e3262c3d1720655a1fe6587a6ff",
-                       "fetch_kib": 1129826.69, "write_kib": 279698.29, "mfma_busy_pct": 59.49,
-                       "trace_avg_us": 1299.4},
+        "accumulate": {"sources_sha256": "760532996b0465f80e64364a5a7a9ae8d1aeee08ae7488488286ad7d243262ec",
+                       "fetch_kib": 1131507.42, "write_kib": 279698.29, "mfma_busy_pct": 61.96,
+                       "trace_avg_us": 1255.0},
         "gram_norm": {"sources_sha256": "a22f5cd2595a5c58255194bb6fda470b276f620ce31f9b99869ede600f370a06",
-                      "fetch_kib": 422855.55, "write_kib": 152505.42, "mfma_busy_pct": 50.23,
-                      "trace_avg_us": 511.9},
+                      "fetch_kib": 416404.74, "write_kib": 152505.24, "mfma_busy_pct": 51.28,
+                      "trace_avg_us": 503.0},
     },
     # --norm-path values that run these kernels on every linear of the workload
     "paths": ("0", "1"),
