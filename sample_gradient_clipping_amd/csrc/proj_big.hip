@@ -14,17 +14,22 @@
 // Workgroup: 512 threads = 8 waves, two per SIMD.  Waves w and w + 4 own the
 // same 32 x 32 block of v_mfma_f32_32x32x16_bf16 accumulators (A = P^T: rows
 // along r; B = X~^T: columns along tokens; the 2 x 2 blocks of the tile), the
-// first on features 0..31 of every 64-feature step, the second on 32..63: two
-// independent accumulation chains per SIMD, each wave's LDS reads overlapping
-// its partner's MFMAs.  At the end the second group's sums go through LDS to
-// the first, which adds them (fixed order) and stores Y; each lane ends with
-// 4 consecutive r of one token.  Both operands go from global memory to LDS
-// with 16-byte-per-lane buffer loads that write LDS directly, into a ring of
-// six 16 KiB slots filled five steps ahead, one barrier per step.
-//   X rows (tokens, features contiguous: "K-inner") are read back as whole
-//   16-byte fragments; chunk c of row t sits at c ^ ((t >> 1) & 7).
-//   P rows (features, r contiguous: "K-outer") are read with the transposing
-//   ds_read_b64_tr_b16; chunk c of row k sits at c ^ (4 ((k >> 1) & 1)).
+// first on features 0..63 of every 128-feature step, the second on 64..127,
+// each in two accumulator sets (alternate 16-feature substeps) so that its
+// MFMAs form two independent chains.  At these sizes a step's cost is its
+// serial chain (barrier, LDS read latency, dependent MFMAs), not its data or
+// arithmetic, so each step carries as many features as the LDS ring allows.
+// At the end each wave adds its two sets, the second group's sums go through
+// LDS to the first, which adds them (fixed order) and stores Y; each lane
+// ends with 4 consecutive r of one token.  Both operands go from global
+// memory to LDS with 16-byte-per-lane buffer loads that write LDS directly,
+// into a ring of four 32 KiB slots filled three steps ahead, one barrier per
+// step.
+//   X rows (tokens, features contiguous: "K-inner", 256 B per step) are read
+//   back as whole 16-byte fragments; chunk c of row t sits at c ^ (t % 16).
+//   P rows (features, r contiguous: "K-outer", 128 B per step) are read with
+//   the transposing ds_read_b64_tr_b16; chunk c of row k sits at
+//   c ^ (4 ((k >> 1) & 1)).
 // Both placements keep the reads free of bank conflicts.  Rows past the end,
 // masked tokens and features past din read through out-of-range buffer
 // offsets, which return zeros.
@@ -37,19 +42,22 @@ namespace proj {
 constexpr int kNT = 512;
 constexpr int kWaves = kNT / 64;
 constexpr int kTile = 64;                      // r columns and tokens per tile
-constexpr int kKF = 64;                        // features per step
-constexpr int kRowBytes = kKF * 2;             // an X row or a P row of one step: 128 B
-constexpr int kOpBytes = 64 * kRowBytes;       // 8 KiB per operand per step
-constexpr int kStageBytes = 2 * kOpBytes;      // X rows, then P rows
-constexpr int kStages = 6;
-constexpr int kLdsBytes = kStages * kStageBytes;   // 96 KiB
-constexpr int kDmaPerStep = 2;                 // per wave per step: 8 rows of X, 8 rows of P
+constexpr int kKF = 128;                       // features per step
+constexpr int kXRowBytes = kKF * 2;            // an X row of one step: 256 B
+constexpr int kPRowBytes = kTile * 2;          // a P row (64 r columns): 128 B
+constexpr int kXBytes = kTile * kXRowBytes;    // 16 KiB: 64 token rows
+constexpr int kPBytes = kKF * kPRowBytes;      // 16 KiB: 128 feature rows
+constexpr int kStageBytes = kXBytes + kPBytes; // X rows, then P rows
+constexpr int kStages = 4;
+constexpr int kLdsBytes = kStages * kStageBytes;   // 128 KiB
+constexpr int kDmaPerOp = 2;                   // per wave per step: 2 KiB of X, 2 KiB of P
+constexpr int kDmaPerStep = 2 * kDmaPerOp;
 constexpr int kOOB = 0x7ffffff0;
 // Largest byte span of X or P this kernel addresses (32-bit buffer offsets,
 // with room above for the out-of-range offset).
 constexpr int64_t kMaxSpan = ((int64_t)1 << 31) - ((int64_t)1 << 20);
 
-__device__ __forceinline__ int swz_x(int row, int c) { return c ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_x(int row, int c) { return c ^ (row & 15); }
 __device__ __forceinline__ int swz_p(int k, int c) { return c ^ (((k >> 1) & 1) << 2); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -67,27 +75,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, 
 }
 
 // Wait until at most `steps` (0 .. kStages - 2) of this wave's most recent
-// DMA steps are in flight: two DMAs per step, or one when P is drawn in the
+// DMA steps are in flight: four DMAs per step, or two when P is drawn in the
 // kernel (GEN).
-template <int N>
-__device__ __forceinline__ void vmcnt_le() {
-  static_assert(N >= 0 && N <= 63, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 template <bool GEN>
 __device__ __forceinline__ void wait_dma(int steps) {
-  static_assert(kDmaPerStep == 2 && kStages <= 9, "wait_dma encodes up to 7 steps ahead");
-  constexpr int d = GEN ? 1 : 2;
-  switch (steps <= 0 ? 0 : steps >= 7 ? 7 : steps) {
-    case 0: vmcnt_le<0>(); break;
-    case 1: vmcnt_le<d>(); break;
-    case 2: vmcnt_le<2 * d>(); break;
-    case 3: vmcnt_le<3 * d>(); break;
-    case 4: vmcnt_le<4 * d>(); break;
-    case 5: vmcnt_le<5 * d>(); break;
-    case 6: vmcnt_le<6 * d>(); break;
-    default: vmcnt_le<7 * d>(); break;
-  }
+  static_assert(kDmaPerStep == 4 && kStages == 4, "wait_dma encodes up to 2 steps ahead");
+  if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (steps == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GEN ? 2 : 4) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GEN ? 4 : 8) : "memory");
 }
 
 // Workgroup barrier without a memory fence: each wave has seen its own DMA
@@ -109,31 +104,38 @@ __host__ __device__ inline int64_t x_span(const ProjArgs& p) {
   return ((int64_t)(p.B - 1) * p.X.stride_b + (int64_t)(p.T - 1) * p.X.stride_t + p.din) * 2;
 }
 
-// Per-lane DMA addressing, fixed for the whole K loop.  Wave w fills rows
-// 8 w .. 8 w + 7 of each operand's slot (1 KiB, one DMA each); lane l fills
-// physical chunk l % 8 of row 8 w + l / 8.
+// Per-lane DMA addressing, fixed for the whole K loop.  Wave w fills X rows
+// 8 w .. 8 w + 7 (DMA j: rows 8 w + 4 j .. +3, lane l physical chunk l % 16
+// of row 8 w + 4 j + l / 16) and P rows 16 w .. 16 w + 15 (DMA j: rows
+// 16 w + 8 j .. +7, lane l physical chunk l % 8 of row 16 w + 8 j + l / 8):
+// 1 KiB of consecutive LDS per DMA.
 struct Lanes {
-  uint32_t xoff;   // X: token row + logical chunk, bytes (kOOB: inactive)
-  int xf;          // first feature of the lane's X chunk within a step
-  uint32_t poff;   // P: row within the step + column chunk, bytes (kOOB: past r)
-  int pk;          // the P row (feature) within a step
-  int pcol;        // the first r column of the lane's P chunk
+  uint32_t xoff[kDmaPerOp];   // X: token row + logical chunk, bytes (kOOB: inactive)
+  int xf[kDmaPerOp];          // first feature of the lane's X chunk within a step
+  uint32_t poff[kDmaPerOp];   // P: row within the step + column chunk, bytes (kOOB: past r)
+  int pk[kDmaPerOp];          // the P row (feature) within a step
+  int pcol[kDmaPerOp];        // the first r column of the lane's P chunk
   __device__ __forceinline__ void init(const ProjArgs& p, int64_t q0, int j0) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t ntok = (int64_t)p.B * p.T;
-    const int row = 8 * wave + (lane >> 3);
-    const int cx = swz_x(row, lane & 7);
-    const int64_t tok = q0 + row;
-    bool on = tok < ntok;
-    if (on && p.mask != nullptr) on = p.mask[tok] != 0;
-    const int64_t b = tok / p.T, t = tok - b * p.T;
-    xf = 8 * cx;
-    xoff = on ? (uint32_t)((b * p.X.stride_b + t * p.X.stride_t + 8 * cx) * 2) : (uint32_t)kOOB;
-    const int cp = swz_p(row, lane & 7);
-    const int col = j0 + 8 * cp;
-    pk = row;
-    pcol = col;
-    poff = col < p.r ? (uint32_t)(((int64_t)row * p.r + col) * 2) : (uint32_t)kOOB;
+#pragma unroll
+    for (int j = 0; j < kDmaPerOp; ++j) {
+      const int row = 8 * wave + 4 * j + (lane >> 4);
+      const int cx = swz_x(row, lane & 15);
+      const int64_t tok = q0 + row;
+      bool on = tok < ntok;
+      if (on && p.mask != nullptr) on = p.mask[tok] != 0;
+      const int64_t b = tok / p.T, t = tok - b * p.T;
+      xf[j] = 8 * cx;
+      xoff[j] = on ? (uint32_t)((b * p.X.stride_b + t * p.X.stride_t + 8 * cx) * 2)
+                   : (uint32_t)kOOB;
+      const int k = 16 * wave + 8 * j + (lane >> 3);
+      const int cp = swz_p(k, lane & 7);
+      const int col = j0 + 8 * cp;
+      pk[j] = k;
+      pcol[j] = col;
+      poff[j] = col < p.r ? (uint32_t)(((int64_t)k * p.r + col) * 2) : (uint32_t)kOOB;
+    }
   }
 };
 
@@ -149,19 +151,25 @@ __device__ __forceinline__ void issue(const ProjArgs& p, __amdgpu_buffer_rsrc_t 
   const int k0 = k * kKF;
   const bool tail = k0 + kKF > p.din;
   const uint32_t sx = (uint32_t)k0 * 2u;
-  int xo = (int)ln.xoff;
-  if (tail && k0 + ln.xf >= p.din) xo = kOOB;
-  dma16(rx, xo, base + slot + wdst, sx);
-  if constexpr (GEN) {
-    const int lane = threadIdx.x & 63;
-    const int col = (int)(ln.poff == (uint32_t)kOOB ? p.r : ln.pcol);
-    *(u32x4*)(lds + slot + kOpBytes + wdst + 16 * lane) =
-        gen_p_chunk<BF16>(p.p_seed, p.p_offset, p.p_scale, p.din, p.r, k0 + ln.pk, col);
-  } else {
-    const uint32_t sp = (uint32_t)k0 * (uint32_t)p.r * 2u;
-    int po = (int)ln.poff;
-    if (tail && k0 + ln.pk >= p.din) po = kOOB;
-    dma16(rp, po, base + slot + kOpBytes + wdst, sp);
+#pragma unroll
+  for (int j = 0; j < kDmaPerOp; ++j) {
+    int xo = (int)ln.xoff[j];
+    if (tail && k0 + ln.xf[j] >= p.din) xo = kOOB;
+    dma16(rx, xo, base + slot + wdst + (uint32_t)j * 1024u, sx);
+  }
+#pragma unroll
+  for (int j = 0; j < kDmaPerOp; ++j) {
+    if constexpr (GEN) {
+      const int lane = threadIdx.x & 63;
+      const int col = ln.poff[j] == (uint32_t)kOOB ? p.r : ln.pcol[j];
+      *(u32x4*)(lds + slot + kXBytes + wdst + j * 1024 + 16 * lane) =
+          gen_p_chunk<BF16>(p.p_seed, p.p_offset, p.p_scale, p.din, p.r, k0 + ln.pk[j], col);
+    } else {
+      const uint32_t sp = (uint32_t)k0 * (uint32_t)p.r * 2u;
+      int po = (int)ln.poff[j];
+      if (tail && k0 + ln.pk[j] >= p.din) po = kOOB;
+      dma16(rp, po, base + slot + kXBytes + wdst + (uint32_t)j * 1024u, sp);
+    }
   }
 }
 
@@ -172,8 +180,8 @@ __device__ __forceinline__ u16x8 frag_p(const unsigned char* op, int m0, int ks)
   const int krow = ks * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int c16 = col >> 3, half = (col >> 2) & 1;
-  const unsigned char* p0 = op + krow * kRowBytes + swz_p(krow, c16) * 16 + half * 8;
-  const unsigned char* p1 = op + (krow + 4) * kRowBytes + swz_p(krow + 4, c16) * 16 + half * 8;
+  const unsigned char* p0 = op + krow * kPRowBytes + swz_p(krow, c16) * 16 + half * 8;
+  const unsigned char* p1 = op + (krow + 4) * kPRowBytes + swz_p(krow + 4, c16) * 16 + half * 8;
   const u16x4 lo = lds_read_tr16((const uint16_t*)p0);
   const u16x4 hi = lds_read_tr16((const uint16_t*)p1);
   u16x8 f;
@@ -188,7 +196,7 @@ __device__ __forceinline__ u16x8 frag_x(const unsigned char* op, int m0, int ks)
   const int lane = threadIdx.x & 63;
   const int row = m0 + (lane & 31);
   const int c = 2 * ks + (lane >> 5);
-  return *(const u16x8*)(op + row * kRowBytes + swz_x(row, c) * 16);
+  return *(const u16x8*)(op + row * kXRowBytes + swz_x(row, c) * 16);
 }
 
 // Tiles in token-major order (the r tiles of one token block adjacent), and
@@ -205,7 +213,7 @@ __global__ void __launch_bounds__(kNT) project_big_kernel(ProjArgs p) {
   const int64_t q0 = (int64_t)(L / ntr) * kTile;
   const int j0 = (L % ntr) * kTile;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = wave >> 2;               // features 32 half .. 32 half + 31 of each step
+  const int half = wave >> 2;               // features 64 half .. 64 half + 63 of each step
   const int wm = (wave >> 1) & 1, wn = wave & 1;
 
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.X.data, x_span(p));
@@ -213,12 +221,12 @@ __global__ void __launch_bounds__(kNT) project_big_kernel(ProjArgs p) {
   Lanes ln;
   ln.init(p, q0, j0);
   const uint32_t base = lds_addr(lds);
-  const uint32_t wdst = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+  const uint32_t wdst = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 2048u;
   const int n = (p.din + kKF - 1) / kKF;
 
-  f32x16 acc;
+  f32x16 acc[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 16; ++e) acc[0][e] = acc[1][e] = 0.f;
 
   // Steps 0 .. kStages-2 before the loop; step i + kStages - 1 at iteration
   // i, into the slot that step i - 1 used (free once every wave has passed
@@ -238,31 +246,34 @@ __global__ void __launch_bounds__(kNT) project_big_kernel(ProjArgs p) {
     }
     const unsigned char* st = lds + slot * kStageBytes;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ks = 2 * half + h;
-      const u16x8 a = frag_p(st + kOpBytes, wm * 32, ks);
+    for (int h = 0; h < 4; ++h) {
+      const int ks = 4 * half + h;
+      const u16x8 a = frag_p(st + kXBytes, wm * 32, ks);
       const u16x8 b = frag_x(st, wn * 32, ks);
-      acc = mfma_32x32x16(a, b, acc);
+      acc[h & 1] = mfma_32x32x16(a, b, acc[h & 1]);
     }
     slot = slot + 1 == kStages ? 0 : slot + 1;
   }
 
-  // The second group's sums to the first through LDS (every DMA has landed
-  // and every operand read has returned before the barrier), lane-major so
-  // that the stores and loads of consecutive lanes are contiguous.
+  // Each wave's two sets added, then the second group's sums to the first
+  // through LDS (every DMA has landed and every operand read has returned
+  // before the barrier), lane-major so that the stores and loads of
+  // consecutive lanes are contiguous.
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[0][e] += acc[1][e];
   __syncthreads();
   f32x4* red = (f32x4*)lds + (wave & 3) * 4 * 64 + lane;
   if (half == 1) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      red[g * 64] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      red[g * 64] = f32x4{acc[0][4 * g], acc[0][4 * g + 1], acc[0][4 * g + 2], acc[0][4 * g + 3]};
   }
   __syncthreads();
   if (half == 1) return;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const f32x4 u = red[g * 64];
-    acc[4 * g] += u.x; acc[4 * g + 1] += u.y; acc[4 * g + 2] += u.z; acc[4 * g + 3] += u.w;
+    acc[0][4 * g] += u.x; acc[0][4 * g + 1] += u.y; acc[0][4 * g + 2] += u.z; acc[0][4 * g + 3] += u.w;
   }
 
   // Y[token][j .. j+3] in bf16, 8 bytes per lane and register group.
@@ -275,10 +286,10 @@ __global__ void __launch_bounds__(kNT) project_big_kernel(ProjArgs p) {
     const int j = j0 + wm * 32 + acc_row(4 * g, lane);
     if (j >= p.r) continue;
     u16x4 w;
-    w.s0 = f32_to_bf16_rne(acc[4 * g + 0]);
-    w.s1 = f32_to_bf16_rne(acc[4 * g + 1]);
-    w.s2 = f32_to_bf16_rne(acc[4 * g + 2]);
-    w.s3 = f32_to_bf16_rne(acc[4 * g + 3]);
+    w.s0 = f32_to_bf16_rne(acc[0][4 * g + 0]);
+    w.s1 = f32_to_bf16_rne(acc[0][4 * g + 1]);
+    w.s2 = f32_to_bf16_rne(acc[0][4 * g + 2]);
+    w.s3 = f32_to_bf16_rne(acc[0][4 * g + 3]);
     *(u16x4*)(yrow + j) = w;
   }
 }
