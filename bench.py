@@ -85,6 +85,10 @@ def parse():
                          "up-projection, ragged Llama-13B layer, RoBERTa projected)")
     ap.add_argument("--no-staged", action="store_true",
                     help="skip the staged-path comparison of the headline step")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of c1,c2,c4,c5: measure only those workload "
+                         "configurations (no headline step) and print them as one JSON line; "
+                         "for profiling one configuration")
     return ap.parse_args()
 
 
@@ -194,7 +198,7 @@ def call_memory(dp):
     return lambda: int(dp.get_option("workspace_call_high"))
 
 
-def measure_configs(dp, torch, steps, warmup):
+def measure_configs(dp, torch, steps, warmup, only=None):
     """The other workloads, one fused call per linear, on the automatic path."""
     import workloads
     out = {}
@@ -241,159 +245,165 @@ def measure_configs(dp, torch, steps, warmup):
         del dev
         torch.cuda.empty_cache()
 
-    dense([lambda: workloads.config_c1(sigma=1.0).linears[0]], "c1_fp32_B4_T16_64to32",
-          "one fp32 linear, sigma 1; launch-latency bound; peak = fp32 vector 157.3 TFLOP/s",
-          peak=PEAK_FP32_TFLOPS)
-    dense([lambda: workloads.config_c1(sigma=0.0).linears[0]], "c1_fp32_B4_T16_64to32_sigma0",
-          "as above, sigma 0", peak=PEAK_FP32_TFLOPS)
-    dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
-          "bf16, sigma 0.8; inputs (126 MB) resident in the Infinity Cache across calls")
-    # the GPT-2 layer on each norm path, one after another on the same inputs:
-    # Gram, direct, the single pass (each per-sample gradient once, on chip)
-    # and the opt-in staged form
-    lin = workloads.config_c2().linears[0]
-    X, G = upload(lin.X, torch), upload(lin.G, torch)
-    o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
-    nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
-    f = 2.0 * lin.B * lin.T * lin.din * lin.dout
-    by_path = {}
-    for path, name in ((1, "gram"), (2, "direct"), (4, "one pass"), (3, "staged")):
-        dp.set_option("norm_path", path)
-        try:
-            call = lambda: dp.linear_clip_accumulate(X, G, None, C=lin.C, sigma=lin.sigma,
-                                                     grad_out=o, norms_out=nrm)
-            mem = call_memory(dp)
-            ms = time_calls(torch, call, steps, warmup)
-            taken = norm_path_of(dp, call)
-            by_path[name] = {"ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
-                             "norm_path_taken": taken, "extra_device_bytes_per_call_max": mem()}
-        finally:
-            dp.set_option("norm_path", 0)
-    out["c2_gpt2_up_by_norm_path"] = {
-        "note": "as c2, each norm path forced in turn (the automatic choice is listed above)",
-        **by_path}
-    del X, G, o, nrm
+    want = (lambda k: True) if only is None else (lambda k: k in only)
 
-    # the same layer with its bias (weight and bias clipped together)
-    lin = workloads.config_c2().linears[0]
-    X, G = upload(lin.X, torch), upload(lin.G, torch)
-
-    # c2's inputs (126 MB) fit in the 256 MB Infinity Cache: also time calls
-    # that each follow a 512 MB write, which evicts them
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=X.device)
-    o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
-    nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
-    times = []
-    for i in range(steps + warmup):
-        flush.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dp.linear_clip_accumulate(X, G, None, C=lin.C, sigma=lin.sigma, grad_out=o, norms_out=nrm)
-        e1.record()
-        torch.cuda.synchronize()
-        if i >= warmup:
-            times.append(e0.elapsed_time(e1))
-    ms = sum(times) / len(times)
-    f = 2.0 * lin.B * lin.T * lin.din * lin.dout
-    out["c2_gpt2_up_B32_T512_768to3072_flushed"] = {
-        "note": "as c2, each call after a 512 MB write that evicts the inputs from the cache",
-        "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
-        "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
-        "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
-    del flush
-    o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
-    ob = torch.empty((lin.dout,), dtype=torch.float32, device=X.device)
-    nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
-    ms = time_calls(torch, lambda: dp.linear_clip_accumulate_bias(
-        X, G, None, C=lin.C, sigma=lin.sigma, grad_out=o, bias_grad_out=ob, norms_out=nrm),
-        steps, warmup)
-    f = 2.0 * lin.B * lin.T * lin.din * lin.dout
-    out["c2_gpt2_up_with_bias"] = {
-        "note": "as c2, plus the bias gradient (column sums of G) in the clipping norm and sum",
-        "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
-        "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
-        "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
-    del X, G, o, ob, nrm
-    torch.cuda.empty_cache()
-    dense([lambda i=i: workloads.config_c4_linear(i) for i in range(len(workloads.C4_LINEARS))],
-          "c4_llama13b_ragged_B16_T2048_7_linears",
-          "bf16, prefix masks T_i ~ U[128, 2048], C 0.5, sigma 1.2; useful flops over active tokens")
-
-    # projected variant: Y = X P with P from gaussian_fill(seed 7, offset 0, 1/sqrt(r)), r = 256
-    r = 256
-    dev, Ps = [], {}
-    lins = workloads.config_c5().linears
-    for lin in lins:
-        if lin.din not in Ps:
-            Ps[lin.din] = dp.gaussian_fill(7, 0, lin.din * r, 1.0 / 16.0,
-                                           dtype=torch.bfloat16).view(lin.din, r)
+    if want("c1"):
+        dense([lambda: workloads.config_c1(sigma=1.0).linears[0]], "c1_fp32_B4_T16_64to32",
+              "one fp32 linear, sigma 1; launch-latency bound; peak = fp32 vector 157.3 TFLOP/s",
+              peak=PEAK_FP32_TFLOPS)
+        dense([lambda: workloads.config_c1(sigma=0.0).linears[0]], "c1_fp32_B4_T16_64to32_sigma0",
+              "as above, sigma 0", peak=PEAK_FP32_TFLOPS)
+    if want("c2"):
+        dense([lambda: workloads.config_c2().linears[0]], "c2_gpt2_up_B32_T512_768to3072",
+              "bf16, sigma 0.8; inputs (126 MB) resident in the Infinity Cache across calls")
+        # the GPT-2 layer on each norm path, one after another on the same inputs:
+        # Gram, direct, the single pass (each per-sample gradient once, on chip)
+        # and the opt-in staged form
+        lin = workloads.config_c2().linears[0]
         X, G = upload(lin.X, torch), upload(lin.G, torch)
-        o = torch.empty((lin.dout, r), dtype=torch.float32, device=X.device)
+        o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
         nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
-        dev.append((lin, X, G, o, nrm))
+        f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+        by_path = {}
+        for path, name in ((1, "gram"), (2, "direct"), (4, "one pass"), (3, "staged")):
+            dp.set_option("norm_path", path)
+            try:
+                call = lambda: dp.linear_clip_accumulate(X, G, None, C=lin.C, sigma=lin.sigma,
+                                                         grad_out=o, norms_out=nrm)
+                mem = call_memory(dp)
+                ms = time_calls(torch, call, steps, warmup)
+                taken = norm_path_of(dp, call)
+                by_path[name] = {"ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                                 "norm_path_taken": taken, "extra_device_bytes_per_call_max": mem()}
+            finally:
+                dp.set_option("norm_path", 0)
+        out["c2_gpt2_up_by_norm_path"] = {
+            "note": "as c2, each norm path forced in turn (the automatic choice is listed above)",
+            **by_path}
+        del X, G, o, nrm
 
-    def proj_layer():
-        for lin, X, G, o, nrm in dev:
-            dp.linear_clip_accumulate_projected(X, G, Ps[lin.din], C=lin.C, sigma=lin.sigma,
-                                                grad_out=o, norms_out=nrm)
-    ms = time_calls(torch, proj_layer, steps, warmup)
-    paths = sorted({norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate_projected(
-        d[1], d[2], Ps[d[0].din], C=d[0].C, sigma=d[0].sigma, grad_out=d[3], norms_out=d[4]))
-        for d in dev})
-    useful = sum(2.0 * l.B * l.T * (l.din + l.dout) * r for l in lins)
-    out["c5_roberta_large_projected_r256_6_linears"] = {
-        "note": "bf16, projection then clip in r space; useful flops 2*B*T*(din+dout)*r",
-        "norm_path": ",".join(paths),
-        "linears": len(lins), "ms": round(ms, 4),
-        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "frac_of_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
-        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
+        # the same layer with its bias (weight and bias clipped together)
+        lin = workloads.config_c2().linears[0]
+        X, G = upload(lin.X, torch), upload(lin.G, torch)
 
-    # the same, with P drawn from its seed inside the projection (never stored)
-    def seeded_layer():
-        for lin, X, G, o, nrm in dev:
-            dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7, p_offset=0,
-                                                       C=lin.C, sigma=lin.sigma, grad_out=o,
-                                                       norms_out=nrm)
-    ms = time_calls(torch, seeded_layer, steps, warmup)
-    out["c5_roberta_large_projected_seeded_r256_6_linears"] = {
-        "note": "as above, P drawn from Philox seed 7 in each call (once into workspace), never kept",
-        "linears": len(lins), "ms": round(ms, 4),
-        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
-    dp.set_option("p_in_kernels", 1)
-    try:
+        # c2's inputs (126 MB) fit in the 256 MB Infinity Cache: also time calls
+        # that each follow a 512 MB write, which evicts them
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=X.device)
+        o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
+        nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+        times = []
+        for i in range(steps + warmup):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dp.linear_clip_accumulate(X, G, None, C=lin.C, sigma=lin.sigma, grad_out=o, norms_out=nrm)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+        ms = sum(times) / len(times)
+        f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+        out["c2_gpt2_up_B32_T512_768to3072_flushed"] = {
+            "note": "as c2, each call after a 512 MB write that evicts the inputs from the cache",
+            "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
+        del flush
+        o = torch.empty((lin.dout, lin.din), dtype=torch.float32, device=X.device)
+        ob = torch.empty((lin.dout,), dtype=torch.float32, device=X.device)
+        nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+        ms = time_calls(torch, lambda: dp.linear_clip_accumulate_bias(
+            X, G, None, C=lin.C, sigma=lin.sigma, grad_out=o, bias_grad_out=ob, norms_out=nrm),
+            steps, warmup)
+        f = 2.0 * lin.B * lin.T * lin.din * lin.dout
+        out["c2_gpt2_up_with_bias"] = {
+            "note": "as c2, plus the bias gradient (column sums of G) in the clipping norm and sum",
+            "linears": 1, "ms": round(ms, 4), "useful_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "samples_per_s": round(lin.B / (ms * 1e-3), 1)}
+        del X, G, o, ob, nrm
+        torch.cuda.empty_cache()
+    if want("c4"):
+        dense([lambda i=i: workloads.config_c4_linear(i) for i in range(len(workloads.C4_LINEARS))],
+              "c4_llama13b_ragged_B16_T2048_7_linears",
+              "bf16, prefix masks T_i ~ U[128, 2048], C 0.5, sigma 1.2; useful flops over active tokens")
+
+    if want("c5"):
+        # projected variant: Y = X P with P from gaussian_fill(seed 7, offset 0, 1/sqrt(r)), r = 256
+        r = 256
+        dev, Ps = [], {}
+        lins = workloads.config_c5().linears
+        for lin in lins:
+            if lin.din not in Ps:
+                Ps[lin.din] = dp.gaussian_fill(7, 0, lin.din * r, 1.0 / 16.0,
+                                               dtype=torch.bfloat16).view(lin.din, r)
+            X, G = upload(lin.X, torch), upload(lin.G, torch)
+            o = torch.empty((lin.dout, r), dtype=torch.float32, device=X.device)
+            nrm = torch.empty((lin.B,), dtype=torch.float32, device=X.device)
+            dev.append((lin, X, G, o, nrm))
+
+        def proj_layer():
+            for lin, X, G, o, nrm in dev:
+                dp.linear_clip_accumulate_projected(X, G, Ps[lin.din], C=lin.C, sigma=lin.sigma,
+                                                    grad_out=o, norms_out=nrm)
+        ms = time_calls(torch, proj_layer, steps, warmup)
+        paths = sorted({norm_path_of(dp, lambda d=d: dp.linear_clip_accumulate_projected(
+            d[1], d[2], Ps[d[0].din], C=d[0].C, sigma=d[0].sigma, grad_out=d[3], norms_out=d[4]))
+            for d in dev})
+        useful = sum(2.0 * l.B * l.T * (l.din + l.dout) * r for l in lins)
+        out["c5_roberta_large_projected_r256_6_linears"] = {
+            "note": "bf16, projection then clip in r space; useful flops 2*B*T*(din+dout)*r",
+            "norm_path": ",".join(paths),
+            "linears": len(lins), "ms": round(ms, 4),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
+
+        # the same, with P drawn from its seed inside the projection (never stored)
+        def seeded_layer():
+            for lin, X, G, o, nrm in dev:
+                dp.linear_clip_accumulate_projected_seeded(X, G, r, None, p_seed=7, p_offset=0,
+                                                           C=lin.C, sigma=lin.sigma, grad_out=o,
+                                                           norms_out=nrm)
         ms = time_calls(torch, seeded_layer, steps, warmup)
-    finally:
-        dp.set_option("p_in_kernels", 0)
-    out["c5_roberta_large_projected_seeded_in_kernel_r256_6_linears"] = {
-        "note": "as above, P drawn inside the projection kernel in every token tile; no P tensor",
-        "linears": len(lins), "ms": round(ms, 4),
-        "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
+        out["c5_roberta_large_projected_seeded_r256_6_linears"] = {
+            "note": "as above, P drawn from Philox seed 7 in each call (once into workspace), never kept",
+            "linears": len(lins), "ms": round(ms, 4),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
+        dp.set_option("p_in_kernels", 1)
+        try:
+            ms = time_calls(torch, seeded_layer, steps, warmup)
+        finally:
+            dp.set_option("p_in_kernels", 0)
+        out["c5_roberta_large_projected_seeded_in_kernel_r256_6_linears"] = {
+            "note": "as above, P drawn inside the projection kernel in every token tile; no P tensor",
+            "linears": len(lins), "ms": round(ms, 4),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
 
-    # projected Adam step on the privatised projected gradients (moments in
-    # r-space, weight update W -= lr U P^T with P drawn from its seed)
-    states = []
-    for lin, X, G, o, nrm in dev:
-        states.append((o, torch.zeros_like(o), torch.zeros_like(o),
-                       torch.zeros((lin.dout, lin.din), dtype=torch.float32, device=o.device)))
-    seeded_layer()
-    step_no = [0]
+        # projected Adam step on the privatised projected gradients (moments in
+        # r-space, weight update W -= lr U P^T with P drawn from its seed)
+        states = []
+        for lin, X, G, o, nrm in dev:
+            states.append((o, torch.zeros_like(o), torch.zeros_like(o),
+                           torch.zeros((lin.dout, lin.din), dtype=torch.float32, device=o.device)))
+        seeded_layer()
+        step_no = [0]
 
-    def adam_layer():
-        step_no[0] += 1
-        for h, m, v, W in states:
-            dp.projected_adam_step(h, m, v, W, step_no[0], 1e-4, P=None, p_seed=7, p_offset=0)
-    ms = time_calls(torch, adam_layer, steps, warmup)
-    flops = sum(2.0 * l.dout * l.din * r for l in lins)
-    bytes_ = sum(4.0 * (6 * l.dout * r + 2 * l.dout * l.din) for l in lins)
-    out["c5_roberta_large_projected_adam_step_6_linears"] = {
-        "note": "moments + U P^T update (fp32 MFMA), P drawn from its seed; flops 2*dout*din*r, "
-                "bytes: h, m, v, U in r-space and W read+written",
-        "linears": len(lins), "ms": round(ms, 4),
-        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-        "gb_per_s": round(bytes_ / (ms * 1e-3) / 1e9, 1)}
+        def adam_layer():
+            step_no[0] += 1
+            for h, m, v, W in states:
+                dp.projected_adam_step(h, m, v, W, step_no[0], 1e-4, P=None, p_seed=7, p_offset=0)
+        ms = time_calls(torch, adam_layer, steps, warmup)
+        flops = sum(2.0 * l.dout * l.din * r for l in lins)
+        bytes_ = sum(4.0 * (6 * l.dout * r + 2 * l.dout * l.din) for l in lins)
+        out["c5_roberta_large_projected_adam_step_6_linears"] = {
+            "note": "moments + U P^T update (fp32 MFMA), P drawn from its seed; flops 2*dout*din*r, "
+                    "bytes: h, m, v, U in r-space and W read+written",
+            "linears": len(lins), "ms": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "gb_per_s": round(bytes_ / (ms * 1e-3) / 1e9, 1)}
     return out
 
 
@@ -506,6 +516,17 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.only:
+        only = {c.strip() for c in args.only.split(",") if c.strip()}
+        bad = only - {"c1", "c2", "c4", "c5"}
+        if bad:
+            print(json.dumps({"error": f"unknown configuration(s) {sorted(bad)}"}))
+            sys.exit(2)
+        import torch
+        import sample_gradient_clipping_amd as dp
+        dp.load()
+        print(json.dumps({"configs": measure_configs(dp, torch, args.steps, args.warmup, only)}))
         return
     import torch
     import sample_gradient_clipping_amd as dp
