@@ -108,6 +108,13 @@ int main(void) {
                                                          1.f, 0, 0, out, NULL, NULL),
          DPF_ERR_INVALID_ARGUMENT);
 
+  /* the projection step alone */
+  EXPECT(dpfused_project(&X, NULL, NULL, 8, out, NULL), DPF_ERR_INVALID_ARGUMENT);
+  EXPECT(dpfused_project(&X, NULL, FAKE, 8, NULL, NULL), DPF_ERR_INVALID_ARGUMENT);
+  EXPECT(dpfused_project(&X, NULL, FAKE, 0, out, NULL), DPF_ERR_INVALID_ARGUMENT);
+  EXPECT(dpfused_project(&X, NULL, (const char*)FAKE + 8, 8, out, NULL), DPF_ERR_UNSUPPORTED);
+  EXPECT(dpfused_project(NULL, NULL, FAKE, 8, out, NULL), DPF_ERR_INVALID_ARGUMENT);
+
   /* building blocks */
   EXPECT(dpfused_per_sample_sqnorms(&X, &G, NULL, NULL, 0, NULL), DPF_ERR_INVALID_ARGUMENT);
   EXPECT(dpfused_clip_factors((const double*)FAKE, 0, 1.f, out, NULL, NULL),
