@@ -361,44 +361,15 @@ __device__ __forceinline__ float product_sum(const float* xg, const Acc& gg) {
   return sum;
 }
 
-// Work plan: G persistent workgroups; work index d*G + L (d < D) to
-// workgroup L in D full rounds; each of the R remaining work indices D*G + r
-// split into P chunks of its feature steps (X steps first, then G steps;
-// P == 1: not split), piece pi = c*R + r going to workgroup pi mod G.  A
-// piece stores the partial Gram of each side it touches; the fixup kernel
-// finishes split items.  Work index i is item i, except with xcd set (below).
-//
-// xcd: every block of 256 token rows is read by the 8 items that pair it
-// with another block, and those items share its rows in L2 only on one XCD.
-// With xcd set, XCD x (logical workgroups [x G/8, (x+1) G/8)) works only on
-// samples b = x mod 8: its full rounds take those samples' items in order,
-// and the pieces of its remainder items stay on it -- workgroup l of XCD x
-// takes local pieces lp = l, l + G/8, ... (lp < R/8 * P) as chunk lp / (R/8)
-// of remainder item x R/8 + lp % (R/8), stored at the same pi = c*R + r as
-// without xcd.  Set for unmasked calls with B and G multiples of 8 whose
-// last round is split or empty; each XCD then holds exactly an eighth of the
-// work.
+// Work plan: G persistent workgroups; the first D*G items in D full rounds
+// (item d*G + L to workgroup L); each of the R remaining items split into P
+// chunks of its feature steps (X steps first, then G steps; P == 1: not
+// split), piece pi = c*R + r going to workgroup pi mod G.  A piece stores
+// the partial Gram of each side it touches; the fixup kernel finishes split
+// items.
 struct GramPlan {
   int G, D, R, P;
-  int xcd;
 };
-
-// The item of work index i (layout above).
-__host__ __device__ inline int item_of(const GramPlan& gp, int i, int per_sample) {
-  if (!gp.xcd) return i;
-  const int Gx = gp.G / 8, Rx = gp.R / 8;
-  int x, li;
-  if (i < gp.D * gp.G) {
-    const int u = i / gp.G, L = i % gp.G;
-    x = L / Gx;
-    li = u * Gx + L % Gx;
-  } else {
-    const int r = i - gp.D * gp.G;
-    x = r / Rx;
-    li = gp.D * Gx + r % Rx;
-  }
-  return (x + 8 * (li / per_sample)) * per_sample + li % per_sample;
-}
 
 // D, R and P for `items` items of n feature steps on G workgroups, with at
 // most `cap` pieces.  Cost model in microseconds from measurements on MI355X:
@@ -407,7 +378,7 @@ __host__ __device__ inline int item_of(const GramPlan& gp, int i, int per_sample
 // host, and on the device for masked calls, where only the device knows how
 // many items hold an active token.
 __host__ __device__ inline GramPlan split_items(int items, int G, int n, int cap) {
-  GramPlan gp{G, items / G, items % G, 1, 0};
+  GramPlan gp{G, items / G, items % G, 1};
   if (gp.R == 0) return gp;
   const double step_us = 0.8, piece_us = 8.0;
   double best = n * step_us + piece_us;
@@ -457,17 +428,10 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, Gram
   const int n = nkx + nkg;
   const int L = logical_wg(blockIdx.x, gp.G);
   if (live != nullptr) gp = split_items((int)((c_u32*)live)[0], gp.G, n, cap);
-  auto item_at = [&](int i) {
-    return live != nullptr ? (int)((c_u32*)live)[1 + i] : item_of(gp, i, per_sample);
-  };
+  auto item_at = [&](int i) { return live != nullptr ? (int)((c_u32*)live)[1 + i] : i; };
   // This workgroup's units: whole items d*G + L, then pieces L, L+G, ...
   const int nfull = gp.D + ((gp.P == 1 && L < gp.R) ? 1 : 0);
-  // Pieces: u-th piece of this workgroup is pi = L + u G, or with xcd the
-  // local piece lp = l + u G/8 of XCD x = L / (G/8) (l = L % (G/8)).
-  const int Gx = gp.G / 8, Rx = gp.R / 8;
-  const int npiece = gp.P == 1 ? 0
-                     : gp.xcd ? (Rx * gp.P - L % Gx + Gx - 1) / Gx
-                              : (gp.R * gp.P - L + gp.G - 1) / gp.G;
+  const int npiece = gp.P == 1 ? 0 : (gp.R * gp.P - L + gp.G - 1) / gp.G;
   float* mine = xs + (int64_t)L * kGramFloats;   // this workgroup's X Gram
   Acc acc;
   // Whole items: the X Gram to scratch, then the G Gram, multiplied with the
@@ -488,17 +452,9 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, Gram
   // Pieces: the partial Gram of each side the piece touches.
 #pragma unroll 1
   for (int u = 0; u < npiece; ++u) {
-    int c, r;
-    if (gp.xcd) {
-      const int lp = L % Gx + u * Gx;
-      c = lp / Rx;
-      r = (L / Gx) * Rx + lp % Rx;
-    } else {
-      c = (L + u * gp.G) / gp.R;
-      r = (L + u * gp.G) % gp.R;
-    }
-    const int pi = c * gp.R + r;
-    const int item = item_at(gp.D * gp.G + r);
+    const int pi = L + u * gp.G;
+    const int c = pi / gp.R;
+    const int item = item_at(gp.D * gp.G + pi % gp.R);
     int b, S, Tb;
     item_coords(item, per_sample, p.T, &b, &S, &Tb);
     const Parts pt((int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), nkx);
@@ -532,8 +488,7 @@ __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPla
   const int r = blockIdx.x / kFixParts, h = blockIdx.x % kFixParts;
   if (gp.P == 1 || r >= gp.R) return;
   const int i = gp.D * gp.G + r;
-  const int item =
-      live != nullptr ? (int)((c_u32*)live)[1 + i] : item_of(gp, i, items_per_sample(p.T));
+  const int item = live != nullptr ? (int)((c_u32*)live)[1 + i] : i;
   int b, S, Tb;
   item_coords(item, items_per_sample(p.T), p.T, &b, &S, &Tb);
   f32x4 sx[kFixQuads], sg[kFixQuads];
@@ -569,8 +524,7 @@ __global__ void gram_fixup_sum_kernel(LayerArgs p, GramPlan gp, const uint32_t* 
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (gp.P == 1 || r >= gp.R) return;
   const int i = gp.D * gp.G + r;
-  const int item =
-      live != nullptr ? (int)((c_u32*)live)[1 + i] : item_of(gp, i, items_per_sample(p.T));
+  const int item = live != nullptr ? (int)((c_u32*)live)[1 + i] : i;
   double s = 0.0;
   for (int h = 0; h < kFixParts; ++h) s += part[r * kFixParts + h];
   p.partials[item] = s;
@@ -630,7 +584,6 @@ gram::GramPlan plan_gram(const LayerArgs& p) {
   const int n = (p.din + gram::kKF - 1) / gram::kKF + (p.dout + gram::kKF - 1) / gram::kKF;
   gram::GramPlan gp = gram::split_items(items, G, n, p.max_split == 1 ? 0 : 1 << 30);
   if (gp.P == 1 && gp.D == 0) gp.G = gp.R;
-  gp.xcd = p.mask == nullptr && gp.G % 8 == 0 && p.B % 8 == 0 && (gp.P > 1 || gp.R == 0);
   return gp;
 }
 

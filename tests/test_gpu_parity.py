@@ -284,22 +284,6 @@ def test_masked_gram_dead_row_blocks(path):
     _check(lin, path, sigma=0.7, C=C)
 
 
-@pytest.mark.parametrize("B", [8, 16])
-def test_gram_items_grouped_by_xcd(B):
-    """Unmasked Gram calls with B a multiple of 8 and a split last round take
-    the XCD-grouped work order (each XCD works on samples b = x mod 8, the
-    pieces of its remainder items included).  T = 300 gives 3 items per
-    sample, 1024 + 1024 features a 64-step item, so 24 (48) items split into
-    pieces over all 256 workgroups.  The norms, the clipped sum and the
-    noise against the oracle, with mixed clipping (C at the median norm)."""
-    rng = np.random.default_rng(40 + B)
-    lin = random_linear(rng, B, 300, 1024, 1024)
-    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
-    C = float(np.median(rn))
-    _check(lin, 1, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
-    _check(lin, 1, sigma=0.6, C=C)
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 100, 1000, 72), (3, 33, 1000, 70)])
 def test_projected_split_along_din(dtype, shape):
