@@ -284,6 +284,22 @@ def test_masked_gram_dead_row_blocks(path):
     _check(lin, path, sigma=0.7, C=C)
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_gram_items_split_over_all_workgroups(B):
+    """Unmasked Gram calls whose items all fall in a split last round: T = 300
+    gives 3 items per sample (2 of them diagonal), 1024 + 1024 features a
+    64-step item, so 24 (48) items split into 5 pieces each over the
+    workgroups, with the fixup summing them.  The norms, the clipped sum and
+    the noise against the oracle, with mixed clipping (C at the median
+    norm)."""
+    rng = np.random.default_rng(40 + B)
+    lin = random_linear(rng, B, 300, 1024, 1024)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn))
+    _check(lin, 1, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+    _check(lin, 1, sigma=0.6, C=C)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 100, 1000, 72), (3, 33, 1000, 70)])
 def test_projected_split_along_din(dtype, shape):
