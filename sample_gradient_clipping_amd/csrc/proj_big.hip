@@ -40,7 +40,6 @@ namespace dpf {
 namespace proj {
 
 constexpr int kNT = 512;
-constexpr int kWaves = kNT / 64;
 constexpr int kTile = 64;                      // r columns and tokens per tile
 constexpr int kKF = 128;                       // features per step
 constexpr int kXRowBytes = kKF * 2;            // an X row of one step: 256 B
