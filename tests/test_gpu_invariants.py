@@ -126,6 +126,41 @@ def test_unclipped_noiseless_is_plain_gemm():
     assert rel_fro(out.cpu().numpy(), ref.cpu().numpy()) <= 1e-5
 
 
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
+def test_single_token_norm_is_product_of_row_norms(path):
+    """T = 1: g_i = G_i^T X_i is an outer product, so ||g_i|| = ||G_i|| ||X_i||
+    exactly, and with C huge and sigma = 0 the output is sum_i G_i^T X_i / B.
+    Checked against that closed form (fp64 from the bf16 inputs, no oracle)
+    on the large-tile layout, on every norm path: automatic, Gram (one
+    diagonal item per sample, 255 of its 256 rows past T), direct, staged
+    and the single pass.  bf16 inputs are exact; only fp32 summation and the
+    final fp32 rounding differ: the Gram path sums 768 and 1024 squares in
+    fp32 (at most ~5e-5 relative), hence 1e-4 relative for the norms, and
+    each output entry is a sum of 8 exact products, hence 1e-5 of the
+    largest entry."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    import workloads
+    rng = np.random.default_rng(60 + path)
+    B, din, dout = 8, 768, 1024
+    X = workloads.f32_to_bf16_bits(rng.standard_normal((B, 1, din), dtype=np.float32))
+    G = workloads.f32_to_bf16_bits(rng.standard_normal((B, 1, dout), dtype=np.float32))
+    Xw = workloads.bf16_bits_to_f32(X).astype(np.float64)[:, 0]
+    Gw = workloads.bf16_bits_to_f32(G).astype(np.float64)[:, 0]
+    want_n = np.linalg.norm(Gw, axis=1) * np.linalg.norm(Xw, axis=1)
+    want_out = Gw.T @ Xw / B
+    dp.set_option("norm_path", path)
+    try:
+        out, n = dp.linear_clip_accumulate(to_dev(X, "bf16", torch), to_dev(G, "bf16", torch), None,
+                                           C=1e30, sigma=0.0)
+        torch.cuda.synchronize()
+    finally:
+        dp.set_option("norm_path", 0)
+    assert max_rel(n.cpu().numpy(), want_n) <= 1e-4
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - want_out)) <= 1e-5 * np.max(np.abs(want_out))
+
+
 def test_scale_invariance_of_clipped_sample():
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
