@@ -758,9 +758,12 @@ constexpr int64_t kImgStride = kTileElems;   // floats from one unit's image to 
 // the next unit's first steps are queued before this unit's tile is stored,
 // so the stores overlap the next unit's pipeline fill.  Each wave writes its
 // own fp64 partial (np = 8 per tile), so no LDS is needed between units.
+// Without STORE the same loop is the persistent form of the direct norm:
+// each tile is squared, summed and dropped, and the next unit's pipeline
+// fill overlaps this unit's reduction instead of a new workgroup's start.
 constexpr int kStagedParts = kWaves;
 
-template <bool MASK, bool NT>
+template <bool MASK, bool NT, bool STORE>
 __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned char* smem) {
   const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
   const int ntiles = ntm * ntn;
@@ -798,9 +801,10 @@ __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned
     after_stores = false;
     if (u + G < N) {
       queue(u + G, ps);
-      after_stores = ps.n > 0;
+      after_stores = STORE && ps.n > 0;
     }
-    float* img = p.skws + (int64_t)u * kImgStride + ((int64_t)wave * kImgChunks * 64 + lane) * 4;
+    float* img = STORE ? p.skws + (int64_t)u * kImgStride + ((int64_t)wave * kImgChunks * 64 + lane) * 4
+                       : nullptr;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < kBA; ++i)
@@ -812,6 +816,7 @@ __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned
           v.x = acc.v[i][j][4 * g + 0]; v.y = acc.v[i][j][4 * g + 1];
           v.z = acc.v[i][j][4 * g + 2]; v.w = acc.v[i][j][4 * g + 3];
           s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          if constexpr (!STORE) continue;
           // Plain (cached) stores leave the most recently written tiles in
           // the 256 MB MALL for the combine kernel: 13% faster combines at
           // 5120 x 5120.  Non-temporal stores (NT) suit the calls whose tiles
@@ -829,8 +834,14 @@ __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned
 template <bool NT>
 __global__ void __launch_bounds__(kNT, 1) staged_norm_big_kernel(LayerArgs p, int G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  if (p.steps != nullptr) staged_units<true, NT>(p, G, smem);
-  else staged_units<false, NT>(p, G, smem);
+  if (p.steps != nullptr) staged_units<true, NT, true>(p, G, smem);
+  else staged_units<false, NT, true>(p, G, smem);
+}
+
+__global__ void __launch_bounds__(kNT, 1) direct_norm_units_kernel(LayerArgs p, int G) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if (p.steps != nullptr) staged_units<true, false, false>(p, G, smem);
+  else staged_units<false, false, false>(p, G, smem);
 }
 
 // out = (sum_b c_b g_b + noise_std xi) / B from the staged tiles: one thread
@@ -995,7 +1006,32 @@ hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s) {
   return e;
 }
 
+// The direct norm runs persistent (one workgroup per compute unit walking
+// the (sample, tile) units, eight partials per tile) when the units fill
+// more than one round of the chip; one workgroup per unit otherwise.
+static int direct_units_grid(const LayerArgs& p) {
+  const int64_t units = (int64_t)big_tiles(p.din, p.dout) * p.B;
+  const int cus = device_cus();
+  if (units <= cus || units > 0x7fffffff) return 0;
+  return cus >= 8 ? cus - cus % 8 : cus;
+}
+
+int direct_big_partials_per_sample(const LayerArgs& p) {
+  return big_tiles(p.din, p.dout) * (direct_units_grid(p) > 0 ? big::kStagedParts : 1);
+}
+
 hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s) {
+  const int G = direct_units_grid(p);
+  if (G > 0) {
+    hipError_t e = allow_lds_big<big::direct_norm_units_kernel>(big::kLdsBytes);
+    if (e != hipSuccess) return e;
+    timing_begin("direct_norm", s);
+    hipLaunchKernelGGL(big::direct_norm_units_kernel, dim3((unsigned)G), dim3(big::kNT),
+                       big::kLdsBytes, s, p, G);
+    e = hipGetLastError();
+    timing_end("direct_norm", s);
+    return e;
+  }
   hipError_t e = allow_lds_big<big::direct_norm_big_kernel>(big::kLdsBytes);
   if (e != hipSuccess) return e;
   const int nt = big_tiles(p.din, p.dout);

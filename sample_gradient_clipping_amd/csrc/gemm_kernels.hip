@@ -649,7 +649,7 @@ int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
     return nt * (nt + 1) / 2;
   }
   if (path == NormPath::kStaged && use_big(p, vec)) return staged_big_partials_per_sample(p);
-  if (use_big(p, vec)) return big_tiles(p.din, p.dout);
+  if (use_big(p, vec)) return direct_big_partials_per_sample(p);
   return ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
 }
 

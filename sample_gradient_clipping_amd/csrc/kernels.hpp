@@ -143,6 +143,7 @@ hipError_t launch_accumulate_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_direct_norm_big(const LayerArgs& p, hipStream_t s);
 size_t staged_big_workspace_bytes(const LayerArgs& p);
 int staged_big_partials_per_sample(const LayerArgs& p);
+int direct_big_partials_per_sample(const LayerArgs& p);
 hipError_t launch_staged_norm_big(const LayerArgs& p, hipStream_t s);
 hipError_t launch_staged_combine_big(const LayerArgs& p, hipStream_t s);
 
