@@ -19,16 +19,24 @@
 // item, summed in a fixed order later (finalize_kernel).
 //
 // Operands are feature-contiguous ("K-inner"): each lane's MFMA fragment is
-// one 16-byte LDS read.  A phase streams 32-feature steps of the item's 256 s
-// rows and 256 t rows (32 KiB) from global memory into a ring of five LDS
-// slots with 16-byte-per-lane buffer loads that write LDS directly; rows are
-// 64 bytes with the 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3),
-// which keeps the fragment reads free of bank conflicts.  The main loop has
-// the accumulate kernel's structure: two 16-feature substeps of eight MFMAs
-// per step, fragments double-buffered and read between MFMAs, one barrier
-// per step, each step's DMAs issued four steps ahead.  Masked tokens and rows
-// past T read through out-of-range buffer offsets (zeros).
+// one 16-byte LDS read.  A phase computes 32-feature steps (two 16-feature
+// substeps of eight MFMAs), but loads 64-feature chunks: one side's 256 rows
+// of a chunk (a "half", 32 KiB) is one whole 128-byte line per row, so every
+// 16-byte-per-lane buffer load that writes LDS directly covers 8 full lines
+// (32-feature loads covered 16 half lines per instruction and kept the
+// address unit busy for twice as long per byte).  Five 32 KiB LDS slots
+// hold halves: s halves of chunk c in slot 2 (c mod 3), t halves in slot
+// 1 + 2 (c mod 2).  Rows are 128 bytes with the 16-byte chunk c of row r
+// stored at c ^ ((r >> 1) & 7), which keeps the fragment reads free of bank
+// conflicts.  Each wave reads all of a chunk's t fragments (its 64 t rows,
+// 64 features: 32 registers) as the chunk starts, so the t slot is free one
+// substep into the chunk; the s fragments are read one substep ahead of
+// their MFMAs.  That lets the t half of chunk c + 2 be queued a quarter of
+// the way into chunk c and the s half of chunk c + 3 three quarters of the
+// way (three and four steps ahead of their first use).  Masked tokens and
+// rows past T read through out-of-range buffer offsets (zeros).
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "tiles.hpp"
@@ -41,13 +49,13 @@ constexpr int kWaveRows = 2, kWaveCols = 4;    // wave grid: 2 along s, 4 along 
 constexpr int kBA = 4, kBO = 2;                // 32x32 blocks per wave: 128 (s) x 64 (t)
 constexpr int kRows = 256;                     // token rows on each side of an item
 constexpr int kKF = 32;                        // features per step
-constexpr int kRowBytes = kKF * 2;             // 64
-constexpr int kSideBytes = kRows * kRowBytes;  // 16 KiB
-constexpr int kStageBytes = 2 * kSideBytes;    // 32 KiB: the s rows, then the t rows
-constexpr int kStages = 5;
-constexpr int kLdsBytes = kStages * kStageBytes;   // 160 KiB: all of gfx950's LDS
+constexpr int kChunkF = 2 * kKF;               // features per load chunk: two steps
+constexpr int kRowBytes = kChunkF * 2;         // 128: one cache line
+constexpr int kHalfBytes = kRows * kRowBytes;  // 32 KiB: one side's rows of one chunk
+constexpr int kSlots = 5;
+constexpr int kLdsBytes = kSlots * kHalfBytes; // 160 KiB: all of gfx950's LDS
 constexpr int kWaves = kNT / 64;
-constexpr int kDmaPerStep = kStageBytes / 1024 / kWaves;   // 4 per wave, 16 rows each
+constexpr int kDmaPerHalf = kHalfBytes / 1024 / kWaves;   // 4 per wave, 8 rows each
 constexpr int kOOB = 0x7ffffff0;
 constexpr int kAccFloats = kBA * kBO * 16;            // 128 per lane
 constexpr int kGramFloats = kAccFloats * kNT;         // one Gram tile, thread-major
@@ -55,7 +63,7 @@ constexpr int kMaxSplit = 16;
 
 typedef __attribute__((address_space(4))) const uint32_t c_u32;
 
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 // The thread index, hidden from the optimiser: addressing derived from it
 // is then computed where it is used, once per item, instead of being hoisted
@@ -77,14 +85,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, 
                : "memory");
 }
 
-// Wait until at most `steps` of this wave's most recent DMA steps are in flight.
-__device__ __forceinline__ void wait_dma(int steps) {
-  static_assert(kDmaPerStep == 4, "wait_dma encodes 4 DMAs per step");
-  if (steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (steps == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if (steps == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (steps == 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+// Wait until at most `halves` of this wave's most recently queued halves
+// are in flight (0 to kSlots - 2 of them).
+__device__ __forceinline__ void wait_halves(int halves) {
+  static_assert(kDmaPerHalf == 4, "wait_halves encodes 4 DMAs per half");
+  if (halves <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (halves == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (halves == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -118,49 +126,59 @@ __device__ __forceinline__ void item_coords(int L, int per_sample, int T, int* b
   *Tb = s + r;
 }
 
-// Per-lane DMA addressing of one side (X or G) of an item.  DMA j of wave w
-// fills stage rows 16 (4 w + j) .. +15 (rows < 256: the s rows, the rest the
-// t rows); lane l fills physical chunk l % 4 of row l / 4 of that group, i.e.
-// logical feature chunk swz(row, l % 4).
+// Lane l of DMA j of wave w fills physical chunk l % 8 of row
+// 8 (4 w + j) + l / 8 of a half, i.e. logical 16-byte chunk
+// swz(row, l % 8) of that row's 128 bytes.
+__device__ __forceinline__ int dma_row(int wave, int lane, int j) {
+  return 8 * (kDmaPerHalf * wave + j) + (lane >> 3);
+}
+__device__ __forceinline__ int dma_chunk(int lane, int j) {
+  // (row >> 1) & 7 of dma_row does not depend on the wave
+  return (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
+}
+
+// Per-lane DMA addressing of an item's two row blocks (one side, X or G):
+// byte offset of the lane's token row and 16-byte chunk, or kOOB for masked
+// tokens and rows past T.
 struct DmaLane {
-  uint32_t off[kDmaPerStep];   // token row offset + chunk offset (bytes), or kOOB
-  int cfeat[kDmaPerStep];      // first feature of the lane's chunk within a step
+  uint32_t s[kDmaPerHalf], t[kDmaPerHalf];
   __device__ __forceinline__ void init(const LayerArgs& p, const Act& a, int b, int S, int Tb,
                                        int tid) {
     const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int j = 0; j < kDmaPerStep; ++j) {
-      const int row = 16 * (kDmaPerStep * wave + j) + (lane >> 2);
-      const int c = swz(row, lane & 3);
-      const int tok = row < kRows ? kRows * S + row : kRows * Tb + (row - kRows);
+    auto offset = [&](int tok, int c) {
       bool active = tok < p.T;
       if (active && p.rowbits != nullptr)
         active = (p.rowbits[(int64_t)b * p.nwords + (tok >> 5)] >> (tok & 31)) & 1u;
-      cfeat[j] = 8 * c;
-      off[j] = active ? (uint32_t)(((int64_t)tok * a.stride_t + 8 * c) * 2) : (uint32_t)kOOB;
+      return active ? (uint32_t)(((int64_t)tok * a.stride_t + 8 * c) * 2) : (uint32_t)kOOB;
+    };
+#pragma unroll
+    for (int j = 0; j < kDmaPerHalf; ++j) {
+      const int row = dma_row(wave, lane, j), c = dma_chunk(lane, j);
+      s[j] = offset(kRows * S + row, c);
+      t[j] = offset(kRows * Tb + row, c);
     }
   }
 };
 
-// The DMAs of one 32-feature step k of a side with D features: the
-// feature offset rides in the instruction's scalar offset; only a step that
-// runs past D tests each lane's chunk (D is a multiple of 8 on this path, so
-// a chunk is wholly inside or wholly past the end).
-struct StepDma {
+// The DMAs of one half: chunk m of a side with D features.  The chunk's
+// byte offset rides in the instruction's scalar offset; only a chunk that
+// runs past D tests each lane's 8 features (D is a multiple of 8 on this
+// path, so they are wholly inside or wholly past the end).
+struct HalfDma {
   uint32_t soff;
-  int k0, D;
+  int f0, D;
   bool tail;
-  __device__ __forceinline__ void at(int k, int Dd) {
-    k0 = k * kKF;
+  __device__ __forceinline__ void at(int m, int Dd) {
+    f0 = m * kChunkF;
     D = Dd;
-    soff = (uint32_t)k0 * 2u;
-    tail = k0 + kKF > D;
+    soff = (uint32_t)f0 * 2u;
+    tail = f0 + kChunkF > D;
   }
-  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, const DmaLane& dl, uint32_t dst,
+  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t dst,
                                       int j) const {
-    int off = (int)dl.off[j];
-    if (__builtin_expect(tail, 0) && k0 + dl.cfeat[j] >= D) off = kOOB;
-    dma16(r, off, dst + (uint32_t)j * 1024u, soff);
+    if (__builtin_expect(tail, 0) && f0 + 8 * dma_chunk(opaque_tid() & 63, j) >= D) off = kOOB;
+    dma16(r, (int)off, __builtin_amdgcn_readfirstlane(dst + (uint32_t)j * 1024u),
+          __builtin_amdgcn_readfirstlane(soff));
   }
 };
 
@@ -172,7 +190,7 @@ __device__ __forceinline__ void lds_reads_done() {
 }
 
 // Workgroup barrier without a memory fence: each wave has seen its LDS reads
-// return (lds_reads_done) and its DMA writes land (wait_dma) before it.
+// return (lds_reads_done) and its DMA writes land (wait_halves) before it.
 __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -183,27 +201,39 @@ __device__ __forceinline__ void step_barrier() {
 // MFMAs with LDS reads and DMA issue that the main loop spells out.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// MFMA operand for rows m0..m0+31 of a side, 16-feature substep ks.
-__device__ __forceinline__ u16x8 frag(const unsigned char* side, int m0, int ks) {
-  const int lane = threadIdx.x & 63;
-  const int row = m0 + (lane & 31);
-  const int c = 2 * ks + (lane >> 5);
-  return *(const u16x8*)(side + row * kRowBytes + swz(row, c) * 16);
+// MFMA operands: lane l reads row l % 32 of a 32-row block, 16-byte chunk
+// 2 q + l / 32 of the row (features 16 q .. 16 q + 15 of the chunk).  For
+// a block starting at a multiple of 32 rows the swizzle depends on l alone
+// and 2 q enters it by XOR below the row's 128 bytes, so a fragment's LDS
+// address is half + (lane part ^ 32 q) + 128 * (block's first row): the
+// last term is the instruction's immediate offset, and one register per
+// side holds the lane part (with the wave's first row of that side).
+__device__ __forceinline__ uint32_t frag_lane(int row0) {
+  const int lane = threadIdx.x & 63, lrow = lane & 31;
+  return (uint32_t)((row0 + lrow) * kRowBytes + (swz(lrow, lane >> 5) << 4));
+}
+// Address of substep q's fragments in the half at LDS address half, computed
+// where it is used (not kept live across the loop).
+__device__ __forceinline__ uint32_t sub_addr(uint32_t half, uint32_t lane_part, int q) {
+  asm volatile("" : "+v"(lane_part));
+  return half + (lane_part ^ (uint32_t)(32 * q));
+}
+typedef __attribute__((address_space(3))) const u16x8 lds_u16x8;
+__device__ __forceinline__ u16x8 frag(uint32_t addr, int block) {
+  return *(lds_u16x8*)(size_t)(addr + (uint32_t)(block * 32 * kRowBytes));
 }
 
-struct Frags {
-  u16x8 a[kBA], b[kBO];
-};
 
 __device__ __forceinline__ int wave_row() { return (threadIdx.x >> 6) / kWaveCols; }
 __device__ __forceinline__ int wave_col() { return (threadIdx.x >> 6) % kWaveCols; }
 
-// Fragment q of a substep: q = 0, 1 the t blocks b[0], b[1]; q = 2..5 the s
-// blocks a[0..3] -- the order in which the MFMAs first need them.
-__device__ __forceinline__ void read_frag(Frags& f, const unsigned char* stage, int ks, int q) {
-  if (q < kBO) f.b[q] = frag(stage + kSideBytes, wave_col() * (kBO * 32) + q * 32, ks);
-  else f.a[q - kBO] = frag(stage, wave_row() * (kBA * 32) + (q - kBO) * 32, ks);
-}
+
+// A wave's fragments: s fragments of two substeps (the MFMAs' and the next
+// one's), t fragments of all four substeps of a chunk.
+struct Frags {
+  u16x8 a[2][kBA];
+  u16x8 b[4][kBO];
+};
 
 struct Acc {
   f32x16 v[kBA][kBO];
@@ -224,25 +254,37 @@ struct Acc {
 #pragma unroll
       for (int j = 0; j < kBO; ++j) asm volatile("" : "+a"(v[i][j]));
   }
-  // MFMA k of a substep: block (k / kBO, k % kBO).
-  __device__ __forceinline__ void mma1(const Frags& f, int k) {
-    v[k / kBO][k % kBO] = mfma_32x32x16(f.a[k / kBO], f.b[k % kBO], v[k / kBO][k % kBO]);
+  // MFMA k of substep q: block (k / kBO, k % kBO).
+  __device__ __forceinline__ void mma1(const Frags& f, int q, int k) {
+    v[k / kBO][k % kBO] =
+        mfma_32x32x16(f.a[q & 1][k / kBO], f.b[q][k % kBO], v[k / kBO][k % kBO]);
   }
 };
 
+// Slots of chunk c's halves (c counted from the run's first chunk).
+__device__ __forceinline__ int slot_s(int c) { return 2 * (c % 3); }
+__device__ __forceinline__ int slot_t(int c) { return 1 + 2 * (c & 1); }
+
 // Steps k0 .. k0+n-1 (32 features each) of one side (a: X or G, D features)
-// of item (b, S, Tb) into acc.
+// of item (b, S, Tb) into acc, as 16-feature substeps u = 2 k0 .. 2 (k0+n) - 1
+// (chunk u / 4, substep q = u % 4 of it).  Halves h = 0, 1, 2, ... of the run
+// (h / 2 the chunk counted from the one holding step k0, h % 2 the side)
+// are queued in that order: five up front, then the t half of chunk c + 2
+// in substep 1 of chunk c and the s half of chunk c + 3 in its substep 3.
 //
-// Five 32 KiB LDS slots.  Barrier i (between the two substeps of step i)
-// certifies that step i+1 has landed for every wave and that every wave's
-// reads of step i-1 are complete; slot (i-1) is then refilled with step i+4:
-//
-//   substep 0 of step i : MFMAs on f0, reads of f1 (step i, features 16..31)
-//   wait for f1, wait for step i+1's DMA, barrier
-//   substep 1 of step i : MFMAs on f1, DMA of step i+4, reads of f0 (step i+1)
+//   substep q of chunk c : eight MFMAs; between them the reads of the next
+//     substep's s fragments, in substep 3 also the t fragments 0-2 of chunk
+//     c + 1, in substep 0 the t fragment 3 of chunk c; in substeps 1 and 3
+//     the DMAs of the half named above
+//   after substep 0 : barrier (every wave holds chunk c's t fragments: its t
+//     slot is free)
+//   after substep 2 (chunk c + 1 follows) : wait for chunk c + 1, barrier
+//     (it has landed, and every wave's reads of chunk c's s half are done)
 __device__ __forceinline__ void run(const LayerArgs& p, const Act& a, int D, int b, int S, int Tb,
                                     int k0, int n, Acc& acc, unsigned char* lds) {
-  static_assert(kBA * kBO == 8 && kBA + kBO == 6, "interleave encodes 8 MFMAs and 6 fragments");
+  static_assert(kBA == 4 && kBO == 2, "the interleave encodes 8 MFMAs per substep");
+  static_assert(kWaveRows * kWaveCols == kWaves, "wave grid");
+  static_assert(kSlots == 5, "the slot rota assumes five halves");
   acc.zero();
   if (n <= 0) return;
   const __amdgpu_buffer_rsrc_t r = sample_rsrc(a, b, p.T, D);
@@ -250,65 +292,148 @@ __device__ __forceinline__ void run(const LayerArgs& p, const Act& a, int D, int
   DmaLane dl;
   dl.init(p, a, b, S, Tb, tid);
   const uint32_t base = lds_addr(lds);
-  // This wave's DMAs fill kDmaPerStep consecutive KiB of a slot.
-  const uint32_t wdst = (uint32_t)(kDmaPerStep * __builtin_amdgcn_readfirstlane(tid >> 6)) * 1024u;
+  // This wave's DMAs fill kDmaPerHalf consecutive KiB of a slot.
+  const uint32_t wdst = (uint32_t)(kDmaPerHalf * __builtin_amdgcn_readfirstlane(tid >> 6)) * 1024u;
+  const int m0 = k0 >> 1;
+  const int nc = ((k0 + n - 1) >> 1) - m0 + 1;      // chunks of the run
+  const int nh = 2 * nc;                            // halves of the run
+  const int u0 = 2 * k0 - 4 * m0, u1 = 2 * (k0 + n) - 4 * m0;   // substeps, from chunk 0
+  auto half_slot = [&](int h) { return (h & 1) ? slot_t(h >> 1) : slot_s(h >> 1); };
 #pragma unroll
-  for (int k = 0; k < kStages; ++k) {
-    if (k < n) {
-      StepDma sd;
-      sd.at(k0 + k, D);
+  for (int h = 0; h < kSlots; ++h) {
+    if (h < nh) {
+      HalfDma hd;
+      hd.at(m0 + (h >> 1), D);
+      const uint32_t dst = base + (uint32_t)half_slot(h) * kHalfBytes + wdst;
 #pragma unroll
-      for (int j = 0; j < kDmaPerStep; ++j) sd.dma(r, dl, base + k * kStageBytes + wdst, j);
+      for (int j = 0; j < kDmaPerHalf; ++j) hd.dma(r, (h & 1) ? dl.t[j] : dl.s[j], dst, j);
     }
   }
-  wait_dma(min(kStages - 1, n - 1));   // step 0 has landed for this wave
+  int issued = min(nh, kSlots);
+  wait_halves(issued - 2);             // chunk 0 has landed for this wave
   step_barrier();
-  Frags f0, f1;
+  Frags f;
+  // lane parts of the s blocks (rows wave_row * 128 + 32 i) and the t blocks
+  // (rows wave_col * 64 + 32 j)
+  const uint32_t ls = frag_lane(wave_row() * (kBA * 32));
+  const uint32_t lt = frag_lane(wave_col() * (kBO * 32));
+  auto half_at = [&](int slot) { return base + (uint32_t)slot * kHalfBytes; };
+  {
+    const int q0 = u0 & 3;             // 0 or 2: s fragments in f.a[0]
+    const uint32_t as = sub_addr(half_at(slot_s(0)), ls, q0);
 #pragma unroll
-  for (int q = 0; q < 6; ++q) read_frag(f0, lds, 0, q);
-  int slot = 0;                        // i % kStages
-  for (int i = 0; i < n; ++i) {
-    const unsigned char* st = lds + slot * kStageBytes;
+    for (int i = 0; i < kBA; ++i) f.a[0][i] = frag(as, i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t at = sub_addr(half_at(slot_t(0)), lt, q);
+#pragma unroll
+      for (int j = 0; j < kBO; ++j) f.b[q][j] = frag(at, j);
+    }
+  }
+  lds_reads_done();
+  step_barrier();                      // chunk 0's t slot is free
+  // The next half in line goes out now if it is the t half of chunk 2.
+  HalfDma hd;
+  uint32_t dst = 0;
+  bool tside = false;
+  auto prepare = [&](int h) {          // true: DMAs of half h to issue
+    if (h != issued || h >= nh) return false;
+    hd.at(m0 + (h >> 1), D);
+    dst = base + (uint32_t)half_slot(h) * kHalfBytes + wdst;
+    tside = h & 1;
+    ++issued;
+    return true;
+  };
+  if (prepare(5)) {
+#pragma unroll
+    for (int j = 0; j < kDmaPerHalf; ++j) hd.dma(r, tside ? dl.t[j] : dl.s[j], dst, j);
+  }
+  // Substep q of chunk c: its eight MFMAs, with the reads of the next
+  // substep's fragments and the DMAs of the half queued now between them,
+  // then the barrier after it.  Returns false after the run's last substep.
+  // STEADY: a full chunk with three more after it (both of its halves to
+  // queue, both barriers taken), where nothing needs testing.
+  auto substep = [&](auto qc, auto steady, int c, uint32_t hs, uint32_t ht, uint32_t ns,
+                     uint32_t nt) -> bool {
+    constexpr int q = decltype(qc)::value;
+    constexpr bool STEADY = decltype(steady)::value;
+    const int u = 4 * c + q;
+    if (!STEADY && (u < u0 || u >= u1)) return true;
+    const bool more = STEADY || u + 1 < u1;
+    bool dma = false;
+    if constexpr (q == 1 || q == 3) {
+      if constexpr (STEADY) {
+        // the t half of chunk c + 2 into chunk c's t slot, or the s half of
+        // chunk c + 3 into its s slot
+        hd.at(m0 + c + (q == 1 ? 2 : 3), D);
+        dst = (q == 1 ? ht : hs) + wdst;
+        tside = q == 1;
+        ++issued;
+        dma = true;
+      } else {
+        dma = prepare(q == 1 ? 2 * c + 5 : 2 * c + 6);
+      }
+    }
+    // addresses of this substep's reads
+    const uint32_t an = q < 3 ? sub_addr(hs, ls, q + 1) : sub_addr(ns, ls, 0);
+    uint32_t at = 0;
+    if constexpr (q == 0) at = sub_addr(ht, lt, 3);
     acc.pin();
     sched_fence();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      acc.mma1(f0, k);
+      acc.mma1(f, q, k);
       sched_fence();
-      if (k < 6) read_frag(f1, st, 1, k);
-      sched_fence();
-    }
-    lds_reads_done();                  // f1 is in registers; slot i-1 is no longer read
-    const int next = (slot + 1 == kStages) ? 0 : slot + 1;
-    const unsigned char* sn = lds + next * kStageBytes;
-    // Issued so far: steps 0 .. min(4, n-1) before the loop, then step j+4
-    // at barrier j >= 1, i.e. up to max(4, i+3).  Wait for step i+1: in the
-    // steady state that leaves two steps in flight.
-    const bool steady = i >= 1 && i + kStages - 1 < n;
-    if (steady) {
-      wait_dma(2);
-      step_barrier();
-    } else if (i + 1 < n) {
-      wait_dma(min(n - 1, i <= 1 ? kStages - 1 : i + kStages - 2) - (i + 1));
-      step_barrier();
-    }
-    // slot (i-1) % kStages is free: queue step i+4 into it, one DMA after
-    // every other MFMA.  The reads of f0 follow; on the last step they read
-    // the next slot's stale contents, which are never used.
-    const uint32_t prev = base + ((slot == 0) ? kStages - 1 : slot - 1) * kStageBytes + wdst;
-    StepDma sd;
-    if (steady) sd.at(k0 + i + kStages - 1, D);   // step i+4 of this side
-    sched_fence();
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc.mma1(f1, k);
-      sched_fence();
-      if ((k & 1) == 0 && steady) sd.dma(r, dl, prev, k >> 1);
-      if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
+      if (dma && (k & 1) == 0) hd.dma(r, tside ? dl.t[k >> 1] : dl.s[k >> 1], dst, k >> 1);
+      if (more) {
+        if (k < kBA) {
+          f.a[(q + 1) & 1][k] = frag(an, k);
+        } else if constexpr (q == 3) {
+          // t fragments of substeps 0..2 of chunk c + 1 (3 is in use)
+          const int x = k - kBA;
+          if (x < 3) {
+            const uint32_t ax = sub_addr(nt, lt, x);
+            f.b[x][0] = frag(ax, 0);
+            f.b[x][1] = frag(ax, 1);
+          }
+        } else if constexpr (q == 0) {
+          if (k == kBA && (STEADY || c >= 1)) {
+            f.b[3][0] = frag(at, 0);
+            f.b[3][1] = frag(at, 1);
+          }
+        }
+      }
       sched_fence();
     }
-    slot = next;
-  }
+    if (!more) return false;
+    if constexpr (q == 0) {
+      if (STEADY || c >= 1) {
+        lds_reads_done();
+        step_barrier();                // chunk c's t slot is free
+      }
+    } else if constexpr (q == 2) {
+      if (STEADY || u + 2 < u1) {
+        lds_reads_done();
+        // halves up to 2c + 3 are needed; those queued after may fly
+        wait_halves(STEADY ? 2 : issued - (2 * c + 4));
+        step_barrier();
+      }
+    }
+    return true;
+  };
+  auto chunk = [&](auto steady, int c) -> bool {
+    const uint32_t hs = half_at(slot_s(c)), ht = half_at(slot_t(c));
+    const uint32_t ns = half_at(slot_s(c + 1)), nt = half_at(slot_t(c + 1));
+    return substep(std::integral_constant<int, 0>{}, steady, c, hs, ht, ns, nt) &&
+           substep(std::integral_constant<int, 1>{}, steady, c, hs, ht, ns, nt) &&
+           substep(std::integral_constant<int, 2>{}, steady, c, hs, ht, ns, nt) &&
+           substep(std::integral_constant<int, 3>{}, steady, c, hs, ht, ns, nt);
+  };
+  // chunk 0, then the steady chunks 1 .. nc - 4, then the last ones
+  bool go = chunk(std::false_type{}, 0);
+  int c = 1;
+  for (; go && c <= nc - 4; ++c) chunk(std::true_type{}, c);
+  for (; go && c < nc; ++c) go = chunk(std::false_type{}, c);
   __syncthreads();                     // every wave is done with the slot ring
 }
 
