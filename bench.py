@@ -54,12 +54,12 @@ KERNEL_COUNTERS = {
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     "kernels": {
-        "accumulate": {"sources_sha256": "760532996b0465f80e64364a5a7a9ae8d1aeee08ae7488488286ad7d243262ec",
-                       "fetch_kib": 1131507.42, "write_kib": 279698.29, "mfma_busy_pct": 61.96,
-                       "trace_avg_us": 1255.0},
-        "gram_norm": {"sources_sha256": "a22f5cd2595a5c58255194bb6fda470b276f620ce31f9b99869ede600f370a06",
-                      "fetch_kib": 416404.74, "write_kib": 152505.24, "mfma_busy_pct": 51.28,
-                      "trace_avg_us": 503.0},
+        "accumulate": {"sources_sha256": "3cd0e0ff609994d5eb326b2bd1fe25d1d2abf1edf508fb0863e3c007592ecd48",
+                       "fetch_kib": 1129651.95, "write_kib": 279698.29, "mfma_busy_pct": 60.9,
+                       "trace_avg_us": 1290.0},
+        "gram_norm": {"sources_sha256": "5961bdc8fd6118083cfcb91797fcb5c9f0ba59e18e3b4531a0ed7512fe52b137",
+                      "fetch_kib": 413803.2, "write_kib": 163988.38, "mfma_busy_pct": 64.66,
+                      "trace_avg_us": 434.4},
     },
     # --norm-path values that run these kernels on every linear of the workload
     "paths": ("0", "1"),
