@@ -123,6 +123,14 @@ struct DmaLane {
 // byte offsets of its first token row in X and G.  Without a mask, steps
 // run through every sample in order and the offsets advance by constant
 // increments; with one, the active-step list gives each step.
+//
+// With a mask the list entry and row bits of a step are scalar loads.  In
+// the main loop they are fetched ahead (fetch), just before a point where
+// the wave waits for all of its LDS reads anyway, so that no other wait in
+// the loop has to cover a scalar load: with the entries of steps k + 1 and
+// k + 2 already in registers, the row bits of step k + 1 and the entry of
+// step k + 3 (two independent loads).  Indices past the list's end read its
+// spare entry.
 template <bool MASK>
 struct Issue {
   __amdgpu_buffer_rsrc_t rx, rg;
@@ -131,12 +139,20 @@ struct Issue {
   uint32_t wdst;               // this wave's rows within a slot (LDS bytes)
   uint32_t bits;               // with a mask: this wave's rows' activity bits of the step
   const uint32_t* list;
+  int count;                   // with a mask: active steps (list[count] is a spare entry)
+  uint32_t v1, v2, v3, bits1;  // with a mask: entries of steps k + 1 .. k + 3, bits of k + 1
   __device__ __forceinline__ void rsrc(const LayerArgs& p) {
     rx = sample_rsrc(p.X, b, p.T, p.din);
     rg = sample_rsrc(p.G, b, p.T, p.dout);
   }
-  __device__ __forceinline__ void load(const LayerArgs& p) {
-    const uint32_t v = ((c_u32*)list)[k];
+  __device__ __forceinline__ uint32_t entry(int j) const {
+    return ((c_u32*)list)[j < count ? j : count];
+  }
+  __device__ __forceinline__ uint32_t row_bits_of(const LayerArgs& p, uint32_t v) const {
+    return step_bits<MASK>(p, (int)(v >> 16), (int)(v & 0xffffu));
+  }
+  // Step k from its list entry v and its row bits.
+  __device__ __forceinline__ void decode(const LayerArgs& p, uint32_t v, uint32_t rb) {
     const int nb = (int)(v >> 16);
     s = (int)(v & 0xffffu);
     xs = (uint32_t)s * dx;     // < 2^31: span checked on the host
@@ -145,7 +161,25 @@ struct Issue {
       b = nb;
       rsrc(p);
     }
-    bits = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
+    bits = rb >> (wdst / kRowBytes);
+  }
+  __device__ __forceinline__ void load(const LayerArgs& p) {
+    const uint32_t v = entry(k);
+    decode(p, v, row_bits_of(p, v));
+  }
+  // Arms the look-ahead of the main loop (after the prologue's steps).
+  __device__ __forceinline__ void arm(const LayerArgs& p) {
+    if constexpr (MASK) {
+      v1 = entry(k + 1);
+      v2 = entry(k + 2);
+    }
+  }
+  // The scalar loads for the advance that follows (see above).
+  __device__ __forceinline__ void fetch(const LayerArgs& p) {
+    if constexpr (MASK) {
+      bits1 = row_bits_of(p, v1);
+      v3 = entry(k + 3);
+    }
   }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
@@ -155,6 +189,7 @@ struct Issue {
     k = k0;
     if constexpr (MASK) {
       list = p.steps + 2 + p.B;
+      count = (int)((c_u32*)p.steps)[0];
       b = -1;
       load(p);
     } else {
@@ -166,10 +201,18 @@ struct Issue {
     }
   }
   // Only called while another step remains, so b stays a valid sample.
+  // PRE: the main loop's form, whose entry and bits were fetched ahead.
+  template <bool PRE = false>
   __device__ __forceinline__ void advance(const LayerArgs& p) {
     ++k;
     if constexpr (MASK) {
-      load(p);
+      if constexpr (PRE) {
+        decode(p, v1, bits1);
+        v1 = v2;
+        v2 = v3;
+      } else {
+        load(p);
+      }
     } else if (++s == nsteps) {
       s = 0;
       xs = gs = 0u;
@@ -386,6 +429,7 @@ __device__ __forceinline__ void prologue(const LayerArgs& p, int k0, int n, int 
       if (k + 1 < n) ps.is.advance(p);
     }
   }
+  ps.is.arm(p);
 }
 
 // Wait until step 0 of a run has landed for this wave, `steps` of its DMA
@@ -454,6 +498,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
         // Consumer cursor to step i+1.
         if constexpr (MASK) {
           cc.advance();
+          if (i >= 1 && i + kStages < n) is.fetch(p);   // for the advance below
         } else if (--left == 0) {
           left = cc.nsteps;
           ++cc.b;
@@ -485,7 +530,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
       acc.mma1(f1, k);
       sched_fence();
       if ((k & 1) == 0 && steady) is.dma(p, dl, prev, k >> 1);
-      if (k == 7 && steady && i + kStages < n) is.advance(p);
+      if (k == 7 && steady && i + kStages < n) is.template advance<true>(p);
       if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
       sched_fence();
     }
