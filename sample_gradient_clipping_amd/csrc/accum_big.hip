@@ -336,24 +336,28 @@ struct Acc {
 
 // Cursor over the active (sample, 32-token step) pairs of a call, in order:
 // without a mask every step of every sample, with one the call's active-step
-// list.  k is the position in that sequence.
+// list.  k is the position in that sequence.  With a mask the entry of step
+// k + 1 is held in a register (loaded one advance ahead), so that an advance
+// only decodes it and the load it issues is not needed until the next one.
 template <bool MASK>
 struct Cursor {
   int k, b, s, nsteps;
   const uint32_t* list;
-  __device__ __forceinline__ void load() {
-    if constexpr (MASK) {
-      const uint32_t v = ((c_u32*)list)[k];
-      b = (int)(v >> 16);
-      s = (int)(v & 0xffffu);
-    }
+  int count;                   // with a mask: active steps (list[count] is a spare entry)
+  uint32_t nv;                 // with a mask: entry of step k + 1
+  __device__ __forceinline__ uint32_t entry(int j) const {
+    return ((c_u32*)list)[j < count ? j : count];
   }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
     k = k0;
     if constexpr (MASK) {
       list = p.steps + 2 + p.B;
-      load();
+      count = (int)((c_u32*)p.steps)[0];
+      const uint32_t v = entry(k);
+      b = (int)(v >> 16);
+      s = (int)(v & 0xffffu);
+      nv = entry(k + 1);
     } else {
       b = k0 / nsteps;
       s = k0 - b * nsteps;
@@ -361,8 +365,14 @@ struct Cursor {
   }
   __device__ __forceinline__ void advance() {
     ++k;
-    if constexpr (MASK) load();
-    else if (++s == nsteps) { s = 0; ++b; }
+    if constexpr (MASK) {
+      b = (int)(nv >> 16);
+      s = (int)(nv & 0xffffu);
+      nv = entry(k + 1);
+    } else if (++s == nsteps) {
+      s = 0;
+      ++b;
+    }
   }
 };
 
@@ -471,6 +481,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
   Cursor<MASK>& cc = ps.cc;
   int left = ps.left;
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
+  float c_next = c_last;               // factor of step i's sample, loaded a step ahead
   int cb = cc.b;
   wait_first(min(kStages - 1, n - 1), after_stores);   // step 0 has landed for this wave
   step_barrier();
@@ -482,9 +493,8 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
     if (SCALE && cc.b != cb) {
       // acc holds sum_{j<=cb} (c_j / c_cb) g_j; re-express it in units of the
       // new sample's factor before its tiles are added.
-      const float cn = ((c_f32*)p.c)[cc.b];
-      acc.scale(c_last / cn);
-      c_last = cn;
+      acc.scale(c_last / c_next);
+      c_last = c_next;
       cb = cc.b;
     }
     const unsigned char* st = lds + slot * kStageBytes;
@@ -495,7 +505,8 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
       sched_fence();
       if (k < 6) read_frag(f1, st, 1, k);
       if (k == 7) {
-        // Consumer cursor to step i+1.
+        // Consumer cursor to step i+1, and its sample's clip factor when the
+        // sample changes (a scalar load, waited for with the LDS reads below).
         if constexpr (MASK) {
           cc.advance();
           if (i >= 1 && i + kStages < n) is.fetch(p);   // for the advance below
@@ -503,6 +514,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
           left = cc.nsteps;
           ++cc.b;
         }
+        if (SCALE && i + 1 < n && cc.b != cb) c_next = ((c_f32*)p.c)[cc.b];
       }
       sched_fence();
     }
