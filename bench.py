@@ -54,12 +54,12 @@ KERNEL_COUNTERS = {
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     "kernels": {
-        "accumulate": {"sources_sha256": "fb228f3804e9fd7b9d4af2b6300096b4c2d5614658ad9d6a4c29de130cb2855a",
-                       "fetch_kib": 1129802.17, "write_kib": 279698.29, "mfma_busy_pct": 58.78,
-                       "trace_avg_us": 1272.7},
+        "accumulate": {"sources_sha256": "3cd0e0ff609994d5eb326b2bd1fe25d1d2abf1edf508fb0863e3c007592ecd48",
+                       "fetch_kib": 1129651.95, "write_kib": 279698.29, "mfma_busy_pct": 60.9,
+                       "trace_avg_us": 1290.0},
         "gram_norm": {"sources_sha256": "5961bdc8fd6118083cfcb91797fcb5c9f0ba59e18e3b4531a0ed7512fe52b137",
-                      "fetch_kib": 414131.22, "write_kib": 163988.4, "mfma_busy_pct": 64.47,
-                      "trace_avg_us": 422.3},
+                      "fetch_kib": 413803.2, "write_kib": 163988.38, "mfma_busy_pct": 64.66,
+                      "trace_avg_us": 434.4},
     },
     # --norm-path values that run these kernels on every linear of the workload
     "paths": ("0", "1"),

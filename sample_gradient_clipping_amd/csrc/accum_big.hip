@@ -123,14 +123,6 @@ struct DmaLane {
 // byte offsets of its first token row in X and G.  Without a mask, steps
 // run through every sample in order and the offsets advance by constant
 // increments; with one, the active-step list gives each step.
-//
-// With a mask the list entry and row bits of a step are scalar loads.  In
-// the main loop they are fetched ahead (fetch), just before a point where
-// the wave waits for all of its LDS reads anyway, so that no other wait in
-// the loop has to cover a scalar load: with the entries of steps k + 1 and
-// k + 2 already in registers, the row bits of step k + 1 and the entry of
-// step k + 3 (two independent loads).  Indices past the list's end read its
-// spare entry.
 template <bool MASK>
 struct Issue {
   __amdgpu_buffer_rsrc_t rx, rg;
@@ -139,20 +131,12 @@ struct Issue {
   uint32_t wdst;               // this wave's rows within a slot (LDS bytes)
   uint32_t bits;               // with a mask: this wave's rows' activity bits of the step
   const uint32_t* list;
-  int count;                   // with a mask: active steps (list[count] is a spare entry)
-  uint32_t v1, v2, v3, bits1;  // with a mask: entries of steps k + 1 .. k + 3, bits of k + 1
   __device__ __forceinline__ void rsrc(const LayerArgs& p) {
     rx = sample_rsrc(p.X, b, p.T, p.din);
     rg = sample_rsrc(p.G, b, p.T, p.dout);
   }
-  __device__ __forceinline__ uint32_t entry(int j) const {
-    return ((c_u32*)list)[j < count ? j : count];
-  }
-  __device__ __forceinline__ uint32_t row_bits_of(const LayerArgs& p, uint32_t v) const {
-    return step_bits<MASK>(p, (int)(v >> 16), (int)(v & 0xffffu));
-  }
-  // Step k from its list entry v and its row bits.
-  __device__ __forceinline__ void decode(const LayerArgs& p, uint32_t v, uint32_t rb) {
+  __device__ __forceinline__ void load(const LayerArgs& p) {
+    const uint32_t v = ((c_u32*)list)[k];
     const int nb = (int)(v >> 16);
     s = (int)(v & 0xffffu);
     xs = (uint32_t)s * dx;     // < 2^31: span checked on the host
@@ -161,25 +145,7 @@ struct Issue {
       b = nb;
       rsrc(p);
     }
-    bits = rb >> (wdst / kRowBytes);
-  }
-  __device__ __forceinline__ void load(const LayerArgs& p) {
-    const uint32_t v = entry(k);
-    decode(p, v, row_bits_of(p, v));
-  }
-  // Arms the look-ahead of the main loop (after the prologue's steps).
-  __device__ __forceinline__ void arm(const LayerArgs& p) {
-    if constexpr (MASK) {
-      v1 = entry(k + 1);
-      v2 = entry(k + 2);
-    }
-  }
-  // The scalar loads for the advance that follows (see above).
-  __device__ __forceinline__ void fetch(const LayerArgs& p) {
-    if constexpr (MASK) {
-      bits1 = row_bits_of(p, v1);
-      v3 = entry(k + 3);
-    }
+    bits = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
   }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
@@ -189,7 +155,6 @@ struct Issue {
     k = k0;
     if constexpr (MASK) {
       list = p.steps + 2 + p.B;
-      count = (int)((c_u32*)p.steps)[0];
       b = -1;
       load(p);
     } else {
@@ -201,18 +166,10 @@ struct Issue {
     }
   }
   // Only called while another step remains, so b stays a valid sample.
-  // PRE: the main loop's form, whose entry and bits were fetched ahead.
-  template <bool PRE = false>
   __device__ __forceinline__ void advance(const LayerArgs& p) {
     ++k;
     if constexpr (MASK) {
-      if constexpr (PRE) {
-        decode(p, v1, bits1);
-        v1 = v2;
-        v2 = v3;
-      } else {
-        load(p);
-      }
+      load(p);
     } else if (++s == nsteps) {
       s = 0;
       xs = gs = 0u;
@@ -336,28 +293,24 @@ struct Acc {
 
 // Cursor over the active (sample, 32-token step) pairs of a call, in order:
 // without a mask every step of every sample, with one the call's active-step
-// list.  k is the position in that sequence.  With a mask the entry of step
-// k + 1 is held in a register (loaded one advance ahead), so that an advance
-// only decodes it and the load it issues is not needed until the next one.
+// list.  k is the position in that sequence.
 template <bool MASK>
 struct Cursor {
   int k, b, s, nsteps;
   const uint32_t* list;
-  int count;                   // with a mask: active steps (list[count] is a spare entry)
-  uint32_t nv;                 // with a mask: entry of step k + 1
-  __device__ __forceinline__ uint32_t entry(int j) const {
-    return ((c_u32*)list)[j < count ? j : count];
+  __device__ __forceinline__ void load() {
+    if constexpr (MASK) {
+      const uint32_t v = ((c_u32*)list)[k];
+      b = (int)(v >> 16);
+      s = (int)(v & 0xffffu);
+    }
   }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
     k = k0;
     if constexpr (MASK) {
       list = p.steps + 2 + p.B;
-      count = (int)((c_u32*)p.steps)[0];
-      const uint32_t v = entry(k);
-      b = (int)(v >> 16);
-      s = (int)(v & 0xffffu);
-      nv = entry(k + 1);
+      load();
     } else {
       b = k0 / nsteps;
       s = k0 - b * nsteps;
@@ -365,14 +318,8 @@ struct Cursor {
   }
   __device__ __forceinline__ void advance() {
     ++k;
-    if constexpr (MASK) {
-      b = (int)(nv >> 16);
-      s = (int)(nv & 0xffffu);
-      nv = entry(k + 1);
-    } else if (++s == nsteps) {
-      s = 0;
-      ++b;
-    }
+    if constexpr (MASK) load();
+    else if (++s == nsteps) { s = 0; ++b; }
   }
 };
 
@@ -439,7 +386,6 @@ __device__ __forceinline__ void prologue(const LayerArgs& p, int k0, int n, int 
       if (k + 1 < n) ps.is.advance(p);
     }
   }
-  ps.is.arm(p);
 }
 
 // Wait until step 0 of a run has landed for this wave, `steps` of its DMA
@@ -481,7 +427,6 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
   Cursor<MASK>& cc = ps.cc;
   int left = ps.left;
   float c_last = SCALE ? ((c_f32*)p.c)[cc.b] : 1.0f;
-  float c_next = c_last;               // factor of step i's sample, loaded a step ahead
   int cb = cc.b;
   wait_first(min(kStages - 1, n - 1), after_stores);   // step 0 has landed for this wave
   step_barrier();
@@ -493,8 +438,9 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
     if (SCALE && cc.b != cb) {
       // acc holds sum_{j<=cb} (c_j / c_cb) g_j; re-express it in units of the
       // new sample's factor before its tiles are added.
-      acc.scale(c_last / c_next);
-      c_last = c_next;
+      const float cn = ((c_f32*)p.c)[cc.b];
+      acc.scale(c_last / cn);
+      c_last = cn;
       cb = cc.b;
     }
     const unsigned char* st = lds + slot * kStageBytes;
@@ -505,16 +451,13 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
       sched_fence();
       if (k < 6) read_frag(f1, st, 1, k);
       if (k == 7) {
-        // Consumer cursor to step i+1, and its sample's clip factor when the
-        // sample changes (a scalar load, waited for with the LDS reads below).
+        // Consumer cursor to step i+1.
         if constexpr (MASK) {
           cc.advance();
-          if (i >= 1 && i + kStages < n) is.fetch(p);   // for the advance below
         } else if (--left == 0) {
           left = cc.nsteps;
           ++cc.b;
         }
-        if (SCALE && i + 1 < n && cc.b != cb) c_next = ((c_f32*)p.c)[cc.b];
       }
       sched_fence();
     }
@@ -542,7 +485,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
       acc.mma1(f1, k);
       sched_fence();
       if ((k & 1) == 0 && steady) is.dma(p, dl, prev, k >> 1);
-      if (k == 7 && steady && i + kStages < n) is.template advance<true>(p);
+      if (k == 7 && steady && i + kStages < n) is.advance(p);
       if (k >= 1 && k <= 6) read_frag(f0, sn, 0, k - 1);
       sched_fence();
     }
