@@ -300,6 +300,32 @@ def test_gram_items_split_over_all_workgroups(B):
     _check(lin, 1, sigma=0.6, C=C)
 
 
+def test_gram_split_pieces_on_odd_steps_and_tail_chunks():
+    """The Gram kernel loads 64-feature chunks but computes and splits in
+    32-feature steps.  300 samples of T = 40 give 300 one-block items: 256 in
+    the full round, 44 split.  din = 1096 (35 steps; its last chunk holds 8
+    features) and dout = 520 (17 steps) make 52 steps, which the plan cuts
+    into 3 pieces: X steps [0, 17) (ends half way into a chunk), [17, 34)
+    (starts half way into one), and the single step [34, 35) (the 8-feature
+    tail chunk) followed by all of G.  Norms and the clipped sum against the
+    oracle, with mixed clipping."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(47)
+    lin = random_linear(rng, 300, 40, 1096, 520)
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn))
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        _check(lin, 1, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+        kernels = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    assert "gram_norm" in kernels and "gram_fixup" in kernels, sorted(kernels)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 100, 1000, 72), (3, 33, 1000, 70)])
 def test_projected_split_along_din(dtype, shape):
