@@ -87,15 +87,34 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
 }
 
-// Active-row bits of the 32 tokens of step s of sample b.  MASK: the call
-// has a token mask (row bits in memory); otherwise only the tail past T is
-// inactive, and no memory is read -- which keeps scalar loads out of the
-// main loop, so the compiler can wait for LDS reads precisely.
-template <bool MASK>
+// Token masks come in three forms (MASK): 0 none; 1 a mask, stepped through
+// by the call's active-step list (one list entry and one row-bit word read
+// per step); 2 a mask in which every sample's active tokens are a prefix of
+// its rows (padding at the end), stepped through by the samples' step
+// ranges, so that only a change of sample reads memory.
+//
+// Active-row bits of the 32 tokens of step s of sample b.  With a mask they
+// are in memory; otherwise only the tail past T is inactive, and no memory
+// is read -- which keeps scalar loads out of the main loop, so the compiler
+// can wait for LDS reads precisely.
+template <int MASK>
 __device__ __forceinline__ uint32_t step_bits(const LayerArgs& p, int b, int s) {
   if constexpr (MASK) return ((c_u32*)p.rowbits)[(int64_t)b * p.nwords + s];
   const int n = p.T - s * kKT;
   return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
+
+// MASK 2: the sample whose step range holds position k0 of the call's steps
+// (k0 < n): the last b with first step <= k0, by bisection over the samples'
+// first-step indices (samples without a step share their successor's).
+__device__ __forceinline__ int prefix_sample_of(const LayerArgs& p, int k0) {
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)((c_u32*)p.steps)[1 + mid] <= k0) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 // Per-lane, per-step-invariant part of the DMA addressing: lane l of DMA j
@@ -123,7 +142,7 @@ struct DmaLane {
 // byte offsets of its first token row in X and G.  Without a mask, steps
 // run through every sample in order and the offsets advance by constant
 // increments; with one, the active-step list gives each step.
-template <bool MASK>
+template <int MASK>
 struct Issue {
   __amdgpu_buffer_rsrc_t rx, rg;
   int b, s, k, nsteps;
@@ -131,6 +150,8 @@ struct Issue {
   uint32_t wdst;               // this wave's rows within a slot (LDS bytes)
   uint32_t bits;               // with a mask: this wave's rows' activity bits of the step
   const uint32_t* list;
+  int ns, nxt;                 // MASK 2: steps of sample b, index of sample b + 1's first step
+  uint32_t last;               // MASK 2: row bits of sample b's last step
   __device__ __forceinline__ void rsrc(const LayerArgs& p) {
     rx = sample_rsrc(p.X, b, p.T, p.din);
     rg = sample_rsrc(p.G, b, p.T, p.dout);
@@ -147,13 +168,32 @@ struct Issue {
     }
     bits = step_bits<MASK>(p, b, s) >> (wdst / kRowBytes);
   }
+  // MASK 2: sample b's steps are 0 .. ns - 1, every row active but in the
+  // last step, whose bits are `last`.
+  __device__ __forceinline__ void prefix_bits() {
+    bits = (s == ns - 1 ? last : 0xffffffffu) >> (wdst / kRowBytes);
+  }
+  __device__ __forceinline__ void prefix_enter(const LayerArgs& p) {
+    last = ((c_u32*)p.rowbits)[(int64_t)b * p.nwords + ns - 1];
+    rsrc(p);
+  }
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
     dx = (uint32_t)kKT * (uint32_t)p.X.stride_t * 2u;
     dg = (uint32_t)kKT * (uint32_t)p.G.stride_t * 2u;
     wdst = (uint32_t)(kRowsPerWave * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRowBytes);
     k = k0;
-    if constexpr (MASK) {
+    if constexpr (MASK == 2) {
+      b = prefix_sample_of(p, k0);
+      const int first = (int)((c_u32*)p.steps)[1 + b];
+      nxt = (int)((c_u32*)p.steps)[2 + b];
+      ns = nxt - first;
+      s = k0 - first;
+      xs = (uint32_t)s * dx;
+      gs = (uint32_t)s * dg;
+      prefix_enter(p);
+      prefix_bits();
+    } else if constexpr (MASK) {
       list = p.steps + 2 + p.B;
       b = -1;
       load(p);
@@ -168,7 +208,24 @@ struct Issue {
   // Only called while another step remains, so b stays a valid sample.
   __device__ __forceinline__ void advance(const LayerArgs& p) {
     ++k;
-    if constexpr (MASK) {
+    if constexpr (MASK == 2) {
+      if (++s == ns) {
+        int first;
+        do {                           // the next sample with a step
+          ++b;
+          first = nxt;
+          nxt = (int)((c_u32*)p.steps)[2 + b];
+        } while (nxt == first);
+        ns = nxt - first;
+        s = 0;
+        xs = gs = 0u;
+        prefix_enter(p);
+      } else {
+        xs += dx;
+        gs += dg;
+      }
+      prefix_bits();
+    } else if constexpr (MASK) {
       load(p);
     } else if (++s == nsteps) {
       s = 0;
@@ -294,12 +351,14 @@ struct Acc {
 // Cursor over the active (sample, 32-token step) pairs of a call, in order:
 // without a mask every step of every sample, with one the call's active-step
 // list.  k is the position in that sequence.
-template <bool MASK>
+template <int MASK>
 struct Cursor {
   int k, b, s, nsteps;
   const uint32_t* list;
+  const uint32_t* steps;       // MASK 2: the call's step header
+  int ns, nxt, B;              // MASK 2: steps of sample b, next sample's first step, samples
   __device__ __forceinline__ void load() {
-    if constexpr (MASK) {
+    if constexpr (MASK == 1) {
       const uint32_t v = ((c_u32*)list)[k];
       b = (int)(v >> 16);
       s = (int)(v & 0xffffu);
@@ -308,7 +367,15 @@ struct Cursor {
   __device__ __forceinline__ void start(const LayerArgs& p, int k0) {
     nsteps = (p.T + kKT - 1) / kKT;
     k = k0;
-    if constexpr (MASK) {
+    if constexpr (MASK == 2) {
+      steps = p.steps;
+      B = p.B;
+      b = prefix_sample_of(p, k0);
+      const int first = (int)((c_u32*)steps)[1 + b];
+      nxt = (int)((c_u32*)steps)[2 + b];
+      ns = nxt - first;
+      s = k0 - first;
+    } else if constexpr (MASK) {
       list = p.steps + 2 + p.B;
       load();
     } else {
@@ -316,10 +383,27 @@ struct Cursor {
       s = k0 - b * nsteps;
     }
   }
+  // Also called after a run's last step (the result is then unused): the
+  // prefix form stops at the last sample instead of reading past the header.
   __device__ __forceinline__ void advance() {
     ++k;
-    if constexpr (MASK) load();
-    else if (++s == nsteps) { s = 0; ++b; }
+    if constexpr (MASK == 2) {
+      if (++s == ns) {
+        int first;
+        do {
+          ++b;
+          first = nxt;
+          nxt = (int)((c_u32*)steps)[2 + b];
+        } while (nxt == first && b + 1 < B);
+        ns = nxt - first;
+        s = 0;
+      }
+    } else if constexpr (MASK) {
+      load();
+    } else if (++s == nsteps) {
+      s = 0;
+      ++b;
+    }
   }
 };
 
@@ -361,7 +445,7 @@ __device__ __forceinline__ void step_barrier() {
 // Pipeline state of one run over an output tile: the lanes' DMA offsets,
 // the issue side, and the consumer side (the sample of the step being
 // consumed and, without a mask, the steps left before the next sample).
-template <bool MASK>
+template <int MASK>
 struct Pipe {
   DmaLane dl;
   Issue<MASK> is;
@@ -370,7 +454,7 @@ struct Pipe {
 };
 
 // Queue the first min(kStages, n) steps of a run into the slot ring.
-template <bool MASK>
+template <int MASK>
 __device__ __forceinline__ void prologue(const LayerArgs& p, int k0, int n, int a0, int o0,
                                          Pipe<MASK>& ps, uint32_t base) {
   ps.n = n;
@@ -411,7 +495,7 @@ __device__ __forceinline__ void wait_first(int steps, bool after_stores) {
 }
 
 // The run whose first steps `prologue` queued: the main loop below.
-template <bool SCALE, bool MASK>
+template <bool SCALE, int MASK>
 __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, Acc& acc,
                                             unsigned char* lds, bool after_stores) {
   static_assert(kKT == kBitsTokens, "one row-bit word per step");
@@ -495,7 +579,7 @@ __device__ __forceinline__ float run_queued(const LayerArgs& p, Pipe<MASK>& ps, 
 }
 
 // One run over n steps from position k0 of the call's sequence.
-template <bool SCALE, bool MASK>
+template <bool SCALE, int MASK>
 __device__ __forceinline__ float run(const LayerArgs& p, int k0, int n, int a0, int o0, Acc& acc,
                                      unsigned char* lds) {
   Pipe<MASK> ps;
@@ -628,10 +712,11 @@ __host__ __device__ inline int split_tiles(int R, int G, int n, int maxP) {
 
 // Active steps per tile: all of them without a mask, else the list's count.
 __device__ __forceinline__ int active_steps(const LayerArgs& p) {
-  return p.steps != nullptr ? (int)((c_u32*)p.steps)[0] : p.B * ((p.T + kKT - 1) / kKT);
+  return p.steps != nullptr ? (int)(((c_u32*)p.steps)[0] & kStepCountMask)
+                            : p.B * ((p.T + kKT - 1) / kKT);
 }
 
-template <bool MASK>
+template <int MASK>
 __device__ __forceinline__ void accumulate_body(const LayerArgs& p, SkPlan sk,
                                                 unsigned char* smem) {
   const int n = active_steps(p);
@@ -661,8 +746,9 @@ __device__ __forceinline__ void accumulate_body(const LayerArgs& p, SkPlan sk,
 
 __global__ void __launch_bounds__(kNT, 1) accumulate_big_kernel(LayerArgs p, SkPlan sk) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  if (p.steps != nullptr) accumulate_body<true>(p, sk, smem);
-  else accumulate_body<false>(p, sk, smem);
+  if (p.steps == nullptr) accumulate_body<0>(p, sk, smem);
+  else if (((c_u32*)p.steps)[0] & kStepsPrefix) accumulate_body<2>(p, sk, smem);
+  else accumulate_body<1>(p, sk, smem);
 }
 
 // Split tiles: sum their P partials in chunk order, add the noise, divide by
@@ -675,7 +761,7 @@ constexpr int kFixRows = kFixThreads / (kTile / 4);     // 4 tile rows per workg
 constexpr int kFixBlocksPerTile = kTile / kFixRows;     // 64
 constexpr int kFixBatch = 8;
 __global__ void __launch_bounds__(kFixThreads) accumulate_fixup_kernel(LayerArgs p, SkPlan sk) {
-  if (p.steps != nullptr) sk.P = split_tiles(sk.R, sk.G, (int)((c_u32*)p.steps)[0], sk.P);
+  if (p.steps != nullptr) sk.P = split_tiles(sk.R, sk.G, active_steps(p), sk.P);
   if (sk.P == 1) return;            // masked: the active steps did not call for a split
   const int r = blockIdx.x / kFixBlocksPerTile, rows = blockIdx.x % kFixBlocksPerTile;
   int tm, tn;
@@ -763,7 +849,7 @@ constexpr int64_t kImgStride = kTileElems;   // floats from one unit's image to 
 // fill overlaps this unit's reduction instead of a new workgroup's start.
 constexpr int kStagedParts = kWaves;
 
-template <bool MASK, bool NT, bool STORE>
+template <int MASK, bool NT, bool STORE>
 __device__ __forceinline__ void staged_units(const LayerArgs& p, int G, unsigned char* smem) {
   const int ntm = (p.din + kTile - 1) / kTile, ntn = (p.dout + kTile - 1) / kTile;
   const int ntiles = ntm * ntn;

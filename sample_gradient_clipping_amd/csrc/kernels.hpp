@@ -42,10 +42,15 @@ struct LayerArgs {
 };
 
 // Active-step list of a masked call, built from the row bits:
-//   steps[0]          n, the number of (sample, 32-token step) pairs with an active token
+//   steps[0]          n, the number of (sample, 32-token step) pairs with an active
+//                     token, in bits 0-30; bit 31 set when every sample's active
+//                     tokens are a prefix of its rows (its steps 0 .. k - 1, all rows
+//                     active except in step k - 1)
 //   steps[1 + b]      index of sample b's first entry (b = 0..B; steps[1 + B] = n)
 //   steps[2 + B + k]  entry k = sample << 16 | step, sample-major (k < n), then one
 //                     spare zero entry, so that reading entry n stays in bounds.
+constexpr uint32_t kStepCountMask = 0x7fffffffu;
+constexpr uint32_t kStepsPrefix = 0x80000000u;
 inline size_t step_list_words(int B, int nwords) { return (size_t)B * nwords + B + 3; }
 
 struct ProjArgs {

@@ -60,6 +60,10 @@ __global__ void row_bits_kernel(const uint8_t* mask, int B, int T, uint32_t* bit
 // Active-step list (layout in kernels.hpp) from the row bits: one workgroup
 // walks the words in order, 1024 at a time; an entry's index is the number
 // of active words before it (ballot counts within a wave, then wave totals).
+// Each word also checks that its sample stays a prefix through it: an empty
+// word is followed by an empty one, and a word that is not full is a run of
+// low bits followed by an empty one (the last word of a sample counts as
+// followed by an empty one).
 constexpr int kListThreads = 1024;
 __global__ void __launch_bounds__(kListThreads) step_list_kernel(const uint32_t* bits, int B,
                                                                  int nwords, uint32_t* steps) {
@@ -68,9 +72,17 @@ __global__ void __launch_bounds__(kListThreads) step_list_kernel(const uint32_t*
   const int64_t total = (int64_t)B * nwords;
   uint32_t* entries = steps + 2 + B;
   uint32_t base = 0;                  // active words before this chunk (same in every thread)
+  int prefix = 1;                     // every word so far keeps its sample a prefix
   for (int64_t c0 = 0; c0 < total; c0 += kListThreads) {
     const int64_t i = c0 + tid;
     const bool act = i < total && bits[i] != 0u;
+    bool ok = true;
+    if (i < total) {
+      const uint32_t x = bits[i];
+      const uint32_t next = (i % nwords) + 1 < nwords ? bits[i + 1] : 0u;
+      ok = x == 0u ? next == 0u : ((x & (x + 1u)) == 0u && (x == 0xffffffffu || next == 0u));
+    }
+    prefix = __syncthreads_and(prefix && ok);
     const uint64_t ball = __ballot(act);
     const uint32_t below = (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
     if (lane == 0) wave_count[wave] = (uint32_t)__popcll(ball);
@@ -90,7 +102,7 @@ __global__ void __launch_bounds__(kListThreads) step_list_kernel(const uint32_t*
     __syncthreads();                  // wave_count is rewritten by the next chunk
   }
   if (tid == 0) {
-    steps[0] = base;
+    steps[0] = base | (prefix ? kStepsPrefix : 0u);
     steps[1 + B] = base;
     entries[base] = 0u;               // spare entry
   }

@@ -353,7 +353,7 @@ __device__ void body(const LayerArgs& p, const Params& q, unsigned char* smem) {
   // The active steps: with a mask the call's list (sample-major), else every
   // step of every sample.
   const int nsteps = (p.T + kKT - 1) / kKT;
-  const int N = MASK ? (int)((c_u32*)p.steps)[0] : p.B * nsteps;
+  const int N = MASK ? (int)(((c_u32*)p.steps)[0] & kStepCountMask) : p.B * nsteps;
   auto first_step = [&](int b) {
     return MASK ? (int)((c_u32*)p.steps)[1 + b] : b * nsteps;
   };
