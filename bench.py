@@ -54,12 +54,12 @@ KERNEL_COUNTERS = {
     "batch": 8, "seq": 2048, "linears": "q,k,v,o,gate,up,down",
     "fetch_scale": 2.0, "write_scale": 1.0,
     "kernels": {
-        "accumulate": {"sources_sha256": "3cd0e0ff609994d5eb326b2bd1fe25d1d2abf1edf508fb0863e3c007592ecd48",
-                       "fetch_kib": 1129651.95, "write_kib": 279698.29, "mfma_busy_pct": 60.9,
-                       "trace_avg_us": 1290.0},
+        "accumulate": {"sources_sha256": "cfc2fa80dca168539b532d85f1c9cac808c9ce9461eb95419b504cb4245f4141",
+                       "fetch_kib": 1130394.79, "write_kib": 279698.29, "mfma_busy_pct": 59.84,
+                       "trace_avg_us": 1288.9},
         "gram_norm": {"sources_sha256": "5961bdc8fd6118083cfcb91797fcb5c9f0ba59e18e3b4531a0ed7512fe52b137",
-                      "fetch_kib": 413803.2, "write_kib": 163988.38, "mfma_busy_pct": 64.66,
-                      "trace_avg_us": 434.4},
+                      "fetch_kib": 413918.2, "write_kib": 163988.28, "mfma_busy_pct": 64.81,
+                      "trace_avg_us": 429.1},
     },
     # --norm-path values that run these kernels on every linear of the workload
     "paths": ("0", "1"),
