@@ -326,6 +326,37 @@ def test_gram_split_pieces_on_odd_steps_and_tail_chunks():
     assert "gram_norm" in kernels and "gram_fixup" in kernels, sorted(kernels)
 
 
+@pytest.mark.parametrize("hole", [False, True])
+def test_prefix_mask_pieces_across_samples(hole):
+    """Prefix masks (padding at the end) are walked by each sample's step
+    range, other masks by the active-step list.  One 256 x 256 output tile
+    over 54 active steps is split into 13 pieces of about 4 steps, so
+    pieces start inside samples, right after samples with no token, and
+    cross sample boundaries.  Lengths include multiples of 32 (a full last
+    step), single tokens and empty samples; with `hole` one token inside a
+    sample is masked as well, which makes the mask no prefix.  Norms and the
+    clipped sum (mixed clipping) and the noise against the oracle."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    lengths = [512, 0, 64, 1, 33, 0, 0, 480, 32, 511, 2, 0]
+    rng = np.random.default_rng(48)
+    lin = random_linear(rng, len(lengths), 512, 256, 256, lengths=lengths)
+    if hole:
+        lin.mask[7, 100] = 0
+    _, rn, _ = _oracle(lin, C=1.0, sigma=0.0)
+    C = float(np.median(rn[rn > 0]))
+    dp.timing_reset()
+    dp.set_option("timing", 1)
+    try:
+        _check(lin, 0, sigma=0.0, C=C, agg_tol=SUM_TOL_BF16)
+        _check(lin, 0, sigma=0.7, C=C)
+        kernels = dp.timing_collect()
+    finally:
+        dp.set_option("timing", 0)
+        dp.timing_reset()
+    assert "accumulate_fixup" in kernels, sorted(kernels)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 100, 1000, 72), (3, 33, 1000, 70)])
 def test_projected_split_along_din(dtype, shape):
