@@ -359,6 +359,28 @@ def measure_configs(dp, torch, steps, warmup, only=None):
             "frac_of_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
             "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
 
+        # the same six calls in one library call, queued on the library's streams so that
+        # the linears' small launches overlap (each linear still clipped on its own; the
+        # noise offsets are consecutive, as that call requires with sigma > 0)
+        assert all(l.C == lins[0].C and l.sigma == lins[0].sigma for l in lins)
+        mX, mG = [d[1] for d in dev], [d[2] for d in dev]
+        mP, mo, mn = [Ps[d[0].din] for d in dev], [d[3] for d in dev], [d[4] for d in dev]
+
+        def many_layer():
+            dp.linear_clip_accumulate_projected_many(mX, mG, mP, None, C=lins[0].C,
+                                                     sigma=lins[0].sigma, grad_outs=mo,
+                                                     norms_outs=mn)
+        ms = time_calls(torch, many_layer, steps, warmup)
+        out["c5_roberta_large_projected_r256_6_linears_side_streams"] = {
+            "note": "as c5 above, the six projected calls queued together "
+                    "(linear_clip_accumulate_projected_many: the caller's stream and one library "
+                    "stream, calls alternating; each output bitwise the single call's for the "
+                    "same offsets)",
+            "linears": len(lins), "ms": round(ms, 4),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "samples_per_s": round(lins[0].B / (ms * 1e-3), 1)}
+
         # the same, with P drawn from its seed inside the projection (never stored)
         def seeded_layer():
             for lin, X, G, o, nrm in dev:

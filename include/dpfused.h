@@ -198,6 +198,43 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
                                                     float* grad_out, float* norms_out,
                                                     void* stream);
 
+/* Several independent projected calls queued together, for example the six
+ * linears of one RoBERTa layer: call l is
+ *
+ *   dpfused_linear_clip_accumulate_projected(&X[l], &G[l], masks[l], P[l], r,
+ *       C, sigma, seed, offsets[l], grad_out[l], norms_out[l], stream)
+ *
+ * each clipped on its own (per-layer clipping, as in the single call).  The
+ * calls run on streams of the library, forked from `stream` after its earlier
+ * work and joined back into it, so that the small launches of different
+ * linears overlap on the GPU; every output is bitwise that of the single
+ * call.  Call l runs on branch l mod (k + 1): branch 0 is `stream` itself,
+ * branch j the library's stream j - 1, with k = the "side_streams" option
+ * (default 1, at most 4; 0 queues every call on `stream`).  When `stream` is
+ * being captured into a graph, with n = 1, or with the staged norm path
+ * forced, the calls run one after another on `stream`.  The library's streams
+ * (four per device, default priority) live until the process ends.
+ *
+ *   n          number of calls, 1 .. 64
+ *   X, G       HOST arrays of n descriptors (each call its own B, T, din, dout)
+ *   masks      HOST array of n mask pointers ([B_l, T_l] or NULL), or NULL
+ *   P          HOST array of n DEVICE pointers, P[l] [din_l, r] in X[l]'s dtype
+ *   r          projection width, shared
+ *   offsets    HOST array of n Philox offsets; with sigma > 0 the block ranges
+ *              [offsets[l], offsets[l] + dpfused_noise_blocks(dout_l * r)) must
+ *              be pairwise disjoint, else DPF_ERR_INVALID_ARGUMENT
+ *   grad_out   HOST array of n DEVICE pointers, grad_out[l] [dout_l, r]
+ *   norms_out  HOST array of n DEVICE pointers ([B_l] float32 or NULL), or NULL
+ *
+ * Errors as for the single call, checked for every call before anything is
+ * queued; the workspace of all calls is taken at once, so an allocation
+ * failure leaves every output untouched.  Calls that overlap in time on one
+ * GPU from several host threads are queued one at a time. */
+dpf_status dpfused_linear_clip_accumulate_projected_many(
+    int32_t n, const dpf_act* X, const dpf_act* G, const uint8_t* const* masks,
+    const void* const* P, int64_t r, float C, float sigma, uint64_t seed, const uint64_t* offsets,
+    float* const* grad_out, float* const* norms_out, void* stream);
+
 /* Projected variant with the projection regenerated from a seed instead of
  * stored (same explainer, Methodology, "Random Projection over SVD": the
  * random matrices need not be kept, since they can be drawn again from their
@@ -445,6 +482,10 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                kernels that use it, never stored (slower at many token
  *                tiles); 0 (default) = drawn once per call into workspace
  *                where that is cheaper.  Results are identical.
+ *   "side_streams"  0 .. 4: library streams that
+ *                dpfused_linear_clip_accumulate_projected_many spreads its
+ *                calls over beside the caller's stream (default 1; 0 = all
+ *                on the caller's stream).  Results are identical.
  *   "trace"      1 = push a roctx range named after the entry point around
  *                every call, for rocprofv3 --marker-trace; 0 = off (default)
  *   "debug"      1 = synchronise the launch stream after every kernel and

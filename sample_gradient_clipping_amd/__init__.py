@@ -24,6 +24,7 @@ __all__ = [
     "linear_clip_accumulate", "linear_clip_accumulate_noalloc", "linear_clip_accumulate_projected",
     "linear_clip_accumulate_projected_seeded", "linear_clip_accumulate_bias", "project",
     "group_clip_accumulate", "consecutive_offsets", "projected_adam_step",
+    "linear_clip_accumulate_projected_many",
     "per_sample_sqnorms",
     "clip_factors", "scaled_accumulate", "philox4x32_10", "gaussian_fill", "noise_blocks",
     "set_option", "get_option", "timing_reset", "timing_collect", "DpfError", "load",
@@ -194,6 +195,72 @@ def linear_clip_accumulate_projected(X, G, P, mask=None, C: float = 1.0, sigma: 
         _stream(X, stream))
     _lib.check(st)
     return grad_out, norms_out
+
+
+def linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks=None, C: float = 1.0,
+                                          sigma: float = 0.0, seed: int = 0, offsets=None,
+                                          grad_outs=None, norms_outs=None, stream=None,
+                                          want_norms: bool = True):
+    """Several independent projected calls (each linear clipped on its own) queued
+    together on the library's streams, so that their launches overlap; each result is
+    bitwise that of linear_clip_accumulate_projected.  Ps are [din_l, r] (one r for
+    all); returns ([grad_out per call], [norms per call]).
+
+    offsets (Philox block offsets, one per call) default to consecutive disjoint ranges
+    from 0: offsets[l] = sum over k < l of noise_blocks(dout_k * r)."""
+    torch = _torch()
+    n = len(Xs)
+    if n < 1 or len(Gs) != n or len(Ps) != n:
+        raise ValueError("Xs, Gs and Ps must be non-empty lists of the same length")
+    dev = Xs[0].device
+    pairs = [_pair(x, g) for x, g in zip(Xs, Gs)]
+    for x, g in zip(Xs, Gs):
+        _same_device(x, dev, "every X")
+        _same_device(g, dev, "every G")
+    r = Ps[0].shape[1] if Ps[0].dim() == 2 else -1
+    for l, (x, P) in enumerate(zip(Xs, Ps)):
+        if P.dim() != 2 or not P.is_contiguous() or P.shape[0] != x.shape[2] or P.dtype != x.dtype \
+                or P.shape[1] != r:
+            raise ValueError(f"Ps[{l}] must be a contiguous [din, r] tensor of X's dtype, "
+                             "with the same r for every call")
+        _same_device(P, dev, f"Ps[{l}]")
+    masks = [None] * n if masks is None else list(masks)
+    if len(masks) != n:
+        raise ValueError(f"masks must have one entry per call ({n}), got {len(masks)}")
+    if offsets is None:
+        offsets = consecutive_offsets([(int(g.shape[2]), int(r)) for g in Gs])
+    offsets = list(offsets)
+    if len(offsets) != n:
+        raise ValueError(f"offsets must have one entry per call ({n}), got {len(offsets)}")
+    if grad_outs is None:
+        grad_outs = [torch.empty((g.shape[2], r), dtype=torch.float32, device=dev) for g in Gs]
+    grad_outs = list(grad_outs)
+    if len(grad_outs) != n:
+        raise ValueError(f"grad_outs must have one tensor per call ({n}), got {len(grad_outs)}")
+    for l, (o, g) in enumerate(zip(grad_outs, Gs)):
+        _check_out(o, (g.shape[2], r), f"grad_outs[{l}]", dev)
+    if norms_outs is None:
+        norms_outs = [torch.empty((x.shape[0],), dtype=torch.float32, device=dev) if want_norms
+                      else None for x in Xs]
+    norms_outs = list(norms_outs)
+    if len(norms_outs) != n:
+        raise ValueError(f"norms_outs must have one entry per call ({n}), got {len(norms_outs)}")
+    for l, (nrm, x) in enumerate(zip(norms_outs, Xs)):
+        if nrm is not None:
+            _check_out(nrm, (x.shape[0],), f"norms_outs[{l}]", dev)
+    acts = (DpfAct * n)(*[a for a, _ in pairs])
+    gacts = (DpfAct * n)(*[b for _, b in pairs])
+    mptrs = (ctypes.c_void_p * n)(*[_mask_ptr(m, x.shape[0], x.shape[1], dev)
+                                    for m, x in zip(masks, Xs)])
+    pptrs = (ctypes.c_void_p * n)(*[P.data_ptr() for P in Ps])
+    offs = (ctypes.c_uint64 * n)(*[int(o) for o in offsets])
+    outs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in grad_outs])
+    nptrs = (ctypes.c_void_p * n)(*[_ptr(nrm) for nrm in norms_outs])
+    st = _lib.lib().dpfused_linear_clip_accumulate_projected_many(
+        n, acts, gacts, mptrs, pptrs, int(r), float(C), float(sigma), int(seed), offs, outs, nptrs,
+        _stream(Xs[0], stream))
+    _lib.check(st)
+    return grad_outs, norms_outs
 
 
 def project(X, P, mask=None, out=None, stream=None):

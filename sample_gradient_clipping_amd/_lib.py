@@ -68,6 +68,11 @@ _SIGNATURES = {
         ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p, ctypes.c_float,
         ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p]),
+    "dpfused_linear_clip_accumulate_projected_many": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct),
+        ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.c_int64,
+        ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
+        ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
     "dpfused_group_clip_accumulate": (ctypes.c_int, [
         ctypes.c_int32, ctypes.POINTER(DpfAct), ctypes.POINTER(DpfAct), ctypes.c_void_p,
         ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),

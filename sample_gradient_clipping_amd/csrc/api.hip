@@ -733,17 +733,24 @@ float projection_scale(float p_scale, int64_t r) {
 }
 
 // Shared body of the projected calls: P read from memory (gen == 0) or
-// regenerated from (p_seed, p_offset, p_scale) inside the projection.
-dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, const void* P,
-                           int gen, uint64_t p_seed, uint64_t p_offset, float p_scale, int64_t r,
-                           float C, float sigma, uint64_t seed, uint64_t offset, float* grad_out,
-                           float* norms_out, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t es = elem_size(X->dtype);
-
-  Workspace ws(s);
-  const size_t off_y = ws.reserve((size_t)X->B * X->T * r * es);
+// regenerated from (p_seed, p_offset, p_scale) inside the projection.  Split
+// into the workspace plan (reserve_projected) and the launches
+// (queue_projected), so that several calls can share one workspace.
+struct ProjectedCall {
   dpf::ProjArgs pa{};
+  bool pvec = false;
+  size_t off_y = 0, off_part = 0, pbytes = 0;
+  dpf_act Y{};
+  LayerPlan L;
+  LayerWs o{};
+};
+
+void reserve_projected(ProjectedCall& pc, const dpf_act* X, const dpf_act* G, const uint8_t* mask,
+                       const void* P, int gen, uint64_t p_seed, uint64_t p_offset, float p_scale,
+                       int64_t r, Workspace& ws) {
+  const size_t es = elem_size(X->dtype);
+  pc.off_y = ws.reserve((size_t)X->B * X->T * r * es);
+  dpf::ProjArgs& pa = pc.pa;
   pa.X = to_act(X);
   pa.P = P;
   pa.dtype = X->dtype;
@@ -756,29 +763,31 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   pa.p_seed = p_seed;
   pa.p_offset = p_offset;
   pa.p_scale = p_scale;
-  const bool pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
-  pa.splits = dpf::project_splits(pa, pvec);
-  const size_t pbytes = dpf::project_workspace_bytes(pa, pvec);
-  const size_t off_part = pbytes != 0 ? ws.reserve(pbytes) : 0;
-  // Reserve the layer workspace now so that a single allocation covers both.
-  dpf_act Y{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
-  LayerPlan L = plan_layer(&Y, G, mask, true);
-  const LayerWs o = reserve_layer(L, ws, true, true, true);
-  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
-  if (L.path == dpf::NormPath::kStaged && !lease.acquire(s, o.staged))
-    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
-  Y.data = ws.at<void>(off_y);
-  pa.Y = const_cast<void*>(Y.data);
-  pa.part = pbytes != 0 ? ws.at<float>(off_part) : nullptr;
-  hipError_t e = dpf::launch_project(pa, pvec, s);
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  pc.pvec = vec_ok(X) && ((size_t)r * es) % 16 == 0;
+  pa.splits = dpf::project_splits(pa, pc.pvec);
+  pc.pbytes = dpf::project_workspace_bytes(pa, pc.pvec);
+  pc.off_part = pc.pbytes != 0 ? ws.reserve(pc.pbytes) : 0;
+  // The layer workspace in the same allocation.
+  pc.Y = dpf_act{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
+  pc.L = plan_layer(&pc.Y, G, mask, true);
+  pc.o = reserve_layer(pc.L, ws, true, true, true);
+}
 
-  L = plan_layer(&Y, G, mask, true);
-  e = bind_layer(L, ws, o, s);
+// The launches of a planned call on stream s (ws allocated; for the staged
+// path, staged holds the per-sample tiles).
+dpf_status queue_projected(ProjectedCall& pc, const dpf_act* G, const uint8_t* mask,
+                           const Workspace& ws, void* staged, float C, float sigma, uint64_t seed,
+                           uint64_t offset, float* grad_out, float* norms_out, hipStream_t s) {
+  pc.Y.data = ws.at<void>(pc.off_y);
+  pc.pa.Y = const_cast<void*>(pc.Y.data);
+  pc.pa.part = pc.pbytes != 0 ? ws.at<float>(pc.off_part) : nullptr;
+  hipError_t e = dpf::launch_project(pc.pa, pc.pvec, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  LayerPlan L = plan_layer(&pc.Y, G, mask, true);
+  e = bind_layer(L, ws, pc.o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
-  if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(lease.ptr());
-  float* c = ws.at<float>(o.c);
+  if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(staged);
+  float* c = ws.at<float>(pc.o.c);
   e = norm_phase(L, nullptr, 0, C, c, norms_out, s);
   if (e != hipSuccess) return hip_fail(e, "norm phase launch");
   L.args.c = c;
@@ -789,6 +798,22 @@ dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* ma
   e = accumulate_phase(L, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   return ok();
+}
+
+dpf_status projected_layer(const dpf_act* X, const dpf_act* G, const uint8_t* mask, const void* P,
+                           int gen, uint64_t p_seed, uint64_t p_offset, float p_scale, int64_t r,
+                           float C, float sigma, uint64_t seed, uint64_t offset, float* grad_out,
+                           float* norms_out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace ws(s);
+  ProjectedCall pc;
+  reserve_projected(pc, X, G, mask, P, gen, p_seed, p_offset, p_scale, r, ws);
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  StagedLease lease;   // the staged path's per-sample tiles, until the combine is queued
+  if (pc.L.path == dpf::NormPath::kStaged && !lease.acquire(s, pc.o.staged))
+    return fail(DPF_ERR_OUT_OF_MEMORY, "staged workspace allocation failed");
+  return queue_projected(pc, G, mask, ws, lease.ptr(), C, sigma, seed, offset, grad_out,
+                         norms_out, s);
 }
 
 // Norm phase of one linear into sq[B] (added when accumulate != 0).
@@ -1019,6 +1044,139 @@ dpf_status dpfused_linear_clip_accumulate_projected(const dpf_act* X, const dpf_
   if (!aligned16(grad_out)) return fail(DPF_ERR_UNSUPPORTED, "grad_out is not 16-byte aligned");
   return projected_layer(X, G, mask, P, 0, 0, 0, 0.0f, r, C, sigma, seed, offset, grad_out,
                          norms_out, stream);
+}
+
+// Streams of the library for the calls that run several linears side by
+// side: per device, created on first use at the default priority and kept
+// until the process ends, with a fork event (recorded on the caller's stream)
+// and one join event per stream.  The lock is held while a call queues its
+// work, so the events' records and the waits on them pair up.
+constexpr int kSideStreams = 4;
+// Library streams a call uses beside the caller's own (0 .. kSideStreams).
+// Measured on the RoBERTa layer (six calls): with one, the host's queueing
+// (about 210 us per layer: each fork and join costs event records and waits)
+// and the GPU's time meet at about 217 us; more streams overlap more on the
+// GPU but cost more on the host (235 us with three, 253 with four); none
+// gives the six calls back to back (281 us).
+std::atomic<int> g_side_streams{1};
+struct SidePool {
+  std::mutex mu;
+  int state = 0;   // 0: not yet created, 1: ready, -1: creation failed
+  hipStream_t s[kSideStreams] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kSideStreams] = {};
+};
+SidePool g_side[kMaxDevices];
+
+// Device dev's pool with its lock taken into lk, or nullptr (then the calls
+// run one after another on the caller's stream).
+SidePool* side_pool(int dev, std::unique_lock<std::mutex>& lk) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SidePool& sp = g_side[dev];
+  lk = std::unique_lock<std::mutex>(sp.mu);
+  if (sp.state == 0) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    for (int k = 0; k < kSideStreams && e == hipSuccess; ++k)
+      e = hipStreamCreateWithFlags(&sp.s[k], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sp.fork, hipEventDisableTiming);
+    for (int k = 0; k < kSideStreams && e == hipSuccess; ++k)
+      e = hipEventCreateWithFlags(&sp.join[k], hipEventDisableTiming);
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) (void)hipGetLastError();
+    sp.state = e == hipSuccess ? 1 : -1;
+  }
+  return sp.state == 1 ? &sp : nullptr;
+}
+
+dpf_status dpfused_linear_clip_accumulate_projected_many(
+    int32_t n, const dpf_act* X, const dpf_act* G, const uint8_t* const* masks,
+    const void* const* P, int64_t r, float C, float sigma, uint64_t seed, const uint64_t* offsets,
+    float* const* grad_out, float* const* norms_out, void* stream) {
+  CallScope call_("dpfused_linear_clip_accumulate_projected_many");
+  if (n < 1 || n > 64) return fail(DPF_ERR_INVALID_ARGUMENT, "n must be in 1 .. 64");
+  if (X == nullptr || G == nullptr || P == nullptr || offsets == nullptr || grad_out == nullptr)
+    return fail(DPF_ERR_INVALID_ARGUMENT, "X, G, P, offsets and grad_out must not be NULL");
+  dpf_status st = check_clip(C, sigma);
+  if (st != DPF_OK) return st;
+  if (r < 1) return fail(DPF_ERR_INVALID_ARGUMENT, "r must be >= 1");
+  if (r > kMaxDim) return fail(DPF_ERR_UNSUPPORTED, "r too large");
+  for (int32_t l = 0; l < n; ++l) {
+    if ((st = check_pair(&X[l], &G[l])) != DPF_OK) return st;
+    if (P[l] == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "P[l] is NULL");
+    if (!aligned16(P[l])) return fail(DPF_ERR_UNSUPPORTED, "P[l] is not 16-byte aligned");
+    if (grad_out[l] == nullptr) return fail(DPF_ERR_INVALID_ARGUMENT, "grad_out[l] is NULL");
+    if (!aligned16(grad_out[l]))
+      return fail(DPF_ERR_UNSUPPORTED, "grad_out[l] is not 16-byte aligned");
+  }
+  // With noise, two calls drawing the same Philox blocks would carry the same
+  // normals, which cancel when their outputs are subtracted.
+  if (sigma > 0.0f) {
+    for (int32_t l = 0; l < n; ++l)
+      for (int32_t m = l + 1; m < n; ++m)
+        if (blocks_overlap(offsets[l], noise_blocks_of(G[l].D * r), offsets[m],
+                           noise_blocks_of(G[m].D * r)))
+          return fail(DPF_ERR_INVALID_ARGUMENT,
+                      "the noise block ranges of two calls overlap (offsets[l] .. offsets[l] + "
+                      "dpfused_noise_blocks(dout_l * r) must be disjoint)");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mask_of = [&](int32_t l) { return masks != nullptr ? masks[l] : nullptr; };
+  auto norms_of = [&](int32_t l) { return norms_out != nullptr ? norms_out[l] : nullptr; };
+  // One workspace for every call, on the caller's stream, taken before the
+  // first launch: a failed allocation leaves every output untouched.
+  Workspace ws(s);
+  std::vector<ProjectedCall> pcs((size_t)n);
+  bool staged = false;
+  for (int32_t l = 0; l < n; ++l) {
+    reserve_projected(pcs[(size_t)l], &X[l], &G[l], mask_of(l), P[l], 0, 0, 0, 0.0f, r, ws);
+    staged = staged || pcs[(size_t)l].L.path == dpf::NormPath::kStaged;
+  }
+  if (staged) {
+    // A forced staged path keeps its tiles in the per-device staged buffer,
+    // which one call holds at a time: the calls run one after another.
+    for (int32_t l = 0; l < n; ++l) {
+      st = projected_layer(&X[l], &G[l], mask_of(l), P[l], 0, 0, 0, 0.0f, r, C, sigma, seed,
+                           offsets[l], grad_out[l], norms_of(l), stream);
+      if (st != DPF_OK) return st;
+    }
+    return ok();
+  }
+  if (!ws.allocate()) return fail(DPF_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+  const int side = std::min(n - 1, g_side_streams.load());
+  std::unique_lock<std::mutex> lk;
+  SidePool* sp = (side > 0 && !stream_capturing(s)) ? side_pool(stream_device(s), lk) : nullptr;
+  if (sp == nullptr) {
+    for (int32_t l = 0; l < n; ++l) {
+      st = queue_projected(pcs[(size_t)l], &G[l], mask_of(l), ws, nullptr, C, sigma, seed,
+                           offsets[l], grad_out[l], norms_of(l), s);
+      if (st != DPF_OK) return st;
+    }
+    return ok();
+  }
+  // Fork: the library's streams start after the caller's earlier work (and
+  // the workspace allocation).  Call l runs on branch l mod (side + 1):
+  // branch 0 is the caller's stream itself, branch k the library's stream k-1.
+  hipError_t e = hipEventRecord(sp->fork, s);
+  for (int k = 0; k < side && e == hipSuccess; ++k) e = hipStreamWaitEvent(sp->s[k], sp->fork, 0);
+  if (e != hipSuccess) return hip_fail(e, "stream fork");
+  st = DPF_OK;
+  for (int32_t l = 0; l < n && st == DPF_OK; ++l) {
+    const int br = l % (side + 1);
+    st = queue_projected(pcs[(size_t)l], &G[l], mask_of(l), ws, nullptr, C, sigma, seed,
+                         offsets[l], grad_out[l], norms_of(l), br == 0 ? s : sp->s[br - 1]);
+  }
+  // Join, also after a failed launch: the caller's stream (and the release
+  // of the workspace on it) waits for whatever was queued.
+  hipError_t ej = hipSuccess;
+  for (int k = 0; k < side; ++k) {
+    if (ej == hipSuccess) ej = hipEventRecord(sp->join[k], sp->s[k]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(s, sp->join[k], 0);
+  }
+  if (st != DPF_OK) return st;
+  if (ej != hipSuccess) return hip_fail(ej, "stream join");
+  return ok();
 }
 
 dpf_status dpfused_linear_clip_accumulate_projected_seeded(
@@ -1401,6 +1559,12 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
     g_call_high.store(0);
     return ok();
   }
+  if (std::strcmp(name, "side_streams") == 0) {
+    if (value < 0 || value > kSideStreams)
+      return fail(DPF_ERR_INVALID_ARGUMENT, "side_streams must be in [0, 4]");
+    g_side_streams.store((int)value);
+    return ok();
+  }
   if (std::strcmp(name, "p_in_kernels") == 0) {
     if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "p_in_kernels must be 0 or 1");
     dpf::set_p_in_kernels(value != 0);
@@ -1431,6 +1595,7 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "workspace_call_bytes") == 0) return t_call_bytes;
   if (std::strcmp(name, "workspace_call_high") == 0) return g_call_high.load();
   if (std::strcmp(name, "p_in_kernels") == 0) return dpf::p_in_kernels() ? 1 : 0;
+  if (std::strcmp(name, "side_streams") == 0) return g_side_streams.load();
   if (std::strcmp(name, "trace") == 0) return g_trace.load();
   if (std::strcmp(name, "debug") == 0) return g_debug.load();
   // Read-only: memory the current device's workspace pool holds now, and the

@@ -138,6 +138,16 @@ int main(void) {
            DPF_ERR_INVALID_ARGUMENT);
     EXPECT(dpfused_group_clip_accumulate(1, xs, gs, NULL, 1.f, 1.f, 0, NULL, outs, NULL, NULL),
            DPF_ERR_INVALID_ARGUMENT);
+    const void* ps[2] = {FAKE, FAKE};
+    EXPECT(dpfused_linear_clip_accumulate_projected_many(0, xs, gs, NULL, ps, 8, 1.f, 1.f, 0, offs,
+                                                         outs, NULL, NULL),
+           DPF_ERR_INVALID_ARGUMENT);
+    EXPECT(dpfused_linear_clip_accumulate_projected_many(2, xs, gs, NULL, NULL, 8, 1.f, 1.f, 0, offs,
+                                                         outs, NULL, NULL),
+           DPF_ERR_INVALID_ARGUMENT);
+    EXPECT(dpfused_linear_clip_accumulate_projected_many(2, xs, gs, NULL, ps, 8, 1.f, 1.f, 0, offs,
+                                                         outs, NULL, NULL),
+           DPF_ERR_INVALID_ARGUMENT);   /* the second G has another T */
   }
   EXPECT(dpfused_projected_adam_step(out, out, out, NULL, 8, 8, 8, 1, 1e-3f, 0.9f, 0.999f, 1e-8f,
                                      NULL, DPF_F32, 0, 0, 0.1f, NULL),

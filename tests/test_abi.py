@@ -93,6 +93,14 @@ def test_options(L):
         assert L.dpfused_set_option(name, 0) == DPF_OK
         assert L.dpfused_get_option(name) == 0
         assert L.dpfused_set_option(name, 2) == DPF_ERR_INVALID_ARGUMENT
+    side = L.dpfused_get_option(b"side_streams")
+    assert side == 1
+    for v in (0, 4):
+        assert L.dpfused_set_option(b"side_streams", v) == DPF_OK
+        assert L.dpfused_get_option(b"side_streams") == v
+    assert L.dpfused_set_option(b"side_streams", 5) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"side_streams", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"side_streams", side) == DPF_OK
     assert L.dpfused_get_option(b"workspace_limit_bytes") == 0
     assert L.dpfused_set_option(b"workspace_limit_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"workspace_limit_bytes", 4096) == DPF_OK
@@ -347,6 +355,39 @@ def test_seeded_projection_rejects_noise_drawn_from_its_blocks(L):
     assert call(0, 0, 0, 0) == DPF_ERR_INVALID_ARGUMENT      # the all-default seeds
     # the range wraps modulo 2^64
     assert call(7, 2 ** 64 - 4, 7, 10) == DPF_ERR_INVALID_ARGUMENT
+
+
+def test_projected_many_argument_checks(L):
+    n = 2
+    Xs = (DpfAct * n)(_act(), _act(D=16))
+    Gs = (DpfAct * n)(_act(D=16), _act(D=8))
+    Ps = (ctypes.c_void_p * n)(FAKE, FAKE)
+    offs = (ctypes.c_uint64 * n)(0, 64)
+    outs = (ctypes.c_void_p * n)(FAKE, FAKE)
+    f = L.dpfused_linear_clip_accumulate_projected_many
+    assert f(0, Xs, Gs, None, Ps, 8, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(65, Xs, Gs, None, Ps, 8, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, None, Gs, None, Ps, 8, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, None, 8, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, Ps, 8, 1.0, 1.0, 0, None, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, Ps, 0, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    assert f(n, Xs, Gs, None, Ps, 8, -1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_INVALID_ARGUMENT
+    bad_g = (DpfAct * n)(_act(D=16), _act(T=5, D=8))
+    assert f(n, Xs, bad_g, None, Ps, 8, 1.0, 1.0, 0, offs, outs, None, None) == \
+        DPF_ERR_INVALID_ARGUMENT
+    null_p = (ctypes.c_void_p * n)(FAKE, None)
+    assert f(n, Xs, Gs, None, null_p, 8, 1.0, 1.0, 0, offs, outs, None, None) == \
+        DPF_ERR_INVALID_ARGUMENT
+    odd_p = (ctypes.c_void_p * n)(FAKE, FAKE + 4)
+    assert f(n, Xs, Gs, None, odd_p, 8, 1.0, 1.0, 0, offs, outs, None, None) == DPF_ERR_UNSUPPORTED
+    bad_out = (ctypes.c_void_p * n)(FAKE, FAKE + 4)
+    assert f(n, Xs, Gs, None, Ps, 8, 1.0, 1.0, 0, offs, bad_out, None, None) == DPF_ERR_UNSUPPORTED
+    # noise ranges: dout * r = 16 * 8 and 8 * 8 elements: 32 and 16 blocks
+    for bad in ([0, 0], [0, 31], [10, 0]):
+        o = (ctypes.c_uint64 * n)(*bad)
+        assert f(n, Xs, Gs, None, Ps, 8, 1.0, 0.5, 0, o, outs, None, None) == \
+            DPF_ERR_INVALID_ARGUMENT, bad
+        assert b"overlap" in L.dpfused_last_error()
 
 
 def test_group_rejects_overlapping_noise_ranges(L):

@@ -163,3 +163,39 @@ def test_projected_call_uses_the_same_projection():
     o2, n2 = dp.linear_clip_accumulate(Xd[:, :, :r].contiguous(), Gd, None, C=0.05, sigma=0.0)
     torch.cuda.synchronize()
     assert torch.equal(n1, n2) and torch.equal(o1, o2)
+
+
+def test_projected_many_equals_the_single_calls():
+    """The six linears of a RoBERTa-large layer (B = 8) queued together on the
+    library's streams: every output and norm equals the single projected call
+    bit for bit (the same kernels on the same inputs), with masks on some of
+    the linears and noise from consecutive offsets; two calls in a row agree."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(34)
+    B, T, r = 8, 128, 256
+    shapes = [(1024, 1024)] * 4 + [(1024, 4096), (4096, 1024)]
+    Pd = {d: to_dev(_inputs(rng, 1, 1, d, r, "bf16")[1], "bf16", torch) for d in (1024, 4096)}
+    Xs, Gs, Ps, masks = [], [], [], []
+    for l, (din, dout) in enumerate(shapes):
+        X, _ = _inputs(rng, B, T, din, r, "bf16")
+        G = workloads.f32_to_bf16_bits(rng.standard_normal((B, T, dout), dtype=np.float32) * 1e-2)
+        Xs.append(to_dev(X, "bf16", torch))
+        Gs.append(to_dev(G, "bf16", torch))
+        Ps.append(Pd[din])
+        lengths = rng.integers(1, T + 1, B)
+        lengths[0] = 0
+        m = (np.arange(T)[None, :] < lengths[:, None]).astype(np.uint8)
+        masks.append(None if l % 2 == 0 else mask_dev(m, torch))
+    offsets = dp.consecutive_offsets([(int(g.shape[2]), r) for g in Gs])
+    outs, norms = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05, sigma=0.7,
+                                                           seed=5, offsets=offsets)
+    outs2, norms2 = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05, sigma=0.7,
+                                                             seed=5, offsets=offsets)
+    torch.cuda.synchronize()
+    for l in range(len(shapes)):
+        o1, n1 = dp.linear_clip_accumulate_projected(Xs[l], Gs[l], Ps[l], masks[l], C=0.05,
+                                                     sigma=0.7, seed=5, offset=offsets[l])
+        torch.cuda.synchronize()
+        assert torch.equal(outs[l], o1) and torch.equal(norms[l], n1), l
+        assert torch.equal(outs2[l], o1) and torch.equal(norms2[l], n1), l
