@@ -14,7 +14,9 @@ and r not multiples of the 64-wide tile), a strided view, masks with an
 empty sample, r = 8 and a single token; fp32 inputs take the generic tiles.
 Also: bitwise repeatability, and the projected call's own Y equals this one
 (the projected sum with P = I on the first r features equals the dense sum
-over those features).
+over those features).  The multi-linear projected call equals the single
+calls bit for bit for every number of library streams and with the staged
+fallback, and its graph replays equal its eager result.
 """
 import numpy as np
 import pytest
@@ -165,14 +167,10 @@ def test_projected_call_uses_the_same_projection():
     assert torch.equal(n1, n2) and torch.equal(o1, o2)
 
 
-def test_projected_many_equals_the_single_calls():
-    """The six linears of a RoBERTa-large layer (B = 8) queued together on the
-    library's streams: every output and norm equals the single projected call
-    bit for bit (the same kernels on the same inputs), with masks on some of
-    the linears and noise from consecutive offsets; two calls in a row agree."""
-    torch = need_gpu()
-    import sample_gradient_clipping_amd as dp
-    rng = np.random.default_rng(34)
+def _many_case(torch, dp, seed):
+    """Six RoBERTa-large linears (B = 8, r = 256), masks on every other one
+    (sample 0 empty), with their consecutive noise offsets."""
+    rng = np.random.default_rng(seed)
     B, T, r = 8, 128, 256
     shapes = [(1024, 1024)] * 4 + [(1024, 4096), (4096, 1024)]
     Pd = {d: to_dev(_inputs(rng, 1, 1, d, r, "bf16")[1], "bf16", torch) for d in (1024, 4096)}
@@ -188,14 +186,73 @@ def test_projected_many_equals_the_single_calls():
         m = (np.arange(T)[None, :] < lengths[:, None]).astype(np.uint8)
         masks.append(None if l % 2 == 0 else mask_dev(m, torch))
     offsets = dp.consecutive_offsets([(int(g.shape[2]), r) for g in Gs])
-    outs, norms = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05, sigma=0.7,
-                                                           seed=5, offsets=offsets)
-    outs2, norms2 = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05, sigma=0.7,
-                                                             seed=5, offsets=offsets)
-    torch.cuda.synchronize()
-    for l in range(len(shapes)):
-        o1, n1 = dp.linear_clip_accumulate_projected(Xs[l], Gs[l], Ps[l], masks[l], C=0.05,
-                                                     sigma=0.7, seed=5, offset=offsets[l])
+    return Xs, Gs, Ps, masks, offsets
+
+
+@pytest.mark.parametrize("side,path", [(1, 0), (0, 0), (2, 0), (4, 0), (1, 3)])
+def test_projected_many_equals_the_single_calls(side, path):
+    """The six linears of a RoBERTa-large layer (B = 8) queued together: on the
+    caller's stream alone (side 0), spread over one, two or four library
+    streams, and with the staged norm path asked for (the calls then run one
+    after another).  Every output and norm equals the single projected call
+    bit for bit (the same kernels on the same inputs), with masks on some of
+    the linears and noise from consecutive offsets; two calls in a row agree."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    Xs, Gs, Ps, masks, offsets = _many_case(torch, dp, 34)
+    old_side = dp.get_option("side_streams")
+    dp.set_option("side_streams", side)
+    dp.set_option("norm_path", path)
+    try:
+        outs, norms = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05,
+                                                               sigma=0.7, seed=5, offsets=offsets)
+        outs2, norms2 = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, C=0.05,
+                                                                 sigma=0.7, seed=5,
+                                                                 offsets=offsets)
         torch.cuda.synchronize()
-        assert torch.equal(outs[l], o1) and torch.equal(norms[l], n1), l
-        assert torch.equal(outs2[l], o1) and torch.equal(norms2[l], n1), l
+        for l in range(len(Xs)):
+            o1, n1 = dp.linear_clip_accumulate_projected(Xs[l], Gs[l], Ps[l], masks[l], C=0.05,
+                                                         sigma=0.7, seed=5, offset=offsets[l])
+            torch.cuda.synchronize()
+            assert torch.equal(outs[l], o1) and torch.equal(norms[l], n1), l
+            assert torch.equal(outs2[l], o1) and torch.equal(norms2[l], n1), l
+    finally:
+        dp.set_option("side_streams", old_side)
+        dp.set_option("norm_path", 0)
+
+
+def test_projected_many_graph_replays_match_eager():
+    """The multi-linear call captured into a HIP graph (the calls then run one
+    after another on the capturing stream, in graph-owned workspace) and
+    replayed three times, with eager calls on the same data in between: every
+    replay's outputs and norms equal the eager call's bit for bit."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    Xs, Gs, Ps, masks, offsets = _many_case(torch, dp, 35)
+    kw = dict(C=0.05, sigma=0.7, seed=6, offsets=offsets)
+    ref, ref_n = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, **kw)
+    outs = [torch.empty_like(o) for o in ref]
+    norms = [torch.empty_like(n) for n in ref_n]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, grad_outs=outs,
+                                                     norms_outs=norms, **kw)
+    torch.cuda.synchronize()
+    for it in range(3):
+        for o, n in zip(outs, norms):
+            o.fill_(float(it) - 5.0)
+            n.fill_(-1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(len(Xs)):
+            assert torch.equal(outs[l], ref[l]) and torch.equal(norms[l], ref_n[l]), (it, l)
+        eager, eager_n = dp.linear_clip_accumulate_projected_many(Xs, Gs, Ps, masks, **kw)
+        torch.cuda.synchronize()
+        for l in range(len(Xs)):
+            assert torch.equal(eager[l], ref[l]) and torch.equal(eager_n[l], ref_n[l]), (it, l)
+    del graph
+    torch.cuda.synchronize()
