@@ -486,6 +486,14 @@ uint64_t dpfused_noise_blocks(int64_t n_elements);
  *                dpfused_linear_clip_accumulate_projected_many spreads its
  *                calls over beside the caller's stream (default 1; 0 = all
  *                on the caller's stream).  Results are identical.
+ *   "rspace_tiles"  projected calls: the r-space sum G~^T Y ([dout, r],
+ *                a few tiles over B*T tokens) accumulated on 128 x 128 tiles
+ *                whose samples are cut into pieces spread over the compute
+ *                units, the pieces' fp32 parts added in a fixed order by a
+ *                second kernel (1, the default); that and the direct norm
+ *                on the same tiles (2); the 256 x 256 tiles (0).  Results
+ *                agree within rounding (a different summation order), and
+ *                each setting is deterministic.
  *   "trace"      1 = push a roctx range named after the entry point around
  *                every call, for rocprofv3 --marker-trace; 0 = off (default)
  *   "debug"      1 = synchronise the launch stream after every kernel and

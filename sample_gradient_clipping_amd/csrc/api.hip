@@ -736,8 +736,23 @@ float projection_scale(float p_scale, int64_t r) {
 // regenerated from (p_seed, p_offset, p_scale) inside the projection.  Split
 // into the workspace plan (reserve_projected) and the launches
 // (queue_projected), so that several calls can share one workspace.
+// The r-space sum G~^T Y of a projected call is a [dout, r] output of a few
+// tiles over B*T tokens: with "rspace_tiles" 1 (the default) its
+// accumulation runs on 128 x 128 tiles whose samples are cut into pieces
+// over the compute units, 2 adds the direct norm on those tiles, 0 keeps the
+// large tiles.  Measured on MI355X (RoBERTa-large, r = 256, B = 32, T = 128).
+std::atomic<int> g_rspace_tiles{1};
+
+LayerPlan plan_rspace(const dpf_act* Y, const dpf_act* G, const uint8_t* mask, int small) {
+  LayerPlan L = plan_layer(Y, G, mask, true);
+  L.args.small_tiles = small;
+  L.np = dpf::norm_partials_per_sample(L.args, L.path, L.vec);
+  return L;
+}
+
 struct ProjectedCall {
   dpf::ProjArgs pa{};
+  int small = 0;   // rspace_tiles when the call was planned
   bool pvec = false;
   size_t off_y = 0, off_part = 0, pbytes = 0;
   dpf_act Y{};
@@ -769,7 +784,8 @@ void reserve_projected(ProjectedCall& pc, const dpf_act* X, const dpf_act* G, co
   pc.off_part = pc.pbytes != 0 ? ws.reserve(pc.pbytes) : 0;
   // The layer workspace in the same allocation.
   pc.Y = dpf_act{nullptr, X->dtype, 0, X->B, X->T, r, X->T * r, r};
-  pc.L = plan_layer(&pc.Y, G, mask, true);
+  pc.small = g_rspace_tiles.load();
+  pc.L = plan_rspace(&pc.Y, G, mask, pc.small);
   pc.o = reserve_layer(pc.L, ws, true, true, true);
 }
 
@@ -783,7 +799,7 @@ dpf_status queue_projected(ProjectedCall& pc, const dpf_act* G, const uint8_t* m
   pc.pa.part = pc.pbytes != 0 ? ws.at<float>(pc.off_part) : nullptr;
   hipError_t e = dpf::launch_project(pc.pa, pc.pvec, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
-  LayerPlan L = plan_layer(&pc.Y, G, mask, true);
+  LayerPlan L = plan_rspace(&pc.Y, G, mask, pc.small);
   e = bind_layer(L, ws, pc.o, s);
   if (e != hipSuccess) return hip_fail(e, "mask preparation launch");
   if (L.path == dpf::NormPath::kStaged) L.args.skws = static_cast<float*>(staged);
@@ -1565,6 +1581,11 @@ dpf_status dpfused_set_option(const char* name, int64_t value) {
     g_side_streams.store((int)value);
     return ok();
   }
+  if (std::strcmp(name, "rspace_tiles") == 0) {
+    if (value < 0 || value > 2) return fail(DPF_ERR_INVALID_ARGUMENT, "rspace_tiles must be 0, 1 or 2");
+    g_rspace_tiles.store((int)value);
+    return ok();
+  }
   if (std::strcmp(name, "p_in_kernels") == 0) {
     if (value != 0 && value != 1) return fail(DPF_ERR_INVALID_ARGUMENT, "p_in_kernels must be 0 or 1");
     dpf::set_p_in_kernels(value != 0);
@@ -1596,6 +1617,7 @@ int64_t dpfused_get_option(const char* name) {
   if (std::strcmp(name, "workspace_call_high") == 0) return g_call_high.load();
   if (std::strcmp(name, "p_in_kernels") == 0) return dpf::p_in_kernels() ? 1 : 0;
   if (std::strcmp(name, "side_streams") == 0) return g_side_streams.load();
+  if (std::strcmp(name, "rspace_tiles") == 0) return g_rspace_tiles.load();
   if (std::strcmp(name, "trace") == 0) return g_trace.load();
   if (std::strcmp(name, "debug") == 0) return g_debug.load();
   // Read-only: memory the current device's workspace pool holds now, and the

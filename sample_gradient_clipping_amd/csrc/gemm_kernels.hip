@@ -247,6 +247,103 @@ __global__ void __launch_bounds__(kNT) accumulate_kernel(LayerArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Few-tile accumulation: outputs of a few 128 x 128 tiles over many tokens
+// (the projected variant's r-space sum G~^T Y, [dout, r]: 16 to 64 tiles at
+// r = 256).  One workgroup per tile and none else would leave most compute
+// units idle, and the large tiles are fewer still; so the samples of each
+// tile are cut into P consecutive pieces [b0, b1), one workgroup each.  Piece
+// q stores its part of the sum, acc * c_last = sum over its samples of
+// c_i g_i (the clip factors already applied), as a 128 x 128 fp32 tile
+// [o - o0][a - a0] at part + (q * ntiles + tile) * 16384; a piece without an
+// active token stores zeros.  accumulate_pieces_fixup_kernel then adds the P
+// parts of every output in piece order, the noise and 1/denom.
+constexpr int kPieceFloats = kTileM * kTileN;
+
+template <class E, bool VEC>
+__global__ void __launch_bounds__(kNT) accumulate_pieces_kernel(LayerArgs p, int P, float* part) {
+  using KG = KOuterGemm<E, VEC>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto* lds = (typename E::storage*)smem;
+  const int ntm = (p.din + kTileM - 1) / kTileM;
+  const int ntiles = ntm * ((p.dout + kTileN - 1) / kTileN);
+  const int tile = (int)(blockIdx.x % (unsigned)ntiles), q = (int)(blockIdx.x / (unsigned)ntiles);
+  const int a0 = (tile % ntm) * kTileM;
+  const int o0 = (tile / ntm) * kTileN;
+  const int b0 = (int)((int64_t)q * p.B / P), b1 = (int)((int64_t)(q + 1) * p.B / P);
+  KG g;
+  float c_last;
+  kouter_run<E, VEC, false>(p, b0, b1, a0, o0, g, lds, &c_last);
+  float* dst = part + ((int64_t)q * ntiles + tile) * kPieceFloats;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / kWN, wn = wave % kWN;
+#pragma unroll
+  for (int i = 0; i < kBM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      const int ol = (wn * kBN + j) * 32 + acc_col(lane);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int al = (wm * kBM + i) * 32 + acc_row(4 * qq, lane);   // 4 consecutive a
+        f32x4 v;
+        v.x = g.acc[i][j][4 * qq + 0] * c_last;
+        v.y = g.acc[i][j][4 * qq + 1] * c_last;
+        v.z = g.acc[i][j][4 * qq + 2] * c_last;
+        v.w = g.acc[i][j][4 * qq + 3] * c_last;
+        *(f32x4*)(dst + ol * kTileM + al) = v;
+      }
+    }
+  }
+}
+
+// One thread per 4 consecutive outputs (o, a .. a+3) of the [dout, din]
+// result (din a multiple of 4): the P parts summed in piece order, then the
+// noise (one Philox block), 1/denom and the prior value when beta.  Each
+// thread keeps the loads of up to kPieceBatch parts in flight (indices past
+// P clamped to the last part, their values dropped).
+constexpr int kPieceFixThreads = 256;
+constexpr int kPieceBatch = 8;
+__global__ void __launch_bounds__(kPieceFixThreads) accumulate_pieces_fixup_kernel(LayerArgs p,
+                                                                                   int P,
+                                                                                   const float* part) {
+  const int nq = p.din >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * kPieceFixThreads + threadIdx.x;
+  if (idx >= (int64_t)p.dout * nq) return;
+  const int o = (int)(idx / nq), a = (int)(idx % nq) * 4;
+  const int ntm = (p.din + kTileM - 1) / kTileM;
+  const int ntiles = ntm * ((p.dout + kTileN - 1) / kTileN);
+  const int tile = (o / kTileN) * ntm + a / kTileM;
+  const float* src = part + (int64_t)tile * kPieceFloats + (o % kTileN) * kTileM + (a % kTileM);
+  const int64_t stride = (int64_t)ntiles * kPieceFloats;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int c0 = 0; c0 < P; c0 += kPieceBatch) {
+    f32x4 w[kPieceBatch];
+#pragma unroll
+    for (int j = 0; j < kPieceBatch; ++j)
+      w[j] = *(const f32x4*)(src + (int64_t)min(c0 + j, P - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < kPieceBatch; ++j) {
+      if (c0 + j < P) {
+        v.x += w[j].x; v.y += w[j].y; v.z += w[j].z; v.w += w[j].w;
+      }
+    }
+  }
+  const float rB = 1.0f / p.denom;   // exact for a power of two, else within one ulp
+  const uint64_t e0 = (uint64_t)o * (uint64_t)p.din + (uint64_t)a;
+  if (p.noise_std != 0.0f) {
+    const f32x4 z = normals_of_block(philox_block(p.seed, p.offset + (e0 >> 2)));
+    v.x += p.noise_std * z.x; v.y += p.noise_std * z.y;
+    v.z += p.noise_std * z.z; v.w += p.noise_std * z.w;
+  }
+  v.x *= rB; v.y *= rB; v.z *= rB; v.w *= rB;
+  if (p.beta) {
+    const f32x4 old = *(const f32x4*)(p.out + e0);
+    v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+  }
+  *(f32x4*)(p.out + e0) = v;
+}
+
+// ---------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ void __launch_bounds__(kNT) direct_norm_kernel(LayerArgs p) {
   using KG = KOuterGemm<E, VEC>;
@@ -564,6 +661,42 @@ hipError_t launch_accumulate_t(const LayerArgs& p, hipStream_t s) {
   timing_end("accumulate", s);
   return e;
 }
+// Pieces per tile of the few-tile accumulation: enough for every compute
+// unit to take one, at most one per sample and at most kMaxPieces.
+constexpr int kMaxPieces = 32;
+int small_tile_count(const LayerArgs& p) {
+  return ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
+}
+int pieces_per_tile(const LayerArgs& p) {
+  const int P = std::max(1, device_cus() / small_tile_count(p));
+  return std::min(P, std::min(p.B, kMaxPieces));
+}
+
+template <class E, bool VEC>
+hipError_t launch_pieces_t(const LayerArgs& p, hipStream_t s) {
+  using KG = KOuterGemm<E, VEC>;
+  const int P = pieces_per_tile(p);
+  if (P == 1) return launch_accumulate_t<E, VEC>(p, s);
+  if (p.skws == nullptr || (p.din & 3) != 0) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)small_tile_count(p) * P;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipError_t e = allow_lds<accumulate_pieces_kernel<E, VEC>>(KG::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  timing_begin("accumulate", s);
+  hipLaunchKernelGGL((accumulate_pieces_kernel<E, VEC>), dim3((unsigned)grid), dim3(kNT),
+                     KG::LDS_BYTES, s, p, P, p.skws);
+  e = hipGetLastError();
+  timing_end("accumulate", s);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)p.dout * (p.din >> 2);
+  timing_begin("accumulate_fixup", s);
+  hipLaunchKernelGGL(accumulate_pieces_fixup_kernel,
+                     dim3((unsigned)((n + kPieceFixThreads - 1) / kPieceFixThreads)),
+                     dim3(kPieceFixThreads), 0, s, p, P, (const float*)p.skws);
+  e = hipGetLastError();
+  timing_end("accumulate_fixup", s);
+  return e;
+}
 template <class E, bool VEC>
 hipError_t launch_direct_t(const LayerArgs& p, hipStream_t s) {
   using KG = KOuterGemm<E, VEC>;
@@ -631,7 +764,23 @@ static bool use_big(const LayerArgs& p, bool vec) {
 
 bool big_path(const LayerArgs& p, bool vec) { return use_big(p, vec); }
 
+// The few-tile kernels (128 x 128 tiles, samples cut into pieces) for a call
+// that asks for them (small_tiles) and has at most half as many of those
+// tiles as compute units; 16-byte rows (din a multiple of 4, 8 for bf16).
+static bool use_pieces(const LayerArgs& p, bool vec) {
+  return p.small_tiles != 0 && vec && (p.din & 3) == 0 &&
+         2 * (int64_t)small_tile_count(p) <= (int64_t)device_cus();
+}
+// ... and, with small_tiles == 2, the direct norm over the same tiles.
+static bool small_norm(const LayerArgs& p, bool vec) {
+  return p.small_tiles == 2 && use_pieces(p, vec);
+}
+
 size_t accumulate_workspace_bytes(const LayerArgs& p, bool vec) {
+  if (use_pieces(p, vec)) {
+    const int P = pieces_per_tile(p);
+    return P == 1 ? 0 : (size_t)P * small_tile_count(p) * kPieceFloats * sizeof(float);
+  }
   return use_big(p, vec) ? accumulate_big_workspace_bytes(p) : 0;
 }
 
@@ -649,11 +798,13 @@ int norm_partials_per_sample(const LayerArgs& p, NormPath path, bool vec) {
     return nt * (nt + 1) / 2;
   }
   if (path == NormPath::kStaged && use_big(p, vec)) return staged_big_partials_per_sample(p);
-  if (use_big(p, vec)) return direct_big_partials_per_sample(p);
+  if (use_big(p, vec) && !small_norm(p, vec)) return direct_big_partials_per_sample(p);
   return ((p.din + kTileM - 1) / kTileM) * ((p.dout + kTileN - 1) / kTileN);
 }
 
 hipError_t launch_accumulate(const LayerArgs& p, bool vec, hipStream_t s) {
+  if (use_pieces(p, vec))
+    return p.dtype == kBF16 ? launch_pieces_t<BF16, true>(p, s) : launch_pieces_t<F32, true>(p, s);
   if (use_big(p, vec)) return launch_accumulate_big(p, s);
   if (p.dtype == kBF16) return vec ? launch_accumulate_t<BF16, true>(p, s) : launch_accumulate_t<BF16, false>(p, s);
   return vec ? launch_accumulate_t<F32, true>(p, s) : launch_accumulate_t<F32, false>(p, s);
@@ -671,7 +822,7 @@ hipError_t launch_norm(const LayerArgs& p, NormPath path, bool vec, hipStream_t 
     if (p.dtype == kBF16) return vec ? launch_gram_t<BF16, true>(p, s) : launch_gram_t<BF16, false>(p, s);
     return vec ? launch_gram_t<F32, true>(p, s) : launch_gram_t<F32, false>(p, s);
   }
-  if (use_big(p, vec)) return launch_direct_norm_big(p, s);
+  if (use_big(p, vec) && !small_norm(p, vec)) return launch_direct_norm_big(p, s);
   if (p.dtype == kBF16) return vec ? launch_direct_t<BF16, true>(p, s) : launch_direct_t<BF16, false>(p, s);
   return vec ? launch_direct_t<F32, true>(p, s) : launch_direct_t<F32, false>(p, s);
 }

@@ -39,6 +39,10 @@ struct LayerArgs {
   float* skws;              // partials of split tiles / items (large-tile kernels), or null
   int max_split;            // 1: never split a tile or Gram item (no split partials in
                             // skws); 0: as the cost model picks
+  int small_tiles;          // few-tile outputs (the projected variant's r-space sums):
+                            // 1 accumulate over 128 x 128 tiles whose samples are cut
+                            // into pieces (partials in skws); 2 also the direct norm
+                            // over 128 x 128 tiles; 0 the large tiles
 };
 
 // Active-step list of a masked call, built from the row bits:

@@ -101,6 +101,14 @@ def test_options(L):
     assert L.dpfused_set_option(b"side_streams", 5) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"side_streams", -1) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"side_streams", side) == DPF_OK
+    tiles = L.dpfused_get_option(b"rspace_tiles")
+    assert tiles == 1
+    for v in (0, 2):
+        assert L.dpfused_set_option(b"rspace_tiles", v) == DPF_OK
+        assert L.dpfused_get_option(b"rspace_tiles") == v
+    assert L.dpfused_set_option(b"rspace_tiles", 3) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"rspace_tiles", -1) == DPF_ERR_INVALID_ARGUMENT
+    assert L.dpfused_set_option(b"rspace_tiles", tiles) == DPF_OK
     assert L.dpfused_get_option(b"workspace_limit_bytes") == 0
     assert L.dpfused_set_option(b"workspace_limit_bytes", -1) == DPF_ERR_INVALID_ARGUMENT
     assert L.dpfused_set_option(b"workspace_limit_bytes", 4096) == DPF_OK

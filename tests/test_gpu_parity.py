@@ -376,3 +376,91 @@ def test_projected_split_along_din(dtype, shape):
     assert max_rel(norms.cpu().numpy(), rn) <= (NORM_TOL if dtype == "f32" else 5e-3)
     assert rel_fro(out.cpu().numpy(), ref) <= (AGG_TOL_F32 * 10 if dtype == "f32" else 1e-2)
     assert_elementwise(out.cpu().numpy(), ref, PROJ_ELEM_TOL[dtype], f"projected split {dtype}")
+
+
+def _projected_case(rng, dtype, B, T, din, dout, r, lengths):
+    lin = random_linear(rng, B, T, din, dout, dtype=dtype, lengths=lengths)
+    Pf = (rng.standard_normal((din, r)) / np.sqrt(r)).astype(np.float32)
+    P = workloads.f32_to_bf16_bits(Pf) if dtype == "bf16" else Pf
+    return lin, P
+
+
+@pytest.mark.parametrize("tiles", [0, 1, 2])
+@pytest.mark.parametrize("dtype,B,T,din,dout,r,lengths", [
+    # 3 tiles of 128 x 128 in r space, one sample per piece, an empty sample
+    ("bf16", 5, 150, 136, 296, 72, [150, 20, 0, 77, 150]),
+    # 15 tiles with ragged tails in r and dout, 7 pieces of one sample
+    ("bf16", 7, 96, 64, 520, 264, None),
+    # fp32, 2 tiles, 6 pieces, samples of 1 and 0 tokens
+    ("f32", 6, 70, 40, 200, 40, [70, 1, 35, 0, 70, 12]),
+])
+def test_projected_rspace_tiles(tiles, dtype, B, T, din, dout, r, lengths):
+    """The r-space sum of the projected call on each "rspace_tiles" setting
+    (0: 256 x 256 tiles; 1: 128 x 128 tiles whose samples are cut into
+    pieces, their parts added in order by a second kernel; 2: that and the
+    direct norm on 128 x 128 tiles) against the oracle: the norms, the
+    clipped sum element by element (mixed clipping, C at the median norm) and
+    the noise; each setting bitwise repeatable."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    rng = np.random.default_rng(70 + B)
+    lin, P = _projected_case(rng, dtype, B, T, din, dout, r, lengths)
+    _, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, lin.mask, P, 1.0, 0.0, 0, 0, dtype)
+    C = float(np.median(rn[rn > 0]))
+    X, G = to_dev(lin.X, dtype, torch), to_dev(lin.G, dtype, torch)
+    Pd, m = to_dev(P, dtype, torch), mask_dev(lin.mask, torch)
+    old = dp.get_option("rspace_tiles")
+    dp.set_option("rspace_tiles", tiles)
+    try:
+        outs = {}
+        for sigma in (0.0, 0.9):
+            out, norms = dp.linear_clip_accumulate_projected(X, G, Pd, m, C=C, sigma=sigma,
+                                                             seed=3, offset=5)
+            again, _ = dp.linear_clip_accumulate_projected(X, G, Pd, m, C=C, sigma=sigma,
+                                                           seed=3, offset=5)
+            torch.cuda.synchronize()
+            assert torch.equal(out, again), "not bitwise repeatable"
+            outs[sigma] = out.cpu().numpy()
+            nrm = norms.cpu().numpy()
+        ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, lin.mask, P, C, 0.0, 3, 5, dtype)
+        tol_n = NORM_TOL if dtype == "f32" else 5e-3
+        live = rn > 0
+        assert max_rel(nrm[live], rn[live]) <= tol_n
+        assert (nrm[~live] == 0.0).all()
+        assert_elementwise(outs[0.0], ref, PROJ_ELEM_TOL[dtype], f"rspace_tiles {tiles} sigma = 0")
+        assert_noise(outs[0.9], outs[0.0], 0.9, C, 3, 5, B, f"rspace_tiles {tiles} noise")
+    finally:
+        dp.set_option("rspace_tiles", old)
+
+
+@pytest.mark.parametrize("tiles", [0, 2])
+@pytest.mark.parametrize("index", [0, 4])
+def test_config_roberta_projected_rspace_tiles(index, tiles):
+    """The RoBERTa-large projected linears q (1024 -> 1024) and fc1 (1024 ->
+    4096) on the other "rspace_tiles" settings (the default, 1, is the
+    projected configuration test above) against the oracle."""
+    torch = need_gpu()
+    import sample_gradient_clipping_amd as dp
+    from oracle import philox
+    lin = workloads.config_c5_linear(index)
+    r = 256
+    P = workloads.f32_to_bf16_bits((philox.gaussian(7, 0, lin.din * r) / 16.0)
+                                   .astype(np.float32)).reshape(lin.din, r)
+    X, G = to_dev(lin.X, "bf16", torch), to_dev(lin.G, "bf16", torch)
+    Pd = to_dev(P, "bf16", torch)
+    old = dp.get_option("rspace_tiles")
+    dp.set_option("rspace_tiles", tiles)
+    try:
+        outs = {}
+        for sigma in (lin.sigma, 0.0):
+            out, norms = dp.linear_clip_accumulate_projected(X, G, Pd, None, C=lin.C, sigma=sigma)
+            torch.cuda.synchronize()
+            outs[sigma] = out.cpu().numpy()
+            nrm = norms.cpu().numpy()
+    finally:
+        dp.set_option("rspace_tiles", old)
+    ref, rn, _ = dp_linear.oracle_projected(lin.X, lin.G, None, P, lin.C, 0.0, 0, 0, "bf16")
+    assert max_rel(nrm, rn) <= NORM_TOL
+    assert_elementwise(outs[0.0], ref, PROJ_ELEM_TOL["bf16"], f"rspace_tiles {tiles} sigma = 0")
+    assert_noise(outs[lin.sigma], outs[0.0], lin.sigma, lin.C, 0, 0, lin.B,
+                 f"rspace_tiles {tiles} noise")
