@@ -765,11 +765,21 @@ static bool use_big(const LayerArgs& p, bool vec) {
 bool big_path(const LayerArgs& p, bool vec) { return use_big(p, vec); }
 
 // The few-tile kernels (128 x 128 tiles, samples cut into pieces) for a call
-// that asks for them (small_tiles) and has at most half as many of those
-// tiles as compute units; 16-byte rows (din a multiple of 4, 8 for bf16).
+// that asks for them (small_tiles), with 16-byte rows (din a multiple of 4,
+// 8 for bf16) and at most half as many of those tiles as compute units.
+// Where the large tiles could run the call instead (bf16), only if the
+// pieces keep at least half of the compute units busy and each piece stays
+// short (at most 32 of the generic loop's steps): the large-tile loop is the
+// faster one per step, and splits a long token range of few samples itself.
 static bool use_pieces(const LayerArgs& p, bool vec) {
-  return p.small_tiles != 0 && vec && (p.din & 3) == 0 &&
-         2 * (int64_t)small_tile_count(p) <= (int64_t)device_cus();
+  if (p.small_tiles == 0 || !vec || (p.din & 3) != 0) return false;
+  const int64_t cus = device_cus(), nt = small_tile_count(p);
+  if (2 * nt > cus) return false;
+  if (!use_big(p, vec)) return true;
+  const int P = pieces_per_tile(p);
+  const int kt = p.dtype == kBF16 ? Cfg<BF16>::KT : Cfg<F32>::KT;
+  const int64_t steps = (int64_t)((p.B + P - 1) / P) * ((p.T + kt - 1) / kt);
+  return 2 * nt * P >= cus && steps <= 32;
 }
 // ... and, with small_tiles == 2, the direct norm over the same tiles.
 static bool small_norm(const LayerArgs& p, bool vec) {

@@ -385,12 +385,17 @@ def _projected_case(rng, dtype, B, T, din, dout, r, lengths):
     return lin, P
 
 
+_LEN32 = [50, 0, 1, 49, 50, 7, 50, 33] * 4
+
+
 @pytest.mark.parametrize("tiles", [0, 1, 2])
 @pytest.mark.parametrize("dtype,B,T,din,dout,r,lengths", [
-    # 3 tiles of 128 x 128 in r space, one sample per piece, an empty sample
-    ("bf16", 5, 150, 136, 296, 72, [150, 20, 0, 77, 150]),
-    # 15 tiles with ragged tails in r and dout, 7 pieces of one sample
-    ("bf16", 7, 96, 64, 520, 264, None),
+    # 4 tiles of 128 x 128 in r space (a tail in r), 32 pieces of one
+    # sample; empty and one-token samples
+    ("bf16", 32, 50, 72, 256, 136, _LEN32),
+    # 15 tiles with ragged tails in r and dout, 20 samples over 17 pieces
+    # (pieces of one and two samples), three 64-token steps per sample
+    ("bf16", 20, 150, 64, 520, 264, None),
     # fp32, 2 tiles, 6 pieces, samples of 1 and 0 tokens
     ("f32", 6, 70, 40, 200, 40, [70, 1, 35, 0, 70, 12]),
 ])
@@ -400,7 +405,8 @@ def test_projected_rspace_tiles(tiles, dtype, B, T, din, dout, r, lengths):
     pieces, their parts added in order by a second kernel; 2: that and the
     direct norm on 128 x 128 tiles) against the oracle: the norms, the
     clipped sum element by element (mixed clipping, C at the median norm) and
-    the noise; each setting bitwise repeatable."""
+    the noise; each setting bitwise repeatable.  The shapes are ones the
+    pieces take (enough pieces to fill half the compute units)."""
     torch = need_gpu()
     import sample_gradient_clipping_amd as dp
     rng = np.random.default_rng(70 + B)
