@@ -603,6 +603,7 @@ __global__ void __launch_bounds__(kNT, 1) gram_norm_big_kernel(LayerArgs p, Gram
 // item and make the plan as the main kernel does.
 constexpr int kFixParts = 8;
 constexpr int kFixQuads = kAccFloats / 4 / kFixParts;   // 4
+constexpr int kFixBatch = 4;                            // pieces whose loads are in flight together
 __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPlan gp,
                                                             const uint32_t* live, int cap,
                                                             const float* pieces, double* part) {
@@ -622,14 +623,34 @@ __global__ void __launch_bounds__(kNT, 1) gram_fixup_kernel(LayerArgs p, GramPla
     sx[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     sg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int c = 0; c < gp.P; ++c) {
-    const Parts pt((int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), nkx);
-    const f32x4* src = (const f32x4*)(pieces + (int64_t)(c * gp.R + r) * 2 * kGramFloats) +
-                       (h * kFixQuads) * kNT + threadIdx.x;
+  // The loads of kFixBatch pieces are issued before any of their sums, so
+  // that they are in flight together; each piece's load covers only the
+  // sides it touched, and the sums run in piece order.
+  for (int c0 = 0; c0 < gp.P; c0 += kFixBatch) {
+    f32x4 wx[kFixBatch][kFixQuads], wg[kFixBatch][kFixQuads];
+    bool tx[kFixBatch], tg[kFixBatch];
 #pragma unroll
-    for (int x = 0; x < kFixQuads; ++x) {
-      if (pt.x1 > pt.x0) sx[x] += src[x * kNT];
-      if (pt.g1 > pt.g0) sg[x] += src[kGramFloats / 4 + x * kNT];
+    for (int j = 0; j < kFixBatch; ++j) {
+      const int c = c0 + j;
+      const Parts pt((int)((int64_t)c * n / gp.P), (int)((int64_t)(c + 1) * n / gp.P), nkx);
+      tx[j] = c < gp.P && pt.x1 > pt.x0;
+      tg[j] = c < gp.P && pt.g1 > pt.g0;
+      const f32x4* src = (const f32x4*)(pieces + (int64_t)(min(c, gp.P - 1) * gp.R + r) * 2 *
+                                                     kGramFloats) +
+                         (h * kFixQuads) * kNT + threadIdx.x;
+#pragma unroll
+      for (int x = 0; x < kFixQuads; ++x) {
+        wx[j][x] = tx[j] ? src[x * kNT] : f32x4{0.f, 0.f, 0.f, 0.f};
+        wg[j][x] = tg[j] ? src[kGramFloats / 4 + x * kNT] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFixBatch; ++j) {
+#pragma unroll
+      for (int x = 0; x < kFixQuads; ++x) {
+        if (tx[j]) sx[x] += wx[j][x];
+        if (tg[j]) sg[x] += wg[j][x];
+      }
     }
   }
   float sum = 0.f;
