@@ -55,11 +55,11 @@ KERNEL_COUNTERS = {
     "fetch_scale": 2.0, "write_scale": 1.0,
     "kernels": {
         "accumulate": {"sources_sha256": "cfc2fa80dca168539b532d85f1c9cac808c9ce9461eb95419b504cb4245f4141",
-                       "fetch_kib": 1130394.79, "write_kib": 279698.29, "mfma_busy_pct": 59.84,
-                       "trace_avg_us": 1288.9},
-        "gram_norm": {"sources_sha256": "5961bdc8fd6118083cfcb91797fcb5c9f0ba59e18e3b4531a0ed7512fe52b137",
-                      "fetch_kib": 413918.2, "write_kib": 163988.28, "mfma_busy_pct": 64.81,
-                      "trace_avg_us": 429.1},
+                       "fetch_kib": 1129356.27, "write_kib": 279698.29, "mfma_busy_pct": 60.04,
+                       "trace_avg_us": 1290.7},
+        "gram_norm": {"sources_sha256": "51d8ce09f519858dcd13a5155fb6c9ea7f3f83ebdad8b08bc83deabd8e6bed25",
+                      "fetch_kib": 413893.85, "write_kib": 163988.44, "mfma_busy_pct": 63.73,
+                      "trace_avg_us": 430.3},
     },
     # --norm-path values that run these kernels on every linear of the workload
     "paths": ("0", "1"),
