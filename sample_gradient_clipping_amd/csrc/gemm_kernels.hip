@@ -17,8 +17,12 @@
 //                      optionally split along din into fp32 partials that
 //                      project_reduce_kernel sums in chunk order; P is read,
 //                      or (GEN) drawn from its seed where it is loaded.
+//  accumulate_pieces_kernel: the accumulation for outputs of few tiles (the
+//                      projected variant's r-space sum), each tile's samples
+//                      cut into pieces; accumulate_pieces_fixup_kernel adds
+//                      the pieces' parts in order, with the noise.
 //
-// All four: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 2 x 2
+// All of them: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 2 x 2
 // blocks of 32 x 32 accumulators (a 128 x 128 workgroup tile), LDS double
 // buffered along K.  Partial results leave as fp64 per workgroup and are
 // summed in index order by finalize_kernel, so every reduction is fixed-order.
